@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs for the group-wise fake-quant linear.
+
+This module only draws random tensors. It holds none of the method's
+arithmetic (no scale, zero point, code, dequantisation or gradient): both the
+HIP path and the fp64 oracle take its outputs as plain inputs.
+
+Shapes and distributions follow the workloads of the EfficientQAT pages:
+Llama-2-7B / 70B linear shapes, Block-AP on 2048-token samples and E2E-QP on
+4096-token samples ("The recipe in numbers" table on the modelfoundations.com
+EfficientQAT note). No dataset or pretrained weight is used; the tensors stand
+in for RedPajama activations and Llama weights.
+
+Conventions
+-----------
+* Generator: ``numpy.random.Generator(PCG64(seed))`` with
+  ``seed = 1000 * cfg + 10 * layer + tensor_id`` and tensor ids
+  W=1, X=2, dY=3, outlier positions=4, s=5, codes/z=6.
+* Values are drawn in fp32. bf16 tensors are produced by round-to-nearest-even
+  from fp32 through torch's CPU conversion and returned as uint16 bit patterns.
+* "0.1% entries x10 outliers": exactly round(0.001*out*in) distinct positions,
+  uniform without replacement, multiplied by 10 (sign kept).
+* "8 outlier channels x20": 8 distinct input-feature columns of X scaled by 20
+  before the bf16 rounding.
+* E2E-QP packed weights with uniform codes: every N-bit field uniform on
+  0..2^N-1 and independent is the same as every byte uniform on 0..255, so the
+  packed tensor is drawn directly as uniform random bytes of shape
+  [out, in*N/8]; no packing is done here.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import List, Optional
+
+import numpy as np
+
+GROUP = 64
+
+TID_W, TID_X, TID_DY, TID_OUTL, TID_S, TID_CODES = 1, 2, 3, 4, 5, 6
+
+
+def rng(cfg: int, layer: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(1000 * cfg + 10 * layer + tensor_id))
+
+
+def to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 (round to nearest even) as uint16 bits, via torch's CPU cast."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def sha256(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def weight(cfg: int, layer: int, out: int, inp: int, sigma: float, outliers: bool) -> np.ndarray:
+    """fp32 master weight [out, in] ~ N(0, sigma), optional 0.1% x10 outliers."""
+    w = rng(cfg, layer, TID_W).standard_normal((out, inp), dtype=np.float32)
+    w *= np.float32(sigma)
+    if outliers:
+        n = int(round(0.001 * out * inp))
+        pos = rng(cfg, layer, TID_OUTL).choice(out * inp, size=n, replace=False)
+        flat = w.reshape(-1)
+        flat[pos] *= np.float32(10.0)
+    return w
+
+
+def activations(cfg: int, layer: int, m: int, inp: int, outlier_channels: int = 0) -> np.ndarray:
+    """bf16 bits [m, in] ~ N(0, 1), optional outlier columns x20 before rounding."""
+    x = rng(cfg, layer, TID_X).standard_normal((m, inp), dtype=np.float32)
+    if outlier_channels:
+        cols = rng(cfg, layer, TID_OUTL + 100).choice(inp, size=outlier_channels, replace=False)
+        x[:, cols] *= np.float32(20.0)
+    return to_bf16_bits(x)
+
+
+def grad_out(cfg: int, layer: int, m: int, out: int, std: float = 1e-3) -> np.ndarray:
+    """bf16 bits [m, out] ~ N(0, std)."""
+    g = rng(cfg, layer, TID_DY).standard_normal((m, out), dtype=np.float32)
+    g *= np.float32(std)
+    return to_bf16_bits(g)
+
+
+def packed_codes(cfg: int, layer: int, out: int, inp: int, bits: int) -> np.ndarray:
+    """Uniform random packed bytes [out, in*bits/8] (uniform independent codes)."""
+    assert (inp * bits) % 8 == 0
+    return rng(cfg, layer, TID_CODES).integers(0, 256, size=(out, inp * bits // 8), dtype=np.uint8)
+
+
+def e2e_scales(cfg: int, layer: int, out: int, inp: int, lo: float = 0.005, hi: float = 0.05) -> np.ndarray:
+    """fp32 step sizes [out, in/64] ~ U(lo, hi)."""
+    return rng(cfg, layer, TID_S).uniform(lo, hi, size=(out, inp // GROUP)).astype(np.float32)
+
+
+def e2e_zeros(cfg: int, layer: int, out: int, inp: int, bits: int) -> np.ndarray:
+    """fp32 integer-valued zero points [out, in/64], uniform over {0..2^bits-1}."""
+    k = (1 << bits) - 1
+    return rng(cfg, layer, TID_CODES + 100).integers(0, k + 1, size=(out, inp // GROUP)).astype(np.float32)
+
+
+def perturb_qparams(seed: int, s: np.ndarray, z: np.ndarray, bits: int, frac: float = 0.25):
+    """Parity-only variant that makes the clamp, the mask and dz non-trivial.
+
+    s <- 0.75*s everywhere; on a seeded `frac` of the groups z moves by +1 or -1
+    and is kept inside [0, 2^bits-1]. Returns new (s, z) fp32 arrays.
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    k = (1 << bits) - 1
+    s2 = (s.astype(np.float32) * np.float32(0.75)).astype(np.float32)
+    pick = g.random(z.shape) < frac
+    step = np.where(g.random(z.shape) < 0.5, -1.0, 1.0).astype(np.float32)
+    z2 = np.where(pick, np.clip(z + step, 0, k), z).astype(np.float32)
+    return s2, z2
+
+
+# --------------------------------------------------------------------------
+# The five workloads
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Linear:
+    name: str
+    out: int
+    inp: int
+    m: int
+    bits: int
+    sigma: float = 0.02
+    outliers: bool = True
+    x_outlier_channels: int = 0
+    cfg: int = 0
+    layer: int = 0
+
+    @property
+    def groups(self) -> int:
+        return self.inp // GROUP
+
+    def W(self) -> np.ndarray:
+        return weight(self.cfg, self.layer, self.out, self.inp, self.sigma, self.outliers)
+
+    def X(self) -> np.ndarray:
+        return activations(self.cfg, self.layer, self.m, self.inp, self.x_outlier_channels)
+
+    def dY(self) -> np.ndarray:
+        return grad_out(self.cfg, self.layer, self.m, self.out)
+
+    def Wq(self) -> np.ndarray:
+        return packed_codes(self.cfg, self.layer, self.out, self.inp, self.bits)
+
+    def s_e2e(self) -> np.ndarray:
+        return e2e_scales(self.cfg, self.layer, self.out, self.inp)
+
+    def z_e2e(self) -> np.ndarray:
+        return e2e_zeros(self.cfg, self.layer, self.out, self.inp, self.bits)
+
+
+def config(cfg: int, bits: Optional[int] = None) -> List[Linear]:
+    """The linears of workload `cfg` (1..5).
+
+    1: toy 256x256, M=128, w2g64.
+    2: Llama-2-7B q_proj 4096x4096, M=2048, w2g64, X with 8 outlier channels.
+    3: the seven linears of a Llama-2-7B block, M=2048, w3g64, no outliers.
+    4: E2E-QP Llama-2-7B MLP (gate, up 11008x4096; down 4096x11008), M=4096, w2.
+    5: Llama-2-70B gate 28672x8192 and down 8192x28672, M=4096, w2/w3/w4.
+    """
+    if cfg == 1:
+        return [Linear("toy", 256, 256, 128, 2, cfg=1)]
+    if cfg == 2:
+        return [Linear("q_proj", 4096, 4096, 2048, 2, x_outlier_channels=8, cfg=2)]
+    if cfg == 3:
+        shapes = [("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096),
+                  ("o_proj", 4096, 4096), ("gate_proj", 11008, 4096), ("up_proj", 11008, 4096),
+                  ("down_proj", 4096, 11008)]
+        return [Linear(n, o, i, 2048, 3, outliers=False, cfg=3, layer=li)
+                for li, (n, o, i) in enumerate(shapes)]
+    if cfg == 4:
+        shapes = [("gate_proj", 11008, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 11008)]
+        return [Linear(n, o, i, 4096, 2, cfg=4, layer=li) for li, (n, o, i) in enumerate(shapes)]
+    if cfg == 5:
+        b = 2 if bits is None else bits
+        shapes = [("gate_proj", 28672, 8192), ("down_proj", 8192, 28672)]
+        return [Linear(n, o, i, 4096, b, sigma=0.015, cfg=5, layer=li + 10 * b)
+                for li, (n, o, i) in enumerate(shapes)]
+    raise ValueError(f"unknown workload {cfg}")
