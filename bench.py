@@ -1,0 +1,201 @@
+"""Benchmark of the group-wise fake-quant linear hot path on one MI355X.
+
+One step = one pass of every operation of the path over one batch:
+  init (min-max) -> fake-quant forward -> straight-through backward
+  (dX, dW, ds, dz) -> pack -> E2E-QP dequant-GEMM forward -> E2E-QP backward
+  (dX, ds),
+on the Llama-2-7B q_proj workload: fp32 W 4096x4096 ~N(0, 0.02) with 0.1% x10
+outliers, w2g64, X 2048x4096 bf16 ~N(0,1) with 8 outlier channels x20,
+dY ~N(0, 1e-3). Inputs are resident in HBM before the timed region.
+
+value = counted GEMM FLOPs of the step / step time, where the count is
+6*M*in*out for the fake-quant forward + backward plus 6*M*in*out for the
+E2E-QP forward + dX + ds (init and pack add time, no FLOPs).
+
+Prints one JSON line (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="weight rows of the bounded oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from weight_quantization_aware_amd import _lib as Q
+    from weight_quantization_aware_amd import synth
+
+    dev = torch.device("cuda:0")
+    lin = synth.config(2)[0]
+    M, out, inp, bits = lin.m, lin.out, lin.inp, lin.bits
+    G = inp // 64
+    W_np, X_np, dY_np = lin.W(), lin.X(), lin.dY()
+
+    W = torch.from_numpy(W_np).to(dev)
+    X = torch.from_numpy(X_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    dY = torch.from_numpy(dY_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    s = torch.empty(out, G, device=dev)
+    z = torch.empty_like(s)
+    Y = torch.empty(M, out, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, inp, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(out, inp, device=dev)
+    ds = torch.empty_like(s)
+    dz = torch.empty_like(s)
+    Wq = torch.empty(out, inp * bits // 8, dtype=torch.uint8, device=dev)
+    zp = torch.empty_like(s)
+    Y2 = torch.empty_like(Y)
+    dX2 = torch.empty_like(dX)
+    ds2 = torch.empty_like(s)
+    ws = Q.workspace(max(Q.fakequant_ws_bytes(M, out, inp), Q.dequant_ws_bytes(M, out, inp)), dev)
+
+    calls = [
+        ("init", lambda: Q.qat_init_minmax(W, bits, s, z)),
+        ("fq_fwd", lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=None)),
+        ("fq_bwd", lambda: Q.qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=dX, dW=dW, ds=ds, dz=dz, ws=ws)),
+        ("pack", lambda: Q.qat_pack(W, s, z, bits, Wq, zp)),
+        ("e2e_fwd", lambda: Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Y2)),
+        ("e2e_bwd", lambda: Q.qat_dequant_gemm_bwd_s(dY, X, Wq, s, zp, bits, ds2, dX=dX2, ws=ws)),
+    ]
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize(dev)
+
+    # Per-call events on the stream the library launches on (the current stream).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        for i, (_, f) in enumerate(calls):
+            f()
+            ev[k][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    per_call = {name: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+                for i, (name, _) in enumerate(calls)}
+
+    flops_fq = 6.0 * M * inp * out
+    flops_e2e = 6.0 * M * inp * out
+    value = (flops_fq + flops_e2e) / (ms_step * 1e-3) / 1e12
+
+    # Dominant kernel: the fused fake-quant forward GEMM (one kernel per call).
+    t_fwd = per_call["fq_fwd"] * 1e-3
+    fwd_tflops = 2.0 * M * inp * out / t_fwd / 1e12
+    roofline = {"kernel": "k_gemm<fp32-quant-into-LDS> (qat_fakequant_linear_fwd, ws=NULL)",
+                "bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None}
+
+    breakdown = {name: {"ms": round(t, 4)} for name, t in per_call.items()}
+    breakdown["fq_fwd"]["tflops"] = round(2 * M * inp * out / (per_call["fq_fwd"] * 1e-3) / 1e12, 1)
+    breakdown["fq_bwd"]["tflops"] = round(4 * M * inp * out / (per_call["fq_bwd"] * 1e-3) / 1e12, 1)
+    breakdown["e2e_fwd"]["tflops"] = round(2 * M * inp * out / (per_call["e2e_fwd"] * 1e-3) / 1e12, 1)
+    breakdown["e2e_bwd"]["tflops"] = round(4 * M * inp * out / (per_call["e2e_bwd"] * 1e-3) / 1e12, 1)
+    breakdown["init"]["gbs"] = round(out * inp * 4.125 / (per_call["init"] * 1e-3) / 1e9, 1)
+    breakdown["pack"]["gbs"] = round(out * inp * (4.125 + bits / 8) / (per_call["pack"] * 1e-3) / 1e9, 1)
+    fq_only = flops_fq / ((per_call["fq_fwd"] + per_call["fq_bwd"]) * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(lin, W_np, X_np, dY_np, args.cpu_rows)
+
+    line = {
+        "metric": "fake-quant linear fwd+bwd TFLOP/s (w2g64, Llama-2-7B shapes); % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama2-7b q_proj 4096x4096, 2048 tokens, w2g64: init + fake-quant "
+                               "fwd/bwd + pack + E2E-QP fwd/bwd", "M": M, "out": out, "in": inp,
+                   "bits": bits, "group": 64},
+        "fq_fwd_bwd_tflops": round(fq_only, 2),
+        "mfma_peak_frac_fq": round(fq_only / MFMA_BF16_PEAK_TFLOPS, 4),
+        "breakdown": breakdown,
+        "wall_s": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(lin, W_np, X_np, dY_np, rows):
+    """The fp64 oracle timed on the host on a bounded sample: the same step
+    restricted to the first `rows` weight rows (all tokens, all inputs)."""
+    from oracle import qat_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    M, inp, bits = lin.m, lin.inp, lin.bits
+    W = W_np[:rows]
+    dY = dY_np[:, :rows].copy()
+
+    def step():
+        s, z = O.init_minmax(W, bits)
+        O.fakequant_fwd(X_np, W, s, z, bits)
+        O.fakequant_bwd(dY, X_np, W, s, z, bits)
+        Wq, zp = O.pack(W, s, z, bits)
+        O.dequant_gemm_fwd(X_np, Wq, s, zp, inp, bits)
+        O.dequant_gemm_bwd_s(dY, X_np, Wq, s, zp, inp, bits)
+
+    t0 = time.perf_counter()
+    step()
+    t1 = time.perf_counter()
+    reps = 1
+    while time.perf_counter() - t0 < 10.0 and reps < 5:
+        step()
+        reps += 1
+    dt = (time.perf_counter() - t1) / max(reps - 1, 1) if reps > 1 else t1 - t0
+    flops = 12.0 * M * inp * rows
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"same step on the first {rows} of {lin.out} weight rows (all {M} tokens, "
+                      f"all {inp} inputs), {reps} runs, mean of the timed ones; fp64 numpy"}
+
+
+if __name__ == "__main__":
+    main()

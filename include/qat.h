@@ -1,0 +1,161 @@
+/*
+ * qat.h -- C ABI of the MI355X (gfx950) group-wise fake-quantised linear.
+ *
+ * The operations are those of EfficientQAT (arXiv 2407.11062):
+ *   Block-AP: per-group min-max init, the quantiser
+ *     W_int = clamp(round(W/s) + z, 0, 2^N - 1)          (Eq. 1)
+ *   and dequantiser W_hat = (W_int - z) * s               (Eq. 2),
+ *   a bf16 GEMM forward and the straight-through backward;
+ *   E2E-QP: packed integer weights and frozen zero points, only the step
+ *   sizes train, with the exact gradient dW_hat/ds = W_int - z.
+ * Sources: "EfficientQAT" Paper-Notes (zhaoyang97, ACL2025), method details
+ * (Eq. 1, Eq. 2, E2E-QP gradient); "EfficientQAT, low-bit training on a single
+ * GPU" (modelfoundations.com), Phase 1 (min-max init, ~4096 steps per block)
+ * and Phase 2 (exact scale gradient), and its "Paper vs. code" section (float
+ * zero point rounded straight-through, hard-rounded at pack; FP32 blocks);
+ * paperlayer.ai summary of arXiv 2407.11062v3, Appendix A (straight-through
+ * estimator; gradients for s, z and W) and Appendix D (one step size and one
+ * N-bit zero point per group of g weights).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Shapes: W is [out, in] row-major (nn.Linear). Groups are `group` = 64
+ *   consecutive elements of a row along `in`; G = in / 64 groups per row.
+ *   s, z, ds, dz are [out, G] fp32 row-major. X is [M, in], Y and dY are
+ *   [M, out], dX is [M, in]; all bf16 passed as uint16_t bit patterns.
+ * - bits N in {2, 3, 4}; K = 2^N - 1.
+ * - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *   never allocates, frees or keeps them beyond the enqueued work.
+ * - Inputs are const and never written. Outputs are fully overwritten (never
+ *   accumulated) and must not overlap inputs or each other.
+ * - Every call is asynchronous on `stream` (0 = the null stream) and performs
+ *   no device synchronisation.
+ * - Every tensor pointer must be 16-byte aligned.
+ * - Arguments are validated on the host BEFORE anything is enqueued; on error
+ *   nothing is launched and no output is touched. No exception crosses the ABI.
+ * - Numerics: s, z and u = W/s are IEEE fp32 results of single correctly
+ *   rounded operations; round() is round-half-to-even; W_hat is rounded
+ *   fp32 -> bf16 (nearest-even) as the GEMM operand; GEMMs accumulate in fp32.
+ *
+ * Return value: QAT_OK or one of the QAT_ERR_* codes below.
+ */
+#ifndef QAT_H
+#define QAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QAT_OK = 0,
+  QAT_ERR_NULL = 1,      /* a required pointer is NULL                                   */
+  QAT_ERR_SHAPE = 2,     /* a dimension <= 0, in % group != 0, or a size overflows         */
+  QAT_ERR_BITS = 3,      /* bits not in {2, 3, 4}                                          */
+  QAT_ERR_GROUP = 4,     /* group != 64                                                    */
+  QAT_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                               */
+  QAT_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the size query returns          */
+  QAT_ERR_HIP = 7,       /* a HIP launch failed; qat_last_error() has the HIP message      */
+  QAT_ERR_ALIAS = 8      /* an output overlaps an input or another output                  */
+};
+
+/* Text of a status code (static storage). */
+const char* qat_status_string(int32_t status);
+
+/* HIP error text of the last QAT_ERR_HIP on the calling thread ("" if none). */
+const char* qat_last_error(void);
+
+/*
+ * a1. Per-group min-max init (modelfoundations.com note, Phase 1):
+ *   for each row o and group j of W:
+ *     d = fl32(max - min);  s = max(fl32(d / K), fl32(1e-5));  z = rint(fl32(-min / s)).
+ * W [out, in] fp32 in; s, z [out, in/64] fp32 out (z is integer valued).
+ */
+int32_t qat_init_minmax(const float* W, int64_t out, int64_t in, int32_t group, int32_t bits,
+                        float* s, float* z, hipStream_t stream);
+
+/*
+ * a2+a3 as a standalone export (Paper-Notes, Eq. 1 and Eq. 2):
+ *   zr = clamp(rint(z), 0, K); u = fl32(W / s); q = clamp(rint(u) + zr, 0, K);
+ *   codes = q (uint8, [out, in]); W_hat = bf16(fl32((q - zr) * s)) ([out, in]).
+ * Either output may be NULL (not both).
+ */
+int32_t qat_quant_codes(const float* W, const float* s, const float* z, int64_t out, int64_t in,
+                        int32_t group, int32_t bits, uint8_t* codes, uint16_t* W_hat,
+                        hipStream_t stream);
+
+/* Workspace bytes that qat_fakequant_linear_fwd / _bwd need for these sizes. */
+size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in);
+
+/*
+ * a2-a4. Fake-quantised linear forward: Y = X * W_hat^T, with W_hat from
+ * W, s, z exactly as in qat_quant_codes (the zero point is rounded and clamped
+ * straight-through, as the "Paper vs. code" section of the modelfoundations.com
+ * note describes). X [M, in] bf16, Y [M, out] bf16; fp32 accumulation.
+ * ws: NULL selects the fused kernel that quantises fp32 W tiles directly into
+ * LDS; otherwise >= qat_fakequant_ws_bytes(M, out, in) bytes of device memory
+ * used as scratch for a bf16 W_hat staged once per call.
+ */
+int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float* s, const float* z,
+                                 int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
+                                 uint16_t* Y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * a5-a7. Straight-through backward (paperlayer.ai summary, Appendix A; the
+ * gradient formulas follow from Eq. 1-2 with identity derivative for round):
+ *   dX = dY * W_hat                                  [M, in]  bf16
+ *   Gw = dY^T * X;  m = [0 <= rint(u) + zr <= K]
+ *   dW = Gw * m                                      [out, in] fp32
+ *   ds[o,j] = sum_{i in j} Gw[o,i] * (m_i ? rint(u_i) - u_i : q_i - zr)
+ *   dz[o,j] = -s[o,j] * sum_{i in j, m_i = 0} Gw[o,i]  [out, G] fp32
+ * Any of dX, dW, ds, dz may be NULL to skip it (ds and dz come together: both
+ * NULL or both set). ws is required: >= qat_fakequant_ws_bytes(M, out, in).
+ */
+int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
+                                 const float* s, const float* z, int64_t M, int64_t out, int64_t in,
+                                 int32_t group, int32_t bits, uint16_t* dX, float* dW, float* ds,
+                                 float* dz, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * a8. Pack (modelfoundations.com note: a trained block is quantised in place;
+ * zero points are hard-rounded at pack time): zp = clamp(rint(z), 0, K),
+ * codes as in qat_quant_codes with zp, written as a per-row LSB-first
+ * bitstream: code i occupies bits [N*i, N*i+N) of the row; row stride in*N/8
+ * bytes. Wq [out, in*N/8] uint8 out; z_round [out, G] fp32 out (may be NULL).
+ */
+int32_t qat_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in,
+                 int32_t group, int32_t bits, uint8_t* Wq, float* z_round, hipStream_t stream);
+
+/* Workspace bytes that qat_dequant_gemm_bwd_s needs for these sizes. */
+size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in);
+
+/*
+ * a9. E2E-QP forward (modelfoundations.com note, Phase 2; Paper-Notes, E2E-QP):
+ * W_hat = bf16(fl32((q - z) * s)) with q unpacked from Wq and z used as stored
+ * (frozen, integer valued); Y = X * W_hat^T. No workspace: the packed codes are
+ * dequantised straight into LDS inside the GEMM.
+ */
+int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* s, const float* z,
+                             int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
+                             uint16_t* Y, hipStream_t stream);
+
+/*
+ * a10. E2E-QP backward with the exact scale gradient dW_hat/ds = q - z:
+ *   dX = dY * W_hat (may be NULL);
+ *   ds[o,j] = sum_{i in j} Gw[o,i] * (q_i - z[o,j]),  Gw = dY^T X (never stored);
+ *   dz[o,j] = -s[o,j] * sum_{i in j} Gw[o,i]  (the train-s-and-z variant of the
+ *   Paper-Notes ablation table; may be NULL).
+ * ws is required: >= qat_dequant_ws_bytes(M, out, in).
+ */
+int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint8_t* Wq,
+                               const float* s, const float* z, int64_t M, int64_t out, int64_t in,
+                               int32_t group, int32_t bits, uint16_t* dX, float* ds, float* dz,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QAT_H */

@@ -1,0 +1,84 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/qat.h declares, and rejects bad arguments on the host before any HIP
+call (these calls return before touching a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_quantization_aware_amd import _lib as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "qat.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qat_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_calls():
+    names = declared()
+    for n in ["qat_init_minmax", "qat_fakequant_linear_fwd", "qat_fakequant_linear_bwd", "qat_pack",
+              "qat_dequant_gemm_fwd", "qat_dequant_gemm_bwd_s", "qat_quant_codes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    h = ctypes.CDLL(Q.LIB_PATH)
+    for n in declared():
+        assert hasattr(h, n), n
+    assert set(declared()) <= set(Q._SIGS)
+
+
+def test_status_strings():
+    L = Q.lib()
+    for st in range(9):
+        assert L.qat_status_string(st)
+    assert L.qat_last_error() == b""
+
+
+def test_workspace_sizes():
+    # [W_hat (out*in*2) | dY^T (out*Mp*2) | X^T (in*Mp*2)], Mp = M rounded up to 64
+    assert Q.fakequant_ws_bytes(2048, 4096, 4096) == 4096 * 4096 * 2 + 2 * 4096 * 2048 * 2
+    assert Q.fakequant_ws_bytes(1, 64, 64) == 64 * 64 * 2 + 2 * 64 * 64 * 2
+    assert Q.fakequant_ws_bytes(0, 64, 64) == 0
+    assert Q.dequant_ws_bytes(100, 192, 128) == Q.fakequant_ws_bytes(100, 192, 128)
+
+
+FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced on the error paths
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 64, 128, 64, 5, FAKE, FAKE + 4096, None), 3),        # bits
+    ((FAKE, 64, 128, 32, 2, FAKE, FAKE + 4096, None), 4),        # group
+    ((FAKE, 64, 96, 64, 2, FAKE, FAKE + 4096, None), 2),         # in % 64
+    ((FAKE, 0, 128, 64, 2, FAKE, FAKE + 4096, None), 2),         # out <= 0
+    ((None, 64, 128, 64, 2, FAKE, FAKE + 4096, None), 1),        # null W
+    ((FAKE + 4, 64, 128, 64, 2, FAKE, FAKE + 4096, None), 5),    # misaligned
+    ((FAKE, 64, 128, 64, 2, FAKE, FAKE, None), 8),               # s aliases z
+    ((FAKE, 64, 128, 64, 2, FAKE + 16, FAKE + 1 << 30, None), 8),  # s inside W
+])
+def test_init_validation(args, status):
+    assert Q.lib().qat_init_minmax(*args) == status
+
+
+def test_fwd_bwd_validation():
+    L = Q.lib()
+    A, B, C, D, E = (FAKE * k for k in range(1, 6))
+    # fwd: workspace given but too small
+    assert L.qat_fakequant_linear_fwd(A, B, C, D, 8, 64, 128, 64, 2, E, FAKE * 7, 16, None) == 6
+    # fwd: M <= 0
+    assert L.qat_fakequant_linear_fwd(A, B, C, D, 0, 64, 128, 64, 2, E, None, 0, None) == 2
+    # bwd: workspace is required
+    assert L.qat_fakequant_linear_bwd(A, B, C, D, E, 8, 64, 128, 64, 2, FAKE * 6, None, None, None,
+                                      None, 0, None) == 6
+    # bwd: ds without dz
+    assert L.qat_fakequant_linear_bwd(A, B, C, D, E, 8, 64, 128, 64, 2, None, None, FAKE * 6, None,
+                                      FAKE * 7, 1 << 30, None) == 1
+    # e2e bwd: ds is required
+    assert L.qat_dequant_gemm_bwd_s(A, B, C, D, E, 8, 64, 128, 64, 2, None, None, None, FAKE * 7,
+                                    1 << 30, None) == 1
+    # pack: 3 bits with a group-aligned row is fine shape-wise, bits 1 is not
+    assert L.qat_pack(A, B, C, 64, 128, 64, 1, D, None, None) == 3

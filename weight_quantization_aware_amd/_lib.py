@@ -1,0 +1,163 @@
+"""Thin ctypes binding over libqat.so (the HIP kernels + C ABI in include/qat.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch supplies device memory and the current HIP stream. If the library is
+not built, importing the functions raises; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqat.so")
+
+QAT_OK = 0
+GROUP = 64
+
+_c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> argument types (all pointers as void*)
+_SIGS = {
+    "qat_init_minmax": [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp],
+    "qat_quant_codes": [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp],
+    "qat_fakequant_linear_fwd": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
+                                 _c_vp, _c_vp, _c_sz, _c_vp],
+    "qat_fakequant_linear_bwd": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32,
+                                 _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
+    "qat_pack": [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp],
+    "qat_dequant_gemm_fwd": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
+                             _c_vp, _c_vp],
+    "qat_dequant_gemm_bwd_s": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32,
+                               _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
+    "qat_fakequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
+    "qat_dequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
+    "qat_status_string": [_c_i32],
+    "qat_last_error": [],
+}
+_RES = {"qat_fakequant_ws_bytes": _c_sz, "qat_dequant_ws_bytes": _c_sz,
+        "qat_status_string": ctypes.c_char_p, "qat_last_error": ctypes.c_char_p}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqat.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m weight_quantization_aware_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(h, name)
+            f.argtypes = args
+            f.restype = _RES.get(name, _c_i32)
+        _lib = h
+    return _lib
+
+
+class QatError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        L = lib()
+        msg = L.qat_status_string(status).decode()
+        if status == 7:
+            msg += ": " + L.qat_last_error().decode()
+        super().__init__(f"{fn} -> {status} ({msg})")
+        self.status = status
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != QAT_OK:
+        raise QatError(name, st)
+
+
+def _u16(t: torch.Tensor) -> torch.Tensor:
+    """bf16 tensors travel as their 16-bit patterns."""
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected a bf16 tensor, got {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# Workspace size queries
+# ---------------------------------------------------------------------------
+
+def fakequant_ws_bytes(M: int, out: int, inp: int) -> int:
+    return int(lib().qat_fakequant_ws_bytes(M, out, inp))
+
+
+def dequant_ws_bytes(M: int, out: int, inp: int) -> int:
+    return int(lib().qat_dequant_ws_bytes(M, out, inp))
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device or "cuda")
+
+
+# ---------------------------------------------------------------------------
+# The C-ABI calls, same names as in include/qat.h
+# ---------------------------------------------------------------------------
+
+def qat_init_minmax(W: torch.Tensor, bits: int, s: torch.Tensor, z: torch.Tensor) -> None:
+    out, inp = W.shape
+    _call("qat_init_minmax", _p(W), out, inp, GROUP, bits, _p(s), _p(z), _stream())
+
+
+def qat_quant_codes(W, s, z, bits, codes=None, W_hat=None) -> None:
+    out, inp = W.shape
+    _call("qat_quant_codes", _p(W), _p(s), _p(z), out, inp, GROUP, bits, _p(codes),
+          _p(None if W_hat is None else _u16(W_hat)), _stream())
+
+
+def qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=None) -> None:
+    M, inp = X.shape
+    out = W.shape[0]
+    _call("qat_fakequant_linear_fwd", _p(_u16(X)), _p(W), _p(s), _p(z), M, out, inp, GROUP, bits,
+          _p(_u16(Y)), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
+
+
+def qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=None, dW=None, ds=None, dz=None, ws=None) -> None:
+    M, inp = X.shape
+    out = W.shape[0]
+    _call("qat_fakequant_linear_bwd", _p(_u16(dY)), _p(_u16(X)), _p(W), _p(s), _p(z), M, out, inp,
+          GROUP, bits, _p(None if dX is None else _u16(dX)), _p(dW), _p(ds), _p(dz), _p(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream())
+
+
+def qat_pack(W, s, z, bits, Wq, z_round=None) -> None:
+    out, inp = W.shape
+    _call("qat_pack", _p(W), _p(s), _p(z), out, inp, GROUP, bits, _p(Wq), _p(z_round), _stream())
+
+
+def qat_dequant_gemm_fwd(X, Wq, s, z, bits, Y) -> None:
+    M, inp = X.shape
+    out = Wq.shape[0]
+    _call("qat_dequant_gemm_fwd", _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp, GROUP, bits,
+          _p(_u16(Y)), _stream())
+
+
+def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None) -> None:
+    M, inp = X.shape
+    out = Wq.shape[0]
+    _call("qat_dequant_gemm_bwd_s", _p(_u16(dY)), _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp,
+          GROUP, bits, _p(None if dX is None else _u16(dX)), _p(ds), _p(dz), _p(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream())

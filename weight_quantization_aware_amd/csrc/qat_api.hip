@@ -1,0 +1,359 @@
+// C ABI of the group-wise fake-quant linear: argument validation, workspace
+// layout and the launch sequence of each call. Everything is validated on the
+// host before the first launch; on error nothing is enqueued.
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/qat.h"
+#include "qat_internal.h"
+
+#define QAT_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;      // GEMM indices are 32-bit
+constexpr int64_t kMaxGridY = 65535;               // y-dimension of the 64x64 tile grids
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+size_t region(int64_t bytes) { return (size_t)round_up(bytes, 256); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Outputs must not overlap inputs or each other.
+int32_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return QAT_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return QAT_ERR_ALIAS;
+  }
+  return QAT_OK;
+}
+
+int32_t check_common(int64_t out, int64_t in, int32_t group, int32_t bits) {
+  if (group != 64) return QAT_ERR_GROUP;
+  if (bits < 2 || bits > 4) return QAT_ERR_BITS;
+  if (out <= 0 || in <= 0 || in % 64 != 0) return QAT_ERR_SHAPE;
+  if (out > kMaxDim || in > kMaxDim || out * in > (int64_t(1) << 40)) return QAT_ERR_SHAPE;
+  if (out / 64 + 1 > kMaxGridY) return QAT_ERR_SHAPE;
+  return QAT_OK;
+}
+
+int32_t check_m(int64_t M) {
+  if (M <= 0 || M > kMaxDim) return QAT_ERR_SHAPE;
+  if (round_up(M, 64) / 64 > kMaxGridY) return QAT_ERR_SHAPE;
+  return QAT_OK;
+}
+
+int32_t check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return QAT_ERR_ALIGN;
+  return QAT_OK;
+}
+
+int32_t finish() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return QAT_ERR_HIP;
+  }
+  return QAT_OK;
+}
+
+#define QAT_CHECK(x)               \
+  do {                             \
+    int32_t _st = (x);             \
+    if (_st != QAT_OK) return _st; \
+  } while (0)
+
+struct Ws {
+  size_t w_hat, x_t, dy_t, total;  // offsets of the regions and the total size
+};
+
+// One layout serves forward and backward: [W_hat or W_hat^T | dY^T | X^T].
+Ws ws_layout(int64_t M, int64_t out, int64_t in) {
+  const int64_t Mp = round_up(M, 64);
+  Ws w;
+  w.w_hat = 0;
+  w.dy_t = region(out * in * 2);
+  w.x_t = w.dy_t + region(out * Mp * 2);
+  w.total = w.x_t + region(in * Mp * 2);
+  return w;
+}
+
+qat::GemmArgs gemm_args() {
+  qat::GemmArgs a;
+  memset(&a, 0, sizeof a);
+  return a;
+}
+
+}  // namespace
+
+QAT_API const char* qat_status_string(int32_t st) {
+  switch (st) {
+    case QAT_OK: return "ok";
+    case QAT_ERR_NULL: return "a required pointer is NULL";
+    case QAT_ERR_SHAPE: return "invalid shape (dimension <= 0, in % 64 != 0, or too large)";
+    case QAT_ERR_BITS: return "bits must be 2, 3 or 4";
+    case QAT_ERR_GROUP: return "group must be 64";
+    case QAT_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case QAT_ERR_WORKSPACE: return "workspace missing or too small";
+    case QAT_ERR_HIP: return "HIP launch failed (see qat_last_error)";
+    case QAT_ERR_ALIAS: return "an output overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+QAT_API const char* qat_last_error(void) { return g_last_error; }
+
+QAT_API size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in) {
+  if (M <= 0 || out <= 0 || in <= 0) return 0;
+  return ws_layout(M, out, in).total;
+}
+
+QAT_API size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in) {
+  return qat_fakequant_ws_bytes(M, out, in);
+}
+
+QAT_API int32_t qat_init_minmax(const float* W, int64_t out, int64_t in, int32_t group, int32_t bits,
+                                float* s, float* z, hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  if (!W || !s || !z) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({W, s, z}));
+  const size_t nw = out * in * 4, ng = out * (in / 64) * 4;
+  Range outs[] = {{s, ng}, {z, ng}};
+  Range ins[] = {{W, nw}};
+  QAT_CHECK(check_alias(outs, 2, ins, 1));
+  qat::launch_init_minmax(W, out, in, bits, s, z, stream);
+  return finish();
+}
+
+QAT_API int32_t qat_quant_codes(const float* W, const float* s, const float* z, int64_t out, int64_t in,
+                                int32_t group, int32_t bits, uint8_t* codes, uint16_t* W_hat,
+                                hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  if (!W || !s || !z || (!codes && !W_hat)) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({W, s, z, codes, W_hat}));
+  const size_t n = out * in, ng = out * (in / 64) * 4;
+  Range outs[] = {{codes, n}, {W_hat, n * 2}};
+  Range ins[] = {{W, n * 4}, {s, ng}, {z, ng}};
+  QAT_CHECK(check_alias(outs, 2, ins, 3));
+  qat::launch_quant_codes(W, s, z, out, in, bits, codes, W_hat, stream);
+  return finish();
+}
+
+QAT_API int32_t qat_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in,
+                         int32_t group, int32_t bits, uint8_t* Wq, float* z_round, hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  if (!W || !s || !z || !Wq) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({W, s, z, Wq, z_round}));
+  const size_t n = out * in, ng = out * (in / 64) * 4;
+  Range outs[] = {{Wq, n * bits / 8}, {z_round, ng}};
+  Range ins[] = {{W, n * 4}, {s, ng}, {z, ng}};
+  QAT_CHECK(check_alias(outs, 2, ins, 3));
+  qat::launch_pack(W, s, z, out, in, bits, Wq, z_round, stream);
+  return finish();
+}
+
+QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float* s,
+                                         const float* z, int64_t M, int64_t out, int64_t in,
+                                         int32_t group, int32_t bits, uint16_t* Y, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  QAT_CHECK(check_m(M));
+  if (!X || !W || !s || !z || !Y) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({X, W, s, z, Y, ws}));
+  const Ws L = ws_layout(M, out, in);
+  if (ws && ws_bytes < L.total) return QAT_ERR_WORKSPACE;
+  const size_t ng = out * (in / 64) * 4;
+  Range outs[] = {{Y, (size_t)(M * out * 2)}, {ws, ws ? L.total : 0}};
+  Range ins[] = {{X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)}, {s, ng}, {z, ng}};
+  QAT_CHECK(check_alias(outs, 2, ins, 4));
+
+  qat::GemmArgs a = gemm_args();
+  a.A = X;
+  a.lda = in;
+  a.M = (int)M;
+  a.N = (int)out;
+  a.K = (int)in;
+  a.C = Y;
+  a.ldc = out;
+  a.s = s;
+  a.z = z;
+  a.G = in / 64;
+  a.Kq = (float)((1 << bits) - 1);
+  if (ws) {
+    uint16_t* w_hat = (uint16_t*)((char*)ws + L.w_hat);
+    qat::launch_quant_codes(W, s, z, out, in, bits, nullptr, w_hat, stream);
+    a.B = w_hat;
+    a.ldb = in;
+    qat::launch_gemm_bf16_out(a, qat::kBf16, bits, stream);
+  } else {
+    a.B = W;
+    a.ldb = in;
+    qat::launch_gemm_bf16_out(a, qat::kFp32Quant, bits, stream);
+  }
+  return finish();
+}
+
+QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
+                                         const float* s, const float* z, int64_t M, int64_t out,
+                                         int64_t in, int32_t group, int32_t bits, uint16_t* dX,
+                                         float* dW, float* ds, float* dz, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  QAT_CHECK(check_m(M));
+  if (!dY || !X || !W || !s || !z) return QAT_ERR_NULL;
+  if ((ds == nullptr) != (dz == nullptr)) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({dY, X, W, s, z, dX, dW, ds, dz, ws}));
+  const Ws L = ws_layout(M, out, in);
+  if (!ws || ws_bytes < L.total) return QAT_ERR_WORKSPACE;
+  const size_t ng = out * (in / 64) * 4;
+  Range outs[] = {{dX, (size_t)(M * in * 2)}, {dW, (size_t)(out * in * 4)}, {ds, ng}, {dz, ng},
+                  {ws, L.total}};
+  Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)},
+                 {s, ng}, {z, ng}};
+  QAT_CHECK(check_alias(outs, 5, ins, 5));
+  const int64_t Mp = round_up(M, 64);
+  const float Kq = (float)((1 << bits) - 1);
+
+  if (dX) {
+    uint16_t* wt = (uint16_t*)((char*)ws + L.w_hat);
+    qat::launch_quant_t(W, s, z, out, in, bits, wt, stream);
+    qat::GemmArgs a = gemm_args();
+    a.A = dY;
+    a.lda = out;
+    a.B = wt;
+    a.ldb = out;
+    a.M = (int)M;
+    a.N = (int)in;
+    a.K = (int)out;
+    a.C = dX;
+    a.ldc = in;
+    qat::launch_gemm_bf16_out(a, qat::kBf16, bits, stream);
+  }
+  if (dW || ds) {
+    uint16_t* dyt = (uint16_t*)((char*)ws + L.dy_t);
+    uint16_t* xt = (uint16_t*)((char*)ws + L.x_t);
+    qat::launch_transpose_bf16(dY, M, out, dyt, Mp, stream);
+    qat::launch_transpose_bf16(X, M, in, xt, Mp, stream);
+    qat::GemmArgs a = gemm_args();
+    a.A = dyt;
+    a.lda = Mp;
+    a.B = xt;
+    a.ldb = Mp;
+    a.M = (int)out;
+    a.N = (int)in;
+    a.K = (int)Mp;
+    a.s = s;
+    a.z = z;
+    a.G = in / 64;
+    a.Kq = Kq;
+    a.W = W;
+    a.ldw = in;
+    a.dW = dW;
+    a.ds = ds;
+    a.dz = dz;
+    qat::launch_gemm_ste_grads(a, stream);
+  }
+  return finish();
+}
+
+QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* s,
+                                     const float* z, int64_t M, int64_t out, int64_t in, int32_t group,
+                                     int32_t bits, uint16_t* Y, hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  QAT_CHECK(check_m(M));
+  if (!X || !Wq || !s || !z || !Y) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({X, Wq, s, z, Y}));
+  const size_t ng = out * (in / 64) * 4;
+  Range outs[] = {{Y, (size_t)(M * out * 2)}};
+  Range ins[] = {{X, (size_t)(M * in * 2)}, {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}};
+  QAT_CHECK(check_alias(outs, 1, ins, 4));
+  qat::GemmArgs a = gemm_args();
+  a.A = X;
+  a.lda = in;
+  a.B = Wq;
+  a.ldb = in * bits / 8;
+  a.M = (int)M;
+  a.N = (int)out;
+  a.K = (int)in;
+  a.C = Y;
+  a.ldc = out;
+  a.s = s;
+  a.z = z;
+  a.G = in / 64;
+  a.Kq = (float)((1 << bits) - 1);
+  qat::launch_gemm_bf16_out(a, qat::kPacked, bits, stream);
+  return finish();
+}
+
+QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint8_t* Wq,
+                                       const float* s, const float* z, int64_t M, int64_t out,
+                                       int64_t in, int32_t group, int32_t bits, uint16_t* dX,
+                                       float* ds, float* dz, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  QAT_CHECK(check_m(M));
+  if (!dY || !X || !Wq || !s || !z || !ds) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({dY, X, Wq, s, z, dX, ds, dz, ws}));
+  const Ws L = ws_layout(M, out, in);
+  if (!ws || ws_bytes < L.total) return QAT_ERR_WORKSPACE;
+  const size_t ng = out * (in / 64) * 4;
+  Range outs[] = {{dX, (size_t)(M * in * 2)}, {ds, ng}, {dz, ng}, {ws, L.total}};
+  Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)},
+                 {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}};
+  QAT_CHECK(check_alias(outs, 4, ins, 5));
+  const int64_t Mp = round_up(M, 64);
+
+  if (dX) {
+    uint16_t* wt = (uint16_t*)((char*)ws + L.w_hat);
+    qat::launch_dequant_t(Wq, s, z, out, in, bits, wt, stream);
+    qat::GemmArgs a = gemm_args();
+    a.A = dY;
+    a.lda = out;
+    a.B = wt;
+    a.ldb = out;
+    a.M = (int)M;
+    a.N = (int)in;
+    a.K = (int)out;
+    a.C = dX;
+    a.ldc = in;
+    qat::launch_gemm_bf16_out(a, qat::kBf16, bits, stream);
+  }
+  uint16_t* dyt = (uint16_t*)((char*)ws + L.dy_t);
+  uint16_t* xt = (uint16_t*)((char*)ws + L.x_t);
+  qat::launch_transpose_bf16(dY, M, out, dyt, Mp, stream);
+  qat::launch_transpose_bf16(X, M, in, xt, Mp, stream);
+  qat::GemmArgs a = gemm_args();
+  a.A = dyt;
+  a.lda = Mp;
+  a.B = xt;
+  a.ldb = Mp;
+  a.M = (int)out;
+  a.N = (int)in;
+  a.K = (int)Mp;
+  a.s = s;
+  a.z = z;
+  a.G = in / 64;
+  a.Kq = (float)((1 << bits) - 1);
+  a.Wq = Wq;
+  a.ldq = in * bits / 8;
+  a.ds = ds;
+  a.dz = dz;
+  qat::launch_gemm_e2e_grads(a, bits, stream);
+  return finish();
+}

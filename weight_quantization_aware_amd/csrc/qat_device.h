@@ -1,0 +1,86 @@
+// Device helpers shared by the gfx950 kernels of the group-wise fake-quant linear.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qat {
+
+constexpr int kGroup = 64;           // elements per quantisation group (along `in`)
+constexpr float kSMin = 1e-5f;       // floor for the step size of a constant group
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+}
+
+// DPP lane exchanges inside a row of 16 lanes.
+enum : int {
+  kDppXor1 = 0xB1,          // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,          // quad_perm [2,3,0,1]
+  kDppRowMirror = 0x140,    // lane i <-> 15 - i
+  kDppRowHalfMirror = 0x141 // lane i <-> 7 - i (within each half row)
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum / min / max over the 16 lanes of a DPP row; every lane gets the result.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  return v;
+}
+__device__ __forceinline__ float row16_min(float v) {
+  v = fminf(v, dpp<kDppXor1>(v));
+  v = fminf(v, dpp<kDppXor2>(v));
+  v = fminf(v, dpp<kDppRowHalfMirror>(v));
+  v = fminf(v, dpp<kDppRowMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  return v;
+}
+
+// Quantiser of one element (Eq. 1 and Eq. 2 of the EfficientQAT paper notes):
+//   u = fl32(w / s); v = rint(u) + zr; q = clamp(v, 0, K); m = 0 <= v <= K;
+//   w_hat = fl32((q - zr) * s).
+// zr is the already rounded and clamped zero point. Plain '/' is the IEEE
+// correctly rounded fp32 division (no fast-math anywhere in this library).
+struct QElem {
+  float u, q, w_hat;
+  bool m;
+};
+
+__device__ __forceinline__ QElem quant_elem(float w, float s, float zr, float K) {
+  QElem e;
+  e.u = w / s;
+  float v = __builtin_rintf(e.u) + zr;
+  e.m = (v >= 0.0f) && (v <= K);
+  e.q = fminf(fmaxf(v, 0.0f), K);
+  e.w_hat = (e.q - zr) * s;
+  return e;
+}
+
+__device__ __forceinline__ float round_clamp_zero(float z, float K) {
+  return fminf(fmaxf(__builtin_rintf(z), 0.0f), K);
+}
+
+}  // namespace qat
