@@ -29,6 +29,7 @@ FQ_CASES = [
     (2085, 4096, 256, 2),
     (100, 4160, 4160, 3),
     (4196, 4160, 128, 2),
+    (2000, 3136, 128, 4),
 ]
 E2E_CASES = [
     (128, 256, 256, 2),

@@ -1,0 +1,519 @@
+// The MFMA GEMM kernel template of the group-wise fake-quant linear (gfx950).
+//
+// C[M, N] = sum_k A[m, k] * B[n, k]: both operands K-contiguous, bf16 in LDS,
+// fp32 accumulation in v_mfma_f32_16x16x32_bf16. A 256-thread workgroup
+// (4 wave64s, 2x2) owns a BM x BN tile; K advances in slabs of BK (32 or 64).
+// With BK = 64 a slab is exactly one quantisation group of a weight row, so a
+// fused B loader needs one (s, z) pair per row and slab.
+//
+// The MFMA's first operand is the B fragment and its second the A fragment, so
+// the 16x16 result a lane holds is 4 consecutive output COLUMNS of one row:
+// acc[j][i][r] = C[m0 + wm0 + 16 i + (lane & 15)][n0 + wn0 + 16 j + 4 (lane >> 4) + r].
+// Stores are then 8-byte (bf16) or 16-byte (fp32) vectors, and a 64-column
+// quantisation group is 4 j-tiles x 4 registers of one lane plus a reduction
+// over the 4 lanes that share (lane & 15).
+//
+// LDS: per operand and stage a [rows][BK] bf16 slab; 16-byte chunk c of row r
+// sits at chunk position c ^ ((r / RPL) & (CH - 1)), which spreads the 16
+// rows that one fragment read touches over distinct bank slots. Two stages:
+// global loads for slab k+1 are issued at the top of slab k, fragments for the
+// next k-step are read while the current k-step's MFMAs run, and the next
+// slab is written to LDS during the last k-step.
+#pragma once
+#include "qat_device.h"
+#include "qat_internal.h"
+
+namespace qat {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t nbytes) {
+  if (nbytes < 0) nbytes = 0;
+  if (nbytes > 0x7FFFFFF0) nbytes = 0x7FFFFFF0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+
+// 16-byte load; offsets at or beyond the resource size read as zero.
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// Workgroup id -> output tile. Consecutive workgroup ids go round-robin to the
+// 8 XCDs; each XCD gets a contiguous range of tiles, walked in groups of 8
+// tile-rows so that neighbouring workgroups share operand tiles in its L2.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int per = T / 8, rem = T % 8;
+  const int xcd = b & 7, idx = b >> 3;
+  const int p = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  constexpr int GM = 8;
+  const int gsize = GM * tiles_n;
+  const int gid = p / gsize;
+  const int first = gid * GM;
+  const int gm = min(tiles_m - first, GM);
+  const int in_g = p - gid * gsize;
+  tm = first + in_g % gm;
+  tn = in_g / gm;
+}
+
+// LDS bank slots (16-byte chunks) served per cycle; the swizzle period. Eight
+// measures free of bank conflicts for these fragment reads on gfx950.
+constexpr int kLdsSlots = 8;
+
+template <int BK, int SLOTS>
+struct LdsLayout {
+  static constexpr int CH = BK / 8;                      // 16-byte chunks per row
+  static constexpr int PITCH = BK * 2;                   // bytes per row
+  static constexpr int RPL = SLOTS / CH > 0 ? SLOTS / CH : 1;
+  __device__ static __forceinline__ int off(int row, int chunk) {
+    return row * PITCH + ((chunk ^ ((row / RPL) & (CH - 1))) << 4);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS operand tiles (bf16, K-contiguous rows).
+// buffer_load_dwordx4 ... lds writes 64 lanes x 16 B = 1 KiB of LDS starting at
+// M0; lane l lands at byte 16 l, i.e. row l / CH, chunk position l % CH of the
+// instruction's rows, so lane l fetches the logical chunk that the swizzle maps
+// to that position. The loads are issued from inline asm because the
+// compiler's own LDS-DMA tracking waits for every outstanding DMA before any
+// LDS read, which would collapse the multi-stage pipeline; the kernel waits on
+// vmcnt itself. Rows at or beyond nrows read as zero (buffer range check).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int64_t nbytes) {
+  if (nbytes < 0) nbytes = 0;
+  if (nbytes > 0x7FFFFFF0) nbytes = 0x7FFFFFF0;
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xFFFF));
+  r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+template <int ROWS, int BK, int SLOTS>
+struct DmaTile {
+  using L = LdsLayout<BK, SLOTS>;
+  static constexpr int RPI = 1024 / L::PITCH;            // rows per DMA instruction
+  static constexpr int NI = ROWS / RPI / 4;              // instructions per wave per slab
+  static_assert(NI * RPI * 4 == ROWS, "tile rows must split over 4 waves");
+  i32x4 rs;
+  uint32_t voff[NI];
+  uint32_t lrow[NI];                                     // wave-uniform LDS byte offsets
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows) {
+    rs = buffer_rsrc(src + (int64_t)row0 * ld, (int64_t)(nrows - row0) * ld * 2);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int r0 = (wave * NI + q) * RPI;
+      const int row = r0 + lane / L::CH;
+      const int pos = lane % L::CH;
+      const int chunk = pos ^ ((row / L::RPL) & (L::CH - 1));
+      voff[q] = (uint32_t)(row * ld * 2 + chunk * 16);
+      lrow[q] = (uint32_t)(r0 * L::PITCH);
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t lds_tile, int k0) const {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * 2);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Register-path B loaders: issue() reads one slab from HBM into registers,
+// commit() converts it to bf16 and writes it into an LDS stage.
+// Thread t covers chunk t % CH of rows t / CH + (256 / CH) p.
+// ---------------------------------------------------------------------------
+
+// fp32 master weight -> quantise (Eq. 1) -> dequantise (Eq. 2) -> bf16 in LDS.
+// u = w * fl32(1/s) lies within 3 ulp of fl32(w/s); where that interval could
+// hold a half-integer the element is redone with the correctly rounded
+// division, so codes equal the exact fp32 quantiser's. Needs BK = 64 (one group).
+template <int ROWS, int BK, int SLOTS>
+struct LoadFp32Quant {
+  using L = LdsLayout<BK, SLOTS>;
+  static constexpr int RP = 256 / L::CH, P = ROWS / RP;
+  static_assert(BK == 64, "a slab must be one quantisation group");
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t base, ld_rows;
+  const float* s;
+  const float* z;
+  int64_t G;
+  int row0, nrows;
+  float K;
+  uint4 r[P][2];
+  float sv[P], zv[P];
+  __device__ __forceinline__ void init(const float* W, int64_t ld, int row0_, int nrows_, const float* s_,
+                                       const float* z_, int64_t G_, float K_) {
+    row0 = row0_;
+    nrows = nrows_;
+    rs = make_rsrc(W + (int64_t)row0 * ld, (int64_t)(nrows - row0) * ld * 4);
+    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
+    base = (uint32_t)(rr * ld * 4 + c * 32);
+    ld_rows = (uint32_t)(RP * ld * 4);
+    s = s_;
+    z = z_;
+    G = G_;
+    K = K_;
+  }
+  __device__ __forceinline__ void issue(int k0) {
+    const int rr = threadIdx.x / L::CH;
+    const int kt = k0 / 64;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      r[p][0] = bload16(rs, base + p * ld_rows + k0 * 4);
+      r[p][1] = bload16(rs, base + p * ld_rows + k0 * 4 + 16);
+      const int row = min(row0 + rr + RP * p, nrows - 1);
+      sv[p] = s[(int64_t)row * G + kt];
+      zv[p] = z[(int64_t)row * G + kt];
+    }
+  }
+  __device__ __forceinline__ void commit(uint8_t* lds) const {
+    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float s_ = sv[p];
+      const float z_ = round_clamp_zero(zv[p], K);
+      const float rcp = 1.0f / s_;
+      const uint32_t wb[8] = {r[p][0].x, r[p][0].y, r[p][0].z, r[p][0].w,
+                              r[p][1].x, r[p][1].y, r[p][1].z, r[p][1].w};
+      float h[8];
+      bool near_tie = false;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = __builtin_bit_cast(float, wb[k]);
+        const float u = w * rcp;
+        const float fr = u - floorf(u);
+        near_tie |= fabsf(fr - 0.5f) <= fabsf(u) * 0x1p-20f + 0x1p-60f;
+        const float q = fminf(fmaxf(__builtin_rintf(u) + z_, 0.0f), K);
+        h[k] = (q - z_) * s_;
+      }
+      if (near_tie) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[k] = quant_elem(__builtin_bit_cast(float, wb[k]), s_, z_, K).w_hat;
+      }
+      const bool ok = row0 + rr + RP * p < nrows;
+      uint4 o = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                           pack_bf16x2(h[6], h[7]));
+      if (!ok) o = make_uint4(0, 0, 0, 0);
+      *(uint4*)(lds + L::off(rr + RP * p, c)) = o;
+    }
+  }
+};
+
+// Packed N-bit codes -> (q - z) * s -> bf16 in LDS (E2E-QP; z as stored). BK = 64.
+template <int ROWS, int BK, int SLOTS, int NB>
+struct LoadPacked {
+  using L = LdsLayout<BK, SLOTS>;
+  static constexpr int RP = 256 / L::CH, P = ROWS / RP;
+  static_assert(BK == 64, "a slab must be one quantisation group");
+  const uint8_t* q;
+  int64_t ldq;
+  const float* s;
+  const float* z;
+  int64_t G;
+  int row0, nrows;
+  uint32_t word[P];
+  float sv[P], zv[P];
+  __device__ __forceinline__ void init(const uint8_t* Wq, int64_t ldq_, int row0_, int nrows_, const float* s_,
+                                       const float* z_, int64_t G_) {
+    q = Wq;
+    ldq = ldq_;
+    row0 = row0_;
+    nrows = nrows_;
+    s = s_;
+    z = z_;
+    G = G_;
+  }
+  __device__ __forceinline__ void issue(int k0) {
+    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
+    const int kt = k0 / 64;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int row = min(row0 + rr + RP * p, nrows - 1);
+      const uint8_t* src = q + (int64_t)row * ldq + (int64_t)kt * 8 * NB + c * NB;
+      if constexpr (NB == 2) word[p] = *(const uint16_t*)src;
+      else if constexpr (NB == 4) word[p] = *(const uint32_t*)src;
+      else word[p] = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16);
+      sv[p] = s[(int64_t)row * G + kt];
+      zv[p] = z[(int64_t)row * G + kt];
+    }
+  }
+  __device__ __forceinline__ void commit(uint8_t* lds) const {
+    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float h[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float qv = (float)((word[p] >> (NB * k)) & ((1u << NB) - 1));
+        h[k] = (qv - zv[p]) * sv[p];
+      }
+      uint4 o = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                           pack_bf16x2(h[6], h[7]));
+      if (row0 + rr + RP * p >= nrows) o = make_uint4(0, 0, 0, 0);
+      *(uint4*)(lds + L::off(rr + RP * p, c)) = o;
+    }
+  }
+};
+
+template <int ROWS, int BK, int SLOTS, int BL, int NB>
+struct BLoaderOf;
+template <int ROWS, int BK, int SLOTS, int NB>
+struct BLoaderOf<ROWS, BK, SLOTS, kBf16, NB> { using T = DmaTile<ROWS, BK, SLOTS>; };
+template <int ROWS, int BK, int SLOTS, int NB>
+struct BLoaderOf<ROWS, BK, SLOTS, kFp32Quant, NB> { using T = LoadFp32Quant<ROWS, BK, SLOTS>; };
+template <int ROWS, int BK, int SLOTS, int NB>
+struct BLoaderOf<ROWS, BK, SLOTS, kPacked, NB> { using T = LoadPacked<ROWS, BK, SLOTS, NB>; };
+
+template <int BL, class Ld>
+__device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
+  if constexpr (BL == kBf16) l.init((const uint16_t*)a.B, a.ldb, n0, a.N);
+  else if constexpr (BL == kFp32Quant) l.init((const float*)a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.Kq);
+  else l.init((const uint8_t*)a.B, a.ldb, n0, a.N, a.s, a.z, a.G);
+}
+
+// Four consecutive codes c0..c0+3 (c0 % 4 == 0) of a packed row.
+template <int NB>
+__device__ __forceinline__ uint32_t codes4(const uint8_t* __restrict__ row, int64_t c0) {
+  const int64_t bit = c0 * NB;
+  if constexpr (NB == 2) return row[bit >> 3];
+  else if constexpr (NB == 4) return *(const uint16_t*)(row + (bit >> 3));
+  else {
+    const uint32_t lo = row[bit >> 3], hi = row[(bit >> 3) + 1];
+    return ((lo | (hi << 8)) >> (bit & 7)) & 0xFFFu;
+  }
+}
+
+template <int TI, int TJ>
+struct Frags {
+  bf16x8 a[TI], b[TJ];
+};
+
+// ---------------------------------------------------------------------------
+// The kernel. STAGES LDS stages (>= 3). With one k-step per slab (BK = 32)
+// U2 = 1 unrolls slabs in pairs so the two fragment sets alternate; U2 = 0
+// copies the next slab's fragments instead (fewer live registers).
+// Invariant at the top of slab kt: slabs
+// <= kt are visible to every wave and F[0] holds the first k-step's fragments
+// of slab kt. The barrier in slab kt certifies slab kt + 1, so the fragments of
+// the next slab are read while the current slab's MFMAs run, and the DMA for
+// slab kt + STAGES - 1 goes into the stage slab kt - 1 has just released.
+// The last slabs re-issue the final slab into idle stages so that the vmcnt
+// bookkeeping is the same on every iteration; nothing reads those copies.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int STAGES, int U2, int BL, int EP, int NB>
+__global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
+  constexpr int SLOTS = kLdsSlots;
+  using L = LdsLayout<BK, SLOTS>;
+  static_assert(STAGES >= 3, "the shifted pipeline needs three stages");
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int KS = BK / 32;                              // k-steps per slab
+  constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t lds0 = lds_addr_of(smem);
+
+  DmaTile<BM, BK, SLOTS> la;
+  typename BLoaderOf<BN, BK, SLOTS, BL, NB>::T lb;
+  la.init(a.A, a.lda, m0, a.M);
+  init_b<BL>(lb, a, n0);
+  constexpr bool B_DMA = (BL == kBf16);
+  constexpr int NL = DmaTile<BM, BK, SLOTS>::NI + (B_DMA ? DmaTile<BN, BK, SLOTS>::NI : 0);
+
+  const int nk = a.K / BK;
+  auto issue = [&](int slab) {               // DMA part of one slab
+    const int sl = slab < nk ? slab : nk - 1;
+    const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
+    la.issue(st, sl * BK);
+    if constexpr (B_DMA) lb.issue(st + A_BYTES, sl * BK);
+  };
+  auto b_reg_issue = [&](int slab) {
+    if constexpr (!B_DMA) lb.issue((slab < nk ? slab : nk - 1) * BK);
+  };
+  auto b_reg_commit = [&](int slab) {
+    if constexpr (!B_DMA) lb.commit(&smem[(slab % STAGES) * STAGE + A_BYTES]);
+  };
+
+  // Fragment reads index the __shared__ array directly (stage given as a byte
+  // offset) so that they stay ds_read instructions.
+  auto read_frags = [&](int st, int ks, Frags<TI, TJ>& f) {
+    const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) f.a[i] = *(const bf16x8*)&smem[st + L::off(wm0 + i * 16 + (lane & 15), chunk)];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      f.b[j] = *(const bf16x8*)&smem[st + A_BYTES + L::off(wn0 + j * 16 + (lane & 15), chunk)];
+  };
+
+  f32x4 acc[TJ][TI];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfmas = [&](const Frags<TI, TJ>& f) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+  };
+
+  // prologue: slabs 0 .. STAGES-2 in flight, slab 0 certified, F[0] loaded.
+  if constexpr (!B_DMA) {
+    b_reg_issue(0);
+    b_reg_commit(0);
+    b_reg_issue(1);
+    b_reg_commit(1);
+  }
+#pragma unroll
+  for (int sl = 0; sl < STAGES - 1; ++sl) issue(sl);
+  wait_vmcnt<(STAGES - 2) * NL>();
+  __syncthreads();
+  Frags<TI, TJ> F[2];
+  read_frags(0, 0, F[0]);
+
+  // One slab: CUR holds its first k-step's fragments on entry, and the next
+  // slab's first fragments are in CUR (two k-steps) or NXT (one k-step) on exit.
+#define QAT_SLAB(KT, CUR, NXT)                                              \
+  do {                                                                      \
+    wait_vmcnt<(STAGES - 3) * NL>(); /* my DMAs for slabs <= KT+1 landed */ \
+    __syncthreads();                 /* everyone's: slab KT+1 is visible */ \
+    issue((KT) + STAGES - 1);                                               \
+    b_reg_issue((KT) + 2);                                                  \
+    const int st_ = ((KT) % STAGES) * STAGE;                                \
+    const int nx_ = (((KT) + 1) % STAGES) * STAGE;                          \
+    if constexpr (KS == 1) {                                                \
+      read_frags(nx_, 0, NXT);                                              \
+      mfmas(CUR);                                                           \
+    } else {                                                                \
+      read_frags(st_, 1, NXT);                                              \
+      mfmas(CUR);                                                           \
+      read_frags(nx_, 0, CUR);                                              \
+      mfmas(NXT);                                                           \
+    }                                                                       \
+    b_reg_commit((KT) + 2);                                                 \
+  } while (0)
+
+  for (int kt = 0; kt < nk; kt += (KS == 1 && U2) ? 2 : 1) {
+    QAT_SLAB(kt, F[0], F[1]);
+    if constexpr (KS == 1) {
+      if constexpr (U2) {
+        if (kt + 1 < nk) QAT_SLAB(kt + 1, F[1], F[0]);
+      } else {
+        F[0] = F[1];
+      }
+    }
+  }
+#undef QAT_SLAB
+  wait_vmcnt<0>();                            // drain the trailing re-issued DMAs
+
+  // ------------------------------------------------------------------ epilogues
+  const int rl = lane & 15, cq = 4 * (lane >> 4);
+  if constexpr (EP == kStoreBf16) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = m0 + wm0 + i * 16 + rl;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn0 + j * 16 + cq;
+        if (col < a.N)
+          *(uint2*)(a.C + (int64_t)row * a.ldc + col) =
+              make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]), pack_bf16x2(acc[j][i][2], acc[j][i][3]));
+      }
+    }
+  } else {
+    // Rows are weight rows o (A = dY^T), columns are inputs c (B = X^T).
+    constexpr int NG = WN / 64;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int o = m0 + wm0 + i * 16 + rl;
+      const bool row_ok = o < a.M;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int cg = n0 + wn0 + g * 64;
+        const bool ok = row_ok && cg < a.N;
+        const int64_t gi = (int64_t)(row_ok ? o : 0) * a.G + cg / 64;
+        float ps = 0.f, pz = 0.f, sv = 0.f;
+        if (ok) {
+          sv = a.s[gi];
+          if constexpr (EP == kSteGrads) {
+            const float zr = round_clamp_zero(a.z[gi], a.Kq);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int col = cg + jj * 16 + cq;
+              const f32x4 gw = acc[g * 4 + jj][i];
+              const float4 w = *(const float4*)(a.W + (int64_t)o * a.ldw + col);
+              const float wv[4] = {w.x, w.y, w.z, w.w};
+              float dw[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const QElem e = quant_elem(wv[r], sv, zr, a.Kq);
+                dw[r] = e.m ? gw[r] : 0.0f;
+                ps += gw[r] * (e.m ? (__builtin_rintf(e.u) - e.u) : (e.q - zr));
+                pz += e.m ? 0.0f : gw[r];
+              }
+              if (a.dW) *(float4*)(a.dW + (int64_t)o * a.ldw + col) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+            }
+          } else {
+            const float zv = a.z[gi];
+            const uint8_t* qrow = a.Wq + (int64_t)o * a.ldq;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int col = cg + jj * 16 + cq;
+              const f32x4 gw = acc[g * 4 + jj][i];
+              const uint32_t c4 = codes4<NB>(qrow, col);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float qv = (float)((c4 >> (NB * r)) & ((1u << NB) - 1));
+                ps += gw[r] * (qv - zv);
+                pz += gw[r];
+              }
+            }
+          }
+        }
+        // the 4 lanes with the same (lane & 15) hold the 4 column quarters of the group
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        pz += __shfl_xor(pz, 16);
+        pz += __shfl_xor(pz, 32);
+        if (ok && lane < 16 && a.ds) {
+          a.ds[gi] = ps;
+          if (a.dz) a.dz[gi] = -sv * pz;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace qat
