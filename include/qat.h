@@ -23,7 +23,10 @@
  *   consecutive elements of a row along `in`; G = in / 64 groups per row.
  *   s, z, ds, dz are [out, G] fp32 row-major. X is [M, in], Y and dY are
  *   [M, out], dX is [M, in]; all bf16 passed as uint16_t bit patterns.
- * - bits N in {2, 3, 4}; K = 2^N - 1.
+ * - bits N in {2, 3, 4}; K = 2^N - 1. in is a multiple of 64. The four GEMM calls
+ *   (fake-quant fwd/bwd, dequant-GEMM fwd/bwd) also need out % 64 == 0, so the
+ *   backward GEMM that contracts over out works in whole 64-wide slabs; M is any
+ *   positive count of tokens. Every operand must be smaller than 2 GiB.
  * - All tensor pointers are DEVICE pointers owned by the caller. The library
  *   never allocates, frees or keeps them beyond the enqueued work.
  * - Inputs are const and never written. Outputs are fully overwritten (never
@@ -53,7 +56,8 @@ extern "C" {
 enum {
   QAT_OK = 0,
   QAT_ERR_NULL = 1,      /* a required pointer is NULL                                   */
-  QAT_ERR_SHAPE = 2,     /* a dimension <= 0, in % group != 0, or a size overflows         */
+  QAT_ERR_SHAPE = 2,     /* a dimension <= 0, in (or, for the GEMM calls, out) not a
+                            multiple of 64, or an operand of 2 GiB or more                  */
   QAT_ERR_BITS = 3,      /* bits not in {2, 3, 4}                                          */
   QAT_ERR_GROUP = 4,     /* group != 64                                                    */
   QAT_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                               */
@@ -87,7 +91,8 @@ int32_t qat_quant_codes(const float* W, const float* s, const float* z, int64_t 
                         int32_t group, int32_t bits, uint8_t* codes, uint16_t* W_hat,
                         hipStream_t stream);
 
-/* Workspace bytes that qat_fakequant_linear_fwd / _bwd need for these sizes. */
+/* Workspace bytes that qat_fakequant_linear_fwd / _bwd need for these sizes: one bf16 W_hat
+ * [out, in] (rounded up to 256 bytes). M does not change it. */
 size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in);
 
 /*
@@ -96,8 +101,10 @@ size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in);
  * straight-through, as the "Paper vs. code" section of the modelfoundations.com
  * note describes). X [M, in] bf16, Y [M, out] bf16; fp32 accumulation.
  * ws: NULL selects the fused kernel that quantises fp32 W tiles directly into
- * LDS; otherwise >= qat_fakequant_ws_bytes(M, out, in) bytes of device memory
- * used as scratch for a bf16 W_hat staged once per call.
+ * LDS (no workspace; the quantiser runs once per 256-token tile, VALU-bound);
+ * otherwise >= qat_fakequant_ws_bytes(M, out, in) bytes of device memory that
+ * receive a bf16 W_hat staged once per call and read by the GEMM. The
+ * workspace is scratch: its contents after the call are unspecified.
  */
 int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float* s, const float* z,
                                  int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
@@ -112,7 +119,10 @@ int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float*
  *   ds[o,j] = sum_{i in j} Gw[o,i] * (m_i ? rint(u_i) - u_i : q_i - zr)
  *   dz[o,j] = -s[o,j] * sum_{i in j, m_i = 0} Gw[o,i]  [out, G] fp32
  * Any of dX, dW, ds, dz may be NULL to skip it (ds and dz come together: both
- * NULL or both set). ws is required: >= qat_fakequant_ws_bytes(M, out, in).
+ * NULL or both set). When dX is wanted, ws (>= qat_fakequant_ws_bytes(M, out,
+ * in) bytes, scratch) receives the bf16 W_hat; otherwise ws may be NULL. dY and
+ * X are read in place (the dW GEMM contracts over tokens reading both with
+ * LDS transpose loads), so no transposed copies are made.
  */
 int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
                                  const float* s, const float* z, int64_t M, int64_t out, int64_t in,
@@ -129,7 +139,7 @@ int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const fl
 int32_t qat_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in,
                  int32_t group, int32_t bits, uint8_t* Wq, float* z_round, hipStream_t stream);
 
-/* Workspace bytes that qat_dequant_gemm_bwd_s needs for these sizes. */
+/* Workspace bytes that qat_dequant_gemm_bwd_s needs: one bf16 W_hat [out, in]. */
 size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in);
 
 /*
@@ -148,7 +158,8 @@ int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* 
  *   ds[o,j] = sum_{i in j} Gw[o,i] * (q_i - z[o,j]),  Gw = dY^T X (never stored);
  *   dz[o,j] = -s[o,j] * sum_{i in j} Gw[o,i]  (the train-s-and-z variant of the
  *   Paper-Notes ablation table; may be NULL).
- * ws is required: >= qat_dequant_ws_bytes(M, out, in).
+ * When dX is wanted, ws (>= qat_dequant_ws_bytes(M, out, in) bytes, scratch)
+ * receives the dequantised bf16 W_hat; otherwise ws may be NULL.
  */
 int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint8_t* Wq,
                                const float* s, const float* z, int64_t M, int64_t out, int64_t in,

@@ -40,9 +40,10 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    # [W_hat (out*in*2) | dY^T (out*Mp*2) | X^T (in*Mp*2)], Mp = M rounded up to 64
-    assert Q.fakequant_ws_bytes(2048, 4096, 4096) == 4096 * 4096 * 2 + 2 * 4096 * 2048 * 2
-    assert Q.fakequant_ws_bytes(1, 64, 64) == 64 * 64 * 2 + 2 * 64 * 64 * 2
+    # one bf16 W_hat [out, in], rounded up to 256 bytes
+    assert Q.fakequant_ws_bytes(2048, 4096, 4096) == 4096 * 4096 * 2
+    assert Q.fakequant_ws_bytes(1, 64, 64) == 64 * 64 * 2
+    assert Q.fakequant_ws_bytes(7, 64, 64) == Q.fakequant_ws_bytes(4096, 64, 64)
     assert Q.fakequant_ws_bytes(0, 64, 64) == 0
     assert Q.dequant_ws_bytes(100, 192, 128) == Q.fakequant_ws_bytes(100, 192, 128)
 
@@ -71,9 +72,11 @@ def test_fwd_bwd_validation():
     assert L.qat_fakequant_linear_fwd(A, B, C, D, 8, 64, 128, 64, 2, E, FAKE * 7, 16, None) == 6
     # fwd: M <= 0
     assert L.qat_fakequant_linear_fwd(A, B, C, D, 0, 64, 128, 64, 2, E, None, 0, None) == 2
-    # bwd: workspace is required
+    # bwd: a workspace is required when dX is wanted
     assert L.qat_fakequant_linear_bwd(A, B, C, D, E, 8, 64, 128, 64, 2, FAKE * 6, None, None, None,
                                       None, 0, None) == 6
+    # out must be a multiple of 64
+    assert L.qat_fakequant_linear_fwd(A, B, C, D, 8, 96, 128, 64, 2, E, None, 0, None) == 2
     # bwd: ds without dz
     assert L.qat_fakequant_linear_bwd(A, B, C, D, E, 8, 64, 128, 64, 2, None, None, FAKE * 6, None,
                                       FAKE * 7, 1 << 30, None) == 1

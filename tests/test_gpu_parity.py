@@ -285,8 +285,9 @@ def test_errors_leave_outputs_untouched():
     X = torch.zeros(8, 128, dtype=torch.bfloat16, device="cuda")
     Y = torch.full((8, 64), 1.5, dtype=torch.bfloat16, device="cuda")
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
-    with pytest.raises(Q.QatError) as e:
-        Q.qat_fakequant_linear_bwd(Y, X, W, s, z, 2, dW=W.clone(), ws=small)
+    gX = torch.empty(8, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(Q.QatError) as e:                          # dX needs the W_hat workspace
+        Q.qat_fakequant_linear_bwd(Y, X, W, s, z, 2, dX=gX, ws=small)
     assert e.value.status == 6
     with pytest.raises(Q.QatError) as e:                          # output aliases input
         Q.qat_quant_codes(W, s, z, 2, W_hat=W.view(torch.bfloat16))

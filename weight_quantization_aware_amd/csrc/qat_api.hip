@@ -14,7 +14,7 @@ namespace {
 thread_local char g_last_error[512] = "";
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;      // GEMM indices are 32-bit
-constexpr int64_t kMaxGridY = 65535;               // y-dimension of the 64x64 tile grids
+constexpr int64_t kMaxBytes = 0x7FFFFFF0;          // kernels address each operand with 32-bit offsets
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 size_t region(int64_t bytes) { return (size_t)round_up(bytes, 256); }
@@ -43,18 +43,19 @@ int32_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
   return QAT_OK;
 }
 
-int32_t check_common(int64_t out, int64_t in, int32_t group, int32_t bits) {
+// Elementwise calls accept any row count; the GEMM calls (gemm = true) also need
+// out % 64 == 0 because the backward dX GEMM contracts over out in 64-wide slabs.
+int32_t check_common(int64_t out, int64_t in, int32_t group, int32_t bits, bool gemm = false) {
   if (group != 64) return QAT_ERR_GROUP;
   if (bits < 2 || bits > 4) return QAT_ERR_BITS;
-  if (out <= 0 || in <= 0 || in % 64 != 0) return QAT_ERR_SHAPE;
-  if (out > kMaxDim || in > kMaxDim || out * in > (int64_t(1) << 40)) return QAT_ERR_SHAPE;
-  if (out / 64 + 1 > kMaxGridY) return QAT_ERR_SHAPE;
+  if (out <= 0 || in <= 0 || in % 64 != 0 || (gemm && out % 64 != 0)) return QAT_ERR_SHAPE;
+  if (out > kMaxDim || in > kMaxDim || out * in * 4 > kMaxBytes) return QAT_ERR_SHAPE;
   return QAT_OK;
 }
 
-int32_t check_m(int64_t M) {
+int32_t check_m(int64_t M, int64_t out, int64_t in) {
   if (M <= 0 || M > kMaxDim) return QAT_ERR_SHAPE;
-  if (round_up(M, 64) / 64 > kMaxGridY) return QAT_ERR_SHAPE;
+  if (M * out * 2 > kMaxBytes || M * in * 2 > kMaxBytes) return QAT_ERR_SHAPE;
   return QAT_OK;
 }
 
@@ -79,20 +80,8 @@ int32_t finish() {
     if (_st != QAT_OK) return _st; \
   } while (0)
 
-struct Ws {
-  size_t w_hat, x_t, dy_t, total;  // offsets of the regions and the total size
-};
-
-// One layout serves forward and backward: [W_hat or W_hat^T | dY^T | X^T].
-Ws ws_layout(int64_t M, int64_t out, int64_t in) {
-  const int64_t Mp = round_up(M, 64);
-  Ws w;
-  w.w_hat = 0;
-  w.dy_t = region(out * in * 2);
-  w.x_t = w.dy_t + region(out * Mp * 2);
-  w.total = w.x_t + region(in * Mp * 2);
-  return w;
-}
+// Workspace: the bf16 W_hat [out][in] that the forward and backward GEMMs read.
+size_t ws_bytes_for(int64_t out, int64_t in) { return region(out * in * 2); }
 
 qat::GemmArgs gemm_args() {
   qat::GemmArgs a;
@@ -106,7 +95,7 @@ QAT_API const char* qat_status_string(int32_t st) {
   switch (st) {
     case QAT_OK: return "ok";
     case QAT_ERR_NULL: return "a required pointer is NULL";
-    case QAT_ERR_SHAPE: return "invalid shape (dimension <= 0, in % 64 != 0, or too large)";
+    case QAT_ERR_SHAPE: return "invalid shape (dimension <= 0, in or out not a multiple of 64, or an operand of 2 GiB or more)";
     case QAT_ERR_BITS: return "bits must be 2, 3 or 4";
     case QAT_ERR_GROUP: return "group must be 64";
     case QAT_ERR_ALIGN: return "a pointer is not 16-byte aligned";
@@ -121,7 +110,7 @@ QAT_API const char* qat_last_error(void) { return g_last_error; }
 
 QAT_API size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in) {
   if (M <= 0 || out <= 0 || in <= 0) return 0;
-  return ws_layout(M, out, in).total;
+  return ws_bytes_for(out, in);
 }
 
 QAT_API size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in) {
@@ -172,14 +161,14 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
                                          const float* z, int64_t M, int64_t out, int64_t in,
                                          int32_t group, int32_t bits, uint16_t* Y, void* ws,
                                          size_t ws_bytes, hipStream_t stream) {
-  QAT_CHECK(check_common(out, in, group, bits));
-  QAT_CHECK(check_m(M));
+  QAT_CHECK(check_common(out, in, group, bits, true));
+  QAT_CHECK(check_m(M, out, in));
   if (!X || !W || !s || !z || !Y) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({X, W, s, z, Y, ws}));
-  const Ws L = ws_layout(M, out, in);
-  if (ws && ws_bytes < L.total) return QAT_ERR_WORKSPACE;
+  const size_t need = ws_bytes_for(out, in);
+  if (ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
   const size_t ng = out * (in / 64) * 4;
-  Range outs[] = {{Y, (size_t)(M * out * 2)}, {ws, ws ? L.total : 0}};
+  Range outs[] = {{Y, (size_t)(M * out * 2)}, {ws, ws ? need : 0}};
   Range ins[] = {{X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)}, {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 2, ins, 4));
 
@@ -195,18 +184,51 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
   a.z = z;
   a.G = in / 64;
   a.Kq = (float)((1 << bits) - 1);
+  a.ldb = in;
   if (ws) {
-    uint16_t* w_hat = (uint16_t*)((char*)ws + L.w_hat);
+    uint16_t* w_hat = (uint16_t*)ws;
     qat::launch_quant_codes(W, s, z, out, in, bits, nullptr, w_hat, stream);
     a.B = w_hat;
-    a.ldb = in;
-    qat::launch_gemm_bf16_out(a, qat::kBf16, bits, stream);
+    qat::launch_gemm_fwd(a, qat::kBf16, bits, stream);
   } else {
     a.B = W;
-    a.ldb = in;
-    qat::launch_gemm_bf16_out(a, qat::kFp32Quant, bits, stream);
+    qat::launch_gemm_fwd(a, qat::kFp32Quant, bits, stream);
   }
   return finish();
+}
+
+// dX = dY W_hat with W_hat [out][in] bf16 read in place.
+static void launch_dx(const uint16_t* dY, const uint16_t* w_hat, int64_t M, int64_t out, int64_t in,
+                      uint16_t* dX, hipStream_t stream) {
+  qat::GemmArgs a = gemm_args();
+  a.A = dY;
+  a.lda = out;
+  a.B = w_hat;
+  a.ldb = in;
+  a.M = (int)M;
+  a.N = (int)in;
+  a.K = (int)out;
+  a.C = dX;
+  a.ldc = in;
+  qat::launch_gemm_dx(a, stream);
+}
+
+// Gw = dY^T X over the M tokens, both read in place, reduced by the epilogue.
+static qat::GemmArgs grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z,
+                                int64_t M, int64_t out, int64_t in, int bits) {
+  qat::GemmArgs a = gemm_args();
+  a.A = dY;
+  a.lda = out;
+  a.B = X;
+  a.ldb = in;
+  a.M = (int)out;
+  a.N = (int)in;
+  a.K = (int)M;
+  a.s = s;
+  a.z = z;
+  a.G = in / 64;
+  a.Kq = (float)((1 << bits) - 1);
+  return a;
 }
 
 QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
@@ -214,60 +236,33 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
                                          int64_t in, int32_t group, int32_t bits, uint16_t* dX,
                                          float* dW, float* ds, float* dz, void* ws, size_t ws_bytes,
                                          hipStream_t stream) {
-  QAT_CHECK(check_common(out, in, group, bits));
-  QAT_CHECK(check_m(M));
+  QAT_CHECK(check_common(out, in, group, bits, true));
+  QAT_CHECK(check_m(M, out, in));
   if (!dY || !X || !W || !s || !z) return QAT_ERR_NULL;
   if ((ds == nullptr) != (dz == nullptr)) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({dY, X, W, s, z, dX, dW, ds, dz, ws}));
-  const Ws L = ws_layout(M, out, in);
-  if (!ws || ws_bytes < L.total) return QAT_ERR_WORKSPACE;
+  const size_t need = ws_bytes_for(out, in);
+  if (dX && (!ws || ws_bytes < need)) return QAT_ERR_WORKSPACE;
   const size_t ng = out * (in / 64) * 4;
   Range outs[] = {{dX, (size_t)(M * in * 2)}, {dW, (size_t)(out * in * 4)}, {ds, ng}, {dz, ng},
-                  {ws, L.total}};
+                  {dX ? ws : nullptr, need}};
   Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)},
                  {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 5, ins, 5));
-  const int64_t Mp = round_up(M, 64);
-  const float Kq = (float)((1 << bits) - 1);
 
   if (dX) {
-    uint16_t* wt = (uint16_t*)((char*)ws + L.w_hat);
-    qat::launch_quant_t(W, s, z, out, in, bits, wt, stream);
-    qat::GemmArgs a = gemm_args();
-    a.A = dY;
-    a.lda = out;
-    a.B = wt;
-    a.ldb = out;
-    a.M = (int)M;
-    a.N = (int)in;
-    a.K = (int)out;
-    a.C = dX;
-    a.ldc = in;
-    qat::launch_gemm_bf16_out(a, qat::kBf16, bits, stream);
+    uint16_t* w_hat = (uint16_t*)ws;
+    qat::launch_quant_codes(W, s, z, out, in, bits, nullptr, w_hat, stream);
+    launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
   if (dW || ds) {
-    uint16_t* dyt = (uint16_t*)((char*)ws + L.dy_t);
-    uint16_t* xt = (uint16_t*)((char*)ws + L.x_t);
-    qat::launch_transpose_bf16(dY, M, out, dyt, Mp, stream);
-    qat::launch_transpose_bf16(X, M, in, xt, Mp, stream);
-    qat::GemmArgs a = gemm_args();
-    a.A = dyt;
-    a.lda = Mp;
-    a.B = xt;
-    a.ldb = Mp;
-    a.M = (int)out;
-    a.N = (int)in;
-    a.K = (int)Mp;
-    a.s = s;
-    a.z = z;
-    a.G = in / 64;
-    a.Kq = Kq;
+    qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, bits);
     a.W = W;
     a.ldw = in;
     a.dW = dW;
     a.ds = ds;
     a.dz = dz;
-    qat::launch_gemm_ste_grads(a, stream);
+    qat::launch_gemm_grads(a, qat::kSteGrads, bits, stream);
   }
   return finish();
 }
@@ -275,8 +270,8 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
 QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* s,
                                      const float* z, int64_t M, int64_t out, int64_t in, int32_t group,
                                      int32_t bits, uint16_t* Y, hipStream_t stream) {
-  QAT_CHECK(check_common(out, in, group, bits));
-  QAT_CHECK(check_m(M));
+  QAT_CHECK(check_common(out, in, group, bits, true));
+  QAT_CHECK(check_m(M, out, in));
   if (!X || !Wq || !s || !z || !Y) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({X, Wq, s, z, Y}));
   const size_t ng = out * (in / 64) * 4;
@@ -297,7 +292,7 @@ QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const
   a.z = z;
   a.G = in / 64;
   a.Kq = (float)((1 << bits) - 1);
-  qat::launch_gemm_bf16_out(a, qat::kPacked, bits, stream);
+  qat::launch_gemm_fwd(a, qat::kPacked, bits, stream);
   return finish();
 }
 
@@ -306,54 +301,28 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
                                        int64_t in, int32_t group, int32_t bits, uint16_t* dX,
                                        float* ds, float* dz, void* ws, size_t ws_bytes,
                                        hipStream_t stream) {
-  QAT_CHECK(check_common(out, in, group, bits));
-  QAT_CHECK(check_m(M));
+  QAT_CHECK(check_common(out, in, group, bits, true));
+  QAT_CHECK(check_m(M, out, in));
   if (!dY || !X || !Wq || !s || !z || !ds) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({dY, X, Wq, s, z, dX, ds, dz, ws}));
-  const Ws L = ws_layout(M, out, in);
-  if (!ws || ws_bytes < L.total) return QAT_ERR_WORKSPACE;
+  const size_t need = ws_bytes_for(out, in);
+  if (dX && (!ws || ws_bytes < need)) return QAT_ERR_WORKSPACE;
   const size_t ng = out * (in / 64) * 4;
-  Range outs[] = {{dX, (size_t)(M * in * 2)}, {ds, ng}, {dz, ng}, {ws, L.total}};
+  Range outs[] = {{dX, (size_t)(M * in * 2)}, {ds, ng}, {dz, ng}, {dX ? ws : nullptr, need}};
   Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)},
                  {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 4, ins, 5));
-  const int64_t Mp = round_up(M, 64);
 
   if (dX) {
-    uint16_t* wt = (uint16_t*)((char*)ws + L.w_hat);
-    qat::launch_dequant_t(Wq, s, z, out, in, bits, wt, stream);
-    qat::GemmArgs a = gemm_args();
-    a.A = dY;
-    a.lda = out;
-    a.B = wt;
-    a.ldb = out;
-    a.M = (int)M;
-    a.N = (int)in;
-    a.K = (int)out;
-    a.C = dX;
-    a.ldc = in;
-    qat::launch_gemm_bf16_out(a, qat::kBf16, bits, stream);
+    uint16_t* w_hat = (uint16_t*)ws;
+    qat::launch_dequant(Wq, s, z, out, in, bits, w_hat, stream);
+    launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
-  uint16_t* dyt = (uint16_t*)((char*)ws + L.dy_t);
-  uint16_t* xt = (uint16_t*)((char*)ws + L.x_t);
-  qat::launch_transpose_bf16(dY, M, out, dyt, Mp, stream);
-  qat::launch_transpose_bf16(X, M, in, xt, Mp, stream);
-  qat::GemmArgs a = gemm_args();
-  a.A = dyt;
-  a.lda = Mp;
-  a.B = xt;
-  a.ldb = Mp;
-  a.M = (int)out;
-  a.N = (int)in;
-  a.K = (int)Mp;
-  a.s = s;
-  a.z = z;
-  a.G = in / 64;
-  a.Kq = (float)((1 << bits) - 1);
+  qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, bits);
   a.Wq = Wq;
   a.ldq = in * bits / 8;
   a.ds = ds;
   a.dz = dz;
-  qat::launch_gemm_e2e_grads(a, bits, stream);
+  qat::launch_gemm_grads(a, qat::kE2eScaleGrad, bits, stream);
   return finish();
 }

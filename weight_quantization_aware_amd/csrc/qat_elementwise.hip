@@ -1,6 +1,6 @@
 // HBM-bound kernels of the group-wise fake-quant linear (gfx950, wave64):
-// min-max init, code export, pack, and the transposed W_hat / operand staging
-// that lets every GEMM of the path read K-contiguous operands.
+// min-max init, code export (also the bf16 W_hat staging of the forward and
+// backward GEMMs), pack, and the E2E-QP dequantisation of packed codes.
 #include "qat_device.h"
 #include "qat_internal.h"
 
@@ -108,102 +108,28 @@ __global__ __launch_bounds__(256) void k_pack(const float4* __restrict__ W, cons
 }
 
 // ---------------------------------------------------------------------------
-// Transposed operand staging through LDS, 64x64 tiles, 256 threads.
-// Source tile rows r (64) x columns c (64); the destination holds the tile
-// transposed. Values go through LDS as fp32 in a [64][65] array (the +1 pad
-// keeps column reads free of bank conflicts).
+// E2E-QP operand staging: packed codes -> W_hat = bf16(fl32((q - z) * s)),
+// z as stored, [out, in] bf16. One chunk of 8 codes (N bytes in, 16 B out) per
+// thread, so both streams are contiguous across a wave.
 // ---------------------------------------------------------------------------
-
-// Store a 64x64 fp32 tile held in `t` transposed as bf16: dst[(c0 + c) * ldd + r0 + r].
-// Thread layout on the way out: column c = tid % 64, rows seg*16 .. +15 with seg = tid / 64.
-__device__ __forceinline__ void store_tile_t(float (*t)[65], uint16_t* __restrict__ dst, int64_t ldd,
-                                             int64_t c0, int64_t r0) {
-  const int c = threadIdx.x & 63, seg = threadIdx.x >> 6;
-  uint32_t p[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) p[k] = pack_bf16x2(t[seg * 16 + 2 * k][c], t[seg * 16 + 2 * k + 1][c]);
-  uint4* o = (uint4*)(dst + (c0 + c) * ldd + r0 + seg * 16);
-  o[0] = make_uint4(p[0], p[1], p[2], p[3]);
-  o[1] = make_uint4(p[4], p[5], p[6], p[7]);
-}
-
-// W [out, in] fp32 -> W_hat^T [in, out] bf16 (Eq. 1 + Eq. 2, straight-through zero point).
-__global__ __launch_bounds__(256) void k_quant_t(const float* __restrict__ W, const float* __restrict__ s,
-                                                 const float* __restrict__ z, int64_t out, int64_t in,
-                                                 float K, uint16_t* __restrict__ Wt) {
-  __shared__ float t[64][65];
-  const int64_t o0 = (int64_t)blockIdx.y * 64, i0 = (int64_t)blockIdx.x * 64;
-  const int64_t G = in / kGroup;
-  const int cv = threadIdx.x & 15, r = threadIdx.x >> 4;   // float4 column, row 0..15
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    int rr = r + 16 * p;
-    int64_t o = o0 + rr;
-    float sv = s[o * G + blockIdx.x];
-    float zr = round_clamp_zero(z[o * G + blockIdx.x], K);
-    float4 w = *(const float4*)(W + o * in + i0 + cv * 4);
-    t[rr][cv * 4 + 0] = quant_elem(w.x, sv, zr, K).w_hat;
-    t[rr][cv * 4 + 1] = quant_elem(w.y, sv, zr, K).w_hat;
-    t[rr][cv * 4 + 2] = quant_elem(w.z, sv, zr, K).w_hat;
-    t[rr][cv * 4 + 3] = quant_elem(w.w, sv, zr, K).w_hat;
-  }
-  __syncthreads();
-  store_tile_t(t, Wt, out, i0, o0);
-}
-
-// Packed Wq [out, in*N/8] -> W_hat^T [in, out] bf16 with W_hat = fl32((q - z) * s), z as stored.
 template <int N>
-__global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ Wq,
-                                                   const float* __restrict__ s,
-                                                   const float* __restrict__ z, int64_t out,
-                                                   int64_t in, uint16_t* __restrict__ Wt) {
-  __shared__ float t[64][65];
-  const int64_t o0 = (int64_t)blockIdx.y * 64, i0 = (int64_t)blockIdx.x * 64;
-  const int64_t G = in / kGroup;
-  const int64_t rowbytes = in * N / 8;
-  const int c8 = threadIdx.x & 7, r = threadIdx.x >> 3;     // 8-code chunk, row 0..31
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ Wq, const float* __restrict__ s,
+                                                 const float* __restrict__ z, int64_t nchunks,
+                                                 uint4* __restrict__ w_hat) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nchunks) return;
+  const int64_t g = c >> 3;
+  const float sv = s[g], zv = z[g];
+  const uint8_t* src = Wq + c * N;
+  uint32_t word;
+  if constexpr (N == 2) word = *(const uint16_t*)src;
+  else if constexpr (N == 4) word = *(const uint32_t*)src;
+  else word = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16);
+  float h[8];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    int rr = r + 32 * p;
-    int64_t o = o0 + rr;
-    float sv = s[o * G + blockIdx.x];
-    float zv = z[o * G + blockIdx.x];
-    const uint8_t* src = Wq + o * rowbytes + (i0 / 8) * N + c8 * N;
-    uint32_t word;
-    if constexpr (N == 2) word = *(const uint16_t*)src;
-    else if constexpr (N == 4) word = *(const uint32_t*)src;
-    else word = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float q = (float)((word >> (N * k)) & ((1u << N) - 1));
-      t[rr][c8 * 8 + k] = (q - zv) * sv;
-    }
-  }
-  __syncthreads();
-  store_tile_t(t, Wt, out, i0, o0);
-}
-
-// bf16 [R, C] (row stride ldsrc) -> [C, Rp] (row stride Rp), rows R..Rp-1 zero.
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int64_t R,
-                                                        int64_t C, int64_t ldsrc,
-                                                        uint16_t* __restrict__ dst, int64_t Rp) {
-  __shared__ float t[64][65];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int c8 = threadIdx.x & 7, r = threadIdx.x >> 3;      // 8-element chunk, row 0..31
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    int rr = r + 32 * p;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + rr < R) v = *(const uint4*)(src + (r0 + rr) * ldsrc + c0 + c8 * 8);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      t[rr][c8 * 8 + 2 * k] = __builtin_bit_cast(float, w[k] << 16);
-      t[rr][c8 * 8 + 2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xFFFF0000u);
-    }
-  }
-  __syncthreads();
-  store_tile_t(t, dst, Rp, c0, r0);
+  for (int k = 0; k < 8; ++k) h[k] = ((float)((word >> (N * k)) & ((1u << N) - 1)) - zv) * sv;
+  w_hat[c] = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                        pack_bf16x2(h[6], h[7]));
 }
 
 // ---------------------------------------------------------------------------
@@ -238,27 +164,13 @@ void launch_pack(const float* W, const float* s, const float* z, int64_t out, in
     hipLaunchKernelGGL(k_pack<4>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, Wq, zround);
 }
 
-void launch_quant_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                    uint16_t* Wt, hipStream_t st) {
-  hipLaunchKernelGGL(k_quant_t, dim3((unsigned)(in / 64), (unsigned)(out / 64)), dim3(256), 0, st, W,
-                     s, z, out, in, (float)((1 << bits) - 1), Wt);
-}
-
-void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in,
-                      int bits, uint16_t* Wt, hipStream_t st) {
-  dim3 grid((unsigned)(in / 64), (unsigned)(out / 64));
-  if (bits == 2)
-    hipLaunchKernelGGL(k_dequant_t<2>, grid, dim3(256), 0, st, Wq, s, z, out, in, Wt);
-  else if (bits == 3)
-    hipLaunchKernelGGL(k_dequant_t<3>, grid, dim3(256), 0, st, Wq, s, z, out, in, Wt);
-  else
-    hipLaunchKernelGGL(k_dequant_t<4>, grid, dim3(256), 0, st, Wq, s, z, out, in, Wt);
-}
-
-void launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, int64_t Rp,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)(C / 64), (unsigned)(Rp / 64)), dim3(256), 0, st,
-                     src, R, C, C, dst, Rp);
+void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
+                    uint16_t* w_hat, hipStream_t st) {
+  const int64_t nchunks = out * in / 8;
+  dim3 grid(blocks_for(nchunks, 256));
+  if (bits == 2) hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
+  else if (bits == 3) hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
+  else hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
 }
 
 }  // namespace qat

@@ -111,7 +111,7 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int64_t nbytes) {
 }
 
 template <int ROWS, int BK, int SLOTS>
-struct DmaTile {
+struct DmaTileK {
   using L = LdsLayout<BK, SLOTS>;
   static constexpr int RPI = 1024 / L::PITCH;            // rows per DMA instruction
   static constexpr int NI = ROWS / RPI / 4;              // instructions per wave per slab
@@ -119,7 +119,8 @@ struct DmaTile {
   i32x4 rs;
   uint32_t voff[NI];
   uint32_t lrow[NI];                                     // wave-uniform LDS byte offsets
-  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows) {
+  // src is [rows][ld] with K contiguous; rows >= nrows read as zero.
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int /*kdim*/) {
     rs = buffer_rsrc(src + (int64_t)row0 * ld, (int64_t)(nrows - row0) * ld * 2);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -137,7 +138,77 @@ struct DmaTile {
 #pragma unroll
     for (int q = 0; q < NI; ++q) dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * 2);
   }
+  // Fragment of tile row r (= 16 t + (lane & 15)) for k-step ks: 8 consecutive k.
+  __device__ __forceinline__ static bf16x8 frag(const uint8_t* tile, int r, int ks, int lane) {
+    return *(const bf16x8*)(tile + L::off(r, ks * 4 + (lane >> 4)));
+  }
 };
+
+
+// MN-contiguous operand: global [K][ld] with the operand's rows contiguous
+// (e.g. dY or X as operands of dY^T X, or W_hat [out][in] as the operand of
+// dY W_hat). LDS keeps the natural [BK][ROWS] layout; 16-byte chunk c of k-row
+// k sits at position c ^ (2 (k & 3)). Fragments are read with
+// ds_read_b64_tr_b16: in each 16-lane group, lane j addresses the 4 elements
+// (k0 + j / 4, r0 + 4 (j % 4) .. +3) and lane i receives element i % 4 of
+// lane 4 e + i / 4's row for e = 0..3, i.e. rows r0 + i at k0 .. k0 + 3. Two
+// reads (k0 and k0 + 4) give the same 8 consecutive k as the K-contiguous
+// fragment. k-rows at or beyond kdim read as zero; rows beyond the operand's
+// extent hold other data and only feed outputs that are never stored.
+template <int ROWS, int BK>
+struct DmaTileMN {
+  static constexpr int CHR = ROWS / 8;                   // 16-byte chunks per k-row
+  static constexpr int PITCH = ROWS * 2;
+  static constexpr int KPI = 1024 / PITCH;               // k-rows per DMA instruction
+  static constexpr int NI = BK / KPI / 4;                // instructions per wave per slab
+  static_assert(CHR >= 8 && NI * KPI * 4 == BK, "tile shape");
+  i32x4 rs;
+  uint32_t voff[NI];
+  uint32_t lrow[NI];
+  uint32_t kstride;                                      // bytes per k-row in global memory
+  __device__ static __forceinline__ int off(int k, int chunk) {
+    return k * PITCH + ((chunk ^ ((k & 3) << 1)) << 4);
+  }
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int /*nrows*/, int kdim) {
+    rs = buffer_rsrc(src + row0, ((int64_t)kdim * ld - row0) * 2);
+    kstride = (uint32_t)(ld * 2);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int k0 = (wave * NI + q) * KPI;
+      const int kr = k0 + lane / CHR;
+      const int pos = lane % CHR;
+      const int chunk = pos ^ ((kr & 3) << 1);
+      voff[q] = (uint32_t)(kr * ld * 2 + chunk * 16);
+      lrow[q] = (uint32_t)(k0 * PITCH);
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t lds_tile, int k0) const {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
+  }
+  __device__ __forceinline__ static bf16x8 frag(const uint8_t* tile, int r, int ks, int lane) {
+    const int j = lane & 15;
+    const int kb = ks * 32 + 8 * (lane >> 4) + (j >> 2);
+    const int e = (r & ~15) + 4 * (j & 3);                  // first of the 4 elements this lane addresses
+    const int c = e >> 3, half = (e >> 2) & 1;
+    const __attribute__((address_space(3))) uint8_t* t = (const __attribute__((address_space(3))) uint8_t*)tile;
+    typedef short i16x4_ __attribute__((ext_vector_type(4)));
+    const i16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_*)(t + off(kb, c) + half * 8));
+    const i16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_*)(t + off(kb + 4, c) + half * 8));
+    typedef short i16x8_ __attribute__((ext_vector_type(8)));
+    const i16x8_ v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+template <int ROWS, int BK, int MN>
+struct DmaTileOf { using T = DmaTileK<ROWS, BK, kLdsSlots>; };
+template <int ROWS, int BK>
+struct DmaTileOf<ROWS, BK, 1> { using T = DmaTileMN<ROWS, BK>; };
 
 // ---------------------------------------------------------------------------
 // Register-path B loaders: issue() reads one slab from HBM into registers,
@@ -277,18 +348,18 @@ struct LoadPacked {
   }
 };
 
-template <int ROWS, int BK, int SLOTS, int BL, int NB>
+template <int ROWS, int BK, int MN, int BL, int NB>
 struct BLoaderOf;
-template <int ROWS, int BK, int SLOTS, int NB>
-struct BLoaderOf<ROWS, BK, SLOTS, kBf16, NB> { using T = DmaTile<ROWS, BK, SLOTS>; };
-template <int ROWS, int BK, int SLOTS, int NB>
-struct BLoaderOf<ROWS, BK, SLOTS, kFp32Quant, NB> { using T = LoadFp32Quant<ROWS, BK, SLOTS>; };
-template <int ROWS, int BK, int SLOTS, int NB>
-struct BLoaderOf<ROWS, BK, SLOTS, kPacked, NB> { using T = LoadPacked<ROWS, BK, SLOTS, NB>; };
+template <int ROWS, int BK, int MN, int NB>
+struct BLoaderOf<ROWS, BK, MN, kBf16, NB> { using T = typename DmaTileOf<ROWS, BK, MN>::T; };
+template <int ROWS, int BK, int MN, int NB>
+struct BLoaderOf<ROWS, BK, MN, kFp32Quant, NB> { using T = LoadFp32Quant<ROWS, BK, kLdsSlots>; };
+template <int ROWS, int BK, int MN, int NB>
+struct BLoaderOf<ROWS, BK, MN, kPacked, NB> { using T = LoadPacked<ROWS, BK, kLdsSlots, NB>; };
 
 template <int BL, class Ld>
 __device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
-  if constexpr (BL == kBf16) l.init((const uint16_t*)a.B, a.ldb, n0, a.N);
+  if constexpr (BL == kBf16) l.init((const uint16_t*)a.B, a.ldb, n0, a.N, a.K);
   else if constexpr (BL == kFp32Quant) l.init((const float*)a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.Kq);
   else l.init((const uint8_t*)a.B, a.ldb, n0, a.N, a.s, a.z, a.G);
 }
@@ -322,10 +393,13 @@ struct Frags {
 // The last slabs re-issue the final slab into idle stages so that the vmcnt
 // bookkeeping is the same on every iteration; nothing reads those copies.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int U2, int BL, int EP, int NB>
+template <int BM, int BN, int BK, int STAGES, int U2, int AMN, int BMN, int BL, int EP, int NB>
 __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
-  constexpr int SLOTS = kLdsSlots;
-  using L = LdsLayout<BK, SLOTS>;
+  using L = LdsLayout<BK, kLdsSlots>;
+  using LA = typename DmaTileOf<BM, BK, AMN>::T;
+  using LB = typename BLoaderOf<BN, BK, BMN, BL, NB>::T;
+  using FB = typename DmaTileOf<BN, BK, (BL == kBf16) ? BMN : 0>::T;   // B fragment reader
+  static_assert(BL == kBf16 || BMN == 0, "fused loaders produce K-contiguous tiles");
   static_assert(STAGES >= 3, "the shifted pipeline needs three stages");
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TI = WM / 16, TJ = WN / 16;
@@ -342,14 +416,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
   const int m0 = tm * BM, n0 = tn * BN;
   const uint32_t lds0 = lds_addr_of(smem);
 
-  DmaTile<BM, BK, SLOTS> la;
-  typename BLoaderOf<BN, BK, SLOTS, BL, NB>::T lb;
-  la.init(a.A, a.lda, m0, a.M);
+  LA la;
+  LB lb;
+  la.init(a.A, a.lda, m0, a.M, a.K);
   init_b<BL>(lb, a, n0);
   constexpr bool B_DMA = (BL == kBf16);
-  constexpr int NL = DmaTile<BM, BK, SLOTS>::NI + (B_DMA ? DmaTile<BN, BK, SLOTS>::NI : 0);
+  constexpr int NL = LA::NI + (B_DMA ? DmaTileOf<BN, BK, BMN>::T::NI : 0);
 
-  const int nk = a.K / BK;
+  const int nk = (a.K + BK - 1) / BK;
   auto issue = [&](int slab) {               // DMA part of one slab
     const int sl = slab < nk ? slab : nk - 1;
     const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
@@ -366,12 +440,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
   // Fragment reads index the __shared__ array directly (stage given as a byte
   // offset) so that they stay ds_read instructions.
   auto read_frags = [&](int st, int ks, Frags<TI, TJ>& f) {
-    const int chunk = ks * 4 + (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < TI; ++i) f.a[i] = *(const bf16x8*)&smem[st + L::off(wm0 + i * 16 + (lane & 15), chunk)];
+    for (int i = 0; i < TI; ++i) f.a[i] = LA::frag(&smem[st], wm0 + i * 16 + (lane & 15), ks, lane);
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      f.b[j] = *(const bf16x8*)&smem[st + A_BYTES + L::off(wn0 + j * 16 + (lane & 15), chunk)];
+    for (int j = 0; j < TJ; ++j) f.b[j] = FB::frag(&smem[st + A_BYTES], wn0 + j * 16 + (lane & 15), ks, lane);
   };
 
   f32x4 acc[TJ][TI];

@@ -12,23 +12,21 @@ void launch_quant_codes(const float* W, const float* s, const float* z, int64_t 
                         int bits, uint8_t* codes, uint16_t* w_hat, hipStream_t st);
 void launch_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
                  uint8_t* Wq, float* zround, hipStream_t st);
-void launch_quant_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                    uint16_t* Wt, hipStream_t st);
-void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in,
-                      int bits, uint16_t* Wt, hipStream_t st);
-void launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, int64_t Rp,
-                           hipStream_t st);
+void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
+                    uint16_t* w_hat, hipStream_t st);
 
 // ---- MFMA GEMMs (qat_gemm.hip) ----
-// All compute C[M, N] = sum_k A[m, k] * B[n, k] with A bf16 [M][lda] K-contiguous and
-// K % 64 == 0; they differ in where B comes from and what the epilogue does.
+// C[M, N] = sum_k A[m, k] * B[n, k] in bf16 with fp32 accumulation. Each operand
+// is either K-contiguous ([rows][ld], ld >= K) or MN-contiguous ([K][ld] with
+// the operand's rows contiguous). K-contiguous operands need K % 64 == 0;
+// with MN-contiguous operands K may be ragged (k beyond K reads as zero).
 struct GemmArgs {
   const uint16_t* A;
   int64_t lda;
-  const void* B;       // bf16 [N][ldb], fp32 W [N][ldb] or packed codes [N][ldb bytes]
+  const void* B;       // bf16 rows, fp32 master weight [N][ldb], or packed codes [N][ldb bytes]
   int64_t ldb;
   int M, N, K;
-  const float* s;      // [N-or-M rows][G] step sizes (fused loaders / epilogues)
+  const float* s;      // [weight rows][G] step sizes (fused loaders / epilogues)
   const float* z;
   int64_t G;           // groups per weight row
   float Kq;            // 2^bits - 1
@@ -39,18 +37,20 @@ struct GemmArgs {
   const uint8_t* Wq;   // packed codes [M][ldq bytes] for the E2E epilogue
   int64_t ldq;
   float* dW;           // [M][ldw] fp32, may be null
-  float* ds;           // [M][G]
-  float* dz;           // [M][G], may be null for E2E
+  float* ds;           // [M][G], may be null
+  float* dz;           // [M][G], may be null
 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
 enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2 };
+enum Layout { kKContig = 0, kMNContig = 1 };
 
-// Y = X W_hat^T style (bf16 output). bload selects the B source; bits used by fused loaders.
-void launch_gemm_bf16_out(const GemmArgs& a, int bload, int bits, hipStream_t st);
-// Straight-through gradient GEMM: rows = out, cols = in, epilogue writes dW, ds, dz.
-void launch_gemm_ste_grads(const GemmArgs& a, hipStream_t st);
-// E2E scale-gradient GEMM: rows = out, cols = in, epilogue writes ds (and dz).
-void launch_gemm_e2e_grads(const GemmArgs& a, int bits, hipStream_t st);
+// Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
+void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
+// dX = dY W_hat: A = dY (K-contiguous), B = W_hat [out][in] read MN-contiguous.
+void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
+// Gradient GEMM over tokens, Gw = dY^T X with both operands MN-contiguous;
+// epi = kSteGrads (dW, ds, dz) or kE2eScaleGrad (ds, dz).
+void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st);
 
 }  // namespace qat
