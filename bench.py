@@ -1,7 +1,7 @@
 """Benchmark of the group-wise fake-quant linear hot path on one MI355X.
 
 One step = one pass of every operation of the path over one batch:
-  init (min-max) -> fake-quant forward -> straight-through backward
+  min-max init -> fake-quant forward -> straight-through backward
   (dX, dW, ds, dz) -> pack -> E2E-QP dequant-GEMM forward -> E2E-QP backward
   (dX, ds),
 on the Llama-2-7B q_proj workload: fp32 W 4096x4096 ~N(0, 0.02) with 0.1% x10
@@ -12,11 +12,18 @@ value = counted GEMM FLOPs of the step / step time, where the count is
 6*M*in*out for the fake-quant forward + backward plus 6*M*in*out for the
 E2E-QP forward + dX + ds (init and pack add time, no FLOPs).
 
-Prints one JSON line (rank 0, N = 1 only).
+The roofline object covers the kernel with the largest share of the timed
+region, timed live by the library (HIP events around each launch on its
+stream). Its `traffic` comes from a committed rocprofv3 FETCH_SIZE /
+WRITE_SIZE summary under profiles/, used only while the kernel sources still
+hash to the value recorded there.
+
+Prints one JSON line (N = 1 only).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +36,11 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["weight_quantization_aware_amd/csrc/qat_gemm_kernel.h",
+                  "weight_quantization_aware_amd/csrc/qat_gemm.hip",
+                  "weight_quantization_aware_amd/csrc/qat_elementwise.hip",
+                  "weight_quantization_aware_amd/csrc/qat_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q_proj_w2g64.json")
 
 
 def parse():
@@ -37,17 +49,43 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512,
-                    help="weight rows of the bounded oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="weight rows of the bounded oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region run one 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def work_per_launch(label, M, out, inp, bits):
+    """Algorithmic work of one launch: ('mfma', flops) or ('hbm', bytes)."""
+    G = inp // 64
+    n = out * inp
+    if label.startswith("gemm"):
+        return "mfma", 2.0 * M * inp * out
+    if label == "init_minmax":
+        return "hbm", n * 4 + 2 * out * G * 4
+    if label == "quant_w_hat":
+        return "hbm", n * (4 + 2) + 2 * out * G * 4
+    if label == "pack":
+        return "hbm", n * (4 + bits / 8) + 3 * out * G * 4
+    if label == "dequant":
+        return "hbm", n * (bits / 8 + 2) + 2 * out * G * 4
+    return "hbm", float("nan")
 
 
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -79,7 +117,7 @@ def main():
 
     calls = [
         ("init", lambda: Q.qat_init_minmax(W, bits, s, z)),
-        ("fq_fwd", lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=None)),
+        ("fq_fwd", lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=ws)),
         ("fq_bwd", lambda: Q.qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=dX, dW=dW, ds=ds, dz=dz, ws=ws)),
         ("pack", lambda: Q.qat_pack(W, s, z, bits, Wq, zp)),
         ("e2e_fwd", lambda: Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Y2)),
@@ -92,8 +130,9 @@ def main():
             f()
     torch.cuda.synchronize(dev)
 
-    # Per-call events on the stream the library launches on (the current stream).
+    # ---- timed region: K steps, per-call events and per-kernel library timing
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    Q.timing_enable(True)
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -106,6 +145,8 @@ def main():
     end.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
+    Q.timing_enable(False)
+    kernels = Q.timing_report()
     ms_step = start.elapsed_time(end) / args.steps
     per_call = {name: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
                 for i, (name, _) in enumerate(calls)}
@@ -114,13 +155,50 @@ def main():
     flops_e2e = 6.0 * M * inp * out
     value = (flops_fq + flops_e2e) / (ms_step * 1e-3) / 1e12
 
-    # Dominant kernel: the fused fake-quant forward GEMM (one kernel per call).
-    t_fwd = per_call["fq_fwd"] * 1e-3
-    fwd_tflops = 2.0 * M * inp * out / t_fwd / 1e12
-    roofline = {"kernel": "k_gemm<fp32-quant-into-LDS> (qat_fakequant_linear_fwd, ws=NULL)",
-                "bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None}
+    # ---- per-kernel table and the dominant kernel's roofline
+    ktab = {}
+    for label, (tot_ms, n) in kernels.items():
+        kind, work = work_per_launch(label, M, out, inp, bits)
+        avg_s = tot_ms / n * 1e-3
+        rate = work / avg_s / (1e12 if kind == "mfma" else 1e9)
+        ktab[label] = {"launches_per_step": n / args.steps, "avg_us": round(avg_s * 1e6, 2),
+                       ("tflops" if kind == "mfma" else "gbs"): round(rate, 1),
+                       "share": round(tot_ms / (ms_step * args.steps), 4)}
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    kind, work = work_per_launch(dom, M, out, inp, bits)
+    avg_s = kernels[dom][0] / kernels[dom][1] * 1e-3
+    if kind == "mfma":
+        achieved, peak, unit = work / avg_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("sources_hash") == sources_hash() and dom in tr.get("kernels", {}):
+            traffic = tr["kernels"][dom]["bytes_per_launch"]
+    roofline = {"kernel": dom, "bound": "mfma" if kind == "mfma" else "hbm", "achieved": round(achieved, 2),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+                "avg_us": round(avg_s * 1e6, 2), "work_per_launch": work}
+
+    # ---- the fused fp32 forward (no workspace), timed on its own as evidence
+    Yf = torch.empty_like(Y)
+    for _ in range(3):
+        Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Yf, ws=None)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Yf, ws=None)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    t_fused = e0.elapsed_time(e1) / 10
+    fused_same = bool(torch.equal(Yf, Y))
+
+    if args.copy_calibration:            # a plain copy of known size for the HBM counters
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize(dev)
 
     breakdown = {name: {"ms": round(t, 4)} for name, t in per_call.items()}
     breakdown["fq_fwd"]["tflops"] = round(2 * M * inp * out / (per_call["fq_fwd"] * 1e-3) / 1e12, 1)
@@ -129,6 +207,9 @@ def main():
     breakdown["e2e_bwd"]["tflops"] = round(4 * M * inp * out / (per_call["e2e_bwd"] * 1e-3) / 1e12, 1)
     breakdown["init"]["gbs"] = round(out * inp * 4.125 / (per_call["init"] * 1e-3) / 1e9, 1)
     breakdown["pack"]["gbs"] = round(out * inp * (4.125 + bits / 8) / (per_call["pack"] * 1e-3) / 1e9, 1)
+    breakdown["fq_fwd_fused_no_ws"] = {"ms": round(t_fused, 4),
+                                       "tflops": round(2 * M * inp * out / (t_fused * 1e-3) / 1e12, 1),
+                                       "bit_identical_to_staged": fused_same}
     fq_only = flops_fq / ((per_call["fq_fwd"] + per_call["fq_bwd"]) * 1e-3) / 1e12
 
     cpu = None
@@ -154,6 +235,7 @@ def main():
         "fq_fwd_bwd_tflops": round(fq_only, 2),
         "mfma_peak_frac_fq": round(fq_only / MFMA_BF16_PEAK_TFLOPS, 4),
         "breakdown": breakdown,
+        "kernels": ktab,
         "wall_s": round(wall, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -191,10 +273,9 @@ def cpu_baseline(lin, W_np, X_np, dY_np, rows):
         reps += 1
     dt = (time.perf_counter() - t1) / max(reps - 1, 1) if reps > 1 else t1 - t0
     flops = 12.0 * M * inp * rows
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"same step on the first {rows} of {lin.out} weight rows (all {M} tokens, "
-                      f"all {inp} inputs), {reps} runs, mean of the timed ones; fp64 numpy"}
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"same step on the first {rows} of {lin.out} weight rows (all {M} tokens, all {inp} "
+                      f"inputs), {reps} runs, mean of the timed ones; fp64 numpy"}
 
 
 if __name__ == "__main__":

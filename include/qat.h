@@ -166,6 +166,19 @@ int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint
                                int32_t group, int32_t bits, uint16_t* dX, float* ds, float* dz,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Kernel timing, for benchmarks. qat_timing_enable(1) clears earlier records
+ * and starts bracketing every kernel the library launches with two HIP events
+ * on its stream; qat_timing_enable(0) stops. qat_timing_count() waits for the
+ * recorded events and returns the number of distinct kernel labels (or
+ * -QAT_ERR_HIP); qat_timing_get(i, ...) returns label i (copied into `label`,
+ * truncated to label_len), its summed elapsed milliseconds and its launch
+ * count. Timing adds one event pair per launch; off, it costs nothing.
+ */
+int32_t qat_timing_enable(int32_t on);
+int32_t qat_timing_count(void);
+int32_t qat_timing_get(int32_t i, char* label, size_t label_len, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

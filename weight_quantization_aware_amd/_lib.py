@@ -35,6 +35,10 @@ _SIGS = {
                                _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
     "qat_fakequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
     "qat_dequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
+    "qat_timing_enable": [_c_i32],
+    "qat_timing_count": [],
+    "qat_timing_get": [_c_i32, ctypes.c_char_p, _c_sz, ctypes.POINTER(ctypes.c_double),
+                       ctypes.POINTER(_c_i64)],
     "qat_status_string": [_c_i32],
     "qat_last_error": [],
 }
@@ -161,3 +165,28 @@ def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None)
     _call("qat_dequant_gemm_bwd_s", _p(_u16(dY)), _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp,
           GROUP, bits, _p(None if dX is None else _u16(dX)), _p(ds), _p(dz), _p(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream())
+
+
+# ---------------------------------------------------------------------------
+# Kernel timing (HIP events recorded by the library around each launch)
+# ---------------------------------------------------------------------------
+
+def timing_enable(on: bool) -> None:
+    lib().qat_timing_enable(1 if on else 0)
+
+
+def timing_report() -> dict:
+    """{label: (total_ms, launches)} for the kernels launched while enabled."""
+    L = lib()
+    n = L.qat_timing_count()
+    if n < 0:
+        raise QatError("qat_timing_count", -n)
+    out = {}
+    buf = ctypes.create_string_buffer(128)
+    for i in range(n):
+        ms, cnt = ctypes.c_double(), _c_i64()
+        st = L.qat_timing_get(i, buf, 128, ctypes.byref(ms), ctypes.byref(cnt))
+        if st != QAT_OK:
+            raise QatError("qat_timing_get", st)
+        out[buf.value.decode()] = (ms.value, int(cnt.value))
+    return out

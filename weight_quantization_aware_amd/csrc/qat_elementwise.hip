@@ -140,6 +140,7 @@ static inline unsigned blocks_for(int64_t n, int64_t per) { return (unsigned)((n
 void launch_init_minmax(const float* W, int64_t out, int64_t in, int bits, float* s, float* z,
                         hipStream_t st) {
   int64_t ngroups = out * (in / kGroup);
+  LaunchTimer t("init_minmax", st);
   hipLaunchKernelGGL(k_init_minmax, dim3(blocks_for(ngroups, 64)), dim3(256), 0, st,
                      (const float4*)W, ngroups, (float)((1 << bits) - 1), s, z);
 }
@@ -147,6 +148,7 @@ void launch_init_minmax(const float* W, int64_t out, int64_t in, int bits, float
 void launch_quant_codes(const float* W, const float* s, const float* z, int64_t out, int64_t in,
                         int bits, uint8_t* codes, uint16_t* w_hat, hipStream_t st) {
   int64_t nvec = out * in / 4;
+  LaunchTimer t(codes ? "quant_codes" : "quant_w_hat", st);
   hipLaunchKernelGGL(k_quant_codes, dim3(blocks_for(nvec, 256)), dim3(256), 0, st,
                      (const float4*)W, s, z, nvec, (float)((1 << bits) - 1), (uint32_t*)codes,
                      (uint2*)w_hat);
@@ -156,6 +158,7 @@ void launch_pack(const float* W, const float* s, const float* z, int64_t out, in
                  uint8_t* Wq, float* zround, hipStream_t st) {
   int64_t nchunks = out * in / 8;
   dim3 grid(blocks_for(nchunks, 256));
+  LaunchTimer t("pack", st);
   if (bits == 2)
     hipLaunchKernelGGL(k_pack<2>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, Wq, zround);
   else if (bits == 3)
@@ -168,6 +171,7 @@ void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t o
                     uint16_t* w_hat, hipStream_t st) {
   const int64_t nchunks = out * in / 8;
   dim3 grid(blocks_for(nchunks, 256));
+  LaunchTimer t("dequant", st);
   if (bits == 2) hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
   else if (bits == 3) hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
   else hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);

@@ -17,8 +17,18 @@ int64_t tiles(const GemmArgs& a, int bm, int bn) {
   return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
+template <int BL, int EP>
+constexpr const char* gemm_label(bool mn_b) {
+  if (EP == kSteGrads) return "gemm_ste_grads";
+  if (EP == kE2eScaleGrad) return "gemm_e2e_grads";
+  if (BL == kFp32Quant) return "gemm_fwd_fused_fp32";
+  if (BL == kPacked) return "gemm_fwd_packed";
+  return mn_b ? "gemm_dx" : "gemm_fwd";
+}
+
 template <int BM, int BN, int BK, int S, int AMN, int BMN, int BL, int EP, int NB>
 void launch_cfg(const GemmArgs& a, hipStream_t st) {
+  LaunchTimer t(gemm_label<BL, EP>(BMN == kMNContig), st);
   hipLaunchKernelGGL((k_gemm<BM, BN, BK, S, 0, AMN, BMN, BL, EP, NB>), dim3((unsigned)tiles(a, BM, BN)),
                      dim3(256), 0, st, a);
 }

@@ -5,6 +5,20 @@
 
 namespace qat {
 
+// Brackets one kernel launch with HIP events when timing is enabled
+// (qat_timing_enable); a single branch otherwise.
+class LaunchTimer {
+ public:
+  LaunchTimer(const char* label, hipStream_t st);
+  ~LaunchTimer();
+
+ private:
+  const char* label_;
+  hipStream_t stream_;
+  void* start_ = nullptr;
+  void* stop_ = nullptr;
+};
+
 // ---- HBM-bound kernels (qat_elementwise.hip) ----
 void launch_init_minmax(const float* W, int64_t out, int64_t in, int bits, float* s, float* z,
                         hipStream_t st);

@@ -1,0 +1,115 @@
+"""Summaries of rocprofv3 result databases for profiles/.
+
+    python -m weight_quantization_aware_amd.profile_summary stats <results.db> [--cmd "..."]
+        per-kernel dispatch count and mean / min / max duration (kernel trace)
+
+    python -m weight_quantization_aware_amd.profile_summary traffic <fetch.db> <write.db> \
+            --copy-bytes N [--cmd "..."]
+        per-kernel HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE
+        run, each scaled by what the same counter reads for the largest
+        non-library dispatch of the run (a plain device copy of N bytes), as
+        JSON keyed by the library's kernel labels, with the hash of the kernel
+        sources it was measured on.
+
+Reads SQLite databases written by rocprofv3 (ROCm 7); prints to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import json
+import re
+import sqlite3
+import sys
+
+# rocprofv3 kernel symbol -> the label the library's own timing uses
+LABELS = [
+    (r"k_gemm<[^>]*,\s*0,\s*1,\s*0,\s*0,\s*0>", "gemm_dx"),
+    (r"k_gemm<[^>]*,\s*1,\s*1,\s*0,\s*1,\s*0>", "gemm_ste_grads"),
+    (r"k_gemm<[^>]*,\s*1,\s*1,\s*0,\s*2,\s*\d>", "gemm_e2e_grads"),
+    (r"k_gemm<[^>]*,\s*0,\s*0,\s*1,\s*0,\s*0>", "gemm_fwd_fused_fp32"),
+    (r"k_gemm<[^>]*,\s*0,\s*0,\s*2,\s*0,\s*\d>", "gemm_fwd_packed"),
+    (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
+    (r"k_init_minmax", "init_minmax"),
+    (r"k_quant_codes", "quant_w_hat"),
+    (r"k_pack<", "pack"),
+    (r"k_dequant<", "dequant"),
+]
+
+
+def label_of(name: str):
+    for pat, lab in LABELS:
+        if re.search(pat, name):
+            return lab
+    return None
+
+
+def stats(db: str, cmd: str) -> None:
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, count(*), avg(end-start), min(end-start), max(end-start), sum(end-start) "
+                     "from kernels group by name order by sum(end-start) desc").fetchall()
+    print(f"# rocprofv3 kernel trace summary\n# command: {cmd}\n#")
+    print(f"{'label':22s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s}  kernel")
+    for name, n, avg, mn, mx, tot in rows:
+        lab = label_of(name) or "-"
+        short = re.sub(r"\(.*", "", name)[:80]
+        print(f"{lab:22s} {n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {tot / 1e3:10.1f}  {short}")
+
+
+def _counter(db: str, counter: str):
+    c = sqlite3.connect(db)
+    rows = c.execute("select kernel_name, dispatch_id, sum(value) from counters_collection "
+                     "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
+    per = collections.defaultdict(list)
+    calib = 0.0
+    for name, _, kib in rows:
+        lab = label_of(name)
+        if lab:
+            per[lab].append(kib)
+        elif "qat::" not in name:
+            calib = max(calib, kib)
+    return per, calib
+
+
+def traffic(fetch_db: str, write_db: str, copy_bytes: int, cmd: str) -> None:
+    sys.path.insert(0, ".")
+    from bench import sources_hash
+
+    fetch, cf = _counter(fetch_db, "FETCH_SIZE")
+    write, cw = _counter(write_db, "WRITE_SIZE")
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("no calibration copy found in the counter runs")
+    sf = copy_bytes / (cf * 1024.0)
+    sw = copy_bytes / (cw * 1024.0)
+    out = {"command": cmd, "sources_hash": sources_hash(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_kib": cf, "write_kib": cw,
+                           "fetch_scale": sf, "write_scale": sw},
+           "kernels": {}}
+    for lab in sorted(set(fetch) | set(write)):
+        f = sum(fetch.get(lab, [0])) / max(len(fetch.get(lab, [])), 1) * 1024.0 * sf
+        w = sum(write.get(lab, [0])) / max(len(write.get(lab, [])), 1) * 1024.0 * sw
+        out["kernels"][lab] = {"fetch_bytes": round(f), "write_bytes": round(w), "bytes_per_launch": round(f + w),
+                               "dispatches": max(len(fetch.get(lab, [])), len(write.get(lab, [])))}
+    print(json.dumps(out, indent=1))
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("db")
+    a.add_argument("--cmd", default="")
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_db")
+    b.add_argument("write_db")
+    b.add_argument("--copy-bytes", type=int, default=1 << 30)
+    b.add_argument("--cmd", default="")
+    args = ap.parse_args()
+    if args.what == "stats":
+        stats(args.db, args.cmd)
+    else:
+        traffic(args.fetch_db, args.write_db, args.copy_bytes, args.cmd)
+
+
+if __name__ == "__main__":
+    main()
