@@ -145,12 +145,15 @@ size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in);
 /*
  * a9. E2E-QP forward (modelfoundations.com note, Phase 2; Paper-Notes, E2E-QP):
  * W_hat = bf16(fl32((q - z) * s)) with q unpacked from Wq and z used as stored
- * (frozen, integer valued); Y = X * W_hat^T. No workspace: the packed codes are
- * dequantised straight into LDS inside the GEMM.
+ * (frozen, integer valued); Y = X * W_hat^T.
+ * ws: NULL selects the fused kernel that dequantises packed codes straight
+ * into LDS inside the GEMM (no workspace; the dequantisation runs once per
+ * 128- or 256-token tile); otherwise >= qat_dequant_ws_bytes(M, out, in)
+ * bytes of scratch that receive the bf16 W_hat, staged once per call.
  */
 int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* s, const float* z,
                              int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
-                             uint16_t* Y, hipStream_t stream);
+                             uint16_t* Y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * a10. E2E-QP backward with the exact scale gradient dW_hat/ds = q - z:
@@ -174,8 +177,12 @@ int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint
  * -QAT_ERR_HIP); qat_timing_get(i, ...) returns label i (copied into `label`,
  * truncated to label_len), its summed elapsed milliseconds and its launch
  * count. Timing adds one event pair per launch; off, it costs nothing.
+ * qat_timing_select(label) restricts the events to launches of that kernel
+ * label (NULL: every launch), so one kernel can be timed inside a run of
+ * the whole path at the cost of its own event pairs only.
  */
 int32_t qat_timing_enable(int32_t on);
+int32_t qat_timing_select(const char* label);
 int32_t qat_timing_count(void);
 int32_t qat_timing_get(int32_t i, char* label, size_t label_len, double* total_ms, int64_t* launches);
 

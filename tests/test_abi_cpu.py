@@ -83,5 +83,17 @@ def test_fwd_bwd_validation():
     # e2e bwd: ds is required
     assert L.qat_dequant_gemm_bwd_s(A, B, C, D, E, 8, 64, 128, 64, 2, None, None, None, FAKE * 7,
                                     1 << 30, None) == 1
+    # e2e fwd: workspace given but too small; M <= 0
+    assert L.qat_dequant_gemm_fwd(A, B, C, D, 8, 64, 128, 64, 2, E, FAKE * 7, 16, None) == 6
+    assert L.qat_dequant_gemm_fwd(A, B, C, D, 0, 64, 128, 64, 2, E, None, 0, None) == 2
     # pack: 3 bits with a group-aligned row is fine shape-wise, bits 1 is not
     assert L.qat_pack(A, B, C, 64, 128, 64, 1, D, None, None) == 3
+
+
+def test_timing_registry_host_side():
+    # enabling, selecting and reading the registry records nothing without launches
+    Q.timing_select("gemm_fwd")
+    Q.timing_enable(True)
+    Q.timing_enable(False)
+    Q.timing_select(None)
+    assert Q.timing_report() == {}

@@ -233,6 +233,8 @@ def test_e2e_parity(M, out, inp, bits):
     Y = torch.empty(M, out, dtype=torch.bfloat16, device="cuda")
     dq, ds_, dz_ = dev_u8(Wq), dev_f32(s), dev_f32(z)
     Q.qat_dequant_gemm_fwd(dev_bf16(X), dq, ds_, dz_, bits, Y)
+    Y_staged = torch.empty_like(Y)
+    Q.qat_dequant_gemm_fwd(dev_bf16(X), dq, ds_, dz_, bits, Y_staged, ws=ws)
     gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
     gs = torch.empty(out, inp // 64, device="cuda")
     gz = torch.empty_like(gs)
@@ -241,6 +243,9 @@ def test_e2e_parity(M, out, inp, bits):
     Y_ref = O.dequant_gemm_fwd(X, Wq, s, z, inp, bits)
     r = O.dequant_gemm_bwd_s(dY, X, Wq, s, z, inp, bits)
     assert rel_fro(O.bf16_bits_to_f64(host_bits(Y)), Y_ref) < TOL_BF16
+    # fused (codes dequantised into LDS) and staged (W_hat in the workspace)
+    # forwards multiply the same bf16 operand in the same k order
+    assert np.array_equal(host_bits(Y), host_bits(Y_staged))
     assert rel_fro(O.bf16_bits_to_f64(host_bits(gX)), r["dX"]) < TOL_BF16
     assert rel_fro(gs.cpu().numpy(), r["ds"]) < TOL_F32
     assert rel_fro(gz.cpu().numpy(), r["dz"]) < TOL_F32
@@ -261,10 +266,13 @@ def test_pack_then_dequant_gemm_equals_fakequant_forward(bits):
     Y1 = torch.empty(M, out, dtype=torch.bfloat16, device="cuda")
     Y2 = torch.empty_like(Y1)
     Xd = dev_bf16(X)
+    Y3 = torch.empty_like(Y1)
     Q.qat_dequant_gemm_fwd(Xd, Wq, ds_, zp, bits, Y1)
+    Q.qat_dequant_gemm_fwd(Xd, Wq, ds_, zp, bits, Y3, ws=Q.workspace(Q.dequant_ws_bytes(M, out, inp)))
     Q.qat_fakequant_linear_fwd(Xd, dW_, ds_, dz_, bits, Y2, ws=Q.workspace(Q.fakequant_ws_bytes(M, out, inp)))
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(Y1), host_bits(Y2))
+    assert np.array_equal(host_bits(Y3), host_bits(Y2))
 
 
 # ---------------------------------------------------------------------------

@@ -30,13 +30,14 @@ _SIGS = {
                                  _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
     "qat_pack": [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp],
     "qat_dequant_gemm_fwd": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
-                             _c_vp, _c_vp],
+                             _c_vp, _c_vp, _c_sz, _c_vp],
     "qat_dequant_gemm_bwd_s": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32,
                                _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
     "qat_fakequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
     "qat_dequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
     "qat_timing_enable": [_c_i32],
     "qat_timing_count": [],
+    "qat_timing_select": [ctypes.c_char_p],
     "qat_timing_get": [_c_i32, ctypes.c_char_p, _c_sz, ctypes.POINTER(ctypes.c_double),
                        ctypes.POINTER(_c_i64)],
     "qat_status_string": [_c_i32],
@@ -152,11 +153,11 @@ def qat_pack(W, s, z, bits, Wq, z_round=None) -> None:
     _call("qat_pack", _p(W), _p(s), _p(z), out, inp, GROUP, bits, _p(Wq), _p(z_round), _stream())
 
 
-def qat_dequant_gemm_fwd(X, Wq, s, z, bits, Y) -> None:
+def qat_dequant_gemm_fwd(X, Wq, s, z, bits, Y, ws=None) -> None:
     M, inp = X.shape
     out = Wq.shape[0]
     _call("qat_dequant_gemm_fwd", _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp, GROUP, bits,
-          _p(_u16(Y)), _stream())
+          _p(_u16(Y)), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
 
 
 def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None) -> None:
@@ -173,6 +174,11 @@ def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None)
 
 def timing_enable(on: bool) -> None:
     lib().qat_timing_enable(1 if on else 0)
+
+
+def timing_select(label: Optional[str]) -> None:
+    """Time only launches of this kernel label (None: every launch)."""
+    lib().qat_timing_select(None if label is None else label.encode())
 
 
 def timing_report() -> dict:

@@ -269,20 +269,21 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
 
 QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* s,
                                      const float* z, int64_t M, int64_t out, int64_t in, int32_t group,
-                                     int32_t bits, uint16_t* Y, hipStream_t stream) {
+                                     int32_t bits, uint16_t* Y, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
   QAT_CHECK(check_common(out, in, group, bits, true));
   QAT_CHECK(check_m(M, out, in));
   if (!X || !Wq || !s || !z || !Y) return QAT_ERR_NULL;
-  QAT_CHECK(check_ptrs({X, Wq, s, z, Y}));
+  QAT_CHECK(check_ptrs({X, Wq, s, z, Y, ws}));
+  const size_t need = ws_bytes_for(out, in);
+  if (ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
   const size_t ng = out * (in / 64) * 4;
-  Range outs[] = {{Y, (size_t)(M * out * 2)}};
+  Range outs[] = {{Y, (size_t)(M * out * 2)}, {ws, ws ? need : 0}};
   Range ins[] = {{X, (size_t)(M * in * 2)}, {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}};
-  QAT_CHECK(check_alias(outs, 1, ins, 4));
+  QAT_CHECK(check_alias(outs, 2, ins, 4));
   qat::GemmArgs a = gemm_args();
   a.A = X;
   a.lda = in;
-  a.B = Wq;
-  a.ldb = in * bits / 8;
   a.M = (int)M;
   a.N = (int)out;
   a.K = (int)in;
@@ -292,7 +293,17 @@ QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const
   a.z = z;
   a.G = in / 64;
   a.Kq = (float)((1 << bits) - 1);
-  qat::launch_gemm_fwd(a, qat::kPacked, bits, stream);
+  if (ws) {
+    uint16_t* w_hat = (uint16_t*)ws;
+    qat::launch_dequant(Wq, s, z, out, in, bits, w_hat, stream);
+    a.B = w_hat;
+    a.ldb = in;
+    qat::launch_gemm_fwd(a, qat::kBf16, bits, stream);
+  } else {
+    a.B = Wq;
+    a.ldb = in * bits / 8;
+    qat::launch_gemm_fwd(a, qat::kPacked, bits, stream);
+  }
   return finish();
 }
 

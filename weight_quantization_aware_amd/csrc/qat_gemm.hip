@@ -5,8 +5,9 @@
 //                                 MLP-sized and 70B-sized forwards
 //   B  128x256, BK 64, 3 stages   about one tile per CU at 128x256
 //   C  128x128, BK 64, 4 stages   small problems
-// Fused B loaders (fp32 quantise, packed dequantise) need BK = 64 (a slab is
-// one quantisation group): 256x128 or 128x128, 3 stages.
+// Fused B operands go through an LDS ring beside the bf16 stages: packed codes
+// (E2E-QP forward) with 256-row B tiles, BK = 32, 4 stages; the fp32 master
+// weight (forward without workspace) with 128-row B tiles, BK = 32, 3 stages.
 #include "qat_gemm_kernel.h"
 
 namespace qat {
@@ -39,9 +40,12 @@ void launch_pick(const GemmArgs& a, hipStream_t st) {
     if (tiles(a, 256, 256) >= 256) launch_cfg<256, 256, 32, 4, AMN, BMN, BL, EP, NB>(a, st);
     else if (tiles(a, 128, 256) >= 192) launch_cfg<128, 256, 64, 3, AMN, BMN, BL, EP, NB>(a, st);
     else launch_cfg<128, 128, 64, 4, AMN, BMN, BL, EP, NB>(a, st);
+  } else if constexpr (BL == kPacked) {
+    if (tiles(a, 256, 256) >= 256) launch_cfg<256, 256, 32, 4, AMN, BMN, BL, EP, NB>(a, st);
+    else launch_cfg<128, 256, 32, 4, AMN, BMN, BL, EP, NB>(a, st);
   } else {
-    if (tiles(a, 256, 128) >= 256) launch_cfg<256, 128, 64, 3, AMN, BMN, BL, EP, NB>(a, st);
-    else launch_cfg<128, 128, 64, 3, AMN, BMN, BL, EP, NB>(a, st);
+    if (tiles(a, 256, 128) >= 256) launch_cfg<256, 128, 32, 3, AMN, BMN, BL, EP, NB>(a, st);
+    else launch_cfg<128, 128, 32, 3, AMN, BMN, BL, EP, NB>(a, st);
   }
 }
 

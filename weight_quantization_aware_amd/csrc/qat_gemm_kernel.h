@@ -27,18 +27,6 @@ namespace qat {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t nbytes) {
-  if (nbytes < 0) nbytes = 0;
-  if (nbytes > 0x7FFFFFF0) nbytes = 0x7FFFFFF0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
-}
-
-// 16-byte load; offsets at or beyond the resource size read as zero.
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
-
 // Workgroup id -> output tile. Consecutive workgroup ids go round-robin to the
 // 8 XCDs; each XCD gets a contiguous range of tiles, walked in groups of 8
 // tile-rows so that neighbouring workgroups share operand tiles in its L2.
@@ -83,6 +71,13 @@ struct LdsLayout {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(rsrc)
                : "memory", "m0");
@@ -210,158 +205,128 @@ struct DmaTileOf { using T = DmaTileK<ROWS, BK, kLdsSlots>; };
 template <int ROWS, int BK>
 struct DmaTileOf<ROWS, BK, 1> { using T = DmaTileMN<ROWS, BK>; };
 
-// ---------------------------------------------------------------------------
-// Register-path B loaders: issue() reads one slab from HBM into registers,
-// commit() converts it to bf16 and writes it into an LDS stage.
-// Thread t covers chunk t % CH of rows t / CH + (256 / CH) p.
-// ---------------------------------------------------------------------------
-
-// fp32 master weight -> quantise (Eq. 1) -> dequantise (Eq. 2) -> bf16 in LDS.
-// u = w * fl32(1/s) lies within 3 ulp of fl32(w/s); where that interval could
-// hold a half-integer the element is redone with the correctly rounded
-// division, so codes equal the exact fp32 quantiser's. Needs BK = 64 (one group).
-template <int ROWS, int BK, int SLOTS>
-struct LoadFp32Quant {
-  using L = LdsLayout<BK, SLOTS>;
-  static constexpr int RP = 256 / L::CH, P = ROWS / RP;
-  static_assert(BK == 64, "a slab must be one quantisation group");
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t base, ld_rows;
-  const float* s;
-  const float* z;
-  int64_t G;
-  int row0, nrows;
+// Quantised-weight operands through an LDS ring. Per slab, the raw weight
+// bytes of ROWS rows (packed N-bit codes, BK*N/8 bytes per row; or the fp32
+// master weight, BK*4 bytes per row) and the rows' s and z reach a ring entry
+// by dword DMA, one slab ahead of the A operand. Every thread then converts
+// its share into the K-contiguous bf16 B stage two slabs ahead of the MFMAs:
+//   packed (E2E-QP):  W_hat = (q - z) * s, z as stored;
+//   fp32 (Block-AP):  Eq. 1 then Eq. 2 with zr = clamp(rint(z), 0, K). u is
+//     w * fl32(1/s), within 3 ulp of fl32(w/s); where that interval could
+//     hold a half-integer the element is redone with the correctly rounded
+//     division, so the codes are exactly the fp32 quantiser's.
+// With BK = 32 a slab is half a quantisation group (same s, z).
+template <int ROWS, int BK, int KIND, int NB>
+struct DmaRing {
+  using L = LdsLayout<BK, kLdsSlots>;
+  static constexpr int DW = KIND == kPacked ? BK * NB / 32 : BK;   // weight dwords per row per slab
+  static constexpr int NI_Q = ROWS * DW / 64 / 4;                  // weight DMA instructions per wave
+  static constexpr int NI_S = 2 * ROWS / 64 / 4;                   // s and z, [2][ROWS] dwords
+  static constexpr int NI = NI_Q + NI_S;
+  static constexpr int P_BYTES = ROWS * DW * 4 + 2 * ROWS * 4;
+  static_assert(NI_Q * 256 == ROWS * DW && NI_S * 256 == 2 * ROWS, "ring tile shape");
+  i32x4 rq, rsz[2];
+  uint32_t vq[NI_Q], vs[NI_S];
+  int wave;
   float K;
-  uint4 r[P][2];
-  float sv[P], zv[P];
-  __device__ __forceinline__ void init(const float* W, int64_t ld, int row0_, int nrows_, const float* s_,
-                                       const float* z_, int64_t G_, float K_) {
-    row0 = row0_;
-    nrows = nrows_;
-    rs = make_rsrc(W + (int64_t)row0 * ld, (int64_t)(nrows - row0) * ld * 4);
-    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
-    base = (uint32_t)(rr * ld * 4 + c * 32);
-    ld_rows = (uint32_t)(RP * ld * 4);
-    s = s_;
-    z = z_;
-    G = G_;
+  __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes, int row0, int nrows, const float* s,
+                                       const float* z, int64_t G, float K_) {
     K = K_;
-  }
-  __device__ __forceinline__ void issue(int k0) {
-    const int rr = threadIdx.x / L::CH;
-    const int kt = k0 / 64;
+    rq = buffer_rsrc((const uint8_t*)Wsrc + (int64_t)row0 * row_bytes, (int64_t)(nrows - row0) * row_bytes);
+    rsz[0] = buffer_rsrc(s + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
+    rsz[1] = buffer_rsrc(z + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      r[p][0] = bload16(rs, base + p * ld_rows + k0 * 4);
-      r[p][1] = bload16(rs, base + p * ld_rows + k0 * 4 + 16);
-      const int row = min(row0 + rr + RP * p, nrows - 1);
-      sv[p] = s[(int64_t)row * G + kt];
-      zv[p] = z[(int64_t)row * G + kt];
+    for (int q = 0; q < NI_Q; ++q) {
+      const int idx = (wave * NI_Q + q) * 64 + lane;       // flat dword of the [ROWS][DW] slab
+      vq[q] = (uint32_t)((idx / DW) * row_bytes + (idx % DW) * 4);
+    }
+#pragma unroll
+    for (int q = 0; q < NI_S; ++q) {
+      const int idx = (wave * NI_S + q) * 64 + lane;       // flat dword of [2][ROWS]
+      vs[q] = (uint32_t)((idx % ROWS) * G * 4);
     }
   }
-  __device__ __forceinline__ void commit(uint8_t* lds) const {
-    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
+  // lds_p: this slab's ring entry: [ROWS][DW] weight dwords, then s[ROWS], z[ROWS].
+  __device__ __forceinline__ void issue(uint32_t lds_p, int k0) const {
+    const uint32_t cb = KIND == kPacked ? (uint32_t)(k0 * NB / 8) : (uint32_t)(k0 * 4);
+    const uint32_t gb = (uint32_t)((k0 / 64) * 4);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const float s_ = sv[p];
-      const float z_ = round_clamp_zero(zv[p], K);
-      const float rcp = 1.0f / s_;
-      const uint32_t wb[8] = {r[p][0].x, r[p][0].y, r[p][0].z, r[p][0].w,
-                              r[p][1].x, r[p][1].y, r[p][1].z, r[p][1].w};
+    for (int q = 0; q < NI_Q; ++q) dma4(rq, lds_p + (uint32_t)((wave * NI_Q + q) * 256), vq[q] + cb);
+#pragma unroll
+    for (int q = 0; q < NI_S; ++q) {
+      const int which = ((wave * NI_S + q) * 64) / ROWS;    // 0: s, 1: z (uniform per instruction)
+      i32x4 r = which ? rsz[1] : rsz[0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_readfirstlane(r[e]);
+      dma4(r, lds_p + ROWS * DW * 4 + (uint32_t)((wave * NI_S + q) * 256), vs[q] + gb);
+    }
+  }
+  // Convert one slab from the ring entry at byte p into the B stage at byte b.
+  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b) const {
+    constexpr int PARTS = 256 / ROWS;                      // threads per row
+    constexpr int CPT = (BK / 8) / PARTS;                  // 8-element chunks per thread
+    const int row = threadIdx.x / PARTS, part = threadIdx.x % PARTS;
+    const uint32_t* q = (const uint32_t*)&smem[p + row * DW * 4];
+    const float sv = *(const float*)&smem[p + ROWS * DW * 4 + row * 4];
+    const float zv = *(const float*)&smem[p + ROWS * DW * 4 + ROWS * 4 + row * 4];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int c = part * CPT + cc;                       // chunk of this row's slab
       float h[8];
-      bool near_tie = false;
+      if constexpr (KIND == kPacked) {
+        const int bit = c * 8 * NB;
+        uint64_t w = q[bit >> 5];
+        if (NB == 3 && (bit & 31) > 8) w |= (uint64_t)q[(bit >> 5) + 1] << 32;
+        const uint32_t word = (uint32_t)(w >> (bit & 31));
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float w = __builtin_bit_cast(float, wb[k]);
-        const float u = w * rcp;
-        const float fr = u - floorf(u);
-        near_tie |= fabsf(fr - 0.5f) <= fabsf(u) * 0x1p-20f + 0x1p-60f;
-        const float q = fminf(fmaxf(__builtin_rintf(u) + z_, 0.0f), K);
-        h[k] = (q - z_) * s_;
+        for (int k = 0; k < 8; ++k) h[k] = ((float)((word >> (NB * k)) & ((1u << NB) - 1)) - zv) * sv;
+      } else {
+        const float zr = round_clamp_zero(zv, K);
+        const float rcp = 1.0f / sv;
+        const uint4 w0 = *(const uint4*)&q[c * 8], w1 = *(const uint4*)&q[c * 8 + 4];
+        const uint32_t wb[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w = __builtin_bit_cast(float, wb[k]);
+          const float u = w * rcp;
+          const float fr = u - floorf(u);
+          if (fabsf(fr - 0.5f) <= fabsf(u) * 0x1p-20f + 0x1p-60f) {
+            h[k] = quant_elem(w, sv, zr, K).w_hat;          // near a rounding tie: exact division
+          } else {
+            const float qv = fminf(fmaxf(__builtin_rintf(u) + zr, 0.0f), K);
+            h[k] = (qv - zr) * sv;
+          }
+        }
       }
-      if (near_tie) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) h[k] = quant_elem(__builtin_bit_cast(float, wb[k]), s_, z_, K).w_hat;
-      }
-      const bool ok = row0 + rr + RP * p < nrows;
-      uint4 o = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
-                           pack_bf16x2(h[6], h[7]));
-      if (!ok) o = make_uint4(0, 0, 0, 0);
-      *(uint4*)(lds + L::off(rr + RP * p, c)) = o;
-    }
-  }
-};
-
-// Packed N-bit codes -> (q - z) * s -> bf16 in LDS (E2E-QP; z as stored). BK = 64.
-template <int ROWS, int BK, int SLOTS, int NB>
-struct LoadPacked {
-  using L = LdsLayout<BK, SLOTS>;
-  static constexpr int RP = 256 / L::CH, P = ROWS / RP;
-  static_assert(BK == 64, "a slab must be one quantisation group");
-  const uint8_t* q;
-  int64_t ldq;
-  const float* s;
-  const float* z;
-  int64_t G;
-  int row0, nrows;
-  uint32_t word[P];
-  float sv[P], zv[P];
-  __device__ __forceinline__ void init(const uint8_t* Wq, int64_t ldq_, int row0_, int nrows_, const float* s_,
-                                       const float* z_, int64_t G_) {
-    q = Wq;
-    ldq = ldq_;
-    row0 = row0_;
-    nrows = nrows_;
-    s = s_;
-    z = z_;
-    G = G_;
-  }
-  __device__ __forceinline__ void issue(int k0) {
-    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
-    const int kt = k0 / 64;
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int row = min(row0 + rr + RP * p, nrows - 1);
-      const uint8_t* src = q + (int64_t)row * ldq + (int64_t)kt * 8 * NB + c * NB;
-      if constexpr (NB == 2) word[p] = *(const uint16_t*)src;
-      else if constexpr (NB == 4) word[p] = *(const uint32_t*)src;
-      else word[p] = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16);
-      sv[p] = s[(int64_t)row * G + kt];
-      zv[p] = z[(int64_t)row * G + kt];
-    }
-  }
-  __device__ __forceinline__ void commit(uint8_t* lds) const {
-    const int c = threadIdx.x % L::CH, rr = threadIdx.x / L::CH;
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      float h[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float qv = (float)((word[p] >> (NB * k)) & ((1u << NB) - 1));
-        h[k] = (qv - zv[p]) * sv[p];
-      }
-      uint4 o = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
-                           pack_bf16x2(h[6], h[7]));
-      if (row0 + rr + RP * p >= nrows) o = make_uint4(0, 0, 0, 0);
-      *(uint4*)(lds + L::off(rr + RP * p, c)) = o;
+      *(uint4*)&smem[b + L::off(row, c)] = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
+                                                       pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7]));
     }
   }
 };
 
 template <int ROWS, int BK, int MN, int BL, int NB>
 struct BLoaderOf;
+
+// LDS bytes of one packed-ring entry (0 unless the B operand is packed) and the
+// DMA instructions per wave per slab of a B loader (0 for the register path).
+template <int BL, int ROWS, int BK, int NB>
+struct RingBytes { static constexpr int BYTES = DmaRing<ROWS, BK, BL, NB>::P_BYTES; };
+template <int ROWS, int BK, int NB>
+struct RingBytes<kBf16, ROWS, BK, NB> { static constexpr int BYTES = 0; };
 template <int ROWS, int BK, int MN, int NB>
 struct BLoaderOf<ROWS, BK, MN, kBf16, NB> { using T = typename DmaTileOf<ROWS, BK, MN>::T; };
 template <int ROWS, int BK, int MN, int NB>
-struct BLoaderOf<ROWS, BK, MN, kFp32Quant, NB> { using T = LoadFp32Quant<ROWS, BK, kLdsSlots>; };
+struct BLoaderOf<ROWS, BK, MN, kFp32Quant, NB> { using T = DmaRing<ROWS, BK, kFp32Quant, NB>; };
 template <int ROWS, int BK, int MN, int NB>
-struct BLoaderOf<ROWS, BK, MN, kPacked, NB> { using T = LoadPacked<ROWS, BK, kLdsSlots, NB>; };
+struct BLoaderOf<ROWS, BK, MN, kPacked, NB> { using T = DmaRing<ROWS, BK, kPacked, NB>; };
 
 template <int BL, class Ld>
 __device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
   if constexpr (BL == kBf16) l.init((const uint16_t*)a.B, a.ldb, n0, a.N, a.K);
-  else if constexpr (BL == kFp32Quant) l.init((const float*)a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.Kq);
-  else l.init((const uint8_t*)a.B, a.ldb, n0, a.N, a.s, a.z, a.G);
+  else if constexpr (BL == kFp32Quant) l.init(a.B, a.ldb * 4, n0, a.N, a.s, a.z, a.G, a.Kq);
+  else l.init(a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.Kq);
 }
 
 // Four consecutive codes c0..c0+3 (c0 % 4 == 0) of a packed row.
@@ -406,7 +371,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
   constexpr int KS = BK / 32;                              // k-steps per slab
   constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+  // B operand modes: bf16 tiles by DMA with A; packed codes or the fp32
+  // master weight by DMA into a ring of their own one slab ahead of A,
+  // converted into the B stage two slabs ahead of the MFMAs.
+  constexpr bool B_BF16 = (BL == kBf16), B_RING = (BL != kBf16);
+  constexpr int P_STAGE = RingBytes<BL, BN, BK, NB>::BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + STAGES * P_STAGE];
+  constexpr int P0 = STAGES * STAGE;                       // byte offset of the packed ring
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
@@ -420,21 +391,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
   LB lb;
   la.init(a.A, a.lda, m0, a.M, a.K);
   init_b<BL>(lb, a, n0);
-  constexpr bool B_DMA = (BL == kBf16);
-  constexpr int NL = LA::NI + (B_DMA ? DmaTileOf<BN, BK, BMN>::T::NI : 0);
+  constexpr int NL = LA::NI + LB::NI;                     // DMA instructions per wave per slab
 
   const int nk = (a.K + BK - 1) / BK;
-  auto issue = [&](int slab) {               // DMA part of one slab
-    const int sl = slab < nk ? slab : nk - 1;
+  auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
+  // All DMA of one iteration: A (and bf16 B) of slab `slab`, ring weights of slab + 1.
+  auto issue = [&](int slab) {
     const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
-    la.issue(st, sl * BK);
-    if constexpr (B_DMA) lb.issue(st + A_BYTES, sl * BK);
+    la.issue(st, clamp_slab(slab) * BK);
+    if constexpr (B_BF16) lb.issue(st + A_BYTES, clamp_slab(slab) * BK);
+    if constexpr (B_RING) lb.issue(lds0 + P0 + (uint32_t)(((slab + 1) % STAGES) * P_STAGE),
+                                   clamp_slab(slab + 1) * BK);
   };
-  auto b_reg_issue = [&](int slab) {
-    if constexpr (!B_DMA) lb.issue((slab < nk ? slab : nk - 1) * BK);
-  };
-  auto b_reg_commit = [&](int slab) {
-    if constexpr (!B_DMA) lb.commit(&smem[(slab % STAGES) * STAGE + A_BYTES]);
+  auto b_commit = [&](int slab) {
+    if constexpr (B_RING) lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
   };
 
   // Fragment reads index the __shared__ array directly (stage given as a byte
@@ -461,16 +431,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
   };
 
   // prologue: slabs 0 .. STAGES-2 in flight, slab 0 certified, F[0] loaded.
-  if constexpr (!B_DMA) {
-    b_reg_issue(0);
-    b_reg_commit(0);
-    b_reg_issue(1);
-    b_reg_commit(1);
-  }
+  if constexpr (B_RING)
+    lb.issue(lds0 + P0, 0);                   // ring slab 0; issue(sl) brings slab sl + 1
 #pragma unroll
   for (int sl = 0; sl < STAGES - 1; ++sl) issue(sl);
-  wait_vmcnt<(STAGES - 2) * NL>();
-  __syncthreads();
+  if constexpr (B_RING) {
+    wait_vmcnt<0>();
+    __syncthreads();                          // ring slabs 0, 1 visible
+    b_commit(0);
+    b_commit(1);
+    __syncthreads();                          // their bf16 tiles visible
+  } else {
+    wait_vmcnt<(STAGES - 2) * NL>();
+    __syncthreads();
+  }
   Frags<TI, TJ> F[2];
   read_frags(0, 0, F[0]);
 
@@ -481,7 +455,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
     wait_vmcnt<(STAGES - 3) * NL>(); /* my DMAs for slabs <= KT+1 landed */ \
     __syncthreads();                 /* everyone's: slab KT+1 is visible */ \
     issue((KT) + STAGES - 1);                                               \
-    b_reg_issue((KT) + 2);                                                  \
     const int st_ = ((KT) % STAGES) * STAGE;                                \
     const int nx_ = (((KT) + 1) % STAGES) * STAGE;                          \
     if constexpr (KS == 1) {                                                \
@@ -493,7 +466,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
       read_frags(nx_, 0, CUR);                                              \
       mfmas(NXT);                                                           \
     }                                                                       \
-    b_reg_commit((KT) + 2);                                                 \
+    b_commit((KT) + 2);                                                     \
   } while (0)
 
   for (int kt = 0; kt < nk; kt += (KS == 1 && U2) ? 2 : 1) {
@@ -508,6 +481,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
   }
 #undef QAT_SLAB
   wait_vmcnt<0>();                            // drain the trailing re-issued DMAs
+  __syncthreads();
 
   // ------------------------------------------------------------------ epilogues
   const int rl = lane & 15, cq = 4 * (lane >> 4);

@@ -1,8 +1,9 @@
 // Optional per-kernel timing. While enabled, every kernel the library launches
-// is bracketed by a pair of HIP events recorded on the launch stream; the
-// report sums elapsed times per kernel label. Events are created only while
+// (or only those with the selected label) is bracketed by a pair of HIP events
+// recorded on the launch stream; the report sums elapsed times per label. Events are created only while
 // timing is on and are kept for reuse until the process ends.
 #include <atomic>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -22,6 +23,7 @@ struct Record {
 struct Timing {
   std::mutex mu;
   std::atomic<bool> on{false};
+  std::string only;                    // empty: every label
   std::vector<hipEvent_t> pool;        // free events
   std::vector<Record> records;
   struct Sum {
@@ -54,6 +56,7 @@ LaunchTimer::LaunchTimer(const char* label, hipStream_t st) : label_(label), str
   Timing& t = timing();
   if (!t.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> g(t.mu);
+  if (!t.only.empty() && t.only != label) return;
   start_ = take_event(t);
   stop_ = take_event(t);
   if (start_ && stop_) hipEventRecord((hipEvent_t)start_, st);
@@ -83,6 +86,13 @@ QAT_API int32_t qat_timing_enable(int32_t on) {
     t.sums.clear();
   }
   t.on.store(on != 0);
+  return QAT_OK;
+}
+
+QAT_API int32_t qat_timing_select(const char* label) {
+  qat::Timing& t = qat::timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.only = label ? label : "";
   return QAT_OK;
 }
 
