@@ -1,10 +1,8 @@
-// The MFMA GEMM kernel template of the group-wise fake-quant linear (gfx950).
+// The MFMA GEMM kernels of the group-wise fake-quant linear (gfx950).
 //
-// C[M, N] = sum_k A[m, k] * B[n, k]: both operands K-contiguous, bf16 in LDS,
-// fp32 accumulation in v_mfma_f32_16x16x32_bf16. A 256-thread workgroup
-// (4 wave64s, 2x2) owns a BM x BN tile; K advances in slabs of BK (32 or 64).
-// With BK = 64 a slab is exactly one quantisation group of a weight row, so a
-// fused B loader needs one (s, z) pair per row and slab.
+// C[M, N] = sum_k A[m, k] * B[n, k] in bf16 with fp32 accumulation in
+// v_mfma_f32_16x16x32_bf16. A 256-thread workgroup (4 wave64s, 2x2, one per
+// SIMD) owns a BM x BN tile; K advances in slabs of BK.
 //
 // The MFMA's first operand is the B fragment and its second the A fragment, so
 // the 16x16 result a lane holds is 4 consecutive output COLUMNS of one row:
@@ -13,12 +11,11 @@
 // quantisation group is 4 j-tiles x 4 registers of one lane plus a reduction
 // over the 4 lanes that share (lane & 15).
 //
-// LDS: per operand and stage a [rows][BK] bf16 slab; 16-byte chunk c of row r
-// sits at chunk position c ^ ((r / RPL) & (CH - 1)), which spreads the 16
-// rows that one fragment read touches over distinct bank slots. Two stages:
-// global loads for slab k+1 are issued at the top of slab k, fragments for the
-// next k-step are read while the current k-step's MFMAs run, and the next
-// slab is written to LDS during the last k-step.
+// LDS: per operand and stage a slab of the tile, filled by direct-to-LDS DMA.
+// K-contiguous tiles are [rows][BK] bf16 with 16-byte chunk c of row r at
+// position c ^ ((r / RPL) & (CH - 1)); MN-contiguous tiles are [BK][rows] read
+// with LDS transpose loads. Both spread a fragment read over distinct bank
+// slots.
 #pragma once
 #include "qat_device.h"
 #include "qat_internal.h"
@@ -133,6 +130,16 @@ struct DmaTileK {
 #pragma unroll
     for (int q = 0; q < NI; ++q) dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * 2);
   }
+  __device__ __forceinline__ void issue_q(uint32_t lds_tile, int k0, int q) const {
+    dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * 2);
+  }
+  // Per-lane byte offset of fragment 0 (tile rows r0 .. r0 + 15) for k-step ks.
+  // The swizzle term (row / RPL) & (CH - 1) repeats every 16 rows (RPL * CH
+  // divides 16), so fragment f of the same k-step sits f * 16 * PITCH further.
+  __device__ __forceinline__ static int frag_base(int r0, int ks, int lane) {
+    return L::off(r0 + (lane & 15), ks * 4 + (lane >> 4));
+  }
+  static constexpr int FRAG_STRIDE = 16 * L::PITCH;
   // Fragment of tile row r (= 16 t + (lane & 15)) for k-step ks: 8 consecutive k.
   __device__ __forceinline__ static bf16x8 frag(const uint8_t* tile, int r, int ks, int lane) {
     return *(const bf16x8*)(tile + L::off(r, ks * 4 + (lane >> 4)));
@@ -182,6 +189,9 @@ struct DmaTileMN {
   __device__ __forceinline__ void issue(uint32_t lds_tile, int k0) const {
 #pragma unroll
     for (int q = 0; q < NI; ++q) dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
+  }
+  __device__ __forceinline__ void issue_q(uint32_t lds_tile, int k0, int q) const {
+    dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
   }
   __device__ __forceinline__ static bf16x8 frag(const uint8_t* tile, int r, int ks, int lane) {
     const int j = lane & 15;
@@ -306,26 +316,9 @@ struct DmaRing {
   }
 };
 
-template <int ROWS, int BK, int MN, int BL, int NB>
-struct BLoaderOf;
-
-// LDS bytes of one packed-ring entry (0 unless the B operand is packed) and the
-// DMA instructions per wave per slab of a B loader (0 for the register path).
-template <int BL, int ROWS, int BK, int NB>
-struct RingBytes { static constexpr int BYTES = DmaRing<ROWS, BK, BL, NB>::P_BYTES; };
-template <int ROWS, int BK, int NB>
-struct RingBytes<kBf16, ROWS, BK, NB> { static constexpr int BYTES = 0; };
-template <int ROWS, int BK, int MN, int NB>
-struct BLoaderOf<ROWS, BK, MN, kBf16, NB> { using T = typename DmaTileOf<ROWS, BK, MN>::T; };
-template <int ROWS, int BK, int MN, int NB>
-struct BLoaderOf<ROWS, BK, MN, kFp32Quant, NB> { using T = DmaRing<ROWS, BK, kFp32Quant, NB>; };
-template <int ROWS, int BK, int MN, int NB>
-struct BLoaderOf<ROWS, BK, MN, kPacked, NB> { using T = DmaRing<ROWS, BK, kPacked, NB>; };
-
 template <int BL, class Ld>
 __device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
-  if constexpr (BL == kBf16) l.init((const uint16_t*)a.B, a.ldb, n0, a.N, a.K);
-  else if constexpr (BL == kFp32Quant) l.init(a.B, a.ldb * 4, n0, a.N, a.s, a.z, a.G, a.Kq);
+  if constexpr (BL == kFp32Quant) l.init(a.B, a.ldb * 4, n0, a.N, a.s, a.z, a.G, a.Kq);
   else l.init(a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.Kq);
 }
 
@@ -346,144 +339,36 @@ struct Frags {
   bf16x8 a[TI], b[TJ];
 };
 
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// v_mfma_f32_16x16x32_bf16 with the accumulator pinned to AGPRs: keeps the
+// register allocator from mixing accumulators and fragments in one class
+// (which spills at 128x128 accumulators per wave). The hazard recogniser does
+// not look inside the asm, so code that reads the accumulators afterwards
+// first waits out the MFMA latency (mfma_drain).
+__device__ __forceinline__ void mfma_acc(f32x4& c, const bf16x8& b, const bf16x8& a) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+}
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
-// The kernel. STAGES LDS stages (>= 3). With one k-step per slab (BK = 32)
-// U2 = 1 unrolls slabs in pairs so the two fragment sets alternate; U2 = 0
-// copies the next slab's fragments instead (fewer live registers).
-// Invariant at the top of slab kt: slabs
-// <= kt are visible to every wave and F[0] holds the first k-step's fragments
-// of slab kt. The barrier in slab kt certifies slab kt + 1, so the fragments of
-// the next slab are read while the current slab's MFMAs run, and the DMA for
-// slab kt + STAGES - 1 goes into the stage slab kt - 1 has just released.
-// The last slabs re-issue the final slab into idle stages so that the vmcnt
-// bookkeeping is the same on every iteration; nothing reads those copies.
+// Epilogues. acc[j][i] holds C[m0 + wm0 + 16 i + (lane & 15)][n0 + wn0 + 16 j
+// + 4 (lane >> 4) + r], r = 0..3.
+//   kStoreBf16:    C (bf16) = acc.
+//   kSteGrads:     rows are weight rows o (A = dY^T), columns inputs c (B =
+//                  X^T); Gw = acc. dW = Gw * m and the group sums of ds, dz of
+//                  the straight-through estimator, from W, s, z re-quantised
+//                  here (quant_elem).
+//   kE2eScaleGrad: as above with packed codes: ds = sum Gw (q - z), dz = -s
+//                  sum Gw.
+// A 64-column quantisation group is 4 j-tiles x 4 registers of one lane plus a
+// reduction over the 4 lanes that share (lane & 15).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int U2, int AMN, int BMN, int BL, int EP, int NB>
-__global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
-  using L = LdsLayout<BK, kLdsSlots>;
-  using LA = typename DmaTileOf<BM, BK, AMN>::T;
-  using LB = typename BLoaderOf<BN, BK, BMN, BL, NB>::T;
-  using FB = typename DmaTileOf<BN, BK, (BL == kBf16) ? BMN : 0>::T;   // B fragment reader
-  static_assert(BL == kBf16 || BMN == 0, "fused loaders produce K-contiguous tiles");
-  static_assert(STAGES >= 3, "the shifted pipeline needs three stages");
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TI = WM / 16, TJ = WN / 16;
-  constexpr int KS = BK / 32;                              // k-steps per slab
-  constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  // B operand modes: bf16 tiles by DMA with A; packed codes or the fp32
-  // master weight by DMA into a ring of their own one slab ahead of A,
-  // converted into the B stage two slabs ahead of the MFMAs.
-  constexpr bool B_BF16 = (BL == kBf16), B_RING = (BL != kBf16);
-  constexpr int P_STAGE = RingBytes<BL, BN, BK, NB>::BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + STAGES * P_STAGE];
-  constexpr int P0 = STAGES * STAGE;                       // byte offset of the packed ring
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const uint32_t lds0 = lds_addr_of(smem);
-
-  LA la;
-  LB lb;
-  la.init(a.A, a.lda, m0, a.M, a.K);
-  init_b<BL>(lb, a, n0);
-  constexpr int NL = LA::NI + LB::NI;                     // DMA instructions per wave per slab
-
-  const int nk = (a.K + BK - 1) / BK;
-  auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
-  // All DMA of one iteration: A (and bf16 B) of slab `slab`, ring weights of slab + 1.
-  auto issue = [&](int slab) {
-    const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
-    la.issue(st, clamp_slab(slab) * BK);
-    if constexpr (B_BF16) lb.issue(st + A_BYTES, clamp_slab(slab) * BK);
-    if constexpr (B_RING) lb.issue(lds0 + P0 + (uint32_t)(((slab + 1) % STAGES) * P_STAGE),
-                                   clamp_slab(slab + 1) * BK);
-  };
-  auto b_commit = [&](int slab) {
-    if constexpr (B_RING) lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
-  };
-
-  // Fragment reads index the __shared__ array directly (stage given as a byte
-  // offset) so that they stay ds_read instructions.
-  auto read_frags = [&](int st, int ks, Frags<TI, TJ>& f) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) f.a[i] = LA::frag(&smem[st], wm0 + i * 16 + (lane & 15), ks, lane);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) f.b[j] = FB::frag(&smem[st + A_BYTES], wn0 + j * 16 + (lane & 15), ks, lane);
-  };
-
-  f32x4 acc[TJ][TI];
-#pragma unroll
-  for (int j = 0; j < TJ; ++j)
-#pragma unroll
-    for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto mfmas = [&](const Frags<TI, TJ>& f) {
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
-  };
-
-  // prologue: slabs 0 .. STAGES-2 in flight, slab 0 certified, F[0] loaded.
-  if constexpr (B_RING)
-    lb.issue(lds0 + P0, 0);                   // ring slab 0; issue(sl) brings slab sl + 1
-#pragma unroll
-  for (int sl = 0; sl < STAGES - 1; ++sl) issue(sl);
-  if constexpr (B_RING) {
-    wait_vmcnt<0>();
-    __syncthreads();                          // ring slabs 0, 1 visible
-    b_commit(0);
-    b_commit(1);
-    __syncthreads();                          // their bf16 tiles visible
-  } else {
-    wait_vmcnt<(STAGES - 2) * NL>();
-    __syncthreads();
-  }
-  Frags<TI, TJ> F[2];
-  read_frags(0, 0, F[0]);
-
-  // One slab: CUR holds its first k-step's fragments on entry, and the next
-  // slab's first fragments are in CUR (two k-steps) or NXT (one k-step) on exit.
-#define QAT_SLAB(KT, CUR, NXT)                                              \
-  do {                                                                      \
-    wait_vmcnt<(STAGES - 3) * NL>(); /* my DMAs for slabs <= KT+1 landed */ \
-    __syncthreads();                 /* everyone's: slab KT+1 is visible */ \
-    issue((KT) + STAGES - 1);                                               \
-    const int st_ = ((KT) % STAGES) * STAGE;                                \
-    const int nx_ = (((KT) + 1) % STAGES) * STAGE;                          \
-    if constexpr (KS == 1) {                                                \
-      read_frags(nx_, 0, NXT);                                              \
-      mfmas(CUR);                                                           \
-    } else {                                                                \
-      read_frags(st_, 1, NXT);                                              \
-      mfmas(CUR);                                                           \
-      read_frags(nx_, 0, CUR);                                              \
-      mfmas(NXT);                                                           \
-    }                                                                       \
-    b_commit((KT) + 2);                                                     \
-  } while (0)
-
-  for (int kt = 0; kt < nk; kt += (KS == 1 && U2) ? 2 : 1) {
-    QAT_SLAB(kt, F[0], F[1]);
-    if constexpr (KS == 1) {
-      if constexpr (U2) {
-        if (kt + 1 < nk) QAT_SLAB(kt + 1, F[1], F[0]);
-      } else {
-        F[0] = F[1];
-      }
-    }
-  }
-#undef QAT_SLAB
-  wait_vmcnt<0>();                            // drain the trailing re-issued DMAs
-  __syncthreads();
-
-  // ------------------------------------------------------------------ epilogues
+template <int EP, int NB, int TI, int TJ, int WN>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
+                                              int wm0, int wn0, int lane) {
   const int rl = lane & 15, cq = 4 * (lane >> 4);
   if constexpr (EP == kStoreBf16) {
 #pragma unroll
@@ -560,6 +445,264 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM kernel for bf16 operands. A 256-thread workgroup (4 wave64s, 2x2,
+// one per SIMD) owns a BM x BN tile; K advances in slabs of BK = 64, two
+// k-steps of 32 each. Operand tiles reach LDS by DMA (AMN / BMN select the
+// K- or MN-contiguous loader).
+//
+// Stage discipline: slab m lives in stage m % STAGES. Barrier B_kt sits
+// between slab kt's two k-steps; before it each wave waits for its own DMA of
+// slab kt + 1, so B_kt certifies slab kt + 1 for everyone. By B_kt every wave
+// has also read all of slab kt's fragments into registers (k-step 0 during
+// slab kt - 1, k-step 1 during slab kt's first k-step), so after B_kt the DMA
+// for slab kt + STAGES may overwrite slab kt's stage: STAGES - 1 slabs of
+// latency cover every load, and two stages already suffice. Slabs beyond the
+// last re-load the last slab into free stages, keeping the vmcnt arithmetic
+// uniform; nothing reads those copies.
+//
+// Schedule: every MFMA is followed by (at most) one fragment read for the next
+// k-step and a share of the slab's DMA instructions, fenced so the compiler
+// keeps that order: LDS reads run a full k-step ahead of their MFMAs and the
+// DMA issue is spread over the k-step.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int STAGES, int AMN, int BMN, int EP, int NB>
+__global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
+  using LA = typename DmaTileOf<BM, BK, AMN>::T;
+  using LB = typename DmaTileOf<BN, BK, BMN>::T;
+  static_assert(BK == 64, "two k-steps per slab");
+  static_assert(STAGES >= 2, "two stages at least");
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int NM = TI * TJ, NR = TI + TJ;
+  constexpr int NLA = LA::NI, NL = LA::NI + LB::NI;      // DMA instructions per wave per slab
+  constexpr int GAP = NM / NL > 0 ? NM / NL : 1;
+  static_assert(NR <= NM && NL * GAP <= NM, "one k-step must cover the reads and the DMA");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t lds0 = lds_addr_of(smem);
+
+  LA la;
+  LB lb;
+  la.init(a.A, a.lda, m0, a.M, a.K);
+  lb.init((const uint16_t*)a.B, a.ldb, n0, a.N, a.K);
+  const int nk = (a.K + BK - 1) / BK;
+
+  auto dma_q = [&](int slab, int q) {                    // DMA instruction q of slab `slab`
+    const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
+    const int k0 = (slab < nk ? slab : nk - 1) * BK;
+    if (q < NLA) la.issue_q(st, k0, q);
+    else lb.issue_q(st + A_BYTES, k0, q - NLA);
+  };
+
+  // Fragment reads. K-contiguous tiles: lane base per k-step + immediate
+  // offsets; MN-contiguous tiles: transpose reads with per-fragment addresses.
+  int a_base[2] = {0, 0}, b_base[2] = {0, 0};
+  if constexpr (AMN == kKContig) {
+    a_base[0] = LA::frag_base(wm0, 0, lane);
+    a_base[1] = LA::frag_base(wm0, 1, lane);
+  }
+  if constexpr (BMN == kKContig) {
+    b_base[0] = A_BYTES + LB::frag_base(wn0, 0, lane);
+    b_base[1] = A_BYTES + LB::frag_base(wn0, 1, lane);
+  }
+  auto read_a = [&](int st, int ks, int i) -> bf16x8 {
+    if constexpr (AMN == kKContig) return *(const bf16x8*)&smem[st + a_base[ks] + i * LA::FRAG_STRIDE];
+    else return LA::frag(&smem[st], wm0 + i * 16 + (lane & 15), ks, lane);
+  };
+  auto read_b = [&](int st, int ks, int j) -> bf16x8 {
+    if constexpr (BMN == kKContig) return *(const bf16x8*)&smem[st + b_base[ks] + j * LB::FRAG_STRIDE];
+    else return LB::frag(&smem[st + A_BYTES], wn0 + j * 16 + (lane & 15), ks, lane);
+  };
+  // read r of a k-step, in the order the MFMAs consume them: b0, a0 .. a(TI-1), b1 .. b(TJ-1)
+  auto read_r = [&](int st, int ks, int r, Frags<TI, TJ>& f) {
+    if (r == 0) f.b[0] = read_b(st, ks, 0);
+    else if (r <= TI) f.a[r - 1] = read_a(st, ks, r - 1);
+    else f.b[r - TI] = read_b(st, ks, r - TI);
+  };
+
+  f32x4 acc[TJ][TI];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One k-step: MFMA t on `cur`, then read t of the next k-step (stage nst,
+  // k-step nks) into `nxt` and, every GAP MFMAs, one DMA instruction of slab
+  // dslab (none if dslab < 0).
+  auto kstep = [&](const Frags<TI, TJ>& cur, int nst, int nks, Frags<TI, TJ>& nxt, int dslab) {
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      const int j = t / TI, i = t % TI;
+      mfma_acc(acc[j][i], cur.b[j], cur.a[i]);
+      if (t < NR) read_r(nst, nks, t, nxt);
+      if (dslab >= 0 && t % GAP == GAP - 1 && t / GAP < NL) dma_q(dslab, t / GAP);
+      sched_fence();
+    }
+  };
+
+  // prologue: slabs 0 .. STAGES-1 in flight; slab 0 visible; F0 = slab 0, k-step 0
+#pragma unroll
+  for (int sl = 0; sl < STAGES; ++sl)
+#pragma unroll
+    for (int q = 0; q < NL; ++q) dma_q(sl, q);
+  wait_vmcnt<(STAGES - 1) * NL>();
+  __syncthreads();
+  Frags<TI, TJ> F0, F1;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) read_r(0, 0, r, F0);
+  sched_fence();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = (kt % STAGES) * STAGE, nx = ((kt + 1) % STAGES) * STAGE;
+    kstep(F0, st, 1, F1, -1);                            // k-step 0; read k-step 1
+    wait_vmcnt<(STAGES - 2) * NL>();
+    __syncthreads();                                     // B_kt
+    sched_fence();
+    kstep(F1, nx, 0, F0, kt + STAGES);                   // k-step 1; read slab kt+1; DMA
+  }
+  wait_vmcnt<0>();                                       // drain the trailing re-loads
+  __syncthreads();
+  mfma_drain();
+  gemm_epilogue<EP, NB, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM with a fused B operand (packed codes or the fp32 master weight through
+// an LDS ring, see DmaRing) and a K-contiguous bf16 A; bf16 output. STAGES
+// LDS stages (>= 3). With one k-step per slab (BK = 32) U2 = 1 unrolls slabs
+// in pairs so the two fragment sets alternate; U2 = 0 copies the next slab's
+// fragments instead (fewer live registers).
+// Invariant at the top of slab kt: slabs <= kt are visible to every wave and
+// F[0] holds the first k-step's fragments of slab kt. The barrier in slab kt
+// certifies slab kt + 1, so the fragments of the next slab are read while the
+// current slab's MFMAs run, and the DMA for slab kt + STAGES - 1 goes into the
+// stage slab kt - 1 has just released. The ring runs one slab ahead of A and
+// is converted into the bf16 B stage two slabs ahead of the MFMAs.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int STAGES, int U2, int BL, int NB>
+__global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
+  using L = LdsLayout<BK, kLdsSlots>;
+  using LA = DmaTileK<BM, BK, kLdsSlots>;
+  using LB = DmaRing<BN, BK, BL, NB>;
+  using FB = DmaTileK<BN, BK, kLdsSlots>;                 // B fragment reader
+  static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
+  static_assert(STAGES >= 3, "the shifted pipeline needs three stages");
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int KS = BK / 32;                              // k-steps per slab
+  constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int P_STAGE = LB::P_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + STAGES * P_STAGE];
+  constexpr int P0 = STAGES * STAGE;                       // byte offset of the ring
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t lds0 = lds_addr_of(smem);
+
+  LA la;
+  LB lb;
+  la.init(a.A, a.lda, m0, a.M, a.K);
+  init_b<BL>(lb, a, n0);
+  constexpr int NL = LA::NI + LB::NI;                     // DMA instructions per wave per slab
+
+  const int nk = (a.K + BK - 1) / BK;
+  auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
+  // All DMA of one iteration: A of slab `slab`, ring weights of slab + 1.
+  auto issue = [&](int slab) {
+    const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
+    la.issue(st, clamp_slab(slab) * BK);
+    lb.issue(lds0 + P0 + (uint32_t)(((slab + 1) % STAGES) * P_STAGE), clamp_slab(slab + 1) * BK);
+  };
+  auto b_commit = [&](int slab) {
+    lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
+  };
+
+  // Fragment reads index the __shared__ array directly (stage given as a byte
+  // offset) so that they stay ds_read instructions.
+  auto read_frags = [&](int st, int ks, Frags<TI, TJ>& f) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) f.a[i] = LA::frag(&smem[st], wm0 + i * 16 + (lane & 15), ks, lane);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) f.b[j] = FB::frag(&smem[st + A_BYTES], wn0 + j * 16 + (lane & 15), ks, lane);
+  };
+
+  f32x4 acc[TJ][TI];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfmas = [&](const Frags<TI, TJ>& f) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+  };
+
+  // prologue: ring slabs 0, 1 converted, A slabs 0 .. STAGES-2 in flight, F[0] loaded.
+  lb.issue(lds0 + P0, 0);                     // ring slab 0; issue(sl) brings slab sl + 1
+#pragma unroll
+  for (int sl = 0; sl < STAGES - 1; ++sl) issue(sl);
+  wait_vmcnt<0>();
+  __syncthreads();                            // ring slabs 0, 1 visible
+  b_commit(0);
+  b_commit(1);
+  __syncthreads();                            // their bf16 tiles visible
+  Frags<TI, TJ> F[2];
+  read_frags(0, 0, F[0]);
+
+  // One slab: CUR holds its first k-step's fragments on entry, and the next
+  // slab's first fragments are in CUR (two k-steps) or NXT (one k-step) on exit.
+#define QAT_SLAB(KT, CUR, NXT)                                              \
+  do {                                                                      \
+    wait_vmcnt<(STAGES - 3) * NL>(); /* my DMAs for slabs <= KT+1 landed */ \
+    __syncthreads();                 /* everyone's: slab KT+1 is visible */ \
+    issue((KT) + STAGES - 1);                                               \
+    const int st_ = ((KT) % STAGES) * STAGE;                                \
+    const int nx_ = (((KT) + 1) % STAGES) * STAGE;                          \
+    if constexpr (KS == 1) {                                                \
+      read_frags(nx_, 0, NXT);                                              \
+      mfmas(CUR);                                                           \
+    } else {                                                                \
+      read_frags(st_, 1, NXT);                                              \
+      mfmas(CUR);                                                           \
+      read_frags(nx_, 0, CUR);                                              \
+      mfmas(NXT);                                                           \
+    }                                                                       \
+    b_commit((KT) + 2);                                                     \
+  } while (0)
+
+  for (int kt = 0; kt < nk; kt += (KS == 1 && U2) ? 2 : 1) {
+    QAT_SLAB(kt, F[0], F[1]);
+    if constexpr (KS == 1) {
+      if constexpr (U2) {
+        if (kt + 1 < nk) QAT_SLAB(kt + 1, F[1], F[0]);
+      } else {
+        F[0] = F[1];
+      }
+    }
+  }
+#undef QAT_SLAB
+  wait_vmcnt<0>();                            // drain the trailing re-issued DMAs
+  __syncthreads();
+  gemm_epilogue<kStoreBf16, NB, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
 }
 
 }  // namespace qat

@@ -24,12 +24,14 @@ import sys
 
 # rocprofv3 kernel symbol -> the label the library's own timing uses
 LABELS = [
-    (r"k_gemm<[^>]*,\s*0,\s*1,\s*0,\s*0,\s*0>", "gemm_dx"),
-    (r"k_gemm<[^>]*,\s*1,\s*1,\s*0,\s*1,\s*0>", "gemm_ste_grads"),
-    (r"k_gemm<[^>]*,\s*1,\s*1,\s*0,\s*2,\s*\d>", "gemm_e2e_grads"),
-    (r"k_gemm<[^>]*,\s*0,\s*0,\s*1,\s*0,\s*0>", "gemm_fwd_fused_fp32"),
-    (r"k_gemm<[^>]*,\s*0,\s*0,\s*2,\s*0,\s*\d>", "gemm_fwd_packed"),
-    (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
+    # k_gemm<BM, BN, BK, STAGES, AMN, BMN, EP, NB>
+    (r"k_gemm<[^>]*,\s*0,\s*1,\s*0,\s*0>", "gemm_dx"),
+    (r"k_gemm<[^>]*,\s*1,\s*1,\s*1,\s*0>", "gemm_ste_grads"),
+    (r"k_gemm<[^>]*,\s*1,\s*1,\s*2,\s*\d>", "gemm_e2e_grads"),
+    (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
+    # k_gemm_fused<BM, BN, BK, STAGES, U2, BL, NB>
+    (r"k_gemm_fused<[^>]*,\s*1,\s*0>", "gemm_fwd_fused_fp32"),
+    (r"k_gemm_fused<[^>]*,\s*2,\s*\d>", "gemm_fwd_packed"),
     (r"k_init_minmax", "init_minmax"),
     (r"k_quant_codes", "quant_w_hat"),
     (r"k_pack<", "pack"),
