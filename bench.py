@@ -71,11 +71,11 @@ def work_per_launch(label, M, out, inp, bits):
         return "mfma", 2.0 * M * inp * out
     if label == "init_minmax":
         return "hbm", n * 4 + 2 * out * G * 4
-    if label == "quant_w_hat":
+    if label in ("quant_w_hat", "quant_w_hat_t"):
         return "hbm", n * (4 + 2) + 2 * out * G * 4
     if label == "pack":
         return "hbm", n * (4 + bits / 8) + 3 * out * G * 4
-    if label == "dequant":
+    if label in ("dequant", "dequant_t"):
         return "hbm", n * (bits / 8 + 2) + 2 * out * G * 4
     return "hbm", float("nan")
 

@@ -120,7 +120,8 @@ int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float*
  *   dz[o,j] = -s[o,j] * sum_{i in j, m_i = 0} Gw[o,i]  [out, G] fp32
  * Any of dX, dW, ds, dz may be NULL to skip it (ds and dz come together: both
  * NULL or both set). When dX is wanted, ws (>= qat_fakequant_ws_bytes(M, out,
- * in) bytes, scratch) receives the bf16 W_hat; otherwise ws may be NULL. dY and
+ * in) bytes, scratch) receives the bf16 W_hat transposed, [in][out], so that
+ * the dX GEMM reads both operands K-contiguous; otherwise ws may be NULL. dY and
  * X are read in place (the dW GEMM contracts over tokens reading both with
  * LDS transpose loads), so no transposed copies are made.
  */
@@ -162,7 +163,8 @@ int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* 
  *   dz[o,j] = -s[o,j] * sum_{i in j} Gw[o,i]  (the train-s-and-z variant of the
  *   Paper-Notes ablation table; may be NULL).
  * When dX is wanted, ws (>= qat_dequant_ws_bytes(M, out, in) bytes, scratch)
- * receives the dequantised bf16 W_hat; otherwise ws may be NULL.
+ * receives the dequantised bf16 W_hat transposed, [in][out]; otherwise ws may
+ * be NULL.
  */
 int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint8_t* Wq,
                                const float* s, const float* z, int64_t M, int64_t out, int64_t in,

@@ -199,6 +199,36 @@ def test_fused_forward_near_tie_fallback():
     assert rel_fro(O.bf16_bits_to_f64(host_bits(Y2)), O.fakequant_fwd(X, W, s, z, bits)) < TOL_BF16
 
 
+def test_ste_backward_near_tie_mask_exact():
+    # Weights on and one ulp beside rounding ties, with zero points that push
+    # codes past both ends, through the backward epilogue: its clamp mask (the
+    # zero pattern of dW) must be exactly the oracle's fp32-quotient decision.
+    say("bwd near-tie")
+    M, out, inp, bits = 96, 128, 256, 2
+    g = np.random.default_rng(9)
+    s = g.uniform(0.01, 0.02, (out, inp // 64)).astype(np.float32)
+    z = g.integers(0, 4, (out, inp // 64)).astype(np.float32)
+    half = g.integers(-4, 5, (out, inp)) + 0.5
+    W = (half * np.repeat(s, 64, 1)).astype(np.float32)
+    W[:, ::3] = np.nextafter(W[:, ::3], np.float32(np.inf))
+    W[:, 1::3] = np.nextafter(W[:, 1::3], np.float32(-np.inf))
+    X = synth.activations(41, 0, M, inp)
+    dY = synth.grad_out(41, 0, M, out)
+    gW = torch.empty(out, inp, device="cuda")
+    gs = torch.empty(out, inp // 64, device="cuda")
+    gz = torch.empty_like(gs)
+    Q.qat_fakequant_linear_bwd(dev_bf16(dY), dev_bf16(X), dev_f32(W), dev_f32(s), dev_f32(z), bits,
+                               dW=gW, ds=gs, dz=gz)
+    torch.cuda.synchronize()
+    m = O.quantize(W, s, z, bits)["m"]
+    r = O.fakequant_bwd(dY, X, W, s, z, bits)
+    assert 0.05 < m.mean() < 0.95
+    assert np.array_equal(gW.cpu().numpy() != 0, m & (r["Gw"] != 0))
+    assert rel_fro(gW.cpu().numpy(), r["dW"]) < TOL_F32
+    assert rel_fro(gs.cpu().numpy(), r["ds"]) < TOL_F32
+    assert rel_fro(gz.cpu().numpy(), r["dz"]) < TOL_F32
+
+
 def test_bwd_optional_outputs():
     say("bwd optional outputs")
     M, out, inp, bits = 96, 192, 256, 3

@@ -197,14 +197,15 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
   return finish();
 }
 
-// dX = dY W_hat with W_hat [out][in] bf16 read in place.
-static void launch_dx(const uint16_t* dY, const uint16_t* w_hat, int64_t M, int64_t out, int64_t in,
+// dX = dY W_hat with W_hat^T [in][out] bf16 staged in the workspace: both
+// operands K-contiguous (K = out).
+static void launch_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, int64_t out, int64_t in,
                       uint16_t* dX, hipStream_t stream) {
   qat::GemmArgs a = gemm_args();
   a.A = dY;
   a.lda = out;
-  a.B = w_hat;
-  a.ldb = in;
+  a.B = w_hat_t;
+  a.ldb = out;
   a.M = (int)M;
   a.N = (int)in;
   a.K = (int)out;
@@ -252,7 +253,7 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
 
   if (dX) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_quant_codes(W, s, z, out, in, bits, nullptr, w_hat, stream);
+    qat::launch_w_hat_t(W, s, z, out, in, bits, w_hat, stream);
     launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
   if (dW || ds) {
@@ -326,7 +327,7 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
 
   if (dX) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_dequant(Wq, s, z, out, in, bits, w_hat, stream);
+    qat::launch_dequant_t(Wq, s, z, out, in, bits, w_hat, stream);
     launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
   qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, bits);

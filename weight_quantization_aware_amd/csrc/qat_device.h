@@ -79,6 +79,27 @@ __device__ __forceinline__ QElem quant_elem(float w, float s, float zr, float K)
   return e;
 }
 
+// quant_elem with the quotient from a reciprocal: u0 = w * r (r = fl32(1/s)),
+// refined by one residual step u = u0 + (w - u0 s) r (the residual is exact
+// with an FMA), which lands within an ulp of fl32(w / s). The code decision
+// rint(u) can only differ from the one of the correctly rounded quotient when
+// u is within a few ulps of a half-integer; there the element is redone with
+// the division, so q, m and w_hat are exactly quant_elem's and u is within an
+// ulp of it.
+__device__ __forceinline__ QElem quant_elem_rcp(float w, float s, float r, float zr, float K) {
+  const float u0 = w * r;
+  const float u = __builtin_fmaf(__builtin_fmaf(-u0, s, w), r, u0);
+  const float fr = u - __builtin_floorf(u);
+  if (__builtin_fabsf(fr - 0.5f) <= __builtin_fabsf(u) * 0x1p-20f + 0x1p-60f) return quant_elem(w, s, zr, K);
+  QElem e;
+  e.u = u;
+  const float v = __builtin_rintf(u) + zr;
+  e.m = (v >= 0.0f) && (v <= K);
+  e.q = fminf(fmaxf(v, 0.0f), K);
+  e.w_hat = (e.q - zr) * s;
+  return e;
+}
+
 __device__ __forceinline__ float round_clamp_zero(float z, float K) {
   return fminf(fmaxf(__builtin_rintf(z), 0.0f), K);
 }

@@ -18,35 +18,28 @@ __global__ __launch_bounds__(256) void k_init_minmax(const float4* __restrict__ 
                                                      float* __restrict__ z) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t base_vec = wave * 256;            // 256 float4 = 16 groups per wave
   const int64_t nvec = ngroups * 16;
+  // Groups never straddle the end (in % 64 == 0): a window past the end holds
+  // whole groups that are not stored, so its zero fill is never used.
   float4 v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int64_t idx = base_vec + j * 64 + lane;
-    if (idx < nvec) v[j] = W[idx];
-    else v[j] = make_float4(__builtin_inff(), __builtin_inff(), __builtin_inff(), __builtin_inff());
+    const int64_t idx = wave * 256 + j * 64 + lane;
+    v[j] = idx < nvec ? W[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float mn[4], mx[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int64_t idx = base_vec + j * 64 + lane;
-    bool ok = idx < nvec;
-    float a = fminf(fminf(v[j].x, v[j].y), fminf(v[j].z, v[j].w));
-    float b = fmaxf(fmaxf(v[j].x, v[j].y), fmaxf(v[j].z, v[j].w));
-    mn[j] = row16_min(a);
-    mx[j] = row16_max(ok ? b : -__builtin_inff());
+    mn[j] = row16_min(fminf(fminf(v[j].x, v[j].y), fminf(v[j].z, v[j].w)));
+    mx[j] = row16_max(fmaxf(fmaxf(v[j].x, v[j].y), fmaxf(v[j].z, v[j].w)));
   }
   const int sel = lane & 15;
   if (sel < 4) {
-    float a = mn[0], b = mx[0];
-    if (sel == 1) { a = mn[1]; b = mx[1]; }
-    if (sel == 2) { a = mn[2]; b = mx[2]; }
-    if (sel == 3) { a = mn[3]; b = mx[3]; }
-    int64_t g = wave * 16 + sel * 4 + (lane >> 4);
+    const float a = sel == 0 ? mn[0] : sel == 1 ? mn[1] : sel == 2 ? mn[2] : mn[3];
+    const float b = sel == 0 ? mx[0] : sel == 1 ? mx[1] : sel == 2 ? mx[2] : mx[3];
+    const int64_t g = wave * 16 + sel * 4 + (lane >> 4);
     if (g < ngroups) {
-      float d = b - a;
-      float sv = fmaxf(d / K, kSMin);
+      const float sv = fmaxf((b - a) / K, kSMin);
       s[g] = sv;
       z[g] = __builtin_rintf(-a / sv);
     }
@@ -133,6 +126,72 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ Wq,
 }
 
 // ---------------------------------------------------------------------------
+// W_hat^T staging for the backward dX GEMM: the bf16 W_hat of a7 (fp32 master
+// weight, SRC = 0: Eq. 1-2 with zr = clamp(rint(z), 0, K)) or of a9 (packed
+// N-bit codes, SRC = 1: (q - z) * s) written transposed, [in][out], so that
+// dX = dY W_hat contracts two K-contiguous operands. A workgroup transposes a
+// 128 (out) x 64 (in) tile through LDS: every thread quantises two rows x 8
+// columns per item (rows read 256 or N*8 bytes contiguous per 8 lanes), stores
+// the row pairs as 4-byte words of the transposed tile, and the tile leaves as
+// 256-byte rows of W_hat^T. out % 64 == 0 and in % 64 == 0.
+// ---------------------------------------------------------------------------
+template <int SRC, int N>
+__global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, const float* __restrict__ s,
+                                                 const float* __restrict__ z, int64_t out, int64_t in, float K,
+                                                 uint16_t* __restrict__ w_hat_t) {
+  constexpr int TO = 128, TIN = 64, P = TO + 8;          // tile rows (out), cols (in), LDS pitch (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t T[TIN * P];
+  const int bo = SRC == 1 ? blockIdx.x : blockIdx.y, bi = SRC == 1 ? blockIdx.y : blockIdx.x;
+  const int64_t o0 = (int64_t)bo * TO, i0 = (int64_t)bi * TIN;
+  const int64_t G = in / kGroup, g = i0 / kGroup;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int item = threadIdx.x + 256 * q;
+    const int rp = item >> 3, co = item & 7;            // row pair, column octet
+    const int64_t o = o0 + 2 * rp;
+    float h[2][8];
+    if (o < out) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float sv = s[(o + r) * G + g];
+        if constexpr (SRC == 0) {
+          const float zr = round_clamp_zero(z[(o + r) * G + g], K);
+          const float4* src = (const float4*)((const float*)Wsrc + (o + r) * in + i0 + co * 8);
+          const float4 w0 = src[0], w1 = src[1];
+          const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) h[r][k] = quant_elem(w[k], sv, zr, K).w_hat;
+        } else {
+          const float zv = z[(o + r) * G + g];
+          const uint8_t* src = (const uint8_t*)Wsrc + (o + r) * (in * N / 8) + (i0 + co * 8) * N / 8;
+          uint32_t word;
+          if constexpr (N == 2) word = *(const uint16_t*)src;
+          else if constexpr (N == 4) word = *(const uint32_t*)src;
+          else word = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) h[r][k] = ((float)((word >> (N * k)) & ((1u << N) - 1)) - zv) * sv;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[r][k] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) *(uint32_t*)&T[(co * 8 + k) * P + 2 * rp] = pack_bf16x2(h[0][k], h[1][k]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = threadIdx.x + 256 * q;
+    const int row = idx >> 4, ch = idx & 15;            // row of W_hat^T in the tile, 8-element chunk
+    const int64_t oc = o0 + ch * 8;
+    if (oc < out) *(uint4*)(w_hat_t + (i0 + row) * out + oc) = *(const uint4*)&T[row * P + ch * 8];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
@@ -175,6 +234,24 @@ void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t o
   if (bits == 2) hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
   else if (bits == 3) hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
   else hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
+}
+
+void launch_w_hat_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
+                    uint16_t* w_hat_t, hipStream_t st) {
+  const dim3 grid((unsigned)(in / 64), (unsigned)((out + 127) / 128));
+  LaunchTimer t("quant_w_hat_t", st);
+  hipLaunchKernelGGL((k_w_hat_t<0, 0>), grid, dim3(256), 0, st, W, s, z, out, in, (float)((1 << bits) - 1),
+                     w_hat_t);
+}
+
+void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
+                      uint16_t* w_hat_t, hipStream_t st) {
+  const dim3 grid((unsigned)((out + 127) / 128), (unsigned)(in / 64));
+  const float K = (float)((1 << bits) - 1);
+  LaunchTimer t("dequant_t", st);
+  if (bits == 2) hipLaunchKernelGGL((k_w_hat_t<1, 2>), grid, dim3(256), 0, st, Wq, s, z, out, in, K, w_hat_t);
+  else if (bits == 3) hipLaunchKernelGGL((k_w_hat_t<1, 3>), grid, dim3(256), 0, st, Wq, s, z, out, in, K, w_hat_t);
+  else hipLaunchKernelGGL((k_w_hat_t<1, 4>), grid, dim3(256), 0, st, Wq, s, z, out, in, K, w_hat_t);
 }
 
 }  // namespace qat

@@ -19,25 +19,28 @@ int64_t tiles(const GemmArgs& a, int bm, int bn) {
   return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
-template <int BL, int EP>
-constexpr const char* gemm_label(bool mn_b) {
+// With the bf16-store epilogue the NB template argument only tags the launch:
+// 0 the forward, 1 the dX GEMM (same code, distinct kernel symbols so that
+// profiles can tell them apart).
+template <int BL, int EP, int NB>
+constexpr const char* gemm_label() {
   if (EP == kSteGrads) return "gemm_ste_grads";
   if (EP == kE2eScaleGrad) return "gemm_e2e_grads";
   if (BL == kFp32Quant) return "gemm_fwd_fused_fp32";
   if (BL == kPacked) return "gemm_fwd_packed";
-  return mn_b ? "gemm_dx" : "gemm_fwd";
+  return NB == 1 ? "gemm_dx" : "gemm_fwd";
 }
 
 template <int BM, int BN, int S, int AMN, int BMN, int EP, int NB>
 void launch_bf16(const GemmArgs& a, hipStream_t st) {
-  LaunchTimer t(gemm_label<kBf16, EP>(BMN == kMNContig), st);
+  LaunchTimer t(gemm_label<kBf16, EP, NB>(), st);
   hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, AMN, BMN, EP, NB>), dim3((unsigned)tiles(a, BM, BN)), dim3(256), 0,
                      st, a);
 }
 
 template <int BM, int BN, int BK, int S, int BL, int NB>
 void launch_fused(const GemmArgs& a, hipStream_t st) {
-  LaunchTimer t(gemm_label<BL, kStoreBf16>(false), st);
+  LaunchTimer t(gemm_label<BL, kStoreBf16, NB>(), st);
   hipLaunchKernelGGL((k_gemm_fused<BM, BN, BK, S, 0, BL, NB>), dim3((unsigned)tiles(a, BM, BN)), dim3(256), 0,
                      st, a);
 }
@@ -71,7 +74,7 @@ void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st) {
 }
 
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {
-  launch_pick<kKContig, kMNContig, kStoreBf16, 0>(a, st);
+  launch_pick<kKContig, kKContig, kStoreBf16, 1>(a, st);
 }
 
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st) {

@@ -150,7 +150,9 @@ struct DmaTileK {
 // MN-contiguous operand: global [K][ld] with the operand's rows contiguous
 // (e.g. dY or X as operands of dY^T X, or W_hat [out][in] as the operand of
 // dY W_hat). LDS keeps the natural [BK][ROWS] layout; 16-byte chunk c of k-row
-// k sits at position c ^ (2 (k & 3)). Fragments are read with
+// k sits at position c ^ (2 (k & 3)) ^ (8 ((k >> 3) & 1)): a 64-lane transpose
+// read touches k-rows k0 + 8 g + (0..3), g = 0..3, and this spreads them over
+// all 64 banks, two dwords each (the minimum for 512 bytes). Fragments are read with
 // ds_read_b64_tr_b16: in each 16-lane group, lane j addresses the 4 elements
 // (k0 + j / 4, r0 + 4 (j % 4) .. +3) and lane i receives element i % 4 of
 // lane 4 e + i / 4's row for e = 0..3, i.e. rows r0 + i at k0 .. k0 + 3. Two
@@ -163,14 +165,13 @@ struct DmaTileMN {
   static constexpr int PITCH = ROWS * 2;
   static constexpr int KPI = 1024 / PITCH;               // k-rows per DMA instruction
   static constexpr int NI = BK / KPI / 4;                // instructions per wave per slab
-  static_assert(CHR >= 8 && NI * KPI * 4 == BK, "tile shape");
+  static_assert(CHR >= 16 && NI * KPI * 4 == BK, "tile shape");
   i32x4 rs;
   uint32_t voff[NI];
   uint32_t lrow[NI];
   uint32_t kstride;                                      // bytes per k-row in global memory
-  __device__ static __forceinline__ int off(int k, int chunk) {
-    return k * PITCH + ((chunk ^ ((k & 3) << 1)) << 4);
-  }
+  __device__ static __forceinline__ int swz(int k) { return ((k & 3) << 1) ^ (((k >> 3) & 1) << 3); }
+  __device__ static __forceinline__ int off(int k, int chunk) { return k * PITCH + ((chunk ^ swz(k)) << 4); }
   __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int /*nrows*/, int kdim) {
     rs = buffer_rsrc(src + row0, ((int64_t)kdim * ld - row0) * 2);
     kstride = (uint32_t)(ld * 2);
@@ -181,7 +182,7 @@ struct DmaTileMN {
       const int k0 = (wave * NI + q) * KPI;
       const int kr = k0 + lane / CHR;
       const int pos = lane % CHR;
-      const int chunk = pos ^ ((kr & 3) << 1);
+      const int chunk = pos ^ swz(kr);
       voff[q] = (uint32_t)(kr * ld * 2 + chunk * 16);
       lrow[q] = (uint32_t)(k0 * PITCH);
     }
@@ -366,6 +367,14 @@ __device__ __forceinline__ void mfma_drain() {
 // A 64-column quantisation group is 4 j-tiles x 4 registers of one lane plus a
 // reduction over the 4 lanes that share (lane & 15).
 // ---------------------------------------------------------------------------
+// Inputs of one (row, group) step of the gradient epilogues.
+template <int EP>
+struct EpiIn {
+  float s, z;
+  float4 w[4];          // kSteGrads: W[o][cg + 16 jj + cq .. + 3]
+  uint32_t c[4];        // kE2eScaleGrad: the same four codes per jj
+};
+
 template <int EP, int NB, int TI, int TJ, int WN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
                                               int wm0, int wn0, int lane) {
@@ -384,65 +393,77 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
       }
     }
   } else {
-    // Rows are weight rows o (A = dY^T), columns are inputs c (B = X^T).
-    constexpr int NG = WN / 64;
+    // Rows are weight rows o (A = dY^T), columns inputs c (B = X^T). Steps
+    // t = (i, g) walk the lane's rows and 64-column groups; the loads of step
+    // t + 1 are issued before step t is computed.
+    constexpr int NG = WN / 64, NT = TI * NG;
+    auto row_of = [&](int t) { return m0 + wm0 + (t / NG) * 16 + rl; };
+    auto col_of = [&](int t) { return n0 + wn0 + (t % NG) * 64; };
+    auto load = [&](int t, EpiIn<EP>& in) {
+      const int o = row_of(t), cg = col_of(t);
+      if (o < a.M && cg < a.N) {
+        const int64_t gi = (int64_t)o * a.G + cg / 64;
+        in.s = a.s[gi];
+        in.z = a.z[gi];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int o = m0 + wm0 + i * 16 + rl;
-      const bool row_ok = o < a.M;
+        for (int jj = 0; jj < 4; ++jj) {
+          if constexpr (EP == kSteGrads) in.w[jj] = *(const float4*)(a.W + (int64_t)o * a.ldw + cg + jj * 16 + cq);
+          else in.c[jj] = codes4<NB>(a.Wq + (int64_t)o * a.ldq, cg + jj * 16 + cq);
+        }
+      }
+    };
+    EpiIn<EP> cur, nxt;
+    load(0, cur);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int cg = n0 + wn0 + g * 64;
-        const bool ok = row_ok && cg < a.N;
-        const int64_t gi = (int64_t)(row_ok ? o : 0) * a.G + cg / 64;
-        float ps = 0.f, pz = 0.f, sv = 0.f;
-        if (ok) {
-          sv = a.s[gi];
-          if constexpr (EP == kSteGrads) {
-            const float zr = round_clamp_zero(a.z[gi], a.Kq);
+    for (int t = 0; t < NT; ++t) {
+      if (t + 1 < NT) load(t + 1, nxt);
+      const int i = t / NG, g = t % NG;
+      const int o = row_of(t), cg = col_of(t);
+      const bool ok = o < a.M && cg < a.N;
+      const int64_t gi = (int64_t)(ok ? o : 0) * a.G + cg / 64;
+      float ps = 0.f, pz = 0.f;
+      if (ok) {
+        if constexpr (EP == kSteGrads) {
+          const float zr = round_clamp_zero(cur.z, a.Kq);
+          const float rcp = 1.0f / cur.s;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int col = cg + jj * 16 + cq;
-              const f32x4 gw = acc[g * 4 + jj][i];
-              const float4 w = *(const float4*)(a.W + (int64_t)o * a.ldw + col);
-              const float wv[4] = {w.x, w.y, w.z, w.w};
-              float dw[4];
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 gw = acc[g * 4 + jj][i];
+            const float wv[4] = {cur.w[jj].x, cur.w[jj].y, cur.w[jj].z, cur.w[jj].w};
+            float dw[4];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const QElem e = quant_elem(wv[r], sv, zr, a.Kq);
-                dw[r] = e.m ? gw[r] : 0.0f;
-                ps += gw[r] * (e.m ? (__builtin_rintf(e.u) - e.u) : (e.q - zr));
-                pz += e.m ? 0.0f : gw[r];
-              }
-              if (a.dW) *(float4*)(a.dW + (int64_t)o * a.ldw + col) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+            for (int r = 0; r < 4; ++r) {
+              const QElem e = quant_elem_rcp(wv[r], cur.s, rcp, zr, a.Kq);
+              dw[r] = e.m ? gw[r] : 0.0f;
+              ps += gw[r] * (e.m ? (__builtin_rintf(e.u) - e.u) : (e.q - zr));
+              pz += e.m ? 0.0f : gw[r];
             }
-          } else {
-            const float zv = a.z[gi];
-            const uint8_t* qrow = a.Wq + (int64_t)o * a.ldq;
+            if (a.dW)
+              *(float4*)(a.dW + (int64_t)o * a.ldw + cg + jj * 16 + cq) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+          }
+        } else {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int col = cg + jj * 16 + cq;
-              const f32x4 gw = acc[g * 4 + jj][i];
-              const uint32_t c4 = codes4<NB>(qrow, col);
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 gw = acc[g * 4 + jj][i];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float qv = (float)((c4 >> (NB * r)) & ((1u << NB) - 1));
-                ps += gw[r] * (qv - zv);
-                pz += gw[r];
-              }
+            for (int r = 0; r < 4; ++r) {
+              const float qv = (float)((cur.c[jj] >> (NB * r)) & ((1u << NB) - 1));
+              ps += gw[r] * (qv - cur.z);
+              pz += gw[r];
             }
           }
         }
-        // the 4 lanes with the same (lane & 15) hold the 4 column quarters of the group
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        pz += __shfl_xor(pz, 16);
-        pz += __shfl_xor(pz, 32);
-        if (ok && lane < 16 && a.ds) {
-          a.ds[gi] = ps;
-          if (a.dz) a.dz[gi] = -sv * pz;
-        }
       }
+      // the 4 lanes with the same (lane & 15) hold the 4 column quarters of the group
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      pz += __shfl_xor(pz, 16);
+      pz += __shfl_xor(pz, 32);
+      if (ok && lane < 16 && a.ds) {
+        a.ds[gi] = ps;
+        if (a.dz) a.dz[gi] = -cur.s * pz;
+      }
+      cur = nxt;
     }
   }
 }

@@ -28,6 +28,12 @@ void launch_pack(const float* W, const float* s, const float* z, int64_t out, in
                  uint8_t* Wq, float* zround, hipStream_t st);
 void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
                     uint16_t* w_hat, hipStream_t st);
+// W_hat^T [in][out] bf16 for the dX GEMM (needs out % 64 == 0): from the fp32
+// master weight (fake-quant) or from packed codes (E2E-QP).
+void launch_w_hat_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
+                    uint16_t* w_hat_t, hipStream_t st);
+void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
+                      uint16_t* w_hat_t, hipStream_t st);
 
 // ---- MFMA GEMMs (qat_gemm.hip) ----
 // C[M, N] = sum_k A[m, k] * B[n, k] in bf16 with fp32 accumulation. Each operand
@@ -61,7 +67,7 @@ enum Layout { kKContig = 0, kMNContig = 1 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
 void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
-// dX = dY W_hat: A = dY (K-contiguous), B = W_hat [out][in] read MN-contiguous.
+// dX = dY W_hat: A = dY [M][out], B = W_hat^T [in][out], both K-contiguous.
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 // Gradient GEMM over tokens, Gw = dY^T X with both operands MN-contiguous;
 // epi = kSteGrads (dW, ds, dz) or kE2eScaleGrad (ds, dz).

@@ -25,7 +25,7 @@ import sys
 # rocprofv3 kernel symbol -> the label the library's own timing uses
 LABELS = [
     # k_gemm<BM, BN, BK, STAGES, AMN, BMN, EP, NB>
-    (r"k_gemm<[^>]*,\s*0,\s*1,\s*0,\s*0>", "gemm_dx"),
+    (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*1>", "gemm_dx"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*1,\s*0>", "gemm_ste_grads"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*2,\s*\d>", "gemm_e2e_grads"),
     (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
@@ -34,6 +34,8 @@ LABELS = [
     (r"k_gemm_fused<[^>]*,\s*2,\s*\d>", "gemm_fwd_packed"),
     (r"k_init_minmax", "init_minmax"),
     (r"k_quant_codes", "quant_w_hat"),
+    (r"k_w_hat_t<0,", "quant_w_hat_t"),
+    (r"k_w_hat_t<1,", "dequant_t"),
     (r"k_pack<", "pack"),
     (r"k_dequant<", "dequant"),
 ]
