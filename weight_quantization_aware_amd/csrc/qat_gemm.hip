@@ -2,9 +2,11 @@
 //
 // bf16 operands (k_gemm, BK = 64), measured on the Llama-2 shapes of this path:
 //   256x256, 2 stages   outputs of >= 256 such tiles (one per CU or more):
-//                       gradient GEMMs, MLP- and 70B-sized forwards
-//   128x256, 3 stages   about one 128x256 tile per CU (2048-token q_proj)
-//   128x128, 4 stages   small problems
+//                       gradient GEMMs, MLP- and 70B-sized forwards; 8 waves
+//                       (two per SIMD) up to K = 4096, 4 waves beyond
+//   128x256, 3 stages   about one 128x256 tile per CU (2048-token q_proj);
+//                       8 waves
+//   128x128, 4 stages   small problems; 4 waves
 // Fused B operands (k_gemm_fused) go through an LDS ring beside the bf16
 // stages: packed codes (E2E-QP forward without workspace) with 256-row B tiles,
 // BK = 32, 4 stages; the fp32 master weight (fake-quant forward without
@@ -31,11 +33,11 @@ constexpr const char* gemm_label() {
   return NB == 1 ? "gemm_dx" : "gemm_fwd";
 }
 
-template <int BM, int BN, int S, int AMN, int BMN, int EP, int NB>
+template <int BM, int BN, int S, int WGM, int WGN, int AMN, int BMN, int EP, int NB>
 void launch_bf16(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<kBf16, EP, NB>(), st);
-  hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, AMN, BMN, EP, NB>), dim3((unsigned)tiles(a, BM, BN)), dim3(256), 0,
-                     st, a);
+  hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, AMN, BMN, EP, NB>), dim3((unsigned)tiles(a, BM, BN)),
+                     dim3(64 * WGM * WGN), 0, st, a);
 }
 
 template <int BM, int BN, int BK, int S, int BL, int NB>
@@ -47,9 +49,14 @@ void launch_fused(const GemmArgs& a, hipStream_t st) {
 
 template <int AMN, int BMN, int EP, int NB>
 void launch_pick(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, AMN, BMN, EP, NB>(a, st);
-  else if (tiles(a, 128, 256) >= 192) launch_bf16<128, 256, 3, AMN, BMN, EP, NB>(a, st);
-  else launch_bf16<128, 128, 4, AMN, BMN, EP, NB>(a, st);
+  if (tiles(a, 256, 256) >= 256) {
+    if (a.K <= 4096) launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, NB>(a, st);
+    else launch_bf16<256, 256, 2, 2, 2, AMN, BMN, EP, NB>(a, st);
+  } else if (tiles(a, 128, 256) >= 192) {
+    launch_bf16<128, 256, 3, 2, 4, AMN, BMN, EP, NB>(a, st);
+  } else {
+    launch_bf16<128, 128, 4, 2, 2, AMN, BMN, EP, NB>(a, st);
+  }
 }
 
 template <int BL, int NB>

@@ -102,12 +102,12 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int64_t nbytes) {
   return r;
 }
 
-template <int ROWS, int BK, int SLOTS>
+template <int ROWS, int BK, int SLOTS, int NW = 4>
 struct DmaTileK {
   using L = LdsLayout<BK, SLOTS>;
   static constexpr int RPI = 1024 / L::PITCH;            // rows per DMA instruction
-  static constexpr int NI = ROWS / RPI / 4;              // instructions per wave per slab
-  static_assert(NI * RPI * 4 == ROWS, "tile rows must split over 4 waves");
+  static constexpr int NI = ROWS / RPI / NW;             // instructions per wave per slab
+  static_assert(NI * RPI * NW == ROWS, "tile rows must split over the waves");
   i32x4 rs;
   uint32_t voff[NI];
   uint32_t lrow[NI];                                     // wave-uniform LDS byte offsets
@@ -159,13 +159,13 @@ struct DmaTileK {
 // reads (k0 and k0 + 4) give the same 8 consecutive k as the K-contiguous
 // fragment. k-rows at or beyond kdim read as zero; rows beyond the operand's
 // extent hold other data and only feed outputs that are never stored.
-template <int ROWS, int BK>
+template <int ROWS, int BK, int NW = 4>
 struct DmaTileMN {
   static constexpr int CHR = ROWS / 8;                   // 16-byte chunks per k-row
   static constexpr int PITCH = ROWS * 2;
   static constexpr int KPI = 1024 / PITCH;               // k-rows per DMA instruction
-  static constexpr int NI = BK / KPI / 4;                // instructions per wave per slab
-  static_assert(CHR >= 16 && NI * KPI * 4 == BK, "tile shape");
+  static constexpr int NI = BK / KPI / NW;               // instructions per wave per slab
+  static_assert(CHR >= 16 && NI * KPI * NW == BK, "tile shape");
   i32x4 rs;
   uint32_t voff[NI];
   uint32_t lrow[NI];
@@ -211,10 +211,10 @@ struct DmaTileMN {
   }
 };
 
-template <int ROWS, int BK, int MN>
-struct DmaTileOf { using T = DmaTileK<ROWS, BK, kLdsSlots>; };
-template <int ROWS, int BK>
-struct DmaTileOf<ROWS, BK, 1> { using T = DmaTileMN<ROWS, BK>; };
+template <int ROWS, int BK, int MN, int NW = 4>
+struct DmaTileOf { using T = DmaTileK<ROWS, BK, kLdsSlots, NW>; };
+template <int ROWS, int BK, int NW>
+struct DmaTileOf<ROWS, BK, 1, NW> { using T = DmaTileMN<ROWS, BK, NW>; };
 
 // Quantised-weight operands through an LDS ring. Per slab, the raw weight
 // bytes of ROWS rows (packed N-bit codes, BK*N/8 bytes per row; or the fp32
@@ -469,8 +469,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
 }
 
 // ---------------------------------------------------------------------------
-// The GEMM kernel for bf16 operands. A 256-thread workgroup (4 wave64s, 2x2,
-// one per SIMD) owns a BM x BN tile; K advances in slabs of BK = 64, two
+// The GEMM kernel for bf16 operands. A workgroup of WGM x WGN wave64s owns a
+// BM x BN tile (4 waves: one per SIMD; 8 waves: two per SIMD, which hide each
+// other's LDS and barrier waits); K advances in slabs of BK = 64, two
 // k-steps of 32 each. Operand tiles reach LDS by DMA (AMN / BMN select the
 // K- or MN-contiguous loader).
 //
@@ -489,13 +490,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
 // keeps that order: LDS reads run a full k-step ahead of their MFMAs and the
 // DMA issue is spread over the k-step.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int AMN, int BMN, int EP, int NB>
-__global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
-  using LA = typename DmaTileOf<BM, BK, AMN>::T;
-  using LB = typename DmaTileOf<BN, BK, BMN>::T;
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int AMN, int BMN, int EP, int NB>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a) {
+  constexpr int NW = WGM * WGN;
+  using LA = typename DmaTileOf<BM, BK, AMN, NW>::T;
+  using LB = typename DmaTileOf<BN, BK, BMN, NW>::T;
   static_assert(BK == 64, "two k-steps per slab");
   static_assert(STAGES >= 2, "two stages at least");
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TI = WM / 16, TJ = WN / 16;
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
