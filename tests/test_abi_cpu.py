@@ -13,9 +13,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared():
-    src = open(os.path.join(ROOT, "include", "qat.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(qat_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in ("qat.h", "qat_peaks.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(qat_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_calls():
@@ -97,3 +100,13 @@ def test_timing_registry_host_side():
     Q.timing_enable(False)
     Q.timing_select(None)
     assert Q.timing_report() == {}
+
+
+def test_peak_probe_host_validation():
+    L = Q.lib()
+    assert L.qat_peak_mfma_flops(256, 100) == 256 * 8 * 8 * 100 * 16 * 16 * 32 * 2
+    assert L.qat_peak_mfma_flops(0, 100) == -1
+    assert L.qat_peak_scratch_bytes(4) == 4 * 512 * 4
+    assert L.qat_peak_mfma(0, 10, FAKE, None) == 1
+    assert L.qat_peak_read(None, 1 << 20, 16, FAKE, None) == 1
+    assert L.qat_peak_read(FAKE + 4, 1 << 20, 16, FAKE, None) == 1

@@ -40,10 +40,15 @@ _SIGS = {
     "qat_timing_select": [ctypes.c_char_p],
     "qat_timing_get": [_c_i32, ctypes.c_char_p, _c_sz, ctypes.POINTER(ctypes.c_double),
                        ctypes.POINTER(_c_i64)],
+    "qat_peak_mfma_flops": [_c_i32, _c_i32],
+    "qat_peak_scratch_bytes": [_c_i32],
+    "qat_peak_mfma": [_c_i32, _c_i32, _c_vp, _c_vp],
+    "qat_peak_read": [_c_vp, _c_sz, _c_i32, _c_vp, _c_vp],
     "qat_status_string": [_c_i32],
     "qat_last_error": [],
 }
-_RES = {"qat_fakequant_ws_bytes": _c_sz, "qat_dequant_ws_bytes": _c_sz,
+_RES = {"qat_fakequant_ws_bytes": _c_sz, "qat_dequant_ws_bytes": _c_sz, "qat_peak_mfma_flops": _c_i64,
+        "qat_peak_scratch_bytes": _c_sz,
         "qat_status_string": ctypes.c_char_p, "qat_last_error": ctypes.c_char_p}
 
 _lib = None
@@ -196,3 +201,20 @@ def timing_report() -> dict:
             raise QatError("qat_timing_get", st)
         out[buf.value.decode()] = (ms.value, int(cnt.value))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Practical-peak probes (include/qat_peaks.h)
+# ---------------------------------------------------------------------------
+
+def peak_mfma(blocks: int, iters: int, scratch: torch.Tensor) -> int:
+    """Launch the MFMA loop on the current stream; returns its flop count."""
+    _call("qat_peak_mfma", blocks, iters, _p(scratch), _stream())
+    return int(lib().qat_peak_mfma_flops(blocks, iters))
+
+
+def peak_read(buf: torch.Tensor, blocks: int, scratch: torch.Tensor) -> int:
+    """Launch the read-stream kernel over buf on the current stream; returns bytes read."""
+    nbytes = buf.numel() * buf.element_size()
+    _call("qat_peak_read", _p(buf), nbytes, blocks, _p(scratch), _stream())
+    return nbytes - nbytes % 16

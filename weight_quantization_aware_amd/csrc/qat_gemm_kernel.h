@@ -350,8 +350,12 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 __device__ __forceinline__ void mfma_acc(f32x4& c, const bf16x8& b, const bf16x8& a) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
 }
+// Waits out the MFMA write-back latency before the epilogue reads the
+// accumulators; the scheduling fence keeps every later instruction (the
+// accumulator reads included) after the wait.
 __device__ __forceinline__ void mfma_drain() {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -593,6 +597,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a) {
     __syncthreads();                                     // B_kt
     sched_fence();
     kstep(F1, nx, 0, F0, kt + STAGES);                   // k-step 1; read slab kt+1; DMA
+    // The last iteration waits out the MFMA latency before leaving the loop,
+    // so nothing placed after the loop (the epilogue, or spill code for an
+    // accumulator) can read an accumulator before its result is written.
+    if (kt == nk - 1) mfma_drain();
   }
   wait_vmcnt<0>();                                       // drain the trailing re-loads
   __syncthreads();

@@ -11,6 +11,14 @@
         JSON keyed by the library's kernel labels, with the hash of the kernel
         sources it was measured on.
 
+    python -m weight_quantization_aware_amd.profile_summary pmc <results.db> [--cmd "..."]
+        per-kernel means of the collected counters (summed over dimensions per
+        dispatch) and, when present, MFMA utilisation =
+        SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) and
+        the LDS bank-conflict share SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.
+        (GRBM_GUI_ACTIVE is summed over the 8 XCDs: it reads 8x the kernel's
+        duration in cycles.)
+
 Reads SQLite databases written by rocprofv3 (ROCm 7); prints to stdout.
 """
 from __future__ import annotations
@@ -97,6 +105,29 @@ def traffic(fetch_db: str, write_db: str, copy_bytes: int, cmd: str) -> None:
     print(json.dumps(out, indent=1))
 
 
+def pmc(db: str, cmd: str) -> None:
+    c = sqlite3.connect(db)
+    rows = c.execute("select kernel_name, dispatch_id, counter_name, sum(value) from counters_collection "
+                     "group by dispatch_id, counter_name").fetchall()
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for name, _, cn, v in rows:
+        lab = label_of(name)
+        if lab:
+            agg[lab][cn].append(v)
+    print(f"# rocprofv3 counter summary (mean per dispatch)\n# command: {cmd}\n#")
+    for lab in sorted(agg):
+        d = {cn: sum(v) / len(v) for cn, v in agg[lab].items()}
+        n = max(len(v) for v in agg[lab].values())
+        extra = []
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and d.get("GRBM_GUI_ACTIVE"):
+            util = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / 8 * 1024)
+            extra.append(f"mfma_util={util:.3f}")
+        if "SQ_LDS_BANK_CONFLICT" in d and d.get("SQ_LDS_IDX_ACTIVE"):
+            extra.append(f"lds_conflict_share={d['SQ_LDS_BANK_CONFLICT'] / d['SQ_LDS_IDX_ACTIVE']:.3f}")
+        vals = "  ".join(f"{cn}={v:.4g}" for cn, v in sorted(d.items()))
+        print(f"{lab:22s} dispatches={n}  {'  '.join(extra)}\n    {vals}")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -108,9 +139,14 @@ def main() -> None:
     b.add_argument("write_db")
     b.add_argument("--copy-bytes", type=int, default=1 << 30)
     b.add_argument("--cmd", default="")
+    c = sub.add_parser("pmc")
+    c.add_argument("db")
+    c.add_argument("--cmd", default="")
     args = ap.parse_args()
     if args.what == "stats":
         stats(args.db, args.cmd)
+    elif args.what == "pmc":
+        pmc(args.db, args.cmd)
     else:
         traffic(args.fetch_db, args.write_db, args.copy_bytes, args.cmd)
 
