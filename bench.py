@@ -305,7 +305,8 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp)
       read stream over 1 GiB (beyond the 256 MiB MALL);
     - init and pack with cold caches: before each timed call a 1 GiB buffer is
       read (not written, so no dirty lines are left to write back), which
-      evicts W from L2 and the MALL (median of 10);
+      evicts W from L2 and the MALL (median of 10); at the q_proj weight
+      (64 MiB) and at the Llama-2-70B gate weight (896 MiB);
     - the Llama-2-7B block of seven w3g64 linears (q, k, v, o 4096x4096; gate,
       up 11008x4096; down 4096x11008; 2048 tokens): fake-quant forward +
       backward of all seven, 2486.79 GFLOP counted;
@@ -353,7 +354,23 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp)
     n = out * inp
     init_bytes = n * 4 + 2 * out * (inp // 64) * 4
     pack_bytes = n * (4 + bits / 8) + 3 * out * (inp // 64) * 4
-    del big
+    del s2, z2, Wq2, zp2
+
+    # the same at the Llama-2-70B gate weight (28672 x 8192 fp32, 896 MiB, w2)
+    lin5 = synth.config(5, 2)[0]
+    W5 = torch.from_numpy(lin5.W()).to(dev)
+    G5 = lin5.inp // 64
+    s5 = torch.empty(lin5.out, G5, device=dev)
+    z5 = torch.empty_like(s5)
+    Wq5 = torch.empty(lin5.out, lin5.inp * 2 // 8, dtype=torch.uint8, device=dev)
+    zp5 = torch.empty_like(s5)
+    Q.qat_init_minmax(W5, 2, s5, z5)
+    t_init5 = cold(lambda: Q.qat_init_minmax(W5, 2, s5, z5))
+    t_pack5 = cold(lambda: Q.qat_pack(W5, s5, z5, 2, Wq5, zp5))
+    n5 = lin5.out * lin5.inp
+    init5_bytes = n5 * 4 + 2 * lin5.out * G5 * 4
+    pack5_bytes = n5 * (4 + 2 / 8) + 3 * lin5.out * G5 * 4
+    del W5, s5, z5, Wq5, zp5, big
 
     # the C3 block
     c3 = []
@@ -388,6 +405,8 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp)
                                    "grid-stride read of 1 GiB"},
         "init_cold": {"us": round(t_init * 1e6, 2), "gbs": round(init_bytes / t_init / 1e9, 1)},
         "pack_cold": {"us": round(t_pack * 1e6, 2), "gbs": round(pack_bytes / t_pack / 1e9, 1)},
+        "init_cold_70b_gate": {"us": round(t_init5 * 1e6, 2), "gbs": round(init5_bytes / t_init5 / 1e9, 1)},
+        "pack_cold_70b_gate_w2": {"us": round(t_pack5 * 1e6, 2), "gbs": round(pack5_bytes / t_pack5 / 1e9, 1)},
         "c3_block_w3g64": {"gflop": round(gflop, 2), "ms": round(t_c3 * 1e3, 4),
                            "tflops": round(gflop / t_c3 / 1e3, 1)},
         "clocks": _clocks(),
