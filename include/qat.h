@@ -19,8 +19,11 @@
  *
  * Conventions shared by every call
  * --------------------------------
- * - Shapes: W is [out, in] row-major (nn.Linear). Groups are `group` = 64
- *   consecutive elements of a row along `in`; G = in / 64 groups per row.
+ * - Shapes: W is [out, in] row-major (nn.Linear). Groups are `group`
+ *   consecutive elements of a row along `in`: 32, 64 or 128 (the sizes the
+ *   paperlayer.ai summary's Appendix F ablates; 64 is the default of every
+ *   workload here), or group == in for channel-wise quantisation (one group
+ *   per row). group must divide in; G = in / group groups per row.
  *   s, z, ds, dz are [out, G] fp32 row-major. X is [M, in], Y and dY are
  *   [M, out], dX is [M, in]; all bf16 passed as uint16_t bit patterns.
  * - bits N in {2, 3, 4}; K = 2^N - 1. in is a multiple of 64. The four GEMM calls
@@ -59,7 +62,7 @@ enum {
   QAT_ERR_SHAPE = 2,     /* a dimension <= 0, in (or, for the GEMM calls, out) not a
                             multiple of 64, or an operand of 2 GiB or more                  */
   QAT_ERR_BITS = 3,      /* bits not in {2, 3, 4}                                          */
-  QAT_ERR_GROUP = 4,     /* group != 64                                                    */
+  QAT_ERR_GROUP = 4,     /* group not 32, 64, 128 or in, or not dividing in                */
   QAT_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                               */
   QAT_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the size query returns          */
   QAT_ERR_HIP = 7,       /* a HIP launch failed; qat_last_error() has the HIP message      */
@@ -76,7 +79,7 @@ const char* qat_last_error(void);
  * a1. Per-group min-max init (modelfoundations.com note, Phase 1):
  *   for each row o and group j of W:
  *     d = fl32(max - min);  s = max(fl32(d / K), fl32(1e-5));  z = rint(fl32(-min / s)).
- * W [out, in] fp32 in; s, z [out, in/64] fp32 out (z is integer valued).
+ * W [out, in] fp32 in; s, z [out, G] fp32 out (z is integer valued).
  */
 int32_t qat_init_minmax(const float* W, int64_t out, int64_t in, int32_t group, int32_t bits,
                         float* s, float* z, hipStream_t stream);

@@ -56,7 +56,10 @@ FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced on the
 
 @pytest.mark.parametrize("args,status", [
     ((FAKE, 64, 128, 64, 5, FAKE, FAKE + 4096, None), 3),        # bits
-    ((FAKE, 64, 128, 32, 2, FAKE, FAKE + 4096, None), 4),        # group
+    ((FAKE, 64, 128, 48, 2, FAKE, FAKE + 4096, None), 4),        # group not 32, 64, 128 or in
+    ((FAKE, 64, 128, 96, 2, FAKE, FAKE + 4096, None), 4),        # group not 32, 64, 128 or in
+    ((FAKE, 64, 192, 128, 2, FAKE, FAKE + 4096, None), 4),       # group 128 does not divide in
+    ((FAKE, 64, 128, 0, 2, FAKE, FAKE + 4096, None), 4),         # group 0
     ((FAKE, 64, 96, 64, 2, FAKE, FAKE + 4096, None), 2),         # in % 64
     ((FAKE, 0, 128, 64, 2, FAKE, FAKE + 4096, None), 2),         # out <= 0
     ((None, 64, 128, 64, 2, FAKE, FAKE + 4096, None), 1),        # null W

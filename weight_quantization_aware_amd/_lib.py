@@ -127,49 +127,50 @@ def workspace(nbytes: int, device=None) -> torch.Tensor:
 # The C-ABI calls, same names as in include/qat.h
 # ---------------------------------------------------------------------------
 
-def qat_init_minmax(W: torch.Tensor, bits: int, s: torch.Tensor, z: torch.Tensor) -> None:
+def qat_init_minmax(W: torch.Tensor, bits: int, s: torch.Tensor, z: torch.Tensor, group: int = GROUP) -> None:
     out, inp = W.shape
-    _call("qat_init_minmax", _p(W), out, inp, GROUP, bits, _p(s), _p(z), _stream())
+    _call("qat_init_minmax", _p(W), out, inp, group, bits, _p(s), _p(z), _stream())
 
 
-def qat_quant_codes(W, s, z, bits, codes=None, W_hat=None) -> None:
+def qat_quant_codes(W, s, z, bits, codes=None, W_hat=None, group: int = GROUP) -> None:
     out, inp = W.shape
-    _call("qat_quant_codes", _p(W), _p(s), _p(z), out, inp, GROUP, bits, _p(codes),
+    _call("qat_quant_codes", _p(W), _p(s), _p(z), out, inp, group, bits, _p(codes),
           _p(None if W_hat is None else _u16(W_hat)), _stream())
 
 
-def qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=None) -> None:
+def qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=None, group: int = GROUP) -> None:
     M, inp = X.shape
     out = W.shape[0]
-    _call("qat_fakequant_linear_fwd", _p(_u16(X)), _p(W), _p(s), _p(z), M, out, inp, GROUP, bits,
+    _call("qat_fakequant_linear_fwd", _p(_u16(X)), _p(W), _p(s), _p(z), M, out, inp, group, bits,
           _p(_u16(Y)), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
 
 
-def qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=None, dW=None, ds=None, dz=None, ws=None) -> None:
+def qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=None, dW=None, ds=None, dz=None, ws=None,
+                             group: int = GROUP) -> None:
     M, inp = X.shape
     out = W.shape[0]
     _call("qat_fakequant_linear_bwd", _p(_u16(dY)), _p(_u16(X)), _p(W), _p(s), _p(z), M, out, inp,
-          GROUP, bits, _p(None if dX is None else _u16(dX)), _p(dW), _p(ds), _p(dz), _p(ws),
+          group, bits, _p(None if dX is None else _u16(dX)), _p(dW), _p(ds), _p(dz), _p(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream())
 
 
-def qat_pack(W, s, z, bits, Wq, z_round=None) -> None:
+def qat_pack(W, s, z, bits, Wq, z_round=None, group: int = GROUP) -> None:
     out, inp = W.shape
-    _call("qat_pack", _p(W), _p(s), _p(z), out, inp, GROUP, bits, _p(Wq), _p(z_round), _stream())
+    _call("qat_pack", _p(W), _p(s), _p(z), out, inp, group, bits, _p(Wq), _p(z_round), _stream())
 
 
-def qat_dequant_gemm_fwd(X, Wq, s, z, bits, Y, ws=None) -> None:
+def qat_dequant_gemm_fwd(X, Wq, s, z, bits, Y, ws=None, group: int = GROUP) -> None:
     M, inp = X.shape
     out = Wq.shape[0]
-    _call("qat_dequant_gemm_fwd", _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp, GROUP, bits,
+    _call("qat_dequant_gemm_fwd", _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp, group, bits,
           _p(_u16(Y)), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
 
 
-def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None) -> None:
+def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None, group: int = GROUP) -> None:
     M, inp = X.shape
     out = Wq.shape[0]
     _call("qat_dequant_gemm_bwd_s", _p(_u16(dY)), _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp,
-          GROUP, bits, _p(None if dX is None else _u16(dX)), _p(ds), _p(dz), _p(ws),
+          group, bits, _p(None if dX is None else _u16(dX)), _p(ds), _p(dz), _p(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream())
 
 

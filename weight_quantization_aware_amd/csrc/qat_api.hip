@@ -45,13 +45,18 @@ int32_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
 
 // Elementwise calls accept any row count; the GEMM calls (gemm = true) also need
 // out % 64 == 0 because the backward dX GEMM contracts over out in 64-wide slabs.
+// Groups: 32, 64 or 128 elements along `in`, or the whole row (group == in,
+// channel-wise).
 int32_t check_common(int64_t out, int64_t in, int32_t group, int32_t bits, bool gemm = false) {
-  if (group != 64) return QAT_ERR_GROUP;
   if (bits < 2 || bits > 4) return QAT_ERR_BITS;
   if (out <= 0 || in <= 0 || in % 64 != 0 || (gemm && out % 64 != 0)) return QAT_ERR_SHAPE;
   if (out > kMaxDim || in > kMaxDim || out * in * 4 > kMaxBytes) return QAT_ERR_SHAPE;
+  if (!(group == 32 || group == 64 || group == 128 || group == in) || in % group != 0) return QAT_ERR_GROUP;
   return QAT_OK;
 }
+
+// Bytes of one [out][in / group] fp32 parameter (s, z, ds, dz).
+size_t gbytes(int64_t out, int64_t in, int32_t group) { return (size_t)(out * (in / group) * 4); }
 
 int32_t check_m(int64_t M, int64_t out, int64_t in) {
   if (M <= 0 || M > kMaxDim) return QAT_ERR_SHAPE;
@@ -97,7 +102,7 @@ QAT_API const char* qat_status_string(int32_t st) {
     case QAT_ERR_NULL: return "a required pointer is NULL";
     case QAT_ERR_SHAPE: return "invalid shape (dimension <= 0, in or out not a multiple of 64, or an operand of 2 GiB or more)";
     case QAT_ERR_BITS: return "bits must be 2, 3 or 4";
-    case QAT_ERR_GROUP: return "group must be 64";
+    case QAT_ERR_GROUP: return "group must be 32, 64, 128 or in (channel-wise), dividing in";
     case QAT_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case QAT_ERR_WORKSPACE: return "workspace missing or too small";
     case QAT_ERR_HIP: return "HIP launch failed (see qat_last_error)";
@@ -122,11 +127,11 @@ QAT_API int32_t qat_init_minmax(const float* W, int64_t out, int64_t in, int32_t
   QAT_CHECK(check_common(out, in, group, bits));
   if (!W || !s || !z) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({W, s, z}));
-  const size_t nw = out * in * 4, ng = out * (in / 64) * 4;
+  const size_t nw = out * in * 4, ng = gbytes(out, in, group);
   Range outs[] = {{s, ng}, {z, ng}};
   Range ins[] = {{W, nw}};
   QAT_CHECK(check_alias(outs, 2, ins, 1));
-  qat::launch_init_minmax(W, out, in, bits, s, z, stream);
+  qat::launch_init_minmax(W, out, in, group, bits, s, z, stream);
   return finish();
 }
 
@@ -136,11 +141,11 @@ QAT_API int32_t qat_quant_codes(const float* W, const float* s, const float* z, 
   QAT_CHECK(check_common(out, in, group, bits));
   if (!W || !s || !z || (!codes && !W_hat)) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({W, s, z, codes, W_hat}));
-  const size_t n = out * in, ng = out * (in / 64) * 4;
+  const size_t n = out * in, ng = gbytes(out, in, group);
   Range outs[] = {{codes, n}, {W_hat, n * 2}};
   Range ins[] = {{W, n * 4}, {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 2, ins, 3));
-  qat::launch_quant_codes(W, s, z, out, in, bits, codes, W_hat, stream);
+  qat::launch_quant_codes(W, s, z, out, in, group, bits, codes, W_hat, stream);
   return finish();
 }
 
@@ -149,11 +154,11 @@ QAT_API int32_t qat_pack(const float* W, const float* s, const float* z, int64_t
   QAT_CHECK(check_common(out, in, group, bits));
   if (!W || !s || !z || !Wq) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({W, s, z, Wq, z_round}));
-  const size_t n = out * in, ng = out * (in / 64) * 4;
+  const size_t n = out * in, ng = gbytes(out, in, group);
   Range outs[] = {{Wq, n * bits / 8}, {z_round, ng}};
   Range ins[] = {{W, n * 4}, {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 2, ins, 3));
-  qat::launch_pack(W, s, z, out, in, bits, Wq, z_round, stream);
+  qat::launch_pack(W, s, z, out, in, group, bits, Wq, z_round, stream);
   return finish();
 }
 
@@ -167,7 +172,7 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
   QAT_CHECK(check_ptrs({X, W, s, z, Y, ws}));
   const size_t need = ws_bytes_for(out, in);
   if (ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
-  const size_t ng = out * (in / 64) * 4;
+  const size_t ng = gbytes(out, in, group);
   Range outs[] = {{Y, (size_t)(M * out * 2)}, {ws, ws ? need : 0}};
   Range ins[] = {{X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)}, {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 2, ins, 4));
@@ -182,12 +187,13 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
   a.ldc = out;
   a.s = s;
   a.z = z;
-  a.G = in / 64;
+  a.G = in / group;
+  a.group = group;
   a.Kq = (float)((1 << bits) - 1);
   a.ldb = in;
   if (ws) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_quant_codes(W, s, z, out, in, bits, nullptr, w_hat, stream);
+    qat::launch_quant_codes(W, s, z, out, in, group, bits, nullptr, w_hat, stream);
     a.B = w_hat;
     qat::launch_gemm_fwd(a, qat::kBf16, bits, stream);
   } else {
@@ -216,7 +222,7 @@ static void launch_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, in
 
 // Gw = dY^T X over the M tokens, both read in place, reduced by the epilogue.
 static qat::GemmArgs grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z,
-                                int64_t M, int64_t out, int64_t in, int bits) {
+                                int64_t M, int64_t out, int64_t in, int group, int bits) {
   qat::GemmArgs a = gemm_args();
   a.A = dY;
   a.lda = out;
@@ -227,9 +233,19 @@ static qat::GemmArgs grads_args(const uint16_t* dY, const uint16_t* X, const flo
   a.K = (int)M;
   a.s = s;
   a.z = z;
-  a.G = in / 64;
+  a.G = in / group;
+  a.group = group;
   a.Kq = (float)((1 << bits) - 1);
   return a;
+}
+
+// Groups wider than the epilogue's 64-column chunks are summed by atomic adds
+// into ds and dz, which start at zero.
+static void zero_wide_group_grads(float* ds, float* dz, int64_t out, int64_t in, int group, hipStream_t stream) {
+  if (group <= 64) return;
+  const int64_t n = out * (in / group);
+  if (ds) qat::launch_fill_zero(ds, n, stream);
+  if (dz) qat::launch_fill_zero(dz, n, stream);
 }
 
 QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
@@ -244,7 +260,7 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
   QAT_CHECK(check_ptrs({dY, X, W, s, z, dX, dW, ds, dz, ws}));
   const size_t need = ws_bytes_for(out, in);
   if (dX && (!ws || ws_bytes < need)) return QAT_ERR_WORKSPACE;
-  const size_t ng = out * (in / 64) * 4;
+  const size_t ng = gbytes(out, in, group);
   Range outs[] = {{dX, (size_t)(M * in * 2)}, {dW, (size_t)(out * in * 4)}, {ds, ng}, {dz, ng},
                   {dX ? ws : nullptr, need}};
   Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)},
@@ -253,11 +269,12 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
 
   if (dX) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_w_hat_t(W, s, z, out, in, bits, w_hat, stream);
+    qat::launch_w_hat_t(W, s, z, out, in, group, bits, w_hat, stream);
     launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
   if (dW || ds) {
-    qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, bits);
+    zero_wide_group_grads(ds, dz, out, in, group, stream);
+    qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, group, bits);
     a.W = W;
     a.ldw = in;
     a.dW = dW;
@@ -278,7 +295,7 @@ QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const
   QAT_CHECK(check_ptrs({X, Wq, s, z, Y, ws}));
   const size_t need = ws_bytes_for(out, in);
   if (ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
-  const size_t ng = out * (in / 64) * 4;
+  const size_t ng = gbytes(out, in, group);
   Range outs[] = {{Y, (size_t)(M * out * 2)}, {ws, ws ? need : 0}};
   Range ins[] = {{X, (size_t)(M * in * 2)}, {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 2, ins, 4));
@@ -292,11 +309,12 @@ QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const
   a.ldc = out;
   a.s = s;
   a.z = z;
-  a.G = in / 64;
+  a.G = in / group;
+  a.group = group;
   a.Kq = (float)((1 << bits) - 1);
   if (ws) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_dequant(Wq, s, z, out, in, bits, w_hat, stream);
+    qat::launch_dequant(Wq, s, z, out, in, group, bits, w_hat, stream);
     a.B = w_hat;
     a.ldb = in;
     qat::launch_gemm_fwd(a, qat::kBf16, bits, stream);
@@ -319,7 +337,7 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
   QAT_CHECK(check_ptrs({dY, X, Wq, s, z, dX, ds, dz, ws}));
   const size_t need = ws_bytes_for(out, in);
   if (dX && (!ws || ws_bytes < need)) return QAT_ERR_WORKSPACE;
-  const size_t ng = out * (in / 64) * 4;
+  const size_t ng = gbytes(out, in, group);
   Range outs[] = {{dX, (size_t)(M * in * 2)}, {ds, ng}, {dz, ng}, {dX ? ws : nullptr, need}};
   Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)},
                  {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}};
@@ -327,10 +345,11 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
 
   if (dX) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_dequant_t(Wq, s, z, out, in, bits, w_hat, stream);
+    qat::launch_dequant_t(Wq, s, z, out, in, group, bits, w_hat, stream);
     launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
-  qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, bits);
+  zero_wide_group_grads(ds, dz, out, in, group, stream);
+  qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, group, bits);
   a.Wq = Wq;
   a.ldq = in * bits / 8;
   a.ds = ds;

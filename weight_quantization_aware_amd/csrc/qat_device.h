@@ -5,8 +5,23 @@
 
 namespace qat {
 
-constexpr int kGroup = 64;           // elements per quantisation group (along `in`)
+constexpr int kGroup = 64;           // the default quantisation group (elements along `in`)
 constexpr float kSMin = 1e-5f;       // floor for the step size of a constant group
+
+// Unsigned division of n < 2^31 by a runtime divisor d >= 1 with one multiply
+// (the round-up reciprocal of Granlund and Montgomery): l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1, q = (umulhi(n, m) + n) >> l. The sum
+// stays below 2^32 because umulhi(n, m) <= n < 2^31.
+struct FastDiv {
+  uint32_t m, l;
+  __host__ __device__ static FastDiv make(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, l};
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const { return (__umulhi(n, m) + n) >> l; }
+};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -49,6 +64,19 @@ __device__ __forceinline__ float row16_min(float v) {
   v = fminf(v, dpp<kDppXor2>(v));
   v = fminf(v, dpp<kDppRowHalfMirror>(v));
   v = fminf(v, dpp<kDppRowMirror>(v));
+  return v;
+}
+// Min / max over the 8 lanes of each half row.
+__device__ __forceinline__ float row8_min(float v) {
+  v = fminf(v, dpp<kDppXor1>(v));
+  v = fminf(v, dpp<kDppXor2>(v));
+  v = fminf(v, dpp<kDppRowHalfMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row8_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
   return v;
 }
 __device__ __forceinline__ float row16_max(float v) {

@@ -9,17 +9,21 @@ namespace qat {
 // ---------------------------------------------------------------------------
 // a1: per-group min-max init (modelfoundations.com EfficientQAT note, Phase 1).
 // A wave reads 4 KiB fully coalesced (lane l loads float4 j*64 + l of the
-// wave's window, j = 0..3), i.e. 16 groups; the 16 lanes that share a group
-// reduce min / max with DPP inside their row. Lane (l & 15) == j of row
-// (l >> 4) writes group j*4 + (l >> 4).
+// wave's window, j = 0..3). In chunk j a group of GS elements covers GS/4
+// consecutive lanes (8, 16 or 32), which reduce min / max with DPP (and one
+// cross-row shuffle for 32 lanes); the first four lanes of each group's lane
+// set write the groups of chunks 0..3.
 // ---------------------------------------------------------------------------
+template <int GS>
 __global__ __launch_bounds__(256) void k_init_minmax(const float4* __restrict__ W, int64_t ngroups,
                                                      float K, float* __restrict__ s,
                                                      float* __restrict__ z) {
+  constexpr int LPG = GS / 4;                           // lanes per group within a chunk
+  constexpr int GPC = 64 / LPG;                         // groups per chunk
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t nvec = ngroups * 16;
-  // Groups never straddle the end (in % 64 == 0): a window past the end holds
+  const int64_t nvec = ngroups * LPG;
+  // Groups never straddle the end (in % GS == 0): a window past the end holds
   // whole groups that are not stored, so its zero fill is never used.
   float4 v[4];
 #pragma unroll
@@ -30,19 +34,57 @@ __global__ __launch_bounds__(256) void k_init_minmax(const float4* __restrict__ 
   float mn[4], mx[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    mn[j] = row16_min(fminf(fminf(v[j].x, v[j].y), fminf(v[j].z, v[j].w)));
-    mx[j] = row16_max(fmaxf(fmaxf(v[j].x, v[j].y), fmaxf(v[j].z, v[j].w)));
+    const float a = fminf(fminf(v[j].x, v[j].y), fminf(v[j].z, v[j].w));
+    const float b = fmaxf(fmaxf(v[j].x, v[j].y), fmaxf(v[j].z, v[j].w));
+    if constexpr (LPG == 8) {
+      mn[j] = row8_min(a);
+      mx[j] = row8_max(b);
+    } else {
+      mn[j] = row16_min(a);
+      mx[j] = row16_max(b);
+      if constexpr (LPG == 32) {
+        mn[j] = fminf(mn[j], __shfl_xor(mn[j], 16));
+        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 16));
+      }
+    }
   }
-  const int sel = lane & 15;
+  const int sel = lane % LPG;
   if (sel < 4) {
     const float a = sel == 0 ? mn[0] : sel == 1 ? mn[1] : sel == 2 ? mn[2] : mn[3];
     const float b = sel == 0 ? mx[0] : sel == 1 ? mx[1] : sel == 2 ? mx[2] : mx[3];
-    const int64_t g = wave * 16 + sel * 4 + (lane >> 4);
+    const int64_t g = wave * 4 * GPC + sel * GPC + lane / LPG;
     if (g < ngroups) {
       const float sv = fmaxf((b - a) / K, kSMin);
       s[g] = sv;
       z[g] = __builtin_rintf(-a / sv);
     }
+  }
+}
+
+// Channel-wise init (one group per weight row): a wave per row.
+__global__ __launch_bounds__(256) void k_init_rows(const float4* __restrict__ W, int64_t out, int64_t vpr,
+                                                   float K, float* __restrict__ s, float* __restrict__ z) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= out) return;                               // uniform per wave
+  const float4* p = W + row * vpr;
+  float a = __builtin_inff(), b = -__builtin_inff();
+#pragma unroll 4
+  for (int64_t i = lane; i < vpr; i += 64) {
+    const float4 v = p[i];
+    a = fminf(a, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+    b = fmaxf(b, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  }
+  a = row16_min(a);
+  b = row16_max(b);
+  a = fminf(a, __shfl_xor(a, 16));
+  b = fmaxf(b, __shfl_xor(b, 16));
+  a = fminf(a, __shfl_xor(a, 32));
+  b = fmaxf(b, __shfl_xor(b, 32));
+  if (lane == 0) {
+    const float sv = fmaxf((b - a) / K, kSMin);
+    s[row] = sv;
+    z[row] = __builtin_rintf(-a / sv);
   }
 }
 
@@ -52,11 +94,11 @@ __global__ __launch_bounds__(256) void k_init_minmax(const float4* __restrict__ 
 __global__ __launch_bounds__(256) void k_quant_codes(const float4* __restrict__ W,
                                                      const float* __restrict__ s,
                                                      const float* __restrict__ z, int64_t nvec,
-                                                     float K, uint32_t* __restrict__ codes,
+                                                     FastDiv vpg, float K, uint32_t* __restrict__ codes,
                                                      uint2* __restrict__ w_hat) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= nvec) return;
-  int64_t g = i >> 4;                    // 16 float4 per group of 64
+  int64_t g = vpg.div((uint32_t)i);      // float4 -> group (group / 4 float4 per group)
   float sv = s[g];
   float zr = round_clamp_zero(z[g], K);
   float4 w = W[i];
@@ -74,12 +116,13 @@ __global__ __launch_bounds__(256) void k_quant_codes(const float4* __restrict__ 
 // ---------------------------------------------------------------------------
 template <int N>
 __global__ __launch_bounds__(256) void k_pack(const float4* __restrict__ W, const float* __restrict__ s,
-                                              const float* __restrict__ z, int64_t nchunks,
-                                              uint8_t* __restrict__ Wq, float* __restrict__ zround) {
+                                              const float* __restrict__ z, int64_t nchunks, FastDiv cpg,
+                                              uint32_t cpg_n, uint8_t* __restrict__ Wq,
+                                              float* __restrict__ zround) {
   constexpr float K = (float)((1 << N) - 1);
   int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;   // chunk of 8 elements
   if (c >= nchunks) return;
-  int64_t g = c >> 3;
+  int64_t g = cpg.div((uint32_t)c);                        // group / 8 chunks per group
   float sv = s[g];
   float zr = round_clamp_zero(z[g], K);
   float4 a = W[2 * c], b = W[2 * c + 1];
@@ -97,7 +140,7 @@ __global__ __launch_bounds__(256) void k_pack(const float4* __restrict__ W, cons
     dst[1] = (uint8_t)(word >> 8);
     dst[2] = (uint8_t)(word >> 16);
   }
-  if (zround && (c & 7) == 0) zround[g] = zr;
+  if (zround && c == g * cpg_n) zround[g] = zr;           // first chunk of the group
 }
 
 // ---------------------------------------------------------------------------
@@ -107,11 +150,11 @@ __global__ __launch_bounds__(256) void k_pack(const float4* __restrict__ W, cons
 // ---------------------------------------------------------------------------
 template <int N>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ Wq, const float* __restrict__ s,
-                                                 const float* __restrict__ z, int64_t nchunks,
+                                                 const float* __restrict__ z, int64_t nchunks, FastDiv cpg,
                                                  uint4* __restrict__ w_hat) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= nchunks) return;
-  const int64_t g = c >> 3;
+  const int64_t g = cpg.div((uint32_t)c);
   const float sv = s[g], zv = z[g];
   const uint8_t* src = Wq + c * N;
   uint32_t word;
@@ -137,8 +180,8 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ Wq,
 // ---------------------------------------------------------------------------
 template <int SRC, int N>
 __global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, const float* __restrict__ s,
-                                                 const float* __restrict__ z, int64_t out, int64_t in, float K,
-                                                 uint16_t* __restrict__ w_hat_t) {
+                                                 const float* __restrict__ z, int64_t out, int64_t in, int64_t G,
+                                                 FastDiv gdiv, float K, uint16_t* __restrict__ w_hat_t) {
   constexpr int TO = 128, TIN = 64;                      // tile rows (out), cols (in)
   // LDS tile T[c][o] (c: input column, o: output row; 256 bytes per c). The
   // 16-byte chunk h of row c sits at h ^ 2 (c / 8): the 64 four-byte writes of
@@ -147,12 +190,12 @@ __global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, 
   __shared__ __attribute__((aligned(16))) uint16_t T[TIN * TO];
   const int bo = SRC == 1 ? blockIdx.x : blockIdx.y, bi = SRC == 1 ? blockIdx.y : blockIdx.x;
   const int64_t o0 = (int64_t)bo * TO, i0 = (int64_t)bi * TIN;
-  const int64_t G = in / kGroup, g = i0 / kGroup;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int item = threadIdx.x + 256 * q;
     const int rp = item >> 3, co = item & 7;            // row pair, column octet
     const int64_t o = o0 + 2 * rp;
+    const int64_t g = gdiv.div((uint32_t)(i0 + co * 8));  // the octet's group
     float h[2][8];
     if (o < out) {
 #pragma unroll
@@ -205,62 +248,95 @@ __global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, 
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
 
-void launch_init_minmax(const float* W, int64_t out, int64_t in, int bits, float* s, float* z,
-                        hipStream_t st) {
-  int64_t ngroups = out * (in / kGroup);
-  LaunchTimer t("init_minmax", st);
-  hipLaunchKernelGGL(k_init_minmax, dim3(blocks_for(ngroups, 64)), dim3(256), 0, st,
-                     (const float4*)W, ngroups, (float)((1 << bits) - 1), s, z);
+// Zero fill (the accumulation target of the gradient epilogues for groups
+// wider than 64 columns).
+__global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, int64_t n4, float* __restrict__ tail,
+                                                   int ntail) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i < ntail) tail[i] = 0.f;
 }
 
-void launch_quant_codes(const float* W, const float* s, const float* z, int64_t out, int64_t in,
+void launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  LaunchTimer t("fill_zero", st);
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks_for(n4 > 0 ? n4 : 1, 256)), dim3(256), 0, st, (float4*)p, n4,
+                     p + n4 * 4, (int)(n - n4 * 4));
+}
+
+void launch_init_minmax(const float* W, int64_t out, int64_t in, int group, int bits, float* s, float* z,
+                        hipStream_t st) {
+  const int64_t ngroups = out * (in / group);
+  const float K = (float)((1 << bits) - 1);
+  LaunchTimer t("init_minmax", st);
+  if (group == in && group != 32 && group != 64 && group != 128) {
+    hipLaunchKernelGGL(k_init_rows, dim3(blocks_for(out, 4)), dim3(256), 0, st, (const float4*)W, out, in / 4, K,
+                       s, z);
+  } else if (group == 32) {
+    hipLaunchKernelGGL(k_init_minmax<32>, dim3(blocks_for(ngroups, 128)), dim3(256), 0, st, (const float4*)W,
+                       ngroups, K, s, z);
+  } else if (group == 64) {
+    hipLaunchKernelGGL(k_init_minmax<64>, dim3(blocks_for(ngroups, 64)), dim3(256), 0, st, (const float4*)W,
+                       ngroups, K, s, z);
+  } else {
+    hipLaunchKernelGGL(k_init_minmax<128>, dim3(blocks_for(ngroups, 32)), dim3(256), 0, st, (const float4*)W,
+                       ngroups, K, s, z);
+  }
+}
+
+void launch_quant_codes(const float* W, const float* s, const float* z, int64_t out, int64_t in, int group,
                         int bits, uint8_t* codes, uint16_t* w_hat, hipStream_t st) {
   int64_t nvec = out * in / 4;
   LaunchTimer t(codes ? "quant_codes" : "quant_w_hat", st);
   hipLaunchKernelGGL(k_quant_codes, dim3(blocks_for(nvec, 256)), dim3(256), 0, st,
-                     (const float4*)W, s, z, nvec, (float)((1 << bits) - 1), (uint32_t*)codes,
-                     (uint2*)w_hat);
+                     (const float4*)W, s, z, nvec, FastDiv::make((uint32_t)group / 4), (float)((1 << bits) - 1),
+                     (uint32_t*)codes, (uint2*)w_hat);
 }
 
-void launch_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
+void launch_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in, int group, int bits,
                  uint8_t* Wq, float* zround, hipStream_t st) {
   int64_t nchunks = out * in / 8;
   dim3 grid(blocks_for(nchunks, 256));
+  const uint32_t cpg = (uint32_t)group / 8;
+  const FastDiv fd = FastDiv::make(cpg);
   LaunchTimer t("pack", st);
   if (bits == 2)
-    hipLaunchKernelGGL(k_pack<2>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, Wq, zround);
+    hipLaunchKernelGGL(k_pack<2>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
   else if (bits == 3)
-    hipLaunchKernelGGL(k_pack<3>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, Wq, zround);
+    hipLaunchKernelGGL(k_pack<3>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
   else
-    hipLaunchKernelGGL(k_pack<4>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, Wq, zround);
+    hipLaunchKernelGGL(k_pack<4>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
 }
 
-void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                    uint16_t* w_hat, hipStream_t st) {
+void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int group,
+                    int bits, uint16_t* w_hat, hipStream_t st) {
   const int64_t nchunks = out * in / 8;
   dim3 grid(blocks_for(nchunks, 256));
+  const FastDiv fd = FastDiv::make((uint32_t)group / 8);
   LaunchTimer t("dequant", st);
-  if (bits == 2) hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
-  else if (bits == 3) hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
-  else hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, st, Wq, s, z, nchunks, (uint4*)w_hat);
+  if (bits == 2) hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
+  else if (bits == 3) hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
+  else hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
 }
 
-void launch_w_hat_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                    uint16_t* w_hat_t, hipStream_t st) {
+void launch_w_hat_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int group,
+                    int bits, uint16_t* w_hat_t, hipStream_t st) {
   const dim3 grid((unsigned)(in / 64), (unsigned)((out + 127) / 128));
   LaunchTimer t("quant_w_hat_t", st);
-  hipLaunchKernelGGL((k_w_hat_t<0, 0>), grid, dim3(256), 0, st, W, s, z, out, in, (float)((1 << bits) - 1),
-                     w_hat_t);
+  hipLaunchKernelGGL((k_w_hat_t<0, 0>), grid, dim3(256), 0, st, W, s, z, out, in, in / group,
+                     FastDiv::make((uint32_t)group), (float)((1 << bits) - 1), w_hat_t);
 }
 
-void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                      uint16_t* w_hat_t, hipStream_t st) {
+void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int group,
+                      int bits, uint16_t* w_hat_t, hipStream_t st) {
   const dim3 grid((unsigned)((out + 127) / 128), (unsigned)(in / 64));
   const float K = (float)((1 << bits) - 1);
+  const int64_t G = in / group;
+  const FastDiv fd = FastDiv::make((uint32_t)group);
   LaunchTimer t("dequant_t", st);
-  if (bits == 2) hipLaunchKernelGGL((k_w_hat_t<1, 2>), grid, dim3(256), 0, st, Wq, s, z, out, in, K, w_hat_t);
-  else if (bits == 3) hipLaunchKernelGGL((k_w_hat_t<1, 3>), grid, dim3(256), 0, st, Wq, s, z, out, in, K, w_hat_t);
-  else hipLaunchKernelGGL((k_w_hat_t<1, 4>), grid, dim3(256), 0, st, Wq, s, z, out, in, K, w_hat_t);
+  if (bits == 2) hipLaunchKernelGGL((k_w_hat_t<1, 2>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
+  else if (bits == 3) hipLaunchKernelGGL((k_w_hat_t<1, 3>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
+  else hipLaunchKernelGGL((k_w_hat_t<1, 4>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
 }
 
 }  // namespace qat

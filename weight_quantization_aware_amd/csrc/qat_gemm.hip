@@ -33,10 +33,10 @@ constexpr const char* gemm_label() {
   return NB == 1 ? "gemm_dx" : "gemm_fwd";
 }
 
-template <int BM, int BN, int S, int WGM, int WGN, int AMN, int BMN, int EP, int NB>
+template <int BM, int BN, int S, int WGM, int WGN, int AMN, int BMN, int EP, int NB, int GM = 0>
 void launch_bf16(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<kBf16, EP, NB>(), st);
-  hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, AMN, BMN, EP, NB>), dim3((unsigned)tiles(a, BM, BN)),
+  hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, GM, AMN, BMN, EP, NB>), dim3((unsigned)tiles(a, BM, BN)),
                      dim3(64 * WGM * WGN), 0, st, a);
 }
 
@@ -57,6 +57,21 @@ void launch_pick(const GemmArgs& a, hipStream_t st) {
   } else {
     launch_bf16<128, 128, 4, 2, 2, AMN, BMN, EP, NB>(a, st);
   }
+}
+
+// Gradient GEMMs for groups other than 64 (GM 1: groups of 32; GM 2: wider
+// groups, accumulated into zero-filled ds and dz): two tile configurations.
+template <int EP, int NB, int GM>
+void launch_pick_grads_gm(const GemmArgs& a, hipStream_t st) {
+  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kMNContig, kMNContig, EP, NB, GM>(a, st);
+  else launch_bf16<128, 128, 4, 2, 2, kMNContig, kMNContig, EP, NB, GM>(a, st);
+}
+
+template <int EP, int NB>
+void launch_grads(const GemmArgs& a, hipStream_t st) {
+  if (a.group == 64) launch_pick<kMNContig, kMNContig, EP, NB>(a, st);
+  else if (a.group == 32) launch_pick_grads_gm<EP, NB, 1>(a, st);
+  else launch_pick_grads_gm<EP, NB, 2>(a, st);
 }
 
 template <int BL, int NB>
@@ -85,10 +100,10 @@ void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {
 }
 
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st) {
-  if (epi == kSteGrads) launch_pick<kMNContig, kMNContig, kSteGrads, 0>(a, st);
-  else if (bits == 2) launch_pick<kMNContig, kMNContig, kE2eScaleGrad, 2>(a, st);
-  else if (bits == 3) launch_pick<kMNContig, kMNContig, kE2eScaleGrad, 3>(a, st);
-  else launch_pick<kMNContig, kMNContig, kE2eScaleGrad, 4>(a, st);
+  if (epi == kSteGrads) launch_grads<kSteGrads, 0>(a, st);
+  else if (bits == 2) launch_grads<kE2eScaleGrad, 2>(a, st);
+  else if (bits == 3) launch_grads<kE2eScaleGrad, 3>(a, st);
+  else launch_grads<kE2eScaleGrad, 4>(a, st);
 }
 
 }  // namespace qat

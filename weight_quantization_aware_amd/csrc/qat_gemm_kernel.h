@@ -226,7 +226,8 @@ struct DmaTileOf<ROWS, BK, 1, NW> { using T = DmaTileMN<ROWS, BK, NW>; };
 //     w * fl32(1/s), within 3 ulp of fl32(w/s); where that interval could
 //     hold a half-integer the element is redone with the correctly rounded
 //     division, so the codes are exactly the fp32 quantiser's.
-// With BK = 32 a slab is half a quantisation group (same s, z).
+// With BK = 32 a slab lies inside one quantisation group (groups of 32, 64,
+// 128 or a whole row), so one (s, z) pair per row and slab.
 template <int ROWS, int BK, int KIND, int NB>
 struct DmaRing {
   using L = LdsLayout<BK, kLdsSlots>;
@@ -240,9 +241,11 @@ struct DmaRing {
   uint32_t vq[NI_Q], vs[NI_S];
   int wave;
   float K;
+  FastDiv gdiv;                                                    // k -> group index
   __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes, int row0, int nrows, const float* s,
-                                       const float* z, int64_t G, float K_) {
+                                       const float* z, int64_t G, int group, float K_) {
     K = K_;
+    gdiv = FastDiv::make((uint32_t)group);
     rq = buffer_rsrc((const uint8_t*)Wsrc + (int64_t)row0 * row_bytes, (int64_t)(nrows - row0) * row_bytes);
     rsz[0] = buffer_rsrc(s + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
     rsz[1] = buffer_rsrc(z + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
@@ -262,7 +265,7 @@ struct DmaRing {
   // lds_p: this slab's ring entry: [ROWS][DW] weight dwords, then s[ROWS], z[ROWS].
   __device__ __forceinline__ void issue(uint32_t lds_p, int k0) const {
     const uint32_t cb = KIND == kPacked ? (uint32_t)(k0 * NB / 8) : (uint32_t)(k0 * 4);
-    const uint32_t gb = (uint32_t)((k0 / 64) * 4);
+    const uint32_t gb = gdiv.div((uint32_t)k0) * 4;               // the slab lies inside one group
 #pragma unroll
     for (int q = 0; q < NI_Q; ++q) dma4(rq, lds_p + (uint32_t)((wave * NI_Q + q) * 256), vq[q] + cb);
 #pragma unroll
@@ -319,8 +322,8 @@ struct DmaRing {
 
 template <int BL, class Ld>
 __device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
-  if constexpr (BL == kFp32Quant) l.init(a.B, a.ldb * 4, n0, a.N, a.s, a.z, a.G, a.Kq);
-  else l.init(a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.Kq);
+  if constexpr (BL == kFp32Quant) l.init(a.B, a.ldb * 4, n0, a.N, a.s, a.z, a.G, a.group, a.Kq);
+  else l.init(a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.group, a.Kq);
 }
 
 // Four consecutive codes c0..c0+3 (c0 % 4 == 0) of a packed row.
@@ -371,15 +374,20 @@ __device__ __forceinline__ void mfma_drain() {
 // A 64-column quantisation group is 4 j-tiles x 4 registers of one lane plus a
 // reduction over the 4 lanes that share (lane & 15).
 // ---------------------------------------------------------------------------
-// Inputs of one (row, group) step of the gradient epilogues.
+// Inputs of one (row, 64-column chunk) step of the gradient epilogues: the
+// chunk's group(s) s and z (two groups when groups are 32 wide).
 template <int EP>
 struct EpiIn {
-  float s, z;
+  float s[2], z[2];
   float4 w[4];          // kSteGrads: W[o][cg + 16 jj + cq .. + 3]
   uint32_t c[4];        // kE2eScaleGrad: the same four codes per jj
 };
 
-template <int EP, int NB, int TI, int TJ, int WN>
+// Group modes of the gradient epilogues (GM): 0 groups of 64 columns, one per
+// chunk; 1 groups of 32, two per chunk (j-tiles 0-1 and 2-3); 2 wider groups
+// (128 or a whole row): each chunk adds its partial sums into ds and dz, which
+// the caller zero-fills first.
+template <int EP, int NB, int GM, int TI, int TJ, int WN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
                                               int wm0, int wn0, int lane) {
   const int rl = lane & 15, cq = 4 * (lane >> 4);
@@ -398,17 +406,27 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
     }
   } else {
     // Rows are weight rows o (A = dY^T), columns inputs c (B = X^T). Steps
-    // t = (i, g) walk the lane's rows and 64-column groups; the loads of step
+    // t = (i, g) walk the lane's rows and 64-column chunks; the loads of step
     // t + 1 are issued before step t is computed.
     constexpr int NG = WN / 64, NT = TI * NG;
+    constexpr int NH = GM == 1 ? 2 : 1;                  // groups per chunk
+    const FastDiv gdiv = FastDiv::make((uint32_t)a.group);
     auto row_of = [&](int t) { return m0 + wm0 + (t / NG) * 16 + rl; };
     auto col_of = [&](int t) { return n0 + wn0 + (t % NG) * 64; };
+    auto group_of = [&](int o, int cg) -> int64_t {     // first group of the chunk at column cg
+      if constexpr (GM == 0) return (int64_t)o * a.G + cg / 64;
+      else if constexpr (GM == 1) return (int64_t)o * a.G + cg / 32;
+      else return (int64_t)o * a.G + gdiv.div((uint32_t)cg);
+    };
     auto load = [&](int t, EpiIn<EP>& in) {
       const int o = row_of(t), cg = col_of(t);
       if (o < a.M && cg < a.N) {
-        const int64_t gi = (int64_t)o * a.G + cg / 64;
-        in.s = a.s[gi];
-        in.z = a.z[gi];
+        const int64_t gi = group_of(o, cg);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          in.s[h] = a.s[gi + h];
+          in.z[h] = a.z[gi + h];
+        }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           if constexpr (EP == kSteGrads) in.w[jj] = *(const float4*)(a.W + (int64_t)o * a.ldw + cg + jj * 16 + cq);
@@ -424,23 +442,30 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
       const int i = t / NG, g = t % NG;
       const int o = row_of(t), cg = col_of(t);
       const bool ok = o < a.M && cg < a.N;
-      const int64_t gi = (int64_t)(ok ? o : 0) * a.G + cg / 64;
-      float ps = 0.f, pz = 0.f;
+      const int64_t gi = ok ? group_of(o, cg) : 0;
+      float ps[NH], pz[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) ps[h] = pz[h] = 0.f;
       if (ok) {
         if constexpr (EP == kSteGrads) {
-          const float zr = round_clamp_zero(cur.z, a.Kq);
-          const float rcp = 1.0f / cur.s;
+          float zr[NH], rcp[NH];
+#pragma unroll
+          for (int h = 0; h < NH; ++h) {
+            zr[h] = round_clamp_zero(cur.z[h], a.Kq);
+            rcp[h] = 1.0f / cur.s[h];
+          }
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
+            const int h = NH == 2 ? (jj >> 1) : 0;
             const f32x4 gw = acc[g * 4 + jj][i];
             const float wv[4] = {cur.w[jj].x, cur.w[jj].y, cur.w[jj].z, cur.w[jj].w};
             float dw[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const QElem e = quant_elem_rcp(wv[r], cur.s, rcp, zr, a.Kq);
+              const QElem e = quant_elem_rcp(wv[r], cur.s[h], rcp[h], zr[h], a.Kq);
               dw[r] = e.m ? gw[r] : 0.0f;
-              ps += gw[r] * (e.m ? (__builtin_rintf(e.u) - e.u) : (e.q - zr));
-              pz += e.m ? 0.0f : gw[r];
+              ps[h] += gw[r] * (e.m ? (__builtin_rintf(e.u) - e.u) : (e.q - zr[h]));
+              pz[h] += e.m ? 0.0f : gw[r];
             }
             if (a.dW)
               *(float4*)(a.dW + (int64_t)o * a.ldw + cg + jj * 16 + cq) = make_float4(dw[0], dw[1], dw[2], dw[3]);
@@ -448,24 +473,36 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
         } else {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
+            const int h = NH == 2 ? (jj >> 1) : 0;
             const f32x4 gw = acc[g * 4 + jj][i];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float qv = (float)((cur.c[jj] >> (NB * r)) & ((1u << NB) - 1));
-              ps += gw[r] * (qv - cur.z);
-              pz += gw[r];
+              ps[h] += gw[r] * (qv - cur.z[h]);
+              pz[h] += gw[r];
             }
           }
         }
       }
-      // the 4 lanes with the same (lane & 15) hold the 4 column quarters of the group
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      pz += __shfl_xor(pz, 16);
-      pz += __shfl_xor(pz, 32);
+      // the 4 lanes with the same (lane & 15) hold the 4 column quarters of the chunk
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        ps[h] += __shfl_xor(ps[h], 16);
+        ps[h] += __shfl_xor(ps[h], 32);
+        pz[h] += __shfl_xor(pz[h], 16);
+        pz[h] += __shfl_xor(pz[h], 32);
+      }
       if (ok && lane < 16 && a.ds) {
-        a.ds[gi] = ps;
-        if (a.dz) a.dz[gi] = -cur.s * pz;
+        if constexpr (GM == 2) {
+          atomicAdd(a.ds + gi, ps[0]);
+          if (a.dz) atomicAdd(a.dz + gi, -cur.s[0] * pz[0]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < NH; ++h) {
+            a.ds[gi + h] = ps[h];
+            if (a.dz) a.dz[gi + h] = -cur.s[h] * pz[h];
+          }
+        }
       }
       cur = nxt;
     }
@@ -494,7 +531,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
 // keeps that order: LDS reads run a full k-step ahead of their MFMAs and the
 // DMA issue is spread over the k-step.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int AMN, int BMN, int EP, int NB>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int GM, int AMN, int BMN, int EP, int NB>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a) {
   constexpr int NW = WGM * WGN;
   using LA = typename DmaTileOf<BM, BK, AMN, NW>::T;
@@ -605,7 +642,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a) {
   wait_vmcnt<0>();                                       // drain the trailing re-loads
   __syncthreads();
   mfma_drain();
-  gemm_epilogue<EP, NB, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
+  gemm_epilogue<EP, NB, GM, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,7 +770,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
 #undef QAT_SLAB
   wait_vmcnt<0>();                            // drain the trailing re-issued DMAs
   __syncthreads();
-  gemm_epilogue<kStoreBf16, NB, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
+  gemm_epilogue<kStoreBf16, NB, 0, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
 }
 
 }  // namespace qat

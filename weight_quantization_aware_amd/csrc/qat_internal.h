@@ -20,20 +20,23 @@ class LaunchTimer {
 };
 
 // ---- HBM-bound kernels (qat_elementwise.hip) ----
-void launch_init_minmax(const float* W, int64_t out, int64_t in, int bits, float* s, float* z,
+// `group` is 32, 64, 128 or in (channel-wise); in % group == 0.
+void launch_init_minmax(const float* W, int64_t out, int64_t in, int group, int bits, float* s, float* z,
                         hipStream_t st);
-void launch_quant_codes(const float* W, const float* s, const float* z, int64_t out, int64_t in,
+void launch_quant_codes(const float* W, const float* s, const float* z, int64_t out, int64_t in, int group,
                         int bits, uint8_t* codes, uint16_t* w_hat, hipStream_t st);
-void launch_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
+void launch_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in, int group, int bits,
                  uint8_t* Wq, float* zround, hipStream_t st);
-void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                    uint16_t* w_hat, hipStream_t st);
+void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int group,
+                    int bits, uint16_t* w_hat, hipStream_t st);
 // W_hat^T [in][out] bf16 for the dX GEMM (needs out % 64 == 0): from the fp32
 // master weight (fake-quant) or from packed codes (E2E-QP).
-void launch_w_hat_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                    uint16_t* w_hat_t, hipStream_t st);
-void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int bits,
-                      uint16_t* w_hat_t, hipStream_t st);
+void launch_w_hat_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int group,
+                    int bits, uint16_t* w_hat_t, hipStream_t st);
+void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int group,
+                      int bits, uint16_t* w_hat_t, hipStream_t st);
+// p[0 .. n) = 0 with a plain store kernel (usable under stream capture).
+void launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // ---- MFMA GEMMs (qat_gemm.hip) ----
 // C[M, N] = sum_k A[m, k] * B[n, k] in bf16 with fp32 accumulation. Each operand
@@ -49,6 +52,7 @@ struct GemmArgs {
   const float* s;      // [weight rows][G] step sizes (fused loaders / epilogues)
   const float* z;
   int64_t G;           // groups per weight row
+  int group;           // elements per group: 32, 64, 128, or the row length (channel-wise)
   float Kq;            // 2^bits - 1
   uint16_t* C;         // bf16 output [M][ldc]
   int64_t ldc;
