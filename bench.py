@@ -244,7 +244,7 @@ def main():
 
     extras = None
     if not args.no_extras:
-        extras = context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp)
+        extras = context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp, X, dY)
         roofline["frac_of_measured_peak"] = round(
             achieved / (extras["measured_peaks"]["mfma_bf16_tflops"] if kind == "mfma"
                         else extras["measured_peaks"]["hbm_read_gbs"]), 4)
@@ -299,7 +299,7 @@ def _clocks():
         return None
 
 
-def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp):
+def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp, X, dY):
     """Context beside the headline (not part of `value`):
     - practical peaks on this GPU: a register-resident bf16 MFMA loop and a
       read stream over 1 GiB (beyond the 256 MiB MALL);
@@ -307,6 +307,8 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp)
       read (not written, so no dirty lines are left to write back), which
       evicts W from L2 and the MALL (median of 10); at the q_proj weight
       (64 MiB) and at the Llama-2-70B gate weight (896 MiB);
+    - the q_proj fake-quant forward + backward at groups of 32, 64, 128 and
+      channel-wise (one group per row);
     - the Llama-2-7B block of seven w3g64 linears (q, k, v, o 4096x4096; gate,
       up 11008x4096; down 4096x11008; 2048 tokens): fake-quant forward +
       backward of all seven, 2486.79 GFLOP counted;
@@ -372,6 +374,27 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp)
     pack5_bytes = n5 * (4 + 2 / 8) + 3 * lin5.out * G5 * 4
     del W5, s5, z5, Wq5, zp5, big
 
+    # the q_proj step's fake-quant forward + backward at the other group sizes
+    groups = {}
+    M2, out2, in2 = X.shape[0], W.shape[0], W.shape[1]
+    ws2 = Q.workspace(Q.fakequant_ws_bytes(M2, out2, in2), dev)
+    Y2 = torch.empty(M2, out2, dtype=torch.bfloat16, device=dev)
+    dX2 = torch.empty(M2, in2, dtype=torch.bfloat16, device=dev)
+    dW2 = torch.empty(out2, in2, device=dev)
+    for gname, gsize in (("32", 32), ("64", 64), ("128", 128), ("row", in2)):
+        sg = torch.empty(out2, in2 // gsize, device=dev)
+        zg = torch.empty_like(sg)
+        dsg, dzg = torch.empty_like(sg), torch.empty_like(sg)
+        Q.qat_init_minmax(W, bits, sg, zg, group=gsize)
+
+        def fq(sg=sg, zg=zg, dsg=dsg, dzg=dzg, gsize=gsize):
+            Q.qat_fakequant_linear_fwd(X, W, sg, zg, bits, Y2, ws=ws2, group=gsize)
+            Q.qat_fakequant_linear_bwd(dY, X, W, sg, zg, bits, dX=dX2, dW=dW2, ds=dsg, dz=dzg, ws=ws2,
+                                       group=gsize)
+        tg = ev_time(fq, 10)
+        groups[gname] = {"ms": round(tg * 1e3, 4), "tflops": round(6.0 * M2 * in2 * out2 / tg / 1e12, 1)}
+    del ws2, Y2, dX2, dW2
+
     # the C3 block
     c3 = []
     for lin in synth.config(3):
@@ -409,6 +432,7 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp)
         "pack_cold_70b_gate_w2": {"us": round(t_pack5 * 1e6, 2), "gbs": round(pack5_bytes / t_pack5 / 1e9, 1)},
         "c3_block_w3g64": {"gflop": round(gflop, 2), "ms": round(t_c3 * 1e3, 4),
                            "tflops": round(gflop / t_c3 / 1e3, 1)},
+        "q_proj_fwd_bwd_by_group": groups,
         "clocks": _clocks(),
     }
 
