@@ -4,7 +4,11 @@ oracle. Same bars as at group 64: s, z, codes, W_hat bits, packed bytes and
 zp bit-exact; bf16 Y and dX within relative Frobenius 2e-2; fp32 dW, ds, dz
 within 1e-5; the fused (no-workspace) forwards bit-identical to the staged
 ones. Shapes cover both gradient tile configurations, ragged output tiles and
-a channel-wise row length that is not a power of two (192).
+a channel-wise row length that is not a power of two (192), and each way
+the gradient epilogue finishes a group: stored per 64- or 32-column chunk,
+summed over the tile's chunks and stored (group 128, or a whole row that fits
+one tile), or summed per tile and accumulated (whole rows over several
+tiles).
 """
 import numpy as np
 import pytest
@@ -29,6 +33,9 @@ CASES = [
     (128, 256, 256, 32, 4),
     (100, 4096, 4096, 128, 2),
     (100, 4096, 4096, 32, 3),
+    (64, 192, 128, None, 3),          # whole row = one 128-column tile: stored
+    (100, 4096, 4096, None, 2),       # whole row over 16 tiles of 256: accumulated
+    (16, 65536, 256, None, 4),        # whole row = one 256-column tile: stored
 ]
 
 

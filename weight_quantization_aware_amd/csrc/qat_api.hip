@@ -239,15 +239,6 @@ static qat::GemmArgs grads_args(const uint16_t* dY, const uint16_t* X, const flo
   return a;
 }
 
-// Groups wider than the epilogue's 64-column chunks are summed by atomic adds
-// into ds and dz, which start at zero.
-static void zero_wide_group_grads(float* ds, float* dz, int64_t out, int64_t in, int group, hipStream_t stream) {
-  if (group <= 64) return;
-  const int64_t n = out * (in / group);
-  if (ds) qat::launch_fill_zero(ds, n, stream);
-  if (dz) qat::launch_fill_zero(dz, n, stream);
-}
-
 QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
                                          const float* s, const float* z, int64_t M, int64_t out,
                                          int64_t in, int32_t group, int32_t bits, uint16_t* dX,
@@ -273,7 +264,6 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
     launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
   if (dW || ds) {
-    zero_wide_group_grads(ds, dz, out, in, group, stream);
     qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, group, bits);
     a.W = W;
     a.ldw = in;
@@ -348,7 +338,6 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
     qat::launch_dequant_t(Wq, s, z, out, in, group, bits, w_hat, stream);
     launch_dx(dY, w_hat, M, out, in, dX, stream);
   }
-  zero_wide_group_grads(ds, dz, out, in, group, stream);
   qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, group, bits);
   a.Wq = Wq;
   a.ldq = in * bits / 8;

@@ -59,8 +59,10 @@ void launch_pick(const GemmArgs& a, hipStream_t st) {
   }
 }
 
-// Gradient GEMMs for groups other than 64 (GM 1: groups of 32; GM 2: wider
-// groups, accumulated into zero-filled ds and dz): two tile configurations.
+// Gradient GEMMs for groups other than 64: two tile configurations. Groups
+// of 32 (GM 1) and groups that tile BN (GM 2: 128, or a short whole row) are
+// stored directly; whole rows wider than BN (GM 3) are accumulated per tile
+// into ds and dz, zero-filled here first.
 template <int EP, int NB, int GM>
 void launch_pick_grads_gm(const GemmArgs& a, hipStream_t st) {
   if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kMNContig, kMNContig, EP, NB, GM>(a, st);
@@ -69,9 +71,21 @@ void launch_pick_grads_gm(const GemmArgs& a, hipStream_t st) {
 
 template <int EP, int NB>
 void launch_grads(const GemmArgs& a, hipStream_t st) {
-  if (a.group == 64) launch_pick<kMNContig, kMNContig, EP, NB>(a, st);
-  else if (a.group == 32) launch_pick_grads_gm<EP, NB, 1>(a, st);
-  else launch_pick_grads_gm<EP, NB, 2>(a, st);
+  if (a.group == 64) {
+    launch_pick<kMNContig, kMNContig, EP, NB>(a, st);
+  } else if (a.group == 32) {
+    launch_pick_grads_gm<EP, NB, 1>(a, st);
+  } else {
+    const int bn = tiles(a, 256, 256) >= 256 ? 256 : 128;
+    if (bn % a.group == 0) {
+      launch_pick_grads_gm<EP, NB, 2>(a, st);
+    } else {
+      const int64_t n = (int64_t)a.M * a.G;
+      if (a.ds) launch_fill_zero(a.ds, n, st);
+      if (a.dz) launch_fill_zero(a.dz, n, st);
+      launch_pick_grads_gm<EP, NB, 3>(a, st);
+    }
+  }
 }
 
 template <int BL, int NB>

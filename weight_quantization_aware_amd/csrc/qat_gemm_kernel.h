@@ -384,12 +384,16 @@ struct EpiIn {
 };
 
 // Group modes of the gradient epilogues (GM): 0 groups of 64 columns, one per
-// chunk; 1 groups of 32, two per chunk (j-tiles 0-1 and 2-3); 2 wider groups
-// (128 or a whole row): each chunk adds its partial sums into ds and dz, which
-// the caller zero-fills first.
-template <int EP, int NB, int GM, int TI, int TJ, int WN>
+// chunk; 1 groups of 32, two per chunk (j-tiles 0-1 and 2-3); 2 groups of
+// 64 c columns that tile BN (128, or a whole row no wider than the tile): the
+// chunk sums meet in LDS (`red`, free once the main loop has drained) and
+// one thread per (row, group) adds the group's c chunks and stores; 3 whole
+// rows wider than the tile: the same LDS sum over all of the tile's chunks,
+// then one atomic add per row and tile into ds and dz, which the launcher
+// zero-fills first.
+template <int EP, int NB, int GM, int BM, int BN, int TI, int TJ, int WN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
-                                              int wm0, int wn0, int lane) {
+                                              int wm0, int wn0, int lane, float* red) {
   const int rl = lane & 15, cq = 4 * (lane >> 4);
   if constexpr (EP == kStoreBf16) {
 #pragma unroll
@@ -492,19 +496,46 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
         pz[h] += __shfl_xor(pz[h], 16);
         pz[h] += __shfl_xor(pz[h], 32);
       }
-      if (ok && lane < 16 && a.ds) {
-        if constexpr (GM == 2) {
-          atomicAdd(a.ds + gi, ps[0]);
-          if (a.dz) atomicAdd(a.dz + gi, -cur.s[0] * pz[0]);
-        } else {
+      if constexpr (GM >= 2) {
+        // every (chunk, row) slot of the tile is written, zeros outside the problem
+        if (lane < 16) {
+          const int c = wn0 / 64 + g, r = wm0 + i * 16 + rl;
+          red[c * BM + r] = ps[0];
+          red[(BN / 64 + c) * BM + r] = pz[0];
+        }
+      } else if (ok && lane < 16 && a.ds) {
 #pragma unroll
-          for (int h = 0; h < NH; ++h) {
-            a.ds[gi + h] = ps[h];
-            if (a.dz) a.dz[gi + h] = -cur.s[h] * pz[h];
-          }
+        for (int h = 0; h < NH; ++h) {
+          a.ds[gi + h] = ps[h];
+          if (a.dz) a.dz[gi + h] = -cur.s[h] * pz[h];
         }
       }
       cur = nxt;
+    }
+    if constexpr (GM >= 2) {
+      __syncthreads();
+      constexpr int NC = BN / 64;
+      const int cpg = GM == 2 ? a.group / 64 : NC;       // chunks per output
+      const int n_out = BM * (NC / cpg);
+      for (int idx = threadIdx.x; idx < n_out; idx += (int)blockDim.x) {
+        const int r = idx % BM, c0 = (idx / BM) * cpg;
+        const int o = m0 + r, col = n0 + c0 * 64;
+        if (o >= a.M || col >= a.N || !a.ds) continue;
+        float S = 0.f, Z = 0.f;
+        for (int c = c0; c < c0 + cpg; ++c) {
+          S += red[c * BM + r];
+          Z += red[(NC + c) * BM + r];
+        }
+        const int64_t gi = (int64_t)o * a.G + gdiv.div((uint32_t)col);
+        const float dz = -a.s[gi] * Z;
+        if constexpr (GM == 2) {
+          a.ds[gi] = S;
+          if (a.dz) a.dz[gi] = dz;
+        } else {
+          atomicAdd(a.ds + gi, S);
+          if (a.dz) atomicAdd(a.dz + gi, dz);
+        }
+      }
     }
   }
 }
@@ -547,6 +578,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a) {
   constexpr int GAP = NM / NL > 0 ? NM / NL : 1;
   static_assert(NR <= NM && NL * GAP <= NM, "one k-step must cover the reads and the DMA");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+  static_assert(GM < 2 || 2 * (BN / 64) * BM * 4 <= STAGES * STAGE, "LDS holds the chunk sums");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
@@ -642,7 +674,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a) {
   wait_vmcnt<0>();                                       // drain the trailing re-loads
   __syncthreads();
   mfma_drain();
-  gemm_epilogue<EP, NB, GM, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
+  gemm_epilogue<EP, NB, GM, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, (float*)smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,7 +802,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
 #undef QAT_SLAB
   wait_vmcnt<0>();                            // drain the trailing re-issued DMAs
   __syncthreads();
-  gemm_epilogue<kStoreBf16, NB, 0, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane);
+  gemm_epilogue<kStoreBf16, NB, 0, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, nullptr);
 }
 
 }  // namespace qat
