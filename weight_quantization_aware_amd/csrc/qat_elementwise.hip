@@ -248,8 +248,8 @@ __global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, 
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
 
-// Zero fill (the accumulation target of the gradient epilogues for groups
-// wider than 64 columns).
+// Zero fill (the accumulation target of the gradient epilogues for whole-row
+// groups wider than one GEMM tile).
 __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, int64_t n4, float* __restrict__ tail,
                                                    int ntail) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
