@@ -25,7 +25,11 @@ EfficientQAT pages define. Sources (page title -- section / equation):
                Block-AP uses a straight-through estimator through the rounding,
                with gradients for step size, zero point and weight.
 * [Summ-D]     same summary -- Appendix D: each group of g weights shares a
-               step size and an N-bit zero point.
+               step size and an N-bit zero point; stored for deployment, the
+               step size is FP16.
+* [Summ-A-inf] same summary -- Appendix A and section 4: the deployed INT2
+               model's linear-layer matrix-vector product, compared against the
+               FP16 PyTorch linear.
 
 Readings where the pages are silent (the kernel follows the same readings):
 
@@ -34,7 +38,8 @@ Readings where the pages are silent (the kernel follows the same readings):
   rounded fp32 operation in the order written below. Here each such operation
   is done in fp64 and rounded once to fp32, which equals the fp32 result
   because 53 >= 2*24 + 2 (double rounding is innocuous);
-* groups are 64 consecutive elements along the input dimension of W [out, in];
+* groups are g consecutive elements along the input dimension of W [out, in],
+  g = 64 by default (32, 128, or the whole row for channel-wise);
 * a degenerate group (max == min) gets s = S_MIN = fp32(1e-5);
 * the zero point used in the Block-AP forward is zr = clamp(rint(z), 0, K)
   with identity derivative (straight-through round and clamp);
@@ -48,8 +53,10 @@ Readings where the pages are silent (the kernel follows the same readings):
   [N*i, N*i + N) of the row's bytes, row stride in*N/8 bytes.
 
 Parity status: every function here is pinned by the CPU tests in
-tests/test_oracle_pins.py (closed forms, brute force, finite differences,
-invariants, and library routines for the rounding helpers). The absolute
+tests/test_oracle_pins.py, tests/test_oracle_groups.py and
+tests/test_oracle_deploy.py (closed forms, brute force, finite differences,
+exact rational sums, invariants, and library routines for the rounding
+helpers). The absolute
 values the method produces on real weights are not pinned by any page
 (the pages print no worked example).
 """
@@ -209,11 +216,11 @@ def fakequant_bwd(dY_bits, X_bits, W, s, z, bits, group: int = GROUP) -> dict:
 # ---------------------------------------------------------------------------
 
 def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
-    """LSB-first bitstream per row: code i sits in bits [N*i, N*i+N)."""
+    """LSB-first bitstream per row: code i sits in bits [N*i, N*i+N). A row
+    whose bit count is not a multiple of 8 ends in a zero-padded byte."""
     q = np.asarray(q).astype(np.int64)
     out, inp = q.shape
-    assert (inp * bits) % 8 == 0
-    nbytes = inp * bits // 8
+    nbytes = -(-inp * bits // 8)
     res = np.zeros((out, nbytes), dtype=np.int64)
     for b in range(bits):                       # bit b of code i -> stream bit N*i + b
         pos = np.arange(inp) * bits + b
@@ -270,3 +277,50 @@ def dequant_gemm_bwd_s(dY_bits, X_bits, Wq, s, z, inp, bits, group: int = GROUP)
     ds = _groups(Gw * (q - ze), group).sum(axis=-1)
     dz = -np.asarray(s, np.float64) * _groups(Gw, group).sum(axis=-1)
     return {"dX": dX, "ds": ds, "dz": dz, "Gw": Gw}
+
+
+# ---------------------------------------------------------------------------
+# Deployment format and the inference linear  [Summ-D], [Summ-A-inf]
+#
+# Readings: the deployed model is FP16 (activations, outputs and the step
+# size); a group's step size is fp16(s), rounded to nearest even; its zero
+# point is the N-bit integer clamp(rint(z), 0, K), stored as an LSB-first
+# bitstream per row like the codes (row stride ceil(G*N/8) bytes); the
+# dequantised weight is fp16((q - z) * s16), one rounding of the exact
+# product; the linear sums x * W_hat exactly and rounds once to fp16.
+# ---------------------------------------------------------------------------
+
+def f16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def f64_to_f16_bits(v: np.ndarray) -> np.ndarray:
+    """Round to nearest even fp16 (numpy's double -> half conversion); values
+    beyond the fp16 range become infinities."""
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def deploy_qparams(s, z, bits: int):
+    """(s16 bits [out, G] uint16, zq [out, ceil(G*N/8)] uint8) from the fp32
+    step sizes and zero points."""
+    K = levels(bits)
+    s16 = f64_to_f16_bits(np.asarray(s, dtype=np.float32).astype(np.float64))
+    zint = np.clip(np.rint(np.asarray(z, dtype=np.float32)), 0, K).astype(np.int64)
+    return s16, pack_codes(zint, bits)
+
+
+def deploy_w_hat(Wq, s16_bits, zq, inp: int, bits: int, group: int = GROUP) -> np.ndarray:
+    """W_hat = fp16((q - z) * s16), as fp64 values [out, in]."""
+    G = inp // group
+    q = unpack_codes(Wq, inp, bits)
+    z = unpack_codes(zq, G, bits)
+    prod = (q - _expand(z, group)).astype(np.float64) * _expand(f16_bits_to_f64(s16_bits), group)
+    return f16_bits_to_f64(f64_to_f16_bits(prod))
+
+
+def deploy_gemv(X16_bits, Wq, s16_bits, zq, inp: int, bits: int, group: int = GROUP) -> np.ndarray:
+    """Y = fp16(X W_hat^T) for fp16 activations X [M, in]; returns the exact
+    (unrounded) fp64 product and the rounded fp16 bits."""
+    y = f16_bits_to_f64(X16_bits) @ deploy_w_hat(Wq, s16_bits, zq, inp, bits, group).T
+    return y, f64_to_f16_bits(y)
