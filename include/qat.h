@@ -175,6 +175,37 @@ int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Deployment format (paperlayer.ai summary of EfficientQAT, Appendix D: each
+ * group of g weights shares an FP16 step size and an N-bit zero point).
+ * From fp32 s, z [out, G] (G = in / group):
+ *   s16[o][j] = fp16(s[o][j]), round to nearest even (beyond the fp16 range:
+ *               infinity), [out, G] uint16 bit patterns;
+ *   zq         = clamp(rint(z), 0, K) as N-bit fields of an LSB-first bitstream
+ *               per row, field j in bits [N j, N j + N), row stride
+ *               qat_deploy_zq_stride(in, group, bits) = ceil(G N / 8) bytes,
+ *               padding bits zero.
+ * The codes stay qat_pack's Wq. Outputs are caller-owned device memory; same
+ * checks and status codes as the other calls (out may be any row count).
+ */
+int64_t qat_deploy_zq_stride(int64_t in, int32_t group, int32_t bits);
+int32_t qat_deploy_qparams(const float* s, const float* z, int64_t out, int64_t in, int32_t group,
+                           int32_t bits, uint16_t* s16, uint8_t* zq, hipStream_t stream);
+
+/*
+ * The deployed model's linear layer (summary, Appendix A and section 4: the
+ * INT2 model's linear-layer matrix-vector product, against the FP16 linear):
+ *   Y[m][o] = fp16( sum_k X[m][k] * W_hat[o][k] ),  W_hat[o][k] = fp16((q - z) s16)
+ * with q from Wq [out, in N / 8], s16 and zq as above, X fp16 [M, in], Y fp16
+ * [M, out] (16-bit patterns), fp32 accumulation, one rounding to fp16 at the
+ * end. 1 <= M <= 16 (QAT_ERR_SHAPE otherwise; larger batches are GEMMs); out
+ * may be any row count. No workspace; the call allocates nothing. Needs
+ * |s16| * 2^N below the fp16 range (any trained step size is far below).
+ */
+int32_t qat_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s16, const uint8_t* zq,
+                        int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits, uint16_t* Y,
+                        hipStream_t stream);
+
+/*
  * Kernel timing, for benchmarks. qat_timing_enable(1) clears earlier records
  * and starts bracketing every kernel the library launches with two HIP events
  * on its stream; qat_timing_enable(0) stops. qat_timing_count() waits for the

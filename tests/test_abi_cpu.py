@@ -113,3 +113,28 @@ def test_peak_probe_host_validation():
     assert L.qat_peak_mfma(0, 10, FAKE, None) == 1
     assert L.qat_peak_read(None, 1 << 20, 16, FAKE, None) == 1
     assert L.qat_peak_read(FAKE + 4, 1 << 20, 16, FAKE, None) == 1
+
+
+def test_deploy_validation():
+    L = Q.lib()
+    A, B, C, D, E = (FAKE * k for k in range(1, 6))
+    # M must be 1..16
+    assert L.qat_deploy_gemv(A, B, C, D, 0, 64, 256, 64, 2, E, None) == 2
+    assert L.qat_deploy_gemv(A, B, C, D, 17, 64, 256, 64, 2, E, None) == 2
+    # bits, group, in % 64
+    assert L.qat_deploy_gemv(A, B, C, D, 1, 64, 256, 64, 5, E, None) == 3
+    assert L.qat_deploy_gemv(A, B, C, D, 1, 64, 256, 48, 2, E, None) == 4
+    assert L.qat_deploy_gemv(A, B, C, D, 1, 64, 96, 32, 2, E, None) == 2
+    # null and misaligned pointers, Y overlapping the codes
+    assert L.qat_deploy_gemv(A, None, C, D, 1, 64, 256, 64, 2, E, None) == 1
+    assert L.qat_deploy_gemv(A, B + 4, C, D, 1, 64, 256, 64, 2, E, None) == 5
+    assert L.qat_deploy_gemv(A, B, C, D, 1, 64, 256, 64, 2, B + 16, None) == 8
+    # qparams: s16 overlapping s
+    assert L.qat_deploy_qparams(A, B, 64, 256, 64, 2, A + 16, C, None) == 8
+    assert L.qat_deploy_qparams(A, B, 64, 256, 64, 7, C, D, None) == 3
+    # zq row stride: ceil(G N / 8); 0 for invalid arguments
+    assert Q.deploy_zq_stride(256, 2) == 1
+    assert Q.deploy_zq_stride(192, 3) == 2
+    assert Q.deploy_zq_stride(192, 3, group=192) == 1
+    assert Q.deploy_zq_stride(4096, 4) == 32
+    assert Q.deploy_zq_stride(4096, 4, group=48) == 0

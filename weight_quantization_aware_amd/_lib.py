@@ -33,6 +33,9 @@ _SIGS = {
                              _c_vp, _c_vp, _c_sz, _c_vp],
     "qat_dequant_gemm_bwd_s": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32,
                                _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
+    "qat_deploy_zq_stride": [_c_i64, _c_i32, _c_i32],
+    "qat_deploy_qparams": [_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp],
+    "qat_deploy_gemv": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp],
     "qat_fakequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
     "qat_dequant_ws_bytes": [_c_i64, _c_i64, _c_i64],
     "qat_timing_enable": [_c_i32],
@@ -47,7 +50,7 @@ _SIGS = {
     "qat_status_string": [_c_i32],
     "qat_last_error": [],
 }
-_RES = {"qat_fakequant_ws_bytes": _c_sz, "qat_dequant_ws_bytes": _c_sz, "qat_peak_mfma_flops": _c_i64,
+_RES = {"qat_deploy_zq_stride": _c_i64, "qat_fakequant_ws_bytes": _c_sz, "qat_dequant_ws_bytes": _c_sz, "qat_peak_mfma_flops": _c_i64,
         "qat_peak_scratch_bytes": _c_sz,
         "qat_status_string": ctypes.c_char_p, "qat_last_error": ctypes.c_char_p}
 
@@ -99,7 +102,8 @@ def _call(name: str, *args) -> None:
 
 
 def _u16(t: torch.Tensor) -> torch.Tensor:
-    """bf16 tensors travel as their 16-bit patterns."""
+    """bf16 (or, for the deployment calls, fp16) tensors travel as their 16-bit
+    patterns."""
     if t.dtype == torch.bfloat16:
         return t
     if t.dtype in (torch.int16, torch.uint16):
@@ -172,6 +176,28 @@ def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None,
     _call("qat_dequant_gemm_bwd_s", _p(_u16(dY)), _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp,
           group, bits, _p(None if dX is None else _u16(dX)), _p(ds), _p(dz), _p(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream())
+
+
+def _f16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype in (torch.float16, torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected an fp16 tensor, got {t.dtype}")
+
+
+def deploy_zq_stride(inp: int, bits: int, group: int = GROUP) -> int:
+    return int(lib().qat_deploy_zq_stride(inp, group, bits))
+
+
+def qat_deploy_qparams(s, z, bits, s16, zq, inp: int, group: int = GROUP) -> None:
+    out = s.shape[0]
+    _call("qat_deploy_qparams", _p(s), _p(z), out, inp, group, bits, _p(_f16(s16)), _p(zq), _stream())
+
+
+def qat_deploy_gemv(X, Wq, s16, zq, bits, Y, group: int = GROUP) -> None:
+    M, inp = X.shape
+    out = Wq.shape[0]
+    _call("qat_deploy_gemv", _p(_f16(X)), _p(Wq), _p(_f16(s16)), _p(zq), M, out, inp, group, bits,
+          _p(_f16(Y)), _stream())
 
 
 # ---------------------------------------------------------------------------

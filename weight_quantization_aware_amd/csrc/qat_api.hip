@@ -346,3 +346,44 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
   qat::launch_gemm_grads(a, qat::kE2eScaleGrad, bits, stream);
   return finish();
 }
+
+// ---------------------------------------------------------------------------
+// Deployment format and the inference linear
+// ---------------------------------------------------------------------------
+
+static int64_t zq_stride(int64_t in, int32_t group, int32_t bits) { return ((in / group) * bits + 7) / 8; }
+
+QAT_API int64_t qat_deploy_zq_stride(int64_t in, int32_t group, int32_t bits) {
+  if (check_common(1, in, group, bits) != QAT_OK) return 0;
+  return zq_stride(in, group, bits);
+}
+
+QAT_API int32_t qat_deploy_qparams(const float* s, const float* z, int64_t out, int64_t in, int32_t group,
+                                   int32_t bits, uint16_t* s16, uint8_t* zq, hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  if (!s || !z || !s16 || !zq) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({s, z, s16, zq}));
+  const size_t ng = gbytes(out, in, group);
+  Range outs[] = {{s16, ng / 2}, {zq, (size_t)(out * zq_stride(in, group, bits))}};
+  Range ins[] = {{s, ng}, {z, ng}};
+  QAT_CHECK(check_alias(outs, 2, ins, 2));
+  qat::launch_deploy_qparams(s, z, out, in, group, bits, s16, zq, stream);
+  return finish();
+}
+
+QAT_API int32_t qat_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s16, const uint8_t* zq,
+                                int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits, uint16_t* Y,
+                                hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits));
+  if (M < 1 || M > 16) return QAT_ERR_SHAPE;
+  if (!X || !Wq || !s16 || !zq || !Y) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({X, Wq, s16, zq, Y}));
+  Range outs[] = {{Y, (size_t)(M * out * 2)}};
+  Range ins[] = {{X, (size_t)(M * in * 2)},
+                 {Wq, (size_t)(out * in * bits / 8)},
+                 {s16, gbytes(out, in, group) / 2},
+                 {zq, (size_t)(out * zq_stride(in, group, bits))}};
+  QAT_CHECK(check_alias(outs, 1, ins, 4));
+  qat::launch_deploy_gemv(X, Wq, s16, zq, M, out, in, group, bits, Y, stream);
+  return finish();
+}

@@ -1,0 +1,610 @@
+// Deployment format and the inference linear of a quantised model (gfx950,
+// wave64). paperlayer.ai summary of EfficientQAT, Appendix D: each group of g
+// weights shares an FP16 step size and an N-bit zero point; Appendix A and
+// section 4: the INT2 model's linear-layer matrix-vector product, measured
+// against the FP16 linear.
+//
+// Format: the packed codes of qat_pack ([out][in*N/8], LSB-first per row),
+// s16 = fp16(s) [out][G], and zq, the N-bit zero points clamp(rint(z), 0, K)
+// as an LSB-first bitstream per row, row stride ceil(G*N/8) bytes.
+//
+// The linear: Y[M][out] = fp16(sum_k X[m][k] W_hat[o][k]), fp16 X and Y, with
+// W_hat = fp16((q - z) * s16) and fp32 accumulation, for M = 1..16 tokens.
+#include "qat_device.h"
+#include "qat_dma.h"
+#include "qat_internal.h"
+
+namespace qat {
+
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// s16 and zq from the fp32 step sizes and zero points. Thread i writes s16[i]
+// (i < out*G) and zq byte i (i < out*ldz): the byte gathers the bits of the
+// zero points that overlap it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_deploy_qparams(const float* __restrict__ s, const float* __restrict__ z,
+                                                        int64_t out, int64_t G, int N, float Kq, int64_t ldz,
+                                                        uint16_t* __restrict__ s16, uint8_t* __restrict__ zq) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < out * G) s16[i] = __builtin_bit_cast(uint16_t, (_Float16)s[i]);
+  if (i < out * ldz) {
+    const int64_t o = i / ldz, b = i - o * ldz;
+    const int64_t g0 = 8 * b / N, g1 = min<int64_t>(G - 1, (8 * b + 7) / N);
+    uint32_t v = 0;
+    for (int64_t g = g0; g <= g1; ++g) {
+      const uint32_t c = (uint32_t)fminf(fmaxf(__builtin_rintf(z[o * G + g]), 0.0f), Kq);
+      const int64_t sh = N * g - 8 * b;
+      v |= sh >= 0 ? (c << sh) : (c >> -sh);
+    }
+    zq[i] = (uint8_t)v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The inference linear. MFMA v_mfma_f32_16x16x32_f16: A = W_hat (16 weight
+// rows), B = X^T (16 token columns, zero beyond M). A workgroup owns 16 rows;
+// its 8 waves split `in` into super-steps of 256 (wave w takes super-steps
+// w, w + 8, ...). In a super-step lane l (row / token l & 15, quarter
+// kq = l >> 4) owns the 64 consecutive inputs k0 = 256 ss + 64 kq .. + 63, and
+// MFMA step t (0..7) puts inputs k0 + 8t .. k0 + 8t + 7 in the lane's 8
+// k-slots, for A and B alike. So a lane reads its row's 8N bytes of codes, its
+// token's 128 bytes of X and one (s16, zq) group (two for groups of 32) per
+// super-step; the next super-step's loads are issued before this one's math.
+//
+// Dequantisation of a pair of codes (a, b) into two fp16 lanes: the codes go
+// into the low mantissa bits under the exponent of 1024 (bits 0x6400), so the
+// pair reads (1024 + a, 1024 + b) exactly; a packed add of -(1024 + z) gives
+// a - z, b - z exactly, and a packed multiply by s16 rounds once: fp16((q - z)
+// s16). Accumulation is fp32 in the MFMA; the 8 waves' partial sums meet in
+// LDS and are rounded once to fp16.
+// ---------------------------------------------------------------------------
+// One lane's share of a 64-input chunk of one weight row: the codes and the
+// raw step size / zero-point bits of the chunk's group (two groups of 32).
+template <int N>
+struct RowChunk {
+  uint32_t c[2 * N];     // 64 codes, N * 8 bytes
+  uint32_t sb[2], zb[2]; // raw s16 bits and zq bytes of the chunk's (first, second) group
+};
+
+// A chunk of the X-in-registers kernel: the row part plus the token's X.
+template <int N>
+struct Chunk {
+  RowChunk<N> w;
+  h8 x[8];               // X[tok][k0 + 8t .. + 7], t = 0..7
+  int kl;                // first input of the chunk (clamped into range)
+  bool live;             // false: the chunk lies beyond `in` (ragged last super-step)
+};
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
+// Codes 2a and 2a + 1 of step t (the step's 8 codes are k0 + 8t .. + 7) at
+// bits 0.. and 16.. of a dword; other bits are garbage, removed by the mask.
+template <int N>
+__device__ __forceinline__ uint32_t code_pair(const uint32_t (&c)[2 * N], int t, int a) {
+  if constexpr (N == 2) {
+    const uint32_t h = (c[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+    const u16x2 v = u16x2{(uint16_t)h, (uint16_t)h} >> u16x2{(uint16_t)(4 * a), (uint16_t)(4 * a + 2)};
+    return __builtin_bit_cast(uint32_t, v);
+  } else if constexpr (N == 4) {
+    const uint32_t h = (c[t] >> (16 * (a >> 1))) & 0xFFFFu;
+    const uint16_t s0 = (uint16_t)(8 * (a & 1));
+    const u16x2 v = u16x2{(uint16_t)h, (uint16_t)h} >> u16x2{s0, (uint16_t)(s0 + 4)};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    const int bit = 24 * t, w = bit >> 5, sh = bit & 31;
+    uint32_t x = c[w] >> sh;
+    if (sh > 8) x |= c[w + 1] << (32 - sh);
+    const uint32_t u = (x >> (6 * a)) & 63u;    // the two codes, nothing above them
+    return u | (u << 13);
+  }
+}
+
+// Loop-invariant constants in registers: VOP3 instructions (v_and_or_b32)
+// take no literal operands on gfx950, so the code mask sits in an SGPR and the
+// exponent bits of 1024 in a VGPR. The asm makes the values opaque, so the
+// compiler cannot turn them back into literals of separate v_and / v_or.
+struct DqConst {
+  uint32_t mask, magic;
+};
+
+template <int N>
+__device__ __forceinline__ DqConst dq_const() {
+  DqConst k;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(k.mask) : "i"(((1u << N) - 1) * 0x00010001u));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.magic));
+  return k;
+}
+
+template <int N>
+__device__ __forceinline__ h8 dequant_step(const uint32_t (&c)[2 * N], int t, const DqConst& k,
+                                           const uint32_t (&zc)[2], const uint32_t (&sc)[2]) {
+  uint32_t p[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) p[a] = code_pair<N>(c, t, a);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) p[a] = (p[a] & k.mask) | k.magic;
+  h2 w[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) w[a] = as_h2(p[a]) + as_h2(zc[t >> 2]);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) w[a] = w[a] * as_h2(sc[t >> 2]);
+  return __builtin_bit_cast(h8, w);
+}
+
+struct GemvArgs {
+  const uint16_t* X;
+  const uint8_t* Wq;
+  const uint16_t* s16;
+  const uint8_t* zq;
+  int M, out, K;
+  int64_t G, ldq, ldz;
+  int group;
+  uint16_t* Y;
+};
+
+// Loads of one chunk (issue only: nothing here waits for them). Rows beyond
+// `out` and tokens beyond M read the last row / token instead: they only feed
+// output rows and columns that are never stored. In the ragged last
+// super-step a lane whose k0 lies beyond `in` reads the last chunk and is
+// zeroed when it is used.
+template <int N>
+__device__ __forceinline__ void load_row_chunk(const GemvArgs& a, const FastDiv& gdiv, int row, int kl,
+                                               RowChunk<N>& w) {
+  const uint8_t* src = a.Wq + (int64_t)row * a.ldq + (int64_t)(kl / 64) * (8 * N);
+  if constexpr (N == 2) {
+    const uint4 v = *(const uint4*)src;
+    w.c[0] = v.x, w.c[1] = v.y, w.c[2] = v.z, w.c[3] = v.w;
+  } else if constexpr (N == 4) {
+    const uint4 v0 = *(const uint4*)src, v1 = *(const uint4*)(src + 16);
+    w.c[0] = v0.x, w.c[1] = v0.y, w.c[2] = v0.z, w.c[3] = v0.w;
+    w.c[4] = v1.x, w.c[5] = v1.y, w.c[6] = v1.z, w.c[7] = v1.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint2 v = *(const uint2*)(src + 8 * i);
+      w.c[2 * i] = v.x, w.c[2 * i + 1] = v.y;
+    }
+  }
+  const int64_t g0 = gdiv.div((uint32_t)kl);
+  const int64_t g1 = a.group == 32 ? g0 + 1 : g0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t g = h ? g1 : g0;
+    w.sb[h] = a.s16[(int64_t)row * a.G + g];
+    const int64_t bit = g * N;
+    const uint8_t* zr = a.zq + (int64_t)row * a.ldz + (bit >> 3);
+    // the byte after the field's first byte (the same byte again at the row's
+    // end); its bits are used only when the field straddles the two
+    w.zb[h] = zr[0] | (uint32_t)zr[(bit >> 3) + 1 < a.ldz ? 1 : 0] << 8;
+  }
+}
+
+// Loads of one chunk (issue only: nothing here waits for them). Rows beyond
+// `out` and tokens beyond M read the last row / token instead: they only feed
+// output rows and columns that are never stored. In the ragged last
+// super-step a lane whose k0 lies beyond `in` reads the last chunk and is
+// zeroed when it is used.
+template <int N>
+__device__ __forceinline__ void load_chunk(const GemvArgs& a, const FastDiv& gdiv, int row, int tok, int k0,
+                                           Chunk<N>& ch) {
+  ch.live = k0 < a.K;
+  ch.kl = ch.live ? k0 : a.K - 64;
+  load_row_chunk<N>(a, gdiv, row, ch.kl, ch.w);
+  const h8* xs = (const h8*)(a.X + (int64_t)tok * a.K + ch.kl);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ch.x[t] = xs[t];
+}
+
+// -(1024 + z) and s16 fp16 pairs of the chunk's two group slots; zero step
+// sizes for a dead chunk make its dequantised weights exactly 0.
+template <int N>
+__device__ __forceinline__ void decode_qparams(const RowChunk<N>& w, const GemvArgs& a, const FastDiv& gdiv, int kl,
+                                               bool live, uint32_t (&zc)[2], uint32_t (&sc)[2]) {
+  const int64_t g0 = gdiv.div((uint32_t)kl);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int sh = (int)(((h && a.group == 32 ? g0 + 1 : g0) * N) & 7);
+    const uint32_t zv = (w.zb[h] >> sh) & ((1u << N) - 1);
+    zc[h] = (0xE400u | zv) * 0x00010001u;
+    sc[h] = live ? w.sb[h] * 0x00010001u : 0u;
+  }
+}
+
+// The 8 MFMA steps of a chunk, alternating between two accumulators; the
+// next step's operand is dequantised before this step's MFMA is issued.
+template <int N>
+__device__ __forceinline__ void gemv_steps(Chunk<N>& ch, const GemvArgs& a, const FastDiv& gdiv, bool tail,
+                                           const DqConst& k, f32x4 (&acc)[2]) {
+  uint32_t zc[2], sc[2];
+  decode_qparams<N>(ch.w, a, gdiv, ch.kl, ch.live, zc, sc);
+  if (tail) {                                    // wave-uniform: only the ragged last super-step
+    if (!ch.live) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ch.x[t] = h8{};
+    }
+  }
+  h8 A = dequant_step<N>(ch.w.c, 0, k, zc, sc);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const h8 An = dequant_step<N>(ch.w.c, t < 7 ? t + 1 : t, k, zc, sc);
+    acc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ch.x[t], acc[t & 1], 0, 0, 0);
+    A = An;
+  }
+}
+
+template <int N>
+__global__ __launch_bounds__(512, 2) void k_deploy_gemv(const GemvArgs a) {
+  __shared__ float red[8][4 * 64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int kq = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int row = min(row0 + (lane & 15), a.out - 1), tok = min(lane & 15, a.M - 1);
+  const FastDiv gdiv = FastDiv::make((uint32_t)a.group);
+  const int nfull = a.K / 256, nss = (a.K + 255) / 256;
+  auto load = [&](int ss, Chunk<N>& ch) {
+    load_chunk<N>(a, gdiv, row, tok, ss * 256 + 64 * kq, ch);
+    asm volatile("" ::: "memory");                       // keep the prefetch ahead of the math
+  };
+
+  const DqConst k = dq_const<N>();
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  int ss = wave;
+  if (ss < nss) {                            // wave-uniform
+    // Two buffers, no register copies. The prefetch is unconditional (past
+    // the end it re-reads the last super-step), so no branch separates a
+    // load from its use and the compiler waits for exactly the loads needed.
+    Chunk<N> c0, c1;
+    load(ss, c0);
+    for (;;) {
+      load(min(ss + 8, nss - 1), c1);
+      gemv_steps<N>(c0, a, gdiv, ss >= nfull, k, acc);
+      ss += 8;
+      if (ss >= nss) break;
+      load(min(ss + 8, nss - 1), c0);
+      gemv_steps<N>(c1, a, gdiv, ss >= nfull, k, acc);
+      ss += 8;
+      if (ss >= nss) break;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][i * 64 + lane] = acc[0][i] + acc[1][i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sum += red[w][i * 64 + l];
+    const int t = l & 15, o = row0 + 4 * (l >> 4) + i;
+    if (t < a.M && o < a.out) a.Y[(int64_t)t * a.out + o] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The inference linear with X staged in LDS (used whenever X [M][in] fp16 fits
+// in LDS): a persistent workgroup of 16 waves per CU. Workgroup b takes the
+// row blocks b, b + grid, ... of 16 RW weight rows (RW row tiles); in each,
+// its waves split `in` into chunks of 256 inputs (wave w takes chunks w,
+// w + 16, ...) and run all RW tiles on them, so one X fragment read from LDS
+// feeds RW MFMAs. The in-chunk mapping is that of the kernel above.
+//
+// X reaches LDS once per workgroup, by direct-to-LDS loads issued after the
+// wave's first code loads so that both are in flight together. Each token's
+// row sits at a stride of lds_x_stride(in) halves, whole KiB with at least 192
+// inputs of zeros after the row: a lane whose chunk lies beyond `in` (the
+// ragged last chunk) reads those zeros as X and the last valid chunk as codes,
+// so it adds exactly 0 without any masking.
+//
+// A wave's chunks over all its row blocks form one sequence of jobs, and the
+// codes of the next NB - 1 jobs are in flight while it computes the current
+// one (NB register buffers; loads past the last job re-read it, so no branch
+// separates a load from its use), also across row-block ends. A job's step
+// sizes and zero points come by one direct-to-LDS load per wave (qp_dma)
+// rather than as per-lane 1- and 2-byte loads, whose instruction count, not
+// their bytes, limited the first version of this kernel. At the end of a
+// row block the partial sums go to LDS (one fp32 per wave, row and token < M,
+// double-buffered by row block) and the waves meet at a bare s_barrier after
+// waiting for their LDS writes only: a full __syncthreads would also wait for
+// the code loads in flight. Then RW * 16 * M threads add the 16 partials and
+// round once to fp16, into an LDS copy of the workgroup's outputs that goes
+// to HBM after the last row block.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int lds_x_stride(int K) { return ((K * 2 + 384 + 1023) / 1024) * 512; }
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The codes of one chunk of RW row tiles (the step sizes and zero points come
+// through LDS, see qp_dma).
+template <int N, int RW>
+struct CodeChunks {
+  uint32_t c[RW][2 * N];
+};
+
+template <int N>
+__device__ __forceinline__ void load_codes(const GemvArgs& a, int row, int kl, uint32_t (&c)[2 * N]) {
+  const uint8_t* src = a.Wq + (int64_t)row * a.ldq + (int64_t)(kl / 64) * (8 * N);
+  if constexpr (N == 2) {
+    const uint4 v = *(const uint4*)src;
+    c[0] = v.x, c[1] = v.y, c[2] = v.z, c[3] = v.w;
+  } else if constexpr (N == 4) {
+    const uint4 v0 = *(const uint4*)src, v1 = *(const uint4*)(src + 16);
+    c[0] = v0.x, c[1] = v0.y, c[2] = v0.z, c[3] = v0.w;
+    c[4] = v1.x, c[5] = v1.y, c[6] = v1.z, c[7] = v1.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint2 v = *(const uint2*)(src + 8 * i);
+      c[2 * i] = v.x, c[2 * i + 1] = v.y;
+    }
+  }
+}
+
+template <int N, int RW, int NB>
+__global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t dsm[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int kq = lane >> 4, r16 = lane & 15;
+  const int tok = min(r16, a.M - 1);
+  const FastDiv gdiv = FastDiv::make((uint32_t)a.group);
+  const int nch = (a.K + 255) / 256;
+  const int nbusy = min(nch, 16);                        // waves with chunks
+  const int xs = lds_x_stride(a.K);                      // halves per token row in LDS
+  const _Float16* xl = (const _Float16*)dsm;
+  float* red = (float*)(dsm + (int64_t)a.M * xs * 2);    // [2][16][RW * 16][M]
+  const int nrb = (a.out + 16 * RW - 1) / (16 * RW);
+  const int my_rb = (nrb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // grid <= nrb
+  // this workgroup's outputs [my_rb][M][RW * 16], written to HBM after the loop:
+  // a global store inside it would make later waits for the code loads wait
+  // for the store as well (one counter covers both)
+  uint16_t* ybuf = (uint16_t*)(red + 2 * 16 * RW * 16 * a.M);
+  // per wave and code buffer, 1 KiB of step sizes and zero points (qp_dma)
+  uint8_t* qp = (uint8_t*)ybuf + ((my_rb * a.M * RW * 16 * 2 + 1023) & ~1023);
+  const int cpw = wave < nch ? (nch - 1 - wave) / 16 + 1 : 0;         // chunks per row block
+  const int njobs = cpw * my_rb;
+  const i32x4 s_rsrc = buffer_rsrc(a.s16, (int64_t)a.out * a.G * 2);
+  const i32x4 z_rsrc = buffer_rsrc(a.zq, (int64_t)a.out * a.ldz);
+
+  // Step sizes and zero points of a chunk, for all RW * 16 rows, by one
+  // direct-to-LDS load: lane L < RW * 16 fetches 16 bytes of s16 holding row
+  // L's step sizes for the chunk's groups, lane RW * 16 + L 16 bytes of zq
+  // holding the row's zero-point bits for them. Each piece starts at the
+  // 4-byte aligned address at or below the first needed byte, moved back if
+  // needed so that it ends inside its buffer (both buffers hold at least 16
+  // bytes); piece_start() gives the start on both sides. Issued before the
+  // chunk's code loads, so it is complete once they are (loads complete in
+  // order).
+  const uint32_t s_size = (uint32_t)(a.out * a.G * 2), z_size = (uint32_t)(a.out * a.ldz);
+  auto piece_start = [&](uint32_t first, uint32_t size) { return min(first & ~3u, size - 16u); };
+  auto qp_dma = [&](int rb, int c, int jb) {
+    const int g_first = (int)gdiv.div((uint32_t)(c * 256));
+    const int L = lane & (RW * 16 - 1);
+    const int row = min(rb * 16 * RW + L, a.out - 1);
+    uint32_t src;
+    if (lane < RW * 16) src = piece_start((uint32_t)(row * a.G + g_first) * 2u, s_size);
+    else src = piece_start((uint32_t)(row * a.ldz) + ((uint32_t)g_first * N >> 3), z_size);
+    const uint32_t dst = lds_addr_of(qp) + (uint32_t)(wave * NB + jb) * 1024u;
+    // lanes past 2 * RW * 16 (RW = 1) repeat the zero-point fetch
+    if (lane < RW * 16) dma16(s_rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)dst), src);
+    else dma16(z_rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)dst), src);
+  };
+
+  // loads walk the job sequence with their own (row block, chunk) counters
+  int l_rb = 0, l_cc = 0, l_j = 0;
+  auto load = [&](CodeChunks<N, RW>& b, int jb) {
+    const int rb = (int)blockIdx.x + l_rb * (int)gridDim.x;
+    const int c = wave + 16 * l_cc;
+    qp_dma(rb, c, jb);
+    const int k0 = c * 256 + 64 * kq;
+    const int kl = k0 < a.K ? k0 : a.K - 64;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) load_codes<N>(a, min(rb * 16 * RW + 16 * i + r16, a.out - 1), kl, b.c[i]);
+    asm volatile("" ::: "memory");                       // keep the prefetch ahead of the math
+    if (l_j + 1 < njobs) {
+      ++l_j;
+      if (++l_cc == cpw) {
+        l_cc = 0;
+        ++l_rb;
+      }
+    }
+  };
+  CodeChunks<N, RW> b[NB];
+  if (cpw > 0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load(b[j], j);
+  }
+  {
+    // token m's row: xs * 2 / 1024 instructions of 1 KiB; source bytes past the
+    // row's end are moved out of the buffer's range, so they land as zeros
+    const i32x4 rsrc = buffer_rsrc(a.X, (int64_t)a.M * a.K * 2);
+    const uint32_t base = lds_addr_of(dsm);
+    const int per_row = xs * 2 / 1024;
+    for (int i = wave; i < a.M * per_row; i += 16) {
+      const int m = i / per_row, j = i - m * per_row;
+      const int col = j * 1024 + 16 * lane;              // byte within the row
+      const uint32_t src = col < a.K * 2 ? (uint32_t)(m * a.K * 2 + col) : 0x7FFFFFF0u;
+      dma16(rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + 1024u * i)), src);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const DqConst k = dq_const<N>();
+  f32x4 acc[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const CodeChunks<N, RW>& bc, int cc, int jb, int rbi) {
+    const int c = wave + 16 * cc;
+    const int k0 = c * 256 + 64 * kq;
+    const int kl = k0 < a.K ? k0 : a.K - 64;
+    // the codes have arrived, hence this chunk's step sizes and zero points too
+    asm volatile("" ::"v"(bc.c[0][0]), "v"(bc.c[RW - 1][2 * N - 1]) : "memory");
+    const int g_first = (int)gdiv.div((uint32_t)(c * 256));
+    const int g0 = (int)gdiv.div((uint32_t)kl);
+    const uint8_t* slot = qp + (wave * NB + jb) * 1024;
+    uint32_t zc[RW][2], sc[RW][2];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int row = min(((int)blockIdx.x + rbi * (int)gridDim.x) * 16 * RW + 16 * i + r16, a.out - 1);
+      const uint32_t s0 = piece_start((uint32_t)(row * a.G + g_first) * 2u, s_size);
+      const uint32_t z0 = piece_start((uint32_t)(row * a.ldz) + ((uint32_t)g_first * N >> 3), z_size);
+      const uint8_t* sp = slot + (16 * i + r16) * 16;
+      const uint32_t* zp = (const uint32_t*)(slot + (RW * 16 + 16 * i + r16) * 16);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = h && a.group == 32 ? g0 + 1 : g0;
+        const uint32_t sbits = *(const uint16_t*)(sp + ((uint32_t)(row * a.G + g) * 2u - s0));
+        const int bit = (int)(((uint32_t)(row * a.ldz) - z0) * 8u + (uint32_t)(g * N));
+        const int w = bit >> 5;
+        const uint64_t zw = (uint64_t)zp[w] | ((uint64_t)zp[min(w + 1, 3)] << 32);
+        const uint32_t zv = (uint32_t)(zw >> (bit & 31)) & ((1u << N) - 1);
+        zc[i][h] = (0xE400u | zv) * 0x00010001u;
+        sc[i][h] = sbits * 0x00010001u;
+      }
+    }
+    const _Float16* xr = xl + tok * xs + k0;             // zeros past `in`
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const h8 B = *(const h8*)(xr + 8 * t);
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_step<N>(bc.c[i], t, k, zc[i], sc[i]), B, acc[i], 0,
+                                                        0, 0);
+    }
+  };
+  // end of row block rbi: partials to LDS, barrier, reduce into ybuf
+  auto flush = [&](int rbi) {
+    float* rd = red + (rbi & 1) * (16 * RW * 16 * a.M);
+    if (cpw > 0 && r16 < a.M) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rd[((wave * RW + i) * 16 + 4 * kq + r) * a.M + r16] = acc[i][r];
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    lds_barrier();
+    for (int e = threadIdx.x; e < RW * 16 * a.M; e += 1024) {
+      const int m = e % a.M, rr = e / a.M;               // rr: row within the row block
+      float sum = 0.f;
+      for (int w = 0; w < nbusy; ++w) sum += rd[(w * RW * 16 + rr) * a.M + m];
+      ybuf[(rbi * a.M + m) * (RW * 16) + rr] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+    }
+  };
+  if (cpw > 0) {
+    int cc = 0, rbi = 0;
+    for (int j0 = 0; j0 < njobs; j0 += NB) {
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        if (j0 + jb < njobs) {                           // wave-uniform
+          compute(b[jb], cc, jb, rbi);
+          load(b[jb], jb);
+          if (++cc == cpw) {
+            flush(rbi);
+            cc = 0;
+            ++rbi;
+          }
+        }
+      }
+    }
+  } else {
+    for (int rbi = 0; rbi < my_rb; ++rbi) flush(rbi);
+  }
+  lds_barrier();
+  for (int e = threadIdx.x; e < my_rb * a.M * RW * 16; e += 1024) {
+    const int rr = e % (RW * 16), m = (e / (RW * 16)) % a.M, rbi = e / (RW * 16 * a.M);
+    const int o = ((int)blockIdx.x + rbi * (int)gridDim.x) * 16 * RW + rr;
+    if (o < a.out) a.Y[(int64_t)m * a.out + o] = ybuf[e];
+  }
+}
+
+}  // namespace
+
+void launch_deploy_qparams(const float* s, const float* z, int64_t out, int64_t in, int group, int bits,
+                           uint16_t* s16, uint8_t* zq, hipStream_t st) {
+  const int64_t G = in / group, ldz = (G * bits + 7) / 8;
+  const int64_t n = out * (G > ldz ? G : ldz);
+  LaunchTimer t("deploy_qparams", st);
+  hipLaunchKernelGGL(k_deploy_qparams, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, z, out, G, bits,
+                     (float)((1 << bits) - 1), ldz, s16, zq);
+}
+
+namespace {
+
+constexpr int64_t kLdsLimit = 160 * 1024;                // LDS per workgroup on gfx950
+
+// Compute units of the current device (one persistent workgroup each).
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int N, int RW, int NB>
+void launch_lds(const GemvArgs& a, dim3 grid, int lds, hipStream_t st) {
+  static bool raised = false;                            // allow more than 64 KiB of dynamic LDS, once
+  if (!raised) {
+    (void)hipFuncSetAttribute((const void*)k_deploy_gemv_lds<N, RW, NB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsLimit);
+    raised = true;
+  }
+  hipLaunchKernelGGL((k_deploy_gemv_lds<N, RW, NB>), grid, dim3(1024), (size_t)lds, st, a);
+}
+
+}  // namespace
+
+void launch_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s16, const uint8_t* zq, int64_t M,
+                        int64_t out, int64_t in, int group, int bits, uint16_t* Y, hipStream_t st) {
+  GemvArgs a;
+  a.X = X;
+  a.Wq = Wq;
+  a.s16 = s16;
+  a.zq = zq;
+  a.M = (int)M;
+  a.out = (int)out;
+  a.K = (int)in;
+  a.G = in / group;
+  a.ldq = in * bits / 8;
+  a.ldz = (a.G * bits + 7) / 8;
+  a.group = group;
+  a.Y = Y;
+  LaunchTimer t("deploy_gemv", st);
+  // X in LDS when it fits beside the partial sums (2 x 16 waves x 32 rows x M
+  // fp32), the workgroup's fp16 outputs and the step-size / zero-point slots
+  // (16 waves x NB KiB): one persistent workgroup per CU. Three code buffers for 2-bit
+  // codes, two for 3 and 4 bits (register budget).
+  constexpr int kRW = 2;
+  const int64_t nrb = (out + 16 * kRW - 1) / (16 * kRW);
+  const int64_t grid_n = nrb < num_cus() ? nrb : num_cus();
+  const int64_t my_rb = (nrb + grid_n - 1) / grid_n;
+  const int nb = bits == 2 ? 3 : 2;
+  const int64_t lds = M * lds_x_stride((int)in) * 2 + 2 * 16 * kRW * 16 * M * 4 +
+                      (my_rb * M * kRW * 16 * 2 + 1023) / 1024 * 1024 + 16 * nb * 1024;
+  const bool qp_fits = out * (in / group) * 2 >= 16 && out * a.ldz >= 16;   // one 16-byte piece per buffer
+  if (lds <= kLdsLimit && qp_fits) {
+    const dim3 grid((unsigned)grid_n);
+    if (bits == 2) launch_lds<2, kRW, 3>(a, grid, (int)lds, st);
+    else if (bits == 3) launch_lds<3, kRW, 2>(a, grid, (int)lds, st);
+    else launch_lds<4, kRW, 2>(a, grid, (int)lds, st);
+    return;
+  }
+  const dim3 grid((unsigned)((out + 15) / 16));
+  if (bits == 2) hipLaunchKernelGGL(k_deploy_gemv<2>, grid, dim3(512), 0, st, a);
+  else if (bits == 3) hipLaunchKernelGGL(k_deploy_gemv<3>, grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL(k_deploy_gemv<4>, grid, dim3(512), 0, st, a);
+}
+
+}  // namespace qat

@@ -38,6 +38,15 @@ void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t
 // p[0 .. n) = 0 with a plain store kernel (usable under stream capture).
 void launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
+// ---- Deployment format and the inference linear (qat_deploy.hip) ----
+// s16 = fp16(s) [out][G]; zq = N-bit clamp(rint(z), 0, K), LSB-first per row,
+// row stride ceil(G*N/8) bytes.
+void launch_deploy_qparams(const float* s, const float* z, int64_t out, int64_t in, int group, int bits,
+                           uint16_t* s16, uint8_t* zq, hipStream_t st);
+// Y[M][out] fp16 = X[M][in] fp16 times fp16((q - z) s16)^T, M <= 16.
+void launch_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s16, const uint8_t* zq, int64_t M,
+                        int64_t out, int64_t in, int group, int bits, uint16_t* Y, hipStream_t st);
+
 // ---- MFMA GEMMs (qat_gemm.hip) ----
 // C[M, N] = sum_k A[m, k] * B[n, k] in bf16 with fp32 accumulation. Each operand
 // is either K-contiguous ([rows][ld], ld >= K) or MN-contiguous ([K][ld] with

@@ -51,6 +51,14 @@ def to_bf16_bits(x32: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def to_f16_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16 (round to nearest even) as uint16 bits, via torch's CPU cast."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
 
@@ -74,6 +82,16 @@ def activations(cfg: int, layer: int, m: int, inp: int, outlier_channels: int = 
         cols = rng(cfg, layer, TID_OUTL + 100).choice(inp, size=outlier_channels, replace=False)
         x[:, cols] *= np.float32(20.0)
     return to_bf16_bits(x)
+
+
+def activations_f16(cfg: int, layer: int, m: int, inp: int, outlier_channels: int = 0) -> np.ndarray:
+    """fp16 bits [m, in] ~ N(0, 1), optional outlier columns x20 before rounding
+    (the inputs of a deployed FP16 model's linear layers)."""
+    x = rng(cfg, layer, TID_X).standard_normal((m, inp), dtype=np.float32)
+    if outlier_channels:
+        cols = rng(cfg, layer, TID_OUTL + 100).choice(inp, size=outlier_channels, replace=False)
+        x[:, cols] *= np.float32(20.0)
+    return to_f16_bits(x)
 
 
 def grad_out(cfg: int, layer: int, m: int, out: int, std: float = 1e-3) -> np.ndarray:
@@ -183,3 +201,14 @@ def config(cfg: int, bits: Optional[int] = None) -> List[Linear]:
         return [Linear(n, o, i, 4096, b, sigma=0.015, cfg=5, layer=li + 10 * b)
                 for li, (n, o, i) in enumerate(shapes)]
     raise ValueError(f"unknown workload {cfg}")
+
+
+# Linear layers of the deployed Llama-2 models (name, out, in) for the
+# inference linear: token-by-token decoding runs one matrix-vector product (or
+# a few, M <= 16) per layer.
+DEPLOY_SHAPES = {
+    "7b": [("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096), ("o_proj", 4096, 4096),
+           ("gate_proj", 11008, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 11008)],
+    "70b": [("q_proj", 8192, 8192), ("k_proj", 1024, 8192), ("v_proj", 1024, 8192), ("o_proj", 8192, 8192),
+            ("gate_proj", 28672, 8192), ("up_proj", 28672, 8192), ("down_proj", 8192, 28672)],
+}
