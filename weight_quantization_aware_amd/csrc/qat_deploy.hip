@@ -303,17 +303,33 @@ __global__ __launch_bounds__(512, 2) void k_deploy_gemv(const GemvArgs a) {
 // codes of the next NB - 1 jobs are in flight while it computes the current
 // one (NB register buffers; loads past the last job re-read it, so no branch
 // separates a load from its use), also across row-block ends. A job's step
-// sizes and zero points come by one direct-to-LDS load per wave (qp_dma)
-// rather than as per-lane 1- and 2-byte loads, whose instruction count, not
-// their bytes, limited the first version of this kernel. At the end of a
-// row block the partial sums go to LDS (one fp32 per wave, row and token < M,
-// double-buffered by row block) and the waves meet at a bare s_barrier after
-// waiting for their LDS writes only: a full __syncthreads would also wait for
-// the code loads in flight. Then RW * 16 * M threads add the 16 partials and
-// round once to fp16, into an LDS copy of the workgroup's outputs that goes
-// to HBM after the last row block.
+// sizes and zero points come by one 16-byte load per lane (qp_load) rather
+// than as per-lane 1- and 2-byte loads, whose instruction count, not their
+// bytes, limited the first version of this kernel. At the end of a
+// row block a wave writes its partial sums to LDS (one fp32 per row and token
+// < M, a slot per row block) and adds one to the row block's LDS counter; the
+// wave that brings the counter to the number of busy waves adds the partials
+// and rounds them once to fp16, into an LDS copy of the workgroup's outputs
+// that goes to HBM after the last row block. No wave waits for another
+// before the end (a global store inside the loop would also make later waits
+// for code loads wait for it: one counter covers both).
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int lds_x_stride(int K) { return ((K * 2 + 384 + 1023) / 1024) * 512; }
+
+// LDS layout of the kernel below (byte offsets; the same on host and device).
+struct DeployLds {
+  int part, cnt, ybuf, qp, total;
+  __host__ __device__ static DeployLds of(int M, int K, int my_rb, int RW, int NB = 3) {
+    DeployLds l;
+    auto up = [](int v) { return (v + 1023) / 1024 * 1024; };
+    l.part = M * lds_x_stride(K) * 2;
+    l.cnt = l.part + up(my_rb * 16 * RW * 16 * M * 4);
+    l.ybuf = l.cnt + up(my_rb * 4);
+    l.qp = l.ybuf + up(my_rb * M * RW * 16 * 2);
+    l.total = l.qp + 16 * NB * 2 * RW * 16 * 16;
+    return l;
+  }
+};
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -321,11 +337,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The codes of one chunk of RW row tiles (the step sizes and zero points come
-// through LDS, see qp_dma).
+// The codes of one chunk of RW row tiles and this lane's piece of its step
+// sizes or zero points (see qp_load).
 template <int N, int RW>
 struct CodeChunks {
-  uint32_t c[RW][2 * N];
+  uint4 q;               // this lane's 16-byte piece of step sizes or zero points (qp_load)
+  uint32_t c[RW][2 * N]; // (q first: no padding, which keeps the 3-bit case out of scratch memory)
 };
 
 template <int N>
@@ -358,50 +375,47 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
   const int nbusy = min(nch, 16);                        // waves with chunks
   const int xs = lds_x_stride(a.K);                      // halves per token row in LDS
   const _Float16* xl = (const _Float16*)dsm;
-  float* red = (float*)(dsm + (int64_t)a.M * xs * 2);    // [2][16][RW * 16][M]
   const int nrb = (a.out + 16 * RW - 1) / (16 * RW);
   const int my_rb = (nrb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // grid <= nrb
-  // this workgroup's outputs [my_rb][M][RW * 16], written to HBM after the loop:
-  // a global store inside it would make later waits for the code loads wait
-  // for the store as well (one counter covers both)
-  uint16_t* ybuf = (uint16_t*)(red + 2 * 16 * RW * 16 * a.M);
-  // per wave and code buffer, 1 KiB of step sizes and zero points (qp_dma)
-  uint8_t* qp = (uint8_t*)ybuf + ((my_rb * a.M * RW * 16 * 2 + 1023) & ~1023);
+  // LDS after X: partial sums [my_rb][16][RW * 16][M] fp32, arrival counters
+  // [my_rb], the workgroup's outputs [my_rb][M][RW * 16] fp16, and per wave
+  // and code buffer 2 RW * 16 16-byte pieces of step sizes and zero points
+  // (qp_load)
+  const DeployLds L = DeployLds::of(a.M, a.K, my_rb, RW, NB);
+  float* part = (float*)(dsm + L.part);
+  uint32_t* cnt = (uint32_t*)(dsm + L.cnt);
+  uint16_t* ybuf = (uint16_t*)(dsm + L.ybuf);
+  uint8_t* qp = dsm + L.qp;
   const int cpw = wave < nch ? (nch - 1 - wave) / 16 + 1 : 0;         // chunks per row block
   const int njobs = cpw * my_rb;
-  const i32x4 s_rsrc = buffer_rsrc(a.s16, (int64_t)a.out * a.G * 2);
-  const i32x4 z_rsrc = buffer_rsrc(a.zq, (int64_t)a.out * a.ldz);
 
   // Step sizes and zero points of a chunk, for all RW * 16 rows, by one
-  // direct-to-LDS load: lane L < RW * 16 fetches 16 bytes of s16 holding row
-  // L's step sizes for the chunk's groups, lane RW * 16 + L 16 bytes of zq
+  // 16-byte load per lane: lane L < RW * 16 fetches 16 bytes of s16 holding
+  // row L's step sizes for the chunk's groups, lane RW * 16 + L 16 bytes of zq
   // holding the row's zero-point bits for them. Each piece starts at the
   // 4-byte aligned address at or below the first needed byte, moved back if
   // needed so that it ends inside its buffer (both buffers hold at least 16
-  // bytes); piece_start() gives the start on both sides. Issued before the
-  // chunk's code loads, so it is complete once they are (loads complete in
-  // order).
+  // bytes); piece_start() gives the start on both sides. At use time the wave
+  // passes the pieces through its LDS slot, so that each lane can read the
+  // values of its own rows and groups.
   const uint32_t s_size = (uint32_t)(a.out * a.G * 2), z_size = (uint32_t)(a.out * a.ldz);
-  auto piece_start = [&](uint32_t first, uint32_t size) { return min(first & ~3u, size - 16u); };
-  auto qp_dma = [&](int rb, int c, int jb) {
+  auto piece_start = [&](uint32_t first, uint32_t size) __attribute__((always_inline)) { return min(first & ~3u, size - 16u); };
+  auto qp_load = [&](int rb, int c, uint4& q) __attribute__((always_inline)) {
     const int g_first = (int)gdiv.div((uint32_t)(c * 256));
     const int L = lane & (RW * 16 - 1);
     const int row = min(rb * 16 * RW + L, a.out - 1);
-    uint32_t src;
-    if (lane < RW * 16) src = piece_start((uint32_t)(row * a.G + g_first) * 2u, s_size);
-    else src = piece_start((uint32_t)(row * a.ldz) + ((uint32_t)g_first * N >> 3), z_size);
-    const uint32_t dst = lds_addr_of(qp) + (uint32_t)(wave * NB + jb) * 1024u;
-    // lanes past 2 * RW * 16 (RW = 1) repeat the zero-point fetch
-    if (lane < RW * 16) dma16(s_rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)dst), src);
-    else dma16(z_rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)dst), src);
+    const bool sp = lane < RW * 16;
+    const uint32_t src = sp ? piece_start((uint32_t)(row * a.G + g_first) * 2u, s_size)
+                            : piece_start((uint32_t)(row * a.ldz) + ((uint32_t)g_first * N >> 3), z_size);
+    q = *(const uint4*)((sp ? (const uint8_t*)a.s16 : a.zq) + src);
   };
 
   // loads walk the job sequence with their own (row block, chunk) counters
   int l_rb = 0, l_cc = 0, l_j = 0;
-  auto load = [&](CodeChunks<N, RW>& b, int jb) {
+  auto load = [&](CodeChunks<N, RW>& b, int jb) __attribute__((always_inline)) {
     const int rb = (int)blockIdx.x + l_rb * (int)gridDim.x;
     const int c = wave + 16 * l_cc;
-    qp_dma(rb, c, jb);
+    qp_load(rb, c, b.q);
     const int k0 = c * 256 + 64 * kq;
     const int kl = k0 < a.K ? k0 : a.K - 64;
 #pragma unroll
@@ -415,10 +429,13 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
       }
     }
   };
-  CodeChunks<N, RW> b[NB];
+  // named buffers (an array of them ends up in scratch memory when the
+  // compiler keeps a loop over it)
+  CodeChunks<N, RW> b0, b1, b2;
   if (cpw > 0) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) load(b[j], j);
+    load(b0, 0);
+    load(b1, 1);
+    if constexpr (NB == 3) load(b2, 2);
   }
   {
     // token m's row: xs * 2 / 1024 instructions of 1 KiB; source bytes past the
@@ -433,6 +450,7 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
       dma16(rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + 1024u * i)), src);
     }
   }
+  for (int i = threadIdx.x; i < my_rb; i += 1024) cnt[i] = 0;
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -440,15 +458,14 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
   f32x4 acc[RW];
 #pragma unroll
   for (int i = 0; i < RW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const CodeChunks<N, RW>& bc, int cc, int jb, int rbi) {
+  auto compute = [&](const CodeChunks<N, RW>& bc, int cc, int jb, int rbi) __attribute__((always_inline)) {
     const int c = wave + 16 * cc;
     const int k0 = c * 256 + 64 * kq;
     const int kl = k0 < a.K ? k0 : a.K - 64;
-    // the codes have arrived, hence this chunk's step sizes and zero points too
-    asm volatile("" ::"v"(bc.c[0][0]), "v"(bc.c[RW - 1][2 * N - 1]) : "memory");
     const int g_first = (int)gdiv.div((uint32_t)(c * 256));
     const int g0 = (int)gdiv.div((uint32_t)kl);
-    const uint8_t* slot = qp + (wave * NB + jb) * 1024;
+    uint8_t* slot = qp + (wave * NB + jb) * (2 * RW * 16 * 16);
+    if (lane < 2 * RW * 16) *(uint4*)(slot + 16 * lane) = bc.q;   // read back below by this wave only
     uint32_t zc[RW][2], sc[RW][2];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -457,16 +474,21 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
       const uint32_t z0 = piece_start((uint32_t)(row * a.ldz) + ((uint32_t)g_first * N >> 3), z_size);
       const uint8_t* sp = slot + (16 * i + r16) * 16;
       const uint32_t* zp = (const uint32_t*)(slot + (RW * 16 + 16 * i + r16) * 16);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int g = h && a.group == 32 ? g0 + 1 : g0;
+      auto decode = [&](int g, uint32_t& zcv, uint32_t& scv) __attribute__((always_inline)) {
         const uint32_t sbits = *(const uint16_t*)(sp + ((uint32_t)(row * a.G + g) * 2u - s0));
         const int bit = (int)(((uint32_t)(row * a.ldz) - z0) * 8u + (uint32_t)(g * N));
         const int w = bit >> 5;
         const uint64_t zw = (uint64_t)zp[w] | ((uint64_t)zp[min(w + 1, 3)] << 32);
         const uint32_t zv = (uint32_t)(zw >> (bit & 31)) & ((1u << N) - 1);
-        zc[i][h] = (0xE400u | zv) * 0x00010001u;
-        sc[i][h] = sbits * 0x00010001u;
+        zcv = (0xE400u | zv) * 0x00010001u;
+        scv = sbits * 0x00010001u;
+      };
+      decode(g0, zc[i][0], sc[i][0]);
+      if (a.group == 32) {                               // wave-uniform: the chunk's second group
+        decode(g0 + 1, zc[i][1], sc[i][1]);
+      } else {
+        zc[i][1] = zc[i][0];
+        sc[i][1] = sc[i][0];
       }
     }
     const _Float16* xr = xl + tok * xs + k0;             // zeros past `in`
@@ -479,43 +501,57 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
                                                         0, 0);
     }
   };
-  // end of row block rbi: partials to LDS, barrier, reduce into ybuf
-  auto flush = [&](int rbi) {
-    float* rd = red + (rbi & 1) * (16 * RW * 16 * a.M);
-    if (cpw > 0 && r16 < a.M) {
+  // end of row block rbi: this wave's partial sums to LDS; the last of the
+  // busy waves to arrive reduces them into ybuf
+  auto flush = [&](int rbi) __attribute__((always_inline)) {
+    float* pp = part + rbi * (16 * RW * 16 * a.M);
+    if (r16 < a.M) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) rd[((wave * RW + i) * 16 + 4 * kq + r) * a.M + r16] = acc[i][r];
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r) pp[((wave * RW + i) * 16 + 4 * kq + r) * a.M + r16] = acc[i][r];
       }
     }
-    lds_barrier();
-    for (int e = threadIdx.x; e < RW * 16 * a.M; e += 1024) {
-      const int m = e % a.M, rr = e / a.M;               // rr: row within the row block
-      float sum = 0.f;
-      for (int w = 0; w < nbusy; ++w) sum += rd[(w * RW * 16 + rr) * a.M + m];
-      ybuf[(rbi * a.M + m) * (RW * 16) + rr] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // LDS operations of a wave are performed in order: the partials are in
+    // place before the increment, and every wave counted before ours has
+    // written its own
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // partials written before the count
+    uint32_t prev = 0;
+    if (lane == 0) prev = atomicAdd(cnt + rbi, 1u);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    asm volatile("" ::: "memory");                        // no partial is read before the count
+    if (prev == (uint32_t)nbusy - 1) {
+      for (int e = lane; e < RW * 16 * a.M; e += 64) {
+        const int m = e % a.M, rr = e / a.M;             // rr: row within the row block
+        float sum = 0.f;
+        for (int w = 0; w < nbusy; ++w) sum += pp[(w * RW * 16 + rr) * a.M + m];
+        ybuf[(rbi * a.M + m) * (RW * 16) + rr] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+      }
     }
   };
   if (cpw > 0) {
+    // the loads are unconditional (past the last job they re-read it), so no
+    // branch separates a load from its use and the compiler's waits count
+    // exactly the loads still needed
     int cc = 0, rbi = 0;
-    for (int j0 = 0; j0 < njobs; j0 += NB) {
-#pragma unroll
-      for (int jb = 0; jb < NB; ++jb) {
-        if (j0 + jb < njobs) {                           // wave-uniform
-          compute(b[jb], cc, jb, rbi);
-          load(b[jb], jb);
-          if (++cc == cpw) {
-            flush(rbi);
-            cc = 0;
-            ++rbi;
-          }
+    auto step = [&](CodeChunks<N, RW>& bc, int j, int jb) __attribute__((always_inline)) {
+      if (j < njobs) {                                   // wave-uniform
+        compute(bc, cc, jb, rbi);
+        if (++cc == cpw) {
+          flush(rbi);
+          cc = 0;
+          ++rbi;
         }
       }
+      load(bc, jb);
+    };
+    for (int j0 = 0; j0 < njobs; j0 += NB) {
+      step(b0, j0, 0);
+      step(b1, j0 + 1, 1);
+      if constexpr (NB == 3) step(b2, j0 + 2, 2);
     }
-  } else {
-    for (int rbi = 0; rbi < my_rb; ++rbi) flush(rbi);
   }
   lds_barrier();
   for (int e = threadIdx.x; e < my_rb * a.M * RW * 16; e += 1024) {
@@ -553,14 +589,23 @@ int num_cus() {
   return cached[dev];
 }
 
+// One persistent workgroup per resident slot: as many per CU as registers and
+// LDS allow (the grid is capped by the row blocks).
 template <int N, int RW, int NB>
-void launch_lds(const GemvArgs& a, dim3 grid, int lds, hipStream_t st) {
+void launch_lds(const GemvArgs& a, int64_t nrb, int lds, hipStream_t st) {
   static bool raised = false;                            // allow more than 64 KiB of dynamic LDS, once
   if (!raised) {
     (void)hipFuncSetAttribute((const void*)k_deploy_gemv_lds<N, RW, NB>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsLimit);
     raised = true;
   }
+  int per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_deploy_gemv_lds<N, RW, NB>, 1024, (size_t)lds) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int64_t slots = (int64_t)num_cus() * per_cu;
+  const dim3 grid((unsigned)(nrb < slots ? nrb : slots));
   hipLaunchKernelGGL((k_deploy_gemv_lds<N, RW, NB>), grid, dim3(1024), (size_t)lds, st, a);
 }
 
@@ -582,23 +627,24 @@ void launch_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s1
   a.group = group;
   a.Y = Y;
   LaunchTimer t("deploy_gemv", st);
-  // X in LDS when it fits beside the partial sums (2 x 16 waves x 32 rows x M
-  // fp32), the workgroup's fp16 outputs and the step-size / zero-point slots
-  // (16 waves x NB KiB): one persistent workgroup per CU. Three code buffers for 2-bit
-  // codes, two for 3 and 4 bits (register budget).
-  constexpr int kRW = 2;
+  // X in LDS when it fits beside the partial sums (16 waves x 16 rows x M fp32
+  // per row block), the workgroup's fp16 outputs and the step-size / zero-point
+  // slots: persistent workgroups (the LDS size assumes one per CU, the largest
+  // share of row blocks). Two code buffers: the loads of one job are in
+  // flight during the previous one; deeper buffering measured slower (it adds
+  // redundant loads past a wave's last job and LDS slots).
+  constexpr int kRW = 1;
   const int64_t nrb = (out + 16 * kRW - 1) / (16 * kRW);
-  const int64_t grid_n = nrb < num_cus() ? nrb : num_cus();
-  const int64_t my_rb = (nrb + grid_n - 1) / grid_n;
-  const int nb = bits == 2 ? 3 : 2;
-  const int64_t lds = M * lds_x_stride((int)in) * 2 + 2 * 16 * kRW * 16 * M * 4 +
-                      (my_rb * M * kRW * 16 * 2 + 1023) / 1024 * 1024 + 16 * nb * 1024;
+  const int64_t grid1 = nrb < num_cus() ? nrb : num_cus();
+  const int64_t my_rb = (nrb + grid1 - 1) / grid1;
+  constexpr int nb = 2;
+  const int64_t xbytes = M * (int64_t)lds_x_stride((int)in) * 2;
+  const int64_t lds = xbytes > kLdsLimit ? xbytes : DeployLds::of((int)M, (int)in, (int)my_rb, kRW, nb).total;
   const bool qp_fits = out * (in / group) * 2 >= 16 && out * a.ldz >= 16;   // one 16-byte piece per buffer
   if (lds <= kLdsLimit && qp_fits) {
-    const dim3 grid((unsigned)grid_n);
-    if (bits == 2) launch_lds<2, kRW, 3>(a, grid, (int)lds, st);
-    else if (bits == 3) launch_lds<3, kRW, 2>(a, grid, (int)lds, st);
-    else launch_lds<4, kRW, 2>(a, grid, (int)lds, st);
+    if (bits == 2) launch_lds<2, kRW, nb>(a, nrb, (int)lds, st);
+    else if (bits == 3) launch_lds<3, kRW, nb>(a, nrb, (int)lds, st);
+    else launch_lds<4, kRW, nb>(a, nrb, (int)lds, st);
     return;
   }
   const dim3 grid((unsigned)((out + 15) / 16));
