@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["weight_quantization_aware_amd/csrc/qat_gemm_kernel.h",
+KERNEL_SOURCES = ["weight_quantization_aware_amd/csrc/qat_gemm_kernel.h", "weight_quantization_aware_amd/csrc/qat_dma.h",
                   "weight_quantization_aware_amd/csrc/qat_gemm.hip",
                   "weight_quantization_aware_amd/csrc/qat_elementwise.hip",
                   "weight_quantization_aware_amd/csrc/qat_device.h"]
@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=512, help="weight rows of the bounded oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region run one 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--deploy-only", action="store_true",
+                    help="only the inference linear on the deployment format (Llama-2-70B block, M = 1 and 16)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the context measurements (practical peaks, cold HBM, the C3 block)")
     return ap.parse_args()
@@ -95,6 +97,10 @@ def main():
     from weight_quantization_aware_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.deploy_only:
+        print(json.dumps({"inference_linear_70b_block":
+                          deploy_measurements(Q, torch, dev, torch.cuda.current_stream(dev))}), flush=True)
+        return
     lin = synth.config(2)[0]
     M, out, inp, bits = lin.m, lin.out, lin.inp, lin.bits
     G = inp // 64
@@ -245,6 +251,7 @@ def main():
     extras = None
     if not args.no_extras:
         extras = context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp, X, dY)
+        extras["inference_linear_70b_block"] = deploy_measurements(Q, torch, dev, stream)
         roofline["frac_of_measured_peak"] = round(
             achieved / (extras["measured_peaks"]["mfma_bf16_tflops"] if kind == "mfma"
                         else extras["measured_peaks"]["hbm_read_gbs"]), 4)
@@ -435,6 +442,57 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp,
         "q_proj_fwd_bwd_by_group": groups,
         "clocks": _clocks(),
     }
+
+
+def deploy_measurements(Q, torch, dev, stream):
+    """The inference linear on the deployment format (fp16 step sizes, N-bit
+    zero points) for one token (M = 1) and for 16, over the seven linears of a
+    Llama-2-70B block at w2g64 and w4g64, against torch's fp16 linear on the
+    same shapes (the comparison the EfficientQAT pages make for INT2). Each
+    figure is the median GPU time of 20 calls, every call between its own
+    event pair, all queued behind a GPU sleep so that host launch overhead
+    does not enter; TB/s counts codes, s16, zq, X and Y."""
+    from weight_quantization_aware_amd import synth
+
+    def gpu_med_us(fn, reps=20):
+        fn()
+        torch.cuda.synchronize(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda._sleep(5_000_000)
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        return t[len(t) // 2] * 1e3
+
+    res = {"what": "deployed Llama-2-70B block, group 64; us = median GPU time per call", "linears": {}}
+    tot = {}
+    for name, out, inp in synth.DEPLOY_SHAPES["70b"]:
+        row = {"out": out, "in": inp}
+        for M in (1, 16):
+            X = torch.randn(M, inp, device=dev).half()
+            Y = torch.empty(M, out, dtype=torch.float16, device=dev)
+            W16 = torch.randn(out, inp, device=dev).half()
+            t16 = gpu_med_us(lambda: torch.nn.functional.linear(X, W16))
+            del W16
+            row[f"fp16_M{M}_us"] = round(t16, 2)
+            tot[f"fp16_M{M}"] = tot.get(f"fp16_M{M}", 0.0) + t16
+            for bits in (2, 4):
+                Wq = torch.randint(0, 256, (out, inp * bits // 8), dtype=torch.uint8, device=dev)
+                s16 = (torch.rand(out, inp // 64, device=dev) * 0.05 + 0.002).half()
+                zq = torch.randint(0, 256, (out, Q.deploy_zq_stride(inp, bits)), dtype=torch.uint8, device=dev)
+                t = gpu_med_us(lambda: Q.qat_deploy_gemv(X, Wq, s16, zq, bits, Y))
+                nbytes = Wq.numel() + s16.numel() * 2 + zq.numel() + X.numel() * 2 + Y.numel() * 2
+                row[f"w{bits}_M{M}"] = {"us": round(t, 2), "tbs": round(nbytes / t / 1e6, 2)}
+                tot[f"w{bits}_M{M}"] = tot.get(f"w{bits}_M{M}", 0.0) + t
+        res["linears"][name] = row
+    res["block"] = {k: round(v, 1) for k, v in tot.items()}
+    for M in (1, 16):
+        for bits in (2, 4):
+            res["block"][f"speedup_w{bits}_M{M}_vs_fp16"] = round(tot[f"fp16_M{M}"] / tot[f"w{bits}_M{M}"], 2)
+    return res
 
 
 def cpu_baseline(lin, W_np, X_np, dY_np, rows):

@@ -46,6 +46,14 @@ LABELS = [
     (r"k_w_hat_t<1,", "dequant_t"),
     (r"k_pack<", "pack"),
     (r"k_dequant<", "dequant"),
+    # inference linear on the deployment format: k_deploy_gemv_lds<N, RW, NB>, k_deploy_gemv<N>
+    (r"k_deploy_gemv_lds<2,", "deploy_gemv_w2"),
+    (r"k_deploy_gemv_lds<3,", "deploy_gemv_w3"),
+    (r"k_deploy_gemv_lds<4,", "deploy_gemv_w4"),
+    (r"k_deploy_gemv<2>", "deploy_gemv_xreg_w2"),
+    (r"k_deploy_gemv<3>", "deploy_gemv_xreg_w3"),
+    (r"k_deploy_gemv<4>", "deploy_gemv_xreg_w4"),
+    (r"k_deploy_qparams", "deploy_qparams"),
 ]
 
 
@@ -64,7 +72,7 @@ def stats(db: str, cmd: str) -> None:
     print(f"{'label':22s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s}  kernel")
     for name, n, avg, mn, mx, tot in rows:
         lab = label_of(name) or "-"
-        short = re.sub(r"\(.*", "", name)[:80]
+        short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))[:80]
         print(f"{lab:22s} {n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {tot / 1e3:10.1f}  {short}")
 
 
