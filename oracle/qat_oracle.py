@@ -196,10 +196,15 @@ def fakequant_bwd(dY_bits, X_bits, W, s, z, bits, group: int = GROUP) -> dict:
     ds[o, j] = sum_{i in j} Gw[o, i] * (m_i ? rint(u_i) - u_i : q_i - zr);
     dz[o, j] = sum_{i in j} Gw[o, i] * (m_i ? 0 : -s[o, j]).
     """
+    return fakequant_bwd_values(bf16_bits_to_f64(dY_bits), bf16_bits_to_f64(X_bits), W, s, z, bits, group)
+
+
+def fakequant_bwd_values(dY, X, W, s, z, bits, group: int = GROUP) -> dict:
+    """The same straight-through backward for dY and X given as fp64 values."""
     t = quantize(W, s, z, bits, group)
     w_hat = dequantize_exact(t["q"], t["zr"], t["s"])
-    dY = bf16_bits_to_f64(dY_bits)
-    X = bf16_bits_to_f64(X_bits)
+    dY = np.asarray(dY, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
     dX = dY @ w_hat
     Gw = dY.T @ X
     m = t["m"]
