@@ -35,6 +35,9 @@ Readings where the pages are silent (the GPU path follows the same):
 * all arithmetic fp64 here; the quantiser's own fp32 operations are those of
   qat_oracle.
 
+block_forward_rows gives the output at a few tokens of one sequence (the
+check of the full-size GPU forward on sampled tokens).
+
 Parity status: pinned by tests/test_oracle_block.py (finite differences of
 the whole block loss under the straight-through surrogate, torch autograd on
 an independent float64 statement of the block, torch's AdamW and
@@ -98,19 +101,27 @@ def rope_angles(seq: int, head_dim: int):
     return np.cos(ang), np.sin(ang)                     # [seq, half]
 
 
-def rope(x, shape: BlockShape, inverse: bool = False):
-    """Rotate each head's pair (i, i + head_dim/2) by the angle pos * theta_i
-    (the inverse rotation for the gradient). x: [batch * seq, hidden]."""
-    B, T, nh, hd = shape.batch, shape.seq, shape.heads, shape.head_dim
-    half = hd // 2
-    c, s = rope_angles(T, hd)
+def rope_at(x, pos, heads: int, head_dim: int, inverse: bool = False):
+    """Rotate each head's pair (i, i + head_dim/2) of row r by the angle
+    pos[r] * theta_i, theta_i = 10000^(-2 i / head_dim) (the inverse rotation
+    for the gradient). x: [rows, heads * head_dim]."""
+    half = head_dim // 2
+    inv = ROPE_BASE ** (-np.arange(half, dtype=np.float64) * 2.0 / head_dim)
+    ang = np.asarray(pos, np.float64)[:, None] * inv[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
     if inverse:
         s = -s
-    v = x.reshape(B, T, nh, hd)
+    v = x.reshape(x.shape[0], heads, head_dim)
     a, b = v[..., :half], v[..., half:]
-    c, s = c[None, :, None, :], s[None, :, None, :]
     out = np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
-    return out.reshape(B * T, nh * hd)
+    return out.reshape(x.shape[0], heads * head_dim)
+
+
+def rope(x, shape: BlockShape, inverse: bool = False):
+    """rope_at over a [batch * seq, hidden] tensor: row b * seq + t is at
+    position t."""
+    pos = np.tile(np.arange(shape.seq), shape.batch)
+    return rope_at(x, pos, shape.heads, shape.head_dim, inverse)
 
 
 def attention(q, k, v, shape: BlockShape):
@@ -181,6 +192,31 @@ def block_forward(x, params, g1, g2, shape: BlockShape):
     c["a"] = silu(c["gate"]) * c["up"]
     c["y"] = c["x2"] + fq(c["a"], params["down_proj"], shape)
     return c
+
+
+def block_forward_rows(x, params, g1, g2, shape: BlockShape, b: int, rows):
+    """The block output y at tokens `rows` (positions within sequence b), from
+    that sequence's tokens 0 .. max(rows) only (attention is causal; every
+    other step works row by row). Returns [len(rows), hidden]."""
+    T, nh, hd = shape.seq, shape.heads, shape.head_dim
+    rows = np.asarray(rows)
+    tmax = int(rows.max())
+    xb = x[b * T: b * T + tmax + 1]
+    h1, _ = rmsnorm(xb, g1)
+    k = rope_at(fq(h1, params["k_proj"], shape), np.arange(tmax + 1), nh, hd)
+    v = fq(h1, params["v_proj"], shape)
+    q = rope_at(fq(h1[rows], params["q_proj"], shape), rows, nh, hd)
+    attn = np.empty((len(rows), nh * hd))
+    for r, t in enumerate(rows):
+        for h in range(nh):
+            cols = slice(h * hd, (h + 1) * hd)
+            sc = k[: t + 1, cols] @ q[r, cols] / math.sqrt(hd)
+            p = np.exp(sc - sc.max())
+            attn[r, cols] = (p / p.sum()) @ v[: t + 1, cols]
+    x2 = xb[rows] + fq(attn, params["o_proj"], shape)
+    h2, _ = rmsnorm(x2, g2)
+    a = silu(fq(h2, params["gate_proj"], shape)) * fq(h2, params["up_proj"], shape)
+    return x2 + fq(a, params["down_proj"], shape)
 
 
 def mse(y, target):

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from weight_quantization_aware_amd import _lib as Q
@@ -14,7 +15,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def declared():
     names = set()
-    for h in ("qat.h", "qat_peaks.h"):
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
         src = open(os.path.join(ROOT, "include", h)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         names |= set(re.findall(r"\b(qat_[a-z0-9_]+)\s*\(", src))
@@ -24,7 +27,8 @@ def declared():
 def test_header_declares_the_calls():
     names = declared()
     for n in ["qat_init_minmax", "qat_fakequant_linear_fwd", "qat_fakequant_linear_bwd", "qat_pack",
-              "qat_dequant_gemm_fwd", "qat_dequant_gemm_bwd_s", "qat_quant_codes"]:
+              "qat_dequant_gemm_fwd", "qat_dequant_gemm_bwd_s", "qat_quant_codes", "qat_block_ap_step",
+              "qat_block_forward", "qat_block_ws_bytes"]:
         assert n in names
 
 
@@ -138,3 +142,72 @@ def test_deploy_validation():
     assert Q.deploy_zq_stride(192, 3, group=192) == 1
     assert Q.deploy_zq_stride(4096, 4) == 32
     assert Q.deploy_zq_stride(4096, 4, group=48) == 0
+
+
+# ---------------------------------------------------------------------------
+# The Block-AP step (include/qat_block.h): host-side validation only
+# ---------------------------------------------------------------------------
+
+def _block_args(shape, n_lin=7, step=True):
+    lins = (Q.BlockLinear * 7)()
+    for i in range(n_lin):
+        for j, f in enumerate(Q._LIN_FIELDS):
+            if step or f in ("W", "s", "z"):
+                setattr(lins[i], f, FAKE * (1 + 64 * i + 4 * j))
+    return lins
+
+
+def test_block_ws_bytes():
+    sh = Q.block_shape(4096, 32, 11008, 2048, 2, 2)
+    n = Q.block_ws_bytes(sh)
+    BT, H, I, S = 4096, 4096, 11008, 2 * 32 * 2048 * 2048
+    # at least the activations the backward reads and the scores in fp32 and bf16
+    assert n >= S * 6 + BT * H * 2 * 4 + BT * I * 2 * 3
+    assert n % 256 == 0 and n < 3 * 2 ** 30
+    for bad in [Q.block_shape(4096, 30, 11008, 2048, 2, 2),    # head size not 128
+                Q.block_shape(4096, 32, 11000, 2048, 2, 2),    # inter % 64
+                Q.block_shape(4096, 32, 11008, 2000, 2, 2),    # seq % 64
+                Q.block_shape(4096, 32, 11008, 8192, 1, 2),    # seq > 4096
+                Q.block_shape(16384, 128, 11008, 2048, 2, 2),  # hidden > 8192
+                Q.block_shape(4096, 32, 11008, 2048, 2, 5),    # bits
+                Q.block_shape(4096, 32, 11008, 2048, 2, 2, 96),
+                Q.block_shape(4096, 32, 11072, 2048, 2, 2, 128)]:  # group does not divide inter
+        assert Q.block_ws_bytes(bad) == 0
+
+
+def test_block_validation():
+    L = Q.lib()
+    sh = Q.block_shape(256, 2, 704, 192, 2, 2)
+    need = Q.block_ws_bytes(sh)
+    opt = Q.BlockAdamW(2e-5, 1e-4, 0.9, 0.999, 1e-8, 0.0, 0, 4096)
+    X, T, G1, G2, Y, LOSS, WS = (FAKE << 12) * np.arange(1, 8)
+    X, T, G1, G2, Y, LOSS, WS = (int(v) for v in (X, T, G1, G2, Y, LOSS, WS))
+    lins = _block_args(sh)
+    step = lambda **kw: L.qat_block_ap_step(kw.get("shape", ctypes.byref(sh)), kw.get("lins", lins), G1, G2, X, T,
+                                            kw.get("opt", ctypes.byref(opt)), Y, LOSS, WS, kw.get("ws", need), None)
+    assert step(ws=need - 256) == 6                               # workspace too small
+    bad = Q.block_shape(256, 2, 704, 100, 2, 2)
+    assert step(shape=ctypes.byref(bad)) == 2
+    bad = Q.block_shape(256, 2, 704, 192, 2, 2, 48)
+    assert step(shape=ctypes.byref(bad)) == 4
+    assert step(opt=None) == 1
+    o2 = Q.BlockAdamW(2e-5, 1e-4, 1.0, 0.999, 1e-8, 0.0, 0, 4096)    # beta1 outside [0, 1)
+    assert step(opt=ctypes.byref(o2)) == 2
+    o3 = Q.BlockAdamW(2e-5, 1e-4, 0.9, 0.999, 1e-8, 0.0, 0, 0)       # no schedule length
+    assert step(opt=ctypes.byref(o3)) == 2
+    assert step(lins=_block_args(sh, step=False)) == 1             # gradients and moments required
+    l2 = _block_args(sh)
+    l2[3].ds = l2[3].dz                                            # two outputs share memory
+    assert step(lins=l2) == 8
+    l3 = _block_args(sh)
+    l3[6].W = l3[6].W + 4                                          # misaligned
+    assert step(lins=l3) == 5
+    l4 = _block_args(sh)
+    l4[0].m_W = X                                                  # a moment over the input
+    assert step(lins=l4) == 8
+    # the forward call needs only W, s, z but checks the same shapes and regions
+    fwd = L.qat_block_forward(ctypes.byref(sh), _block_args(sh, step=False), G1, G2, X, T, Y, LOSS, WS, need - 1,
+                              None)
+    assert fwd == 6
+    assert L.qat_block_forward(ctypes.byref(sh), _block_args(sh, step=False), G1, G2, X, T, X, LOSS, WS, need,
+                               None) == 8                          # y over x

@@ -1,0 +1,289 @@
+"""GPU parity of one Block-AP step on a Llama-2 decoder block (include/qat_block.h)
+against the fp64 block oracle, through the C ABI.
+
+Bars. Every block output passes through bf16 activations (h1, q, k, v, P, the
+attention output, h2, gate, up, the SiLU product and every gradient that
+enters a GEMM; unit roundoff u = 2^-9) and bf16 W_hat, while the oracle
+carries fp64 throughout. A gradient at q_proj crosses about eight such
+roundings between the loss and its GEMM (dy, down dX, SiLU backward, gate/up
+dX, RMSNorm backward, o dX, the attention backward, RoPE), each adding a
+relative Frobenius error of order u; sqrt(8) * 2 u ~ 1.1e-2. The bar is the
+one for bf16 GEMM outputs, relative Frobenius 2e-2, on the loss, the block's
+contribution y - x, every dW, ds, dz and every parameter update.
+The optimiser itself is checked tightly on the GPU's own gradients and
+moments (fp32 rounding only): AdamW is elementwise, so its outputs must equal
+the fp64 update of those inputs to a few fp32 ulps.
+Parameter updates against the oracle's: an early AdamW step is close to
+lr * sign(g), so an element whose gradient is near zero may take the other
+sign under bf16 rounding and move by 2 lr. Updates are compared where
+|g_ref| >= 0.1 rms(g_ref) (relative Frobenius 2e-2), and the fraction of
+elements whose update has the other sign is bounded by 2e-2 / pi per step:
+for a gradient g ~ N(0, sigma^2) with an independent error of relative size
+eps, P(sign(g + e) != sign(g)) = arctan(eps) / pi <= eps / pi, and eps is
+the gradient bar. After two steps the mask takes both steps' gradients.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import block_oracle as B
+from oracle import qat_oracle as O
+from tests.helpers import dev_bf16, dev_f32, rel_fro, say
+from weight_quantization_aware_amd import _lib as Q
+from weight_quantization_aware_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BAR = 2e-2
+KEYS = ("W", "s", "z")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    Q.lib()
+
+
+def bf(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def make(case, cfg=6):
+    H, nh, I, T, Bn, bits, g = case
+    sh = B.BlockShape(hidden=H, heads=nh, inter=I, seq=T, batch=Bn, bits=bits, group=g)
+    d = synth.block_inputs(cfg, H, I, T * Bn, 4 if H < 512 else 8)
+    params = {}
+    for n in B.LINEARS:
+        W = d["W"][n]
+        s, z = O.init_minmax(W, bits, g)
+        params[n] = {"W": W, "s": s, "z": z}
+    return sh, d, params
+
+
+def opt_dict(o: B.AdamW, step: int):
+    return {"lr_weight": o.lr_weight, "lr_quant": o.lr_quant, "beta1": o.betas[0], "beta2": o.betas[1],
+            "eps": o.eps, "weight_decay": o.weight_decay, "step": step, "total_steps": o.total_steps}
+
+
+class GpuBlock:
+    def __init__(self, sh, d, params):
+        self.shape = Q.block_shape(sh.hidden, sh.heads, sh.inter, sh.seq, sh.batch, sh.bits, sh.group)
+        self.ws = Q.workspace(Q.block_ws_bytes(self.shape))
+        self.lins = []
+        for n in B.LINEARS:
+            e = {k: dev_f32(params[n][k]) for k in KEYS}
+            for k in KEYS:
+                e["d" + k] = torch.full_like(e[k], float("nan"))
+                e["m_" + k] = torch.zeros_like(e[k])
+                e["v_" + k] = torch.zeros_like(e[k])
+            self.lins.append(e)
+        self.x, self.t = dev_bf16(d["x"]), dev_bf16(d["target"])
+        self.g1, self.g2 = dev_f32(d["g1"]), dev_f32(d["g2"])
+        self.loss = torch.empty(1, dtype=torch.float32, device="cuda")
+        self.y = torch.empty(sh.batch * sh.seq, sh.hidden, dtype=torch.float32, device="cuda")
+
+    def step(self, opt):
+        Q.qat_block_ap_step(self.shape, self.lins, self.g1, self.g2, self.x, self.t, opt, self.loss, y=self.y,
+                            ws=self.ws)
+        torch.cuda.synchronize()
+        return float(self.loss.item())
+
+    def forward(self):
+        Q.qat_block_forward(self.shape, self.lins, self.g1, self.g2, self.x, self.t, self.loss, y=self.y,
+                            ws=self.ws)
+        torch.cuda.synchronize()
+        return float(self.loss.item())
+
+    def host(self, i, key):
+        return self.lins[i][key].cpu().numpy()
+
+
+def zero_state(params):
+    return {n: {k: (np.zeros(v.shape), np.zeros(v.shape)) for k, v in p.items()} for n, p in params.items()}
+
+
+def check_adamw_identity(lin_before, lin_after, opt, ctx):
+    """AdamW on the GPU's own gradient and moments, recomputed in fp64."""
+    b1, b2 = np.float32(opt["beta1"]), np.float32(opt["beta2"])
+    k = opt["step"]
+    c = (1.0 + math.cos(math.pi * k / opt["total_steps"])) / 2.0
+    t = k + 1
+    bc1, bc2 = 1.0 - opt["beta1"] ** t, 1.0 - opt["beta2"] ** t
+    for key in KEYS:
+        lr = (opt["lr_weight"] if key == "W" else opt["lr_quant"]) * c
+        p0, m0, v0 = (lin_before[x].astype(np.float64) for x in (key, "m_" + key, "v_" + key))
+        g = lin_after["d" + key].astype(np.float64)
+        p1, m1, v1 = (lin_after[x].astype(np.float64) for x in (key, "m_" + key, "v_" + key))
+        # fp32: each moment is a sum of two rounded products (the second moment's
+        # second term two products), so its error is a few units of 2^-24 of
+        # the terms' magnitudes (the sum itself may cancel)
+        m_ref = float(b1) * m0 + (1.0 - float(b1)) * g
+        v_ref = float(b2) * v0 + (1.0 - float(b2)) * g * g
+        m_mag = float(b1) * np.abs(m0) + (1.0 - float(b1)) * np.abs(g)
+        v_mag = float(b2) * v0 + (1.0 - float(b2)) * g * g
+        assert np.all(np.abs(m1 - m_ref) <= 2.0 ** -22 * m_mag + 1e-45), (ctx, key, "m")
+        assert np.all(np.abs(v1 - v_ref) <= 2.0 ** -21 * v_mag + 1e-45), (ctx, key, "v")
+        upd = (lr / bc1) * m1 / (np.sqrt(v1 / bc2) + opt["eps"])
+        p_ref = p0 * (1.0 - lr * opt["weight_decay"]) - upd
+        ulp = np.spacing(np.abs(p_ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(p1 - p_ref) <= 2 * ulp + 1e-5 * np.abs(upd)), (ctx, key, "p")
+
+
+def check_update(p_gpu, p0, p_ref, g_refs, ctx):
+    """Update after len(g_refs) steps, whose oracle gradients are g_refs."""
+    d_gpu = np.asarray(p_gpu, np.float64) - p0
+    d_ref = np.asarray(p_ref, np.float64) - p0
+    big = np.ones(d_ref.shape, bool)
+    for g in g_refs:
+        g = np.asarray(g, np.float64)
+        big &= np.abs(g) >= 0.1 * np.sqrt(np.mean(g * g))
+    e = rel_fro(d_gpu[big], d_ref[big])
+    flips = np.mean(np.sign(d_gpu) != np.sign(d_ref))
+    assert e < BAR and flips < len(g_refs) * BAR / math.pi, (ctx, e, flips)
+    return e, flips
+
+
+def report(name, v):
+    say(f"  {name}: {v:.3e}")
+    return v
+
+
+CASES = [
+    # hidden, heads, inter, seq, batch, bits, group
+    pytest.param((256, 2, 704, 192, 2, 2, 64), id="h256-t192x2-w2g64"),
+    pytest.param((512, 4, 1408, 320, 1, 3, 128), id="h512-t320-w3g128"),
+    pytest.param((1024, 8, 2816, 1024, 2, 4, 32), id="h1024-t1024x2-w4g32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_block_step_parity(case):
+    sh, d, params = make(case)
+    say(f"block step {case}")
+    o = B.AdamW()
+    x64, t64 = bf(d["x"]), bf(d["target"])
+    g1, g2 = d["g1"].astype(np.float64), d["g2"].astype(np.float64)
+    ref_y = B.block_forward(x64, params, g1, g2, sh)["y"]
+    loss_ref, p_ref, _, grads_ref = B.block_ap_step(x64, t64, params, zero_state(params), g1, g2, sh, 0, o)
+
+    gb = GpuBlock(sh, d, params)
+    before = [{k: v.cpu().numpy() for k, v in lin.items()} for lin in gb.lins]
+    loss = gb.step(opt_dict(o, 0))
+    after = [{k: v.cpu().numpy() for k, v in lin.items()} for lin in gb.lins]
+    y = gb.y.cpu().numpy()
+
+    assert report("loss", abs(loss - loss_ref) / loss_ref) < BAR
+    assert report("y - x", rel_fro(y - x64, ref_y - x64)) < BAR
+    worst = worst_u = worst_f = 0.0
+    for i, n in enumerate(B.LINEARS):
+        for key in KEYS:
+            e = rel_fro(after[i]["d" + key], grads_ref[n][key])
+            worst = max(worst, e)
+            assert e < BAR, (n, key, e)
+            du, fl = check_update(after[i][key], params[n][key], p_ref[n][key], [grads_ref[n][key]], (n, key))
+            worst_u, worst_f = max(worst_u, du), max(worst_f, fl)
+        check_adamw_identity(before[i], after[i], opt_dict(o, 0), n)
+    report("worst gradient", worst)
+    report("worst update (|g| >= 0.1 rms)", worst_u)
+    report("worst sign-flip fraction", worst_f)
+
+
+def test_block_forward_call_matches_step_forward():
+    sh, d, params = make(CASES[0].values[0])
+    gb = GpuBlock(sh, d, params)
+    loss_f = gb.forward()
+    y_f = gb.y.cpu().numpy()
+    x64 = bf(d["x"])
+    c = B.block_forward(x64, params, d["g1"].astype(np.float64), d["g2"].astype(np.float64), sh)
+    loss_ref, _ = B.mse(c["y"], bf(d["target"]))
+    assert rel_fro(y_f - x64, c["y"] - x64) < BAR
+    assert abs(loss_f - loss_ref) / loss_ref < BAR
+    # the forward call leaves the parameters alone; the step's forward is the same computation
+    for i, n in enumerate(B.LINEARS):
+        for key in KEYS:
+            assert np.array_equal(gb.host(i, key), params[n][key])
+    loss_s = gb.step(opt_dict(B.AdamW(), 0))
+    assert loss_s == loss_f
+    assert np.array_equal(gb.y.cpu().numpy(), y_f)
+
+
+def test_block_two_steps_and_schedule():
+    # two consecutive steps (moments carried): the second step's loss and
+    # gradients (after one update) and its update; then a step late in the
+    # cosine schedule with weight decay from fresh moments
+    sh, d, params = make(CASES[0].values[0])
+    o = B.AdamW()
+    x64, t64 = bf(d["x"]), bf(d["target"])
+    g1, g2 = d["g1"].astype(np.float64), d["g2"].astype(np.float64)
+    _, p1, st1, grads1_ref = B.block_ap_step(x64, t64, params, zero_state(params), g1, g2, sh, 0, o)
+    loss2_ref, p2, _, grads2_ref = B.block_ap_step(x64, t64, p1, st1, g1, g2, sh, 1, o)
+    gb = GpuBlock(sh, d, params)
+    gb.step(opt_dict(o, 0))
+    mid = [{k: v.cpu().numpy() for k, v in lin.items()} for lin in gb.lins]
+    loss2 = gb.step(opt_dict(o, 1))
+    end = [{k: v.cpu().numpy() for k, v in lin.items()} for lin in gb.lins]
+    assert report("second-step loss", abs(loss2 - loss2_ref) / loss2_ref) < BAR
+    for i, n in enumerate(B.LINEARS):
+        check_adamw_identity(mid[i], end[i], opt_dict(o, 1), n)
+        for key in KEYS:
+            assert rel_fro(end[i]["d" + key], grads2_ref[n][key]) < BAR, (n, key)
+            check_update(end[i][key], params[n][key], p2[n][key], [grads1_ref[n][key], grads2_ref[n][key]],
+                         (n, key, "two steps"))
+
+    o2 = B.AdamW(weight_decay=0.01, total_steps=4096)
+    k = 3000
+    _, p3, _, g3 = B.block_ap_step(x64, t64, params, zero_state(params), g1, g2, sh, k, o2)
+    gb = GpuBlock(sh, d, params)
+    before = [{k_: v.cpu().numpy() for k_, v in lin.items()} for lin in gb.lins]
+    gb.step(opt_dict(o2, k))
+    after = [{k_: v.cpu().numpy() for k_, v in lin.items()} for lin in gb.lins]
+    for i, n in enumerate(B.LINEARS):
+        check_adamw_identity(before[i], after[i], opt_dict(o2, k), n)
+        for key in KEYS:
+            check_update(after[i][key], params[n][key], p3[n][key], [g3[n][key]], (n, key, "late step"))
+
+
+def test_block_step_full_size_7b():
+    """Llama-2-7B block, 2 x 2048 tokens, w2g64 (the benchmark's step): the
+    forward on sampled tokens of the second sequence against the oracle; the
+    loss against the GPU's own y; the straight-through mask and the in-range
+    ds identity of every linear; AdamW on the GPU's own gradients."""
+    H, nh, I, T, Bn = synth.BLOCK_7B
+    case = (H, nh, I, T, Bn, 2, 64)
+    say(f"block step full size {case}")
+    sh, d, params = make(case)
+    gb = GpuBlock(sh, d, params)
+    o = opt_dict(B.AdamW(), 0)
+    loss = gb.step(o)
+    y = gb.y.cpu().numpy()
+    x64, t64 = bf(d["x"]), bf(d["target"])
+    assert abs(loss - np.mean((y - t64) ** 2)) <= 1e-5 * loss
+
+    rows = np.array([0, 1, 63, 64, 777, 1500, T - 1])
+    yr = B.block_forward_rows(x64, params, d["g1"].astype(np.float64), d["g2"].astype(np.float64), sh, 1, rows)
+    assert report("sampled y - x", rel_fro(y[T + rows] - x64[T + rows], yr - x64[T + rows])) < BAR
+
+    for i, n in enumerate(B.LINEARS):
+        p = params[n]
+        dW = gb.host(i, "dW")
+        ds, dz = gb.host(i, "ds"), gb.host(i, "dz")
+        t = O.quantize(p["W"], p["s"], p["z"], 2, 64)
+        m = t["m"].astype(bool)
+        assert np.all(dW[~m] == 0.0), n
+        assert np.isfinite(dW).all() and np.isfinite(ds).all() and np.isfinite(dz).all()
+        G = p["W"].shape[1] // 64
+        allin = m.reshape(m.shape[0], G, 64).all(-1)
+        frac = (np.rint(t["u"]) - t["u"]).astype(np.float64)
+        pred = (dW.astype(np.float64) * frac).reshape(m.shape[0], G, 64).sum(-1)
+        scale = (np.abs(dW.astype(np.float64)) * np.abs(frac)).reshape(m.shape[0], G, 64).sum(-1)
+        assert np.all(np.abs(ds - pred)[allin] <= 1e-5 * scale[allin] + 1e-30), n
+        assert np.all(dz[allin] == 0.0), n
+    # AdamW identity on the first three linears' tensors (the others share the kernel)
+    for i in range(3):
+        before = {k: params[B.LINEARS[i]][k] for k in KEYS}
+        before.update({f"{mv}_{k}": np.zeros_like(before[k]) for k in KEYS for mv in ("m", "v")})
+        after = {k: v.cpu().numpy() for k, v in gb.lins[i].items()}
+        check_adamw_identity(before, after, o, B.LINEARS[i])

@@ -310,3 +310,28 @@ def test_block_ap_step_moves_every_parameter_group():
             g = grads[n][key]
             expect = Q.fl32(np.asarray(params[n][key], np.float64) - lr * g / (np.abs(g) + opt.eps))
             assert np.array_equal(newp[n][key], expect), (n, key)
+
+
+def test_forward_rows_match_torch_statement():
+    # the sampled-token forward against the independent torch statement's output
+    rng = np.random.default_rng(9)
+    sh = B.BlockShape(hidden=32, heads=2, inter=48, seq=9, batch=2, bits=3, group=16)
+    params = _params(sh, rng)
+    x, tgt, g1, g2 = _inputs(sh, rng)
+    ty, _, _ = _torch_block(x, tgt, g1, g2, params, sh)
+    for b, rows in ((0, [0, 4, 8]), (1, [3]), (1, [0, 1, 2, 5, 6])):
+        y = B.block_forward_rows(x, params, g1, g2, sh, b, rows)
+        assert np.allclose(y, ty[b * sh.seq + np.asarray(rows)], rtol=1e-12, atol=1e-12), (b, rows)
+
+
+def test_rope_at_positions():
+    # rope over a whole tensor equals rope_at with the tokens' positions; a
+    # position-p rotation composed with its inverse is the identity
+    rng = np.random.default_rng(10)
+    sh = B.BlockShape(hidden=64, heads=2, inter=64, seq=5, batch=3, bits=2)
+    x = rng.standard_normal((sh.batch * sh.seq, sh.hidden))
+    pos = np.tile(np.arange(sh.seq), sh.batch)
+    assert np.array_equal(B.rope(x, sh), B.rope_at(x, pos, sh.heads, sh.head_dim))
+    p = rng.integers(0, 4096, x.shape[0])
+    back = B.rope_at(B.rope_at(x, p, 2, 32), p, 2, 32, inverse=True)
+    assert np.allclose(back, x, rtol=1e-12, atol=1e-12)

@@ -54,6 +54,35 @@ _RES = {"qat_deploy_zq_stride": _c_i64, "qat_fakequant_ws_bytes": _c_sz, "qat_de
         "qat_peak_scratch_bytes": _c_sz,
         "qat_status_string": ctypes.c_char_p, "qat_last_error": ctypes.c_char_p}
 
+# include/qat_block.h
+BLOCK_LINEARS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+_LIN_FIELDS = ("W", "s", "z", "dW", "ds", "dz", "m_W", "v_W", "m_s", "v_s", "m_z", "v_z")
+
+
+class BlockShape(ctypes.Structure):
+    _fields_ = [("hidden", _c_i64), ("heads", _c_i64), ("inter", _c_i64), ("seq", _c_i64),
+                ("batch", _c_i64), ("bits", _c_i32), ("group", _c_i32)]
+
+
+class BlockLinear(ctypes.Structure):
+    _fields_ = [(f, _c_vp) for f in _LIN_FIELDS]
+
+
+class BlockAdamW(ctypes.Structure):
+    _fields_ = [("lr_weight", ctypes.c_double), ("lr_quant", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("step", _c_i64), ("total_steps", _c_i64)]
+
+
+_SIGS.update({
+    "qat_block_ws_bytes": [ctypes.POINTER(BlockShape)],
+    "qat_block_forward": [ctypes.POINTER(BlockShape), ctypes.POINTER(BlockLinear), _c_vp, _c_vp, _c_vp, _c_vp,
+                          _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
+    "qat_block_ap_step": [ctypes.POINTER(BlockShape), ctypes.POINTER(BlockLinear), _c_vp, _c_vp, _c_vp, _c_vp,
+                          ctypes.POINTER(BlockAdamW), _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
+})
+_RES["qat_block_ws_bytes"] = _c_sz
+
 _lib = None
 
 
@@ -245,3 +274,45 @@ def peak_read(buf: torch.Tensor, blocks: int, scratch: torch.Tensor) -> int:
     nbytes = buf.numel() * buf.element_size()
     _call("qat_peak_read", _p(buf), nbytes, blocks, _p(scratch), _stream())
     return nbytes - nbytes % 16
+
+
+# ---------------------------------------------------------------------------
+# One Block-AP step on a Llama-2 decoder block (include/qat_block.h)
+# ---------------------------------------------------------------------------
+
+def block_shape(hidden, heads, inter, seq, batch, bits, group: int = GROUP) -> BlockShape:
+    return BlockShape(hidden, heads, inter, seq, batch, bits, group)
+
+
+def block_ws_bytes(shape: BlockShape) -> int:
+    return int(lib().qat_block_ws_bytes(ctypes.byref(shape)))
+
+
+def _linears(lins):
+    """lins: 7 dicts (q, k, v, o, gate, up, down) of fp32 tensors keyed by
+    W, s, z, dW, ds, dz, m_W, v_W, m_s, v_s, m_z, v_z (missing keys: NULL)."""
+    if len(lins) != 7:
+        raise ValueError("seven linears: q, k, v, o, gate, up, down")
+    arr = (BlockLinear * 7)()
+    for i, d in enumerate(lins):
+        for f in _LIN_FIELDS:
+            t = d.get(f)
+            if t is not None and t.dtype != torch.float32:
+                raise TypeError(f"linear {i} {f}: expected fp32, got {t.dtype}")
+            setattr(arr[i], f, _p(t))
+    return arr
+
+
+def qat_block_forward(shape: BlockShape, lins, g1, g2, x, target, loss, y=None, ws=None) -> None:
+    arr = _linears(lins)
+    _call("qat_block_forward", ctypes.byref(shape), arr, _p(g1), _p(g2), _p(_u16(x)), _p(_u16(target)), _p(y),
+          _p(loss), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
+
+
+def qat_block_ap_step(shape: BlockShape, lins, g1, g2, x, target, opt: dict, loss, y=None, ws=None) -> None:
+    """opt: lr_weight, lr_quant, beta1, beta2, eps, weight_decay, step (0-based), total_steps."""
+    o = BlockAdamW(opt["lr_weight"], opt["lr_quant"], opt["beta1"], opt["beta2"], opt["eps"],
+                   opt["weight_decay"], opt["step"], opt["total_steps"])
+    arr = _linears(lins)
+    _call("qat_block_ap_step", ctypes.byref(shape), arr, _p(g1), _p(g2), _p(_u16(x)), _p(_u16(target)),
+          ctypes.byref(o), _p(y), _p(loss), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())

@@ -203,9 +203,11 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
   return finish();
 }
 
+namespace qat {
+
 // dX = dY W_hat with W_hat^T [in][out] bf16 staged in the workspace: both
 // operands K-contiguous (K = out).
-static void launch_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, int64_t out, int64_t in,
+void launch_linear_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, int64_t out, int64_t in,
                       uint16_t* dX, hipStream_t stream) {
   qat::GemmArgs a = gemm_args();
   a.A = dY;
@@ -221,7 +223,7 @@ static void launch_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, in
 }
 
 // Gw = dY^T X over the M tokens, both read in place, reduced by the epilogue.
-static qat::GemmArgs grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z,
+qat::GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z,
                                 int64_t M, int64_t out, int64_t in, int group, int bits) {
   qat::GemmArgs a = gemm_args();
   a.A = dY;
@@ -238,6 +240,11 @@ static qat::GemmArgs grads_args(const uint16_t* dY, const uint16_t* X, const flo
   a.Kq = (float)((1 << bits) - 1);
   return a;
 }
+
+// QAT_OK, or QAT_ERR_HIP with the launch error kept for qat_last_error.
+int32_t finish_call() { return finish(); }
+
+}  // namespace qat
 
 QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
                                          const float* s, const float* z, int64_t M, int64_t out,
@@ -261,10 +268,10 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
   if (dX) {
     uint16_t* w_hat = (uint16_t*)ws;
     qat::launch_w_hat_t(W, s, z, out, in, group, bits, w_hat, stream);
-    launch_dx(dY, w_hat, M, out, in, dX, stream);
+    qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
   }
   if (dW || ds) {
-    qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, group, bits);
+    qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
     a.W = W;
     a.ldw = in;
     a.dW = dW;
@@ -336,9 +343,9 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
   if (dX) {
     uint16_t* w_hat = (uint16_t*)ws;
     qat::launch_dequant_t(Wq, s, z, out, in, group, bits, w_hat, stream);
-    launch_dx(dY, w_hat, M, out, in, dX, stream);
+    qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
   }
-  qat::GemmArgs a = grads_args(dY, X, s, z, M, out, in, group, bits);
+  qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
   a.Wq = Wq;
   a.ldq = in * bits / 8;
   a.ds = ds;

@@ -1,0 +1,944 @@
+// One Block-AP training step on a Llama-2 decoder block with seven
+// fake-quantised linears (gfx950): the row kernels of the block (RMSNorm,
+// rotary embedding, causal softmax, SiLU-gated product, mean-squared error),
+// the multi-tensor AdamW, and the launch sequence of the forward, the
+// straight-through backward and the update.
+//
+// Sources: "EfficientQAT, low-bit training on a single GPU"
+// (modelfoundations.com), Phase 1 (Block-AP: block-wise MSE to the
+// full-precision outputs, W with s and z trained together, AdamW with two
+// learning rates on cosine schedules); paperlayer.ai summary of arXiv
+// 2407.11062v3, Appendix A (straight-through gradients of W, s, z). The block
+// itself is Llama-2's (the pages name the model family, not its layers).
+//
+// Memory-bound row kernels: one workgroup per token row for the norms (a row
+// of H <= 8192 values stays in registers between the reduction and the
+// write), one wave per score row for the softmax (a row of T <= 4096 scores
+// in registers), 16-byte vector accesses throughout.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/qat_block.h"
+#include "qat_device.h"
+#include "qat_internal.h"
+
+namespace qat {
+namespace {
+
+constexpr float kRmsEps = 1e-5f;
+constexpr double kRopeBase = 10000.0;
+constexpr int kHeadDim = 128;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+__device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Sum over a 256-thread workgroup; every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();                        // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm forward: h = bf16(x r g), r = 1 / sqrt(mean(x^2) + eps) per row.
+// RES = 1 forms the residual x = x_in + o (bf16 + fp32) first and stores it
+// as fp32 (the block's x2). A thread owns chunks of 8 columns t, t + 256, ...
+// (at most 4: H <= 8192).
+// ---------------------------------------------------------------------------
+template <int RES>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd(const uint16_t* __restrict__ x, const float* __restrict__ o,
+                                                      float* __restrict__ xres, const float* __restrict__ g,
+                                                      uint16_t* __restrict__ h, float* __restrict__ r, int H) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nc = H / 8;
+  float v[4][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < nc) {
+      unpack8(*(const uint4*)(x + row * H + 8 * c), v[j]);
+      if constexpr (RES) {
+        const float4 a = *(const float4*)(o + row * H + 8 * c), b = *(const float4*)(o + row * H + 8 * c + 4);
+        const float ov[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] += ov[e];
+        *(float4*)(xres + row * H + 8 * c) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+        *(float4*)(xres + row * H + 8 * c + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+    }
+  }
+  const float tot = block_sum(ss, red);
+  const float rr = 1.0f / sqrtf(tot / (float)H + kRmsEps);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < nc) {
+      const float4 a = *(const float4*)(g + 8 * c), b = *(const float4*)(g + 8 * c + 4);
+      const float gv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      float out[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = v[j][e] * rr * gv[e];
+      *(uint4*)(h + row * H + 8 * c) = pack8(out);
+    }
+  }
+  if (threadIdx.x == 0) r[row] = rr;
+}
+
+// RMSNorm backward with the residual: dx = dres + r (g dh) - r^3 x mean(x g dh),
+// dh = dh_a + dh_b (the two linears fed by the normed row), out bf16.
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict__ dha,
+                                                      const uint16_t* __restrict__ dhb,
+                                                      const float* __restrict__ x, const float* __restrict__ r,
+                                                      const float* __restrict__ g, const uint16_t* __restrict__ dres,
+                                                      uint16_t* __restrict__ dx, int H) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nc = H / 8;
+  float gd[4][8], xv[4][8];
+  float dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < nc) {
+      float a[8], b[8];
+      unpack8(*(const uint4*)(dha + row * H + 8 * c), a);
+      unpack8(*(const uint4*)(dhb + row * H + 8 * c), b);
+      const float4 g0 = *(const float4*)(g + 8 * c), g1 = *(const float4*)(g + 8 * c + 4);
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float4 x0 = *(const float4*)(x + row * H + 8 * c), x1 = *(const float4*)(x + row * H + 8 * c + 4);
+      const float xx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        gd[j][e] = (a[e] + b[e]) * gv[e];
+        xv[j][e] = xx[e];
+        dot += xx[e] * gd[j][e];
+      }
+    }
+  }
+  const float mean = block_sum(dot, red) / (float)H;
+  const float rr = r[row];
+  const float r3m = rr * rr * rr * mean;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < nc) {
+      float d[8], out[8];
+      unpack8(*(const uint4*)(dres + row * H + 8 * c), d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = d[e] + (rr * gd[j][e] - r3m * xv[j][e]);
+      *(uint4*)(dx + row * H + 8 * c) = pack8(out);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rotary embedding. cs[t][i] = (cos, sin) of t * 10000^(-2 i / 128), from
+// double-precision angles. A thread rotates 8 pairs (i, i + 64) of one head
+// in place: a' = a c - b s, b' = b c + a s (s negated for the gradient,
+// which is the inverse rotation).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rope_table(float2* __restrict__ cs, int T) {
+  constexpr int half = kHeadDim / 2;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, i = idx % half;
+  const double ang = (double)t * pow(kRopeBase, -2.0 * i / kHeadDim);
+  cs[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+__global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                                              const float2* __restrict__ cs, int64_t rows, int T, int H,
+                                              float sgn) {
+  constexpr int half = kHeadDim / 2, TPH = half / 8;   // threads per head
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = rows * (H / 16);                  // threads per tensor
+  if (idx >= 2 * per) return;
+  uint16_t* x = idx < per ? q : k;
+  const int64_t rem = idx < per ? idx : idx - per;
+  const int64_t row = rem / (H / 16);
+  const int j = (int)(rem % (H / 16));
+  const int head = j / TPH, i0 = (j % TPH) * 8;
+  const int t = (int)(row % T);
+  uint16_t* base = x + row * H + head * kHeadDim + i0;
+  float a[8], b[8], oa[8], ob[8];
+  unpack8(*(const uint4*)base, a);
+  unpack8(*(const uint4*)(base + half), b);
+  const float2* c = cs + (int64_t)t * half + i0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float2 v = c[e];
+    const float sn = sgn * v.y;
+    oa[e] = a[e] * v.x - b[e] * sn;
+    ob[e] = b[e] * v.x + a[e] * sn;
+  }
+  *(uint4*)base = pack8(oa);
+  *(uint4*)(base + half) = pack8(ob);
+}
+
+// ---------------------------------------------------------------------------
+// Causal softmax over the scores of one query row (one wave per row): P[k] =
+// exp(scale S[k] - max) / sum for k <= q, 0 beyond (the probabilities are
+// stored in full so that the P V product reads zeros above the diagonal).
+// Row index = problem * T + q. A lane holds columns 256 j + 4 lane .. + 3.
+// ---------------------------------------------------------------------------
+template <int NJ>
+__global__ __launch_bounds__(256) void k_softmax_fwd(const float* __restrict__ S, uint16_t* __restrict__ P,
+                                                      int64_t rows, int T, float scale) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int q = (int)(row % T);
+  const float* s = S + row * T;
+  uint16_t* p = P + row * T;
+  float v[NJ][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c0 = 256 * j + 4 * lane;
+    if (c0 <= q && c0 < T) {
+      const float4 a = *(const float4*)(s + c0);
+      const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = c0 + e <= q ? av[e] * scale : -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[j][e]);
+  }
+  mx = wave_max(mx);                     // finite: column 0 is always valid
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[j][e] = __expf(v[j][e] - mx);    // exactly 0 for the masked -inf
+      sum += v[j][e];
+    }
+  const float inv = 1.0f / wave_sum(sum);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c0 = 256 * j + 4 * lane;
+    if (c0 < T)
+      *(uint2*)(p + c0) = make_uint2(pack_bf16x2(v[j][0] * inv, v[j][1] * inv), pack_bf16x2(v[j][2] * inv, v[j][3] * inv));
+  }
+}
+
+// Softmax backward in place over P: dS = scale P (dP - sum_k P dP) for k <= q
+// (P, and so dS, is 0 beyond the diagonal and stays untouched there).
+template <int NJ>
+__global__ __launch_bounds__(256) void k_softmax_bwd(const float* __restrict__ dP, uint16_t* __restrict__ P,
+                                                      int64_t rows, int T, float scale) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int q = (int)(row % T);
+  const float* d = dP + row * T;
+  uint16_t* p = P + row * T;
+  float pv[NJ][4], dv[NJ][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c0 = 256 * j + 4 * lane;
+    if (c0 <= q && c0 < T) {
+      const uint2 pb = *(const uint2*)(p + c0);
+      const float4 a = *(const float4*)(d + c0);
+      pv[j][0] = __builtin_bit_cast(float, pb.x << 16);
+      pv[j][1] = __builtin_bit_cast(float, pb.x & 0xFFFF0000u);
+      pv[j][2] = __builtin_bit_cast(float, pb.y << 16);
+      pv[j][3] = __builtin_bit_cast(float, pb.y & 0xFFFF0000u);
+      dv[j][0] = a.x;
+      dv[j][1] = a.y;
+      dv[j][2] = a.z;
+      dv[j][3] = a.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[j][e] = dv[j][e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot += pv[j][e] * dv[j][e];
+  }
+  dot = wave_sum(dot);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c0 = 256 * j + 4 * lane;
+    if (c0 <= q && c0 < T) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = scale * pv[j][e] * (dv[j][e] - dot);
+      *(uint2*)(p + c0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SiLU-gated product: a = bf16(silu(gate) up); backward in place:
+// gate <- da up silu'(gate), up <- da silu(gate), with
+// silu'(x) = sg (1 + x (1 - sg)), sg = 1 / (1 + e^-x).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_swiglu_fwd(const uint16_t* __restrict__ gate, const uint16_t* __restrict__ up,
+                                                     uint16_t* __restrict__ a, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  float g[8], u[8], o[8];
+  unpack8(((const uint4*)gate)[i], g);
+  unpack8(((const uint4*)up)[i], u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
+  ((uint4*)a)[i] = pack8(o);
+}
+
+__global__ __launch_bounds__(256) void k_swiglu_bwd(uint16_t* __restrict__ gate, uint16_t* __restrict__ up,
+                                                     const uint16_t* __restrict__ da, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  float g[8], u[8], d[8], dg[8], du[8];
+  unpack8(((const uint4*)gate)[i], g);
+  unpack8(((const uint4*)up)[i], u);
+  unpack8(((const uint4*)da)[i], d);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float sg = 1.0f / (1.0f + __expf(-g[e]));
+    dg[e] = d[e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
+    du[e] = d[e] * (g[e] * sg);
+  }
+  ((uint4*)gate)[i] = pack8(dg);
+  ((uint4*)up)[i] = pack8(du);
+}
+
+// ---------------------------------------------------------------------------
+// Output, loss and its gradient: y = x2 + o_down (fp32), d = y - target,
+// dy = bf16(d * 2 / n); one fp32 partial of sum d^2 per workgroup (2048
+// elements), summed in double by k_loss_final.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_mse(const float* __restrict__ x2, const float* __restrict__ dn,
+                                              const uint16_t* __restrict__ target, float* __restrict__ y,
+                                              uint16_t* __restrict__ dy, float* __restrict__ partial, int64_t n8,
+                                              float two_over_n) {
+  __shared__ float red[4];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float ss = 0.f;
+  if (i < n8) {
+    float t[8], yv[8], d[8];
+    unpack8(((const uint4*)target)[i], t);
+    const float4 a0 = ((const float4*)x2)[2 * i], a1 = ((const float4*)x2)[2 * i + 1];
+    const float4 b0 = ((const float4*)dn)[2 * i], b1 = ((const float4*)dn)[2 * i + 1];
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      yv[e] = av[e] + bv[e];
+      const float df = yv[e] - t[e];
+      d[e] = df * two_over_n;
+      ss += df * df;
+    }
+    if (y) {
+      ((float4*)y)[2 * i] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+      ((float4*)y)[2 * i + 1] = make_float4(yv[4], yv[5], yv[6], yv[7]);
+    }
+    ((uint4*)dy)[i] = pack8(d);
+  }
+  const float tot = block_sum(ss, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(256) void k_loss_final(const float* __restrict__ partial, int nblk, double inv_n,
+                                                     float* __restrict__ loss) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nblk; i += 256) s += (double)partial[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = (float)(red[0] * inv_n);
+}
+
+// ---------------------------------------------------------------------------
+// AdamW over up to 21 tensors in one launch. Segment i covers blocks
+// [start[i], start[i + 1]); a thread updates 4 consecutive parameters of 16
+// per thread (4 float4 steps), all in fp32:
+//   p <- p decay; m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
+//   p <- p - step_size m / (sqrt(v) inv_sqrt_bc2 + eps).
+// ---------------------------------------------------------------------------
+constexpr int kAdamSegs = 3 * QAT_BLOCK_LINEARS;
+constexpr int kAdamPerBlock = 256 * 16;
+
+struct AdamSeg {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  int64_t n4;              // float4 count
+  float step_size;         // lr / (1 - b1^t)
+  float decay;             // 1 - lr wd
+};
+
+struct AdamArgs {
+  AdamSeg seg[kAdamSegs];
+  int start[kAdamSegs + 1];
+  int nseg;
+  float b1, b2, inv_sqrt_bc2, eps;
+};
+
+__global__ __launch_bounds__(256) void k_adamw(const AdamArgs a) {
+  int si = 0;
+  while (si + 1 < a.nseg && (int)blockIdx.x >= a.start[si + 1]) ++si;
+  const AdamSeg sg = a.seg[si];
+  const int64_t base = (int64_t)(blockIdx.x - a.start[si]) * (kAdamPerBlock / 4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t i = base + r * 256 + threadIdx.x;
+    if (i >= sg.n4) break;
+    float4 p = ((float4*)sg.p)[i], m = ((float4*)sg.m)[i], v = ((float4*)sg.v)[i];
+    const float4 g = ((const float4*)sg.g)[i];
+    float* pp = &p.x;
+    float* mm = &m.x;
+    float* vv = &v.x;
+    const float* gg = &g.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = pp[e] * sg.decay;
+      mm[e] = a.b1 * mm[e] + (1.0f - a.b1) * gg[e];
+      vv[e] = a.b2 * vv[e] + (1.0f - a.b2) * gg[e] * gg[e];
+      const float den = sqrtf(vv[e]) * a.inv_sqrt_bc2 + a.eps;
+      pp[e] = pe - sg.step_size * (mm[e] / den);
+    }
+    ((float4*)sg.p)[i] = p;
+    ((float4*)sg.m)[i] = m;
+    ((float4*)sg.v)[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: shapes, workspace layout, launch sequence.
+// ---------------------------------------------------------------------------
+int blocks_of(int64_t n, int per) { return (int)((n + per - 1) / per); }
+
+struct Dims {
+  int64_t H, nh, I, T, B, BT;
+  int bits, group;
+  int64_t out[QAT_BLOCK_LINEARS], in[QAT_BLOCK_LINEARS];
+};
+
+Dims dims_of(const qat_block_shape& s) {
+  Dims d;
+  d.H = s.hidden;
+  d.nh = s.heads;
+  d.I = s.inter;
+  d.T = s.seq;
+  d.B = s.batch;
+  d.BT = s.batch * s.seq;
+  d.bits = s.bits;
+  d.group = s.group;
+  for (int i = 0; i < QAT_BLOCK_LINEARS; ++i) {
+    d.out[i] = (i == QAT_BLOCK_GATE || i == QAT_BLOCK_UP) ? d.I : d.H;
+    d.in[i] = i == QAT_BLOCK_DOWN ? d.I : d.H;
+  }
+  return d;
+}
+
+int32_t check_shape(const qat_block_shape* s) {
+  if (!s) return QAT_ERR_NULL;
+  if (s->bits < 2 || s->bits > 4) return QAT_ERR_BITS;
+  const int64_t H = s->hidden, I = s->inter, T = s->seq, B = s->batch, nh = s->heads;
+  if (H <= 0 || I <= 0 || T <= 0 || B <= 0 || nh <= 0) return QAT_ERR_SHAPE;
+  if (H % 128 != 0 || H > 8192 || H != nh * kHeadDim) return QAT_ERR_SHAPE;
+  if (I % 64 != 0 || I > (int64_t(1) << 20)) return QAT_ERR_SHAPE;
+  if (T % 64 != 0 || T > 4096 || B > (int64_t(1) << 16)) return QAT_ERR_SHAPE;
+  const int64_t BT = B * T;
+  if (BT * I * 2 > 0x7FFFFFF0 || BT * H * 4 > 0x7FFFFFF0 || H * I * 4 > 0x7FFFFFF0) return QAT_ERR_SHAPE;
+  if (!(s->group == 32 || s->group == 64 || s->group == 128) || H % s->group || I % s->group) return QAT_ERR_GROUP;
+  return QAT_OK;
+}
+
+// Workspace regions (each 256-byte aligned).
+struct Ws {
+  float2* rope;          // [T][64]
+  uint16_t *h1, *q, *k, *v, *attn, *h2, *gate, *up, *a, *dy, *wh, *da, *dxg, *dxu, *dx2, *dattn, *dq, *dk, *dv;
+  float *S, *o, *x2, *dn, *r1, *r2, *partial;
+  uint16_t* P;
+  size_t bytes;
+};
+
+int mse_blocks(const Dims& d) { return blocks_of(d.BT * d.H / 8, 256); }
+
+Ws ws_layout(const Dims& d, uint8_t* base) {
+  Ws w;
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    void* p = base ? (void*)(base + off) : nullptr;
+    off += (size_t)((bytes + 255) / 256 * 256);
+    return p;
+  };
+  const int64_t th = d.BT * d.H, ti = d.BT * d.I, sc = d.B * d.nh * d.T * d.T;
+  int64_t wmax = 0;
+  for (int i = 0; i < QAT_BLOCK_LINEARS; ++i) wmax = d.out[i] * d.in[i] > wmax ? d.out[i] * d.in[i] : wmax;
+  w.rope = (float2*)take(d.T * (kHeadDim / 2) * 8);
+  w.h1 = (uint16_t*)take(th * 2);
+  w.q = (uint16_t*)take(th * 2);
+  w.k = (uint16_t*)take(th * 2);
+  w.v = (uint16_t*)take(th * 2);
+  w.S = (float*)take(sc * 4);
+  w.P = (uint16_t*)take(sc * 2);
+  w.attn = (uint16_t*)take(th * 2);
+  w.o = (float*)take(th * 4);
+  w.x2 = (float*)take(th * 4);
+  w.r1 = (float*)take(d.BT * 4);
+  w.r2 = (float*)take(d.BT * 4);
+  w.h2 = (uint16_t*)take(th * 2);
+  w.gate = (uint16_t*)take(ti * 2);
+  w.up = (uint16_t*)take(ti * 2);
+  w.a = (uint16_t*)take(ti * 2);
+  w.dn = (float*)take(th * 4);
+  w.dy = (uint16_t*)take(th * 2);
+  w.partial = (float*)take(mse_blocks(d) * 4);
+  w.wh = (uint16_t*)take(wmax * 2);
+  w.da = (uint16_t*)take(ti * 2);
+  w.dxg = (uint16_t*)take(th * 2);
+  w.dxu = (uint16_t*)take(th * 2);
+  w.dx2 = (uint16_t*)take(th * 2);
+  w.dattn = (uint16_t*)take(th * 2);
+  w.dq = (uint16_t*)take(th * 2);
+  w.dk = (uint16_t*)take(th * 2);
+  w.dv = (uint16_t*)take(th * 2);
+  w.bytes = off;
+  return w;
+}
+
+GemmArgs zero_args() {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  return a;
+}
+
+// Y = X W_hat^T with W_hat staged as bf16 [out][in] in ws.wh; bf16 or fp32 out.
+void fq_forward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* X, uint16_t* Y, float* Yf,
+                const Ws& w, hipStream_t st) {
+  const int64_t out = d.out[li], in = d.in[li];
+  launch_quant_codes(L.W, L.s, L.z, out, in, d.group, d.bits, nullptr, w.wh, st);
+  GemmArgs a = zero_args();
+  a.A = X;
+  a.lda = in;
+  a.B = w.wh;
+  a.ldb = in;
+  a.M = (int)d.BT;
+  a.N = (int)out;
+  a.K = (int)in;
+  a.ldc = out;
+  if (Yf) {
+    a.Cf = Yf;
+    launch_gemm_fwd_f32(a, st);
+  } else {
+    a.C = Y;
+    launch_gemm_fwd(a, kBf16, d.bits, st);
+  }
+}
+
+// Straight-through backward of linear li: dX (if requested) from W_hat^T
+// staged in ws.wh, and dW, ds, dz from the gradient GEMM's epilogue.
+void fq_backward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* dY, const uint16_t* X,
+                 uint16_t* dX, const Ws& w, hipStream_t st) {
+  const int64_t out = d.out[li], in = d.in[li];
+  if (dX) {
+    launch_w_hat_t(L.W, L.s, L.z, out, in, d.group, d.bits, w.wh, st);
+    launch_linear_dx(dY, w.wh, d.BT, out, in, dX, st);
+  }
+  GemmArgs a = linear_grads_args(dY, X, L.s, L.z, d.BT, out, in, d.group, d.bits);
+  a.W = L.W;
+  a.ldw = in;
+  a.dW = L.dW;
+  a.ds = L.ds;
+  a.dz = L.dz;
+  launch_gemm_grads(a, kSteGrads, d.bits, st);
+}
+
+// Per-(sequence, head) views for the attention products: the operand that
+// lives in a token-major [B*T][H] tensor advances by T*H per sequence and 128
+// per head; one that lives in a [B*nh][T][T] score tensor by nh*T*T and T*T.
+enum View { kTok = 0, kScore = 1 };
+void set_batch(GemmArgs& a, const Dims& d, View va, View vb, View vc) {
+  auto sb = [&](View v) { return v == kTok ? d.T * d.H : d.nh * d.T * d.T; };
+  auto sh = [&](View v) { return v == kTok ? (int64_t)kHeadDim : d.T * d.T; };
+  a.batch_h = (int)d.nh;
+  a.batches = (int)(d.B * d.nh);
+  a.sa_b = sb(va);
+  a.sa_h = sh(va);
+  a.sb_b = sb(vb);
+  a.sb_h = sh(vb);
+  a.sc_b = sb(vc);
+  a.sc_h = sh(vc);
+}
+
+void softmax_fwd(const Dims& d, const Ws& w, float scale, hipStream_t st) {
+  const int64_t rows = d.B * d.nh * d.T;
+  const int T = (int)d.T;
+  LaunchTimer t("softmax_fwd", st);
+  const dim3 grid((unsigned)blocks_of(rows, 4)), block(256);
+  if (T <= 256) hipLaunchKernelGGL(k_softmax_fwd<1>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else if (T <= 512) hipLaunchKernelGGL(k_softmax_fwd<2>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else if (T <= 1024) hipLaunchKernelGGL(k_softmax_fwd<4>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else if (T <= 2048) hipLaunchKernelGGL(k_softmax_fwd<8>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else hipLaunchKernelGGL(k_softmax_fwd<16>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+}
+
+void softmax_bwd(const Dims& d, const Ws& w, float scale, hipStream_t st) {
+  const int64_t rows = d.B * d.nh * d.T;
+  const int T = (int)d.T;
+  LaunchTimer t("softmax_bwd", st);
+  const dim3 grid((unsigned)blocks_of(rows, 4)), block(256);
+  if (T <= 256) hipLaunchKernelGGL(k_softmax_bwd<1>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else if (T <= 512) hipLaunchKernelGGL(k_softmax_bwd<2>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else if (T <= 1024) hipLaunchKernelGGL(k_softmax_bwd<4>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else if (T <= 2048) hipLaunchKernelGGL(k_softmax_bwd<8>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+  else hipLaunchKernelGGL(k_softmax_bwd<16>, grid, block, 0, st, w.S, w.P, rows, T, scale);
+}
+
+void rope(const Dims& d, uint16_t* q, uint16_t* k, const Ws& w, float sgn, hipStream_t st) {
+  LaunchTimer t("rope", st);
+  const int64_t n = 2 * d.BT * (d.H / 16);
+  hipLaunchKernelGGL(k_rope, dim3((unsigned)blocks_of(n, 256)), dim3(256), 0, st, q, k, w.rope, d.BT, (int)d.T,
+                     (int)d.H, sgn);
+}
+
+// The forward through the loss; leaves in the workspace everything the
+// backward reads.
+void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, const float* g2, const uint16_t* x,
+                   const uint16_t* target, float* y, float* loss, const Ws& w, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)kHeadDim);
+  {
+    LaunchTimer t("rope_table", st);
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)blocks_of(d.T * (kHeadDim / 2), 256)), dim3(256), 0, st,
+                       w.rope, (int)d.T);
+  }
+  {
+    LaunchTimer t("rmsnorm_fwd", st);
+    hipLaunchKernelGGL(k_rmsnorm_fwd<0>, dim3((unsigned)d.BT), dim3(256), 0, st, x, nullptr, nullptr, g1, w.h1,
+                       w.r1, (int)d.H);
+  }
+  fq_forward(d, L[QAT_BLOCK_Q], QAT_BLOCK_Q, w.h1, w.q, nullptr, w, st);
+  fq_forward(d, L[QAT_BLOCK_K], QAT_BLOCK_K, w.h1, w.k, nullptr, w, st);
+  fq_forward(d, L[QAT_BLOCK_V], QAT_BLOCK_V, w.h1, w.v, nullptr, w, st);
+  rope(d, w.q, w.k, w, 1.0f, st);
+  {
+    // S = q k^T per (sequence, head), fp32
+    GemmArgs a = zero_args();
+    a.A = w.q;
+    a.lda = d.H;
+    a.B = w.k;
+    a.ldb = d.H;
+    a.M = a.N = (int)d.T;
+    a.K = kHeadDim;
+    a.Cf = w.S;
+    a.ldc = d.T;
+    set_batch(a, d, kTok, kTok, kScore);
+    launch_gemm_attn(a, kKK_F32, st);
+  }
+  softmax_fwd(d, w, scale, st);
+  {
+    // attn = P v: B[n = d][k = key] = v[key][d] (MN-contiguous)
+    GemmArgs a = zero_args();
+    a.A = w.P;
+    a.lda = d.T;
+    a.B = w.v;
+    a.ldb = d.H;
+    a.M = (int)d.T;
+    a.N = kHeadDim;
+    a.K = (int)d.T;
+    a.C = w.attn;
+    a.ldc = d.H;
+    set_batch(a, d, kScore, kTok, kTok);
+    launch_gemm_attn(a, kKMN_BF16, st);
+  }
+  fq_forward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.attn, nullptr, w.o, w, st);
+  {
+    LaunchTimer t("rmsnorm_fwd", st);
+    hipLaunchKernelGGL(k_rmsnorm_fwd<1>, dim3((unsigned)d.BT), dim3(256), 0, st, x, w.o, w.x2, g2, w.h2, w.r2,
+                       (int)d.H);
+  }
+  fq_forward(d, L[QAT_BLOCK_GATE], QAT_BLOCK_GATE, w.h2, w.gate, nullptr, w, st);
+  fq_forward(d, L[QAT_BLOCK_UP], QAT_BLOCK_UP, w.h2, w.up, nullptr, w, st);
+  {
+    LaunchTimer t("swiglu_fwd", st);
+    const int64_t n8 = d.BT * d.I / 8;
+    hipLaunchKernelGGL(k_swiglu_fwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.a, n8);
+  }
+  fq_forward(d, L[QAT_BLOCK_DOWN], QAT_BLOCK_DOWN, w.a, nullptr, w.dn, w, st);
+  {
+    LaunchTimer t("mse", st);
+    const int64_t n = d.BT * d.H;
+    const int nb = mse_blocks(d);
+    hipLaunchKernelGGL(k_mse, dim3((unsigned)nb), dim3(256), 0, st, w.x2, w.dn, target, y, w.dy, w.partial, n / 8,
+                       (float)(2.0 / (double)n));
+    hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, st, w.partial, nb, 1.0 / (double)n, loss);
+  }
+}
+
+void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, const Ws& w, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)kHeadDim);
+  fq_backward(d, L[QAT_BLOCK_DOWN], QAT_BLOCK_DOWN, w.dy, w.a, w.da, w, st);
+  {
+    LaunchTimer t("swiglu_bwd", st);
+    const int64_t n8 = d.BT * d.I / 8;
+    hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.da, n8);
+  }
+  // gate and up now hold their output gradients
+  fq_backward(d, L[QAT_BLOCK_GATE], QAT_BLOCK_GATE, w.gate, w.h2, w.dxg, w, st);
+  fq_backward(d, L[QAT_BLOCK_UP], QAT_BLOCK_UP, w.up, w.h2, w.dxu, w, st);
+  {
+    LaunchTimer t("rmsnorm_bwd", st);
+    hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)d.BT), dim3(256), 0, st, w.dxg, w.dxu, w.x2, w.r2, g2, w.dy,
+                       w.dx2, (int)d.H);
+  }
+  fq_backward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.dx2, w.attn, w.dattn, w, st);
+  {
+    // dv = P^T dattn: A[m = key][k = query] = P[query][key], both MN-contiguous
+    GemmArgs a = zero_args();
+    a.A = w.P;
+    a.lda = d.T;
+    a.B = w.dattn;
+    a.ldb = d.H;
+    a.M = (int)d.T;
+    a.N = kHeadDim;
+    a.K = (int)d.T;
+    a.C = w.dv;
+    a.ldc = d.H;
+    set_batch(a, d, kScore, kTok, kTok);
+    launch_gemm_attn(a, kMNMN_BF16, st);
+  }
+  {
+    // dP = dattn v^T, fp32 into the score buffer
+    GemmArgs a = zero_args();
+    a.A = w.dattn;
+    a.lda = d.H;
+    a.B = w.v;
+    a.ldb = d.H;
+    a.M = a.N = (int)d.T;
+    a.K = kHeadDim;
+    a.Cf = w.S;
+    a.ldc = d.T;
+    set_batch(a, d, kTok, kTok, kScore);
+    launch_gemm_attn(a, kKK_F32, st);
+  }
+  softmax_bwd(d, w, scale, st);          // P <- dS (scaled)
+  {
+    // dq = dS k
+    GemmArgs a = zero_args();
+    a.A = w.P;
+    a.lda = d.T;
+    a.B = w.k;
+    a.ldb = d.H;
+    a.M = (int)d.T;
+    a.N = kHeadDim;
+    a.K = (int)d.T;
+    a.C = w.dq;
+    a.ldc = d.H;
+    set_batch(a, d, kScore, kTok, kTok);
+    launch_gemm_attn(a, kKMN_BF16, st);
+  }
+  {
+    // dk = dS^T q
+    GemmArgs a = zero_args();
+    a.A = w.P;
+    a.lda = d.T;
+    a.B = w.q;
+    a.ldb = d.H;
+    a.M = (int)d.T;
+    a.N = kHeadDim;
+    a.K = (int)d.T;
+    a.C = w.dk;
+    a.ldc = d.H;
+    set_batch(a, d, kScore, kTok, kTok);
+    launch_gemm_attn(a, kMNMN_BF16, st);
+  }
+  rope(d, w.dq, w.dk, w, -1.0f, st);
+  // q, k, v: gradients of W, s, z only (the block input's gradient is not needed)
+  fq_backward(d, L[QAT_BLOCK_Q], QAT_BLOCK_Q, w.dq, w.h1, nullptr, w, st);
+  fq_backward(d, L[QAT_BLOCK_K], QAT_BLOCK_K, w.dk, w.h1, nullptr, w, st);
+  fq_backward(d, L[QAT_BLOCK_V], QAT_BLOCK_V, w.dv, w.h1, nullptr, w, st);
+}
+
+void adamw(const Dims& d, const qat_block_linear* L, const qat_block_adamw& o, hipStream_t st) {
+  const double pi = 3.14159265358979323846;
+  const double cosf_ = (1.0 + cos(pi * (double)o.step / (double)o.total_steps)) / 2.0;
+  const double lr_w = o.lr_weight * cosf_, lr_q = o.lr_quant * cosf_;
+  const double t = (double)(o.step + 1);
+  const double bc1 = 1.0 - pow(o.beta1, t), bc2 = 1.0 - pow(o.beta2, t);
+  AdamArgs a;
+  memset(&a, 0, sizeof a);
+  a.b1 = (float)o.beta1;
+  a.b2 = (float)o.beta2;
+  a.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+  a.eps = (float)o.eps;
+  int nseg = 0, blk = 0;
+  for (int i = 0; i < QAT_BLOCK_LINEARS; ++i) {
+    const int64_t nw = d.out[i] * d.in[i], ng = d.out[i] * (d.in[i] / d.group);
+    struct {
+      float *p, *g, *m, *v;
+      int64_t n;
+      double lr;
+    } t3[3] = {{L[i].W, L[i].dW, L[i].m_W, L[i].v_W, nw, lr_w},
+               {L[i].s, L[i].ds, L[i].m_s, L[i].v_s, ng, lr_q},
+               {L[i].z, L[i].dz, L[i].m_z, L[i].v_z, ng, lr_q}};
+    for (auto& e : t3) {
+      AdamSeg& s = a.seg[nseg];
+      s.p = e.p;
+      s.g = e.g;
+      s.m = e.m;
+      s.v = e.v;
+      s.n4 = e.n / 4;
+      s.step_size = (float)(e.lr / bc1);
+      s.decay = (float)(1.0 - e.lr * o.weight_decay);
+      a.start[nseg] = blk;
+      blk += blocks_of(e.n, kAdamPerBlock);
+      ++nseg;
+    }
+  }
+  a.start[nseg] = blk;
+  a.nseg = nseg;
+  LaunchTimer tm("adamw", st);
+  hipLaunchKernelGGL(k_adamw, dim3((unsigned)blk), dim3(256), 0, st, a);
+}
+
+// ---- validation ----
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+bool spans_overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || !a.n || !b.n) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Every pointer present and aligned; no written region overlaps any other region.
+int32_t check_args(const Dims& d, const qat_block_linear* L, const float* g1, const float* g2, const uint16_t* x,
+                   const uint16_t* target, float* y, float* loss, void* ws, bool step) {
+  if (!L || !g1 || !g2 || !x || !target || !loss || !ws) return QAT_ERR_NULL;
+  const size_t th = (size_t)(d.BT * d.H);
+  Span rd[4 + 3 * QAT_BLOCK_LINEARS];
+  Span wr[3 + 12 * QAT_BLOCK_LINEARS];   // W, s, z, 3 gradients, 6 moments per linear
+  int nr = 0, nw = 0;
+  rd[nr++] = {g1, (size_t)d.H * 4};
+  rd[nr++] = {g2, (size_t)d.H * 4};
+  rd[nr++] = {x, th * 2};
+  rd[nr++] = {target, th * 2};
+  wr[nw++] = {y, y ? th * 4 : 0};
+  wr[nw++] = {loss, 4};
+  wr[nw++] = {ws, ws_layout(d, nullptr).bytes};
+  for (int i = 0; i < QAT_BLOCK_LINEARS; ++i) {
+    const qat_block_linear& l = L[i];
+    const size_t nwt = (size_t)(d.out[i] * d.in[i]) * 4, ng = (size_t)(d.out[i] * (d.in[i] / d.group)) * 4;
+    if (!l.W || !l.s || !l.z) return QAT_ERR_NULL;
+    if (step && (!l.dW || !l.ds || !l.dz || !l.m_W || !l.v_W || !l.m_s || !l.v_s || !l.m_z || !l.v_z))
+      return QAT_ERR_NULL;
+    const void* all[] = {l.W, l.s, l.z, l.dW, l.ds, l.dz, l.m_W, l.v_W, l.m_s, l.v_s, l.m_z, l.v_z};
+    for (const void* p : all)
+      if (p && !al16(p)) return QAT_ERR_ALIGN;
+    Span* dst = step ? wr : rd;
+    int& nd = step ? nw : nr;
+    dst[nd++] = {l.W, nwt};
+    dst[nd++] = {l.s, ng};
+    dst[nd++] = {l.z, ng};
+    if (step) {
+      const Span more[] = {{l.dW, nwt}, {l.ds, ng}, {l.dz, ng}, {l.m_W, nwt}, {l.v_W, nwt},
+                           {l.m_s, ng}, {l.v_s, ng}, {l.m_z, ng}, {l.v_z, ng}};
+      for (const Span& s : more) wr[nw++] = s;
+    }
+  }
+  const void* top[] = {g1, g2, x, target, y, loss, ws};
+  for (const void* p : top)
+    if (p && !al16(p)) return QAT_ERR_ALIGN;
+  for (int i = 0; i < nw; ++i) {
+    for (int j = i + 1; j < nw; ++j)
+      if (spans_overlap(wr[i], wr[j])) return QAT_ERR_ALIAS;
+    for (int j = 0; j < nr; ++j)
+      if (spans_overlap(wr[i], rd[j])) return QAT_ERR_ALIAS;
+  }
+  return QAT_OK;
+}
+
+}  // namespace
+}  // namespace qat
+
+#define QAT_API extern "C" __attribute__((visibility("default")))
+
+QAT_API size_t qat_block_ws_bytes(const qat_block_shape* shape) {
+  if (qat::check_shape(shape) != QAT_OK) return 0;
+  return qat::ws_layout(qat::dims_of(*shape), nullptr).bytes;
+}
+
+QAT_API int32_t qat_block_forward(const qat_block_shape* shape, const qat_block_linear* lin, const float* g1,
+                                  const float* g2, const uint16_t* x, const uint16_t* target, float* y, float* loss,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  using namespace qat;
+  const int32_t sc = check_shape(shape);
+  if (sc != QAT_OK) return sc;
+  const Dims d = dims_of(*shape);
+  const int32_t ac = check_args(d, lin, g1, g2, x, target, y, loss, ws, false);
+  if (ac != QAT_OK) return ac;
+  if (ws_bytes < ws_layout(d, nullptr).bytes) return QAT_ERR_WORKSPACE;
+  const Ws w = ws_layout(d, (uint8_t*)ws);
+  block_forward(d, lin, g1, g2, x, target, y, loss, w, stream);
+  return finish_call();
+}
+
+QAT_API int32_t qat_block_ap_step(const qat_block_shape* shape, const qat_block_linear* lin, const float* g1,
+                                  const float* g2, const uint16_t* x, const uint16_t* target,
+                                  const qat_block_adamw* opt, float* y, float* loss, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  using namespace qat;
+  const int32_t sc = check_shape(shape);
+  if (sc != QAT_OK) return sc;
+  if (!opt) return QAT_ERR_NULL;
+  if (opt->total_steps <= 0 || opt->step < 0 || !(opt->beta1 >= 0 && opt->beta1 < 1) ||
+      !(opt->beta2 >= 0 && opt->beta2 < 1) || !(opt->eps > 0))
+    return QAT_ERR_SHAPE;
+  const Dims d = dims_of(*shape);
+  const int32_t ac = check_args(d, lin, g1, g2, x, target, y, loss, ws, true);
+  if (ac != QAT_OK) return ac;
+  if (ws_bytes < ws_layout(d, nullptr).bytes) return QAT_ERR_WORKSPACE;
+  const Ws w = ws_layout(d, (uint8_t*)ws);
+  block_forward(d, lin, g1, g2, x, target, y, loss, w, stream);
+  block_backward(d, lin, g2, w, stream);
+  adamw(d, lin, *opt, stream);
+  return finish_call();
+}

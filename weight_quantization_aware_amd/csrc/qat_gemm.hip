@@ -21,23 +21,28 @@ int64_t tiles(const GemmArgs& a, int bm, int bn) {
   return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
-// With the bf16-store epilogue the NB template argument only tags the launch:
-// 0 the forward, 1 the dX GEMM (same code, distinct kernel symbols so that
-// profiles can tell them apart).
+// With the store epilogues the NB template argument only tags the launch: 0
+// the forward, 1 the dX GEMM, 5 the products of attention (same code,
+// distinct kernel symbols so that profiles can tell them apart).
+constexpr int kTagAttn = 5;
 template <int BL, int EP, int NB>
 constexpr const char* gemm_label() {
   if (EP == kSteGrads) return "gemm_ste_grads";
   if (EP == kE2eScaleGrad) return "gemm_e2e_grads";
   if (BL == kFp32Quant) return "gemm_fwd_fused_fp32";
   if (BL == kPacked) return "gemm_fwd_packed";
+  if (NB == kTagAttn) return EP == kStoreF32 ? "attn_gemm_f32" : "attn_gemm_bf16";
+  if (EP == kStoreF32) return "gemm_fwd_f32";
   return NB == 1 ? "gemm_dx" : "gemm_fwd";
 }
+
+int batches(const GemmArgs& a) { return a.batch_h > 0 ? a.batches : 1; }
 
 template <int BM, int BN, int S, int WGM, int WGN, int AMN, int BMN, int EP, int NB, int GM = 0>
 void launch_bf16(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<kBf16, EP, NB>(), st);
-  hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, GM, AMN, BMN, EP, NB>), dim3((unsigned)tiles(a, BM, BN)),
-                     dim3(64 * WGM * WGN), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, GM, AMN, BMN, EP, NB>),
+                     dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
 template <int BM, int BN, int BK, int S, int BL, int NB>
@@ -88,6 +93,17 @@ void launch_grads(const GemmArgs& a, hipStream_t st) {
   }
 }
 
+// Batched attention products: 256x256 tiles for the T x T score-shaped
+// outputs when they fill the chip, 128x128 tiles otherwise (the head-sized
+// outputs, N = head_dim).
+template <int AMN, int BMN, int EP>
+void launch_pick_attn(const GemmArgs& a, hipStream_t st) {
+  if (a.N >= 256 && tiles(a, 256, 256) * batches(a) >= 256)
+    launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, kTagAttn>(a, st);
+  else
+    launch_bf16<128, 128, 4, 2, 2, AMN, BMN, EP, kTagAttn>(a, st);
+}
+
 template <int BL, int NB>
 void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
   if constexpr (BL == kPacked) {
@@ -107,6 +123,16 @@ void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st) {
   else if (bits == 2) launch_pick_fused<kPacked, 2>(a, st);
   else if (bits == 3) launch_pick_fused<kPacked, 3>(a, st);
   else launch_pick_fused<kPacked, 4>(a, st);
+}
+
+void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st) {
+  launch_pick<kKContig, kKContig, kStoreF32, 0>(a, st);
+}
+
+void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st) {
+  if (kind == kKK_F32) launch_pick_attn<kKContig, kKContig, kStoreF32>(a, st);
+  else if (kind == kKMN_BF16) launch_pick_attn<kKContig, kMNContig, kStoreBf16>(a, st);
+  else launch_pick_attn<kMNContig, kMNContig, kStoreBf16>(a, st);
 }
 
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {

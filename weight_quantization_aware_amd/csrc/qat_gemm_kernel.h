@@ -41,6 +41,20 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
   tn = in_g / gm;
 }
 
+// The problem of a batched launch (grid y index; see GemmArgs::batch_h).
+__device__ __forceinline__ GemmArgs batch_view(const GemmArgs& a0) {
+  GemmArgs a = a0;
+  if (a.batch_h > 0) {
+    const int z = blockIdx.y, b = z / a.batch_h, h = z - b * a.batch_h;
+    a.A += b * a.sa_b + h * a.sa_h;
+    a.B = (const uint16_t*)a.B + b * a.sb_b + h * a.sb_h;
+    const int64_t oc = b * a.sc_b + h * a.sc_h;
+    if (a.C) a.C += oc;
+    if (a.Cf) a.Cf += oc;
+  }
+  return a;
+}
+
 // LDS bank slots (16-byte chunks) served per cycle; the swizzle period. Eight
 // measures free of bank conflicts for these fragment reads on gfx950.
 constexpr int kLdsSlots = 8;
@@ -74,9 +88,11 @@ struct DmaTileK {
   i32x4 rs;
   uint32_t voff[NI];
   uint32_t lrow[NI];                                     // wave-uniform LDS byte offsets
-  // src is [rows][ld] with K contiguous; rows >= nrows read as zero.
-  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int /*kdim*/) {
-    rs = buffer_rsrc(src + (int64_t)row0 * ld, (int64_t)(nrows - row0) * ld * 2);
+  // src is [rows][ld] with K contiguous; rows >= nrows read as zero. The
+  // range ends with the last row's kdim-th element, so a view into a wider
+  // tensor (one head's columns) reads nothing past that tensor.
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int kdim) {
+    rs = buffer_rsrc(src + (int64_t)row0 * ld, ((int64_t)(nrows - 1 - row0) * ld + kdim) * 2);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
@@ -135,8 +151,11 @@ struct DmaTileMN {
   uint32_t kstride;                                      // bytes per k-row in global memory
   __device__ static __forceinline__ int swz(int k) { return ((k & 3) << 1) ^ (((k >> 3) & 1) << 3); }
   __device__ static __forceinline__ int off(int k, int chunk) { return k * PITCH + ((chunk ^ swz(k)) << 4); }
-  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int /*nrows*/, int kdim) {
-    rs = buffer_rsrc(src + row0, ((int64_t)kdim * ld - row0) * 2);
+  // The range ends with the last k-row's row nrows (rounded up to a whole
+  // 16-byte chunk), so a view into a wider tensor reads nothing past it.
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int kdim) {
+    const int64_t end = min((int64_t)kdim * ld, (int64_t)(kdim - 1) * ld + ((nrows + 7) & ~7));
+    rs = buffer_rsrc(src + row0, (end - row0) * 2);
     kstride = (uint32_t)(ld * 2);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -328,6 +347,7 @@ __device__ __forceinline__ void mfma_drain() {
 // Epilogues. acc[j][i] holds C[m0 + wm0 + 16 i + (lane & 15)][n0 + wn0 + 16 j
 // + 4 (lane >> 4) + r], r = 0..3.
 //   kStoreBf16:    C (bf16) = acc.
+//   kStoreF32:     Cf (fp32) = acc.
 //   kSteGrads:     rows are weight rows o (A = dY^T), columns inputs c (B =
 //                  X^T); Gw = acc. dW = Gw * m and the group sums of ds, dz of
 //                  the straight-through estimator, from W, s, z re-quantised
@@ -358,7 +378,19 @@ template <int EP, int NB, int GM, int BM, int BN, int TI, int TJ, int WN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
                                               int wm0, int wn0, int lane, float* red) {
   const int rl = lane & 15, cq = 4 * (lane >> 4);
-  if constexpr (EP == kStoreBf16) {
+  if constexpr (EP == kStoreF32) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = m0 + wm0 + i * 16 + rl;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn0 + j * 16 + cq;
+        if (col < a.N)
+          *(float4*)(a.Cf + (int64_t)row * a.ldc + col) = make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+      }
+    }
+  } else if constexpr (EP == kStoreBf16) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int row = m0 + wm0 + i * 16 + rl;
@@ -526,7 +558,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
 // DMA issue is spread over the k-step.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int GM, int AMN, int BMN, int EP, int NB>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a) {
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
+  const GemmArgs a = batch_view(a0);
   constexpr int NW = WGM * WGN;
   using LA = typename DmaTileOf<BM, BK, AMN, NW>::T;
   using LB = typename DmaTileOf<BN, BK, BMN, NW>::T;

@@ -19,6 +19,10 @@ class LaunchTimer {
   void* stop_ = nullptr;
 };
 
+// Status of the launches a C-ABI call has just enqueued: QAT_OK, or QAT_ERR_HIP
+// with the HIP error text kept for qat_last_error (qat_api.hip).
+int32_t finish_call();
+
 // ---- HBM-bound kernels (qat_elementwise.hip) ----
 // `group` is 32, 64, 128 or in (channel-wise); in % group == 0.
 void launch_init_minmax(const float* W, int64_t out, int64_t in, int group, int bits, float* s, float* z,
@@ -72,10 +76,18 @@ struct GemmArgs {
   float* dW;           // [M][ldw] fp32, may be null
   float* ds;           // [M][G], may be null
   float* dz;           // [M][G], may be null
+  float* Cf;           // fp32 output [M][ldc] (kStoreF32)
+  // Batched products (plain bf16 loads and the store epilogues only): with
+  // batch_h > 0 the grid's y index z = b * batch_h + h selects the problem
+  // whose A, B and C start at b * s?_b + h * s?_h elements from the given
+  // pointers (the per-(sequence, head) products of attention).
+  int batch_h;
+  int batches;
+  int64_t sa_b, sa_h, sb_b, sb_h, sc_b, sc_h;
 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
-enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2 };
+enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3 };
 enum Layout { kKContig = 0, kMNContig = 1 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
@@ -85,5 +97,21 @@ void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 // Gradient GEMM over tokens, Gw = dY^T X with both operands MN-contiguous;
 // epi = kSteGrads (dW, ds, dz) or kE2eScaleGrad (ds, dz).
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st);
+// Forward-type GEMM on a staged bf16 W_hat with fp32 output (a.Cf).
+void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st);
+// The linear's backward GEMMs (argument set-up shared by the C-ABI calls and
+// the block step): dX = dY W_hat from W_hat^T [in][out] bf16, and the
+// gradient GEMM's arguments Gw = dY^T X over M tokens (epilogue fields W, Wq,
+// dW, ds, dz left to the caller).
+void launch_linear_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, int64_t out, int64_t in,
+                      uint16_t* dX, hipStream_t st);
+GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z, int64_t M,
+                           int64_t out, int64_t in, int group, int bits);
+// Batched products of attention (a.batches problems, a.batch_h per sequence):
+//   kKK_F32:   C fp32 = A B^T, both K-contiguous (scores, their gradient);
+//   kKMN_BF16: C bf16, A K-contiguous, B MN-contiguous (P V, dS K);
+//   kMNMN_BF16: C bf16, both MN-contiguous (P^T dO, dS^T Q).
+enum AttnGemm { kKK_F32 = 0, kKMN_BF16 = 1, kMNMN_BF16 = 2 };
+void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st);
 
 }  // namespace qat

@@ -212,3 +212,46 @@ DEPLOY_SHAPES = {
     "70b": [("q_proj", 8192, 8192), ("k_proj", 1024, 8192), ("v_proj", 1024, 8192), ("o_proj", 8192, 8192),
             ("gate_proj", 28672, 8192), ("up_proj", 28672, 8192), ("down_proj", 8192, 28672)],
 }
+
+
+# --------------------------------------------------------------------------
+# One Llama-2 decoder block for the Block-AP step
+# --------------------------------------------------------------------------
+
+BLOCK_LINEARS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+TID_TARGET, TID_NORM1, TID_NORM2 = 7, 8, 9
+
+# (hidden, heads, inter, seq, batch): Llama-2-7B's block on the pages' Block-AP
+# samples (2048 tokens, batch 2); head size 128 as in every Llama-2 model.
+BLOCK_7B = (4096, 32, 11008, 2048, 2)
+
+
+def block_linear_shapes(hidden: int, inter: int):
+    """(name, out, in) of the seven linears, in the order q, k, v, o, gate, up, down."""
+    H, I = hidden, inter
+    return [("q_proj", H, H), ("k_proj", H, H), ("v_proj", H, H), ("o_proj", H, H),
+            ("gate_proj", I, H), ("up_proj", I, H), ("down_proj", H, I)]
+
+
+def block_inputs(cfg: int, hidden: int, inter: int, tokens: int, outlier_channels: int = 8,
+                 sigma: float = 0.02, target_std: float = 0.1):
+    """Seeded inputs of one block step.
+
+    W: per linear fp32 ~ N(0, sigma) with 0.1% x10 outliers (layer index =
+    position in BLOCK_LINEARS); x: bf16 bits [tokens, hidden] ~ N(0, 1) with
+    `outlier_channels` columns x20; target: bf16 bits of x + N(0, target_std)
+    (a stand-in for the full-precision block's output, which sits close to its
+    input through the residual); g1, g2: fp32 norm weights ~ 1 + N(0, 0.1).
+    """
+    W = {n: weight(cfg, li, o, i, sigma, True) for li, (n, o, i) in enumerate(block_linear_shapes(hidden, inter))}
+    x32 = rng(cfg, 0, TID_X).standard_normal((tokens, hidden), dtype=np.float32)
+    if outlier_channels:
+        cols = rng(cfg, 0, TID_OUTL + 100).choice(hidden, size=outlier_channels, replace=False)
+        x32[:, cols] *= np.float32(20.0)
+    x = to_bf16_bits(x32)
+    xv = (x.astype(np.uint32) << 16).view(np.float32)
+    noise = rng(cfg, 0, TID_TARGET).standard_normal((tokens, hidden), dtype=np.float32)
+    target = to_bf16_bits(xv + np.float32(target_std) * noise)
+    g1 = (1.0 + 0.1 * rng(cfg, 0, TID_NORM1).standard_normal(hidden)).astype(np.float32)
+    g2 = (1.0 + 0.1 * rng(cfg, 0, TID_NORM2).standard_normal(hidden)).astype(np.float32)
+    return {"W": W, "x": x, "target": target, "g1": g1, "g2": g2}
