@@ -54,6 +54,8 @@ def parse():
                     help="after the timed region run one 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--deploy-only", action="store_true",
                     help="only the inference linear on the deployment format (Llama-2-70B block, M = 1 and 16)")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only one Block-AP step on a Llama-2-7B block (2 x 2048 tokens, w2g64)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the context measurements (practical peaks, cold HBM, the C3 block)")
     return ap.parse_args()
@@ -100,6 +102,10 @@ def main():
     if args.deploy_only:
         print(json.dumps({"inference_linear_70b_block":
                           deploy_measurements(Q, torch, dev, torch.cuda.current_stream(dev))}), flush=True)
+        return
+    if args.block_only:
+        print(json.dumps({"block_ap_step_7b": block_step_measurements(Q, torch, dev, torch.cuda.current_stream(dev))}),
+              flush=True)
         return
     lin = synth.config(2)[0]
     M, out, inp, bits = lin.m, lin.out, lin.inp, lin.bits
@@ -252,6 +258,7 @@ def main():
     if not args.no_extras:
         extras = context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp, X, dY)
         extras["inference_linear_70b_block"] = deploy_measurements(Q, torch, dev, stream)
+        extras["block_ap_step_7b"] = block_step_measurements(Q, torch, dev, stream)
         roofline["frac_of_measured_peak"] = round(
             achieved / (extras["measured_peaks"]["mfma_bf16_tflops"] if kind == "mfma"
                         else extras["measured_peaks"]["hbm_read_gbs"]), 4)
@@ -493,6 +500,92 @@ def deploy_measurements(Q, torch, dev, stream):
         for bits in (2, 4):
             res["block"][f"speedup_w{bits}_M{M}_vs_fp16"] = round(tot[f"fp16_M{M}"] / tot[f"w{bits}_M{M}"], 2)
     return res
+
+
+def block_step_flops(H, nh, I, T, Bn):
+    """GEMM FLOPs of one Block-AP step as the kernels compute them: the seven
+    linears' forward and weight-gradient products, the dX products of o, gate,
+    up and down (the block input's gradient is not needed), and the six
+    attention products per (sequence, head) over full T x T score tiles."""
+    from weight_quantization_aware_amd import synth
+    shapes = synth.block_linear_shapes(H, I)
+    BT = Bn * T
+    lin = 2.0 * BT * sum(o * i for _, o, i in shapes)
+    dx = 2.0 * BT * sum(o * i for n, o, i in shapes if n not in ("q_proj", "k_proj", "v_proj"))
+    attn = 6 * 2.0 * Bn * nh * T * T * (H // nh)
+    return {"linears": 2 * lin + dx, "attention": attn}
+
+
+def block_step_measurements(Q, torch, dev, stream, steps=10):
+    """One Block-AP step (include/qat_block.h) on a Llama-2-7B block: 2
+    sequences of 2048 tokens, w2g64, seeded synthetic inputs (synth.block_inputs),
+    s and z from the library's min-max init. Whole steps between events
+    (parameters and moments advance from step to step, as in training), then
+    one step with the library's per-launch events for the kernel table."""
+    from weight_quantization_aware_amd import synth
+    H, nh, I, T, Bn = synth.BLOCK_7B
+    bits, group = 2, 64
+    d = synth.block_inputs(6, H, I, Bn * T)
+    shape = Q.block_shape(H, nh, I, T, Bn, bits, group)
+    lins = []
+    for n, o, i in synth.block_linear_shapes(H, I):
+        W = torch.from_numpy(d["W"][n]).to(dev)
+        sz = torch.empty(o, i // group, device=dev)
+        zz = torch.empty_like(sz)
+        Q.qat_init_minmax(W, bits, sz, zz, group=group)
+        e = {"W": W, "s": sz, "z": zz}
+        for k in ("W", "s", "z"):
+            e["d" + k] = torch.empty_like(e[k])
+            e["m_" + k] = torch.zeros_like(e[k])
+            e["v_" + k] = torch.zeros_like(e[k])
+        lins.append(e)
+    del d["W"]
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    tgt = torch.from_numpy(d["target"].view(np.int16)).view(torch.bfloat16).to(dev)
+    g1, g2 = torch.from_numpy(d["g1"]).to(dev), torch.from_numpy(d["g2"]).to(dev)
+    ws = Q.workspace(Q.block_ws_bytes(shape), dev)
+    loss = torch.empty(1, device=dev)
+    opt = {"lr_weight": 2e-5, "lr_quant": 1e-4, "beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "weight_decay": 0.0,
+           "step": 0, "total_steps": 4096}
+    k = [0]
+
+    def step():
+        opt["step"] = k[0]
+        Q.qat_block_ap_step(shape, lins, g1, g2, x, tgt, opt, loss, ws=ws)
+        k[0] += 1
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize(dev)
+    loss0 = float(loss.item())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    Q.timing_enable(True)
+    step()
+    torch.cuda.synchronize(dev)
+    rep = Q.timing_report()
+    Q.timing_enable(False)
+    fl = block_step_flops(H, nh, I, T, Bn)
+    ktab = {lab: {"ms": round(t, 4), "launches": n} for lab, (t, n) in sorted(rep.items(), key=lambda kv: -kv[1][0])}
+    ksum = sum(t for t, _ in rep.values())
+    for lab in ktab:
+        ktab[lab]["share"] = round(ktab[lab]["ms"] / ksum, 4)
+    nparam = sum(o * i + 2 * o * (i // group) for _, o, i in synth.block_linear_shapes(H, I))
+    if "adamw" in ktab:
+        ktab["adamw"]["gbs"] = round(28.0 * nparam / (ktab["adamw"]["ms"] * 1e-3) / 1e9, 1)
+    return {"what": "Llama-2-7B block (hidden 4096, 32 heads, inter 11008), 2 x 2048 tokens, w2g64: forward, "
+                    "MSE, straight-through backward, AdamW (two groups, cosine)",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(Bn * T / (ms * 1e-3)),
+            "gemm_tflop": round((fl["linears"] + fl["attention"]) / 1e12, 4),
+            "gemm_tflops": round((fl["linears"] + fl["attention"]) / (ms * 1e-3) / 1e12, 1),
+            "linear_gemm_tflop": round(fl["linears"] / 1e12, 4),
+            "loss_after_two_steps": round(loss0, 6), "kernels_one_step": ktab,
+            "kernel_sum_ms": round(ksum, 4), "params": nparam}
 
 
 def cpu_baseline(lin, W_np, X_np, dY_np, rows):

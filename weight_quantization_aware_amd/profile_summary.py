@@ -37,6 +37,9 @@ LABELS = [
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*1,\s*0>", "gemm_ste_grads"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*2,\s*\d>", "gemm_e2e_grads"),
     (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
+    (r"k_gemm<[^>]*,\s*0,\s*0,\s*3,\s*0>", "gemm_fwd_f32"),
+    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*3,\s*5>", "attn_gemm_f32"),
+    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*0,\s*5>", "attn_gemm_bf16"),
     # k_gemm_fused<BM, BN, BK, STAGES, U2, BL, NB>
     (r"k_gemm_fused<[^>]*,\s*1,\s*0>", "gemm_fwd_fused_fp32"),
     (r"k_gemm_fused<[^>]*,\s*2,\s*\d>", "gemm_fwd_packed"),
@@ -54,6 +57,18 @@ LABELS = [
     (r"k_deploy_gemv<3>", "deploy_gemv_xreg_w3"),
     (r"k_deploy_gemv<4>", "deploy_gemv_xreg_w4"),
     (r"k_deploy_qparams", "deploy_qparams"),
+    # the Block-AP step's row kernels and optimiser
+    (r"k_rmsnorm_fwd", "rmsnorm_fwd"),
+    (r"k_rmsnorm_bwd", "rmsnorm_bwd"),
+    (r"k_rope_table", "rope_table"),
+    (r"k_rope\(", "rope"),
+    (r"k_softmax_fwd", "softmax_fwd"),
+    (r"k_softmax_bwd", "softmax_bwd"),
+    (r"k_swiglu_fwd", "swiglu_fwd"),
+    (r"k_swiglu_bwd", "swiglu_bwd"),
+    (r"k_mse|k_loss_final", "mse"),
+    (r"k_adamw", "adamw"),
+    (r"k_fill_zero", "fill_zero"),
 ]
 
 
