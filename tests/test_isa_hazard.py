@@ -1,0 +1,87 @@
+"""CPU check of the GEMM kernels' generated gfx950 code.
+
+The MFMA GEMM (`k_gemm`) issues v_mfma_f32_16x16x32_bf16 from inline asm with
+its accumulators pinned to AGPRs, so the compiler's hazard recogniser does not
+see the MFMA's write-back latency. The kernel waits it out itself (three
+`s_nop 15`, 48 wait states) before anything reads an accumulator. A compiler
+transformation that copies or reads accumulators in between (e.g. a peeled
+loop iteration whose accumulators live in other AGPRs) gives wrong results
+without any fault, so every instantiation is checked: after each MFMA, no
+v_accvgpr_read / v_accvgpr_mov may come before the drain.
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "weight_quantization_aware_amd")
+
+
+def _hipcc():
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def _device_asm(src: str) -> str:
+    from weight_quantization_aware_amd import build
+    out = os.path.join(tempfile.mkdtemp(), "k.s")
+    cmd = [_hipcc(), *build.FLAGS, "--cuda-device-only", "-S", os.path.join(PKG, "csrc", src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return open(out).read()
+
+
+def accumulator_hazards(asm: str):
+    """{kernel: count} of accumulator reads or moves between an MFMA and the drain."""
+    found = {}
+    for m in re.finditer(r"^(_Z[^:\s]+):", asm, re.M):
+        name = m.group(1)
+        end = asm.index(".Lfunc_end", m.end())
+        pending, nops, cnt = False, 0, 0
+        for line in asm[m.end():end].split("\n"):
+            t = line.strip()
+            if t.startswith("v_mfma"):
+                pending, nops = True, 0
+            elif pending and t.startswith("s_nop 15"):
+                nops += 1
+                pending = nops < 3
+            elif pending and (t.startswith("v_accvgpr_read") or t.startswith("v_accvgpr_mov")):
+                cnt += 1
+        if cnt:
+            found[name] = cnt
+    return found
+
+
+def test_scanner_flags_a_copy_before_the_drain():
+    asm = """_Zk:
+\tv_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]
+\tv_accvgpr_mov_b32 a4, a0
+\ts_nop 15
+\ts_nop 15
+\ts_nop 15
+\tv_accvgpr_read_b32 v8, a0
+.Lfunc_end0:
+_Zok:
+\tv_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]
+\ts_nop 15
+\ts_nop 15
+\ts_nop 15
+\tv_accvgpr_read_b32 v8, a0
+.Lfunc_end1:
+"""
+    assert accumulator_hazards(asm) == {"_Zk": 1}
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_asm_mfma_gemms_wait_before_reading_accumulators():
+    asm = _device_asm("qat_gemm.hip")
+    kernels = re.findall(r"^(_ZN3qat6k_gemmI[^:\s]+):", asm, re.M)
+    assert len(kernels) >= 20
+    bad = {k: n for k, n in accumulator_hazards(asm).items() if k.startswith("_ZN3qat6k_gemmI")}
+    assert not bad, bad

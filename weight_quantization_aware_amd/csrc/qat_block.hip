@@ -209,8 +209,9 @@ __global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ q, uint16_t
 
 // ---------------------------------------------------------------------------
 // Causal softmax over the scores of one query row (one wave per row): P[k] =
-// exp(scale S[k] - max) / sum for k <= q, 0 beyond (the probabilities are
-// stored in full so that the P V product reads zeros above the diagonal).
+// exp(scale S[k] - max) / sum for k <= q, 0 for q < k < the end of q's
+// 256-column block (the causal products read the row tile's diagonal block,
+// nothing beyond it).
 // Row index = problem * T + q. A lane holds columns 256 j + 4 lane .. + 3.
 // ---------------------------------------------------------------------------
 template <int NJ>
@@ -249,10 +250,14 @@ __global__ __launch_bounds__(256) void k_softmax_fwd(const float* __restrict__ S
       sum += v[j][e];
     }
   const float inv = 1.0f / wave_sum(sum);
+  // zeros beyond the diagonal only as far as the causal products read them:
+  // up to the end of the 256-column block that holds q (row tiles are 128 or
+  // 256 tokens)
+  const int wend = min(T, (q / 256 + 1) * 256);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c0 = 256 * j + 4 * lane;
-    if (c0 < T)
+    if (c0 < wend)
       *(uint2*)(p + c0) = make_uint2(pack_bf16x2(v[j][0] * inv, v[j][1] * inv), pack_bf16x2(v[j][2] * inv, v[j][3] * inv));
   }
 }
@@ -420,17 +425,28 @@ __global__ __launch_bounds__(256) void k_adamw(const AdamArgs a) {
   int si = 0;
   while (si + 1 < a.nseg && (int)blockIdx.x >= a.start[si + 1]) ++si;
   const AdamSeg sg = a.seg[si];
-  const int64_t base = (int64_t)(blockIdx.x - a.start[si]) * (kAdamPerBlock / 4);
+  const int64_t base = (int64_t)(blockIdx.x - a.start[si]) * (kAdamPerBlock / 4) + threadIdx.x;
+  // every load of the thread's 16 parameters is issued before any arithmetic
+  float4 p[4], m[4], v[4], g[4];
+  bool ok[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t i = base + r * 256 + threadIdx.x;
-    if (i >= sg.n4) break;
-    float4 p = ((float4*)sg.p)[i], m = ((float4*)sg.m)[i], v = ((float4*)sg.v)[i];
-    const float4 g = ((const float4*)sg.g)[i];
-    float* pp = &p.x;
-    float* mm = &m.x;
-    float* vv = &v.x;
-    const float* gg = &g.x;
+    const int64_t i = base + r * 256;
+    ok[r] = i < sg.n4;
+    if (ok[r]) {
+      p[r] = ((const float4*)sg.p)[i];
+      m[r] = ((const float4*)sg.m)[i];
+      v[r] = ((const float4*)sg.v)[i];
+      g[r] = ((const float4*)sg.g)[i];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (!ok[r]) continue;
+    float* pp = &p[r].x;
+    float* mm = &m[r].x;
+    float* vv = &v[r].x;
+    const float* gg = &g[r].x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float pe = pp[e] * sg.decay;
@@ -439,9 +455,10 @@ __global__ __launch_bounds__(256) void k_adamw(const AdamArgs a) {
       const float den = sqrtf(vv[e]) * a.inv_sqrt_bc2 + a.eps;
       pp[e] = pe - sg.step_size * (mm[e] / den);
     }
-    ((float4*)sg.p)[i] = p;
-    ((float4*)sg.m)[i] = m;
-    ((float4*)sg.v)[i] = v;
+    const int64_t i = base + r * 256;
+    ((float4*)sg.p)[i] = p[r];
+    ((float4*)sg.m)[i] = m[r];
+    ((float4*)sg.v)[i] = v[r];
   }
 }
 
@@ -666,6 +683,7 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
     a.K = kHeadDim;
     a.Cf = w.S;
     a.ldc = d.T;
+    a.causal = kCausalSkip;
     set_batch(a, d, kTok, kTok, kScore);
     launch_gemm_attn(a, kKK_F32, st);
   }
@@ -682,6 +700,7 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
     a.K = (int)d.T;
     a.C = w.attn;
     a.ldc = d.H;
+    a.causal = kCausalLower;
     set_batch(a, d, kScore, kTok, kTok);
     launch_gemm_attn(a, kKMN_BF16, st);
   }
@@ -738,6 +757,7 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     a.K = (int)d.T;
     a.C = w.dv;
     a.ldc = d.H;
+    a.causal = kCausalUpper;
     set_batch(a, d, kScore, kTok, kTok);
     launch_gemm_attn(a, kMNMN_BF16, st);
   }
@@ -752,6 +772,7 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     a.K = kHeadDim;
     a.Cf = w.S;
     a.ldc = d.T;
+    a.causal = kCausalSkip;
     set_batch(a, d, kTok, kTok, kScore);
     launch_gemm_attn(a, kKK_F32, st);
   }
@@ -768,6 +789,7 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     a.K = (int)d.T;
     a.C = w.dq;
     a.ldc = d.H;
+    a.causal = kCausalLower;
     set_batch(a, d, kScore, kTok, kTok);
     launch_gemm_attn(a, kKMN_BF16, st);
   }
@@ -783,6 +805,7 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     a.K = (int)d.T;
     a.C = w.dk;
     a.ldc = d.H;
+    a.causal = kCausalUpper;
     set_batch(a, d, kScore, kTok, kTok);
     launch_gemm_attn(a, kMNMN_BF16, st);
   }

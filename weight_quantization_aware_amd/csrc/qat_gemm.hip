@@ -38,11 +38,22 @@ constexpr const char* gemm_label() {
 
 int batches(const GemmArgs& a) { return a.batch_h > 0 ? a.batches : 1; }
 
+// Workgroups of one problem: every tile, or for kCausalSkip (square tiles of a
+// square problem) only the lower triangle of tiles.
+template <int BM, int BN>
+int64_t grid_tiles(const GemmArgs& a) {
+  if (a.causal == kCausalSkip) {
+    const int64_t t = (a.M + BM - 1) / BM;
+    return t * (t + 1) / 2;
+  }
+  return tiles(a, BM, BN);
+}
+
 template <int BM, int BN, int S, int WGM, int WGN, int AMN, int BMN, int EP, int NB, int GM = 0>
 void launch_bf16(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<kBf16, EP, NB>(), st);
   hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, GM, AMN, BMN, EP, NB>),
-                     dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
+                     dim3((unsigned)grid_tiles<BM, BN>(a), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
 template <int BM, int BN, int BK, int S, int BL, int NB>
@@ -94,14 +105,17 @@ void launch_grads(const GemmArgs& a, hipStream_t st) {
 }
 
 // Batched attention products: 256x256 tiles for the T x T score-shaped
-// outputs when they fill the chip, 128x128 tiles otherwise (the head-sized
-// outputs, N = head_dim).
+// outputs (fp32) when they fill the chip, 128x128 tiles otherwise (the
+// head-sized outputs, N = head_dim = 128).
 template <int AMN, int BMN, int EP>
 void launch_pick_attn(const GemmArgs& a, hipStream_t st) {
-  if (a.N >= 256 && tiles(a, 256, 256) * batches(a) >= 256)
-    launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, kTagAttn>(a, st);
-  else
-    launch_bf16<128, 128, 4, 2, 2, AMN, BMN, EP, kTagAttn>(a, st);
+  if constexpr (EP == kStoreF32) {
+    if (a.N >= 256 && tiles(a, 256, 256) * batches(a) >= 256) {
+      launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, kTagAttn>(a, st);
+      return;
+    }
+  }
+  launch_bf16<128, 128, 4, 2, 2, AMN, BMN, EP, kTagAttn>(a, st);
 }
 
 template <int BL, int NB>
@@ -129,6 +143,8 @@ void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st) {
   launch_pick<kKContig, kKContig, kStoreF32, 0>(a, st);
 }
 
+// kCausalSkip enumerates the lower triangle of square tiles: the problem must
+// be square (M == N); every attention tile configuration is square.
 void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st) {
   if (kind == kKK_F32) launch_pick_attn<kKContig, kKContig, kStoreF32>(a, st);
   else if (kind == kKMN_BF16) launch_pick_attn<kKContig, kMNContig, kStoreBf16>(a, st);

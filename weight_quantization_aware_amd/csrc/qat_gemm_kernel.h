@@ -41,6 +41,28 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
   tn = in_g / gm;
 }
 
+// Tiles of causal products. kCausalSkip (square tiles, M = N): the grid
+// enumerates only the lower triangle, tn <= tm, row by row; consecutive ids go
+// to different XCDs, which then get equal shares of the triangle.
+// kCausalLower / kCausalUpper (every row tile present, contractions of
+// different lengths): row tiles in boustrophedon order, every other group of
+// 8 reversed, so the XCD that takes a short tile in one group takes a long
+// one in the next.
+__device__ __forceinline__ void causal_tile_of(int b, int causal, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if (causal == kCausalSkip) {
+    int r = (int)((__builtin_sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
+    while (r * (r + 1) / 2 > b) --r;
+    while ((r + 1) * (r + 2) / 2 <= b) ++r;
+    tm = r;
+    tn = b - r * (r + 1) / 2;
+  } else {
+    const int p = b / tiles_n, g = p / 8;
+    tn = b % tiles_n;
+    const int end = min(8 * g + 8, tiles_m);
+    tm = (g & 1) ? 8 * g + (end - 1 - p) : p;
+  }
+}
+
 // The problem of a batched launch (grid y index; see GemmArgs::batch_h).
 __device__ __forceinline__ GemmArgs batch_view(const GemmArgs& a0) {
   GemmArgs a = a0;
@@ -580,19 +602,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  if (a.causal == kCausalNone) tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  else causal_tile_of(blockIdx.x, a.causal, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const uint32_t lds0 = lds_addr_of(smem);
+
+  // Slabs [kb, kb + nk) of the contraction (all of it unless causal).
+  int kb = 0, nk = (a.K + BK - 1) / BK;
+  if (a.causal == kCausalSkip) {
+    if (n0 >= m0 + BM) return;                           // every column beyond every row: not needed
+  } else if (a.causal == kCausalLower) {
+    nk = min(nk, (m0 + BM + BK - 1) / BK);
+  } else if (a.causal == kCausalUpper) {
+    kb = m0 / BK;
+    nk -= kb;
+  }
 
   LA la;
   LB lb;
   la.init(a.A, a.lda, m0, a.M, a.K);
   lb.init((const uint16_t*)a.B, a.ldb, n0, a.N, a.K);
-  const int nk = (a.K + BK - 1) / BK;
 
   auto dma_q = [&](int slab, int q) {                    // DMA instruction q of slab `slab`
     const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
-    const int k0 = (slab < nk ? slab : nk - 1) * BK;
+    const int k0 = (kb + (slab < nk ? slab : nk - 1)) * BK;
     if (q < NLA) la.issue_q(st, k0, q);
     else lb.issue_q(st + A_BYTES, k0, q - NLA);
   };
@@ -655,6 +688,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   for (int r = 0; r < NR; ++r) read_r(0, 0, r, F0);
   sched_fence();
 
+  // No unrolling or peeling: a peeled copy of the last iteration (the one
+  // with the drain) lets the register allocator copy accumulators between
+  // AGPRs right after their MFMAs, which the hazard recogniser cannot see.
+#pragma clang loop unroll(disable)
   for (int kt = 0; kt < nk; ++kt) {
     const int st = (kt % STAGES) * STAGE, nx = ((kt + 1) % STAGES) * STAGE;
     kstep(F0, st, 1, F1, -1);                            // k-step 0; read k-step 1

@@ -84,7 +84,15 @@ struct GemmArgs {
   int batch_h;
   int batches;
   int64_t sa_b, sa_h, sb_b, sb_h, sc_b, sc_h;
+  // Causal structure of attention products (rows m, columns n and the
+  // contraction index k are token positions of one sequence): 0 none;
+  // kCausalSkip: tiles whose every column exceeds every row (n > m) are not
+  // computed; kCausalLower: k runs over [0, end of the row tile); kCausalUpper:
+  // k runs over [start of the row tile, K).
+  int causal;
 };
+
+enum Causal { kCausalNone = 0, kCausalSkip = 1, kCausalLower = 2, kCausalUpper = 3 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
 enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3 };
