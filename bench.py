@@ -519,7 +519,8 @@ def block_step_flops(H, nh, I, T, Bn):
 def block_step_measurements(Q, torch, dev, stream, steps=10):
     """One Block-AP step (include/qat_block.h) on a Llama-2-7B block: 2
     sequences of 2048 tokens, w2g64, seeded synthetic inputs (synth.block_inputs),
-    s and z from the library's min-max init. Whole steps between events
+    s and z from the library's min-max init, no dW buffer (W's AdamW runs in
+    the epilogue of its gradient product). Whole steps between events
     (parameters and moments advance from step to step, as in training), then
     one step with the library's per-launch events for the kernel table."""
     from weight_quantization_aware_amd import synth
@@ -535,7 +536,8 @@ def block_step_measurements(Q, torch, dev, stream, steps=10):
         Q.qat_init_minmax(W, bits, sz, zz, group=group)
         e = {"W": W, "s": sz, "z": zz}
         for k in ("W", "s", "z"):
-            e["d" + k] = torch.empty_like(e[k])
+            if k != "W":             # dW is not needed by the update at group 64
+                e["d" + k] = torch.empty_like(e[k])
             e["m_" + k] = torch.zeros_like(e[k])
             e["v_" + k] = torch.zeros_like(e[k])
         lins.append(e)
@@ -576,8 +578,9 @@ def block_step_measurements(Q, torch, dev, stream, steps=10):
     for lab in ktab:
         ktab[lab]["share"] = round(ktab[lab]["ms"] / ksum, 4)
     nparam = sum(o * i + 2 * o * (i // group) for _, o, i in synth.block_linear_shapes(H, I))
-    if "adamw" in ktab:
-        ktab["adamw"]["gbs"] = round(28.0 * nparam / (ktab["adamw"]["ms"] * 1e-3) / 1e9, 1)
+    nqp = sum(2 * o * (i // group) for _, o, i in synth.block_linear_shapes(H, I))
+    if "adamw" in ktab:                  # s and z only
+        ktab["adamw"]["gbs"] = round(28.0 * nqp / (ktab["adamw"]["ms"] * 1e-3) / 1e9, 1)
     return {"what": "Llama-2-7B block (hidden 4096, 32 heads, inter 11008), 2 x 2048 tokens, w2g64: forward, "
                     "MSE, straight-through backward, AdamW (two groups, cosine)",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(Bn * T / (ms * 1e-3)),

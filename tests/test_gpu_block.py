@@ -246,6 +246,22 @@ def test_block_two_steps_and_schedule():
             check_update(after[i][key], params[n][key], p3[n][key], [g3[n][key]], (n, key, "late step"))
 
 
+@pytest.mark.parametrize("case", [CASES[0], CASES[1]])
+def test_block_step_without_dw_is_identical(case):
+    # groups of 64 and 128 update W in the gradient epilogue, so dW is optional:
+    # the step without it must leave every parameter and moment bit-identical
+    sh, d, params = make(case)
+    o = opt_dict(B.AdamW(), 0)
+    a, b = GpuBlock(sh, d, params), GpuBlock(sh, d, params)
+    for lin in b.lins:
+        del lin["dW"]
+    la, lb = a.step(o), b.step(o)
+    assert la == lb
+    for la_, lb_ in zip(a.lins, b.lins):
+        for k, t in lb_.items():
+            assert torch.equal(la_[k], t), k
+
+
 def test_block_step_full_size_7b():
     """Llama-2-7B block, 2 x 2048 tokens, w2g64 (the benchmark's step): the
     forward on sampled tokens of the second sequence against the oracle; the

@@ -395,7 +395,8 @@ __global__ __launch_bounds__(256) void k_loss_final(const float* __restrict__ pa
 }
 
 // ---------------------------------------------------------------------------
-// AdamW over up to 21 tensors in one launch. Segment i covers blocks
+// AdamW over up to 21 tensors in one launch (the seven linears' s and z, and
+// their W where the gradient epilogue does not update it). Segment i covers blocks
 // [start[i], start[i + 1]); a thread updates 4 consecutive parameters of 16
 // per thread (4 float4 steps), all in fp32:
 //   p <- p decay; m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
@@ -587,10 +588,30 @@ void fq_forward(const Dims& d, const qat_block_linear& L, int li, const uint16_t
   }
 }
 
+// One optimizer step's constants (host, double precision): learning rates
+// after the cosine schedule and the bias corrections of step t = k + 1.
+// fuse_w: W's update runs in its gradient epilogue (groups of 64 and 128);
+// otherwise in the multi-tensor kernel with s and z.
+struct AdamConst {
+  double lr_w, lr_q, bc1, bc2;
+  const qat_block_adamw* o;
+  bool fuse_w;
+};
+
+AdamConst adam_const(const qat_block_adamw& o, int group) {
+  const double pi = 3.14159265358979323846;
+  const double c = (1.0 + cos(pi * (double)o.step / (double)o.total_steps)) / 2.0;
+  const double t = (double)(o.step + 1);
+  return AdamConst{o.lr_weight * c, o.lr_quant * c, 1.0 - pow(o.beta1, t), 1.0 - pow(o.beta2, t), &o,
+                   group == 64 || group == 128};
+}
+
 // Straight-through backward of linear li: dX (if requested) from W_hat^T
-// staged in ws.wh, and dW, ds, dz from the gradient GEMM's epilogue.
+// staged in ws.wh, and dW, ds, dz from the gradient GEMM's epilogue. With an
+// optimizer step (ac), the same epilogue also applies AdamW to W and its
+// moments; s and z are updated afterwards by k_adamw.
 void fq_backward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* dY, const uint16_t* X,
-                 uint16_t* dX, const Ws& w, hipStream_t st) {
+                 uint16_t* dX, const Ws& w, const AdamConst* ac, hipStream_t st) {
   const int64_t out = d.out[li], in = d.in[li];
   if (dX) {
     launch_w_hat_t(L.W, L.s, L.z, out, in, d.group, d.bits, w.wh, st);
@@ -602,7 +623,19 @@ void fq_backward(const Dims& d, const qat_block_linear& L, int li, const uint16_
   a.dW = L.dW;
   a.ds = L.ds;
   a.dz = L.dz;
-  launch_gemm_grads(a, kSteGrads, d.bits, st);
+  const bool fuse = ac && ac->fuse_w;
+  if (fuse) {
+    a.Wupd = L.W;
+    a.mW = L.m_W;
+    a.vW = L.v_W;
+    a.adam_b1 = (float)ac->o->beta1;
+    a.adam_b2 = (float)ac->o->beta2;
+    a.adam_isbc2 = (float)(1.0 / sqrt(ac->bc2));
+    a.adam_eps = (float)ac->o->eps;
+    a.adam_step = (float)(ac->lr_w / ac->bc1);
+    a.adam_decay = (float)(1.0 - ac->lr_w * ac->o->weight_decay);
+  }
+  launch_gemm_grads(a, fuse ? kSteAdam : kSteGrads, d.bits, st);
 }
 
 // Per-(sequence, head) views for the attention products: the operand that
@@ -728,23 +761,24 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
   }
 }
 
-void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, const Ws& w, hipStream_t st) {
+void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, const Ws& w, const AdamConst* ac,
+                    hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)kHeadDim);
-  fq_backward(d, L[QAT_BLOCK_DOWN], QAT_BLOCK_DOWN, w.dy, w.a, w.da, w, st);
+  fq_backward(d, L[QAT_BLOCK_DOWN], QAT_BLOCK_DOWN, w.dy, w.a, w.da, w, ac, st);
   {
     LaunchTimer t("swiglu_bwd", st);
     const int64_t n8 = d.BT * d.I / 8;
     hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.da, n8);
   }
   // gate and up now hold their output gradients
-  fq_backward(d, L[QAT_BLOCK_GATE], QAT_BLOCK_GATE, w.gate, w.h2, w.dxg, w, st);
-  fq_backward(d, L[QAT_BLOCK_UP], QAT_BLOCK_UP, w.up, w.h2, w.dxu, w, st);
+  fq_backward(d, L[QAT_BLOCK_GATE], QAT_BLOCK_GATE, w.gate, w.h2, w.dxg, w, ac, st);
+  fq_backward(d, L[QAT_BLOCK_UP], QAT_BLOCK_UP, w.up, w.h2, w.dxu, w, ac, st);
   {
     LaunchTimer t("rmsnorm_bwd", st);
     hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)d.BT), dim3(256), 0, st, w.dxg, w.dxu, w.x2, w.r2, g2, w.dy,
                        w.dx2, (int)d.H);
   }
-  fq_backward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.dx2, w.attn, w.dattn, w, st);
+  fq_backward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.dx2, w.attn, w.dattn, w, ac, st);
   {
     // dv = P^T dattn: A[m = key][k = query] = P[query][key], both MN-contiguous
     GemmArgs a = zero_args();
@@ -811,22 +845,20 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
   }
   rope(d, w.dq, w.dk, w, -1.0f, st);
   // q, k, v: gradients of W, s, z only (the block input's gradient is not needed)
-  fq_backward(d, L[QAT_BLOCK_Q], QAT_BLOCK_Q, w.dq, w.h1, nullptr, w, st);
-  fq_backward(d, L[QAT_BLOCK_K], QAT_BLOCK_K, w.dk, w.h1, nullptr, w, st);
-  fq_backward(d, L[QAT_BLOCK_V], QAT_BLOCK_V, w.dv, w.h1, nullptr, w, st);
+  fq_backward(d, L[QAT_BLOCK_Q], QAT_BLOCK_Q, w.dq, w.h1, nullptr, w, ac, st);
+  fq_backward(d, L[QAT_BLOCK_K], QAT_BLOCK_K, w.dk, w.h1, nullptr, w, ac, st);
+  fq_backward(d, L[QAT_BLOCK_V], QAT_BLOCK_V, w.dv, w.h1, nullptr, w, ac, st);
 }
 
-void adamw(const Dims& d, const qat_block_linear* L, const qat_block_adamw& o, hipStream_t st) {
-  const double pi = 3.14159265358979323846;
-  const double cosf_ = (1.0 + cos(pi * (double)o.step / (double)o.total_steps)) / 2.0;
-  const double lr_w = o.lr_weight * cosf_, lr_q = o.lr_quant * cosf_;
-  const double t = (double)(o.step + 1);
-  const double bc1 = 1.0 - pow(o.beta1, t), bc2 = 1.0 - pow(o.beta2, t);
+// AdamW on every linear's s and z, and on W unless its gradient epilogue
+// updated it.
+void adamw_rest(const Dims& d, const qat_block_linear* L, const AdamConst& ac, hipStream_t st) {
+  const qat_block_adamw& o = *ac.o;
   AdamArgs a;
   memset(&a, 0, sizeof a);
   a.b1 = (float)o.beta1;
   a.b2 = (float)o.beta2;
-  a.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+  a.inv_sqrt_bc2 = (float)(1.0 / sqrt(ac.bc2));
   a.eps = (float)o.eps;
   int nseg = 0, blk = 0;
   for (int i = 0; i < QAT_BLOCK_LINEARS; ++i) {
@@ -835,18 +867,20 @@ void adamw(const Dims& d, const qat_block_linear* L, const qat_block_adamw& o, h
       float *p, *g, *m, *v;
       int64_t n;
       double lr;
-    } t3[3] = {{L[i].W, L[i].dW, L[i].m_W, L[i].v_W, nw, lr_w},
-               {L[i].s, L[i].ds, L[i].m_s, L[i].v_s, ng, lr_q},
-               {L[i].z, L[i].dz, L[i].m_z, L[i].v_z, ng, lr_q}};
+      bool on;
+    } t3[3] = {{L[i].W, L[i].dW, L[i].m_W, L[i].v_W, nw, ac.lr_w, !ac.fuse_w},
+               {L[i].s, L[i].ds, L[i].m_s, L[i].v_s, ng, ac.lr_q, true},
+               {L[i].z, L[i].dz, L[i].m_z, L[i].v_z, ng, ac.lr_q, true}};
     for (auto& e : t3) {
-      AdamSeg& s = a.seg[nseg];
-      s.p = e.p;
-      s.g = e.g;
-      s.m = e.m;
-      s.v = e.v;
-      s.n4 = e.n / 4;
-      s.step_size = (float)(e.lr / bc1);
-      s.decay = (float)(1.0 - e.lr * o.weight_decay);
+      if (!e.on) continue;
+      AdamSeg& sg = a.seg[nseg];
+      sg.p = e.p;
+      sg.g = e.g;
+      sg.m = e.m;
+      sg.v = e.v;
+      sg.n4 = e.n / 4;
+      sg.step_size = (float)(e.lr / ac.bc1);
+      sg.decay = (float)(1.0 - e.lr * o.weight_decay);
       a.start[nseg] = blk;
       blk += blocks_of(e.n, kAdamPerBlock);
       ++nseg;
@@ -891,8 +925,9 @@ int32_t check_args(const Dims& d, const qat_block_linear* L, const float* g1, co
     const qat_block_linear& l = L[i];
     const size_t nwt = (size_t)(d.out[i] * d.in[i]) * 4, ng = (size_t)(d.out[i] * (d.in[i] / d.group)) * 4;
     if (!l.W || !l.s || !l.z) return QAT_ERR_NULL;
-    if (step && (!l.dW || !l.ds || !l.dz || !l.m_W || !l.v_W || !l.m_s || !l.v_s || !l.m_z || !l.v_z))
+    if (step && (!l.ds || !l.dz || !l.m_W || !l.v_W || !l.m_s || !l.v_s || !l.m_z || !l.v_z))
       return QAT_ERR_NULL;
+    if (step && !l.dW && d.group == 32) return QAT_ERR_NULL;   // W's update reads dW at this group size
     const void* all[] = {l.W, l.s, l.z, l.dW, l.ds, l.dz, l.m_W, l.v_W, l.m_s, l.v_s, l.m_z, l.v_z};
     for (const void* p : all)
       if (p && !al16(p)) return QAT_ERR_ALIGN;
@@ -956,12 +991,13 @@ QAT_API int32_t qat_block_ap_step(const qat_block_shape* shape, const qat_block_
       !(opt->beta2 >= 0 && opt->beta2 < 1) || !(opt->eps > 0))
     return QAT_ERR_SHAPE;
   const Dims d = dims_of(*shape);
-  const int32_t ac = check_args(d, lin, g1, g2, x, target, y, loss, ws, true);
-  if (ac != QAT_OK) return ac;
+  const int32_t st = check_args(d, lin, g1, g2, x, target, y, loss, ws, true);
+  if (st != QAT_OK) return st;
   if (ws_bytes < ws_layout(d, nullptr).bytes) return QAT_ERR_WORKSPACE;
   const Ws w = ws_layout(d, (uint8_t*)ws);
+  const AdamConst ac = adam_const(*opt, d.group);
   block_forward(d, lin, g1, g2, x, target, y, loss, w, stream);
-  block_backward(d, lin, g2, w, stream);
-  adamw(d, lin, *opt, stream);
+  block_backward(d, lin, g2, w, &ac, stream);
+  adamw_rest(d, lin, ac, stream);
   return finish_call();
 }

@@ -28,6 +28,7 @@ constexpr int kTagAttn = 5;
 template <int BL, int EP, int NB>
 constexpr const char* gemm_label() {
   if (EP == kSteGrads) return "gemm_ste_grads";
+  if (EP == kSteAdam) return "gemm_ste_grads_adamw";
   if (EP == kE2eScaleGrad) return "gemm_e2e_grads";
   if (BL == kFp32Quant) return "gemm_fwd_fused_fp32";
   if (BL == kPacked) return "gemm_fwd_packed";
@@ -79,10 +80,21 @@ void launch_pick(const GemmArgs& a, hipStream_t st) {
 // of 32 (GM 1) and groups that tile BN (GM 2: 128, or a short whole row) are
 // stored directly; whole rows wider than BN (GM 3) are accumulated per tile
 // into ds and dz, zero-filled here first.
+// The weight-updating epilogue (kSteAdam) holds W, m and v of the next step
+// in registers: 256x256 tiles run with 4 waves (512 registers each), which
+// leaves room for them; 8 waves would spill.
 template <int EP, int NB, int GM>
 void launch_pick_grads_gm(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kMNContig, kMNContig, EP, NB, GM>(a, st);
+  constexpr int WGN = EP == kSteAdam ? 2 : 4;
+  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, WGN, kMNContig, kMNContig, EP, NB, GM>(a, st);
   else launch_bf16<128, 128, 4, 2, 2, kMNContig, kMNContig, EP, NB, GM>(a, st);
+}
+
+// The weight-updating epilogue exists for groups of 64 (GM 0) and 128 (GM 2);
+// the caller updates W separately at other group sizes.
+void launch_grads_adam(const GemmArgs& a, hipStream_t st) {
+  if (a.group == 64) launch_pick_grads_gm<kSteAdam, 0, 0>(a, st);
+  else launch_pick_grads_gm<kSteAdam, 0, 2>(a, st);
 }
 
 template <int EP, int NB>
@@ -157,6 +169,7 @@ void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {
 
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st) {
   if (epi == kSteGrads) launch_grads<kSteGrads, 0>(a, st);
+  else if (epi == kSteAdam) launch_grads_adam(a, st);
   else if (bits == 2) launch_grads<kE2eScaleGrad, 2>(a, st);
   else if (bits == 3) launch_grads<kE2eScaleGrad, 3>(a, st);
   else launch_grads<kE2eScaleGrad, 4>(a, st);

@@ -374,6 +374,9 @@ __device__ __forceinline__ void mfma_drain() {
 //                  X^T); Gw = acc. dW = Gw * m and the group sums of ds, dz of
 //                  the straight-through estimator, from W, s, z re-quantised
 //                  here (quant_elem).
+//   kSteAdam:      kSteGrads, then AdamW on each weight from its masked
+//                  gradient: W, mW, vW updated in place (the elements of a
+//                  tile are read and written by that tile's epilogue only).
 //   kE2eScaleGrad: as above with packed codes: ds = sum Gw (q - z), dz = -s
 //                  sum Gw.
 // A 64-column quantisation group is 4 j-tiles x 4 registers of one lane plus a
@@ -384,9 +387,12 @@ __device__ __forceinline__ void mfma_drain() {
 template <int EP>
 struct EpiIn {
   float s[2], z[2];
-  float4 w[4];          // kSteGrads: W[o][cg + 16 jj + cq .. + 3]
+  float4 w[4];          // kSteGrads, kSteAdam: W[o][cg + 16 jj + cq .. + 3]
+  float4 m[4], v[4];    // kSteAdam: W's AdamW moments at the same positions
   uint32_t c[4];        // kE2eScaleGrad: the same four codes per jj
 };
+
+constexpr bool is_ste(int ep) { return ep == kSteGrads || ep == kSteAdam; }
 
 // Group modes of the gradient epilogues (GM): 0 groups of 64 columns, one per
 // chunk; 1 groups of 32, two per chunk (j-tiles 0-1 and 2-3); 2 groups of
@@ -450,8 +456,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          if constexpr (EP == kSteGrads) in.w[jj] = *(const float4*)(a.W + (int64_t)o * a.ldw + cg + jj * 16 + cq);
+          const int64_t wi = (int64_t)o * a.ldw + cg + jj * 16 + cq;
+          if constexpr (is_ste(EP)) in.w[jj] = *(const float4*)(a.W + wi);
           else in.c[jj] = codes4<NB>(a.Wq + (int64_t)o * a.ldq, cg + jj * 16 + cq);
+          if constexpr (EP == kSteAdam) {
+            in.m[jj] = *(const float4*)(a.mW + wi);
+            in.v[jj] = *(const float4*)(a.vW + wi);
+          }
         }
       }
     };
@@ -468,7 +479,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
 #pragma unroll
       for (int h = 0; h < NH; ++h) ps[h] = pz[h] = 0.f;
       if (ok) {
-        if constexpr (EP == kSteGrads) {
+        if constexpr (is_ste(EP)) {
           float zr[NH], rcp[NH];
 #pragma unroll
           for (int h = 0; h < NH; ++h) {
@@ -488,8 +499,25 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
               ps[h] += gw[r] * (e.m ? (__builtin_rintf(e.u) - e.u) : (e.q - zr[h]));
               pz[h] += e.m ? 0.0f : gw[r];
             }
-            if (a.dW)
-              *(float4*)(a.dW + (int64_t)o * a.ldw + cg + jj * 16 + cq) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+            const int64_t wi = (int64_t)o * a.ldw + cg + jj * 16 + cq;
+            if (a.dW) *(float4*)(a.dW + wi) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+            if constexpr (EP == kSteAdam) {
+              // AdamW (the multi-tensor kernel's arithmetic) on the masked gradient
+              float mv[4] = {cur.m[jj].x, cur.m[jj].y, cur.m[jj].z, cur.m[jj].w};
+              float vv[4] = {cur.v[jj].x, cur.v[jj].y, cur.v[jj].z, cur.v[jj].w};
+              float pv[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float pe = wv[r] * a.adam_decay;
+                mv[r] = a.adam_b1 * mv[r] + (1.0f - a.adam_b1) * dw[r];
+                vv[r] = a.adam_b2 * vv[r] + (1.0f - a.adam_b2) * dw[r] * dw[r];
+                const float den = sqrtf(vv[r]) * a.adam_isbc2 + a.adam_eps;
+                pv[r] = pe - a.adam_step * (mv[r] / den);
+              }
+              *(float4*)(a.Wupd + wi) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+              *(float4*)(a.mW + wi) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+              *(float4*)(a.vW + wi) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+            }
           }
         } else {
 #pragma unroll

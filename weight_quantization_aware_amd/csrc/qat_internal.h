@@ -90,12 +90,19 @@ struct GemmArgs {
   // computed; kCausalLower: k runs over [0, end of the row tile); kCausalUpper:
   // k runs over [start of the row tile, K).
   int causal;
+  // kSteAdam: AdamW on the weight in the straight-through epilogue. W (the
+  // same array as the const W above) and its moments mW, vW are updated in
+  // place from the masked gradient; dW is still stored when non-null.
+  float* Wupd;
+  float* mW;
+  float* vW;
+  float adam_b1, adam_b2, adam_isbc2, adam_eps, adam_step, adam_decay;
 };
 
 enum Causal { kCausalNone = 0, kCausalSkip = 1, kCausalLower = 2, kCausalUpper = 3 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
-enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3 };
+enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4 };
 enum Layout { kKContig = 0, kMNContig = 1 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
@@ -103,7 +110,8 @@ void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
 // dX = dY W_hat: A = dY [M][out], B = W_hat^T [in][out], both K-contiguous.
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 // Gradient GEMM over tokens, Gw = dY^T X with both operands MN-contiguous;
-// epi = kSteGrads (dW, ds, dz) or kE2eScaleGrad (ds, dz).
+// epi = kSteGrads (dW, ds, dz), kSteAdam (the same, and AdamW on W, m, v in
+// place; groups of 64 or 128 only) or kE2eScaleGrad (ds, dz).
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st);
 // Forward-type GEMM on a staged bf16 W_hat with fp32 output (a.Cf).
 void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st);

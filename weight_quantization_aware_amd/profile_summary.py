@@ -35,6 +35,7 @@ LABELS = [
     # k_gemm<BM, BN, BK, STAGES, AMN, BMN, EP, NB>
     (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*1>", "gemm_dx"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*1,\s*0>", "gemm_ste_grads"),
+    (r"k_gemm<[^>]*,\s*1,\s*1,\s*4,\s*0>", "gemm_ste_grads_adamw"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*2,\s*\d>", "gemm_e2e_grads"),
     (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
     (r"k_gemm<[^>]*,\s*0,\s*0,\s*3,\s*0>", "gemm_fwd_f32"),
