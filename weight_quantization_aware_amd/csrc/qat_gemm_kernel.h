@@ -48,7 +48,17 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 // different lengths): row tiles in boustrophedon order, every other group of
 // 8 reversed, so the XCD that takes a short tile in one group takes a long
 // one in the next.
-__device__ __forceinline__ void causal_tile_of(int b, int causal, int tiles_m, int tiles_n, int& tm, int& tn) {
+// With the problem's tiles on one XCD (grouped), the contraction-range modes
+// instead issue the longest tiles first (the XCD's CUs take workgroups in
+// order as they free up).
+__device__ __forceinline__ void causal_tile_of(int b, int causal, bool grouped, int tiles_m, int tiles_n, int& tm,
+                                               int& tn) {
+  if (causal != kCausalSkip && grouped) {
+    const int p = b / tiles_n;
+    tn = b % tiles_n;
+    tm = causal == kCausalLower ? tiles_m - 1 - p : p;
+    return;
+  }
   if (causal == kCausalSkip) {
     int r = (int)((__builtin_sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
     while (r * (r + 1) / 2 > b) --r;
@@ -63,11 +73,29 @@ __device__ __forceinline__ void causal_tile_of(int b, int causal, int tiles_m, i
   }
 }
 
-// The problem of a batched launch (grid y index; see GemmArgs::batch_h).
-__device__ __forceinline__ GemmArgs batch_view(const GemmArgs& a0) {
+// Workgroup -> (tile id, problem) of a launch. Batched launches whose problem
+// count is a multiple of 8 keep all tiles of one problem on one XCD
+// (workgroups go round-robin to the 8 XCDs in dispatch order, x fastest), so
+// its shared operands are fetched into one L2: in each run of 8 x tiles
+// consecutive workgroups, XCD j takes every tile of problem j of the run.
+__device__ __forceinline__ void work_of(const GemmArgs& a0, int& tile, int& prob, bool& grouped) {
+  tile = blockIdx.x;
+  prob = blockIdx.y;
+  grouped = a0.batch_h > 0 && (a0.batches & 7) == 0;
+  if (grouped) {
+    const int nt = gridDim.x;
+    const int w = blockIdx.x + blockIdx.y * nt;
+    const int r = w % (8 * nt);
+    prob = 8 * (w / (8 * nt)) + (r & 7);
+    tile = r >> 3;
+  }
+}
+
+// The problem of a batched launch (see GemmArgs::batch_h).
+__device__ __forceinline__ GemmArgs batch_view(const GemmArgs& a0, int z) {
   GemmArgs a = a0;
   if (a.batch_h > 0) {
-    const int z = blockIdx.y, b = z / a.batch_h, h = z - b * a.batch_h;
+    const int b = z / a.batch_h, h = z - b * a.batch_h;
     a.A += b * a.sa_b + h * a.sa_h;
     a.B = (const uint16_t*)a.B + b * a.sb_b + h * a.sb_h;
     const int64_t oc = b * a.sc_b + h * a.sc_h;
@@ -609,7 +637,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int GM, int AMN, int BMN, int EP, int NB>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
-  const GemmArgs a = batch_view(a0);
+  int tile_id, prob;
+  bool grouped;
+  work_of(a0, tile_id, prob, grouped);
+  const GemmArgs a = batch_view(a0, prob);
   constexpr int NW = WGM * WGN;
   using LA = typename DmaTileOf<BM, BK, AMN, NW>::T;
   using LB = typename DmaTileOf<BN, BK, BMN, NW>::T;
@@ -630,8 +661,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   int tm, tn;
-  if (a.causal == kCausalNone) tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  else causal_tile_of(blockIdx.x, a.causal, tiles_m, tiles_n, tm, tn);
+  if (a.causal == kCausalNone) tile_of(tile_id, tiles_m, tiles_n, tm, tn);
+  else causal_tile_of(tile_id, a.causal, grouped, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const uint32_t lds0 = lds_addr_of(smem);
 
