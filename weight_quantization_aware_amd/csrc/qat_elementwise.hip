@@ -184,9 +184,11 @@ __global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, 
                                                  FastDiv gdiv, float K, uint16_t* __restrict__ w_hat_t) {
   constexpr int TO = 128, TIN = 64;                      // tile rows (out), cols (in)
   // LDS tile T[c][o] (c: input column, o: output row; 256 bytes per c). The
-  // 16-byte chunk h of row c sits at h ^ 2 (c / 8): the 64 four-byte writes of
-  // one instruction (8 columns x 8 row pairs) then fall on 64 distinct banks,
-  // and a row is still read as whole 16-byte chunks.
+  // 16-byte chunk h of row c sits at h ^ (c / 8) ^ 8 (h & 1): the 64 four-byte
+  // writes of one instruction (8 columns x 8 row pairs) fall on 64 distinct
+  // banks, and so do the 32 of each half-wave on 32 banks (the former h ^ 2
+  // (c / 8) put two of them on one bank there); a row is still read as whole
+  // 16-byte chunks, every bank used equally.
   __shared__ __attribute__((aligned(16))) uint16_t T[TIN * TO];
   const int bo = SRC == 1 ? blockIdx.x : blockIdx.y, bi = SRC == 1 ? blockIdx.y : blockIdx.x;
   const int64_t o0 = (int64_t)bo * TO, i0 = (int64_t)bi * TIN;
@@ -228,7 +230,8 @@ __global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, 
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int c = co * 8 + k;
-      const int dw = (((rp >> 2) ^ ((c >> 3) << 1)) << 2) | (rp & 3);   // swizzled 4-byte slot of rows 2rp, 2rp+1
+      const int hc = rp >> 2;                                                 // chunk of rows 2rp, 2rp+1
+      const int dw = ((hc ^ (c >> 3) ^ ((hc & 1) << 3)) << 2) | (rp & 3);   // their swizzled 4-byte slot
       *(uint32_t*)&T[c * TO + 2 * dw] = pack_bf16x2(h[0][k], h[1][k]);
     }
   }
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(256) void k_w_hat_t(const void* __restrict__ Wsrc, 
     const int row = idx >> 4, ch = idx & 15;            // row of W_hat^T in the tile, 8-element chunk
     const int64_t oc = o0 + ch * 8;
     if (oc < out)
-      *(uint4*)(w_hat_t + (i0 + row) * out + oc) = *(const uint4*)&T[row * TO + ((ch ^ ((row >> 3) << 1)) * 8)];
+      *(uint4*)(w_hat_t + (i0 + row) * out + oc) = *(const uint4*)&T[row * TO + ((ch ^ (row >> 3) ^ ((ch & 1) << 3)) * 8)];
   }
 }
 
