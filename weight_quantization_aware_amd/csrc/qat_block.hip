@@ -14,7 +14,9 @@
 // Memory-bound row kernels: one workgroup per token row for the norms (a row
 // of H <= 8192 values stays in registers between the reduction and the
 // write), one wave per score row for the softmax (a row of T <= 4096 scores
-// in registers), 16-byte vector accesses throughout.
+// in registers), 16-byte vector accesses throughout. The softmax backward
+// runs in the epilogue of the dP product (kSoftmaxGrad) from a per-query row
+// term.
 #include <math.h>
 #include <string.h>
 
@@ -262,51 +264,29 @@ __global__ __launch_bounds__(256) void k_softmax_fwd(const float* __restrict__ S
   }
 }
 
-// Softmax backward in place over P: dS = scale P (dP - sum_k P dP) for k <= q
-// (P, and so dS, is 0 beyond the diagonal and stays untouched there).
-template <int NJ>
-__global__ __launch_bounds__(256) void k_softmax_bwd(const float* __restrict__ dP, uint16_t* __restrict__ P,
-                                                      int64_t rows, int T, float scale) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const int q = (int)(row % T);
-  const float* d = dP + row * T;
-  uint16_t* p = P + row * T;
-  float pv[NJ][4], dv[NJ][4];
-  float dot = 0.f;
+// Row term of the softmax backward: D[problem][q] = sum_k P[q][k] dP[q][k],
+// which equals dO[q] . O[q] (sum over k of P dP = dO . sum_k P v_k = dO . O),
+// from the attention output and its gradient (bf16 [B*T][H]). One thread per
+// (token, head), 128 products in fp32.
+__global__ __launch_bounds__(256) void k_attn_rowdot(const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
+                                                      float* __restrict__ D, int64_t rows, int T, int H, int nh) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * nh) return;
+  const int64_t tok = idx / nh;
+  const int head = (int)(idx % nh);
+  const uint4* a = (const uint4*)(dO + tok * H + head * kHeadDim);
+  const uint4* o = (const uint4*)(O + tok * H + head * kHeadDim);
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < kHeadDim / 8; ++c) {
+    float x[8], y[8];
+    unpack8(a[c], x);
+    unpack8(o[c], y);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int c0 = 256 * j + 4 * lane;
-    if (c0 <= q && c0 < T) {
-      const uint2 pb = *(const uint2*)(p + c0);
-      const float4 a = *(const float4*)(d + c0);
-      pv[j][0] = __builtin_bit_cast(float, pb.x << 16);
-      pv[j][1] = __builtin_bit_cast(float, pb.x & 0xFFFF0000u);
-      pv[j][2] = __builtin_bit_cast(float, pb.y << 16);
-      pv[j][3] = __builtin_bit_cast(float, pb.y & 0xFFFF0000u);
-      dv[j][0] = a.x;
-      dv[j][1] = a.y;
-      dv[j][2] = a.z;
-      dv[j][3] = a.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pv[j][e] = dv[j][e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dot += pv[j][e] * dv[j][e];
+    for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
   }
-  dot = wave_sum(dot);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int c0 = 256 * j + 4 * lane;
-    if (c0 <= q && c0 < T) {
-      float o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = scale * pv[j][e] * (dv[j][e] - dot);
-      *(uint2*)(p + c0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    }
-  }
+  const int64_t b = tok / T, t = tok % T;
+  D[(b * nh + head) * T + t] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -509,7 +489,7 @@ int32_t check_shape(const qat_block_shape* s) {
 struct Ws {
   float2* rope;          // [T][64]
   uint16_t *h1, *q, *k, *v, *attn, *h2, *gate, *up, *a, *dy, *wh, *da, *dxg, *dxu, *dx2, *dattn, *dq, *dk, *dv;
-  float *S, *o, *x2, *dn, *r1, *r2, *partial;
+  float *S, *o, *x2, *dn, *r1, *r2, *partial, *D;
   uint16_t* P;
   size_t bytes;
 };
@@ -555,6 +535,7 @@ Ws ws_layout(const Dims& d, uint8_t* base) {
   w.dq = (uint16_t*)take(th * 2);
   w.dk = (uint16_t*)take(th * 2);
   w.dv = (uint16_t*)take(th * 2);
+  w.D = (float*)take(d.B * d.nh * d.T * 4);
   w.bytes = off;
   return w;
 }
@@ -665,18 +646,6 @@ void softmax_fwd(const Dims& d, const Ws& w, float scale, hipStream_t st) {
   else if (T <= 1024) hipLaunchKernelGGL(k_softmax_fwd<4>, grid, block, 0, st, w.S, w.P, rows, T, scale);
   else if (T <= 2048) hipLaunchKernelGGL(k_softmax_fwd<8>, grid, block, 0, st, w.S, w.P, rows, T, scale);
   else hipLaunchKernelGGL(k_softmax_fwd<16>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-}
-
-void softmax_bwd(const Dims& d, const Ws& w, float scale, hipStream_t st) {
-  const int64_t rows = d.B * d.nh * d.T;
-  const int T = (int)d.T;
-  LaunchTimer t("softmax_bwd", st);
-  const dim3 grid((unsigned)blocks_of(rows, 4)), block(256);
-  if (T <= 256) hipLaunchKernelGGL(k_softmax_bwd<1>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else if (T <= 512) hipLaunchKernelGGL(k_softmax_bwd<2>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else if (T <= 1024) hipLaunchKernelGGL(k_softmax_bwd<4>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else if (T <= 2048) hipLaunchKernelGGL(k_softmax_bwd<8>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else hipLaunchKernelGGL(k_softmax_bwd<16>, grid, block, 0, st, w.S, w.P, rows, T, scale);
 }
 
 void rope(const Dims& d, uint16_t* q, uint16_t* k, const Ws& w, float sgn, hipStream_t st) {
@@ -796,7 +765,14 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     launch_gemm_attn(a, kMNMN_BF16, st);
   }
   {
-    // dP = dattn v^T, fp32 into the score buffer
+    // D = rowsum(P dP) = dO . O per query
+    LaunchTimer t("attn_rowdot", st);
+    const int64_t n = d.BT * d.nh;
+    hipLaunchKernelGGL(k_attn_rowdot, dim3((unsigned)blocks_of(n, 256)), dim3(256), 0, st, w.dattn, w.attn, w.D,
+                       d.BT, (int)d.T, (int)d.H, (int)d.nh);
+  }
+  {
+    // dP = dattn v^T; its epilogue writes dS = scale P (dP - D) over P
     GemmArgs a = zero_args();
     a.A = w.dattn;
     a.lda = d.H;
@@ -804,13 +780,16 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     a.ldb = d.H;
     a.M = a.N = (int)d.T;
     a.K = kHeadDim;
-    a.Cf = w.S;
+    a.C = w.P;
     a.ldc = d.T;
     a.causal = kCausalSkip;
+    a.Dvec = w.D;
+    a.sd_b = d.nh * d.T;
+    a.sd_h = d.T;
+    a.escale = scale;
     set_batch(a, d, kTok, kTok, kScore);
-    launch_gemm_attn(a, kKK_F32, st);
+    launch_gemm_attn(a, kKK_DSOFTMAX, st);
   }
-  softmax_bwd(d, w, scale, st);          // P <- dS (scaled)
   {
     // dq = dS k
     GemmArgs a = zero_args();

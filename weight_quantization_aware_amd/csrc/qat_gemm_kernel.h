@@ -101,6 +101,7 @@ __device__ __forceinline__ GemmArgs batch_view(const GemmArgs& a0, int z) {
     const int64_t oc = b * a.sc_b + h * a.sc_h;
     if (a.C) a.C += oc;
     if (a.Cf) a.Cf += oc;
+    if (a.Dvec) a.Dvec += b * a.sd_b + h * a.sd_h;
   }
   return a;
 }
@@ -398,6 +399,8 @@ __device__ __forceinline__ void mfma_drain() {
 // + 4 (lane >> 4) + r], r = 0..3.
 //   kStoreBf16:    C (bf16) = acc.
 //   kStoreF32:     Cf (fp32) = acc.
+//   kSoftmaxGrad:  C (bf16, holding P) = escale P (acc - Dvec[row]): the
+//                  softmax backward of attention applied to dP = acc.
 //   kSteGrads:     rows are weight rows o (A = dY^T), columns inputs c (B =
 //                  X^T); Gw = acc. dW = Gw * m and the group sums of ds, dz of
 //                  the straight-through estimator, from W, s, z re-quantised
@@ -434,7 +437,27 @@ template <int EP, int NB, int GM, int BM, int BN, int TI, int TJ, int WN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
                                               int wm0, int wn0, int lane, float* red) {
   const int rl = lane & 15, cq = 4 * (lane >> 4);
-  if constexpr (EP == kStoreF32) {
+  if constexpr (EP == kSoftmaxGrad) {
+    // dS = escale P (dP - D[row]) over P, 4 consecutive columns per lane
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = m0 + wm0 + i * 16 + rl;
+      if (row >= a.M) continue;
+      const float dr = a.Dvec[row];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn0 + j * 16 + cq;
+        if (col < a.N) {
+          uint2* pp = (uint2*)(a.C + (int64_t)row * a.ldc + col);
+          const uint2 pb = *pp;
+          const float p0 = __builtin_bit_cast(float, pb.x << 16), p1 = __builtin_bit_cast(float, pb.x & 0xFFFF0000u);
+          const float p2 = __builtin_bit_cast(float, pb.y << 16), p3 = __builtin_bit_cast(float, pb.y & 0xFFFF0000u);
+          *pp = make_uint2(pack_bf16x2(a.escale * p0 * (acc[j][i][0] - dr), a.escale * p1 * (acc[j][i][1] - dr)),
+                           pack_bf16x2(a.escale * p2 * (acc[j][i][2] - dr), a.escale * p3 * (acc[j][i][3] - dr)));
+        }
+      }
+    }
+  } else if constexpr (EP == kStoreF32) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int row = m0 + wm0 + i * 16 + rl;

@@ -97,12 +97,18 @@ struct GemmArgs {
   float* mW;
   float* vW;
   float adam_b1, adam_b2, adam_isbc2, adam_eps, adam_step, adam_decay;
+  // kSoftmaxGrad: the product is dP = dO v^T of one attention problem and the
+  // epilogue writes dS = escale P (dP - Dvec[row]) in bf16 over P (C, ldc),
+  // the problem's P and Dvec at b * s?_b + h * s?_h (C offsets as above).
+  const float* Dvec;
+  int64_t sd_b, sd_h;
+  float escale;
 };
 
 enum Causal { kCausalNone = 0, kCausalSkip = 1, kCausalLower = 2, kCausalUpper = 3 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
-enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4 };
+enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4, kSoftmaxGrad = 5 };
 enum Layout { kKContig = 0, kMNContig = 1 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
@@ -124,10 +130,11 @@ void launch_linear_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, in
 GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z, int64_t M,
                            int64_t out, int64_t in, int group, int bits);
 // Batched products of attention (a.batches problems, a.batch_h per sequence):
-//   kKK_F32:   C fp32 = A B^T, both K-contiguous (scores, their gradient);
+//   kKK_F32:   C fp32 = A B^T, both K-contiguous (scores);
+//   kKK_DSOFTMAX: the same product (dP), epilogue kSoftmaxGrad (dS over P);
 //   kKMN_BF16: C bf16, A K-contiguous, B MN-contiguous (P V, dS K);
 //   kMNMN_BF16: C bf16, both MN-contiguous (P^T dO, dS^T Q).
-enum AttnGemm { kKK_F32 = 0, kKMN_BF16 = 1, kMNMN_BF16 = 2 };
+enum AttnGemm { kKK_F32 = 0, kKMN_BF16 = 1, kMNMN_BF16 = 2, kKK_DSOFTMAX = 3 };
 void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st);
 
 }  // namespace qat
