@@ -80,13 +80,9 @@ void launch_pick(const GemmArgs& a, hipStream_t st) {
 // of 32 (GM 1) and groups that tile BN (GM 2: 128, or a short whole row) are
 // stored directly; whole rows wider than BN (GM 3) are accumulated per tile
 // into ds and dz, zero-filled here first.
-// The weight-updating epilogue (kSteAdam) holds W, m and v of the next step
-// in registers: 256x256 tiles run with 4 waves (512 registers each), which
-// leaves room for them; 8 waves would spill.
 template <int EP, int NB, int GM>
 void launch_pick_grads_gm(const GemmArgs& a, hipStream_t st) {
-  constexpr int WGN = EP == kSteAdam ? 2 : 4;
-  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, WGN, kMNContig, kMNContig, EP, NB, GM>(a, st);
+  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kMNContig, kMNContig, EP, NB, GM>(a, st);
   else launch_bf16<128, 128, 4, 2, 2, kMNContig, kMNContig, EP, NB, GM>(a, st);
 }
 

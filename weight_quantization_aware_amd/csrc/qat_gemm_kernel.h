@@ -484,20 +484,25 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
     }
   } else {
     // Rows are weight rows o (A = dY^T), columns inputs c (B = X^T). Steps
-    // t = (i, g) walk the lane's rows and 64-column chunks; the loads of step
-    // t + 1 are issued before step t is computed.
-    constexpr int NG = WN / 64, NT = TI * NG;
+    // t = (i, g, half) walk the lane's rows, 64-column chunks and, for the
+    // weight-updating epilogue, the chunk's two halves (jj 0-1, 2-3: W, m and
+    // v of one half-step fit beside the accumulators of 8-wave tiles); the
+    // loads of step t + 1 are issued before step t is computed.
+    constexpr int NG = WN / 64;
+    constexpr int JJ = EP == kSteAdam ? 2 : 4;           // 16-column quarters per step
+    constexpr int HS = 4 / JJ;                           // steps per chunk
+    constexpr int NT = TI * NG * HS;
     constexpr int NH = GM == 1 ? 2 : 1;                  // groups per chunk
     const FastDiv gdiv = FastDiv::make((uint32_t)a.group);
-    auto row_of = [&](int t) { return m0 + wm0 + (t / NG) * 16 + rl; };
-    auto col_of = [&](int t) { return n0 + wn0 + (t % NG) * 64; };
+    auto row_of = [&](int t) { return m0 + wm0 + (t / (NG * HS)) * 16 + rl; };
+    auto col_of = [&](int t) { return n0 + wn0 + ((t / HS) % NG) * 64; };
     auto group_of = [&](int o, int cg) -> int64_t {     // first group of the chunk at column cg
       if constexpr (GM == 0) return (int64_t)o * a.G + cg / 64;
       else if constexpr (GM == 1) return (int64_t)o * a.G + cg / 32;
       else return (int64_t)o * a.G + gdiv.div((uint32_t)cg);
     };
     auto load = [&](int t, EpiIn<EP>& in) {
-      const int o = row_of(t), cg = col_of(t);
+      const int o = row_of(t), cg = col_of(t), q0 = (t % HS) * JJ;
       if (o < a.M && cg < a.N) {
         const int64_t gi = group_of(o, cg);
 #pragma unroll
@@ -506,29 +511,32 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
           in.z[h] = a.z[gi + h];
         }
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int u = 0; u < JJ; ++u) {
+          const int jj = q0 + u;
           const int64_t wi = (int64_t)o * a.ldw + cg + jj * 16 + cq;
-          if constexpr (is_ste(EP)) in.w[jj] = *(const float4*)(a.W + wi);
-          else in.c[jj] = codes4<NB>(a.Wq + (int64_t)o * a.ldq, cg + jj * 16 + cq);
+          if constexpr (is_ste(EP)) in.w[u] = *(const float4*)(a.W + wi);
+          else in.c[u] = codes4<NB>(a.Wq + (int64_t)o * a.ldq, cg + jj * 16 + cq);
           if constexpr (EP == kSteAdam) {
-            in.m[jj] = *(const float4*)(a.mW + wi);
-            in.v[jj] = *(const float4*)(a.vW + wi);
+            in.m[u] = *(const float4*)(a.mW + wi);
+            in.v[u] = *(const float4*)(a.vW + wi);
           }
         }
       }
     };
     EpiIn<EP> cur, nxt;
     load(0, cur);
+    float ps[NH], pz[NH];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t + 1 < NT) load(t + 1, nxt);
-      const int i = t / NG, g = t % NG;
+      const int i = t / (NG * HS), g = (t / HS) % NG, q0 = (t % HS) * JJ;
       const int o = row_of(t), cg = col_of(t);
       const bool ok = o < a.M && cg < a.N;
       const int64_t gi = ok ? group_of(o, cg) : 0;
-      float ps[NH], pz[NH];
+      if (t % HS == 0) {
 #pragma unroll
-      for (int h = 0; h < NH; ++h) ps[h] = pz[h] = 0.f;
+        for (int h = 0; h < NH; ++h) ps[h] = pz[h] = 0.f;
+      }
       if (ok) {
         if constexpr (is_ste(EP)) {
           float zr[NH], rcp[NH];
@@ -538,10 +546,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
             rcp[h] = 1.0f / cur.s[h];
           }
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
+          for (int u = 0; u < JJ; ++u) {
+            const int jj = q0 + u;
             const int h = NH == 2 ? (jj >> 1) : 0;
             const f32x4 gw = acc[g * 4 + jj][i];
-            const float wv[4] = {cur.w[jj].x, cur.w[jj].y, cur.w[jj].z, cur.w[jj].w};
+            const float wv[4] = {cur.w[u].x, cur.w[u].y, cur.w[u].z, cur.w[u].w};
             float dw[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -554,8 +563,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
             if (a.dW) *(float4*)(a.dW + wi) = make_float4(dw[0], dw[1], dw[2], dw[3]);
             if constexpr (EP == kSteAdam) {
               // AdamW (the multi-tensor kernel's arithmetic) on the masked gradient
-              float mv[4] = {cur.m[jj].x, cur.m[jj].y, cur.m[jj].z, cur.m[jj].w};
-              float vv[4] = {cur.v[jj].x, cur.v[jj].y, cur.v[jj].z, cur.v[jj].w};
+              float mv[4] = {cur.m[u].x, cur.m[u].y, cur.m[u].z, cur.m[u].w};
+              float vv[4] = {cur.v[u].x, cur.v[u].y, cur.v[u].z, cur.v[u].w};
               float pv[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
@@ -572,17 +581,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
           }
         } else {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
+          for (int u = 0; u < JJ; ++u) {
+            const int jj = q0 + u;
             const int h = NH == 2 ? (jj >> 1) : 0;
             const f32x4 gw = acc[g * 4 + jj][i];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float qv = (float)((cur.c[jj] >> (NB * r)) & ((1u << NB) - 1));
+              const float qv = (float)((cur.c[u] >> (NB * r)) & ((1u << NB) - 1));
               ps[h] += gw[r] * (qv - cur.z[h]);
               pz[h] += gw[r];
             }
           }
         }
+      }
+      if (t % HS != HS - 1) {                            // the chunk's sums continue in its next step
+        cur = nxt;
+        continue;
       }
       // the 4 lanes with the same (lane & 15) hold the 4 column quarters of the chunk
 #pragma unroll
