@@ -111,6 +111,11 @@ GEMV_CASES = [
     (5, 4096, 4096, 64, 2),
     (2, 1000, 2880, 64, 4),    # 2880 = 11 super-steps + 64: waves with 1 and 2 chunks, tail lanes
     (16, 512, 4096, None, 4),
+    # X larger than LDS: staged chunk by chunk (4096 inputs per chunk)
+    (16, 100, 8512, 64, 3),    # 3 chunks, the last one 320 inputs (a ragged 256-input slice)
+    (12, 700, 6144, 32, 2),    # groups of 32, one and a half chunks
+    (16, 48, 12288, None, 4),  # channel-wise, 3 full chunks
+    (16, 8200, 4160, 64, 2),   # 2 or 3 row blocks per workgroup, ragged rows, a 64-input last chunk
 ]
 
 
@@ -172,6 +177,26 @@ def test_deploy_gemv_full_size_sampled(model, name, M, bits):
     z = synth.e2e_zeros(7, bits, out, inp, bits)
     s16, zq = O.deploy_qparams(s, z, bits)
     X = synth.activations_f16(7, bits, M, inp, outlier_channels=8)
+    Y = torch.empty(M, out, dtype=torch.float16, device="cuda")
+    Q.qat_deploy_gemv(dev_u16(X).view(torch.float16), dev_u8(Wq), dev_u16(s16).view(torch.float16), dev_u8(zq),
+                      bits, Y)
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([[0, out - 1], g.choice(np.arange(1, out - 1), 62, replace=False)]))
+    check_y(host_u16(Y)[:, rows], X, Wq, s16, zq, inp, bits, 64, rows=rows)
+
+
+def test_deploy_gemv_x_in_registers_sampled():
+    # M = 16 with so many rows that a workgroup's accumulators no longer fit
+    # beside an X chunk: X stays in registers (the remaining path), checked on
+    # sampled rows
+    M, out, inp, bits = 16, 36000, 4096, 2
+    say(f"deploy gemv x-in-registers M={M} out={out} in={inp} bits={bits}")
+    g = np.random.default_rng(12)
+    Wq = synth.packed_codes(8, bits, out, inp, bits)
+    s = synth.e2e_scales(8, bits, out, inp)
+    z = synth.e2e_zeros(8, bits, out, inp, bits)
+    s16, zq = O.deploy_qparams(s, z, bits)
+    X = synth.activations_f16(8, bits, M, inp, outlier_channels=8)
     Y = torch.empty(M, out, dtype=torch.float16, device="cuda")
     Q.qat_deploy_gemv(dev_u16(X).view(torch.float16), dev_u8(Wq), dev_u16(s16).view(torch.float16), dev_u8(zq),
                       bits, Y)

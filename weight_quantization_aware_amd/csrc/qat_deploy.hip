@@ -561,6 +561,175 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The inference linear when X [M][in] is too large for LDS (several tokens on
+// a wide input, e.g. M = 16 at in = 8192): persistent workgroups of 16 waves
+// stage X one chunk of 4096 inputs at a time, and a workgroup takes every
+// chunk for all of its row blocks (row blocks b, b + grid, ...), so X crosses
+// L2 once per workgroup rather than once per 16 rows. In a chunk, wave w takes
+// the 256 inputs w * 256 .. + 255 (in-chunk lane mapping of the kernels
+// above) for 16 rows; the 16 waves' partial sums of a row block meet in LDS
+// behind a barrier and are added, in wave order, to the row block's fp32
+// accumulator; after the last chunk the accumulators are rounded once to
+// fp16. Each token's row of the X chunk sits at a stride of 4096 + 8 halves:
+// the 16 tokens of a fragment read fall on distinct banks. Inputs beyond `in`
+// are staged as zeros and multiply the last valid codes (adds exactly 0).
+// Code loads run two jobs ahead of the math, across row blocks and chunks.
+// ---------------------------------------------------------------------------
+constexpr int kXC = 4096;                                // inputs per X chunk: 16 waves x 256
+constexpr int kXStride = kXC + 8;                        // halves per token row in LDS
+
+struct XChunkLds {
+  int part, yacc, qp, total;
+  __host__ __device__ static XChunkLds of(int M, int my_rb) {
+    XChunkLds l;
+    l.part = M * kXStride * 2;                           // X chunk [M][kXStride] fp16 at 0
+    l.yacc = l.part + 16 * 16 * M * 4;                   // partials [16 waves][16 rows][M] fp32
+    l.qp = l.yacc + my_rb * 16 * M * 4;                  // accumulators [my_rb][16 rows][M] fp32
+    l.total = l.qp + 16 * 2 * 16 * 16;                   // step-size / zero-point pieces [16 waves][32][16 B]
+    return l;
+  }
+};
+
+template <int N>
+__global__ __launch_bounds__(1024) void k_deploy_gemv_xchunk(const GemvArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t dsm[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int kq = lane >> 4, r16 = lane & 15;
+  const int tok = min(r16, a.M - 1);
+  const FastDiv gdiv = FastDiv::make((uint32_t)a.group);
+  const int nch = (a.K + 255) / 256;                     // 256-input chunks
+  const int nxc = (a.K + kXC - 1) / kXC;                 // X chunks
+  const int nrb = (a.out + 15) / 16;
+  const int my_rb = (nrb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // grid <= nrb
+  const int njobs = nxc * my_rb;                         // the same sequence for every wave
+  const XChunkLds L = XChunkLds::of(a.M, my_rb);
+  const _Float16* xl = (const _Float16*)dsm;
+  float* part = (float*)(dsm + L.part);
+  float* yacc = (float*)(dsm + L.yacc);
+  uint8_t* slot = dsm + L.qp + wave * (2 * 16 * 16);
+
+  // job j: X chunk j / my_rb, row block (j % my_rb); chunk c of 256 inputs
+  auto job_rb = [&](int j) __attribute__((always_inline)) { return (int)blockIdx.x + (j % my_rb) * (int)gridDim.x; };
+  auto job_c = [&](int j) __attribute__((always_inline)) { return (j / my_rb) * 16 + wave; };
+
+  // step sizes and zero points of a chunk by one 16-byte piece per lane (as in
+  // the kernel above, one row tile)
+  const uint32_t s_size = (uint32_t)(a.out * a.G * 2), z_size = (uint32_t)(a.out * a.ldz);
+  auto piece_start = [&](uint32_t first, uint32_t size) __attribute__((always_inline)) { return min(first & ~3u, size - 16u); };
+  auto load = [&](CodeChunks<N, 1>& b, int j) __attribute__((always_inline)) {
+    j = min(j, njobs - 1);                               // past the last job: re-read it
+    const int rb = job_rb(j), c = min(job_c(j), nch - 1);
+    const int g_first = (int)gdiv.div((uint32_t)(c * 256));
+    const int row = min(rb * 16 + r16, a.out - 1);
+    const bool sp = lane < 16;
+    const uint32_t src = sp ? piece_start((uint32_t)(row * a.G + g_first) * 2u, s_size)
+                            : piece_start((uint32_t)(row * a.ldz) + ((uint32_t)g_first * N >> 3), z_size);
+    b.q = *(const uint4*)((sp ? (const uint8_t*)a.s16 : a.zq) + src);
+    const int k0 = c * 256 + 64 * kq;
+    load_codes<N>(a, row, k0 < a.K ? k0 : a.K - 64, b.c[0]);
+    asm volatile("" ::: "memory");                       // keep the prefetch ahead of the math
+  };
+  const DqConst k = dq_const<N>();
+  auto compute = [&](const CodeChunks<N, 1>& bc, int j, f32x4& acc) __attribute__((always_inline)) {
+    const int rb = job_rb(j), c = job_c(j);
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c >= nch) return;                                // wave-uniform: no chunk for this wave here
+    const int k0 = c * 256 + 64 * kq;
+    const int kl = k0 < a.K ? k0 : a.K - 64;
+    const int g_first = (int)gdiv.div((uint32_t)(c * 256));
+    const int g0 = (int)gdiv.div((uint32_t)kl);
+    if (lane < 32) *(uint4*)(slot + 16 * lane) = bc.q;   // read back below by this wave only
+    const int row = min(rb * 16 + r16, a.out - 1);
+    const uint32_t s0 = piece_start((uint32_t)(row * a.G + g_first) * 2u, s_size);
+    const uint32_t z0 = piece_start((uint32_t)(row * a.ldz) + ((uint32_t)g_first * N >> 3), z_size);
+    const uint8_t* sp = slot + r16 * 16;
+    const uint32_t* zp = (const uint32_t*)(slot + (16 + r16) * 16);
+    uint32_t zc[2], sc[2];
+    auto decode = [&](int g, uint32_t& zcv, uint32_t& scv) __attribute__((always_inline)) {
+      const uint32_t sbits = *(const uint16_t*)(sp + ((uint32_t)(row * a.G + g) * 2u - s0));
+      const int bit = (int)(((uint32_t)(row * a.ldz) - z0) * 8u + (uint32_t)(g * N));
+      const int w = bit >> 5;
+      const uint64_t zw = (uint64_t)zp[w] | ((uint64_t)zp[min(w + 1, 3)] << 32);
+      const uint32_t zv = (uint32_t)(zw >> (bit & 31)) & ((1u << N) - 1);
+      zcv = (0xE400u | zv) * 0x00010001u;
+      scv = sbits * 0x00010001u;
+    };
+    decode(g0, zc[0], sc[0]);
+    if (a.group == 32) {                                 // wave-uniform: the chunk's second group
+      decode(g0 + 1, zc[1], sc[1]);
+    } else {
+      zc[1] = zc[0];
+      sc[1] = sc[0];
+    }
+    const _Float16* xr = xl + tok * kXStride + (k0 - (j / my_rb) * kXC);   // zeros past `in`
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const h8 B = *(const h8*)(xr + 8 * t);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_step<N>(bc.c[0], t, k, zc, sc), B, acc, 0, 0, 0);
+    }
+  };
+
+  CodeChunks<N, 1> b0, b1;
+  load(b0, 0);
+  load(b1, 1);
+  for (int e = threadIdx.x; e < my_rb * 16 * a.M; e += 1024) yacc[e] = 0.f;
+  const i32x4 rsrc = buffer_rsrc(a.X, (int64_t)a.M * a.K * 2);
+  const uint32_t xbase = lds_addr_of(dsm);
+  // one row block of job j (buffer bc): partials, sum in wave order, prefetch
+  auto step = [&](CodeChunks<N, 1>& bc, int j) __attribute__((always_inline)) {
+    f32x4 acc;
+    compute(bc, j, acc);
+    load(bc, j + 2);
+    if (r16 < a.M) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(wave * 16 + 4 * kq + r) * a.M + r16] = acc[r];
+    }
+    lds_barrier();
+    float* ya = yacc + (j % my_rb) * 16 * a.M;
+    for (int e = threadIdx.x; e < 16 * a.M; e += 1024) {
+      float sum = ya[e];
+      for (int w = 0; w < 16; ++w) sum += part[w * 16 * a.M + e];
+      ya[e] = sum;
+    }
+    lds_barrier();                                       // partials free again
+  };
+  for (int xc = 0; xc < nxc; ++xc) {
+    // stage X chunk xc: token m's row in 8 instructions of 1 KiB; inputs past
+    // `in` are moved out of the buffer's range and land as zeros
+    for (int i = wave; i < a.M * 8; i += 16) {
+      const int m = i >> 3, q = i & 7;
+      const int col = xc * kXC + q * 512 + 8 * lane;     // input index (multiples of 8)
+      const uint32_t src = col < a.K ? (uint32_t)((m * a.K + col) * 2) : 0x7FFFFFF0u;
+      dma16(rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)(xbase + (uint32_t)(m * kXStride * 2 + q * 1024))),
+            src);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int j0 = xc * my_rb;
+    int i = 0;
+    for (; i + 1 < my_rb; i += 2) {                      // buffers alternate with the job index
+      if (((j0 + i) & 1) == 0) {
+        step(b0, j0 + i);
+        step(b1, j0 + i + 1);
+      } else {
+        step(b1, j0 + i);
+        step(b0, j0 + i + 1);
+      }
+    }
+    if (i < my_rb) {
+      if (((j0 + i) & 1) == 0) step(b0, j0 + i);
+      else step(b1, j0 + i);
+    }
+  }
+  for (int e = threadIdx.x; e < my_rb * 16 * a.M; e += 1024) {
+    const int rbi = e / (16 * a.M), rem = e - rbi * 16 * a.M;
+    const int r = rem / a.M, m = rem - r * a.M;
+    const int o = ((int)blockIdx.x + rbi * (int)gridDim.x) * 16 + r;
+    if (o < a.out) a.Y[(int64_t)m * a.out + o] = __builtin_bit_cast(uint16_t, (_Float16)yacc[e]);
+  }
+}
+
 }  // namespace
 
 void launch_deploy_qparams(const float* s, const float* z, int64_t out, int64_t in, int group, int bits,
@@ -609,6 +778,17 @@ void launch_lds(const GemvArgs& a, int64_t nrb, int lds, hipStream_t st) {
   hipLaunchKernelGGL((k_deploy_gemv_lds<N, RW, NB>), grid, dim3(1024), (size_t)lds, st, a);
 }
 
+template <int N>
+void launch_xchunk(const GemvArgs& a, int64_t grid, int lds, hipStream_t st) {
+  static bool raised = false;                            // allow more than 64 KiB of dynamic LDS, once
+  if (!raised) {
+    (void)hipFuncSetAttribute((const void*)k_deploy_gemv_xchunk<N>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsLimit);
+    raised = true;
+  }
+  hipLaunchKernelGGL((k_deploy_gemv_xchunk<N>), dim3((unsigned)grid), dim3(1024), (size_t)lds, st, a);
+}
+
 }  // namespace
 
 void launch_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s16, const uint8_t* zq, int64_t M,
@@ -645,6 +825,17 @@ void launch_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s1
     if (bits == 2) launch_lds<2, kRW, nb>(a, nrb, (int)lds, st);
     else if (bits == 3) launch_lds<3, kRW, nb>(a, nrb, (int)lds, st);
     else launch_lds<4, kRW, nb>(a, nrb, (int)lds, st);
+    return;
+  }
+  // X too large for LDS: stage it chunk by chunk when the accumulators of one
+  // workgroup's row blocks fit beside a chunk; otherwise X stays in registers.
+  const int64_t rb16 = (out + 15) / 16;
+  const int64_t gx = rb16 < num_cus() ? rb16 : num_cus();
+  const int64_t xlds = XChunkLds::of((int)M, (int)((rb16 + gx - 1) / gx)).total;
+  if (xlds <= kLdsLimit && qp_fits) {
+    if (bits == 2) launch_xchunk<2>(a, gx, (int)xlds, st);
+    else if (bits == 3) launch_xchunk<3>(a, gx, (int)xlds, st);
+    else launch_xchunk<4>(a, gx, (int)xlds, st);
     return;
   }
   const dim3 grid((unsigned)((out + 15) / 16));
