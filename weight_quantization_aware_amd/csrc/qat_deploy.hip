@@ -294,8 +294,9 @@ __global__ __launch_bounds__(512, 2) void k_deploy_gemv(const GemvArgs a) {
 //
 // X reaches LDS once per workgroup, by direct-to-LDS loads issued after the
 // wave's first code loads so that both are in flight together. Each token's
-// row sits at a stride of lds_x_stride(in) halves, whole KiB with at least 192
-// inputs of zeros after the row: a lane whose chunk lies beyond `in` (the
+// row takes lds_x_stride(in) halves, whole KiB with at least 192 inputs of
+// zeros after the row, and rows are 16 bytes further apart than that
+// (lds_x_pitch: the tokens of one fragment read on distinct banks): a lane whose chunk lies beyond `in` (the
 // ragged last chunk) reads those zeros as X and the last valid chunk as codes,
 // so it adds exactly 0 without any masking.
 //
@@ -315,6 +316,9 @@ __global__ __launch_bounds__(512, 2) void k_deploy_gemv(const GemvArgs a) {
 // for code loads wait for it: one counter covers both).
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int lds_x_stride(int K) { return ((K * 2 + 384 + 1023) / 1024) * 512; }
+// Halves between two token rows in LDS: the row plus 16 bytes, so that the
+// tokens of one fragment read (lane & 15) fall on distinct banks.
+__host__ __device__ inline int lds_x_pitch(int K) { return lds_x_stride(K) + 8; }
 
 // LDS layout of the kernel below (byte offsets; the same on host and device).
 struct DeployLds {
@@ -322,7 +326,7 @@ struct DeployLds {
   __host__ __device__ static DeployLds of(int M, int K, int my_rb, int RW, int NB = 3) {
     DeployLds l;
     auto up = [](int v) { return (v + 1023) / 1024 * 1024; };
-    l.part = M * lds_x_stride(K) * 2;
+    l.part = M * lds_x_pitch(K) * 2;
     l.cnt = l.part + up(my_rb * 16 * RW * 16 * M * 4);
     l.ybuf = l.cnt + up(my_rb * 4);
     l.qp = l.ybuf + up(my_rb * M * RW * 16 * 2);
@@ -373,7 +377,8 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
   const FastDiv gdiv = FastDiv::make((uint32_t)a.group);
   const int nch = (a.K + 255) / 256;
   const int nbusy = min(nch, 16);                        // waves with chunks
-  const int xs = lds_x_stride(a.K);                      // halves per token row in LDS
+  const int xs = lds_x_stride(a.K);                      // halves of a token row in LDS (data and zeros)
+  const int xp = lds_x_pitch(a.K);                       // halves from one token row to the next
   const _Float16* xl = (const _Float16*)dsm;
   const int nrb = (a.out + 16 * RW - 1) / (16 * RW);
   const int my_rb = (nrb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // grid <= nrb
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
       const int m = i / per_row, j = i - m * per_row;
       const int col = j * 1024 + 16 * lane;              // byte within the row
       const uint32_t src = col < a.K * 2 ? (uint32_t)(m * a.K * 2 + col) : 0x7FFFFFF0u;
-      dma16(rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + 1024u * i)), src);
+      dma16(rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + (uint32_t)(m * xp * 2 + j * 1024))), src);
     }
   }
   for (int i = threadIdx.x; i < my_rb; i += 1024) cnt[i] = 0;
@@ -491,7 +496,7 @@ __global__ __launch_bounds__(1024) void k_deploy_gemv_lds(const GemvArgs a) {
         sc[i][1] = sc[i][0];
       }
     }
-    const _Float16* xr = xl + tok * xs + k0;             // zeros past `in`
+    const _Float16* xr = xl + tok * xp + k0;             // zeros past `in`
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const h8 B = *(const h8*)(xr + 8 * t);
@@ -818,7 +823,7 @@ void launch_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s1
   const int64_t grid1 = nrb < num_cus() ? nrb : num_cus();
   const int64_t my_rb = (nrb + grid1 - 1) / grid1;
   constexpr int nb = 2;
-  const int64_t xbytes = M * (int64_t)lds_x_stride((int)in) * 2;
+  const int64_t xbytes = M * (int64_t)lds_x_pitch((int)in) * 2;
   const int64_t lds = xbytes > kLdsLimit ? xbytes : DeployLds::of((int)M, (int)in, (int)my_rb, kRW, nb).total;
   const bool qp_fits = out * (in / group) * 2 >= 16 && out * a.ldz >= 16;   // one 16-byte piece per buffer
   if (lds <= kLdsLimit && qp_fits) {
