@@ -438,24 +438,44 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
                                               int wm0, int wn0, int lane, float* red) {
   const int rl = lane & 15, cq = 4 * (lane >> 4);
   if constexpr (EP == kSoftmaxGrad) {
-    // dS = escale P (dP - D[row]) over P, 4 consecutive columns per lane
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int row = m0 + wm0 + i * 16 + rl;
-      if (row >= a.M) continue;
-      const float dr = a.Dvec[row];
+    // dS = escale P (dP - D[row]) over P, 4 consecutive columns per lane. The
+    // P values and D of the next 16-row step are in flight while this one is
+    // computed (the contraction is short, so these loads set the pace).
+    struct Row {
+      uint2 p[TJ];
+      float d;
+    };
+    auto load_row = [&](int i, Row& r) {
+      const int row = min(m0 + wm0 + i * 16 + rl, a.M - 1);
+      r.d = a.Dvec[row];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const int col = n0 + wn0 + j * 16 + cq;
-        if (col < a.N) {
-          uint2* pp = (uint2*)(a.C + (int64_t)row * a.ldc + col);
-          const uint2 pb = *pp;
-          const float p0 = __builtin_bit_cast(float, pb.x << 16), p1 = __builtin_bit_cast(float, pb.x & 0xFFFF0000u);
-          const float p2 = __builtin_bit_cast(float, pb.y << 16), p3 = __builtin_bit_cast(float, pb.y & 0xFFFF0000u);
-          *pp = make_uint2(pack_bf16x2(a.escale * p0 * (acc[j][i][0] - dr), a.escale * p1 * (acc[j][i][1] - dr)),
+        const int col = min(n0 + wn0 + j * 16 + cq, a.N - 4);
+        r.p[j] = *(const uint2*)(a.C + (int64_t)row * a.ldc + col);
+      }
+    };
+    Row cur, nxt;
+    load_row(0, cur);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      if (i + 1 < TI) load_row(i + 1, nxt);
+      const int row = m0 + wm0 + i * 16 + rl;
+      if (row < a.M) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int col = n0 + wn0 + j * 16 + cq;
+          if (col < a.N) {
+            const uint2 pb = cur.p[j];
+            const float dr = cur.d;
+            const float p0 = __builtin_bit_cast(float, pb.x << 16), p1 = __builtin_bit_cast(float, pb.x & 0xFFFF0000u);
+            const float p2 = __builtin_bit_cast(float, pb.y << 16), p3 = __builtin_bit_cast(float, pb.y & 0xFFFF0000u);
+            *(uint2*)(a.C + (int64_t)row * a.ldc + col) =
+                make_uint2(pack_bf16x2(a.escale * p0 * (acc[j][i][0] - dr), a.escale * p1 * (acc[j][i][1] - dr)),
                            pack_bf16x2(a.escale * p2 * (acc[j][i][2] - dr), a.escale * p3 * (acc[j][i][3] - dr)));
+          }
         }
       }
+      cur = nxt;
     }
   } else if constexpr (EP == kStoreF32) {
 #pragma unroll
