@@ -31,8 +31,6 @@ constexpr float kRmsEps = 1e-5f;
 constexpr double kRopeBase = 10000.0;
 constexpr int kHeadDim = 128;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
-
 __device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
