@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqat.so")
 SOURCES = ["qat_api.hip", "qat_elementwise.hip", "qat_gemm.hip", "qat_deploy.hip", "qat_block.hip",
-           "qat_timing.hip", "qat_peaks.hip"]
+           "qat_attn.hip", "qat_timing.hip", "qat_peaks.hip"]
 ARCH = os.environ.get("QAT_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -1,0 +1,240 @@
+// Causal attention forward of the Block-AP step, fused (gfx950): for one
+// (sequence, head) problem and a block of 128 queries, the scores of each
+// 64-key block are formed by MFMA, folded into a running softmax (row max and
+// sum in registers) and multiplied into the output by MFMA without leaving
+// registers; only O (bf16) and the log-sum-exp of every row (fp32, base 2)
+// reach memory. The backward recomputes the probabilities from the log-sum-
+// exp in the epilogue of its score product (kSoftmaxProbs).
+//
+// Sources: the block is Llama-2's (causal softmax attention scaled by
+// 1/sqrt(128)); see qat_block.hip.
+//
+// Layout. 256 threads = 4 waves; wave w owns queries q0 + 32 w .. + 31 as two
+// 16-row tiles. MFMA v_mfma_f32_16x16x32_bf16 with the B operand first, so a
+// lane holds 4 consecutive columns of one row (16-row tile row lane & 15,
+// columns 4 (lane >> 4) + 0..3 of a 16-column tile).
+//   S = Q K^T: Q fragments (row, 8 consecutive d) from global, kept for the
+//   whole loop; K fragments from the LDS key block.
+//   O += P V: the probabilities of key tiles 2 ks and 2 ks + 1 form the A
+//   fragment of k-step ks as they sit in registers (the lane's keys 32 ks + 4 g
+//   + 0..3 and 32 ks + 16 + 4 g + 0..3, g = lane >> 4); the V fragment takes
+//   the same keys by two transposing LDS reads (ds_read_b64_tr_b16).
+// LDS: two buffers of the K and V blocks [64 keys][128 d] bf16 (256-byte
+// rows); 16-byte chunk c of key row k sits at c ^ (k & 15), so both the K
+// fragment reads and the V transposing reads use every bank equally.
+#include "qat_device.h"
+#include "qat_dma.h"
+#include "qat_internal.h"
+
+namespace qat {
+namespace {
+
+constexpr int kHD = 128;             // head size
+constexpr int kBQ = 128;             // queries per workgroup
+constexpr int kBK = 64;              // keys per block
+constexpr int kRowBytes = kHD * 2;   // 256
+constexpr int kTileBytes = kBK * kRowBytes;               // 16 KiB per K or V block
+
+__device__ __forceinline__ int swz(int k, int c) { return (c ^ (k & 15)) << 4; }
+
+struct AttnArgs {
+  const uint16_t* q;                 // [B*T][H] bf16 (after RoPE)
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;                       // [B*T][H] bf16
+  float* lse;                        // [B*nh][T] fp32, log2 units
+  int T, H, nh, batches;
+  float scale_log2;                  // log2(e) / sqrt(128)
+};
+
+__global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kTileBytes];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  // (query block, problem), all blocks of one problem on one XCD when the
+  // problem count is a multiple of 8, longest (last) query blocks first
+  const int nqb = (int)gridDim.x;
+  int qb = blockIdx.x, prob = blockIdx.y;
+  if ((a.batches & 7) == 0) {
+    const int w = blockIdx.x + blockIdx.y * nqb;
+    const int r = w % (8 * nqb);
+    prob = 8 * (w / (8 * nqb)) + (r & 7);
+    qb = nqb - 1 - (r >> 3);
+  }
+  const int b = prob / a.nh, h = prob - b * a.nh;
+  const int64_t tok0 = (int64_t)b * a.T;
+  const int q0 = qb * kBQ;
+  // key blocks up to the diagonal (T is a multiple of 64; a ragged last query
+  // block has rows past T, whose loads re-read row T - 1 and which are not stored)
+  const int nkb = min((q0 + kBQ - 1) / kBK + 1, a.T / kBK);
+
+  // K and V blocks by DMA: instruction j of a wave moves 4 rows (1 KiB); lane
+  // l lands at row 4 (4 w + j) + l / 16, position l % 16, and fetches the
+  // logical chunk that position holds
+  const i32x4 rk = buffer_rsrc(a.k + tok0 * a.H + h * kHD, ((int64_t)(a.T - 1) * a.H + kHD) * 2);
+  const i32x4 rv = buffer_rsrc(a.v + tok0 * a.H + h * kHD, ((int64_t)(a.T - 1) * a.H + kHD) * 2);
+  const uint32_t lds0 = lds_addr_of(smem);
+  uint32_t voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * (4 * wave + j) + (lane >> 4);
+    const int chunk = (lane & 15) ^ (row & 15);
+    voff[j] = (uint32_t)(row * a.H * 2 + chunk * 16);
+  }
+  auto issue = [&](int kb, int buf) {
+    kb = min(kb, nkb - 1);                               // past the last block: re-load it (uniform counts)
+    const uint32_t base = lds0 + (uint32_t)(buf * 2 * kTileBytes);
+    const uint32_t koff = (uint32_t)(kb * kBK * a.H * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + (uint32_t)((4 * wave + j) * 1024)));
+      dma16(rk, dst, voff[j] + koff);
+      dma16(rv, dst + kTileBytes, voff[j] + koff);
+    }
+  };
+
+  // Q fragments: rows q0 + 32 w + 16 i + r16, d = 32 ks + 8 g .. + 7
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint16_t* qr = a.q + (tok0 + min(q0 + 32 * wave + 16 * i + r16, a.T - 1)) * a.H + h * kHD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[i][ks] = *(const bf16x8*)(qr + 32 * ks);
+  }
+  issue(0, 0);
+  issue(1, 1);
+
+  f32x4 o[8][2];
+#pragma unroll
+  for (int jd = 0; jd < 8; ++jd)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) o[jd][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  const int qrow0 = q0 + 32 * wave + r16;                // query of this lane in tile i: qrow0 + 16 i
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    wait_vmcnt<8>();                                     // this wave's DMA of block kb has landed
+    __syncthreads();                                     // ... and everyone's
+    const uint8_t* kt = smem + (kb & 1) * 2 * kTileBytes;
+    const uint8_t* vt = kt + kTileBytes;
+    // S = Q K^T for 64 keys: s[jt][i][r] = S[q of tile i][key 16 jt + 4 g + r]
+    f32x4 s[4][2];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) s[jt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int key = 16 * jt + r16;
+        const bf16x8 kf = *(const bf16x8*)(kt + key * kRowBytes + swz(key, 4 * ks + g));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) s[jt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i][ks], s[jt][i], 0, 0, 0);
+      }
+    }
+    // running softmax over the block (rows of tile i: query qrow0 + 16 i)
+    const bool diag = kb * kBK + kBK - 1 > q0;            // the block reaches past the first query
+    bf16x8 pf[2][2];                                      // [i][ks]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = qrow0 + 16 * i;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = s[jt][i][r] * a.scale_log2;
+          if (diag && kb * kBK + 16 * jt + 4 * g + r > q) v = -INFINITY;
+          s[jt][i][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[i], mx);                   // finite: key 0 of block 0 is valid for every row
+      const float alpha = exp2f(m[i] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(s[jt][i][r] - mn);
+          s[jt][i][r] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      l[i] = l[i] * alpha + sum;
+      m[i] = mn;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[jd][i][r] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f32x4 lo = s[2 * ks][i], hi = s[2 * ks + 1][i];
+        pf[i][ks] = bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                           (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+      }
+    }
+    // O += P V: V fragment of d-tile jd and k-step ks = keys 32 ks + 4 g + 0..3
+    // and 32 ks + 16 + 4 g + 0..3 at d = 16 jd + r16 (two transposing reads;
+    // lane j of the 16-lane group addresses key k0 + j / 4, d 16 jd + 4 (j % 4))
+    typedef short i16x4_ __attribute__((ext_vector_type(4)));
+    const __attribute__((address_space(3))) uint8_t* vl = (const __attribute__((address_space(3))) uint8_t*)vt;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) {
+        const int d0 = 16 * jd + 4 * (r16 & 3);
+        const int ka = 32 * ks + 4 * g + (r16 >> 2), kc = ka + 16;
+        const i16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_*)(vl + ka * kRowBytes + swz(ka, d0 >> 3) + (d0 & 7) * 2));
+        const i16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_*)(vl + kc * kRowBytes + swz(kc, d0 >> 3) + (d0 & 7) * 2));
+        typedef short i16x8_ __attribute__((ext_vector_type(8)));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, (i16x8_)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) o[jd][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i][ks], o[jd][i], 0, 0, 0);
+      }
+    }
+    __syncthreads();                                     // every wave is done with this buffer
+    issue(kb + 2, kb & 1);
+  }
+  wait_vmcnt<0>();                                       // drain the trailing re-loads
+
+  // O / l to bf16; the log-sum-exp (base 2) of each row
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = qrow0 + 16 * i;
+    if (q >= a.T) continue;
+    const float inv = 1.0f / l[i];
+    uint16_t* orow = a.o + (tok0 + q) * a.H + h * kHD + 4 * g;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd)
+      *(uint2*)(orow + 16 * jd) = make_uint2(pack_bf16x2(o[jd][i][0] * inv, o[jd][i][1] * inv),
+                                             pack_bf16x2(o[jd][i][2] * inv, o[jd][i][3] * inv));
+    if (g == 0) a.lse[(int64_t)prob * a.T + q] = m[i] + __log2f(l[i]);
+  }
+}
+
+}  // namespace
+
+void launch_flash_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B, int T,
+                      int H, hipStream_t st) {
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.T = T;
+  a.H = H;
+  a.nh = H / kHD;
+  a.batches = B * a.nh;
+  a.scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
+  LaunchTimer t("attn_fwd", st);
+  hipLaunchKernelGGL(k_flash_fwd, dim3((unsigned)((T + kBQ - 1) / kBQ), (unsigned)a.batches), dim3(256), 0, st, a);
+}
+
+}  // namespace qat

@@ -13,10 +13,10 @@
 //
 // Memory-bound row kernels: one workgroup per token row for the norms (a row
 // of H <= 8192 values stays in registers between the reduction and the
-// write), one wave per score row for the softmax (a row of T <= 4096 scores
-// in registers), 16-byte vector accesses throughout. The softmax backward
-// runs in the epilogue of the dP product (kSoftmaxGrad) from a per-query row
-// term.
+// write), 16-byte vector accesses throughout. Attention: the forward is one
+// fused kernel (qat_attn.hip); the backward rebuilds P in the epilogue of the
+// score product (kSoftmaxProbs) and applies the softmax backward in the
+// epilogue of the dP product (kSoftmaxGrad) from a per-query row term.
 #include <math.h>
 #include <string.h>
 
@@ -208,60 +208,6 @@ __global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ q, uint16_t
 }
 
 // ---------------------------------------------------------------------------
-// Causal softmax over the scores of one query row (one wave per row): P[k] =
-// exp(scale S[k] - max) / sum for k <= q, 0 for q < k < the end of q's
-// 256-column block (the causal products read the row tile's diagonal block,
-// nothing beyond it).
-// Row index = problem * T + q. A lane holds columns 256 j + 4 lane .. + 3.
-// ---------------------------------------------------------------------------
-template <int NJ>
-__global__ __launch_bounds__(256) void k_softmax_fwd(const float* __restrict__ S, uint16_t* __restrict__ P,
-                                                      int64_t rows, int T, float scale) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const int q = (int)(row % T);
-  const float* s = S + row * T;
-  uint16_t* p = P + row * T;
-  float v[NJ][4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int c0 = 256 * j + 4 * lane;
-    if (c0 <= q && c0 < T) {
-      const float4 a = *(const float4*)(s + c0);
-      const float av[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[j][e] = c0 + e <= q ? av[e] * scale : -INFINITY;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[j][e] = -INFINITY;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[j][e]);
-  }
-  mx = wave_max(mx);                     // finite: column 0 is always valid
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[j][e] = __expf(v[j][e] - mx);    // exactly 0 for the masked -inf
-      sum += v[j][e];
-    }
-  const float inv = 1.0f / wave_sum(sum);
-  // zeros beyond the diagonal only as far as the causal products read them:
-  // up to the end of the 256-column block that holds q (row tiles are 128 or
-  // 256 tokens)
-  const int wend = min(T, (q / 256 + 1) * 256);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int c0 = 256 * j + 4 * lane;
-    if (c0 < wend)
-      *(uint2*)(p + c0) = make_uint2(pack_bf16x2(v[j][0] * inv, v[j][1] * inv), pack_bf16x2(v[j][2] * inv, v[j][3] * inv));
-  }
-}
-
 // Row term of the softmax backward: D[problem][q] = sum_k P[q][k] dP[q][k],
 // which equals dO[q] . O[q] (sum over k of P dP = dO . sum_k P v_k = dO . O),
 // from the attention output and its gradient (bf16 [B*T][H]). One thread per
@@ -487,7 +433,7 @@ int32_t check_shape(const qat_block_shape* s) {
 struct Ws {
   float2* rope;          // [T][64]
   uint16_t *h1, *q, *k, *v, *attn, *h2, *gate, *up, *a, *dy, *wh, *da, *dxg, *dxu, *dx2, *dattn, *dq, *dk, *dv;
-  float *S, *o, *x2, *dn, *r1, *r2, *partial, *D;
+  float *lse, *o, *x2, *dn, *r1, *r2, *partial, *D;
   uint16_t* P;
   size_t bytes;
 };
@@ -510,7 +456,7 @@ Ws ws_layout(const Dims& d, uint8_t* base) {
   w.q = (uint16_t*)take(th * 2);
   w.k = (uint16_t*)take(th * 2);
   w.v = (uint16_t*)take(th * 2);
-  w.S = (float*)take(sc * 4);
+  w.lse = (float*)take(d.B * d.nh * d.T * 4);
   w.P = (uint16_t*)take(sc * 2);
   w.attn = (uint16_t*)take(th * 2);
   w.o = (float*)take(th * 4);
@@ -634,18 +580,6 @@ void set_batch(GemmArgs& a, const Dims& d, View va, View vb, View vc) {
   a.sc_h = sh(vc);
 }
 
-void softmax_fwd(const Dims& d, const Ws& w, float scale, hipStream_t st) {
-  const int64_t rows = d.B * d.nh * d.T;
-  const int T = (int)d.T;
-  LaunchTimer t("softmax_fwd", st);
-  const dim3 grid((unsigned)blocks_of(rows, 4)), block(256);
-  if (T <= 256) hipLaunchKernelGGL(k_softmax_fwd<1>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else if (T <= 512) hipLaunchKernelGGL(k_softmax_fwd<2>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else if (T <= 1024) hipLaunchKernelGGL(k_softmax_fwd<4>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else if (T <= 2048) hipLaunchKernelGGL(k_softmax_fwd<8>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-  else hipLaunchKernelGGL(k_softmax_fwd<16>, grid, block, 0, st, w.S, w.P, rows, T, scale);
-}
-
 void rope(const Dims& d, uint16_t* q, uint16_t* k, const Ws& w, float sgn, hipStream_t st) {
   LaunchTimer t("rope", st);
   const int64_t n = 2 * d.BT * (d.H / 16);
@@ -657,7 +591,6 @@ void rope(const Dims& d, uint16_t* q, uint16_t* k, const Ws& w, float sgn, hipSt
 // backward reads.
 void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, const float* g2, const uint16_t* x,
                    const uint16_t* target, float* y, float* loss, const Ws& w, hipStream_t st) {
-  const float scale = 1.0f / sqrtf((float)kHeadDim);
   {
     LaunchTimer t("rope_table", st);
     hipLaunchKernelGGL(k_rope_table, dim3((unsigned)blocks_of(d.T * (kHeadDim / 2), 256)), dim3(256), 0, st,
@@ -672,38 +605,8 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
   fq_forward(d, L[QAT_BLOCK_K], QAT_BLOCK_K, w.h1, w.k, nullptr, w, st);
   fq_forward(d, L[QAT_BLOCK_V], QAT_BLOCK_V, w.h1, w.v, nullptr, w, st);
   rope(d, w.q, w.k, w, 1.0f, st);
-  {
-    // S = q k^T per (sequence, head), fp32
-    GemmArgs a = zero_args();
-    a.A = w.q;
-    a.lda = d.H;
-    a.B = w.k;
-    a.ldb = d.H;
-    a.M = a.N = (int)d.T;
-    a.K = kHeadDim;
-    a.Cf = w.S;
-    a.ldc = d.T;
-    a.causal = kCausalSkip;
-    set_batch(a, d, kTok, kTok, kScore);
-    launch_gemm_attn(a, kKK_F32, st);
-  }
-  softmax_fwd(d, w, scale, st);
-  {
-    // attn = P v: B[n = d][k = key] = v[key][d] (MN-contiguous)
-    GemmArgs a = zero_args();
-    a.A = w.P;
-    a.lda = d.T;
-    a.B = w.v;
-    a.ldb = d.H;
-    a.M = (int)d.T;
-    a.N = kHeadDim;
-    a.K = (int)d.T;
-    a.C = w.attn;
-    a.ldc = d.H;
-    a.causal = kCausalLower;
-    set_batch(a, d, kScore, kTok, kTok);
-    launch_gemm_attn(a, kKMN_BF16, st);
-  }
+  // causal attention, fused: attn and the rows' log-sum-exp (P is rebuilt in the backward)
+  launch_flash_fwd(w.q, w.k, w.v, w.attn, w.lse, (int)d.B, (int)d.T, (int)d.H, st);
   fq_forward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.attn, nullptr, w.o, w, st);
   {
     LaunchTimer t("rmsnorm_fwd", st);
@@ -746,6 +649,25 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
                        w.dx2, (int)d.H);
   }
   fq_backward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.dx2, w.attn, w.dattn, w, ac, st);
+  {
+    // P = exp2(S log2(e) / sqrt(128) - lse) from S = q k^T, bf16, causal tiles
+    GemmArgs a = zero_args();
+    a.A = w.q;
+    a.lda = d.H;
+    a.B = w.k;
+    a.ldb = d.H;
+    a.M = a.N = (int)d.T;
+    a.K = kHeadDim;
+    a.C = w.P;
+    a.ldc = d.T;
+    a.causal = kCausalSkip;
+    a.Dvec = w.lse;
+    a.sd_b = d.nh * d.T;
+    a.sd_h = d.T;
+    a.escale = 1.4426950408889634f * scale;
+    set_batch(a, d, kTok, kTok, kScore);
+    launch_gemm_attn(a, kKK_PROBS, st);
+  }
   {
     // dv = P^T dattn: A[m = key][k = query] = P[query][key], both MN-contiguous
     GemmArgs a = zero_args();

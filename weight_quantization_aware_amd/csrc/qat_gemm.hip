@@ -32,7 +32,9 @@ constexpr const char* gemm_label() {
   if (EP == kE2eScaleGrad) return "gemm_e2e_grads";
   if (BL == kFp32Quant) return "gemm_fwd_fused_fp32";
   if (BL == kPacked) return "gemm_fwd_packed";
-  if (NB == kTagAttn) return EP == kStoreF32 ? "attn_gemm_f32" : EP == kSoftmaxGrad ? "attn_gemm_dsoftmax" : "attn_gemm_bf16";
+  if (NB == kTagAttn)
+    return EP == kStoreF32 ? "attn_gemm_f32" : EP == kSoftmaxGrad ? "attn_gemm_dsoftmax"
+           : EP == kSoftmaxProbs ? "attn_gemm_probs" : "attn_gemm_bf16";
   if (EP == kStoreF32) return "gemm_fwd_f32";
   return NB == 1 ? "gemm_dx" : "gemm_fwd";
 }
@@ -117,7 +119,7 @@ void launch_grads(const GemmArgs& a, hipStream_t st) {
 // head-sized outputs, N = head_dim = 128).
 template <int AMN, int BMN, int EP>
 void launch_pick_attn(const GemmArgs& a, hipStream_t st) {
-  if constexpr (EP == kStoreF32 || EP == kSoftmaxGrad) {
+  if constexpr (EP == kStoreF32 || EP == kSoftmaxGrad || EP == kSoftmaxProbs) {
     if (a.N >= 256 && tiles(a, 256, 256) * batches(a) >= 256) {
       launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, kTagAttn>(a, st);
       return;
@@ -156,6 +158,7 @@ void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st) {
 void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st) {
   if (kind == kKK_F32) launch_pick_attn<kKContig, kKContig, kStoreF32>(a, st);
   else if (kind == kKK_DSOFTMAX) launch_pick_attn<kKContig, kKContig, kSoftmaxGrad>(a, st);
+  else if (kind == kKK_PROBS) launch_pick_attn<kKContig, kKContig, kSoftmaxProbs>(a, st);
   else if (kind == kKMN_BF16) launch_pick_attn<kKContig, kMNContig, kStoreBf16>(a, st);
   else launch_pick_attn<kMNContig, kMNContig, kStoreBf16>(a, st);
 }

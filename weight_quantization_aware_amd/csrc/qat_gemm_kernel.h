@@ -477,6 +477,24 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
       }
       cur = nxt;
     }
+  } else if constexpr (EP == kSoftmaxProbs) {
+    // P = exp2(escale S - lse[row]) for col <= row, 0 beyond
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = m0 + wm0 + i * 16 + rl;
+      if (row >= a.M) continue;
+      const float lr = a.Dvec[row];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn0 + j * 16 + cq;
+        if (col < a.N) {
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pv[r] = col + r <= row ? exp2f(a.escale * acc[j][i][r] - lr) : 0.0f;
+          *(uint2*)(a.C + (int64_t)row * a.ldc + col) = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+        }
+      }
+    }
   } else if constexpr (EP == kStoreF32) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {

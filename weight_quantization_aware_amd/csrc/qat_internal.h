@@ -100,6 +100,9 @@ struct GemmArgs {
   // kSoftmaxGrad: the product is dP = dO v^T of one attention problem and the
   // epilogue writes dS = escale P (dP - Dvec[row]) in bf16 over P (C, ldc),
   // the problem's P and Dvec at b * s?_b + h * s?_h (C offsets as above).
+  // kSoftmaxProbs: the product is S = q k^T and the epilogue writes the causal
+  // probabilities P = exp2(escale S - Dvec[row]) (Dvec: the rows' base-2
+  // log-sum-exp of escale S), 0 above the diagonal, in bf16 to C.
   const float* Dvec;
   int64_t sd_b, sd_h;
   float escale;
@@ -108,7 +111,8 @@ struct GemmArgs {
 enum Causal { kCausalNone = 0, kCausalSkip = 1, kCausalLower = 2, kCausalUpper = 3 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
-enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4, kSoftmaxGrad = 5 };
+enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4, kSoftmaxGrad = 5,
+           kSoftmaxProbs = 6 };
 enum Layout { kKContig = 0, kMNContig = 1 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
@@ -129,12 +133,18 @@ void launch_linear_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, in
                       uint16_t* dX, hipStream_t st);
 GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z, int64_t M,
                            int64_t out, int64_t in, int group, int bits);
+// Fused causal attention forward (qat_attn.hip): O [B*T][H] bf16 and the
+// rows' base-2 log-sum-exp lse [B*nh][T] of S / sqrt(128) from q, k, v
+// [B*T][H] bf16 (head size 128, T a multiple of 64).
+void launch_flash_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B, int T,
+                      int H, hipStream_t st);
 // Batched products of attention (a.batches problems, a.batch_h per sequence):
 //   kKK_F32:   C fp32 = A B^T, both K-contiguous (scores);
 //   kKK_DSOFTMAX: the same product (dP), epilogue kSoftmaxGrad (dS over P);
+//   kKK_PROBS: the same product (S), epilogue kSoftmaxProbs (P);
 //   kKMN_BF16: C bf16, A K-contiguous, B MN-contiguous (P V, dS K);
 //   kMNMN_BF16: C bf16, both MN-contiguous (P^T dO, dS^T Q).
-enum AttnGemm { kKK_F32 = 0, kKMN_BF16 = 1, kMNMN_BF16 = 2, kKK_DSOFTMAX = 3 };
+enum AttnGemm { kKK_F32 = 0, kKMN_BF16 = 1, kMNMN_BF16 = 2, kKK_DSOFTMAX = 3, kKK_PROBS = 4 };
 void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st);
 
 }  // namespace qat
