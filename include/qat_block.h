@@ -85,9 +85,9 @@ typedef struct qat_block_linear {
   float* W;        /* parameters: read by the step, then updated in place */
   float* s;
   float* z;
-  float* dW;       /* this step's gradients (outputs). dW may be NULL in a step with groups of
-                      64 or 128 (W's update then never materialises it); all three may be
-                      NULL in qat_block_forward */
+  float* dW;       /* this step's gradients (outputs). dW may be NULL in a step (W's update
+                      then never materialises it); all three may be NULL in
+                      qat_block_forward */
   float* ds;
   float* dz;
   float* m_W;      /* AdamW first and second moments (updated in place) */
@@ -133,9 +133,9 @@ int32_t qat_block_forward(const qat_block_shape* shape, const qat_block_linear* 
  * One Block-AP step: forward and loss (as qat_block_forward, before the
  * update), the straight-through backward into every linear's dW, ds, dz,
  * then AdamW on W, s, z and their moments. ds and dz are required; dW is
- * required at group 32 and optional at 64 and 128, where W's update is made
- * in the epilogue of its gradient product (same arithmetic). lin points to
- * QAT_BLOCK_LINEARS entries in the order of the enum above.
+ * optional: W's update is made in the epilogue of its gradient product, from
+ * the masked gradient in registers. lin points to QAT_BLOCK_LINEARS entries in
+ * the order of the enum above.
  */
 int32_t qat_block_ap_step(const qat_block_shape* shape, const qat_block_linear* lin, const float* g1,
                           const float* g2, const uint16_t* x, const uint16_t* target, const qat_block_adamw* opt,

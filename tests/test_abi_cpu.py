@@ -207,12 +207,12 @@ def test_block_validation():
     l4[0].m_W = X                                                  # a moment over the input
     assert step(lins=l4) == 8
     l5 = _block_args(sh)
-    l5[2].dW = None                                                # dW is optional at group 64 ...
+    l5[2].dW = None                                                # dW is optional at every group size
     assert step(lins=l5, ws=need - 256) == 6                       # (validation reaches the workspace check)
     sh32 = Q.block_shape(256, 2, 704, 192, 2, 2, 32)
     l5 = _block_args(sh32)
-    l5[2].dW = None                                                # ... but W's update reads it at group 32
-    assert step(shape=ctypes.byref(sh32), lins=l5) == 1
+    l5[2].dW = None
+    assert step(shape=ctypes.byref(sh32), lins=l5, ws=need - 256) == 6
     # the forward call needs only W, s, z but checks the same shapes and regions
     fwd = L.qat_block_forward(ctypes.byref(sh), _block_args(sh, step=False), G1, G2, X, T, Y, LOSS, WS, need - 1,
                               None)

@@ -246,10 +246,11 @@ def test_block_two_steps_and_schedule():
             check_update(after[i][key], params[n][key], p3[n][key], [g3[n][key]], (n, key, "late step"))
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[1]])
+@pytest.mark.parametrize("case", CASES)
 def test_block_step_without_dw_is_identical(case):
-    # groups of 64 and 128 update W in the gradient epilogue, so dW is optional:
-    # the step without it must leave every parameter and moment bit-identical
+    # W is updated in the gradient epilogue at every group size, so dW is
+    # optional: the step without it must leave every parameter and moment
+    # bit-identical
     sh, d, params = make(case)
     o = opt_dict(B.AdamW(), 0)
     a, b = GpuBlock(sh, d, params), GpuBlock(sh, d, params)

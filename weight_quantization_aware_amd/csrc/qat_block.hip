@@ -319,14 +319,14 @@ __global__ __launch_bounds__(256) void k_loss_final(const float* __restrict__ pa
 }
 
 // ---------------------------------------------------------------------------
-// AdamW over up to 21 tensors in one launch (the seven linears' s and z, and
-// their W where the gradient epilogue does not update it). Segment i covers blocks
+// AdamW over up to 14 tensors in one launch (the seven linears' s and z; each W
+// is updated in its gradient epilogue). Segment i covers blocks
 // [start[i], start[i + 1]); a thread updates 4 consecutive parameters of 16
 // per thread (4 float4 steps), all in fp32:
 //   p <- p decay; m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
 //   p <- p - step_size m / (sqrt(v) inv_sqrt_bc2 + eps).
 // ---------------------------------------------------------------------------
-constexpr int kAdamSegs = 3 * QAT_BLOCK_LINEARS;
+constexpr int kAdamSegs = 2 * QAT_BLOCK_LINEARS;
 constexpr int kAdamPerBlock = 256 * 16;
 
 struct AdamSeg {
@@ -514,21 +514,19 @@ void fq_forward(const Dims& d, const qat_block_linear& L, int li, const uint16_t
 }
 
 // One optimizer step's constants (host, double precision): learning rates
-// after the cosine schedule and the bias corrections of step t = k + 1.
-// fuse_w: W's update runs in its gradient epilogue (groups of 64 and 128);
-// otherwise in the multi-tensor kernel with s and z.
+// after the cosine schedule and the bias corrections of step t = k + 1. W's
+// update runs in its gradient epilogue; s and z go through the multi-tensor
+// kernel.
 struct AdamConst {
   double lr_w, lr_q, bc1, bc2;
   const qat_block_adamw* o;
-  bool fuse_w;
 };
 
-AdamConst adam_const(const qat_block_adamw& o, int group) {
+AdamConst adam_const(const qat_block_adamw& o) {
   const double pi = 3.14159265358979323846;
   const double c = (1.0 + cos(pi * (double)o.step / (double)o.total_steps)) / 2.0;
   const double t = (double)(o.step + 1);
-  return AdamConst{o.lr_weight * c, o.lr_quant * c, 1.0 - pow(o.beta1, t), 1.0 - pow(o.beta2, t), &o,
-                   group == 64 || group == 128};
+  return AdamConst{o.lr_weight * c, o.lr_quant * c, 1.0 - pow(o.beta1, t), 1.0 - pow(o.beta2, t), &o};
 }
 
 // Straight-through backward of linear li: dX (if requested) from W_hat^T
@@ -548,7 +546,7 @@ void fq_backward(const Dims& d, const qat_block_linear& L, int li, const uint16_
   a.dW = L.dW;
   a.ds = L.ds;
   a.dz = L.dz;
-  const bool fuse = ac && ac->fuse_w;
+  const bool fuse = ac != nullptr;
   if (fuse) {
     a.Wupd = L.W;
     a.mW = L.m_W;
@@ -749,8 +747,7 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
   fq_backward(d, L[QAT_BLOCK_V], QAT_BLOCK_V, w.dv, w.h1, nullptr, w, ac, st);
 }
 
-// AdamW on every linear's s and z, and on W unless its gradient epilogue
-// updated it.
+// AdamW on every linear's s and z (W was updated in its gradient epilogue).
 void adamw_rest(const Dims& d, const qat_block_linear* L, const AdamConst& ac, hipStream_t st) {
   const qat_block_adamw& o = *ac.o;
   AdamArgs a;
@@ -761,17 +758,13 @@ void adamw_rest(const Dims& d, const qat_block_linear* L, const AdamConst& ac, h
   a.eps = (float)o.eps;
   int nseg = 0, blk = 0;
   for (int i = 0; i < QAT_BLOCK_LINEARS; ++i) {
-    const int64_t nw = d.out[i] * d.in[i], ng = d.out[i] * (d.in[i] / d.group);
+    const int64_t ng = d.out[i] * (d.in[i] / d.group);
     struct {
       float *p, *g, *m, *v;
       int64_t n;
       double lr;
-      bool on;
-    } t3[3] = {{L[i].W, L[i].dW, L[i].m_W, L[i].v_W, nw, ac.lr_w, !ac.fuse_w},
-               {L[i].s, L[i].ds, L[i].m_s, L[i].v_s, ng, ac.lr_q, true},
-               {L[i].z, L[i].dz, L[i].m_z, L[i].v_z, ng, ac.lr_q, true}};
-    for (auto& e : t3) {
-      if (!e.on) continue;
+    } t2[2] = {{L[i].s, L[i].ds, L[i].m_s, L[i].v_s, ng, ac.lr_q}, {L[i].z, L[i].dz, L[i].m_z, L[i].v_z, ng, ac.lr_q}};
+    for (auto& e : t2) {
       AdamSeg& sg = a.seg[nseg];
       sg.p = e.p;
       sg.g = e.g;
@@ -826,7 +819,6 @@ int32_t check_args(const Dims& d, const qat_block_linear* L, const float* g1, co
     if (!l.W || !l.s || !l.z) return QAT_ERR_NULL;
     if (step && (!l.ds || !l.dz || !l.m_W || !l.v_W || !l.m_s || !l.v_s || !l.m_z || !l.v_z))
       return QAT_ERR_NULL;
-    if (step && !l.dW && d.group == 32) return QAT_ERR_NULL;   // W's update reads dW at this group size
     const void* all[] = {l.W, l.s, l.z, l.dW, l.ds, l.dz, l.m_W, l.v_W, l.m_s, l.v_s, l.m_z, l.v_z};
     for (const void* p : all)
       if (p && !al16(p)) return QAT_ERR_ALIGN;
@@ -894,7 +886,7 @@ QAT_API int32_t qat_block_ap_step(const qat_block_shape* shape, const qat_block_
   if (st != QAT_OK) return st;
   if (ws_bytes < ws_layout(d, nullptr).bytes) return QAT_ERR_WORKSPACE;
   const Ws w = ws_layout(d, (uint8_t*)ws);
-  const AdamConst ac = adam_const(*opt, d.group);
+  const AdamConst ac = adam_const(*opt);
   block_forward(d, lin, g1, g2, x, target, y, loss, w, stream);
   block_backward(d, lin, g2, w, &ac, stream);
   adamw_rest(d, lin, ac, stream);

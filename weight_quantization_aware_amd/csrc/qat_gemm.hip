@@ -88,11 +88,11 @@ void launch_pick_grads_gm(const GemmArgs& a, hipStream_t st) {
   else launch_bf16<128, 128, 4, 2, 2, kMNContig, kMNContig, EP, NB, GM>(a, st);
 }
 
-// The weight-updating epilogue exists for groups of 64 (GM 0) and 128 (GM 2);
-// the caller updates W separately at other group sizes.
+// The weight-updating epilogue streams whole 256-column tile rows (groups of
+// 32 to 256 columns that divide 256): always 256x256 tiles on 8 waves, also
+// for problems of fewer tiles than CUs.
 void launch_grads_adam(const GemmArgs& a, hipStream_t st) {
-  if (a.group == 64) launch_pick_grads_gm<kSteAdam, 0, 0>(a, st);
-  else launch_pick_grads_gm<kSteAdam, 0, 2>(a, st);
+  launch_bf16<256, 256, 2, 2, 4, kMNContig, kMNContig, kSteAdam, 0, 0>(a, st);
 }
 
 template <int EP, int NB>

@@ -405,9 +405,6 @@ __device__ __forceinline__ void mfma_drain() {
 //                  X^T); Gw = acc. dW = Gw * m and the group sums of ds, dz of
 //                  the straight-through estimator, from W, s, z re-quantised
 //                  here (quant_elem).
-//   kSteAdam:      kSteGrads, then AdamW on each weight from its masked
-//                  gradient: W, mW, vW updated in place (the elements of a
-//                  tile are read and written by that tile's epilogue only).
 //   kE2eScaleGrad: as above with packed codes: ds = sum Gw (q - z), dz = -s
 //                  sum Gw.
 // A 64-column quantisation group is 4 j-tiles x 4 registers of one lane plus a
@@ -418,12 +415,9 @@ __device__ __forceinline__ void mfma_drain() {
 template <int EP>
 struct EpiIn {
   float s[2], z[2];
-  float4 w[4];          // kSteGrads, kSteAdam: W[o][cg + 16 jj + cq .. + 3]
-  float4 m[4], v[4];    // kSteAdam: W's AdamW moments at the same positions
+  float4 w[4];          // kSteGrads: W[o][cg + 16 jj + cq .. + 3]
   uint32_t c[4];        // kE2eScaleGrad: the same four codes per jj
 };
-
-constexpr bool is_ste(int ep) { return ep == kSteGrads || ep == kSteAdam; }
 
 // Group modes of the gradient epilogues (GM): 0 groups of 64 columns, one per
 // chunk; 1 groups of 32, two per chunk (j-tiles 0-1 and 2-3); 2 groups of
@@ -522,25 +516,21 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
     }
   } else {
     // Rows are weight rows o (A = dY^T), columns inputs c (B = X^T). Steps
-    // t = (i, g, half) walk the lane's rows, 64-column chunks and, for the
-    // weight-updating epilogue, the chunk's two halves (jj 0-1, 2-3: W, m and
-    // v of one half-step fit beside the accumulators of 8-wave tiles); the
-    // loads of step t + 1 are issued before step t is computed.
+    // t = (i, g) walk the lane's rows and 64-column chunks; the loads of step
+    // t + 1 are issued before step t is computed.
     constexpr int NG = WN / 64;
-    constexpr int JJ = EP == kSteAdam ? 2 : 4;           // 16-column quarters per step
-    constexpr int HS = 4 / JJ;                           // steps per chunk
-    constexpr int NT = TI * NG * HS;
+    constexpr int NT = TI * NG;
     constexpr int NH = GM == 1 ? 2 : 1;                  // groups per chunk
     const FastDiv gdiv = FastDiv::make((uint32_t)a.group);
-    auto row_of = [&](int t) { return m0 + wm0 + (t / (NG * HS)) * 16 + rl; };
-    auto col_of = [&](int t) { return n0 + wn0 + ((t / HS) % NG) * 64; };
+    auto row_of = [&](int t) { return m0 + wm0 + (t / NG) * 16 + rl; };
+    auto col_of = [&](int t) { return n0 + wn0 + (t % NG) * 64; };
     auto group_of = [&](int o, int cg) -> int64_t {     // first group of the chunk at column cg
       if constexpr (GM == 0) return (int64_t)o * a.G + cg / 64;
       else if constexpr (GM == 1) return (int64_t)o * a.G + cg / 32;
       else return (int64_t)o * a.G + gdiv.div((uint32_t)cg);
     };
     auto load = [&](int t, EpiIn<EP>& in) {
-      const int o = row_of(t), cg = col_of(t), q0 = (t % HS) * JJ;
+      const int o = row_of(t), cg = col_of(t);
       if (o < a.M && cg < a.N) {
         const int64_t gi = group_of(o, cg);
 #pragma unroll
@@ -549,34 +539,26 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
           in.z[h] = a.z[gi + h];
         }
 #pragma unroll
-        for (int u = 0; u < JJ; ++u) {
-          const int jj = q0 + u;
-          const int64_t wi = (int64_t)o * a.ldw + cg + jj * 16 + cq;
-          if constexpr (is_ste(EP)) in.w[u] = *(const float4*)(a.W + wi);
-          else in.c[u] = codes4<NB>(a.Wq + (int64_t)o * a.ldq, cg + jj * 16 + cq);
-          if constexpr (EP == kSteAdam) {
-            in.m[u] = *(const float4*)(a.mW + wi);
-            in.v[u] = *(const float4*)(a.vW + wi);
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          if constexpr (EP == kSteGrads) in.w[jj] = *(const float4*)(a.W + (int64_t)o * a.ldw + cg + jj * 16 + cq);
+          else in.c[jj] = codes4<NB>(a.Wq + (int64_t)o * a.ldq, cg + jj * 16 + cq);
         }
       }
     };
     EpiIn<EP> cur, nxt;
     load(0, cur);
-    float ps[NH], pz[NH];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t + 1 < NT) load(t + 1, nxt);
-      const int i = t / (NG * HS), g = (t / HS) % NG, q0 = (t % HS) * JJ;
+      const int i = t / NG, g = t % NG;
       const int o = row_of(t), cg = col_of(t);
       const bool ok = o < a.M && cg < a.N;
       const int64_t gi = ok ? group_of(o, cg) : 0;
-      if (t % HS == 0) {
+      float ps[NH], pz[NH];
 #pragma unroll
-        for (int h = 0; h < NH; ++h) ps[h] = pz[h] = 0.f;
-      }
+      for (int h = 0; h < NH; ++h) ps[h] = pz[h] = 0.f;
       if (ok) {
-        if constexpr (is_ste(EP)) {
+        if constexpr (EP == kSteGrads) {
           float zr[NH], rcp[NH];
 #pragma unroll
           for (int h = 0; h < NH; ++h) {
@@ -584,11 +566,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
             rcp[h] = 1.0f / cur.s[h];
           }
 #pragma unroll
-          for (int u = 0; u < JJ; ++u) {
-            const int jj = q0 + u;
+          for (int jj = 0; jj < 4; ++jj) {
             const int h = NH == 2 ? (jj >> 1) : 0;
             const f32x4 gw = acc[g * 4 + jj][i];
-            const float wv[4] = {cur.w[u].x, cur.w[u].y, cur.w[u].z, cur.w[u].w};
+            const float wv[4] = {cur.w[jj].x, cur.w[jj].y, cur.w[jj].z, cur.w[jj].w};
             float dw[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -599,42 +580,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
             }
             const int64_t wi = (int64_t)o * a.ldw + cg + jj * 16 + cq;
             if (a.dW) *(float4*)(a.dW + wi) = make_float4(dw[0], dw[1], dw[2], dw[3]);
-            if constexpr (EP == kSteAdam) {
-              // AdamW (the multi-tensor kernel's arithmetic) on the masked gradient
-              float mv[4] = {cur.m[u].x, cur.m[u].y, cur.m[u].z, cur.m[u].w};
-              float vv[4] = {cur.v[u].x, cur.v[u].y, cur.v[u].z, cur.v[u].w};
-              float pv[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float pe = wv[r] * a.adam_decay;
-                mv[r] = a.adam_b1 * mv[r] + (1.0f - a.adam_b1) * dw[r];
-                vv[r] = a.adam_b2 * vv[r] + (1.0f - a.adam_b2) * dw[r] * dw[r];
-                const float den = sqrtf(vv[r]) * a.adam_isbc2 + a.adam_eps;
-                pv[r] = pe - a.adam_step * (mv[r] / den);
-              }
-              *(float4*)(a.Wupd + wi) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-              *(float4*)(a.mW + wi) = make_float4(mv[0], mv[1], mv[2], mv[3]);
-              *(float4*)(a.vW + wi) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-            }
           }
         } else {
 #pragma unroll
-          for (int u = 0; u < JJ; ++u) {
-            const int jj = q0 + u;
+          for (int jj = 0; jj < 4; ++jj) {
             const int h = NH == 2 ? (jj >> 1) : 0;
             const f32x4 gw = acc[g * 4 + jj][i];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float qv = (float)((cur.c[u] >> (NB * r)) & ((1u << NB) - 1));
+              const float qv = (float)((cur.c[jj] >> (NB * r)) & ((1u << NB) - 1));
               ps[h] += gw[r] * (qv - cur.z[h]);
               pz[h] += gw[r];
             }
           }
         }
-      }
-      if (t % HS != HS - 1) {                            // the chunk's sums continue in its next step
-        cur = nxt;
-        continue;
       }
       // the 4 lanes with the same (lane & 15) hold the 4 column quarters of the chunk
 #pragma unroll
@@ -683,6 +642,107 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
           atomicAdd(a.ds + gi, S);
           if (a.dz) atomicAdd(a.dz + gi, dz);
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kSteAdam epilogue, row by row. Once the main loop has drained, the LDS is
+// free: the accumulators of one wave-row of the tile (WM rows x 256 columns,
+// fp32, 128 KiB at 256x256) are written there, then every wave takes whole
+// rows, one 16-byte column quad per lane, so that each access to W, m, v (and
+// dW) is one contiguous KiB of the row and PF rows of loads are in flight per
+// wave. A group of 32, 64, 128 or 256 columns is 8, 16, 32 or 64 lanes, whose
+// s and z sums meet by lane shuffles. Column quad c of staged row r sits at
+// quad c ^ 4 (r & 3): the 16 rows x 4 quads of one accumulator write then
+// cover every bank four times, and a row read is a permutation of one row.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int TI, int TJ, int WN>
+__device__ __forceinline__ void ste_adam_rows(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
+                                              int wm0, int wn0, int lane, float* lds) {
+  static_assert(BN == 256, "a row of the tile is one 16-byte quad per lane");
+  constexpr int WM = TI * 16, WGM = BM / WM, NWAVE = WGM * (BN / WN), RPW = WM / NWAVE;
+  constexpr int PF = 3;                                  // rows of loads in flight per wave
+  static_assert(RPW * NWAVE == WM && RPW >= PF, "the staged rows split evenly over the waves");
+  const int wave = threadIdx.x >> 6;
+  const int col = n0 + 4 * lane;
+  const bool col_ok = col < a.N;
+  const int gl = a.group >> 2;                           // lanes per group
+  const int64_t gcol = col_ok ? (int64_t)FastDiv::make((uint32_t)a.group).div((uint32_t)col) : 0;
+  struct RowIn {
+    float4 w, m, v;
+    float s, z;
+  };
+#pragma unroll
+  for (int h = 0; h < WGM; ++h) {
+    const int row0 = m0 + h * WM;
+    auto load = [&](int k, RowIn& in) {
+      const int o = row0 + k * NWAVE + wave;
+      if (o < a.M && col_ok) {
+        const int64_t wi = (int64_t)o * a.ldw + col, gi = (int64_t)o * a.G + gcol;
+        in.w = *(const float4*)(a.W + wi);
+        in.m = *(const float4*)(a.mW + wi);
+        in.v = *(const float4*)(a.vW + wi);
+        in.s = a.s[gi];
+        in.z = a.z[gi];
+      }
+    };
+    RowIn buf[PF];                                       // the first rows' loads fly during the staging
+#pragma unroll
+    for (int k = 0; k < PF; ++k) load(k, buf[k]);
+    __syncthreads();                                     // every read of the previous phase's rows is done
+    if (wm0 == h * WM) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int r = 16 * i + (lane & 15), c = (wn0 >> 2) + 4 * j + (lane >> 4);
+          *(f32x4*)&lds[r * BN + ((c ^ ((r & 3) << 2)) << 2)] = acc[j][i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const RowIn cur = buf[k % PF];
+      if (k + PF < RPW) load(k + PF, buf[k % PF]);
+      const int r = k * NWAVE + wave, o = row0 + r;
+      const bool ok = o < a.M && col_ok;
+      const f32x4 gw = *(const f32x4*)&lds[r * BN + ((lane ^ ((r & 3) << 2)) << 2)];
+      float ps = 0.f, pz = 0.f;
+      if (ok) {
+        const float zr = round_clamp_zero(cur.z, a.Kq), rcp = 1.0f / cur.s;
+        const float wv[4] = {cur.w.x, cur.w.y, cur.w.z, cur.w.w};
+        float mv[4] = {cur.m.x, cur.m.y, cur.m.z, cur.m.w};
+        float vv[4] = {cur.v.x, cur.v.y, cur.v.z, cur.v.w};
+        float dw[4], pv[4];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const QElem e = quant_elem_rcp(wv[e4], cur.s, rcp, zr, a.Kq);
+          dw[e4] = e.m ? gw[e4] : 0.0f;
+          ps += gw[e4] * (e.m ? (__builtin_rintf(e.u) - e.u) : (e.q - zr));
+          pz += e.m ? 0.0f : gw[e4];
+          // AdamW (the multi-tensor kernel's arithmetic) on the masked gradient
+          const float pe = wv[e4] * a.adam_decay;
+          mv[e4] = a.adam_b1 * mv[e4] + (1.0f - a.adam_b1) * dw[e4];
+          vv[e4] = a.adam_b2 * vv[e4] + (1.0f - a.adam_b2) * dw[e4] * dw[e4];
+          const float den = sqrtf(vv[e4]) * a.adam_isbc2 + a.adam_eps;
+          pv[e4] = pe - a.adam_step * (mv[e4] / den);
+        }
+        const int64_t wi = (int64_t)o * a.ldw + col;
+        if (a.dW) *(float4*)(a.dW + wi) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+        *(float4*)(a.Wupd + wi) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        *(float4*)(a.mW + wi) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+        *(float4*)(a.vW + wi) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+      }
+      for (int off = 1; off < gl; off <<= 1) {
+        ps += __shfl_xor(ps, off);
+        pz += __shfl_xor(pz, off);
+      }
+      if (ok && (lane & (gl - 1)) == 0 && a.ds) {
+        const int64_t gi = (int64_t)o * a.G + gcol;
+        a.ds[gi] = ps;
+        if (a.dz) a.dz[gi] = -cur.s * pz;
       }
     }
   }
@@ -841,7 +901,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   wait_vmcnt<0>();                                       // drain the trailing re-loads
   __syncthreads();
   mfma_drain();
-  gemm_epilogue<EP, NB, GM, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, (float*)smem);
+  if constexpr (EP == kSteAdam) {
+    static_assert(BM / WGM * BN * 4 <= STAGES * STAGE, "LDS holds one wave-row of accumulators");
+    ste_adam_rows<BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, (float*)smem);
+  } else {
+    gemm_epilogue<EP, NB, GM, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, (float*)smem);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -121,7 +121,7 @@ void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 // Gradient GEMM over tokens, Gw = dY^T X with both operands MN-contiguous;
 // epi = kSteGrads (dW, ds, dz), kSteAdam (the same, and AdamW on W, m, v in
-// place; groups of 64 or 128 only) or kE2eScaleGrad (ds, dz).
+// place; groups of 32 to 256 that divide 256) or kE2eScaleGrad (ds, dz).
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st);
 // Forward-type GEMM on a staged bf16 W_hat with fp32 output (a.Cf).
 void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st);
