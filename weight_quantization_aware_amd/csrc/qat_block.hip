@@ -433,6 +433,7 @@ int32_t check_shape(const qat_block_shape* s) {
 struct Ws {
   float2* rope;          // [T][64]
   uint16_t *h1, *q, *k, *v, *attn, *h2, *gate, *up, *a, *dy, *wh, *da, *dxg, *dxu, *dx2, *dattn, *dq, *dk, *dv;
+  uint16_t* whk[QAT_BLOCK_LINEARS];   // W_hat kept from the forward for the dX products (o, gate, up, down)
   float *lse, *o, *x2, *dn, *r1, *r2, *partial, *D;
   uint16_t* P;
   size_t bytes;
@@ -449,8 +450,8 @@ Ws ws_layout(const Dims& d, uint8_t* base) {
     return p;
   };
   const int64_t th = d.BT * d.H, ti = d.BT * d.I, sc = d.B * d.nh * d.T * d.T;
-  int64_t wmax = 0;
-  for (int i = 0; i < QAT_BLOCK_LINEARS; ++i) wmax = d.out[i] * d.in[i] > wmax ? d.out[i] * d.in[i] : wmax;
+  int64_t wmax = 0;                                      // the staging buffer of q, k and v
+  for (int i = QAT_BLOCK_Q; i <= QAT_BLOCK_V; ++i) wmax = d.out[i] * d.in[i] > wmax ? d.out[i] * d.in[i] : wmax;
   w.rope = (float2*)take(d.T * (kHeadDim / 2) * 8);
   w.h1 = (uint16_t*)take(th * 2);
   w.q = (uint16_t*)take(th * 2);
@@ -471,6 +472,8 @@ Ws ws_layout(const Dims& d, uint8_t* base) {
   w.dy = (uint16_t*)take(th * 2);
   w.partial = (float*)take(mse_blocks(d) * 4);
   w.wh = (uint16_t*)take(wmax * 2);
+  for (int i = 0; i < QAT_BLOCK_LINEARS; ++i)
+    w.whk[i] = i >= QAT_BLOCK_O ? (uint16_t*)take(d.out[i] * d.in[i] * 2) : nullptr;
   w.da = (uint16_t*)take(ti * 2);
   w.dxg = (uint16_t*)take(th * 2);
   w.dxu = (uint16_t*)take(th * 2);
@@ -490,15 +493,18 @@ GemmArgs zero_args() {
   return a;
 }
 
-// Y = X W_hat^T with W_hat staged as bf16 [out][in] in ws.wh; bf16 or fp32 out.
+// Y = X W_hat^T with W_hat staged as bf16 [out][in] (kept for the backward's
+// dX product where the linear has one, else in the shared ws.wh); bf16 or
+// fp32 out.
 void fq_forward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* X, uint16_t* Y, float* Yf,
                 const Ws& w, hipStream_t st) {
   const int64_t out = d.out[li], in = d.in[li];
-  launch_quant_codes(L.W, L.s, L.z, out, in, d.group, d.bits, nullptr, w.wh, st);
+  uint16_t* wh = w.whk[li] ? w.whk[li] : w.wh;
+  launch_quant_codes(L.W, L.s, L.z, out, in, d.group, d.bits, nullptr, wh, st);
   GemmArgs a = zero_args();
   a.A = X;
   a.lda = in;
-  a.B = w.wh;
+  a.B = wh;
   a.ldb = in;
   a.M = (int)d.BT;
   a.N = (int)out;
@@ -529,16 +535,26 @@ AdamConst adam_const(const qat_block_adamw& o) {
   return AdamConst{o.lr_weight * c, o.lr_quant * c, 1.0 - pow(o.beta1, t), 1.0 - pow(o.beta2, t), &o};
 }
 
-// Straight-through backward of linear li: dX (if requested) from W_hat^T
-// staged in ws.wh, and dW, ds, dz from the gradient GEMM's epilogue. With an
-// optimizer step (ac), the same epilogue also applies AdamW to W and its
-// moments; s and z are updated afterwards by k_adamw.
+// Straight-through backward of linear li: dX (if requested) from the W_hat
+// its forward staged, read in place, and dW, ds, dz from the gradient GEMM's
+// epilogue. With an optimizer step (ac), the same epilogue also applies AdamW
+// to W and its moments (W_hat is already staged, so the dX product does not
+// depend on the update's order); s and z are updated afterwards by k_adamw.
 void fq_backward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* dY, const uint16_t* X,
                  uint16_t* dX, const Ws& w, const AdamConst* ac, hipStream_t st) {
   const int64_t out = d.out[li], in = d.in[li];
   if (dX) {
-    launch_w_hat_t(L.W, L.s, L.z, out, in, d.group, d.bits, w.wh, st);
-    launch_linear_dx(dY, w.wh, d.BT, out, in, dX, st);
+    GemmArgs a = zero_args();
+    a.A = dY;
+    a.lda = out;
+    a.B = w.whk[li];
+    a.ldb = in;
+    a.M = (int)d.BT;
+    a.N = (int)in;
+    a.K = (int)out;
+    a.C = dX;
+    a.ldc = in;
+    launch_gemm_dx_mn(a, st);
   }
   GemmArgs a = linear_grads_args(dY, X, L.s, L.z, d.BT, out, in, d.group, d.bits);
   a.W = L.W;

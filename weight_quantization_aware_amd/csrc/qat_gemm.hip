@@ -167,6 +167,14 @@ void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {
   launch_pick<kKContig, kKContig, kStoreBf16, 1>(a, st);
 }
 
+// On the Llama-2-7B block's shapes W_hat read in place costs the same as a
+// staged W_hat^T; 8 waves also beyond K = 4096 (measured faster with this
+// loader at K = 11008).
+void launch_gemm_dx_mn(const GemmArgs& a, hipStream_t st) {
+  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kKContig, kMNContig, kStoreBf16, 1>(a, st);
+  else launch_bf16<128, 128, 4, 2, 2, kKContig, kMNContig, kStoreBf16, 1>(a, st);
+}
+
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st) {
   if (epi == kSteGrads) launch_grads<kSteGrads, 0>(a, st);
   else if (epi == kSteAdam) launch_grads_adam(a, st);

@@ -119,6 +119,8 @@ enum Layout { kKContig = 0, kMNContig = 1 };
 void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
 // dX = dY W_hat: A = dY [M][out], B = W_hat^T [in][out], both K-contiguous.
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
+// The same product on W_hat [out][in] read in place (B MN-contiguous, ldb = in).
+void launch_gemm_dx_mn(const GemmArgs& a, hipStream_t st);
 // Gradient GEMM over tokens, Gw = dY^T X with both operands MN-contiguous;
 // epi = kSteGrads (dW, ds, dz), kSteAdam (the same, and AdamW on W, m, v in
 // place; groups of 32 to 256 that divide 256) or kE2eScaleGrad (ds, dz).
