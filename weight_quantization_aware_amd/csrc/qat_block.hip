@@ -1,8 +1,9 @@
 // One Block-AP training step on a Llama-2 decoder block with seven
 // fake-quantised linears (gfx950): the row kernels of the block (RMSNorm,
-// rotary embedding, causal softmax, SiLU-gated product, mean-squared error),
-// the multi-tensor AdamW, and the launch sequence of the forward, the
-// straight-through backward and the update.
+// rotary embedding, the softmax-gradient row term, SiLU-gated product, the
+// loss sum), the multi-tensor AdamW, and the launch sequence of the forward,
+// the straight-through backward and the update. The output, the loss and its
+// gradient come from the epilogue of the down product (kResidMse).
 //
 // Sources: "EfficientQAT, low-bit training on a single GPU"
 // (modelfoundations.com), Phase 1 (Block-AP: block-wise MSE to the
@@ -269,41 +270,9 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(uint16_t* __restrict__ gate,
 }
 
 // ---------------------------------------------------------------------------
-// Output, loss and its gradient: y = x2 + o_down (fp32), d = y - target,
-// dy = bf16(d * 2 / n); one fp32 partial of sum d^2 per workgroup (2048
-// elements), summed in double by k_loss_final.
+// The loss: the down product's epilogue (kResidMse) leaves one fp32 partial
+// of sum (y - target)^2 per workgroup; one workgroup sums them in double.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_mse(const float* __restrict__ x2, const float* __restrict__ dn,
-                                              const uint16_t* __restrict__ target, float* __restrict__ y,
-                                              uint16_t* __restrict__ dy, float* __restrict__ partial, int64_t n8,
-                                              float two_over_n) {
-  __shared__ float red[4];
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  float ss = 0.f;
-  if (i < n8) {
-    float t[8], yv[8], d[8];
-    unpack8(((const uint4*)target)[i], t);
-    const float4 a0 = ((const float4*)x2)[2 * i], a1 = ((const float4*)x2)[2 * i + 1];
-    const float4 b0 = ((const float4*)dn)[2 * i], b1 = ((const float4*)dn)[2 * i + 1];
-    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      yv[e] = av[e] + bv[e];
-      const float df = yv[e] - t[e];
-      d[e] = df * two_over_n;
-      ss += df * df;
-    }
-    if (y) {
-      ((float4*)y)[2 * i] = make_float4(yv[0], yv[1], yv[2], yv[3]);
-      ((float4*)y)[2 * i + 1] = make_float4(yv[4], yv[5], yv[6], yv[7]);
-    }
-    ((uint4*)dy)[i] = pack8(d);
-  }
-  const float tot = block_sum(ss, red);
-  if (threadIdx.x == 0) partial[blockIdx.x] = tot;
-}
-
 __global__ __launch_bounds__(256) void k_loss_final(const float* __restrict__ partial, int nblk, double inv_n,
                                                      float* __restrict__ loss) {
   __shared__ double red[256];
@@ -434,12 +403,10 @@ struct Ws {
   float2* rope;          // [T][64]
   uint16_t *h1, *q, *k, *v, *attn, *h2, *gate, *up, *a, *dy, *wh, *da, *dxg, *dxu, *dx2, *dattn, *dq, *dk, *dv;
   uint16_t* whk[QAT_BLOCK_LINEARS];   // W_hat kept from the forward for the dX products (o, gate, up, down)
-  float *lse, *o, *x2, *dn, *r1, *r2, *partial, *D;
+  float *lse, *o, *x2, *r1, *r2, *partial, *D;
   uint16_t* P;
   size_t bytes;
 };
-
-int mse_blocks(const Dims& d) { return blocks_of(d.BT * d.H / 8, 256); }
 
 Ws ws_layout(const Dims& d, uint8_t* base) {
   Ws w;
@@ -468,9 +435,8 @@ Ws ws_layout(const Dims& d, uint8_t* base) {
   w.gate = (uint16_t*)take(ti * 2);
   w.up = (uint16_t*)take(ti * 2);
   w.a = (uint16_t*)take(ti * 2);
-  w.dn = (float*)take(th * 4);
   w.dy = (uint16_t*)take(th * 2);
-  w.partial = (float*)take(mse_blocks(d) * 4);
+  w.partial = (float*)take(gemm_fwd_max_workgroups(d.BT, d.H) * 4);
   w.wh = (uint16_t*)take(wmax * 2);
   for (int i = 0; i < QAT_BLOCK_LINEARS; ++i)
     w.whk[i] = i >= QAT_BLOCK_O ? (uint16_t*)take(d.out[i] * d.in[i] * 2) : nullptr;
@@ -493,11 +459,12 @@ GemmArgs zero_args() {
   return a;
 }
 
-// Y = X W_hat^T with W_hat staged as bf16 [out][in] (kept for the backward's
-// dX product where the linear has one, else in the shared ws.wh); bf16 or
-// fp32 out.
-void fq_forward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* X, uint16_t* Y, float* Yf,
-                const Ws& w, hipStream_t st) {
+// The forward product of linear li on X: W_hat staged as bf16 [out][in] (kept
+// for the backward's dX product where the linear has one, else in the shared
+// ws.wh), and the GEMM arguments of Y = X W_hat^T with the output left to the
+// caller.
+GemmArgs fq_forward_args(const Dims& d, const qat_block_linear& L, int li, const uint16_t* X, const Ws& w,
+                         hipStream_t st) {
   const int64_t out = d.out[li], in = d.in[li];
   uint16_t* wh = w.whk[li] ? w.whk[li] : w.wh;
   launch_quant_codes(L.W, L.s, L.z, out, in, d.group, d.bits, nullptr, wh, st);
@@ -510,6 +477,13 @@ void fq_forward(const Dims& d, const qat_block_linear& L, int li, const uint16_t
   a.N = (int)out;
   a.K = (int)in;
   a.ldc = out;
+  return a;
+}
+
+// Y = X W_hat^T, bf16 (Y) or fp32 (Yf) out.
+void fq_forward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* X, uint16_t* Y, float* Yf,
+                const Ws& w, hipStream_t st) {
+  GemmArgs a = fq_forward_args(d, L, li, X, w, st);
   if (Yf) {
     a.Cf = Yf;
     launch_gemm_fwd_f32(a, st);
@@ -535,11 +509,12 @@ AdamConst adam_const(const qat_block_adamw& o) {
   return AdamConst{o.lr_weight * c, o.lr_quant * c, 1.0 - pow(o.beta1, t), 1.0 - pow(o.beta2, t), &o};
 }
 
-// Straight-through backward of linear li: dX (if requested) from the W_hat
-// its forward staged, read in place, and dW, ds, dz from the gradient GEMM's
-// epilogue. With an optimizer step (ac), the same epilogue also applies AdamW
-// to W and its moments (W_hat is already staged, so the dX product does not
-// depend on the update's order); s and z are updated afterwards by k_adamw.
+// Straight-through backward of linear li: dX (if requested; q, k and v need
+// none) from the W_hat its forward staged, read in place, and dW, ds, dz from
+// the gradient GEMM's epilogue. With an optimizer step (ac), the same epilogue
+// also applies AdamW to W and its moments (W_hat is already staged, so the dX
+// product does not depend on the update's order); s and z are updated
+// afterwards by k_adamw.
 void fq_backward(const Dims& d, const qat_block_linear& L, int li, const uint16_t* dY, const uint16_t* X,
                  uint16_t* dX, const Ws& w, const AdamConst* ac, hipStream_t st) {
   const int64_t out = d.out[li], in = d.in[li];
@@ -634,14 +609,19 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
     const int64_t n8 = d.BT * d.I / 8;
     hipLaunchKernelGGL(k_swiglu_fwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.a, n8);
   }
-  fq_forward(d, L[QAT_BLOCK_DOWN], QAT_BLOCK_DOWN, w.a, nullptr, w.dn, w, st);
   {
-    LaunchTimer t("mse", st);
+    // down, with y = x2 + down, dy = 2 (y - target) / n and the loss partials in its epilogue
     const int64_t n = d.BT * d.H;
-    const int nb = mse_blocks(d);
-    hipLaunchKernelGGL(k_mse, dim3((unsigned)nb), dim3(256), 0, st, w.x2, w.dn, target, y, w.dy, w.partial, n / 8,
-                       (float)(2.0 / (double)n));
-    hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, st, w.partial, nb, 1.0 / (double)n, loss);
+    GemmArgs a = fq_forward_args(d, L[QAT_BLOCK_DOWN], QAT_BLOCK_DOWN, w.a, w, st);
+    a.Cf = y;
+    a.C = w.dy;
+    a.resid = w.x2;
+    a.target = target;
+    a.partial = w.partial;
+    a.escale = (float)(2.0 / (double)n);
+    const int64_t nb = launch_gemm_fwd_mse(a, st);
+    LaunchTimer t("loss", st);
+    hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, st, w.partial, (int)nb, 1.0 / (double)n, loss);
   }
 }
 

@@ -32,6 +32,7 @@ constexpr const char* gemm_label() {
   if (EP == kE2eScaleGrad) return "gemm_e2e_grads";
   if (BL == kFp32Quant) return "gemm_fwd_fused_fp32";
   if (BL == kPacked) return "gemm_fwd_packed";
+  if (EP == kResidMse) return "gemm_fwd_mse";
   if (NB == kTagAttn)
     return EP == kStoreF32 ? "attn_gemm_f32" : EP == kSoftmaxGrad ? "attn_gemm_dsoftmax"
            : EP == kSoftmaxProbs ? "attn_gemm_probs" : "attn_gemm_bf16";
@@ -66,15 +67,19 @@ void launch_fused(const GemmArgs& a, hipStream_t st) {
                      st, a);
 }
 
+// Returns the number of workgroups launched.
 template <int AMN, int BMN, int EP, int NB>
-void launch_pick(const GemmArgs& a, hipStream_t st) {
+int64_t launch_pick(const GemmArgs& a, hipStream_t st) {
   if (tiles(a, 256, 256) >= 256) {
     if (a.K <= 4096) launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, NB>(a, st);
     else launch_bf16<256, 256, 2, 2, 2, AMN, BMN, EP, NB>(a, st);
+    return tiles(a, 256, 256);
   } else if (tiles(a, 128, 256) >= 192) {
     launch_bf16<128, 256, 3, 2, 4, AMN, BMN, EP, NB>(a, st);
+    return tiles(a, 128, 256);
   } else {
     launch_bf16<128, 128, 4, 2, 2, AMN, BMN, EP, NB>(a, st);
+    return tiles(a, 128, 128);
   }
 }
 
@@ -174,6 +179,12 @@ void launch_gemm_dx_mn(const GemmArgs& a, hipStream_t st) {
   if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kKContig, kMNContig, kStoreBf16, 1>(a, st);
   else launch_bf16<128, 128, 4, 2, 2, kKContig, kMNContig, kStoreBf16, 1>(a, st);
 }
+
+int64_t launch_gemm_fwd_mse(const GemmArgs& a, hipStream_t st) {
+  return launch_pick<kKContig, kKContig, kResidMse, 0>(a, st);
+}
+
+int64_t gemm_fwd_max_workgroups(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
 void launch_gemm_grads(const GemmArgs& a, int epi, int bits, hipStream_t st) {
   if (epi == kSteGrads) launch_grads<kSteGrads, 0>(a, st);

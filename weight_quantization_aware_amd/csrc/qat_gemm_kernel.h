@@ -398,6 +398,8 @@ __device__ __forceinline__ void mfma_drain() {
 // Epilogues. acc[j][i] holds C[m0 + wm0 + 16 i + (lane & 15)][n0 + wn0 + 16 j
 // + 4 (lane >> 4) + r], r = 0..3.
 //   kStoreBf16:    C (bf16) = acc.
+//   kResidMse:     y = resid + acc, dy = bf16(escale (y - target)), and the
+//                  workgroup's sum of (y - target)^2.
 //   kStoreF32:     Cf (fp32) = acc.
 //   kSoftmaxGrad:  C (bf16, holding P) = escale P (acc - Dvec[row]): the
 //                  softmax backward of attention applied to dP = acc.
@@ -500,6 +502,65 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
         if (col < a.N)
           *(float4*)(a.Cf + (int64_t)row * a.ldc + col) = make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
       }
+    }
+  } else if constexpr (EP == kResidMse) {
+    // y = resid + product, d = y - target, dy = bf16(escale d), 4 consecutive
+    // columns per lane; resid and target of the next 16-row step are in flight
+    // while this one is computed (as in kSoftmaxGrad). Rows and columns beyond
+    // the problem are clamped for the loads and skipped for the stores.
+    struct Row {
+      uint2 t[TJ];
+      float4 r[TJ];
+    };
+    auto load_row = [&](int i, Row& r) {
+      const int row = min(m0 + wm0 + i * 16 + rl, a.M - 1);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int64_t at = (int64_t)row * a.ldc + min(n0 + wn0 + j * 16 + cq, a.N - 4);
+        r.t[j] = *(const uint2*)(a.target + at);
+        r.r[j] = *(const float4*)(a.resid + at);
+      }
+    };
+    float sq = 0.f;                                      // this lane's sum of d^2
+    Row cur, nxt;
+    load_row(0, cur);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      if (i + 1 < TI) load_row(i + 1, nxt);
+      const int row = m0 + wm0 + i * 16 + rl;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn0 + j * 16 + cq;
+        if (row >= a.M || col >= a.N) continue;
+        const int64_t at = (int64_t)row * a.ldc + col;
+        const uint2 tb = cur.t[j];
+        const float4 rv = cur.r[j];
+        const float t[4] = {__builtin_bit_cast(float, tb.x << 16), __builtin_bit_cast(float, tb.x & 0xFFFF0000u),
+                            __builtin_bit_cast(float, tb.y << 16), __builtin_bit_cast(float, tb.y & 0xFFFF0000u)};
+        const float y[4] = {rv.x + acc[j][i][0], rv.y + acc[j][i][1], rv.z + acc[j][i][2], rv.w + acc[j][i][3]};
+        float dd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dd[e] = y[e] - t[e];
+          sq += dd[e] * dd[e];
+        }
+        if (a.Cf) *(float4*)(a.Cf + at) = make_float4(y[0], y[1], y[2], y[3]);
+        *(uint2*)(a.C + at) = make_uint2(pack_bf16x2(a.escale * dd[0], a.escale * dd[1]),
+                                         pack_bf16x2(a.escale * dd[2], a.escale * dd[3]));
+      }
+      cur = nxt;
+    }
+    // the tile's sum over lanes (shuffles), then over the waves in wave order
+    // (LDS): the same partial from run to run
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
+    const int wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+    if (lane == 0) red[wave] = sq;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = 0.f;
+      for (int w = 0; w < nwave; ++w) t += red[w];
+      a.partial[blockIdx.x] = t;
     }
   } else if constexpr (EP == kStoreBf16) {
 #pragma unroll

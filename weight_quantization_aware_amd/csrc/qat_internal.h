@@ -106,13 +106,19 @@ struct GemmArgs {
   const float* Dvec;
   int64_t sd_b, sd_h;
   float escale;
+  // kResidMse: y = resid + product (fp32, [M][ldc]; stored to Cf when
+  // non-null), d = y - target (bf16 target), C = bf16(escale d), and one fp32
+  // partial of sum d^2 per workgroup at partial[blockIdx.x].
+  const float* resid;
+  const uint16_t* target;
+  float* partial;
 };
 
 enum Causal { kCausalNone = 0, kCausalSkip = 1, kCausalLower = 2, kCausalUpper = 3 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
 enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4, kSoftmaxGrad = 5,
-           kSoftmaxProbs = 6 };
+           kSoftmaxProbs = 6, kResidMse = 7 };
 enum Layout { kKContig = 0, kMNContig = 1 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
@@ -121,6 +127,11 @@ void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 // The same product on W_hat [out][in] read in place (B MN-contiguous, ldb = in).
 void launch_gemm_dx_mn(const GemmArgs& a, hipStream_t st);
+// The forward product (K-contiguous operands) with the kResidMse epilogue;
+// returns the number of workgroups launched (one loss partial each), at most
+// gemm_fwd_max_workgroups(M, N).
+int64_t launch_gemm_fwd_mse(const GemmArgs& a, hipStream_t st);
+int64_t gemm_fwd_max_workgroups(int64_t M, int64_t N);
 // Gradient GEMM over tokens, Gw = dY^T X with both operands MN-contiguous;
 // epi = kSteGrads (dW, ds, dz), kSteAdam (the same, and AdamW on W, m, v in
 // place; groups of 32 to 256 that divide 256) or kE2eScaleGrad (ds, dz).

@@ -42,6 +42,7 @@ LABELS = [
     (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*3,\s*5>", "attn_gemm_f32"),
     (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*5,\s*5>", "attn_gemm_dsoftmax"),
     (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*6,\s*5>", "attn_gemm_probs"),
+    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*7,\s*0>", "gemm_fwd_mse"),
     (r"k_attn_rowdot", "attn_rowdot"),
     (r"k_flash_fwd", "attn_fwd"),
     (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*0,\s*5>", "attn_gemm_bf16"),
@@ -71,7 +72,7 @@ LABELS = [
     (r"k_softmax_bwd", "softmax_bwd"),
     (r"k_swiglu_fwd", "swiglu_fwd"),
     (r"k_swiglu_bwd", "swiglu_bwd"),
-    (r"k_mse|k_loss_final", "mse"),
+    (r"k_loss_final", "loss"),
     (r"k_adamw", "adamw"),
     (r"k_fill_zero", "fill_zero"),
 ]
