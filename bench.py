@@ -132,10 +132,11 @@ def main():
     calls = [
         ("init", lambda: Q.qat_init_minmax(W, bits, s, z)),
         ("fq_fwd", lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=ws)),
-        ("fq_bwd", lambda: Q.qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=dX, dW=dW, ds=ds, dz=dz, ws=ws)),
+        # the backwards read the W_hat their forward left in ws (autograd's saved tensor)
+        ("fq_bwd", lambda: Q.qat_fakequant_linear_bwd_saved(dY, X, W, s, z, ws, bits, dX=dX, dW=dW, ds=ds, dz=dz)),
         ("pack", lambda: Q.qat_pack(W, s, z, bits, Wq, zp)),
         ("e2e_fwd", lambda: Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Y2, ws=ws)),
-        ("e2e_bwd", lambda: Q.qat_dequant_gemm_bwd_s(dY, X, Wq, s, zp, bits, ds2, dX=dX2, ws=ws)),
+        ("e2e_bwd", lambda: Q.qat_dequant_gemm_bwd_s_saved(dY, X, Wq, s, zp, ws, bits, ds2, dX=dX2)),
     ]
 
     stream = torch.cuda.current_stream(dev)
@@ -403,8 +404,8 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp,
 
         def fq(sg=sg, zg=zg, dsg=dsg, dzg=dzg, gsize=gsize):
             Q.qat_fakequant_linear_fwd(X, W, sg, zg, bits, Y2, ws=ws2, group=gsize)
-            Q.qat_fakequant_linear_bwd(dY, X, W, sg, zg, bits, dX=dX2, dW=dW2, ds=dsg, dz=dzg, ws=ws2,
-                                       group=gsize)
+            Q.qat_fakequant_linear_bwd_saved(dY, X, W, sg, zg, ws2, bits, dX=dX2, dW=dW2, ds=dsg, dz=dzg,
+                                             group=gsize)
         tg = ev_time(fq, 10)
         groups[gname] = {"ms": round(tg * 1e3, 4), "tflops": round(6.0 * M2 * in2 * out2 / tg / 1e12, 1)}
     del ws2, Y2, dX2, dW2
@@ -431,9 +432,9 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp,
         for lin, Wc, Xc, dYc, sc, zc in c3:
             o, i = lin.out, lin.inp
             Q.qat_fakequant_linear_fwd(Xc, Wc, sc, zc, lin.bits, Y3[:M3 * o].view(M3, o), ws=ws3)
-            Q.qat_fakequant_linear_bwd(dYc, Xc, Wc, sc, zc, lin.bits, dX=dX3[:M3 * i].view(M3, i),
-                                       dW=dW3[:o * i].view(o, i), ds=ds3[:o * (i // 64)].view(o, i // 64),
-                                       dz=dz3[:o * (i // 64)].view(o, i // 64), ws=ws3)
+            Q.qat_fakequant_linear_bwd_saved(dYc, Xc, Wc, sc, zc, ws3, lin.bits, dX=dX3[:M3 * i].view(M3, i),
+                                             dW=dW3[:o * i].view(o, i), ds=ds3[:o * (i // 64)].view(o, i // 64),
+                                             dz=dz3[:o * (i // 64)].view(o, i // 64))
     t_c3 = ev_time(block, 5)
     gflop = sum(6.0 * lin.m * lin.inp * lin.out for lin, *_ in c3) / 1e9
     return {

@@ -106,8 +106,10 @@ size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in);
  * ws: NULL selects the fused kernel that quantises fp32 W tiles directly into
  * LDS (no workspace; the quantiser runs once per 256-token tile, VALU-bound);
  * otherwise >= qat_fakequant_ws_bytes(M, out, in) bytes of device memory that
- * receive a bf16 W_hat staged once per call and read by the GEMM. The
- * workspace is scratch: its contents after the call are unspecified.
+ * receive a bf16 W_hat staged once per call and read by the GEMM. After the
+ * call the workspace holds that W_hat, [out, in] row-major from its first
+ * byte: the tensor a training step saves for its backward
+ * (qat_fakequant_linear_bwd_saved).
  */
 int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float* s, const float* z,
                                  int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
@@ -134,6 +136,19 @@ int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const fl
                                  float* dz, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The same backward on the W_hat its forward staged (what autograd saves for
+ * dX = dY * W_hat): w_hat, bf16 [out, in], is the workspace of a
+ * qat_fakequant_linear_fwd call on the same W, s, z (or qat_quant_codes'
+ * W_hat), read in place by the dX GEMM; nothing is staged and no workspace is
+ * needed. w_hat is required when dX is wanted (else it may be NULL) and must
+ * not overlap an output. Results are those of qat_fakequant_linear_bwd.
+ */
+int32_t qat_fakequant_linear_bwd_saved(const uint16_t* dY, const uint16_t* X, const float* W,
+                                       const float* s, const float* z, const uint16_t* w_hat, int64_t M,
+                                       int64_t out, int64_t in, int32_t group, int32_t bits, uint16_t* dX,
+                                       float* dW, float* ds, float* dz, hipStream_t stream);
+
+/*
  * a8. Pack (modelfoundations.com note: a trained block is quantised in place;
  * zero points are hard-rounded at pack time): zp = clamp(rint(z), 0, K),
  * codes as in qat_quant_codes with zp, written as a per-row LSB-first
@@ -153,7 +168,9 @@ size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in);
  * ws: NULL selects the fused kernel that dequantises packed codes straight
  * into LDS inside the GEMM (no workspace; the dequantisation runs once per
  * 128- or 256-token tile); otherwise >= qat_dequant_ws_bytes(M, out, in)
- * bytes of scratch that receive the bf16 W_hat, staged once per call.
+ * bytes that receive the bf16 W_hat, staged once per call; after the call the
+ * workspace holds it, [out, in] row-major from its first byte
+ * (qat_dequant_gemm_bwd_s_saved reads it).
  */
 int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* s, const float* z,
                              int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
@@ -173,6 +190,17 @@ int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint
                                const float* s, const float* z, int64_t M, int64_t out, int64_t in,
                                int32_t group, int32_t bits, uint16_t* dX, float* ds, float* dz,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same backward on the W_hat its forward staged: w_hat, bf16 [out, in],
+ * is the workspace of a qat_dequant_gemm_fwd call on the same Wq, s, z, read
+ * in place by the dX GEMM (required when dX is wanted, else it may be NULL;
+ * must not overlap an output). Results are those of qat_dequant_gemm_bwd_s.
+ */
+int32_t qat_dequant_gemm_bwd_s_saved(const uint16_t* dY, const uint16_t* X, const uint8_t* Wq,
+                                     const float* s, const float* z, const uint16_t* w_hat, int64_t M,
+                                     int64_t out, int64_t in, int32_t group, int32_t bits, uint16_t* dX,
+                                     float* ds, float* dz, hipStream_t stream);
 
 /*
  * Deployment format (paperlayer.ai summary of EfficientQAT, Appendix D: each

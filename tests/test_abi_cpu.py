@@ -28,6 +28,7 @@ def test_header_declares_the_calls():
     names = declared()
     for n in ["qat_init_minmax", "qat_fakequant_linear_fwd", "qat_fakequant_linear_bwd", "qat_pack",
               "qat_dequant_gemm_fwd", "qat_dequant_gemm_bwd_s", "qat_quant_codes", "qat_block_ap_step",
+              "qat_fakequant_linear_bwd_saved", "qat_dequant_gemm_bwd_s_saved",
               "qat_block_forward", "qat_block_ws_bytes"]:
         assert n in names
 
@@ -98,6 +99,29 @@ def test_fwd_bwd_validation():
     assert L.qat_dequant_gemm_fwd(A, B, C, D, 0, 64, 128, 64, 2, E, None, 0, None) == 2
     # pack: 3 bits with a group-aligned row is fine shape-wise, bits 1 is not
     assert L.qat_pack(A, B, C, 64, 128, 64, 1, D, None, None) == 3
+
+
+def test_saved_backward_validation():
+    L = Q.lib()
+    A, B, C, D, E, WH, DX = (FAKE * k for k in range(1, 8))
+    # dX wanted without the saved W_hat
+    assert L.qat_fakequant_linear_bwd_saved(A, B, C, D, E, None, 8, 64, 128, 64, 2, DX, None, None, None,
+                                            None) == 1
+    assert L.qat_dequant_gemm_bwd_s_saved(A, B, C, D, E, None, 8, 64, 128, 64, 2, DX, FAKE * 9, None,
+                                          None) == 1
+    # dX writing over the saved W_hat
+    assert L.qat_fakequant_linear_bwd_saved(A, B, C, D, E, WH, 8, 64, 128, 64, 2, WH, None, None, None,
+                                            None) == 8
+    # misaligned W_hat; ds without dz; e2e without ds
+    assert L.qat_fakequant_linear_bwd_saved(A, B, C, D, E, WH + 8, 8, 64, 128, 64, 2, DX, None, None, None,
+                                            None) == 5
+    assert L.qat_fakequant_linear_bwd_saved(A, B, C, D, E, WH, 8, 64, 128, 64, 2, None, None, FAKE * 9, None,
+                                            None) == 1
+    assert L.qat_dequant_gemm_bwd_s_saved(A, B, C, D, E, WH, 8, 64, 128, 64, 2, DX, None, None, None) == 1
+    # shapes as in the staging variants
+    assert L.qat_fakequant_linear_bwd_saved(A, B, C, D, E, WH, 0, 64, 128, 64, 2, DX, None, None, None,
+                                            None) == 2
+    assert L.qat_dequant_gemm_bwd_s_saved(A, B, C, D, E, WH, 8, 64, 128, 64, 5, DX, FAKE * 9, None, None) == 3
 
 
 def test_timing_registry_host_side():

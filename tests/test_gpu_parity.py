@@ -281,6 +281,52 @@ def test_e2e_parity(M, out, inp, bits):
     assert rel_fro(gz.cpu().numpy(), r["dz"]) < TOL_F32
 
 
+@pytest.mark.parametrize("M,out,inp,bits", [(300, 320, 512, 3), (2085, 4096, 256, 2), (100, 4160, 4160, 3),
+                                             (4196, 4160, 128, 4), (2048, 4096, 4096, 2)])
+def test_saved_backward_equals_staging_backward(M, out, inp, bits):
+    # The backward on the forward's saved W_hat (dX reads W_hat [out, in] in
+    # place) against the staging backward (W_hat^T staged from W): the same
+    # bf16 operand in the same k order, so every output is bit-identical; the
+    # E2E pair likewise, on the W_hat its staged forward left in the workspace.
+    say(f"saved backward M={M} out={out} in={inp} bits={bits}")
+    W, X, dY = _inputs(M, out, inp, 90 + bits)
+    s, z = _qparams(W, bits, True, 9)
+    dY_, X_, W_, s_, z_ = dev_bf16(dY), dev_bf16(X), dev_f32(W), dev_f32(s), dev_f32(z)
+    ws_fwd = Q.workspace(Q.fakequant_ws_bytes(M, out, inp))
+    ws_bwd = Q.workspace(Q.fakequant_ws_bytes(M, out, inp))
+    Y = torch.empty(M, out, dtype=torch.bfloat16, device="cuda")
+    Q.qat_fakequant_linear_fwd(X_, W_, s_, z_, bits, Y, ws=ws_fwd)
+    outs = []
+    for saved in (False, True):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gW = torch.empty(out, inp, device="cuda")
+        gs = torch.empty(out, inp // 64, device="cuda")
+        gz = torch.empty_like(gs)
+        if saved:
+            Q.qat_fakequant_linear_bwd_saved(dY_, X_, W_, s_, z_, ws_fwd, bits, dX=gX, dW=gW, ds=gs, dz=gz)
+        else:
+            Q.qat_fakequant_linear_bwd(dY_, X_, W_, s_, z_, bits, dX=gX, dW=gW, ds=gs, dz=gz, ws=ws_bwd)
+        outs.append((host_bits(gX), gW.cpu().numpy(), gs.cpu().numpy(), gz.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    Wq = synth.packed_codes(62, bits, out, inp, bits)
+    es, ez = dev_f32(synth.e2e_scales(62, bits, out, inp)), dev_f32(synth.e2e_zeros(62, bits, out, inp, bits))
+    dq = dev_u8(Wq)
+    Q.qat_dequant_gemm_fwd(X_, dq, es, ez, bits, Y, ws=ws_fwd)
+    outs = []
+    for saved in (False, True):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gs = torch.empty(out, inp // 64, device="cuda")
+        gz = torch.empty_like(gs)
+        if saved:
+            Q.qat_dequant_gemm_bwd_s_saved(dY_, X_, dq, es, ez, ws_fwd, bits, gs, dX=gX, dz=gz)
+        else:
+            Q.qat_dequant_gemm_bwd_s(dY_, X_, dq, es, ez, bits, gs, dX=gX, dz=gz, ws=ws_bwd)
+        outs.append((host_bits(gX), gs.cpu().numpy(), gz.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_pack_then_dequant_gemm_equals_fakequant_forward(bits):
     # Cross-path: with the hard-rounded zero point, dequant(pack(W)) is the same

@@ -33,6 +33,10 @@ _SIGS = {
                              _c_vp, _c_vp, _c_sz, _c_vp],
     "qat_dequant_gemm_bwd_s": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32,
                                _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
+    "qat_fakequant_linear_bwd_saved": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                       _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp],
+    "qat_dequant_gemm_bwd_s_saved": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                     _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp],
     "qat_deploy_zq_stride": [_c_i64, _c_i32, _c_i32],
     "qat_deploy_qparams": [_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp],
     "qat_deploy_gemv": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp],
@@ -197,6 +201,34 @@ def qat_dequant_gemm_fwd(X, Wq, s, z, bits, Y, ws=None, group: int = GROUP) -> N
     out = Wq.shape[0]
     _call("qat_dequant_gemm_fwd", _p(_u16(X)), _p(Wq), _p(s), _p(z), M, out, inp, group, bits,
           _p(_u16(Y)), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
+
+
+def _check_saved(w_hat, out: int, inp: int) -> None:
+    """w_hat: a forward's workspace (any dtype) or a bf16 W_hat, at least out * in * 2 bytes."""
+    if w_hat is not None and w_hat.numel() * w_hat.element_size() < out * inp * 2:
+        raise ValueError("w_hat holds fewer than out * in bf16 values")
+
+
+def qat_fakequant_linear_bwd_saved(dY, X, W, s, z, w_hat, bits, dX=None, dW=None, ds=None, dz=None,
+                                   group: int = GROUP) -> None:
+    """Backward on the W_hat [out, in] (bf16) its forward staged: the forward's
+    workspace, or qat_quant_codes' W_hat."""
+    M, inp = X.shape
+    out = W.shape[0]
+    _check_saved(w_hat, out, inp)
+    _call("qat_fakequant_linear_bwd_saved", _p(_u16(dY)), _p(_u16(X)), _p(W), _p(s), _p(z), _p(w_hat),
+          M, out, inp, group, bits,
+          _p(None if dX is None else _u16(dX)), _p(dW), _p(ds), _p(dz), _stream())
+
+
+def qat_dequant_gemm_bwd_s_saved(dY, X, Wq, s, z, w_hat, bits, ds, dX=None, dz=None, group: int = GROUP) -> None:
+    """E2E-QP backward on the W_hat [out, in] (bf16) its forward staged."""
+    M, inp = X.shape
+    out = Wq.shape[0]
+    _check_saved(w_hat, out, inp)
+    _call("qat_dequant_gemm_bwd_s_saved", _p(_u16(dY)), _p(_u16(X)), _p(Wq), _p(s), _p(z), _p(w_hat),
+          M, out, inp, group, bits,
+          _p(None if dX is None else _u16(dX)), _p(ds), _p(dz), _stream())
 
 
 def qat_dequant_gemm_bwd_s(dY, X, Wq, s, z, bits, ds, dX=None, dz=None, ws=None, group: int = GROUP) -> None:

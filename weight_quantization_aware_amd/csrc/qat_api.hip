@@ -282,6 +282,51 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
   return finish();
 }
 
+// dX = dY W_hat on a W_hat [out][in] staged by a forward call, read in place.
+static void launch_linear_dx_saved(const uint16_t* dY, const uint16_t* w_hat, int64_t M, int64_t out, int64_t in,
+                            uint16_t* dX, hipStream_t stream) {
+  qat::GemmArgs a = gemm_args();
+  a.A = dY;
+  a.lda = out;
+  a.B = w_hat;
+  a.ldb = in;
+  a.M = (int)M;
+  a.N = (int)in;
+  a.K = (int)out;
+  a.C = dX;
+  a.ldc = in;
+  qat::launch_gemm_dx_mn(a, stream);
+}
+
+QAT_API int32_t qat_fakequant_linear_bwd_saved(const uint16_t* dY, const uint16_t* X, const float* W,
+                                               const float* s, const float* z, const uint16_t* w_hat,
+                                               int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
+                                               uint16_t* dX, float* dW, float* ds, float* dz,
+                                               hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits, true));
+  QAT_CHECK(check_m(M, out, in));
+  if (!dY || !X || !W || !s || !z || (dX && !w_hat)) return QAT_ERR_NULL;
+  if ((ds == nullptr) != (dz == nullptr)) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({dY, X, W, s, z, w_hat, dX, dW, ds, dz}));
+  const size_t ng = gbytes(out, in, group);
+  Range outs[] = {{dX, (size_t)(M * in * 2)}, {dW, (size_t)(out * in * 4)}, {ds, ng}, {dz, ng}};
+  Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)},
+                 {s, ng}, {z, ng}, {dX ? w_hat : nullptr, (size_t)(out * in * 2)}};
+  QAT_CHECK(check_alias(outs, 4, ins, 6));
+
+  if (dX) launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
+  if (dW || ds) {
+    qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
+    a.W = W;
+    a.ldw = in;
+    a.dW = dW;
+    a.ds = ds;
+    a.dz = dz;
+    qat::launch_gemm_grads(a, qat::kSteGrads, bits, stream);
+  }
+  return finish();
+}
+
 QAT_API int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* s,
                                      const float* z, int64_t M, int64_t out, int64_t in, int32_t group,
                                      int32_t bits, uint16_t* Y, void* ws, size_t ws_bytes,
@@ -345,6 +390,30 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
     qat::launch_dequant_t(Wq, s, z, out, in, group, bits, w_hat, stream);
     qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
   }
+  qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
+  a.Wq = Wq;
+  a.ldq = in * bits / 8;
+  a.ds = ds;
+  a.dz = dz;
+  qat::launch_gemm_grads(a, qat::kE2eScaleGrad, bits, stream);
+  return finish();
+}
+
+QAT_API int32_t qat_dequant_gemm_bwd_s_saved(const uint16_t* dY, const uint16_t* X, const uint8_t* Wq,
+                                             const float* s, const float* z, const uint16_t* w_hat, int64_t M,
+                                             int64_t out, int64_t in, int32_t group, int32_t bits,
+                                             uint16_t* dX, float* ds, float* dz, hipStream_t stream) {
+  QAT_CHECK(check_common(out, in, group, bits, true));
+  QAT_CHECK(check_m(M, out, in));
+  if (!dY || !X || !Wq || !s || !z || !ds || (dX && !w_hat)) return QAT_ERR_NULL;
+  QAT_CHECK(check_ptrs({dY, X, Wq, s, z, w_hat, dX, ds, dz}));
+  const size_t ng = gbytes(out, in, group);
+  Range outs[] = {{dX, (size_t)(M * in * 2)}, {ds, ng}, {dz, ng}};
+  Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)},
+                 {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}, {dX ? w_hat : nullptr, (size_t)(out * in * 2)}};
+  QAT_CHECK(check_alias(outs, 3, ins, 6));
+
+  if (dX) launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
   qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
   a.Wq = Wq;
   a.ldq = in * bits / 8;

@@ -172,11 +172,13 @@ void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {
   launch_pick<kKContig, kKContig, kStoreBf16, 1>(a, st);
 }
 
-// On the Llama-2-7B block's shapes W_hat read in place costs the same as a
-// staged W_hat^T; 8 waves also beyond K = 4096 (measured faster with this
-// loader at K = 11008).
+// W_hat read in place costs the same as a staged W_hat^T on the Llama-2-7B
+// block's shapes (4096 tokens) and 4% more at 2048 tokens (128x256 tiles);
+// 8 waves also beyond K = 4096 (measured faster with this loader at
+// K = 11008).
 void launch_gemm_dx_mn(const GemmArgs& a, hipStream_t st) {
   if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kKContig, kMNContig, kStoreBf16, 1>(a, st);
+  else if (tiles(a, 128, 256) >= 192) launch_bf16<128, 256, 3, 2, 4, kKContig, kMNContig, kStoreBf16, 1>(a, st);
   else launch_bf16<128, 128, 4, 2, 2, kKContig, kMNContig, kStoreBf16, 1>(a, st);
 }
 

@@ -33,7 +33,7 @@ import sys
 # rocprofv3 kernel symbol -> the label the library's own timing uses
 LABELS = [
     # k_gemm<BM, BN, BK, STAGES, AMN, BMN, EP, NB>
-    (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*1>", "gemm_dx"),
+    (r"k_gemm<[^>]*,\s*0,\s*\d,\s*0,\s*1>", "gemm_dx"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*1,\s*0>", "gemm_ste_grads"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*4,\s*0>", "gemm_ste_grads_adamw"),
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*2,\s*\d>", "gemm_e2e_grads"),
