@@ -22,6 +22,8 @@
 // LDS: two buffers of the K and V blocks [64 keys][128 d] bf16 (256-byte
 // rows); 16-byte chunk c of key row k sits at c ^ (k & 15), so both the K
 // fragment reads and the V transposing reads use every bank equally.
+#include <type_traits>
+
 #include "qat_device.h"
 #include "qat_dma.h"
 #include "qat_internal.h"
@@ -47,7 +49,7 @@ struct AttnArgs {
   float scale_log2;                  // log2(e) / sqrt(128)
 };
 
-__global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void k_flash_fwd(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kTileBytes];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -109,10 +111,21 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
   for (int jd = 0; jd < 8; ++jd)
 #pragma unroll
     for (int i = 0; i < 2; ++i) o[jd][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Running softmax per row, base 2: m is the subtracted maximum and moves
+  // only when a block's maximum exceeds it by more than kLazy (a wave-uniform
+  // test), so the 64 output accumulators per lane are rescaled rarely; the
+  // probabilities exp2(s - m) then stay below 2^kLazy, and O / l and the
+  // log-sum-exp m + log2(l) do not depend on which m was subtracted.
+  // exp2 is the hardware's v_exp_f32: results below 2^-126 flush to zero,
+  // which no probability that matters reaches.
+  constexpr float kLazy = 8.0f;
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   const int qrow0 = q0 + 32 * wave + r16;                // query of this lane in tile i: qrow0 + 16 i
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  // One 64-key block; DIAG: the block crosses the diagonal of this query block
+  // (keys beyond a row's query are masked), which only the last two do.
+  auto key_block = [&](int kb, auto diag_c) {
+    constexpr bool DIAG = decltype(diag_c)::value;
     wait_vmcnt<8>();                                     // this wave's DMA of block kb has landed
     __syncthreads();                                     // ... and everyone's
     const uint8_t* kt = smem + (kb & 1) * 2 * kTileBytes;
@@ -133,43 +146,56 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
         for (int i = 0; i < 2; ++i) s[jt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i][ks], s[jt][i], 0, 0, 0);
       }
     }
-    // running softmax over the block (rows of tile i: query qrow0 + 16 i)
-    const bool diag = kb * kBK + kBK - 1 > q0;            // the block reaches past the first query
-    bf16x8 pf[2][2];                                      // [i][ks]
+    // scaled scores and each row's block maximum (rows of tile i: query qrow0 + 16 i)
+    float mx[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = qrow0 + 16 * i;
-      float mx = -INFINITY;
+      float x = -INFINITY;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float v = s[jt][i][r] * a.scale_log2;
-          if (diag && kb * kBK + 16 * jt + 4 * g + r > q) v = -INFINITY;
+          if constexpr (DIAG) {
+            if (kb * kBK + 16 * jt + 4 * g + r > q) v = -INFINITY;
+          }
           s[jt][i][r] = v;
-          mx = fmaxf(mx, v);
+          x = fmaxf(x, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[i], mx);                   // finite: key 0 of block 0 is valid for every row
-      const float alpha = exp2f(m[i] - mn);
+      x = fmaxf(x, __shfl_xor(x, 16));
+      mx[i] = fmaxf(x, __shfl_xor(x, 32));
+    }
+    // a row with every key masked has mx = -inf and never moves m; key 0 of
+    // block 0 is valid for every row, so m is finite from block 0 on
+    if (__any(mx[0] > m[0] + kLazy || mx[1] > m[1] + kLazy)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float mn = fmaxf(m[i], mx[i]);
+        const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
+        l[i] *= alpha;
+        m[i] = mn;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[jd][i][r] *= alpha;
+      }
+    }
+    bf16x8 pf[2][2];                                      // [i][ks]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       float sum = 0.f;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[jt][i][r] - mn);
+          const float p = __builtin_amdgcn_exp2f(s[jt][i][r] - m[i]);
           s[jt][i][r] = p;
           sum += p;
         }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
-      l[i] = l[i] * alpha + sum;
-      m[i] = mn;
-#pragma unroll
-      for (int jd = 0; jd < 8; ++jd)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[jd][i][r] *= alpha;
+      l[i] += sum;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const f32x4 lo = s[2 * ks][i], hi = s[2 * ks + 1][i];
@@ -200,7 +226,12 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
     }
     __syncthreads();                                     // every wave is done with this buffer
     issue(kb + 2, kb & 1);
-  }
+  };
+  // blocks kb < q0 / 64 lie wholly below the diagonal of every row here
+  const int kd = min(q0 / kBK, nkb);
+  int kb = 0;
+  for (; kb < kd; ++kb) key_block(kb, std::false_type{});
+  for (; kb < nkb; ++kb) key_block(kb, std::true_type{});
   wait_vmcnt<0>();                                       // drain the trailing re-loads
 
   // O / l to bf16; the log-sum-exp (base 2) of each row
