@@ -132,8 +132,9 @@ def check_adamw_identity(lin_before, lin_after, opt, ctx):
         assert np.all(np.abs(p1 - p_ref) <= 2 * ulp + 1e-5 * np.abs(upd)), (ctx, key, "p")
 
 
-def check_update(p_gpu, p0, p_ref, g_refs, ctx):
+def check_update(p_gpu, p0, p_ref, g_refs, ctx, bar=None):
     """Update after len(g_refs) steps, whose oracle gradients are g_refs."""
+    bar = BAR if bar is None else bar
     d_gpu = np.asarray(p_gpu, np.float64) - p0
     d_ref = np.asarray(p_ref, np.float64) - p0
     big = np.ones(d_ref.shape, bool)
@@ -142,7 +143,7 @@ def check_update(p_gpu, p0, p_ref, g_refs, ctx):
         big &= np.abs(g) >= 0.1 * np.sqrt(np.mean(g * g))
     e = rel_fro(d_gpu[big], d_ref[big])
     flips = np.mean(np.sign(d_gpu) != np.sign(d_ref))
-    assert e < BAR and flips < len(g_refs) * BAR / math.pi, (ctx, e, flips)
+    assert e < bar and flips < len(g_refs) * bar / math.pi, (ctx, e, flips)
     return e, flips
 
 
@@ -163,6 +164,34 @@ CASES = [
 def test_block_step_parity(case):
     sh, d, params = make(case)
     say(f"block step {case}")
+    _check_step_parity(sh, d, params)
+
+
+def test_block_step_parity_peaked_attention():
+    # q and k weights scaled by 8 (scores ~64x larger: std ~13 in log2 units,
+    # the largest probability of a row 0.76 on average): the running maximum
+    # of the fused attention forward then exceeds itself by more than 2^8 at
+    # 382 (row, key block) pairs past the first block (the oracle's scores,
+    # counted on the CPU), so its deferred rescale runs mid-sequence; at the
+    # unscaled weights it never does. 512 tokens give up to six key blocks
+    # below the diagonal per query block.
+    # The forward, the loss and every gradient but q's and k's keep the bar.
+    # q's and k's come through dS = P (dP - D), D = sum_j P_j dP_j: where one
+    # probability p dominates a row, dS cancels to about (1 - p) |dP| while the
+    # bf16 rounding of P and dP stays about 2u |dP|, so the relative error
+    # grows by 1 / (1 - p); at the mean p = 0.76 that is 4.2x: bar 0.1.
+    case = (256, 2, 704, 512, 1, 2, 64)
+    sh, d, params = make(case)
+    say(f"block step, peaked attention {case}")
+    for n in ("q_proj", "k_proj"):
+        W = params[n]["W"] * 8.0
+        s_, z_ = O.init_minmax(W, case[5], case[6])
+        params[n] = {"W": W, "s": s_, "z": z_}
+    _check_step_parity(sh, d, params, {"q_proj": 0.1, "k_proj": 0.1})
+
+
+def _check_step_parity(sh, d, params, bars=None):
+    bars = bars or {}
     o = B.AdamW()
     x64, t64 = bf(d["x"]), bf(d["target"])
     g1, g2 = d["g1"].astype(np.float64), d["g2"].astype(np.float64)
@@ -179,11 +208,13 @@ def test_block_step_parity(case):
     assert report("y - x", rel_fro(y - x64, ref_y - x64)) < BAR
     worst = worst_u = worst_f = 0.0
     for i, n in enumerate(B.LINEARS):
+        bar = bars.get(n, BAR)
         for key in KEYS:
             e = rel_fro(after[i]["d" + key], grads_ref[n][key])
             worst = max(worst, e)
-            assert e < BAR, (n, key, e)
-            du, fl = check_update(after[i][key], params[n][key], p_ref[n][key], [grads_ref[n][key]], (n, key))
+            assert e < bar, (n, key, e)
+            du, fl = check_update(after[i][key], params[n][key], p_ref[n][key], [grads_ref[n][key]], (n, key),
+                                  bar)
             worst_u, worst_f = max(worst_u, du), max(worst_f, fl)
         check_adamw_identity(before[i], after[i], opt_dict(o, 0), n)
     report("worst gradient", worst)
