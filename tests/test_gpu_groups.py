@@ -8,7 +8,9 @@ a channel-wise row length that is not a power of two (192), and each way
 the gradient epilogue finishes a group: stored per 64- or 32-column chunk,
 summed over the tile's chunks and stored (group 128, or a whole row that fits
 one tile), or summed per tile and accumulated (whole rows over several
-tiles).
+tiles). The backwards on the forward's saved W_hat match the staging ones bit
+for bit at every group size (ds, dz of whole-row groups to fp32 reassociation:
+their per-tile atomic adds meet in no fixed order).
 """
 import numpy as np
 import pytest
@@ -75,6 +77,18 @@ def test_init_codes_pack_bit_exact(M, out, inp, group, bits):
     assert np.array_equal(Wq.cpu().numpy(), Wq_ref) and np.array_equal(zp.cpu().numpy(), zp_ref)
 
 
+def _same_backward(outs, whole_rows, n_exact):
+    """The saved-W_hat backward against the staging one: the first n_exact
+    outputs (dX, dW) bit-identical; ds and dz too, except for whole-row groups,
+    whose sums over rows wider than a gradient tile meet by one atomic add per
+    tile in no fixed order, so they agree to fp32 reassociation."""
+    for k, (a_, b_) in enumerate(zip(*outs)):
+        if k < n_exact or not whole_rows:
+            assert torch.equal(a_, b_), k
+        else:
+            assert rel_fro(a_.cpu().numpy(), b_.cpu().numpy()) < 1e-6, k
+
+
 @pytest.mark.parametrize("M,out,inp,group,bits", CASES)
 def test_fakequant_fwd_bwd(M, out, inp, group, bits):
     gs = _gs(group, inp)
@@ -89,13 +103,23 @@ def test_fakequant_fwd_bwd(M, out, inp, group, bits):
     Y = torch.empty(M, out, dtype=torch.bfloat16, device="cuda")
     Yf = torch.empty_like(Y)
     Q.qat_fakequant_linear_fwd(Xd, Wd, sd, zd, bits, Y, ws=ws, group=gs)
+    saved = ws.clone()                                          # the forward's W_hat
     Q.qat_fakequant_linear_fwd(Xd, Wd, sd, zd, bits, Yf, ws=None, group=gs)
-    gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
-    gW = torch.empty(out, inp, device="cuda")
-    gs_ = torch.full((out, inp // gs), 9.0, device="cuda")     # must be overwritten, not accumulated
-    gz = torch.full_like(gs_, 9.0)
-    Q.qat_fakequant_linear_bwd(dYd, Xd, Wd, sd, zd, bits, dX=gX, dW=gW, ds=gs_, dz=gz, ws=ws, group=gs)
+    outs = []
+    for use_saved in (False, True):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gW = torch.empty(out, inp, device="cuda")
+        gs_ = torch.full((out, inp // gs), 9.0, device="cuda")  # must be overwritten, not accumulated
+        gz = torch.full_like(gs_, 9.0)
+        if use_saved:
+            Q.qat_fakequant_linear_bwd_saved(dYd, Xd, Wd, sd, zd, saved, bits, dX=gX, dW=gW, ds=gs_, dz=gz,
+                                             group=gs)
+        else:
+            Q.qat_fakequant_linear_bwd(dYd, Xd, Wd, sd, zd, bits, dX=gX, dW=gW, ds=gs_, dz=gz, ws=ws, group=gs)
+        outs.append((gX, gW, gs_, gz))
     torch.cuda.synchronize()
+    _same_backward(outs, gs == inp, 2)
+    gX, gW, gs_, gz = outs[0]
     assert torch.equal(Y, Yf)
     assert rel_fro(O.bf16_bits_to_f64(host_bits(Y)), O.fakequant_fwd(X, W, s, z, bits, gs)) < TOL_BF16
     r = O.fakequant_bwd(dY, X, W, s, z, bits, gs)
@@ -120,12 +144,21 @@ def test_e2e_fwd_bwd(M, out, inp, group, bits):
     Y = torch.empty(M, out, dtype=torch.bfloat16, device="cuda")
     Yf = torch.empty_like(Y)
     Q.qat_dequant_gemm_fwd(Xd, Wqd, sd, zd, bits, Y, ws=ws, group=gs)
+    saved = ws.clone()                                          # the forward's W_hat
     Q.qat_dequant_gemm_fwd(Xd, Wqd, sd, zd, bits, Yf, group=gs)
-    gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
-    gs_ = torch.full((out, inp // gs), 9.0, device="cuda")
-    gz = torch.full_like(gs_, 9.0)
-    Q.qat_dequant_gemm_bwd_s(dYd, Xd, Wqd, sd, zd, bits, gs_, dX=gX, dz=gz, ws=ws, group=gs)
+    outs = []
+    for use_saved in (False, True):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gs_ = torch.full((out, inp // gs), 9.0, device="cuda")
+        gz = torch.full_like(gs_, 9.0)
+        if use_saved:
+            Q.qat_dequant_gemm_bwd_s_saved(dYd, Xd, Wqd, sd, zd, saved, bits, gs_, dX=gX, dz=gz, group=gs)
+        else:
+            Q.qat_dequant_gemm_bwd_s(dYd, Xd, Wqd, sd, zd, bits, gs_, dX=gX, dz=gz, ws=ws, group=gs)
+        outs.append((gX, gs_, gz))
     torch.cuda.synchronize()
+    _same_backward(outs, gs == inp, 1)
+    gX, gs_, gz = outs[0]
     assert torch.equal(Y, Yf)
     assert rel_fro(O.bf16_bits_to_f64(host_bits(Y)), O.dequant_gemm_fwd(X, Wq, s, z, inp, bits, gs)) < TOL_BF16
     r = O.dequant_gemm_bwd_s(dY, X, Wq, s, z, inp, bits, gs)
