@@ -14,10 +14,11 @@
 //
 // Memory-bound row kernels: one workgroup per token row for the norms (a row
 // of H <= 8192 values stays in registers between the reduction and the
-// write), 16-byte vector accesses throughout. Attention: the forward is one
-// fused kernel (qat_attn.hip); the backward rebuilds P in the epilogue of the
-// score product (kSoftmaxProbs) and applies the softmax backward in the
-// epilogue of the dP product (kSoftmaxGrad) from a per-query row term.
+// write), 16-byte vector accesses throughout. Attention (qat_attn.hip): the
+// forward is one fused kernel; the backward is one fused pass per key block
+// for dK and dV (P and dS recomputed in registers from the forward's
+// log-sum-exp and a per-query row term), which also leaves dS^T for the dQ
+// product.
 #include <math.h>
 #include <string.h>
 
@@ -644,68 +645,16 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
   }
   fq_backward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.dx2, w.attn, w.dattn, w, ac, st);
   {
-    // P = exp2(S log2(e) / sqrt(128) - lse) from S = q k^T, bf16, causal tiles
-    GemmArgs a = zero_args();
-    a.A = w.q;
-    a.lda = d.H;
-    a.B = w.k;
-    a.ldb = d.H;
-    a.M = a.N = (int)d.T;
-    a.K = kHeadDim;
-    a.C = w.P;
-    a.ldc = d.T;
-    a.causal = kCausalSkip;
-    a.Dvec = w.lse;
-    a.sd_b = d.nh * d.T;
-    a.sd_h = d.T;
-    a.escale = 1.4426950408889634f * scale;
-    set_batch(a, d, kTok, kTok, kScore);
-    launch_gemm_attn(a, kKK_PROBS, st);
-  }
-  {
-    // dv = P^T dattn: A[m = key][k = query] = P[query][key], both MN-contiguous
-    GemmArgs a = zero_args();
-    a.A = w.P;
-    a.lda = d.T;
-    a.B = w.dattn;
-    a.ldb = d.H;
-    a.M = (int)d.T;
-    a.N = kHeadDim;
-    a.K = (int)d.T;
-    a.C = w.dv;
-    a.ldc = d.H;
-    a.causal = kCausalUpper;
-    set_batch(a, d, kScore, kTok, kTok);
-    launch_gemm_attn(a, kMNMN_BF16, st);
-  }
-  {
     // D = rowsum(P dP) = dO . O per query
     LaunchTimer t("attn_rowdot", st);
     const int64_t n = d.BT * d.nh;
     hipLaunchKernelGGL(k_attn_rowdot, dim3((unsigned)blocks_of(n, 256)), dim3(256), 0, st, w.dattn, w.attn, w.D,
                        d.BT, (int)d.T, (int)d.H, (int)d.nh);
   }
+  // dk, dv and dS^T (into the P buffer) in one pass over the causal pairs
+  launch_flash_bwd_kv(w.q, w.k, w.v, w.dattn, w.lse, w.D, w.dk, w.dv, w.P, (int)d.B, (int)d.T, (int)d.H, st);
   {
-    // dP = dattn v^T; its epilogue writes dS = scale P (dP - D) over P
-    GemmArgs a = zero_args();
-    a.A = w.dattn;
-    a.lda = d.H;
-    a.B = w.v;
-    a.ldb = d.H;
-    a.M = a.N = (int)d.T;
-    a.K = kHeadDim;
-    a.C = w.P;
-    a.ldc = d.T;
-    a.causal = kCausalSkip;
-    a.Dvec = w.D;
-    a.sd_b = d.nh * d.T;
-    a.sd_h = d.T;
-    a.escale = scale;
-    set_batch(a, d, kTok, kTok, kScore);
-    launch_gemm_attn(a, kKK_DSOFTMAX, st);
-  }
-  {
-    // dq = dS k
+    // dq = dS k: A[m = query][k = key] = dS^T[key][query], both MN-contiguous
     GemmArgs a = zero_args();
     a.A = w.P;
     a.lda = d.T;
@@ -718,23 +667,7 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     a.ldc = d.H;
     a.causal = kCausalLower;
     set_batch(a, d, kScore, kTok, kTok);
-    launch_gemm_attn(a, kKMN_BF16, st);
-  }
-  {
-    // dk = dS^T q
-    GemmArgs a = zero_args();
-    a.A = w.P;
-    a.lda = d.T;
-    a.B = w.q;
-    a.ldb = d.H;
-    a.M = (int)d.T;
-    a.N = kHeadDim;
-    a.K = (int)d.T;
-    a.C = w.dk;
-    a.ldc = d.H;
-    a.causal = kCausalUpper;
-    set_batch(a, d, kScore, kTok, kTok);
-    launch_gemm_attn(a, kMNMN_BF16, st);
+    launch_gemm_attn(a, st);
   }
   rope(d, w.dq, w.dk, w, -1.0f, st);
   // q, k, v: gradients of W, s, z only (the block input's gradient is not needed)

@@ -33,31 +33,18 @@ constexpr const char* gemm_label() {
   if (BL == kFp32Quant) return "gemm_fwd_fused_fp32";
   if (BL == kPacked) return "gemm_fwd_packed";
   if (EP == kResidMse) return "gemm_fwd_mse";
-  if (NB == kTagAttn)
-    return EP == kStoreF32 ? "attn_gemm_f32" : EP == kSoftmaxGrad ? "attn_gemm_dsoftmax"
-           : EP == kSoftmaxProbs ? "attn_gemm_probs" : "attn_gemm_bf16";
+  if (NB == kTagAttn) return "attn_gemm_bf16";
   if (EP == kStoreF32) return "gemm_fwd_f32";
   return NB == 1 ? "gemm_dx" : "gemm_fwd";
 }
 
 int batches(const GemmArgs& a) { return a.batch_h > 0 ? a.batches : 1; }
 
-// Workgroups of one problem: every tile, or for kCausalSkip (square tiles of a
-// square problem) only the lower triangle of tiles.
-template <int BM, int BN>
-int64_t grid_tiles(const GemmArgs& a) {
-  if (a.causal == kCausalSkip) {
-    const int64_t t = (a.M + BM - 1) / BM;
-    return t * (t + 1) / 2;
-  }
-  return tiles(a, BM, BN);
-}
-
 template <int BM, int BN, int S, int WGM, int WGN, int AMN, int BMN, int EP, int NB, int GM = 0>
 void launch_bf16(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<kBf16, EP, NB>(), st);
   hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, GM, AMN, BMN, EP, NB>),
-                     dim3((unsigned)grid_tiles<BM, BN>(a), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
+                     dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
 template <int BM, int BN, int BK, int S, int BL, int NB>
@@ -119,20 +106,6 @@ void launch_grads(const GemmArgs& a, hipStream_t st) {
   }
 }
 
-// Batched attention products: 256x256 tiles for the T x T score-shaped
-// outputs (fp32) when they fill the chip, 128x128 tiles otherwise (the
-// head-sized outputs, N = head_dim = 128).
-template <int AMN, int BMN, int EP>
-void launch_pick_attn(const GemmArgs& a, hipStream_t st) {
-  if constexpr (EP == kStoreF32 || EP == kSoftmaxGrad || EP == kSoftmaxProbs) {
-    if (a.N >= 256 && tiles(a, 256, 256) * batches(a) >= 256) {
-      launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, kTagAttn>(a, st);
-      return;
-    }
-  }
-  launch_bf16<128, 128, 4, 2, 2, AMN, BMN, EP, kTagAttn>(a, st);
-}
-
 template <int BL, int NB>
 void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
   if constexpr (BL == kPacked) {
@@ -158,14 +131,9 @@ void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st) {
   launch_pick<kKContig, kKContig, kStoreF32, 0>(a, st);
 }
 
-// kCausalSkip enumerates the lower triangle of square tiles: the problem must
-// be square (M == N); every attention tile configuration is square.
-void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st) {
-  if (kind == kKK_F32) launch_pick_attn<kKContig, kKContig, kStoreF32>(a, st);
-  else if (kind == kKK_DSOFTMAX) launch_pick_attn<kKContig, kKContig, kSoftmaxGrad>(a, st);
-  else if (kind == kKK_PROBS) launch_pick_attn<kKContig, kKContig, kSoftmaxProbs>(a, st);
-  else if (kind == kKMN_BF16) launch_pick_attn<kKContig, kMNContig, kStoreBf16>(a, st);
-  else launch_pick_attn<kMNContig, kMNContig, kStoreBf16>(a, st);
+// The dQ product of attention (N = head size 128): 128x128 tiles.
+void launch_gemm_attn(const GemmArgs& a, hipStream_t st) {
+  launch_bf16<128, 128, 4, 2, 2, kMNContig, kMNContig, kStoreBf16, kTagAttn>(a, st);
 }
 
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {

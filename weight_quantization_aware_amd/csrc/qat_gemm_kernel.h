@@ -41,36 +41,22 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
   tn = in_g / gm;
 }
 
-// Tiles of causal products. kCausalSkip (square tiles, M = N): the grid
-// enumerates only the lower triangle, tn <= tm, row by row; consecutive ids go
-// to different XCDs, which then get equal shares of the triangle.
-// kCausalLower / kCausalUpper (every row tile present, contractions of
-// different lengths): row tiles in boustrophedon order, every other group of
-// 8 reversed, so the XCD that takes a short tile in one group takes a long
-// one in the next.
-// With the problem's tiles on one XCD (grouped), the contraction-range modes
-// instead issue the longest tiles first (the XCD's CUs take workgroups in
-// order as they free up).
-__device__ __forceinline__ void causal_tile_of(int b, int causal, bool grouped, int tiles_m, int tiles_n, int& tm,
-                                               int& tn) {
-  if (causal != kCausalSkip && grouped) {
-    const int p = b / tiles_n;
-    tn = b % tiles_n;
-    tm = causal == kCausalLower ? tiles_m - 1 - p : p;
+// Row tiles of a causal product whose contraction ends at its row tile's end
+// (kCausalLower: tile m contracts over [0, (m + 1) BM)): boustrophedon order,
+// every other group of 8 row tiles reversed, so the XCD that takes a short
+// tile in one group takes a long one in the next. With the problem's tiles on
+// one XCD (grouped), the longest tiles go first instead (the XCD's CUs take
+// workgroups in order as they free up).
+__device__ __forceinline__ void causal_tile_of(int b, bool grouped, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int p = b / tiles_n;
+  tn = b % tiles_n;
+  if (grouped) {
+    tm = tiles_m - 1 - p;
     return;
   }
-  if (causal == kCausalSkip) {
-    int r = (int)((__builtin_sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
-    while (r * (r + 1) / 2 > b) --r;
-    while ((r + 1) * (r + 2) / 2 <= b) ++r;
-    tm = r;
-    tn = b - r * (r + 1) / 2;
-  } else {
-    const int p = b / tiles_n, g = p / 8;
-    tn = b % tiles_n;
-    const int end = min(8 * g + 8, tiles_m);
-    tm = (g & 1) ? 8 * g + (end - 1 - p) : p;
-  }
+  const int g = p / 8;
+  const int end = min(8 * g + 8, tiles_m);
+  tm = (g & 1) ? 8 * g + (end - 1 - p) : p;
 }
 
 // Workgroup -> (tile id, problem) of a launch. Batched launches whose problem
@@ -101,7 +87,6 @@ __device__ __forceinline__ GemmArgs batch_view(const GemmArgs& a0, int z) {
     const int64_t oc = b * a.sc_b + h * a.sc_h;
     if (a.C) a.C += oc;
     if (a.Cf) a.Cf += oc;
-    if (a.Dvec) a.Dvec += b * a.sd_b + h * a.sd_h;
   }
   return a;
 }
@@ -401,8 +386,6 @@ __device__ __forceinline__ void mfma_drain() {
 //   kResidMse:     y = resid + acc, dy = bf16(escale (y - target)), and the
 //                  workgroup's sum of (y - target)^2.
 //   kStoreF32:     Cf (fp32) = acc.
-//   kSoftmaxGrad:  C (bf16, holding P) = escale P (acc - Dvec[row]): the
-//                  softmax backward of attention applied to dP = acc.
 //   kSteGrads:     rows are weight rows o (A = dY^T), columns inputs c (B =
 //                  X^T); Gw = acc. dW = Gw * m and the group sums of ds, dz of
 //                  the straight-through estimator, from W, s, z re-quantised
@@ -433,80 +416,10 @@ template <int EP, int NB, int GM, int BM, int BN, int TI, int TJ, int WN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&acc)[TJ][TI], int m0, int n0,
                                               int wm0, int wn0, int lane, float* red) {
   const int rl = lane & 15, cq = 4 * (lane >> 4);
-  if constexpr (EP == kSoftmaxGrad) {
-    // dS = escale P (dP - D[row]) over P, 4 consecutive columns per lane. The
-    // P values and D of the next 16-row step are in flight while this one is
-    // computed (the contraction is short, so these loads set the pace).
-    struct Row {
-      uint2 p[TJ];
-      float d;
-    };
-    auto load_row = [&](int i, Row& r) {
-      const int row = min(m0 + wm0 + i * 16 + rl, a.M - 1);
-      r.d = a.Dvec[row];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int col = min(n0 + wn0 + j * 16 + cq, a.N - 4);
-        r.p[j] = *(const uint2*)(a.C + (int64_t)row * a.ldc + col);
-      }
-    };
-    Row cur, nxt;
-    load_row(0, cur);
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      if (i + 1 < TI) load_row(i + 1, nxt);
-      const int row = m0 + wm0 + i * 16 + rl;
-      if (row < a.M) {
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int col = n0 + wn0 + j * 16 + cq;
-          if (col < a.N) {
-            const uint2 pb = cur.p[j];
-            const float dr = cur.d;
-            const float p0 = __builtin_bit_cast(float, pb.x << 16), p1 = __builtin_bit_cast(float, pb.x & 0xFFFF0000u);
-            const float p2 = __builtin_bit_cast(float, pb.y << 16), p3 = __builtin_bit_cast(float, pb.y & 0xFFFF0000u);
-            *(uint2*)(a.C + (int64_t)row * a.ldc + col) =
-                make_uint2(pack_bf16x2(a.escale * p0 * (acc[j][i][0] - dr), a.escale * p1 * (acc[j][i][1] - dr)),
-                           pack_bf16x2(a.escale * p2 * (acc[j][i][2] - dr), a.escale * p3 * (acc[j][i][3] - dr)));
-          }
-        }
-      }
-      cur = nxt;
-    }
-  } else if constexpr (EP == kSoftmaxProbs) {
-    // P = exp2(escale S - lse[row]) for col <= row, 0 beyond
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int row = m0 + wm0 + i * 16 + rl;
-      if (row >= a.M) continue;
-      const float lr = a.Dvec[row];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int col = n0 + wn0 + j * 16 + cq;
-        if (col < a.N) {
-          float pv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pv[r] = col + r <= row ? exp2f(a.escale * acc[j][i][r] - lr) : 0.0f;
-          *(uint2*)(a.C + (int64_t)row * a.ldc + col) = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
-        }
-      }
-    }
-  } else if constexpr (EP == kStoreF32) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int row = m0 + wm0 + i * 16 + rl;
-      if (row >= a.M) continue;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int col = n0 + wn0 + j * 16 + cq;
-        if (col < a.N)
-          *(float4*)(a.Cf + (int64_t)row * a.ldc + col) = make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
-      }
-    }
-  } else if constexpr (EP == kResidMse) {
+  if constexpr (EP == kResidMse) {
     // y = resid + product, d = y - target, dy = bf16(escale d), 4 consecutive
     // columns per lane; resid and target of the next 16-row step are in flight
-    // while this one is computed (as in kSoftmaxGrad). Rows and columns beyond
+    // while this one is computed. Rows and columns beyond
     // the problem are clamped for the loads and skipped for the stores.
     struct Row {
       uint2 t[TJ];
@@ -562,6 +475,18 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
       for (int w = 0; w < nwave; ++w) t += red[w];
       a.partial[blockIdx.x] = t;
     }
+  } else if constexpr (EP == kStoreF32) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = m0 + wm0 + i * 16 + rl;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn0 + j * 16 + cq;
+        if (col < a.N)
+          *(float4*)(a.Cf + (int64_t)row * a.ldc + col) = make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+      }
+    }
   } else if constexpr (EP == kStoreBf16) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
@@ -576,6 +501,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
       }
     }
   } else {
+    static_assert(EP == kSteGrads || EP == kE2eScaleGrad, "every other epilogue has its own branch");
     // Rows are weight rows o (A = dY^T), columns inputs c (B = X^T). Steps
     // t = (i, g) walk the lane's rows and 64-column chunks; the loads of step
     // t + 1 are issued before step t is computed.
@@ -858,20 +784,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   int tm, tn;
   if (a.causal == kCausalNone) tile_of(tile_id, tiles_m, tiles_n, tm, tn);
-  else causal_tile_of(tile_id, a.causal, grouped, tiles_m, tiles_n, tm, tn);
+  else causal_tile_of(tile_id, grouped, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const uint32_t lds0 = lds_addr_of(smem);
 
-  // Slabs [kb, kb + nk) of the contraction (all of it unless causal).
-  int kb = 0, nk = (a.K + BK - 1) / BK;
-  if (a.causal == kCausalSkip) {
-    if (n0 >= m0 + BM) return;                           // every column beyond every row: not needed
-  } else if (a.causal == kCausalLower) {
-    nk = min(nk, (m0 + BM + BK - 1) / BK);
-  } else if (a.causal == kCausalUpper) {
-    kb = m0 / BK;
-    nk -= kb;
-  }
+  // Slabs [0, nk) of the contraction (all of it, or up to the row tile's end).
+  int nk = (a.K + BK - 1) / BK;
+  if (a.causal == kCausalLower) nk = min(nk, (m0 + BM + BK - 1) / BK);
 
   LA la;
   LB lb;
@@ -880,7 +799,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 
   auto dma_q = [&](int slab, int q) {                    // DMA instruction q of slab `slab`
     const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
-    const int k0 = (kb + (slab < nk ? slab : nk - 1)) * BK;
+    const int k0 = (slab < nk ? slab : nk - 1) * BK;
     if (q < NLA) la.issue_q(st, k0, q);
     else lb.issue_q(st + A_BYTES, k0, q - NLA);
   };

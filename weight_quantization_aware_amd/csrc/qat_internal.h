@@ -84,11 +84,9 @@ struct GemmArgs {
   int batch_h;
   int batches;
   int64_t sa_b, sa_h, sb_b, sb_h, sc_b, sc_h;
-  // Causal structure of attention products (rows m, columns n and the
-  // contraction index k are token positions of one sequence): 0 none;
-  // kCausalSkip: tiles whose every column exceeds every row (n > m) are not
-  // computed; kCausalLower: k runs over [0, end of the row tile); kCausalUpper:
-  // k runs over [start of the row tile, K).
+  // Causal structure of attention products (rows m and the contraction index
+  // k are token positions of one sequence): 0 none; kCausalLower: k runs over
+  // [0, end of the row tile).
   int causal;
   // kSteAdam: AdamW on the weight in the straight-through epilogue. W (the
   // same array as the const W above) and its moments mW, vW are updated in
@@ -97,14 +95,7 @@ struct GemmArgs {
   float* mW;
   float* vW;
   float adam_b1, adam_b2, adam_isbc2, adam_eps, adam_step, adam_decay;
-  // kSoftmaxGrad: the product is dP = dO v^T of one attention problem and the
-  // epilogue writes dS = escale P (dP - Dvec[row]) in bf16 over P (C, ldc),
-  // the problem's P and Dvec at b * s?_b + h * s?_h (C offsets as above).
-  // kSoftmaxProbs: the product is S = q k^T and the epilogue writes the causal
-  // probabilities P = exp2(escale S - Dvec[row]) (Dvec: the rows' base-2
-  // log-sum-exp of escale S), 0 above the diagonal, in bf16 to C.
-  const float* Dvec;
-  int64_t sd_b, sd_h;
+  // kResidMse: the scale of the loss gradient (2 / n).
   float escale;
   // kResidMse: y = resid + product (fp32, [M][ldc]; stored to Cf when
   // non-null), d = y - target (bf16 target), C = bf16(escale d), and one fp32
@@ -114,11 +105,10 @@ struct GemmArgs {
   float* partial;
 };
 
-enum Causal { kCausalNone = 0, kCausalSkip = 1, kCausalLower = 2, kCausalUpper = 3 };
+enum Causal { kCausalNone = 0, kCausalLower = 1 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
-enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4, kSoftmaxGrad = 5,
-           kSoftmaxProbs = 6, kResidMse = 7 };
+enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4, kResidMse = 5 };
 enum Layout { kKContig = 0, kMNContig = 1 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
@@ -151,13 +141,16 @@ GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s
 // [B*T][H] bf16 (head size 128, T a multiple of 64).
 void launch_flash_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B, int T,
                       int H, hipStream_t st);
-// Batched products of attention (a.batches problems, a.batch_h per sequence):
-//   kKK_F32:   C fp32 = A B^T, both K-contiguous (scores);
-//   kKK_DSOFTMAX: the same product (dP), epilogue kSoftmaxGrad (dS over P);
-//   kKK_PROBS: the same product (S), epilogue kSoftmaxProbs (P);
-//   kKMN_BF16: C bf16, A K-contiguous, B MN-contiguous (P V, dS K);
-//   kMNMN_BF16: C bf16, both MN-contiguous (P^T dO, dS^T Q).
-enum AttnGemm { kKK_F32 = 0, kKMN_BF16 = 1, kMNMN_BF16 = 2, kKK_DSOFTMAX = 3, kKK_PROBS = 4 };
-void launch_gemm_attn(const GemmArgs& a, int kind, hipStream_t st);
+// Fused causal attention backward for dK and dV (qat_attn.hip) from q, k, v,
+// the output's gradient dO [B*T][H] bf16, the forward's lse and the row terms
+// D = rowsum(dO O) [B*nh][T]; also writes dS^T [B*nh][T][T] bf16 ([key][query],
+// zero above the diagonal within every 128-query tile) for the dQ product.
+void launch_flash_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                         const float* lse, const float* D, uint16_t* dk, uint16_t* dv, uint16_t* dsT, int B, int T,
+                         int H, hipStream_t st);
+// The dQ product of attention, batched (a.batches problems, a.batch_h per
+// sequence): C bf16 = A B with A and B MN-contiguous (dS^T [key][query], k
+// [key][d]); a.causal kCausalLower.
+void launch_gemm_attn(const GemmArgs& a, hipStream_t st);
 
 }  // namespace qat

@@ -39,12 +39,10 @@ LABELS = [
     (r"k_gemm<[^>]*,\s*1,\s*1,\s*2,\s*\d>", "gemm_e2e_grads"),
     (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
     (r"k_gemm<[^>]*,\s*0,\s*0,\s*3,\s*0>", "gemm_fwd_f32"),
-    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*3,\s*5>", "attn_gemm_f32"),
-    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*5,\s*5>", "attn_gemm_dsoftmax"),
-    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*6,\s*5>", "attn_gemm_probs"),
-    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*7,\s*0>", "gemm_fwd_mse"),
+    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*5,\s*0>", "gemm_fwd_mse"),
     (r"k_attn_rowdot", "attn_rowdot"),
     (r"k_flash_fwd", "attn_fwd"),
+    (r"k_flash_bwd_kv", "attn_bwd_kv"),
     (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*0,\s*5>", "attn_gemm_bf16"),
     # k_gemm_fused<BM, BN, BK, STAGES, U2, BL, NB>
     (r"k_gemm_fused<[^>]*,\s*1,\s*0>", "gemm_fwd_fused_fp32"),
