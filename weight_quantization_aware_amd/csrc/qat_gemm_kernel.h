@@ -634,6 +634,18 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f32x4 (&a
   }
 }
 
+// Nontemporal 16-byte accesses: the AdamW stream (W, its moments and dW) is
+// touched once per step, so it bypasses the caches' retention and leaves L2
+// and the MALL to the operands of the products around it (measured: the
+// Block-AP step 5.86 -> 5.61 ms, the gradient products 2.48 -> 2.35 ms).
+__device__ __forceinline__ float4 nt_load4(const float* p) {
+  const f32x4 t = __builtin_nontemporal_load((const f32x4*)p);
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void nt_store4(float* p, const float (&v)[4]) {
+  __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, (f32x4*)p);
+}
+
 // ---------------------------------------------------------------------------
 // kSteAdam epilogue, row by row. Once the main loop has drained, the LDS is
 // free: the accumulators of one wave-row of the tile (WM rows x 256 columns,
@@ -668,9 +680,9 @@ __device__ __forceinline__ void ste_adam_rows(const GemmArgs& a, const f32x4 (&a
       const int o = row0 + k * NWAVE + wave;
       if (o < a.M && col_ok) {
         const int64_t wi = (int64_t)o * a.ldw + col, gi = (int64_t)o * a.G + gcol;
-        in.w = *(const float4*)(a.W + wi);
-        in.m = *(const float4*)(a.mW + wi);
-        in.v = *(const float4*)(a.vW + wi);
+        in.w = nt_load4(a.W + wi);
+        in.m = nt_load4(a.mW + wi);
+        in.v = nt_load4(a.vW + wi);
         in.s = a.s[gi];
         in.z = a.z[gi];
       }
@@ -717,10 +729,10 @@ __device__ __forceinline__ void ste_adam_rows(const GemmArgs& a, const f32x4 (&a
           pv[e4] = pe - a.adam_step * (mv[e4] / den);
         }
         const int64_t wi = (int64_t)o * a.ldw + col;
-        if (a.dW) *(float4*)(a.dW + wi) = make_float4(dw[0], dw[1], dw[2], dw[3]);
-        *(float4*)(a.Wupd + wi) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-        *(float4*)(a.mW + wi) = make_float4(mv[0], mv[1], mv[2], mv[3]);
-        *(float4*)(a.vW + wi) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+        if (a.dW) nt_store4(a.dW + wi, dw);
+        nt_store4(a.Wupd + wi, pv);
+        nt_store4(a.mW + wi, mv);
+        nt_store4(a.vW + wi, vv);
       }
       for (int off = 1; off < gl; off <<= 1) {
         ps += __shfl_xor(ps, off);
