@@ -1,10 +1,10 @@
-// Causal attention forward of the Block-AP step, fused (gfx950): for one
-// (sequence, head) problem and a block of 128 queries, the scores of each
-// 64-key block are formed by MFMA, folded into a running softmax (row max and
-// sum in registers) and multiplied into the output by MFMA without leaving
-// registers; only O (bf16) and the log-sum-exp of every row (fp32, base 2)
-// reach memory. The backward recomputes the probabilities from the log-sum-
-// exp in the epilogue of its score product (kSoftmaxProbs).
+// Causal attention of the Block-AP step, fused (gfx950).
+// Forward: for one (sequence, head) problem and a block of 128 queries, the
+// scores of each 64-key block are formed by MFMA, folded into a running
+// softmax (row max and sum in registers) and multiplied into the output by
+// MFMA without leaving registers; only O (bf16) and the log-sum-exp of every
+// row (fp32, base 2) reach memory. Backward (k_flash_bwd_kv, below): per block
+// of 128 keys, the probabilities are recomputed from that log-sum-exp.
 //
 // Sources: the block is Llama-2's (causal softmax attention scaled by
 // 1/sqrt(128)); see qat_block.hip.
