@@ -212,6 +212,28 @@ struct DmaTileMN {
   __device__ __forceinline__ void issue_q(uint32_t lds_tile, int k0, int q) const {
     dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
   }
+  // The lane's byte offset, within the tile, of its first read of the
+  // fragment of rows r0 .. r0 + 15 (r0 a multiple of 16) at k-step 0. The
+  // second read (k + 4) lies 4 k-rows further and k-step ks 32 ks k-rows
+  // further, both at a constant distance: the lane's k-row differs from kb
+  // only in bits 2 and 5, which the swizzle does not use.
+  __device__ __forceinline__ static int frag_off(int r0, int lane) {
+    const int j = lane & 15;
+    const int kb = 8 * (lane >> 4) + (j >> 2);
+    const int e = r0 + 4 * (j & 3);
+    return off(kb, e >> 3) + ((e >> 2) & 1) * 8;
+  }
+  // The fragment whose first read is at p (tile + frag_off + 32 ks PITCH).
+  __device__ __forceinline__ static bf16x8 frag_at(const uint8_t* p) {
+    const __attribute__((address_space(3))) uint8_t* t = (const __attribute__((address_space(3))) uint8_t*)p;
+    typedef short i16x4_ __attribute__((ext_vector_type(4)));
+    const i16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_*)t);
+    const i16x4_ hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_*)(t + 4 * PITCH));
+    typedef short i16x8_ __attribute__((ext_vector_type(8)));
+    const i16x8_ v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
   __device__ __forceinline__ static bf16x8 frag(const uint8_t* tile, int r, int ks, int lane) {
     const int j = lane & 15;
     const int kb = ks * 32 + 8 * (lane >> 4) + (j >> 2);
@@ -809,16 +831,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   la.init(a.A, a.lda, m0, a.M, a.K);
   lb.init((const uint16_t*)a.B, a.ldb, n0, a.N, a.K);
 
-  auto dma_q = [&](int slab, int q) {                    // DMA instruction q of slab `slab`
-    const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
+  // DMA instruction q of slab `slab` into the stage at byte offset soff
+  auto dma_q = [&](int slab, int q, int soff) {
+    const uint32_t st = lds0 + (uint32_t)soff;
     const int k0 = (slab < nk ? slab : nk - 1) * BK;
     if (q < NLA) la.issue_q(st, k0, q);
     else lb.issue_q(st + A_BYTES, k0, q - NLA);
   };
 
   // Fragment reads. K-contiguous tiles: lane base per k-step + immediate
-  // offsets; MN-contiguous tiles: transpose reads with per-fragment addresses.
+  // offsets; MN-contiguous tiles: transpose reads at a lane offset per
+  // fragment, computed once, + the stage and k-step as immediates.
   int a_base[2] = {0, 0}, b_base[2] = {0, 0};
+  int a_off[AMN == kKContig ? 1 : TI], b_off[BMN == kKContig ? 1 : TJ];
+  if constexpr (AMN != kKContig) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) a_off[i] = LA::frag_off(wm0 + i * 16, lane);
+  }
+  if constexpr (BMN != kKContig) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) b_off[j] = A_BYTES + LB::frag_off(wn0 + j * 16, lane);
+  }
   if constexpr (AMN == kKContig) {
     a_base[0] = LA::frag_base(wm0, 0, lane);
     a_base[1] = LA::frag_base(wm0, 1, lane);
@@ -829,11 +862,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   }
   auto read_a = [&](int st, int ks, int i) -> bf16x8 {
     if constexpr (AMN == kKContig) return *(const bf16x8*)&smem[st + a_base[ks] + i * LA::FRAG_STRIDE];
-    else return LA::frag(&smem[st], wm0 + i * 16 + (lane & 15), ks, lane);
+    else return LA::frag_at(&smem[st + a_off[i] + ks * 32 * LA::PITCH]);
   };
   auto read_b = [&](int st, int ks, int j) -> bf16x8 {
     if constexpr (BMN == kKContig) return *(const bf16x8*)&smem[st + b_base[ks] + j * LB::FRAG_STRIDE];
-    else return LB::frag(&smem[st + A_BYTES], wn0 + j * 16 + (lane & 15), ks, lane);
+    else return LB::frag_at(&smem[st + b_off[j] + ks * 32 * LB::PITCH]);
   };
   // read r of a k-step, in the order the MFMAs consume them: b0, a0 .. a(TI-1), b1 .. b(TJ-1)
   auto read_r = [&](int st, int ks, int r, Frags<TI, TJ>& f) {
@@ -850,14 +883,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 
   // One k-step: MFMA t on `cur`, then read t of the next k-step (stage nst,
   // k-step nks) into `nxt` and, every GAP MFMAs, one DMA instruction of slab
-  // dslab (none if dslab < 0).
-  auto kstep = [&](const Frags<TI, TJ>& cur, int nst, int nks, Frags<TI, TJ>& nxt, int dslab) {
+  // dslab into the stage at dsoff (none if dslab < 0).
+  auto kstep = [&](const Frags<TI, TJ>& cur, int nst, int nks, Frags<TI, TJ>& nxt, int dslab, int dsoff) {
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
       const int j = t / TI, i = t % TI;
       mfma_acc(acc[j][i], cur.b[j], cur.a[i]);
       if (t < NR) read_r(nst, nks, t, nxt);
-      if (dslab >= 0 && t % GAP == GAP - 1 && t / GAP < NL) dma_q(dslab, t / GAP);
+      if (dslab >= 0 && t % GAP == GAP - 1 && t / GAP < NL) dma_q(dslab, t / GAP, dsoff);
       sched_fence();
     }
   };
@@ -866,7 +899,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 #pragma unroll
   for (int sl = 0; sl < STAGES; ++sl)
 #pragma unroll
-    for (int q = 0; q < NL; ++q) dma_q(sl, q);
+    for (int q = 0; q < NL; ++q) dma_q(sl, q, sl * STAGE);
   wait_vmcnt<(STAGES - 1) * NL>();
   __syncthreads();
   Frags<TI, TJ> F0, F1;
@@ -877,14 +910,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   // No unrolling or peeling: a peeled copy of the last iteration (the one
   // with the drain) lets the register allocator copy accumulators between
   // AGPRs right after their MFMAs, which the hazard recogniser cannot see.
+  // The stage offsets of slabs kt and kt + 1 rotate from one iteration to
+  // the next (no modulo in the loop); slab kt + STAGES reuses slab kt's.
+  int st = 0, nx = STAGE % (STAGES * STAGE);
 #pragma clang loop unroll(disable)
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = (kt % STAGES) * STAGE, nx = ((kt + 1) % STAGES) * STAGE;
-    kstep(F0, st, 1, F1, -1);                            // k-step 0; read k-step 1
+    kstep(F0, st, 1, F1, -1, 0);                         // k-step 0; read k-step 1
     wait_vmcnt<(STAGES - 2) * NL>();
     __syncthreads();                                     // B_kt
     sched_fence();
-    kstep(F1, nx, 0, F0, kt + STAGES);                   // k-step 1; read slab kt+1; DMA
+    kstep(F1, nx, 0, F0, kt + STAGES, st);               // k-step 1; read slab kt+1; DMA
+    st = nx;
+    nx = nx + STAGE == STAGES * STAGE ? 0 : nx + STAGE;
     // The last iteration waits out the MFMA latency before leaving the loop,
     // so nothing placed after the loop (the epilogue, or spill code for an
     // accumulator) can read an accumulator before its result is written.
