@@ -107,6 +107,12 @@ __device__ __forceinline__ QElem quant_elem(float w, float s, float zr, float K)
   return e;
 }
 
+// Marks the rare branch it sits in: an empty volatile asm statement cannot be
+// hoisted out of its branch, so the code after it (the exact division of a
+// near-tie) stays behind the branch, skipped when no lane of the wave takes
+// it, instead of being computed for every element and selected.
+__device__ __forceinline__ void rare_branch(float& x) { asm volatile("" : "+v"(x)); }
+
 // quant_elem with the quotient from a reciprocal: u0 = w * r (r = fl32(1/s)),
 // refined by one residual step u = u0 + (w - u0 s) r (the residual is exact
 // with an FMA), which lands within an ulp of fl32(w / s). The code decision
@@ -118,7 +124,10 @@ __device__ __forceinline__ QElem quant_elem_rcp(float w, float s, float r, float
   const float u0 = w * r;
   const float u = __builtin_fmaf(__builtin_fmaf(-u0, s, w), r, u0);
   const float fr = u - __builtin_floorf(u);
-  if (__builtin_fabsf(fr - 0.5f) <= __builtin_fabsf(u) * 0x1p-20f + 0x1p-60f) return quant_elem(w, s, zr, K);
+  if (__builtin_fabsf(fr - 0.5f) <= __builtin_fabsf(u) * 0x1p-20f + 0x1p-60f) {
+    rare_branch(w);
+    return quant_elem(w, s, zr, K);
+  }
   QElem e;
   e.u = u;
   const float v = __builtin_rintf(u) + zr;

@@ -347,7 +347,9 @@ struct DmaRing {
           const float u = w * rcp;
           const float fr = u - floorf(u);
           if (fabsf(fr - 0.5f) <= fabsf(u) * 0x1p-20f + 0x1p-60f) {
-            h[k] = quant_elem(w, sv, zr, K).w_hat;          // near a rounding tie: exact division
+            float wt = w;
+            rare_branch(wt);
+            h[k] = quant_elem(wt, sv, zr, K).w_hat;         // near a rounding tie: exact division
           } else {
             const float qv = fminf(fmaxf(__builtin_rintf(u) + zr, 0.0f), K);
             h[k] = (qv - zr) * sv;
