@@ -318,6 +318,10 @@ struct DmaRing {
     }
   }
   // Convert one slab from the ring entry at byte p into the B stage at byte b.
+  // IL > 0: the caller's IL MFMAs of the same slab precede this in the same
+  // basic block; the conversion's VALU work is interleaved with them (all
+  // fast paths first, near-ties redone behind one branch, then the stores).
+  template <int IL = 0>
   __device__ __forceinline__ void commit(uint8_t* smem, int p, int b) const {
     constexpr int PARTS = 256 / ROWS;                      // threads per row
     constexpr int CPT = (BK / 8) / PARTS;                  // 8-element chunks per thread
@@ -325,20 +329,21 @@ struct DmaRing {
     const uint32_t* q = (const uint32_t*)&smem[p + row * DW * 4];
     const float sv = *(const float*)&smem[p + ROWS * DW * 4 + row * 4];
     const float zv = *(const float*)&smem[p + ROWS * DW * 4 + ROWS * 4 + row * 4];
+    float h[CPT][8];
+    uint32_t tie = 0;                                      // fp32: elements near a rounding tie
+    const float zr = round_clamp_zero(zv, K);
+    const float rcp = 1.0f / sv;
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
       const int c = part * CPT + cc;                       // chunk of this row's slab
-      float h[8];
       if constexpr (KIND == kPacked) {
         const int bit = c * 8 * NB;
         uint64_t w = q[bit >> 5];
         if (NB == 3 && (bit & 31) > 8) w |= (uint64_t)q[(bit >> 5) + 1] << 32;
         const uint32_t word = (uint32_t)(w >> (bit & 31));
 #pragma unroll
-        for (int k = 0; k < 8; ++k) h[k] = ((float)((word >> (NB * k)) & ((1u << NB) - 1)) - zv) * sv;
+        for (int k = 0; k < 8; ++k) h[cc][k] = ((float)((word >> (NB * k)) & ((1u << NB) - 1)) - zv) * sv;
       } else {
-        const float zr = round_clamp_zero(zv, K);
-        const float rcp = 1.0f / sv;
         const uint4 w0 = *(const uint4*)&q[c * 8], w1 = *(const uint4*)&q[c * 8 + 4];
         const uint32_t wb[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
@@ -346,18 +351,41 @@ struct DmaRing {
           const float w = __builtin_bit_cast(float, wb[k]);
           const float u = w * rcp;
           const float fr = u - floorf(u);
-          if (fabsf(fr - 0.5f) <= fabsf(u) * 0x1p-20f + 0x1p-60f) {
-            float wt = w;
-            rare_branch(wt);
-            h[k] = quant_elem(wt, sv, zr, K).w_hat;         // near a rounding tie: exact division
-          } else {
-            const float qv = fminf(fmaxf(__builtin_rintf(u) + zr, 0.0f), K);
-            h[k] = (qv - zr) * sv;
-          }
+          if (fabsf(fr - 0.5f) <= fabsf(u) * 0x1p-20f + 0x1p-60f) tie |= 1u << (cc * 8 + k);
+          const float qv = fminf(fmaxf(__builtin_rintf(u) + zr, 0.0f), K);
+          h[cc][k] = (qv - zr) * sv;
         }
       }
-      *(uint4*)&smem[b + L::off(row, c)] = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
-                                                       pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7]));
+    }
+    if constexpr (IL > 0) {
+      constexpr int NV = KIND == kPacked ? 5 : 12;          // VALU per element, roughly
+      constexpr int PER = (CPT * 8 * NV + IL - 1) / IL;
+#pragma unroll
+      for (int i = 0; i < IL; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0); // then VALU
+      }
+    }
+    if constexpr (KIND != kPacked) {
+      if (tie) {                                           // near a rounding tie: exact division
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+          const uint32_t* qc = q + (part * CPT + cc) * 8;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (tie & (1u << (cc * 8 + k))) {
+              float wt = __builtin_bit_cast(float, qc[k]);
+              rare_branch(wt);
+              h[cc][k] = quant_elem(wt, sv, zr, K).w_hat;
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int c = part * CPT + cc;
+      *(uint4*)&smem[b + L::off(row, c)] = make_uint4(pack_bf16x2(h[cc][0], h[cc][1]), pack_bf16x2(h[cc][2], h[cc][3]),
+                                                       pack_bf16x2(h[cc][4], h[cc][5]), pack_bf16x2(h[cc][6], h[cc][7]));
     }
   }
 };
@@ -995,6 +1023,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
   auto b_commit = [&](int slab) {
     lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
   };
+  auto b_commit_il = [&](int slab) {
+    lb.template commit<KS == 1 ? TI * TJ : 0>(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
+  };
 
   // Fragment reads index the __shared__ array directly (stage given as a byte
   // offset) so that they stay ds_read instructions.
@@ -1049,7 +1080,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
       read_frags(nx_, 0, CUR);                                              \
       mfmas(NXT);                                                           \
     }                                                                       \
-    b_commit((KT) + 2);                                                     \
+    b_commit_il((KT) + 2);                                                  \
   } while (0)
 
   for (int kt = 0; kt < nk; kt += (KS == 1 && U2) ? 2 : 1) {
