@@ -358,7 +358,10 @@ struct DmaRing {
       }
     }
     if constexpr (IL > 0) {
-      constexpr int NV = KIND == kPacked ? 5 : 12;          // VALU per element, roughly
+      // VALU instructions placed after each MFMA: NV per converted element,
+      // spread over the IL MFMAs (NV measured best on the 2048- and 4096-token
+      // shapes; the rest of the conversion follows the last MFMA).
+      constexpr int NV = KIND == kPacked ? 2 : 6;
       constexpr int PER = (CPT * 8 * NV + IL - 1) / IL;
 #pragma unroll
       for (int i = 0; i < IL; ++i) {
