@@ -326,6 +326,11 @@ struct DmaRing {
     constexpr int PARTS = 256 / ROWS;                      // threads per row
     constexpr int CPT = (BK / 8) / PARTS;                  // 8-element chunks per thread
     const int row = threadIdx.x / PARTS, part = threadIdx.x % PARTS;
+    // fp32 rows are 128 bytes: odd row pairs take their two chunks in the
+    // other order, so that the 16-byte reads of 8 neighbouring lanes fall on
+    // distinct banks
+    const int cx = (KIND != kPacked && PARTS == 2 && CPT == 2) ? (row >> 1) & 1 : 0;
+    auto chunk = [&](int cc) { return (part * CPT + cc) ^ cx; };
     const uint32_t* q = (const uint32_t*)&smem[p + row * DW * 4];
     const float sv = *(const float*)&smem[p + ROWS * DW * 4 + row * 4];
     const float zv = *(const float*)&smem[p + ROWS * DW * 4 + ROWS * 4 + row * 4];
@@ -335,7 +340,7 @@ struct DmaRing {
     const float rcp = 1.0f / sv;
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
-      const int c = part * CPT + cc;                       // chunk of this row's slab
+      const int c = chunk(cc);                             // chunk of this row's slab
       if constexpr (KIND == kPacked) {
         const int bit = c * 8 * NB;
         uint64_t w = q[bit >> 5];
@@ -350,9 +355,11 @@ struct DmaRing {
         for (int k = 0; k < 8; ++k) {
           const float w = __builtin_bit_cast(float, wb[k]);
           const float u = w * rcp;
-          const float fr = u - floorf(u);
-          if (fabsf(fr - 0.5f) <= fabsf(u) * 0x1p-20f + 0x1p-60f) tie |= 1u << (cc * 8 + k);
-          const float qv = fminf(fmaxf(__builtin_rintf(u) + zr, 0.0f), K);
+          const float ru = __builtin_rintf(u);
+          // distance to the nearest half-integer: 0.5 - |u - rint(u)|, exact
+          // wherever it can fall under the threshold
+          if (0.5f - fabsf(u - ru) <= fabsf(u) * 0x1p-20f + 0x1p-60f) tie |= 1u << (cc * 8 + k);
+          const float qv = fminf(fmaxf(ru + zr, 0.0f), K);
           h[cc][k] = (qv - zr) * sv;
         }
       }
@@ -373,7 +380,7 @@ struct DmaRing {
       if (tie) {                                           // near a rounding tie: exact division
 #pragma unroll
         for (int cc = 0; cc < CPT; ++cc) {
-          const uint32_t* qc = q + (part * CPT + cc) * 8;
+          const uint32_t* qc = q + chunk(cc) * 8;
 #pragma unroll
           for (int k = 0; k < 8; ++k)
             if (tie & (1u << (cc * 8 + k))) {
@@ -386,7 +393,7 @@ struct DmaRing {
     }
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
-      const int c = part * CPT + cc;
+      const int c = chunk(cc);
       *(uint4*)&smem[b + L::off(row, c)] = make_uint4(pack_bf16x2(h[cc][0], h[cc][1]), pack_bf16x2(h[cc][2], h[cc][3]),
                                                        pack_bf16x2(h[cc][4], h[cc][5]), pack_bf16x2(h[cc][6], h[cc][7]));
     }
