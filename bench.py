@@ -127,7 +127,7 @@ def main():
     Y2 = torch.empty_like(Y)
     dX2 = torch.empty_like(dX)
     ds2 = torch.empty_like(s)
-    ws = Q.workspace(max(Q.fakequant_ws_bytes(M, out, inp), Q.dequant_ws_bytes(M, out, inp)), dev)
+    ws = Q.workspace(max(Q.fakequant_ws_bytes(out, inp, bits), Q.dequant_ws_bytes(out, inp, bits)), dev)
 
     calls = [
         ("init", lambda: Q.qat_init_minmax(W, bits, s, z)),
@@ -392,7 +392,7 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp,
     # the q_proj step's fake-quant forward + backward at the other group sizes
     groups = {}
     M2, out2, in2 = X.shape[0], W.shape[0], W.shape[1]
-    ws2 = Q.workspace(Q.fakequant_ws_bytes(M2, out2, in2), dev)
+    ws2 = Q.workspace(Q.fakequant_ws_bytes(out2, in2, bits), dev)
     Y2 = torch.empty(M2, out2, dtype=torch.bfloat16, device=dev)
     dX2 = torch.empty(M2, in2, dtype=torch.bfloat16, device=dev)
     dW2 = torch.empty(out2, in2, device=dev)
@@ -421,7 +421,7 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp,
         Q.qat_init_minmax(Wc, lin.bits, sc, zc)
         c3.append((lin, Wc, Xc, dYc, sc, zc))
     M3 = c3[0][0].m
-    ws3 = Q.workspace(max(Q.fakequant_ws_bytes(M3, l.out, l.inp) for l, *_ in c3), dev)
+    ws3 = Q.workspace(max(Q.fakequant_ws_bytes(l.out, l.inp, l.bits) for l, *_ in c3), dev)
     Y3 = torch.empty(M3 * max(l.out for l, *_ in c3), dtype=torch.bfloat16, device=dev)
     dX3 = torch.empty(M3 * max(l.inp for l, *_ in c3), dtype=torch.bfloat16, device=dev)
     dW3 = torch.empty(max(l.out * l.inp for l, *_ in c3), device=dev)

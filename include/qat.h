@@ -95,8 +95,8 @@ int32_t qat_quant_codes(const float* W, const float* s, const float* z, int64_t 
                         hipStream_t stream);
 
 /* Workspace bytes that qat_fakequant_linear_fwd / _bwd need for these sizes: one bf16 W_hat
- * [out, in] (rounded up to 256 bytes). M does not change it. */
-size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in);
+ * [out, in] (rounded up to 256 bytes); the same at every bit width. 0 for invalid sizes. */
+size_t qat_fakequant_ws_bytes(int64_t out, int64_t in, int32_t bits);
 
 /*
  * a2-a4. Fake-quantised linear forward: Y = X * W_hat^T, with W_hat from
@@ -105,7 +105,7 @@ size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in);
  * note describes). X [M, in] bf16, Y [M, out] bf16; fp32 accumulation.
  * ws: NULL selects the fused kernel that quantises fp32 W tiles directly into
  * LDS (no workspace; the quantiser runs once per 256-token tile, VALU-bound);
- * otherwise >= qat_fakequant_ws_bytes(M, out, in) bytes of device memory that
+ * otherwise >= qat_fakequant_ws_bytes(out, in, bits) bytes of device memory that
  * receive a bf16 W_hat staged once per call and read by the GEMM. After the
  * call the workspace holds that W_hat, [out, in] row-major from its first
  * byte: the tensor a training step saves for its backward
@@ -124,8 +124,8 @@ int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float*
  *   ds[o,j] = sum_{i in j} Gw[o,i] * (m_i ? rint(u_i) - u_i : q_i - zr)
  *   dz[o,j] = -s[o,j] * sum_{i in j, m_i = 0} Gw[o,i]  [out, G] fp32
  * Any of dX, dW, ds, dz may be NULL to skip it (ds and dz come together: both
- * NULL or both set). When dX is wanted, ws (>= qat_fakequant_ws_bytes(M, out,
- * in) bytes, scratch) receives the bf16 W_hat transposed, [in][out], so that
+ * NULL or both set). When dX is wanted, ws (>= qat_fakequant_ws_bytes(out, in,
+ * bits) bytes, scratch) receives the bf16 W_hat transposed, [in][out], so that
  * the dX GEMM reads both operands K-contiguous; otherwise ws may be NULL. dY and
  * X are read in place (the dW GEMM contracts over tokens reading both with
  * LDS transpose loads), so no transposed copies are made.
@@ -158,8 +158,9 @@ int32_t qat_fakequant_linear_bwd_saved(const uint16_t* dY, const uint16_t* X, co
 int32_t qat_pack(const float* W, const float* s, const float* z, int64_t out, int64_t in,
                  int32_t group, int32_t bits, uint8_t* Wq, float* z_round, hipStream_t stream);
 
-/* Workspace bytes that qat_dequant_gemm_bwd_s needs: one bf16 W_hat [out, in]. */
-size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in);
+/* Workspace bytes that qat_dequant_gemm_fwd / _bwd_s need: one bf16 W_hat [out, in]
+ * (rounded up to 256 bytes); 0 for invalid sizes. */
+size_t qat_dequant_ws_bytes(int64_t out, int64_t in, int32_t bits);
 
 /*
  * a9. E2E-QP forward (modelfoundations.com note, Phase 2; Paper-Notes, E2E-QP):
@@ -167,7 +168,7 @@ size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in);
  * (frozen, integer valued); Y = X * W_hat^T.
  * ws: NULL selects the fused kernel that dequantises packed codes straight
  * into LDS inside the GEMM (no workspace; the dequantisation runs once per
- * 128- or 256-token tile); otherwise >= qat_dequant_ws_bytes(M, out, in)
+ * 128- or 256-token tile); otherwise >= qat_dequant_ws_bytes(out, in, bits)
  * bytes that receive the bf16 W_hat, staged once per call; after the call the
  * workspace holds it, [out, in] row-major from its first byte
  * (qat_dequant_gemm_bwd_s_saved reads it).
@@ -182,7 +183,7 @@ int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* 
  *   ds[o,j] = sum_{i in j} Gw[o,i] * (q_i - z[o,j]),  Gw = dY^T X (never stored);
  *   dz[o,j] = -s[o,j] * sum_{i in j} Gw[o,i]  (the train-s-and-z variant of the
  *   Paper-Notes ablation table; may be NULL).
- * When dX is wanted, ws (>= qat_dequant_ws_bytes(M, out, in) bytes, scratch)
+ * When dX is wanted, ws (>= qat_dequant_ws_bytes(out, in, bits) bytes, scratch)
  * receives the dequantised bf16 W_hat transposed, [in][out]; otherwise ws may
  * be NULL.
  */

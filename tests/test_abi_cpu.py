@@ -43,17 +43,20 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     L = Q.lib()
     for st in range(9):
-        assert L.qat_status_string(st)
+        assert L.qat_status_string(st) != b"unknown status"
+    assert L.qat_status_string(9) == b"unknown status"
     assert L.qat_last_error() == b""
 
 
 def test_workspace_sizes():
-    # one bf16 W_hat [out, in], rounded up to 256 bytes
-    assert Q.fakequant_ws_bytes(2048, 4096, 4096) == 4096 * 4096 * 2
-    assert Q.fakequant_ws_bytes(1, 64, 64) == 64 * 64 * 2
-    assert Q.fakequant_ws_bytes(7, 64, 64) == Q.fakequant_ws_bytes(4096, 64, 64)
-    assert Q.fakequant_ws_bytes(0, 64, 64) == 0
-    assert Q.dequant_ws_bytes(100, 192, 128) == Q.fakequant_ws_bytes(100, 192, 128)
+    # one bf16 W_hat [out, in], rounded up to 256 bytes, at every bit width
+    assert Q.fakequant_ws_bytes(4096, 4096, 2) == 4096 * 4096 * 2
+    assert Q.fakequant_ws_bytes(64, 64, 4) == 64 * 64 * 2
+    assert Q.fakequant_ws_bytes(4100, 64, 3) == 4100 * 64 * 2
+    assert Q.fakequant_ws_bytes(7, 64, 2) == 1024
+    assert Q.fakequant_ws_bytes(0, 64, 2) == 0
+    assert Q.fakequant_ws_bytes(64, 64, 5) == 0
+    assert Q.dequant_ws_bytes(192, 128, 3) == Q.fakequant_ws_bytes(192, 128, 3)
 
 
 FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced on the error paths
@@ -122,6 +125,7 @@ def test_saved_backward_validation():
     assert L.qat_fakequant_linear_bwd_saved(A, B, C, D, E, WH, 0, 64, 128, 64, 2, DX, None, None, None,
                                             None) == 2
     assert L.qat_dequant_gemm_bwd_s_saved(A, B, C, D, E, WH, 8, 64, 128, 64, 5, DX, FAKE * 9, None, None) == 3
+
 
 
 def test_timing_registry_host_side():
@@ -243,3 +247,84 @@ def test_block_validation():
     assert fwd == 6
     assert L.qat_block_forward(ctypes.byref(sh), _block_args(sh, step=False), G1, G2, X, T, X, LOSS, WS, need,
                                None) == 8                          # y over x
+
+
+# ---------------------------------------------------------------------------
+# The Python binding checks dtype, shape and device before the C call (the C
+# ABI sees raw pointers only). Dtype and shape are checked first, so host
+# tensors exercise them here; a host tensor that passes them is refused as
+# not on the GPU.
+# ---------------------------------------------------------------------------
+
+def _fq_args(M=8, out=64, inp=128, g=64):
+    import torch
+    return dict(X=torch.zeros(M, inp, dtype=torch.bfloat16), W=torch.zeros(out, inp),
+                s=torch.ones(out, inp // g), z=torch.zeros(out, inp // g),
+                Y=torch.zeros(M, out, dtype=torch.bfloat16))
+
+
+def test_binding_rejects_wrong_dtype_shape_device():
+    import torch
+    a = _fq_args()
+    fwd = lambda **kw: Q.qat_fakequant_linear_fwd(kw.get("X", a["X"]), kw.get("W", a["W"]), kw.get("s", a["s"]),
+                                                  kw.get("z", a["z"]), 2, kw.get("Y", a["Y"]), group=kw.get("g", 64))
+    with pytest.raises(TypeError, match="X must be"):
+        fwd(X=a["X"].float())                                          # X not bf16
+    with pytest.raises(TypeError, match="W must be"):
+        fwd(W=a["W"].double())
+    with pytest.raises(ValueError, match="s must have shape"):
+        fwd(s=torch.ones(64, 4))                                       # s sized for group 32
+    with pytest.raises(ValueError, match="W must have shape"):
+        fwd(W=torch.zeros(64, 256))                                    # W's in differs from X's
+    with pytest.raises(ValueError, match="Y must have shape"):
+        fwd(Y=torch.zeros(8, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="group 48 must divide"):
+        fwd(g=48, s=torch.ones(64, 2), z=torch.zeros(64, 2))
+    with pytest.raises(ValueError, match="contiguous"):
+        fwd(W=torch.zeros(128, 64).t())
+    with pytest.raises(ValueError, match="CUDA"):
+        fwd()                                                          # right shapes, host memory
+    # packed weights at another bit width; bwd outputs of the wrong shape
+    Wq = torch.zeros(64, 128 * 3 // 8, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="Wq must have shape"):
+        Q.qat_dequant_gemm_fwd(a["X"], Wq, a["s"], a["z"], 2, a["Y"])
+    with pytest.raises(ValueError, match="bits must be"):
+        Q.qat_pack(a["W"], a["s"], a["z"], 5, Wq)
+    dY = torch.zeros(8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dX must have shape"):
+        Q.qat_fakequant_linear_bwd(dY, a["X"], a["W"], a["s"], a["z"], 2, dX=torch.zeros(8, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="dW must be"):
+        Q.qat_fakequant_linear_bwd(dY, a["X"], a["W"], a["s"], a["z"], 2, dW=torch.zeros(64, 128, dtype=torch.half))
+    with pytest.raises(ValueError, match="ds must have shape"):
+        Q.qat_dequant_gemm_bwd_s(dY, a["X"], torch.zeros(64, 32, dtype=torch.uint8), a["s"], a["z"], 2,
+                                 torch.zeros(64, 4))
+    with pytest.raises(ValueError, match="w_hat holds"):
+        Q.qat_fakequant_linear_bwd_saved(dY, a["X"], a["W"], a["s"], a["z"], torch.zeros(100, dtype=torch.uint8), 2,
+                                         dX=torch.zeros(8, 128, dtype=torch.bfloat16))
+    # deployment: fp16 operands
+    with pytest.raises(TypeError, match="X must be"):
+        Q.qat_deploy_gemv(a["X"], torch.zeros(64, 32, dtype=torch.uint8), torch.zeros(64, 2, dtype=torch.half),
+                          torch.zeros(64, 1, dtype=torch.uint8), 2, torch.zeros(8, 64, dtype=torch.half))
+
+
+def test_binding_block_checks():
+    import torch
+    sh = Q.block_shape(256, 2, 704, 192, 2, 2)
+    lins = []
+    for o, i in [(256, 256)] * 4 + [(704, 256), (704, 256), (256, 704)]:
+        e = {"W": torch.zeros(o, i), "s": torch.ones(o, i // 64), "z": torch.zeros(o, i // 64)}
+        lins.append(e)
+    x = torch.zeros(384, 256, dtype=torch.bfloat16)
+    g = torch.ones(256)
+    loss = torch.zeros(1)
+    bad = [dict(d) for d in lins]
+    bad[6] = {"W": torch.zeros(704, 256), "s": torch.ones(704, 4), "z": torch.zeros(704, 4)}   # down transposed
+    with pytest.raises(ValueError, match="down_proj.W must have shape"):
+        Q.qat_block_forward(sh, bad, g, g, x, x, loss)
+    with pytest.raises(ValueError, match="x must have shape"):
+        Q.qat_block_forward(sh, lins, g, g, x[:100], x, loss)
+    with pytest.raises(ValueError, match="q_proj.ds is required"):
+        Q.qat_block_ap_step(sh, lins, g, g, x, x, {"lr_weight": 0, "lr_quant": 0, "beta1": 0.9, "beta2": 0.999,
+                                                   "eps": 1e-8, "weight_decay": 0, "step": 0, "total_steps": 1}, loss)
+    with pytest.raises(ValueError, match="CUDA"):
+        Q.qat_block_forward(sh, lins, g, g, x, x, loss)

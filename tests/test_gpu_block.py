@@ -3,13 +3,21 @@ against the fp64 block oracle, through the C ABI.
 
 Bars. Every block output passes through bf16 activations (h1, q, k, v, P, the
 attention output, h2, gate, up, the SiLU product and every gradient that
-enters a GEMM; unit roundoff u = 2^-9) and bf16 W_hat, while the oracle
-carries fp64 throughout. A gradient at q_proj crosses about eight such
-roundings between the loss and its GEMM (dy, down dX, SiLU backward, gate/up
-dX, RMSNorm backward, o dX, the attention backward, RoPE), each adding a
-relative Frobenius error of order u; sqrt(8) * 2 u ~ 1.1e-2. The bar is the
-one for bf16 GEMM outputs, relative Frobenius 2e-2, on the loss, the block's
-contribution y - x, every dW, ds, dz and every parameter update.
+enters a GEMM; unit roundoff u = 2^-8, 8 significant bits) and bf16 W_hat,
+while the oracle carries fp64 throughout. One round-to-nearest bf16 rounding
+adds a relative error of RMS about u / sqrt(3) ~ 2.3e-3; a gradient at
+q_proj crosses about eight such roundings between the loss and its GEMM (dy,
+down dX, SiLU backward, gate/up dX, RMSNorm backward, o dX, the attention
+backward, RoPE), sqrt(8) * 2.3e-3 ~ 6.4e-3. The bar is the one for bf16 GEMM
+outputs, relative Frobenius 2e-2, on the loss, the block's contribution
+y - x, every dW, ds, dz and every parameter update.
+Element by element, the block's contribution c = y - x must also satisfy
+|c - c_ref| <= 2^-3 (|c_ref| + rms of c_ref over the token's row): c is the
+sum of the o and down products, whose inputs each carry a few bf16 roundings,
+so an element's error is a few u/sqrt(3) of the row's scale (~1e-2 rms of
+the row scale measured); 2^-3 leaves room for the tails over a million
+elements while a token row or an output tile that is wrong as a whole (an
+error of the order of the row scale) falls outside it.
 The optimiser itself is checked tightly on the GPU's own gradients and
 moments (fp32 rounding only): AdamW is elementwise, so its outputs must equal
 the fp64 update of those inputs to a few fp32 ulps.
@@ -30,7 +38,7 @@ import torch
 
 from oracle import block_oracle as B
 from oracle import qat_oracle as O
-from tests.helpers import dev_bf16, dev_f32, rel_fro, say
+from tests.helpers import check_bound, dev_bf16, dev_f32, rel_fro, say
 from weight_quantization_aware_amd import _lib as Q
 from weight_quantization_aware_amd import synth
 
@@ -152,6 +160,13 @@ def report(name, v):
     return v
 
 
+def check_contribution(name, c, c_ref, tau=2.0 ** -3):
+    """|c - c_ref| <= tau (|c_ref| + rms over the row of c_ref), element by element."""
+    rms = np.sqrt(np.mean(c_ref * c_ref, axis=-1, keepdims=True))
+    r = check_bound(name, c, c_ref, tau * (np.abs(c_ref) + rms))
+    say(f"  {name}: largest error / element-wise bound {r:.3f}")
+
+
 CASES = [
     # hidden, heads, inter, seq, batch, bits, group
     pytest.param((256, 2, 704, 192, 2, 2, 64), id="h256-t192x2-w2g64"),
@@ -180,6 +195,12 @@ def test_block_step_parity_peaked_attention():
     # probability p dominates a row, dS cancels to about (1 - p) |dP| while the
     # bf16 rounding of P and dP stays about 2u |dP|, so the relative error
     # grows by 1 / (1 - p); at the mean p = 0.76 that is 4.2x: bar 0.1.
+    # Element by element, y - x gets tau = 2^-2 instead of 2^-3: a score S
+    # carries an error of about 2u |S| from the bf16 q and k, up to ~0.2 nats
+    # at the largest peaked scores (~30 nats), which moves the ratio of two
+    # competing probabilities by up to ~20%, and with it the attention output
+    # of such a row by a fraction of the row's scale (measured 0.14 of it at
+    # the worst of 131072 elements).
     case = (256, 2, 704, 512, 1, 2, 64)
     sh, d, params = make(case)
     say(f"block step, peaked attention {case}")
@@ -187,10 +208,10 @@ def test_block_step_parity_peaked_attention():
         W = params[n]["W"] * 8.0
         s_, z_ = O.init_minmax(W, case[5], case[6])
         params[n] = {"W": W, "s": s_, "z": z_}
-    _check_step_parity(sh, d, params, {"q_proj": 0.1, "k_proj": 0.1})
+    _check_step_parity(sh, d, params, {"q_proj": 0.1, "k_proj": 0.1}, tau=2.0 ** -2)
 
 
-def _check_step_parity(sh, d, params, bars=None):
+def _check_step_parity(sh, d, params, bars=None, tau=2.0 ** -3):
     bars = bars or {}
     o = B.AdamW()
     x64, t64 = bf(d["x"]), bf(d["target"])
@@ -206,6 +227,7 @@ def _check_step_parity(sh, d, params, bars=None):
 
     assert report("loss", abs(loss - loss_ref) / loss_ref) < BAR
     assert report("y - x", rel_fro(y - x64, ref_y - x64)) < BAR
+    check_contribution("y - x", y - x64, ref_y - x64, tau)
     worst = worst_u = worst_f = 0.0
     for i, n in enumerate(B.LINEARS):
         bar = bars.get(n, BAR)
@@ -231,6 +253,7 @@ def test_block_forward_call_matches_step_forward():
     c = B.block_forward(x64, params, d["g1"].astype(np.float64), d["g2"].astype(np.float64), sh)
     loss_ref, _ = B.mse(c["y"], bf(d["target"]))
     assert rel_fro(y_f - x64, c["y"] - x64) < BAR
+    check_contribution("y - x", y_f - x64, c["y"] - x64)
     assert abs(loss_f - loss_ref) / loss_ref < BAR
     # the forward call leaves the parameters alone; the step's forward is the same computation
     for i, n in enumerate(B.LINEARS):
@@ -313,6 +336,7 @@ def test_block_step_full_size_7b():
     rows = np.array([0, 1, 63, 64, 777, 1500, T - 1])
     yr = B.block_forward_rows(x64, params, d["g1"].astype(np.float64), d["g2"].astype(np.float64), sh, 1, rows)
     assert report("sampled y - x", rel_fro(y[T + rows] - x64[T + rows], yr - x64[T + rows])) < BAR
+    check_contribution("sampled y - x", y[T + rows] - x64[T + rows], yr - x64[T + rows])
 
     for i, n in enumerate(B.LINEARS):
         p = params[n]

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+
 #include "../../include/qat.h"
 #include "qat_internal.h"
 
@@ -113,13 +114,13 @@ QAT_API const char* qat_status_string(int32_t st) {
 
 QAT_API const char* qat_last_error(void) { return g_last_error; }
 
-QAT_API size_t qat_fakequant_ws_bytes(int64_t M, int64_t out, int64_t in) {
-  if (M <= 0 || out <= 0 || in <= 0) return 0;
+QAT_API size_t qat_fakequant_ws_bytes(int64_t out, int64_t in, int32_t bits) {
+  if (bits < 2 || bits > 4 || out <= 0 || in <= 0 || out > kMaxDim || in > kMaxDim) return 0;
   return ws_bytes_for(out, in);
 }
 
-QAT_API size_t qat_dequant_ws_bytes(int64_t M, int64_t out, int64_t in) {
-  return qat_fakequant_ws_bytes(M, out, in);
+QAT_API size_t qat_dequant_ws_bytes(int64_t out, int64_t in, int32_t bits) {
+  return qat_fakequant_ws_bytes(out, in, bits);
 }
 
 QAT_API int32_t qat_init_minmax(const float* W, int64_t out, int64_t in, int32_t group, int32_t bits,
@@ -162,21 +163,27 @@ QAT_API int32_t qat_pack(const float* W, const float* s, const float* z, int64_t
   return finish();
 }
 
-QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float* s,
-                                         const float* z, int64_t M, int64_t out, int64_t in,
-                                         int32_t group, int32_t bits, uint16_t* Y, void* ws,
-                                         size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Validation shared by the fake-quant forwards (Y over the inputs; the
+// workspace `ws` of `need` bytes, if any, over neither).
+int32_t check_fq_fwd(const uint16_t* X, const float* W, const float* s, const float* z, int64_t M, int64_t out,
+                     int64_t in, int32_t group, int32_t bits, const uint16_t* Y, const void* ws, size_t need) {
   QAT_CHECK(check_common(out, in, group, bits, true));
   QAT_CHECK(check_m(M, out, in));
   if (!X || !W || !s || !z || !Y) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({X, W, s, z, Y, ws}));
-  const size_t need = ws_bytes_for(out, in);
-  if (ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
   const size_t ng = gbytes(out, in, group);
   Range outs[] = {{Y, (size_t)(M * out * 2)}, {ws, ws ? need : 0}};
   Range ins[] = {{X, (size_t)(M * in * 2)}, {W, (size_t)(out * in * 4)}, {s, ng}, {z, ng}};
-  QAT_CHECK(check_alias(outs, 2, ins, 4));
+  return check_alias(outs, 2, ins, 4);
+}
 
+// Y = X W_hat^T: with w_hat (device memory of out * in bf16) the quantiser
+// stages W_hat there and the GEMM reads it; without, the fused kernel
+// quantises fp32 W tiles into LDS.
+void launch_fq_fwd(const uint16_t* X, const float* W, const float* s, const float* z, int64_t M, int64_t out,
+                   int64_t in, int32_t group, int32_t bits, uint16_t* Y, uint16_t* w_hat, hipStream_t stream) {
   qat::GemmArgs a = gemm_args();
   a.A = X;
   a.lda = in;
@@ -191,8 +198,7 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
   a.group = group;
   a.Kq = (float)((1 << bits) - 1);
   a.ldb = in;
-  if (ws) {
-    uint16_t* w_hat = (uint16_t*)ws;
+  if (w_hat) {
     qat::launch_quant_codes(W, s, z, out, in, group, bits, nullptr, w_hat, stream);
     a.B = w_hat;
     qat::launch_gemm_fwd(a, qat::kBf16, bits, stream);
@@ -200,8 +206,21 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
     a.B = W;
     qat::launch_gemm_fwd(a, qat::kFp32Quant, bits, stream);
   }
+}
+
+}  // namespace
+
+QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float* s,
+                                         const float* z, int64_t M, int64_t out, int64_t in,
+                                         int32_t group, int32_t bits, uint16_t* Y, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  const size_t need = ws_bytes_for(out, in);
+  QAT_CHECK(check_fq_fwd(X, W, s, z, M, out, in, group, bits, Y, ws, need));
+  if (ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
+  launch_fq_fwd(X, W, s, z, M, out, in, group, bits, Y, (uint16_t*)ws, stream);
   return finish();
 }
+
 
 namespace qat {
 
