@@ -66,7 +66,9 @@ enum {
   QAT_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                               */
   QAT_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the size query returns          */
   QAT_ERR_HIP = 7,       /* a HIP launch failed; qat_last_error() has the HIP message      */
-  QAT_ERR_ALIAS = 8      /* an output overlaps an input or another output                  */
+  QAT_ERR_ALIAS = 8,     /* an output overlaps an input or another output                  */
+  QAT_ERR_SCRATCH = 9    /* the problem exceeds the static scratch of the no-allocation
+                            entry point (qat_noalloc_max_weights)                          */
 };
 
 /* Text of a status code (static storage). */
@@ -114,6 +116,24 @@ size_t qat_fakequant_ws_bytes(int64_t out, int64_t in, int32_t bits);
 int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, const float* s, const float* z,
                                  int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
                                  uint16_t* Y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): the forward of
+ * qat_fakequant_linear_fwd with a workspace, bit-identical to it, whose W_hat
+ * is staged in a static device array of qat_noalloc_max_weights() bf16 values
+ * (48 Mi, 96 MiB) that the library holds on each GPU it runs on until the
+ * process ends. Allocates nothing. Returns QAT_ERR_SCRATCH when out * in
+ * exceeds that maximum (nothing enqueued), and QAT_ERR_HIP if the array's
+ * device address cannot be looked up. Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller. The array keeps the last
+ * call's W_hat; nothing in it has to start at zero.
+ */
+int64_t qat_noalloc_max_weights(void);
+int32_t qat_fakequant_linear_fwd_noalloc(const uint16_t* X, const float* W, const float* s, const float* z,
+                                         int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
+                                         uint16_t* Y, hipStream_t stream);
 
 /*
  * a5-a7. Straight-through backward (paperlayer.ai summary, Appendix A; the

@@ -42,9 +42,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = Q.lib()
-    for st in range(9):
+    for st in range(10):
         assert L.qat_status_string(st) != b"unknown status"
-    assert L.qat_status_string(9) == b"unknown status"
+    assert L.qat_status_string(10) == b"unknown status"
     assert L.qat_last_error() == b""
 
 
@@ -126,6 +126,17 @@ def test_saved_backward_validation():
                                             None) == 2
     assert L.qat_dequant_gemm_bwd_s_saved(A, B, C, D, E, WH, 8, 64, 128, 64, 5, DX, FAKE * 9, None, None) == 3
 
+
+def test_noalloc_forward_validation():
+    L = Q.lib()
+    A, B, C, D, E = ((FAKE << 12) * k for k in range(1, 6))        # 4 GiB apart: no overlaps
+    assert L.qat_noalloc_max_weights() == 48 << 20
+    # more weights than the static scratch holds: refused before any launch
+    assert L.qat_fakequant_linear_fwd_noalloc(A, B, C, D, 1, 8192, 8192, 64, 2, E, None) == 9
+    # the checks of the workspace forward
+    assert L.qat_fakequant_linear_fwd_noalloc(A, B, C, D, 0, 64, 128, 64, 2, E, None) == 2
+    assert L.qat_fakequant_linear_fwd_noalloc(A, None, C, D, 8, 64, 128, 64, 2, E, None) == 1
+    assert L.qat_fakequant_linear_fwd_noalloc(A, B, C, D, 8, 64, 128, 64, 2, A, None) == 8
 
 
 def test_timing_registry_host_side():

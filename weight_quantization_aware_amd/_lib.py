@@ -51,10 +51,13 @@ _SIGS = {
     "qat_peak_scratch_bytes": [_c_i32],
     "qat_peak_mfma": [_c_i32, _c_i32, _c_vp, _c_vp],
     "qat_peak_read": [_c_vp, _c_sz, _c_i32, _c_vp, _c_vp],
+    "qat_fakequant_linear_fwd_noalloc": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
+                                         _c_vp, _c_vp],
+    "qat_noalloc_max_weights": [],
     "qat_status_string": [_c_i32],
     "qat_last_error": [],
 }
-_RES = {"qat_deploy_zq_stride": _c_i64, "qat_fakequant_ws_bytes": _c_sz, "qat_dequant_ws_bytes": _c_sz, "qat_peak_mfma_flops": _c_i64,
+_RES = {"qat_deploy_zq_stride": _c_i64, "qat_noalloc_max_weights": _c_i64, "qat_fakequant_ws_bytes": _c_sz, "qat_dequant_ws_bytes": _c_sz, "qat_peak_mfma_flops": _c_i64,
         "qat_peak_scratch_bytes": _c_sz,
         "qat_status_string": ctypes.c_char_p, "qat_last_error": ctypes.c_char_p}
 
@@ -263,6 +266,24 @@ def qat_fakequant_linear_fwd(X, W, s, z, bits, Y, ws=None, group: int = GROUP) -
             M, out, inp, group, bits, a.t("Y", Y, BF16, (M, out)))
     a.done()
     _call(fn, *args, *_ws(a, ws, fakequant_ws_bytes(out, inp, bits)), _stream())
+
+
+def noalloc_max_weights() -> int:
+    return int(lib().qat_noalloc_max_weights())
+
+
+def qat_fakequant_linear_fwd_noalloc(X, W, s, z, bits, Y, group: int = GROUP) -> None:
+    """The staged forward with W_hat in the library's static device scratch
+    (allocates nothing; out * in <= noalloc_max_weights())."""
+    fn = "qat_fakequant_linear_fwd_noalloc"
+    M, inp = _dims2(fn, "X", X, "[M, in]")
+    out = _dims2(fn, "W", W, "[out, in]")[0]
+    G = _groups(fn, inp, group)
+    a = _Args(fn)
+    args = (a.t("X", X, BF16), a.t("W", W, F32, (out, inp)), a.t("s", s, F32, (out, G)), a.t("z", z, F32, (out, G)),
+            M, out, inp, group, bits, a.t("Y", Y, BF16, (M, out)))
+    a.done()
+    _call(fn, *args, _stream())
 
 
 def qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=None, dW=None, ds=None, dz=None, ws=None,

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/qat.h"
 #include "qat_internal.h"
@@ -108,6 +109,7 @@ QAT_API const char* qat_status_string(int32_t st) {
     case QAT_ERR_WORKSPACE: return "workspace missing or too small";
     case QAT_ERR_HIP: return "HIP launch failed (see qat_last_error)";
     case QAT_ERR_ALIAS: return "an output overlaps an input or another output";
+    case QAT_ERR_SCRATCH: return "out * in exceeds the static scratch of the no-allocation entry point (qat_noalloc_max_weights)";
     default: return "unknown status";
   }
 }
@@ -221,6 +223,78 @@ QAT_API int32_t qat_fakequant_linear_fwd(const uint16_t* X, const float* W, cons
   return finish();
 }
 
+// ---------------------------------------------------------------------------
+// The staged forward for callers that cannot allocate device memory. Its
+// W_hat lives in `scratch`, a file-scope device array of kScratchWeights bf16
+// values of which each GPU that runs the library holds one copy until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address of each
+// GPU's copy is looked up once per device, with that device current, and
+// kept in g_scratch. The array has external linkage (in a namespace of its
+// own): the runtime resolves a device variable through the code object's
+// dynamic symbol table, which lists a namespace-scope __device__ variable
+// (GLOBAL, PROTECTED, like the kernels) but not a `static` one (LOCAL only),
+// and its lookup of a static one aborts the process.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchWeights = int64_t(48) << 20;   // 96 MiB of bf16: out * in <= 48 Mi
+
+namespace qat {
+namespace noalloc {
+__device__ __align__(256) uint16_t scratch[kScratchWeights];
+}  // namespace noalloc
+}  // namespace qat
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint16_t* g_scratch[kMaxDevices] = {};
+
+int32_t hip_error(hipError_t e) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return QAT_ERR_HIP;
+}
+
+// The device address of the scratch copy on the device that runs `stream`.
+int32_t scratch_for(hipStream_t stream, uint16_t** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_error(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_error(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_error(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_error(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(qat::noalloc::scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_error(e);
+    if (!p) return hip_error(hipErrorInvalidSymbol);
+    g_scratch[dev] = (uint16_t*)p;
+  }
+  *out = g_scratch[dev];
+  return QAT_OK;
+}
+
+}  // namespace
+
+QAT_API int64_t qat_noalloc_max_weights(void) { return kScratchWeights; }
+
+QAT_API int32_t qat_fakequant_linear_fwd_noalloc(const uint16_t* X, const float* W, const float* s, const float* z,
+                                                 int64_t M, int64_t out, int64_t in, int32_t group, int32_t bits,
+                                                 uint16_t* Y, hipStream_t stream) {
+  QAT_CHECK(check_fq_fwd(X, W, s, z, M, out, in, group, bits, Y, nullptr, 0));
+  if (out * in > kScratchWeights) return QAT_ERR_SCRATCH;
+  uint16_t* w_hat = nullptr;
+  QAT_CHECK(scratch_for(stream, &w_hat));
+  launch_fq_fwd(X, W, s, z, M, out, in, group, bits, Y, w_hat, stream);
+  return finish();
+}
 
 namespace qat {
 
