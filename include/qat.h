@@ -144,11 +144,14 @@ int32_t qat_fakequant_linear_fwd_noalloc(const uint16_t* X, const float* W, cons
  *   ds[o,j] = sum_{i in j} Gw[o,i] * (m_i ? rint(u_i) - u_i : q_i - zr)
  *   dz[o,j] = -s[o,j] * sum_{i in j, m_i = 0} Gw[o,i]  [out, G] fp32
  * Any of dX, dW, ds, dz may be NULL to skip it (ds and dz come together: both
- * NULL or both set). When dX is wanted, ws (>= qat_fakequant_ws_bytes(out, in,
- * bits) bytes, scratch) receives the bf16 W_hat transposed, [in][out], so that
- * the dX GEMM reads both operands K-contiguous; otherwise ws may be NULL. dY and
- * X are read in place (the dW GEMM contracts over tokens reading both with
- * LDS transpose loads), so no transposed copies are made.
+ * NULL or both set). ws, when dX is wanted: NULL recomputes W_hat from W, s,
+ * z inside the dX GEMM (W's rows quantised straight into LDS, no workspace);
+ * otherwise >= qat_fakequant_ws_bytes(out, in, bits) bytes of scratch that
+ * receive the bf16 W_hat transposed, [in][out], so that the dX GEMM reads
+ * both operands K-contiguous. Both give the same dX bit for bit. ws is unused
+ * when dX is NULL. dY and X are read in place (the dW GEMM contracts over
+ * tokens reading both with LDS transpose loads), so no transposed copies are
+ * made.
  */
 int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* W,
                                  const float* s, const float* z, int64_t M, int64_t out, int64_t in,
@@ -203,9 +206,11 @@ int32_t qat_dequant_gemm_fwd(const uint16_t* X, const uint8_t* Wq, const float* 
  *   ds[o,j] = sum_{i in j} Gw[o,i] * (q_i - z[o,j]),  Gw = dY^T X (never stored);
  *   dz[o,j] = -s[o,j] * sum_{i in j} Gw[o,i]  (the train-s-and-z variant of the
  *   Paper-Notes ablation table; may be NULL).
- * When dX is wanted, ws (>= qat_dequant_ws_bytes(out, in, bits) bytes, scratch)
- * receives the dequantised bf16 W_hat transposed, [in][out]; otherwise ws may
- * be NULL.
+ * ws, when dX is wanted: NULL dequantises the packed codes inside the dX
+ * GEMM (straight into LDS, no workspace); otherwise >= qat_dequant_ws_bytes(
+ * out, in, bits) bytes of scratch that receive the dequantised bf16 W_hat
+ * transposed, [in][out]. Both give the same dX bit for bit. ws is unused when
+ * dX is NULL.
  */
 int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, const uint8_t* Wq,
                                const float* s, const float* z, int64_t M, int64_t out, int64_t in,

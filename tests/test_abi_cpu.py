@@ -86,9 +86,11 @@ def test_fwd_bwd_validation():
     assert L.qat_fakequant_linear_fwd(A, B, C, D, 8, 64, 128, 64, 2, E, FAKE * 7, 16, None) == 6
     # fwd: M <= 0
     assert L.qat_fakequant_linear_fwd(A, B, C, D, 0, 64, 128, 64, 2, E, None, 0, None) == 2
-    # bwd: a workspace is required when dX is wanted
+    # bwd: a workspace, when given for dX, must hold W_hat (NULL: W_hat is made inside the dX GEMM)
     assert L.qat_fakequant_linear_bwd(A, B, C, D, E, 8, 64, 128, 64, 2, FAKE * 6, None, None, None,
-                                      None, 0, None) == 6
+                                      FAKE * 7, 16, None) == 6
+    assert L.qat_dequant_gemm_bwd_s(A, B, C, D, E, 8, 64, 128, 64, 2, FAKE * 6, FAKE * 8, None, FAKE * 7,
+                                    16, None) == 6
     # out must be a multiple of 64
     assert L.qat_fakequant_linear_fwd(A, B, C, D, 8, 96, 128, 64, 2, E, None, 0, None) == 2
     # bwd: ds without dz

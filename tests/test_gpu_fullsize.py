@@ -19,6 +19,8 @@ exact restrictions of the full results. Samples include the first and last
 token, row and column (the ragged edges of the tile grid).
 Tolerances: the element-wise bounds above, and beside them relative
 Frobenius 2e-2 for bf16 outputs and 1e-5 for fp32 outputs; codes bit-exact.
+The backwards without a workspace (W_hat made inside the dX GEMM) give the
+staging backward's dX bit for bit at q_proj and at the E2E-QP workloads.
 """
 import numpy as np
 import pytest
@@ -113,6 +115,12 @@ def test_fakequant_q_proj_whole():
     s, z = O.init_minmax(W, b)
     s, z = synth.perturb_qparams(7, s, z, b)          # make clamp, mask and dz non-trivial
     Y, gX, gW, gs, gz = _run_fakequant(lin, W, X, dY, s, z)
+    # the backward without a workspace (W_hat made in the dX GEMM's LDS)
+    gX2 = torch.empty_like(gX)
+    Q.qat_fakequant_linear_bwd(dev_bf16(dY), dev_bf16(X), dev_f32(W), dev_f32(s), dev_f32(z), b, dX=gX2)
+    torch.cuda.synchronize()
+    assert torch.equal(gX, gX2)
+    del gX2
     wh = w_hat_exact(W, s, z, b)
     ry = check_gemm_bf16("Y", host_bits(Y), X, wh, TOL_BF16)
     rx = check_gemm_bf16("dX", host_bits(gX), dY, wh.T.copy(), TOL_BF16)
@@ -202,8 +210,13 @@ def test_e2e_full_size_every_tile(cfg, name, bits):
     gs = torch.empty(out, inp // 64, device="cuda")
     gz = torch.empty_like(gs)
     Q.qat_dequant_gemm_bwd_s(dY_, X_, Wq_, s_, z_, b, gs, dX=gX, dz=gz, ws=ws)
+    gX2 = torch.empty_like(gX)
+    gs2 = torch.empty_like(gs)
+    Q.qat_dequant_gemm_bwd_s(dY_, X_, Wq_, s_, z_, b, gs2, dX=gX2)            # no workspace
     torch.cuda.synchronize()
     assert torch.equal(Y, Yf)
+    assert torch.equal(gX, gX2) and torch.equal(gs, gs2)
+    del gX2, gs2
 
     T, R, C = tile_samples(M, 128, g), tile_samples(out, 64, g), tile_samples(inp, 64, g)
     wh = e2e_w_hat_exact(Wq, s, z, inp, b)

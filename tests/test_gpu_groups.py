@@ -9,7 +9,8 @@ a channel-wise row length that is not a power of two (192), and each way
 the gradient epilogue finishes a group: stored per 64- or 32-column chunk,
 summed over the tile's chunks and stored (group 128, or a whole row that fits
 one tile), or summed per tile and accumulated (whole rows over several
-tiles). The backwards on the forward's saved W_hat match the staging ones bit
+tiles). The backwards on the forward's saved W_hat, and those without a
+workspace (W_hat made in the dX GEMM's LDS), match the staging ones bit
 for bit at every group size (ds, dz of whole-row groups to fp32 reassociation:
 their per-tile atomic adds meet in no fixed order).
 """
@@ -108,19 +109,21 @@ def test_fakequant_fwd_bwd(M, out, inp, group, bits):
     saved = ws.clone()                                          # the forward's W_hat
     Q.qat_fakequant_linear_fwd(Xd, Wd, sd, zd, bits, Yf, ws=None, group=gs)
     outs = []
-    for use_saved in (False, True):
+    for variant in ("staging", "saved", "no workspace"):
         gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
         gW = torch.empty(out, inp, device="cuda")
         gs_ = torch.full((out, inp // gs), 9.0, device="cuda")  # must be overwritten, not accumulated
         gz = torch.full_like(gs_, 9.0)
-        if use_saved:
+        if variant == "saved":
             Q.qat_fakequant_linear_bwd_saved(dYd, Xd, Wd, sd, zd, saved, bits, dX=gX, dW=gW, ds=gs_, dz=gz,
                                              group=gs)
         else:
-            Q.qat_fakequant_linear_bwd(dYd, Xd, Wd, sd, zd, bits, dX=gX, dW=gW, ds=gs_, dz=gz, ws=ws, group=gs)
+            Q.qat_fakequant_linear_bwd(dYd, Xd, Wd, sd, zd, bits, dX=gX, dW=gW, ds=gs_, dz=gz,
+                                       ws=ws if variant == "staging" else None, group=gs)
         outs.append((gX, gW, gs_, gz))
     torch.cuda.synchronize()
-    _same_backward(outs, gs == inp, 2)
+    _same_backward(outs[:2], gs == inp, 2)
+    _same_backward(outs[::2], gs == inp, 2)
     gX, gW, gs_, gz = outs[0]
     assert torch.equal(Y, Yf)
     wh = w_hat_exact(W, s, z, bits, gs)
@@ -150,17 +153,19 @@ def test_e2e_fwd_bwd(M, out, inp, group, bits):
     saved = ws.clone()                                          # the forward's W_hat
     Q.qat_dequant_gemm_fwd(Xd, Wqd, sd, zd, bits, Yf, group=gs)
     outs = []
-    for use_saved in (False, True):
+    for variant in ("staging", "saved", "no workspace"):
         gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
         gs_ = torch.full((out, inp // gs), 9.0, device="cuda")
         gz = torch.full_like(gs_, 9.0)
-        if use_saved:
+        if variant == "saved":
             Q.qat_dequant_gemm_bwd_s_saved(dYd, Xd, Wqd, sd, zd, saved, bits, gs_, dX=gX, dz=gz, group=gs)
         else:
-            Q.qat_dequant_gemm_bwd_s(dYd, Xd, Wqd, sd, zd, bits, gs_, dX=gX, dz=gz, ws=ws, group=gs)
+            Q.qat_dequant_gemm_bwd_s(dYd, Xd, Wqd, sd, zd, bits, gs_, dX=gX, dz=gz,
+                                     ws=ws if variant == "staging" else None, group=gs)
         outs.append((gX, gs_, gz))
     torch.cuda.synchronize()
-    _same_backward(outs, gs == inp, 1)
+    _same_backward(outs[:2], gs == inp, 1)
+    _same_backward(outs[::2], gs == inp, 1)
     gX, gs_, gz = outs[0]
     assert torch.equal(Y, Yf)
     wh = e2e_w_hat_exact(Wq, s, z, inp, bits, gs)

@@ -339,6 +339,69 @@ def test_saved_backward_equals_staging_backward(M, out, inp, bits):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("M,out,inp,bits", [(128, 256, 256, 2), (300, 320, 512, 3), (1, 64, 64, 4),
+                                             (2085, 4096, 256, 2), (100, 4160, 4160, 3), (4196, 4160, 128, 4)])
+def test_backward_without_workspace(M, out, inp, bits):
+    # ws = NULL: the dX GEMM makes W_hat in LDS from the fp32 master weight
+    # (fake-quant) or the packed codes (E2E-QP), read along the weight's rows.
+    # Same bf16 operand, same k order as the staging backward: every output is
+    # bit-identical to it, and dX is inside the element-wise bound.
+    say(f"no-workspace backward M={M} out={out} in={inp} bits={bits}")
+    W, X, dY = _inputs(M, out, inp, 110 + bits)
+    s, z = _qparams(W, bits, True, 11)
+    dY_, X_, W_, s_, z_ = dev_bf16(dY), dev_bf16(X), dev_f32(W), dev_f32(s), dev_f32(z)
+    ws = Q.workspace(Q.fakequant_ws_bytes(out, inp, bits))
+    outs = []
+    for w in (ws, None):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gW = torch.empty(out, inp, device="cuda")
+        gs = torch.empty(out, inp // 64, device="cuda")
+        gz = torch.empty_like(gs)
+        Q.qat_fakequant_linear_bwd(dY_, X_, W_, s_, z_, bits, dX=gX, dW=gW, ds=gs, dz=gz, ws=w)
+        outs.append((gX, gW, gs, gz))
+    torch.cuda.synchronize()
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
+    check_gemm_bf16("dX", host_bits(outs[1][0]), dY, w_hat_exact(W, s, z, bits).T.copy(), TOL_BF16)
+    Wq = synth.packed_codes(112, bits, out, inp, bits)
+    es, ez = synth.e2e_scales(112, bits, out, inp), synth.e2e_zeros(112, bits, out, inp, bits)
+    dq, es_, ez_ = dev_u8(Wq), dev_f32(es), dev_f32(ez)
+    outs = []
+    for w in (ws, None):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gs = torch.empty(out, inp // 64, device="cuda")
+        Q.qat_dequant_gemm_bwd_s(dY_, X_, dq, es_, ez_, bits, gs, dX=gX, ws=w)
+        outs.append((gX, gs))
+    torch.cuda.synchronize()
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
+    check_gemm_bf16("dX", host_bits(outs[1][0]), dY, e2e_w_hat_exact(Wq, es, ez, inp, bits).T.copy(), TOL_BF16)
+
+
+def test_backward_without_workspace_near_tie():
+    # weights on and one ulp beside rounding ties through the transposed fp32
+    # ring of the no-workspace dX: the exact-division fallback gives the
+    # staging backward's W_hat, so dX is bit-identical
+    say("no-workspace backward near-tie")
+    M, out, inp, bits = 96, 128, 256, 2
+    g = np.random.default_rng(12)
+    s = g.uniform(0.01, 0.02, (out, inp // 64)).astype(np.float32)
+    z = g.integers(0, 4, (out, inp // 64)).astype(np.float32)
+    half = g.integers(-4, 5, (out, inp)) + 0.5
+    W = (half * np.repeat(s, 64, 1)).astype(np.float32)
+    W[:, ::3] = np.nextafter(W[:, ::3], np.float32(np.inf))
+    W[:, 1::3] = np.nextafter(W[:, 1::3], np.float32(-np.inf))
+    dY = synth.grad_out(42, 0, M, out)
+    args = (dev_bf16(dY), dev_bf16(synth.activations(42, 0, M, inp)), dev_f32(W), dev_f32(s), dev_f32(z), bits)
+    g1 = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+    g2 = torch.empty_like(g1)
+    Q.qat_fakequant_linear_bwd(*args, dX=g1, ws=Q.workspace(Q.fakequant_ws_bytes(out, inp, bits)))
+    Q.qat_fakequant_linear_bwd(*args, dX=g2)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g2)
+    check_gemm_bf16("dX", host_bits(g2), dY, w_hat_exact(W, s, z, bits).T.copy(), TOL_BF16)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_pack_then_dequant_gemm_equals_fakequant_forward(bits):
     # Cross-path: with the hard-rounded zero point, dequant(pack(W)) is the same

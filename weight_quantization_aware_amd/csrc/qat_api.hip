@@ -315,6 +315,28 @@ void launch_linear_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, in
   qat::launch_gemm_dx(a, stream);
 }
 
+// dX = dY W_hat with W_hat made in LDS from B (the fp32 master weight,
+// ldb elements per row, or packed codes, ldb bytes per row) inside the GEMM.
+void launch_linear_dx_fused(const uint16_t* dY, const void* B, int64_t ldb, const float* s, const float* z, int64_t M,
+                            int64_t out, int64_t in, int group, int bits, uint16_t* dX, int bload, hipStream_t stream) {
+  qat::GemmArgs a = gemm_args();
+  a.A = dY;
+  a.lda = out;
+  a.B = B;
+  a.ldb = ldb;
+  a.M = (int)M;
+  a.N = (int)in;
+  a.K = (int)out;
+  a.C = dX;
+  a.ldc = in;
+  a.s = s;
+  a.z = z;
+  a.G = in / group;
+  a.group = group;
+  a.Kq = (float)((1 << bits) - 1);
+  qat::launch_gemm_dx_fused(a, bload, bits, stream);
+}
+
 // Gw = dY^T X over the M tokens, both read in place, reduced by the epilogue.
 qat::GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z,
                                 int64_t M, int64_t out, int64_t in, int group, int bits) {
@@ -350,7 +372,7 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
   if ((ds == nullptr) != (dz == nullptr)) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({dY, X, W, s, z, dX, dW, ds, dz, ws}));
   const size_t need = ws_bytes_for(out, in);
-  if (dX && (!ws || ws_bytes < need)) return QAT_ERR_WORKSPACE;
+  if (dX && ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
   const size_t ng = gbytes(out, in, group);
   Range outs[] = {{dX, (size_t)(M * in * 2)}, {dW, (size_t)(out * in * 4)}, {ds, ng}, {dz, ng},
                   {dX ? ws : nullptr, need}};
@@ -358,10 +380,12 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
                  {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 5, ins, 5));
 
-  if (dX) {
+  if (dX && ws) {
     uint16_t* w_hat = (uint16_t*)ws;
     qat::launch_w_hat_t(W, s, z, out, in, group, bits, w_hat, stream);
     qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
+  } else if (dX) {
+    qat::launch_linear_dx_fused(dY, W, in, s, z, M, out, in, group, bits, dX, qat::kFp32Quant, stream);
   }
   if (dW || ds) {
     qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
@@ -471,17 +495,19 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
   if (!dY || !X || !Wq || !s || !z || !ds) return QAT_ERR_NULL;
   QAT_CHECK(check_ptrs({dY, X, Wq, s, z, dX, ds, dz, ws}));
   const size_t need = ws_bytes_for(out, in);
-  if (dX && (!ws || ws_bytes < need)) return QAT_ERR_WORKSPACE;
+  if (dX && ws && ws_bytes < need) return QAT_ERR_WORKSPACE;
   const size_t ng = gbytes(out, in, group);
   Range outs[] = {{dX, (size_t)(M * in * 2)}, {ds, ng}, {dz, ng}, {dX ? ws : nullptr, need}};
   Range ins[] = {{dY, (size_t)(M * out * 2)}, {X, (size_t)(M * in * 2)},
                  {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}};
   QAT_CHECK(check_alias(outs, 4, ins, 5));
 
-  if (dX) {
+  if (dX && ws) {
     uint16_t* w_hat = (uint16_t*)ws;
     qat::launch_dequant_t(Wq, s, z, out, in, group, bits, w_hat, stream);
     qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
+  } else if (dX) {
+    qat::launch_linear_dx_fused(dY, Wq, in * bits / 8, s, z, M, out, in, group, bits, dX, qat::kPacked, stream);
   }
   qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
   a.Wq = Wq;

@@ -25,8 +25,9 @@ int64_t tiles(const GemmArgs& a, int bm, int bn) {
 // the forward, 1 the dX GEMM, 5 the products of attention (same code,
 // distinct kernel symbols so that profiles can tell them apart).
 constexpr int kTagAttn = 5;
-template <int BL, int EP, int NB>
+template <int BL, int EP, int NB, int BT = 0>
 constexpr const char* gemm_label() {
+  if (BT == 1) return BL == kFp32Quant ? "gemm_dx_fused_fp32" : "gemm_dx_packed";
   if (EP == kSteGrads) return "gemm_ste_grads";
   if (EP == kSteAdam) return "gemm_ste_grads_adamw";
   if (EP == kE2eScaleGrad) return "gemm_e2e_grads";
@@ -47,10 +48,10 @@ void launch_bf16(const GemmArgs& a, hipStream_t st) {
                      dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
-template <int BM, int BN, int BK, int S, int BL, int NB>
+template <int BM, int BN, int BK, int S, int BL, int NB, int BT = 0>
 void launch_fused(const GemmArgs& a, hipStream_t st) {
-  LaunchTimer t(gemm_label<BL, kStoreBf16, NB>(), st);
-  hipLaunchKernelGGL((k_gemm_fused<BM, BN, BK, S, 0, BL, NB>), dim3((unsigned)tiles(a, BM, BN)), dim3(256), 0,
+  LaunchTimer t(gemm_label<BL, kStoreBf16, NB, BT>(), st);
+  hipLaunchKernelGGL((k_gemm_fused<BM, BN, BK, S, 0, BL, NB, BT>), dim3((unsigned)tiles(a, BM, BN)), dim3(256), 0,
                      st, a);
 }
 
@@ -117,7 +118,28 @@ void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
   }
 }
 
+// dX = dY W_hat with W_hat made in LDS from the weight's rows (the
+// transposed ring): fp32 master weight with 128-column B tiles; packed codes
+// with 256-column B tiles (a 32-row slab of 3-bit rows is then whole dwords).
+template <int BL, int NB>
+void launch_pick_dx_fused(const GemmArgs& a, hipStream_t st) {
+  if constexpr (BL == kPacked) {
+    if (tiles(a, 256, 256) >= 256) launch_fused<256, 256, 32, 4, BL, NB, 1>(a, st);
+    else launch_fused<128, 256, 32, 4, BL, NB, 1>(a, st);
+  } else {
+    if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, 32, 3, BL, NB, 1>(a, st);
+    else launch_fused<128, 128, 32, 3, BL, NB, 1>(a, st);
+  }
+}
+
 }  // namespace
+
+void launch_gemm_dx_fused(const GemmArgs& a, int bload, int bits, hipStream_t st) {
+  if (bload == kFp32Quant) launch_pick_dx_fused<kFp32Quant, 0>(a, st);
+  else if (bits == 2) launch_pick_dx_fused<kPacked, 2>(a, st);
+  else if (bits == 3) launch_pick_dx_fused<kPacked, 3>(a, st);
+  else launch_pick_dx_fused<kPacked, 4>(a, st);
+}
 
 void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st) {
   if (bload == kBf16) launch_pick<kKContig, kKContig, kStoreBf16, 0>(a, st);

@@ -17,6 +17,8 @@
 // with LDS transpose loads. Both spread a fragment read over distinct bank
 // slots.
 #pragma once
+#include <type_traits>
+
 #include "qat_device.h"
 #include "qat_dma.h"
 #include "qat_internal.h"
@@ -405,6 +407,151 @@ __device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
   if constexpr (BL == kFp32Quant) l.init(a.B, a.ldb * 4, n0, a.N, a.s, a.z, a.G, a.group, a.Kq);
   else l.init(a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.group, a.Kq);
 }
+
+// The weight as the B operand of dX = dY W_hat (contraction over the weight's
+// rows): B[n][k] = W_hat[k][n], so a slab is BK weight rows k0 .. k0 + BK - 1
+// of ROWS consecutive weights n0 .. n0 + ROWS - 1 each (fp32 master weight,
+// 4 ROWS bytes per row, by 16-byte DMA; or packed codes, ROWS N / 8 bytes per
+// row, by dword DMA, since 3-bit rows are only 8-byte aligned), followed by
+// the (s, z) of every 32-weight slot of those rows: s[BK][SL], z[BK][SL],
+// slot t holding the group of weight n0 + 32 t (groups of 32 or more never
+// split a slot). Every thread converts its share -- fp32: 4 consecutive
+// weights of one row per step; packed: 8 -- with the quantiser of DmaRing,
+// into the bf16 B stage in the MN-contiguous layout of DmaTileMN ([BK][ROWS],
+// read back with transpose loads). Weight rows at or beyond the contraction's
+// end (kdim) read as zero and convert to exactly 0.
+template <int ROWS, int BK, int KIND, int NB>
+struct DmaRingT {
+  using LT = DmaTileMN<ROWS, BK, 4>;
+  static constexpr int RB = KIND == kPacked ? ROWS * NB / 8 : ROWS * 4;    // ring bytes per weight row
+  static constexpr int SL = ROWS / 32;                                      // (s, z) slots per row
+  static constexpr int W_BYTES = BK * RB;
+  static constexpr int P_BYTES = W_BYTES + 2 * BK * SL * 4;
+  static constexpr int DMA_B = KIND == kPacked ? 256 : 1024;               // bytes per DMA instruction
+  static constexpr int NI_Q = W_BYTES / DMA_B / 4;                          // weight DMAs per wave
+  static constexpr int NI_S = 2 * BK * SL / 64 / 4;                         // s and z DMAs per wave
+  static constexpr int NI = NI_Q + NI_S;
+  static_assert(NI_Q * DMA_B * 4 == W_BYTES && NI_S * 256 == 2 * BK * SL, "ring tile shape");
+  static_assert(KIND == kPacked || RB % 16 == 0, "16-byte DMA pieces of fp32 rows");
+  i32x4 rq, rsz[2];
+  uint32_t vq[NI_Q], vs[NI_S];
+  int wave, kdim;
+  int64_t row_bytes, grow;                                                  // weight / (s, z) row strides
+  float K;
+  // Wsrc: the weight [kdim][ld] (fp32) or its packed rows (row_bytes each);
+  // n0: first weight column of the tile; s, z: [kdim][G].
+  __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes_, int n0, int kdim_, const float* s,
+                                       const float* z, int64_t G, int group, float K_) {
+    K = K_;
+    kdim = kdim_;
+    row_bytes = row_bytes_;
+    grow = G * 4;
+    const int64_t cb = KIND == kPacked ? (int64_t)n0 * NB / 8 : (int64_t)n0 * 4;
+    rq = buffer_rsrc((const uint8_t*)Wsrc + cb, (int64_t)kdim * row_bytes - cb);
+    rsz[0] = buffer_rsrc(s, (int64_t)kdim * G * 4);
+    rsz[1] = buffer_rsrc(z, (int64_t)kdim * G * 4);
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int q = 0; q < NI_Q; ++q) {
+      const int b = ((wave * NI_Q + q) * 64 + lane) * (DMA_B / 64);      // byte of the [BK][RB] slab
+      vq[q] = (uint32_t)((b / RB) * row_bytes + b % RB);
+    }
+#pragma unroll
+    for (int q = 0; q < NI_S; ++q) {
+      const int r = ((wave * NI_S + q) * 64 + lane) % (BK * SL);         // slot of [BK][SL]
+      vs[q] = (uint32_t)((r / SL) * G * 4 + ((n0 + 32 * (r % SL)) / group) * 4);
+    }
+  }
+  // lds_p: this slab's ring entry; k0: its first weight row.
+  __device__ __forceinline__ void issue(uint32_t lds_p, int k0) const {
+    const uint32_t rb = (uint32_t)(k0 * row_bytes), gb = (uint32_t)(k0 * grow);
+#pragma unroll
+    for (int q = 0; q < NI_Q; ++q) {
+      const uint32_t dst = lds_p + (uint32_t)((wave * NI_Q + q) * DMA_B);
+      if constexpr (KIND == kPacked) dma4(rq, dst, vq[q] + rb);
+      else dma16(rq, dst, vq[q] + rb);
+    }
+#pragma unroll
+    for (int q = 0; q < NI_S; ++q) {
+      const int which = ((wave * NI_S + q) * 64) / (BK * SL);  // 0: s, 1: z (uniform per instruction)
+      i32x4 r = which ? rsz[1] : rsz[0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_readfirstlane(r[e]);
+      dma4(r, lds_p + W_BYTES + (uint32_t)((wave * NI_S + q) * 256), vs[q] + gb);
+    }
+  }
+  // Convert the slab of weight rows k0 .. from the ring entry at byte p into
+  // the B stage at byte b.
+  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int k0) const {
+    const float* sl = (const float*)&smem[p + W_BYTES];
+    const float* zl = sl + BK * SL;
+    if constexpr (KIND == kPacked) {
+      constexpr int CPR = ROWS / 8, CPT = BK * CPR / 256;                  // 8-weight chunks
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int ch = threadIdx.x + 256 * i, k = ch / CPR, c = ch % CPR;
+        const uint32_t* q = (const uint32_t*)&smem[p + k * RB];
+        const int bit = c * 8 * NB;
+        uint64_t w = q[bit >> 5];
+        if (NB == 3 && (bit & 31) > 8) w |= (uint64_t)q[(bit >> 5) + 1] << 32;
+        const uint32_t word = (uint32_t)(w >> (bit & 31));
+        const float sv = sl[k * SL + c / 4], zv = zl[k * SL + c / 4];
+        const bool live = k0 + k < kdim;
+        float h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = live ? ((float)((word >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv : 0.0f;
+        *(uint4*)&smem[b + LT::off(k, c)] = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
+                                                        pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7]));
+      }
+    } else {
+      constexpr int QPR = ROWS / 4, QPT = BK * QPR / 256;                  // 4-weight quads
+      static_assert(QPT <= 8, "tie mask bits");
+      float h[QPT][4];
+      uint32_t tie = 0;
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const int qd = threadIdx.x + 256 * i, k = qd / QPR, qc = qd % QPR;
+        const float4 w4 = *(const float4*)&smem[p + k * RB + qc * 16];
+        const float sv = sl[k * SL + qc / 8];
+        const float zr = round_clamp_zero(zl[k * SL + qc / 8], K);
+        const float rcp = 1.0f / sv;
+        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float u = wv[e] * rcp;
+          const float ru = __builtin_rintf(u);
+          if (0.5f - fabsf(u - ru) <= fabsf(u) * 0x1p-20f + 0x1p-60f) tie |= 1u << (i * 4 + e);
+          const float qv = fminf(fmaxf(ru + zr, 0.0f), K);
+          h[i][e] = (qv - zr) * sv;
+        }
+      }
+      if (tie) {                                              // near a rounding tie: exact division
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+          const int qd = threadIdx.x + 256 * i, k = qd / QPR, qc = qd % QPR;
+          const float* wr = (const float*)&smem[p + k * RB + qc * 16];
+          const float sv = sl[k * SL + qc / 8];
+          const float zr = round_clamp_zero(zl[k * SL + qc / 8], K);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (tie & (1u << (i * 4 + e))) {
+              float wt = wr[e];
+              rare_branch(wt);
+              h[i][e] = quant_elem(wt, sv, zr, K).w_hat;
+            }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const int qd = threadIdx.x + 256 * i, k = qd / QPR, qc = qd % QPR;
+        const bool live = k0 + k < kdim;
+        *(uint2*)&smem[b + LT::off(k, qc >> 1) + (qc & 1) * 8] =
+            live ? make_uint2(pack_bf16x2(h[i][0], h[i][1]), pack_bf16x2(h[i][2], h[i][3])) : make_uint2(0u, 0u);
+      }
+    }
+  }
+};
 
 // Four consecutive codes c0..c0+3 (c0 % 4 == 0) of a packed row.
 template <int NB>
@@ -991,13 +1138,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 // stage slab kt - 1 has just released. The ring runs one slab ahead of A and
 // is converted into the bf16 B stage two slabs ahead of the MFMAs.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int U2, int BL, int NB>
+template <int BM, int BN, int BK, int STAGES, int U2, int BL, int NB, int BT = 0>
 __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
   using L = LdsLayout<BK, kLdsSlots>;
   using LA = DmaTileK<BM, BK, kLdsSlots>;
-  using LB = DmaRing<BN, BK, BL, NB>;
-  using FB = DmaTileK<BN, BK, kLdsSlots>;                 // B fragment reader
+  // BT = 0: B rows are weight rows (Y = X W_hat^T); BT = 1: B rows are weight
+  // columns (dX = dY W_hat), the stage MN-contiguous
+  using LB = typename std::conditional<BT == 0, DmaRing<BN, BK, BL, NB>, DmaRingT<BN, BK, BL, NB>>::type;
+  using FB = typename std::conditional<BT == 0, DmaTileK<BN, BK, kLdsSlots>, DmaTileMN<BN, BK, 4>>::type;
   static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
+  static_assert(BT == 0 || (BK == 32 && U2 == 0), "the transposed ring runs one k-step per slab");
   static_assert(STAGES >= 3, "the shifted pipeline needs three stages");
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TI = WM / 16, TJ = WN / 16;
@@ -1019,7 +1169,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
   LA la;
   LB lb;
   la.init(a.A, a.lda, m0, a.M, a.K);
-  init_b<BL>(lb, a, n0);
+  if constexpr (BT == 0) init_b<BL>(lb, a, n0);
+  else lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, a.Kq);
   constexpr int NL = LA::NI + LB::NI;                     // DMA instructions per wave per slab
 
   const int nk = (a.K + BK - 1) / BK;
@@ -1031,10 +1182,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
     lb.issue(lds0 + P0 + (uint32_t)(((slab + 1) % STAGES) * P_STAGE), clamp_slab(slab + 1) * BK);
   };
   auto b_commit = [&](int slab) {
-    lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
+    if constexpr (BT == 0) lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
+    else lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES, slab * BK);
   };
   auto b_commit_il = [&](int slab) {
-    lb.template commit<KS == 1 ? TI * TJ : 0>(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
+    if constexpr (BT == 0)
+      lb.template commit<KS == 1 ? TI * TJ : 0>(smem, P0 + (slab % STAGES) * P_STAGE,
+                                                 (slab % STAGES) * STAGE + A_BYTES);
+    else lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES, slab * BK);
   };
 
   // Fragment reads index the __shared__ array directly (stage given as a byte

@@ -117,6 +117,11 @@ void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
 void launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 // The same product on W_hat [out][in] read in place (B MN-contiguous, ldb = in).
 void launch_gemm_dx_mn(const GemmArgs& a, hipStream_t st);
+// The same product with W_hat made in LDS from the weight itself (no
+// workspace): bload kFp32Quant (a.B the fp32 master weight [out][ldb]) or
+// kPacked (a.B the packed codes, ldb bytes per row); a.s, a.z, a.G, a.group,
+// a.Kq as for the fused forward; K = out must be a multiple of 32.
+void launch_gemm_dx_fused(const GemmArgs& a, int bload, int bits, hipStream_t st);
 // The forward product (K-contiguous operands) with the kResidMse epilogue;
 // returns the number of workgroups launched (one loss partial each), at most
 // gemm_fwd_max_workgroups(M, N).
@@ -134,6 +139,8 @@ void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st);
 // dW, ds, dz left to the caller).
 void launch_linear_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, int64_t out, int64_t in,
                       uint16_t* dX, hipStream_t st);
+void launch_linear_dx_fused(const uint16_t* dY, const void* B, int64_t ldb, const float* s, const float* z, int64_t M,
+                            int64_t out, int64_t in, int group, int bits, uint16_t* dX, int bload, hipStream_t st);
 GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z, int64_t M,
                            int64_t out, int64_t in, int group, int bits);
 // Fused causal attention forward (qat_attn.hip): O [B*T][H] bf16 and the
