@@ -26,9 +26,11 @@
  *   per row). group must divide in; G = in / group groups per row.
  *   s, z, ds, dz are [out, G] fp32 row-major. X is [M, in], Y and dY are
  *   [M, out], dX is [M, in]; all bf16 passed as uint16_t bit patterns.
- * - bits N in {2, 3, 4}; K = 2^N - 1. in is a multiple of 64. The four GEMM calls
- *   (fake-quant fwd/bwd, dequant-GEMM fwd/bwd) also need out % 64 == 0, so the
- *   backward GEMM that contracts over out works in whole 64-wide slabs; M is any
+ * - bits N in {2, 3, 4}; K = 2^N - 1. in is a multiple of 64. The GEMM calls
+ *   (fake-quant fwd/bwd, dequant-GEMM fwd/bwd) take any out with out % 4 == 0
+ *   (so that bf16 rows of out elements, Y and dY, are 8-byte aligned); out
+ *   need not fill a tile: when it is not a multiple of 64, dY is read by 4-byte
+ *   DMA and the dX contraction over out is zero-filled past its end. M is any
  *   positive count of tokens. Every operand must be smaller than 2 GiB.
  * - All tensor pointers are DEVICE pointers owned by the caller. The library
  *   never allocates, frees or keeps them beyond the enqueued work.
@@ -59,8 +61,8 @@ extern "C" {
 enum {
   QAT_OK = 0,
   QAT_ERR_NULL = 1,      /* a required pointer is NULL                                   */
-  QAT_ERR_SHAPE = 2,     /* a dimension <= 0, in (or, for the GEMM calls, out) not a
-                            multiple of 64, or an operand of 2 GiB or more                  */
+  QAT_ERR_SHAPE = 2,     /* a dimension <= 0, in not a multiple of 64, out not a multiple
+                            of 4 (GEMM calls), or an operand of 2 GiB or more               */
   QAT_ERR_BITS = 3,      /* bits not in {2, 3, 4}                                          */
   QAT_ERR_GROUP = 4,     /* group not 32, 64, 128 or in, or not dividing in                */
   QAT_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                               */

@@ -91,8 +91,10 @@ def test_fwd_bwd_validation():
                                       FAKE * 7, 16, None) == 6
     assert L.qat_dequant_gemm_bwd_s(A, B, C, D, E, 8, 64, 128, 64, 2, FAKE * 6, FAKE * 8, None, FAKE * 7,
                                     16, None) == 6
-    # out must be a multiple of 64
-    assert L.qat_fakequant_linear_fwd(A, B, C, D, 8, 96, 128, 64, 2, E, None, 0, None) == 2
+    # the GEMM calls need out % 4 == 0 (8-byte aligned rows of Y and dY)
+    for out in (98, 97, 1):
+        assert L.qat_fakequant_linear_fwd(A, B, C, D, 8, out, 128, 64, 2, E, None, 0, None) == 2
+        assert L.qat_dequant_gemm_fwd(A, B, C, D, 8, out, 128, 64, 2, E, None, 0, None) == 2
     # bwd: ds without dz
     assert L.qat_fakequant_linear_bwd(A, B, C, D, E, 8, 64, 128, 64, 2, None, None, FAKE * 6, None,
                                       FAKE * 7, 1 << 30, None) == 1

@@ -143,6 +143,7 @@ def check_dw(dW, dY, X, m, r):
     within the fp32 accumulation bound over the M tokens of dY^T X."""
     a, x = O.bf16_bits_to_f64(dY), O.bf16_bits_to_f64(X)
     check_bound("dW", dW, r["dW"], np.where(m, f32_gemm_bound(np.abs(a).T @ np.abs(x), a.shape[0]), 0.0))
+    assert np.array_equal(dW == 0, ~m | (r["Gw"] == 0))      # the mask itself
 
 
 @pytest.mark.parametrize("M,out,inp,bits", FQ_CASES)
@@ -400,6 +401,90 @@ def test_backward_without_workspace_near_tie():
     torch.cuda.synchronize()
     assert torch.equal(g1, g2)
     check_gemm_bf16("dX", host_bits(g2), dY, w_hat_exact(W, s, z, bits).T.copy(), TOL_BF16)
+
+
+RAGGED_OUT = [
+    # M, out, in, bits, group: out a multiple of 4 but not of 64
+    (300, 4100, 512, 2, 64),
+    (77, 11000, 256, 3, 64),
+    (130, 100, 256, 4, 32),
+    (64, 36, 128, 2, 128),
+    (1, 4100, 192, 3, 192),          # channel-wise
+]
+
+
+@pytest.mark.parametrize("M,out,inp,bits,group", RAGGED_OUT)
+def test_ragged_out(M, out, inp, bits, group):
+    # every GEMM call with out not a multiple of 64 (rows of dY only 8-byte
+    # aligned when out % 8 == 4; the dX contraction over out ends mid-slab):
+    # forward staged and fused, the three backwards (staging, saved W_hat, no
+    # workspace) against the oracle and against each other, and the E2E-QP pair
+    say(f"ragged out M={M} out={out} in={inp} bits={bits} group={group}")
+    W = synth.weight(120, bits, out, inp, 0.02, True)
+    X = synth.activations(120, bits, M, inp, 4)
+    dY = synth.grad_out(120, bits, M, out)
+    s, z = O.init_minmax(W, bits, group)
+    s, z = synth.perturb_qparams(12, s, z, bits)
+    G = inp // group
+    dY_, X_, W_, s_, z_ = dev_bf16(dY), dev_bf16(X), dev_f32(W), dev_f32(s), dev_f32(z)
+    ws = Q.workspace(Q.fakequant_ws_bytes(out, inp, bits))
+    Y = torch.empty(M, out, dtype=torch.bfloat16, device="cuda")
+    Yf = torch.empty_like(Y)
+    Q.qat_fakequant_linear_fwd(X_, W_, s_, z_, bits, Y, ws=ws, group=group)
+    saved = ws.clone()
+    Q.qat_fakequant_linear_fwd(X_, W_, s_, z_, bits, Yf, group=group)
+    outs = []
+    for variant in ("staging", "saved", "no workspace"):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gW = torch.empty(out, inp, device="cuda")
+        gs = torch.empty(out, G, device="cuda")
+        gz = torch.empty_like(gs)
+        if variant == "saved":
+            Q.qat_fakequant_linear_bwd_saved(dY_, X_, W_, s_, z_, saved, bits, dX=gX, dW=gW, ds=gs, dz=gz, group=group)
+        else:
+            Q.qat_fakequant_linear_bwd(dY_, X_, W_, s_, z_, bits, dX=gX, dW=gW, ds=gs, dz=gz,
+                                       ws=ws if variant == "staging" else None, group=group)
+        outs.append((gX, gW, gs, gz))
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Yf)
+    for o in outs[1:]:
+        assert torch.equal(outs[0][0], o[0]) and torch.equal(outs[0][1], o[1])
+        assert rel_fro(o[2].cpu().numpy(), outs[0][2].cpu().numpy()) < 1e-6
+    wh = w_hat_exact(W, s, z, bits, group)
+    check_gemm_bf16("Y", host_bits(Y), X, wh, TOL_BF16)
+    check_gemm_bf16("dX", host_bits(outs[0][0]), dY, wh.T.copy(), TOL_BF16)
+    r = O.fakequant_bwd(dY, X, W, s, z, bits, group)
+    m = O.quantize(W, s, z, bits, group)["m"]
+    gX, gW, gs, gz = outs[0]
+    check_dw(gW.cpu().numpy(), dY, X, m, r)
+    assert rel_fro(gs.cpu().numpy(), r["ds"]) < TOL_F32
+    if np.any(r["dz"] != 0):
+        assert rel_fro(gz.cpu().numpy(), r["dz"]) < TOL_F32
+    # E2E-QP on the packed weight of the same shape
+    Wq = synth.packed_codes(121, bits, out, inp, bits)
+    g = np.random.default_rng(121)
+    es = g.uniform(0.005, 0.05, (out, G)).astype(np.float32)
+    ez = g.integers(0, 1 << bits, (out, G)).astype(np.float32)
+    dq, es_, ez_ = dev_u8(Wq), dev_f32(es), dev_f32(ez)
+    Y1 = torch.empty_like(Y)
+    Y2 = torch.empty_like(Y)
+    Q.qat_dequant_gemm_fwd(X_, dq, es_, ez_, bits, Y1, ws=ws, group=group)
+    Q.qat_dequant_gemm_fwd(X_, dq, es_, ez_, bits, Y2, group=group)
+    outs = []
+    for w in (ws, None):
+        gX = torch.empty(M, inp, dtype=torch.bfloat16, device="cuda")
+        gs = torch.empty(out, G, device="cuda")
+        gz = torch.empty_like(gs)
+        Q.qat_dequant_gemm_bwd_s(dY_, X_, dq, es_, ez_, bits, gs, dX=gX, dz=gz, ws=w, group=group)
+        outs.append((gX, gs, gz))
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(outs[0][0], outs[1][0])
+    whe = e2e_w_hat_exact(Wq, es, ez, inp, bits, group)
+    check_gemm_bf16("Y", host_bits(Y1), X, whe, TOL_BF16)
+    check_gemm_bf16("dX", host_bits(outs[0][0]), dY, whe.T.copy(), TOL_BF16)
+    r = O.dequant_gemm_bwd_s(dY, X, Wq, es, ez, inp, bits, group)
+    assert rel_fro(outs[0][1].cpu().numpy(), r["ds"]) < TOL_F32
+    assert rel_fro(outs[0][2].cpu().numpy(), r["dz"]) < TOL_F32
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])

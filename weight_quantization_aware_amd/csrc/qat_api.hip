@@ -45,13 +45,14 @@ int32_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
   return QAT_OK;
 }
 
-// Elementwise calls accept any row count; the GEMM calls (gemm = true) also need
-// out % 64 == 0 because the backward dX GEMM contracts over out in 64-wide slabs.
-// Groups: 32, 64 or 128 elements along `in`, or the whole row (group == in,
-// channel-wise).
+// Elementwise calls accept any row count; the GEMM calls (gemm = true) need
+// out % 4 == 0: bf16 rows of `out` elements (Y, dY) are then 8-byte aligned,
+// which the 8-byte stores of Y and the 4-byte DMAs that read such dY (out not
+// a multiple of 64) rely on. Groups: 32, 64 or 128 elements along `in`, or the
+// whole row (group == in, channel-wise).
 int32_t check_common(int64_t out, int64_t in, int32_t group, int32_t bits, bool gemm = false) {
   if (bits < 2 || bits > 4) return QAT_ERR_BITS;
-  if (out <= 0 || in <= 0 || in % 64 != 0 || (gemm && out % 64 != 0)) return QAT_ERR_SHAPE;
+  if (out <= 0 || in <= 0 || in % 64 != 0 || (gemm && out % 4 != 0)) return QAT_ERR_SHAPE;
   if (out > kMaxDim || in > kMaxDim || out * in * 4 > kMaxBytes) return QAT_ERR_SHAPE;
   if (!(group == 32 || group == 64 || group == 128 || group == in) || in % group != 0) return QAT_ERR_GROUP;
   return QAT_OK;
@@ -102,7 +103,7 @@ QAT_API const char* qat_status_string(int32_t st) {
   switch (st) {
     case QAT_OK: return "ok";
     case QAT_ERR_NULL: return "a required pointer is NULL";
-    case QAT_ERR_SHAPE: return "invalid shape (dimension <= 0, in or out not a multiple of 64, or an operand of 2 GiB or more)";
+    case QAT_ERR_SHAPE: return "invalid shape (dimension <= 0, in not a multiple of 64, out not a multiple of 4 for the GEMM calls, or an operand of 2 GiB or more)";
     case QAT_ERR_BITS: return "bits must be 2, 3 or 4";
     case QAT_ERR_GROUP: return "group must be 32, 64, 128 or in (channel-wise), dividing in";
     case QAT_ERR_ALIGN: return "a pointer is not 16-byte aligned";
@@ -382,8 +383,13 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
 
   if (dX && ws) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_w_hat_t(W, s, z, out, in, group, bits, w_hat, stream);
-    qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
+    if (out % 64 == 0) {                     // W_hat^T: both dX operands K-contiguous
+      qat::launch_w_hat_t(W, s, z, out, in, group, bits, w_hat, stream);
+      qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
+    } else {                                 // W_hat [out][in], read MN-contiguous
+      qat::launch_quant_codes(W, s, z, out, in, group, bits, nullptr, w_hat, stream);
+      qat::launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
+    }
   } else if (dX) {
     qat::launch_linear_dx_fused(dY, W, in, s, z, M, out, in, group, bits, dX, qat::kFp32Quant, stream);
   }
@@ -400,8 +406,8 @@ QAT_API int32_t qat_fakequant_linear_bwd(const uint16_t* dY, const uint16_t* X, 
 }
 
 // dX = dY W_hat on a W_hat [out][in] staged by a forward call, read in place.
-static void launch_linear_dx_saved(const uint16_t* dY, const uint16_t* w_hat, int64_t M, int64_t out, int64_t in,
-                            uint16_t* dX, hipStream_t stream) {
+void qat::launch_linear_dx_saved(const uint16_t* dY, const uint16_t* w_hat, int64_t M, int64_t out, int64_t in,
+                                 uint16_t* dX, hipStream_t stream) {
   qat::GemmArgs a = gemm_args();
   a.A = dY;
   a.lda = out;
@@ -431,7 +437,7 @@ QAT_API int32_t qat_fakequant_linear_bwd_saved(const uint16_t* dY, const uint16_
                  {s, ng}, {z, ng}, {dX ? w_hat : nullptr, (size_t)(out * in * 2)}};
   QAT_CHECK(check_alias(outs, 4, ins, 6));
 
-  if (dX) launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
+  if (dX) qat::launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
   if (dW || ds) {
     qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
     a.W = W;
@@ -504,8 +510,13 @@ QAT_API int32_t qat_dequant_gemm_bwd_s(const uint16_t* dY, const uint16_t* X, co
 
   if (dX && ws) {
     uint16_t* w_hat = (uint16_t*)ws;
-    qat::launch_dequant_t(Wq, s, z, out, in, group, bits, w_hat, stream);
-    qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
+    if (out % 64 == 0) {
+      qat::launch_dequant_t(Wq, s, z, out, in, group, bits, w_hat, stream);
+      qat::launch_linear_dx(dY, w_hat, M, out, in, dX, stream);
+    } else {
+      qat::launch_dequant(Wq, s, z, out, in, group, bits, w_hat, stream);
+      qat::launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
+    }
   } else if (dX) {
     qat::launch_linear_dx_fused(dY, Wq, in * bits / 8, s, z, M, out, in, group, bits, dX, qat::kPacked, stream);
   }
@@ -532,7 +543,7 @@ QAT_API int32_t qat_dequant_gemm_bwd_s_saved(const uint16_t* dY, const uint16_t*
                  {Wq, (size_t)(out * in * bits / 8)}, {s, ng}, {z, ng}, {dX ? w_hat : nullptr, (size_t)(out * in * 2)}};
   QAT_CHECK(check_alias(outs, 3, ins, 6));
 
-  if (dX) launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
+  if (dX) qat::launch_linear_dx_saved(dY, w_hat, M, out, in, dX, stream);
   qat::GemmArgs a = qat::linear_grads_args(dY, X, s, z, M, out, in, group, bits);
   a.Wq = Wq;
   a.ldq = in * bits / 8;

@@ -48,11 +48,11 @@ void launch_bf16(const GemmArgs& a, hipStream_t st) {
                      dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
-template <int BM, int BN, int BK, int S, int BL, int NB, int BT = 0>
+template <int BM, int BN, int BK, int S, int BL, int NB, int BT = 0, int ADW = 0>
 void launch_fused(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<BL, kStoreBf16, NB, BT>(), st);
-  hipLaunchKernelGGL((k_gemm_fused<BM, BN, BK, S, 0, BL, NB, BT>), dim3((unsigned)tiles(a, BM, BN)), dim3(256), 0,
-                     st, a);
+  hipLaunchKernelGGL((k_gemm_fused<BM, BN, BK, S, 0, BL, NB, BT, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(256),
+                     0, st, a);
 }
 
 // Returns the number of workgroups launched.
@@ -75,10 +75,10 @@ int64_t launch_pick(const GemmArgs& a, hipStream_t st) {
 // of 32 (GM 1) and groups that tile BN (GM 2: 128, or a short whole row) are
 // stored directly; whole rows wider than BN (GM 3) are accumulated per tile
 // into ds and dz, zero-filled here first.
-template <int EP, int NB, int GM>
+template <int EP, int NB, int GM, int AL = kMNContig>
 void launch_pick_grads_gm(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kMNContig, kMNContig, EP, NB, GM>(a, st);
-  else launch_bf16<128, 128, 4, 2, 2, kMNContig, kMNContig, EP, NB, GM>(a, st);
+  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, AL, kMNContig, EP, NB, GM>(a, st);
+  else launch_bf16<128, 128, 4, 2, 2, AL, kMNContig, EP, NB, GM>(a, st);
 }
 
 // The weight-updating epilogue streams whole 256-column tile rows (groups of
@@ -88,23 +88,31 @@ void launch_grads_adam(const GemmArgs& a, hipStream_t st) {
   launch_bf16<256, 256, 2, 2, 4, kMNContig, kMNContig, kSteAdam, 0, 0>(a, st);
 }
 
-template <int EP, int NB>
-void launch_grads(const GemmArgs& a, hipStream_t st) {
+// AL: the layout of A = dY^T (kMNContigD when dY's rows of `out` elements
+// are not 16-byte aligned).
+template <int EP, int NB, int AL>
+void launch_grads_al(const GemmArgs& a, hipStream_t st) {
   if (a.group == 64) {
-    launch_pick<kMNContig, kMNContig, EP, NB>(a, st);
+    launch_pick<AL, kMNContig, EP, NB>(a, st);
   } else if (a.group == 32) {
-    launch_pick_grads_gm<EP, NB, 1>(a, st);
+    launch_pick_grads_gm<EP, NB, 1, AL>(a, st);
   } else {
     const int bn = tiles(a, 256, 256) >= 256 ? 256 : 128;
     if (bn % a.group == 0) {
-      launch_pick_grads_gm<EP, NB, 2>(a, st);
+      launch_pick_grads_gm<EP, NB, 2, AL>(a, st);
     } else {
       const int64_t n = (int64_t)a.M * a.G;
       if (a.ds) launch_fill_zero(a.ds, n, st);
       if (a.dz) launch_fill_zero(a.dz, n, st);
-      launch_pick_grads_gm<EP, NB, 3>(a, st);
+      launch_pick_grads_gm<EP, NB, 3, AL>(a, st);
     }
   }
+}
+
+template <int EP, int NB>
+void launch_grads(const GemmArgs& a, hipStream_t st) {
+  if (a.lda % 8 == 0) launch_grads_al<EP, NB, kMNContig>(a, st);
+  else launch_grads_al<EP, NB, kMNContigD>(a, st);
 }
 
 template <int BL, int NB>
@@ -121,15 +129,23 @@ void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
 // dX = dY W_hat with W_hat made in LDS from the weight's rows (the
 // transposed ring): fp32 master weight with 128-column B tiles; packed codes
 // with 256-column B tiles (a 32-row slab of 3-bit rows is then whole dwords).
+// ADW: dY by 4-byte DMA with the contraction's tail masked (out not a
+// multiple of 64).
+template <int BL, int NB, int ADW>
+void launch_pick_dx_fused_a(const GemmArgs& a, hipStream_t st) {
+  if constexpr (BL == kPacked) {
+    if (tiles(a, 256, 256) >= 256) launch_fused<256, 256, 32, 4, BL, NB, 1, ADW>(a, st);
+    else launch_fused<128, 256, 32, 4, BL, NB, 1, ADW>(a, st);
+  } else {
+    if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, 32, 3, BL, NB, 1, ADW>(a, st);
+    else launch_fused<128, 128, 32, 3, BL, NB, 1, ADW>(a, st);
+  }
+}
+
 template <int BL, int NB>
 void launch_pick_dx_fused(const GemmArgs& a, hipStream_t st) {
-  if constexpr (BL == kPacked) {
-    if (tiles(a, 256, 256) >= 256) launch_fused<256, 256, 32, 4, BL, NB, 1>(a, st);
-    else launch_fused<128, 256, 32, 4, BL, NB, 1>(a, st);
-  } else {
-    if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, 32, 3, BL, NB, 1>(a, st);
-    else launch_fused<128, 128, 32, 3, BL, NB, 1>(a, st);
-  }
+  if (a.K % 64 == 0 && a.lda % 8 == 0) launch_pick_dx_fused_a<BL, NB, 0>(a, st);
+  else launch_pick_dx_fused_a<BL, NB, 1>(a, st);
 }
 
 }  // namespace
@@ -166,10 +182,18 @@ void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {
 // block's shapes (4096 tokens) and 4% more at 2048 tokens (128x256 tiles);
 // 8 waves also beyond K = 4096 (measured faster with this loader at
 // K = 11008).
+template <int AL>
+void launch_gemm_dx_mn_al(const GemmArgs& a, hipStream_t st) {
+  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
+  else if (tiles(a, 128, 256) >= 192) launch_bf16<128, 256, 3, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
+  else launch_bf16<128, 128, 4, 2, 2, AL, kMNContig, kStoreBf16, 1>(a, st);
+}
+
+// dY by 4-byte DMA with the contraction's tail masked when out (K) is not a
+// multiple of 64; W_hat's k-rows at or beyond K read as zero either way.
 void launch_gemm_dx_mn(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, kKContig, kMNContig, kStoreBf16, 1>(a, st);
-  else if (tiles(a, 128, 256) >= 192) launch_bf16<128, 256, 3, 2, 4, kKContig, kMNContig, kStoreBf16, 1>(a, st);
-  else launch_bf16<128, 128, 4, 2, 2, kKContig, kMNContig, kStoreBf16, 1>(a, st);
+  if (a.K % 64 == 0 && a.lda % 8 == 0) launch_gemm_dx_mn_al<kKContig>(a, st);
+  else launch_gemm_dx_mn_al<kKContigD>(a, st);
 }
 
 int64_t launch_gemm_fwd_mse(const GemmArgs& a, hipStream_t st) {

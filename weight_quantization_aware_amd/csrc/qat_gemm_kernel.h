@@ -117,38 +117,56 @@ struct LdsLayout {
 // LDS read, which would collapse the multi-stage pipeline; the kernel waits on
 // vmcnt itself. Rows at or beyond nrows read as zero (buffer range check).
 // ---------------------------------------------------------------------------
-template <int ROWS, int BK, int SLOTS, int NW = 4>
+// DWD = 1: the same tile by 4-byte DMA (64 lanes x 4 B = 256 B per
+// instruction, 4 lanes per 16-byte chunk) for rows that are only 4-byte
+// aligned (ld % 8 != 0), and the contraction's tail masked per lane: a dword
+// at k >= kdim is fetched from an offset beyond the buffer's range and reads
+// as zero, so rows whose kdim is not a multiple of the slab contract over
+// exactly kdim elements (kdim even).
+template <int ROWS, int BK, int SLOTS, int NW = 4, int DWD = 0>
 struct DmaTileK {
   using L = LdsLayout<BK, SLOTS>;
-  static constexpr int RPI = 1024 / L::PITCH;            // rows per DMA instruction
+  static constexpr int IB = DWD ? 256 : 1024;            // bytes per DMA instruction
+  static constexpr int RPI = IB / L::PITCH;              // rows per DMA instruction
   static constexpr int NI = ROWS / RPI / NW;             // instructions per wave per slab
-  static_assert(NI * RPI * NW == ROWS, "tile rows must split over the waves");
+  static_assert(RPI >= 1 && NI * RPI * NW == ROWS, "tile rows must split over the waves");
   i32x4 rs;
   uint32_t voff[NI];
   uint32_t lrow[NI];                                     // wave-uniform LDS byte offsets
+  int kc[DWD ? NI : 1];                                  // DWD: the lane's k within the slab
+  int kdim;
   // src is [rows][ld] with K contiguous; rows >= nrows read as zero. The
   // range ends with the last row's kdim-th element, so a view into a wider
   // tensor (one head's columns) reads nothing past that tensor.
-  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int kdim) {
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int kdim_) {
+    kdim = kdim_;
     rs = buffer_rsrc(src + (int64_t)row0 * ld, ((int64_t)(nrows - 1 - row0) * ld + kdim) * 2);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
       const int r0 = (wave * NI + q) * RPI;
-      const int row = r0 + lane / L::CH;
-      const int pos = lane % L::CH;
+      const int lpc = DWD ? 4 : 1;                       // lanes per 16-byte chunk
+      const int row = r0 + lane / (L::CH * lpc);
+      const int pos = (lane / lpc) % L::CH;
+      const int d = lane % lpc;                          // DWD: dword of the chunk
       const int chunk = pos ^ ((row / L::RPL) & (L::CH - 1));
-      voff[q] = (uint32_t)(row * ld * 2 + chunk * 16);
+      voff[q] = (uint32_t)(row * ld * 2 + chunk * 16 + d * 4);
       lrow[q] = (uint32_t)(r0 * L::PITCH);
+      if constexpr (DWD) kc[q] = chunk * 8 + d * 2;
+    }
+  }
+  __device__ __forceinline__ void issue_q(uint32_t lds_tile, int k0, int q) const {
+    if constexpr (DWD) {
+      const uint32_t off = k0 + kc[q] < kdim ? voff[q] + (uint32_t)k0 * 2 : 0x80000000u;
+      dma4(rs, lds_tile + lrow[q], off);
+    } else {
+      dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * 2);
     }
   }
   __device__ __forceinline__ void issue(uint32_t lds_tile, int k0) const {
 #pragma unroll
-    for (int q = 0; q < NI; ++q) dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * 2);
-  }
-  __device__ __forceinline__ void issue_q(uint32_t lds_tile, int k0, int q) const {
-    dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * 2);
+    for (int q = 0; q < NI; ++q) issue_q(lds_tile, k0, q);
   }
   // Per-lane byte offset of fragment 0 (tile rows r0 .. r0 + 15) for k-step ks.
   // The swizzle term (row / RPL) & (CH - 1) repeats every 16 rows (RPL * CH
@@ -176,13 +194,16 @@ struct DmaTileK {
 // reads (k0 and k0 + 4) give the same 8 consecutive k as the K-contiguous
 // fragment. k-rows at or beyond kdim read as zero; rows beyond the operand's
 // extent hold other data and only feed outputs that are never stored.
-template <int ROWS, int BK, int NW = 4>
+// DWD = 1: the same tile by 4-byte DMA (256 B of the [BK][ROWS] tile per
+// instruction, 4 lanes per 16-byte chunk), for k-rows that are only 4-byte
+// aligned (ld % 8 != 0).
+template <int ROWS, int BK, int NW = 4, int DWD = 0>
 struct DmaTileMN {
   static constexpr int CHR = ROWS / 8;                   // 16-byte chunks per k-row
   static constexpr int PITCH = ROWS * 2;
-  static constexpr int KPI = 1024 / PITCH;               // k-rows per DMA instruction
-  static constexpr int NI = BK / KPI / NW;               // instructions per wave per slab
-  static_assert(CHR >= 16 && NI * KPI * NW == BK, "tile shape");
+  static constexpr int IB = DWD ? 256 : 1024;            // bytes per DMA instruction
+  static constexpr int NI = BK * PITCH / IB / NW;        // instructions per wave per slab
+  static_assert(CHR >= 16 && NI * IB * NW == BK * PITCH && IB % 256 == 0, "tile shape");
   i32x4 rs;
   uint32_t voff[NI];
   uint32_t lrow[NI];
@@ -199,20 +220,22 @@ struct DmaTileMN {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      const int k0 = (wave * NI + q) * KPI;
-      const int kr = k0 + lane / CHR;
-      const int pos = lane % CHR;
+      const int b0 = (wave * NI + q) * IB;               // the instruction's first byte of the tile
+      const int b = b0 + lane * (IB / 64);               // this lane's
+      const int kr = b / PITCH;
+      const int pos = (b % PITCH) / 16;
       const int chunk = pos ^ swz(kr);
-      voff[q] = (uint32_t)(kr * ld * 2 + chunk * 16);
-      lrow[q] = (uint32_t)(k0 * PITCH);
+      voff[q] = (uint32_t)(kr * ld * 2 + chunk * 16 + (b % 16));
+      lrow[q] = (uint32_t)b0;
     }
+  }
+  __device__ __forceinline__ void issue_q(uint32_t lds_tile, int k0, int q) const {
+    if constexpr (DWD) dma4(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
+    else dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
   }
   __device__ __forceinline__ void issue(uint32_t lds_tile, int k0) const {
 #pragma unroll
-    for (int q = 0; q < NI; ++q) dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
-  }
-  __device__ __forceinline__ void issue_q(uint32_t lds_tile, int k0, int q) const {
-    dma16(rs, lds_tile + lrow[q], voff[q] + (uint32_t)k0 * kstride);
+    for (int q = 0; q < NI; ++q) issue_q(lds_tile, k0, q);
   }
   // The lane's byte offset, within the tile, of its first read of the
   // fragment of rows r0 .. r0 + 15 (r0 a multiple of 16) at k-step 0. The
@@ -256,7 +279,15 @@ struct DmaTileMN {
 template <int ROWS, int BK, int MN, int NW = 4>
 struct DmaTileOf { using T = DmaTileK<ROWS, BK, kLdsSlots, NW>; };
 template <int ROWS, int BK, int NW>
-struct DmaTileOf<ROWS, BK, 1, NW> { using T = DmaTileMN<ROWS, BK, NW>; };
+struct DmaTileOf<ROWS, BK, kMNContig, NW> { using T = DmaTileMN<ROWS, BK, NW>; };
+template <int ROWS, int BK, int NW>
+struct DmaTileOf<ROWS, BK, kKContigD, NW> { using T = DmaTileK<ROWS, BK, kLdsSlots, NW, 1>; };
+template <int ROWS, int BK, int NW>
+struct DmaTileOf<ROWS, BK, kMNContigD, NW> { using T = DmaTileMN<ROWS, BK, NW, 1>; };
+
+// K-contiguous operand layouts (read as [rows][BK] fragments), as opposed to
+// the MN-contiguous ones (read with transpose loads).
+constexpr bool k_contig(int layout) { return layout == kKContig || layout == kKContigD; }
 
 // Quantised-weight operands through an LDS ring. Per slab, the raw weight
 // bytes of ROWS rows (packed N-bit codes, BK*N/8 bytes per row; or the fp32
@@ -995,8 +1026,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int NM = TI * TJ, NR = TI + TJ;
   constexpr int NLA = LA::NI, NL = LA::NI + LB::NI;      // DMA instructions per wave per slab
-  constexpr int GAP = NM / NL > 0 ? NM / NL : 1;
-  static_assert(NR <= NM && NL * GAP <= NM, "one k-step must cover the reads and the DMA");
+  // the slab's DMA instructions spread over a k-step's MFMAs: one after every
+  // GAP-th MFMA, or DPM after each when there are more than MFMAs (4-byte DMA)
+  constexpr int DPM = (NL + NM - 1) / NM;
+  constexpr int GAP = DPM > 1 ? 1 : NM / NL;
+  static_assert(NR <= NM && NL <= NM * DPM && (DPM == 1 || GAP == 1), "one k-step must cover the reads and the DMA");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
   static_assert(GM < 2 || 2 * (BN / 64) * BM * 4 <= STAGES * STAGE, "LDS holds the chunk sums");
 
@@ -1030,29 +1064,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
   // offsets; MN-contiguous tiles: transpose reads at a lane offset per
   // fragment, computed once, + the stage and k-step as immediates.
   int a_base[2] = {0, 0}, b_base[2] = {0, 0};
-  int a_off[AMN == kKContig ? 1 : TI], b_off[BMN == kKContig ? 1 : TJ];
-  if constexpr (AMN != kKContig) {
+  int a_off[k_contig(AMN) ? 1 : TI], b_off[k_contig(BMN) ? 1 : TJ];
+  if constexpr (!k_contig(AMN)) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) a_off[i] = LA::frag_off(wm0 + i * 16, lane);
   }
-  if constexpr (BMN != kKContig) {
+  if constexpr (!k_contig(BMN)) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) b_off[j] = A_BYTES + LB::frag_off(wn0 + j * 16, lane);
   }
-  if constexpr (AMN == kKContig) {
+  if constexpr (k_contig(AMN)) {
     a_base[0] = LA::frag_base(wm0, 0, lane);
     a_base[1] = LA::frag_base(wm0, 1, lane);
   }
-  if constexpr (BMN == kKContig) {
+  if constexpr (k_contig(BMN)) {
     b_base[0] = A_BYTES + LB::frag_base(wn0, 0, lane);
     b_base[1] = A_BYTES + LB::frag_base(wn0, 1, lane);
   }
   auto read_a = [&](int st, int ks, int i) -> bf16x8 {
-    if constexpr (AMN == kKContig) return *(const bf16x8*)&smem[st + a_base[ks] + i * LA::FRAG_STRIDE];
+    if constexpr (k_contig(AMN)) return *(const bf16x8*)&smem[st + a_base[ks] + i * LA::FRAG_STRIDE];
     else return LA::frag_at(&smem[st + a_off[i] + ks * 32 * LA::PITCH]);
   };
   auto read_b = [&](int st, int ks, int j) -> bf16x8 {
-    if constexpr (BMN == kKContig) return *(const bf16x8*)&smem[st + b_base[ks] + j * LB::FRAG_STRIDE];
+    if constexpr (k_contig(BMN)) return *(const bf16x8*)&smem[st + b_base[ks] + j * LB::FRAG_STRIDE];
     else return LB::frag_at(&smem[st + b_off[j] + ks * 32 * LB::PITCH]);
   };
   // read r of a k-step, in the order the MFMAs consume them: b0, a0 .. a(TI-1), b1 .. b(TJ-1)
@@ -1069,7 +1103,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
     for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One k-step: MFMA t on `cur`, then read t of the next k-step (stage nst,
-  // k-step nks) into `nxt` and, every GAP MFMAs, one DMA instruction of slab
+  // k-step nks) into `nxt` and, every GAP MFMAs, DPM DMA instructions of slab
   // dslab into the stage at dsoff (none if dslab < 0).
   auto kstep = [&](const Frags<TI, TJ>& cur, int nst, int nks, Frags<TI, TJ>& nxt, int dslab, int dsoff) {
 #pragma unroll
@@ -1077,7 +1111,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
       const int j = t / TI, i = t % TI;
       mfma_acc(acc[j][i], cur.b[j], cur.a[i]);
       if (t < NR) read_r(nst, nks, t, nxt);
-      if (dslab >= 0 && t % GAP == GAP - 1 && t / GAP < NL) dma_q(dslab, t / GAP, dsoff);
+      if (dslab >= 0 && t % GAP == GAP - 1) {
+#pragma unroll
+        for (int d = 0; d < DPM; ++d)
+          if ((t / GAP) * DPM + d < NL) dma_q(dslab, (t / GAP) * DPM + d, dsoff);
+      }
       sched_fence();
     }
   };
@@ -1138,10 +1176,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 // stage slab kt - 1 has just released. The ring runs one slab ahead of A and
 // is converted into the bf16 B stage two slabs ahead of the MFMAs.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int U2, int BL, int NB, int BT = 0>
+template <int BM, int BN, int BK, int STAGES, int U2, int BL, int NB, int BT = 0, int ADW = 0>
 __global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
   using L = LdsLayout<BK, kLdsSlots>;
-  using LA = DmaTileK<BM, BK, kLdsSlots>;
+  using LA = DmaTileK<BM, BK, kLdsSlots, 4, ADW>;         // ADW: A by 4-byte DMA, contraction tail masked
   // BT = 0: B rows are weight rows (Y = X W_hat^T); BT = 1: B rows are weight
   // columns (dX = dY W_hat), the stage MN-contiguous
   using LB = typename std::conditional<BT == 0, DmaRing<BN, BK, BL, NB>, DmaRingT<BN, BK, BL, NB>>::type;

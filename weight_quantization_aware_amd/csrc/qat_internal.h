@@ -109,7 +109,11 @@ enum Causal { kCausalNone = 0, kCausalLower = 1 };
 
 enum BLoad { kBf16 = 0, kFp32Quant = 1, kPacked = 2 };
 enum Epi { kStoreBf16 = 0, kSteGrads = 1, kE2eScaleGrad = 2, kStoreF32 = 3, kSteAdam = 4, kResidMse = 5 };
-enum Layout { kKContig = 0, kMNContig = 1 };
+// Operand layouts of the GEMM: K-contiguous ([rows][ld]) or MN-contiguous
+// ([K][ld], the operand's rows contiguous); the D variants load by 4-byte DMA
+// for rows that are only 4-byte aligned (kKContigD also zero-fills the
+// contraction's tail per lane).
+enum Layout { kKContig = 0, kMNContig = 1, kKContigD = 2, kMNContigD = 3 };
 
 // Forward-type GEMM with bf16 output: Y = X W_hat^T. bload selects the B source.
 void launch_gemm_fwd(const GemmArgs& a, int bload, int bits, hipStream_t st);
@@ -139,6 +143,8 @@ void launch_gemm_fwd_f32(const GemmArgs& a, hipStream_t st);
 // dW, ds, dz left to the caller).
 void launch_linear_dx(const uint16_t* dY, const uint16_t* w_hat_t, int64_t M, int64_t out, int64_t in,
                       uint16_t* dX, hipStream_t st);
+void launch_linear_dx_saved(const uint16_t* dY, const uint16_t* w_hat, int64_t M, int64_t out, int64_t in,
+                            uint16_t* dX, hipStream_t st);
 void launch_linear_dx_fused(const uint16_t* dY, const void* B, int64_t ldb, const float* s, const float* z, int64_t M,
                             int64_t out, int64_t in, int group, int bits, uint16_t* dX, int bload, hipStream_t st);
 GemmArgs linear_grads_args(const uint16_t* dY, const uint16_t* X, const float* s, const float* z, int64_t M,
