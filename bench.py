@@ -8,15 +8,19 @@ on the Llama-2-7B q_proj workload: fp32 W 4096x4096 ~N(0, 0.02) with 0.1% x10
 outliers, w2g64, X 2048x4096 bf16 ~N(0,1) with 8 outlier channels x20,
 dY ~N(0, 1e-3). Inputs are resident in HBM before the timed region.
 
-value = counted GEMM FLOPs of the step / step time, where the count is
-6*M*in*out for the fake-quant forward + backward plus 6*M*in*out for the
-E2E-QP forward + dX + ds (init and pack add time, no FLOPs).
+value = the metric as named: the fake-quant linear's forward + backward,
+6*M*in*out = 206.16 GFLOP, divided by the median over the timed steps of the
+GPU time from the start of the forward to the end of the backward (events
+between the calls of each step). The whole step (all rows, with init, pack
+and the E2E-QP pair) is reported beside it.
 
-The roofline object covers the kernel with the largest share of the timed
-region, timed live by the library (HIP events around each launch on its
-stream). Its `traffic` comes from a committed rocprofv3 FETCH_SIZE /
-WRITE_SIZE summary under profiles/, used only while the kernel sources still
-hash to the value recorded there.
+Per-kernel times come from the library's timing, whose events are bound to
+each kernel's own dispatch (no extra packets on the stream), so they agree
+with a rocprofv3 kernel trace. The roofline object covers the kernel with the
+most device time per step, timed that way inside the timed region. Its
+`traffic` comes from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+under profiles/, used only while the kernel sources still hash to the value
+recorded there.
 
 Prints one JSON line (N = 1 only).
 """
@@ -36,6 +40,8 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
+TARGET_MFMA_FRAC = 0.60        # the GEMM target: 60% of the dense bf16 peak
+TARGET_HBM_FRAC = 0.70         # the HBM target for init, pack and the staging kernels
 KERNEL_SOURCES = ["weight_quantization_aware_amd/csrc/qat_gemm_kernel.h", "weight_quantization_aware_amd/csrc/qat_dma.h",
                   "weight_quantization_aware_amd/csrc/qat_gemm.hip",
                   "weight_quantization_aware_amd/csrc/qat_elementwise.hip",
@@ -49,16 +55,24 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="weight rows of the bounded oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="least host time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region run one 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--deploy-only", action="store_true",
                     help="only the inference linear on the deployment format (Llama-2-70B block, M = 1 and 16)")
     ap.add_argument("--block-only", action="store_true",
                     help="only one Block-AP step on a Llama-2-7B block (2 x 2048 tokens, w2g64)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only the other workloads (C1 latency, C3 block, C4 E2E-QP MLP, C5 70B gate + down)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the context measurements (practical peaks, cold HBM, the C3 block)")
+                    help="skip the context measurements (practical peaks, the other workloads, cold HBM, "
+                         "group sizes, inference linear, Block-AP step)")
     return ap.parse_args()
+
+
+def note(msg: str) -> None:
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def sources_hash() -> str:
@@ -67,6 +81,14 @@ def sources_hash() -> str:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def stats_ms(ts):
+    """median, min and interquartile range of times in ms."""
+    a = np.asarray(ts, np.float64)
+    q25, q50, q75 = np.percentile(a, [25, 50, 75])
+    return {"median_ms": round(float(q50), 5), "min_ms": round(float(a.min()), 5),
+            "iqr_ms": round(float(q75 - q25), 5), "n": int(a.size)}
 
 
 def work_per_launch(label, M, out, inp, bits):
@@ -86,6 +108,69 @@ def work_per_launch(label, M, out, inp, bits):
     return "hbm", float("nan")
 
 
+class Gpu:
+    """Event timing helpers on one stream."""
+
+    def __init__(self, torch, dev, stream, Q):
+        self.torch, self.dev, self.stream, self.Q = torch, dev, stream, Q
+        self._flush_buf = None
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def sync(self):
+        self.torch.cuda.synchronize(self.dev)
+
+    def per_call(self, fn, reps):
+        """GPU time of each of `reps` calls (ms), each between its own event pair,
+        queued back to back."""
+        fn()
+        self.sync()
+        evs = [(self.ev(), self.ev()) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+        self.sync()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    def flush(self):
+        """Evict L2 and the 256 MiB MALL: read a 1 GiB buffer (no dirty lines left)."""
+        if self._flush_buf is None:
+            self._flush_buf = self.torch.ones(1 << 28, dtype=self.torch.float32, device=self.dev)
+            self._flush_scratch = self.torch.empty(2048 * 256, device=self.dev)
+        self.Q.peak_read(self._flush_buf, 2048, self._flush_scratch)
+
+    def kernel_ms(self, label, fn, reps, cold):
+        """Duration of the library kernel `label` inside fn(), from events bound to
+        its dispatch; cold: caches flushed before every call."""
+        Q = self.Q
+        ts = []
+        fn()
+        self.sync()
+        for _ in range(reps):
+            if cold:
+                self.flush()
+            self.sync()
+            Q.timing_select(label)
+            Q.timing_enable(True)
+            fn()
+            self.sync()
+            Q.timing_enable(False)
+            Q.timing_select(None)
+            ms, n = Q.timing_report()[label]
+            ts.append(ms / n)
+        return ts
+
+    def release(self):
+        self._flush_buf = None
+        self._flush_scratch = None
+
+
+def bf16_dev(torch, dev, bits_np):
+    return torch.from_numpy(np.ascontiguousarray(bits_np).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -99,22 +184,26 @@ def main():
     from weight_quantization_aware_amd import synth
 
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = Gpu(torch, dev, stream, Q)
     if args.deploy_only:
-        print(json.dumps({"inference_linear_70b_block":
-                          deploy_measurements(Q, torch, dev, torch.cuda.current_stream(dev))}), flush=True)
+        print(json.dumps({"inference_linear_70b_block": deploy_measurements(Q, torch, dev, stream)}), flush=True)
         return
     if args.block_only:
-        print(json.dumps({"block_ap_step_7b": block_step_measurements(Q, torch, dev, torch.cuda.current_stream(dev))}),
-              flush=True)
+        print(json.dumps({"block_ap_step_7b": block_step_measurements(Q, torch, dev, stream)}), flush=True)
         return
+    if args.configs_only:
+        print(json.dumps(other_workloads(Q, torch, dev, g, synth)), flush=True)
+        return
+
     lin = synth.config(2)[0]
     M, out, inp, bits = lin.m, lin.out, lin.inp, lin.bits
     G = inp // 64
     W_np, X_np, dY_np = lin.W(), lin.X(), lin.dY()
 
     W = torch.from_numpy(W_np).to(dev)
-    X = torch.from_numpy(X_np.view(np.int16)).view(torch.bfloat16).to(dev)
-    dY = torch.from_numpy(dY_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = bf16_dev(torch, dev, X_np)
+    dY = bf16_dev(torch, dev, dY_np)
     s = torch.empty(out, G, device=dev)
     z = torch.empty_like(s)
     Y = torch.empty(M, out, dtype=torch.bfloat16, device=dev)
@@ -139,73 +228,80 @@ def main():
         ("e2e_bwd", lambda: Q.qat_dequant_gemm_bwd_s_saved(dY, X, Wq, s, zp, ws, bits, ds2, dX=dX2)),
     ]
 
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
+    def step():
         for _, f in calls:
             f()
-    torch.cuda.synchronize(dev)
 
-    def run_steps(n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            for _, f in calls:
-                f()
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-        return e0.elapsed_time(e1) / n
+    for _ in range(args.warmup):
+        step()
+    g.sync()
+    note(f"warm-up done ({args.warmup} steps)")
 
-    def kernel_times(label=None):
-        Q.timing_select(label)
-        Q.timing_enable(True)
-        ms = run_steps(args.steps)
-        Q.timing_enable(False)
-        Q.timing_select(None)
-        return ms, Q.timing_report()
-
-    # ---- per-kernel table: every launch of K steps bracketed by HIP events
-    ms_step_all_events, kernels = kernel_times()
+    # ---- per-kernel table: every launch of K steps timed by its own dispatch
+    Q.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    g.sync()
+    Q.timing_enable(False)
+    kernels = Q.timing_report()
     dom = max(kernels, key=lambda k: kernels[k][0])      # most device time per step
 
-    # ---- timed region: K whole steps; only the dominant kernel's launches
-    # carry HIP events (recorded by the library on the launch stream)
+    # ---- timed region: K whole steps between two events; inside each step two
+    # events around the fake-quant forward + backward; the dominant kernel's
+    # launches carry dispatch-bound events (no extra packets)
+    e_fq = [(g.ev(), g.ev()) for _ in range(args.steps)]
+    e0, e1 = g.ev(), g.ev()
     Q.timing_select(dom)
     Q.timing_enable(True)
-    torch.cuda.synchronize(dev)
+    g.sync()
     t0 = time.perf_counter()
-    ms_step = run_steps(args.steps)
+    e0.record(stream)
+    for k in range(args.steps):
+        calls[0][1]()
+        e_fq[k][0].record(stream)
+        calls[1][1]()
+        calls[2][1]()
+        e_fq[k][1].record(stream)
+        for _, f in calls[3:]:
+            f()
+    e1.record(stream)
+    g.sync()
     wall = time.perf_counter() - t0
     Q.timing_enable(False)
     Q.timing_select(None)
     dom_ms, dom_n = Q.timing_report()[dom]
+    ms_step = e0.elapsed_time(e1) / args.steps
+    fq_ms = [a.elapsed_time(b) for a, b in e_fq]
+    fq_stats = stats_ms(fq_ms)
 
-    # ---- the same steps with no kernel events at all
-    ms_step_clean = run_steps(args.steps)
+    flops_fq = 6.0 * M * inp * out
+    flops_step = flops_fq + 6.0 * M * inp * out                # + E2E-QP forward, dX and ds
+    value = flops_fq / (fq_stats["median_ms"] * 1e-3) / 1e12
+    note(f"timed region: {ms_step:.4f} ms per step, fake-quant fwd+bwd {value:.1f} TFLOP/s")
 
-    # ---- per-call breakdown: events between the six calls of a step
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    # ---- per-call breakdown: events between the calls of each step
+    ev = [[g.ev() for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     for k in range(args.steps):
         ev[k][0].record(stream)
         for i, (_, f) in enumerate(calls):
             f()
             ev[k][i + 1].record(stream)
-    torch.cuda.synchronize(dev)
-    per_call = {name: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
-                for i, (name, _) in enumerate(calls)}
+    g.sync()
+    breakdown = {name: stats_ms([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)])
+                 for i, (name, _) in enumerate(calls)}
+    for name, fl in (("fq_fwd", 2), ("fq_bwd", 4), ("e2e_fwd", 2), ("e2e_bwd", 4)):
+        breakdown[name]["tflops"] = round(fl * M * inp * out / (breakdown[name]["median_ms"] * 1e-3) / 1e12, 1)
 
-    flops_fq = 6.0 * M * inp * out
-    flops_e2e = 6.0 * M * inp * out
-    value = (flops_fq + flops_e2e) / (ms_step * 1e-3) / 1e12
-
-    # ---- per-kernel table (from the all-events pass)
+    # ---- per-kernel table (dispatch-bound events)
     ktab = {}
     for label, (tot_ms, n) in kernels.items():
         kind, work = work_per_launch(label, M, out, inp, bits)
         avg_s = tot_ms / n * 1e-3
         rate = work / avg_s / (1e12 if kind == "mfma" else 1e9)
         ktab[label] = {"launches_per_step": n / args.steps, "avg_us": round(avg_s * 1e6, 2),
-                       ("tflops" if kind == "mfma" else "gbs"): round(rate, 1),
-                       "share": round(tot_ms / (ms_step_all_events * args.steps), 4)}
+                       ("tflops" if kind == "mfma" else "gbs_warm"): round(rate, 1),
+                       "frac_of_peak": round(rate / (MFMA_BF16_PEAK_TFLOPS if kind == "mfma" else HBM_PEAK_GBS), 4),
+                       "share": round(tot_ms / sum(t for t, _ in kernels.values()), 4)}
 
     # ---- the dominant kernel's roofline, from its launches in the timed region
     kind, work = work_per_launch(dom, M, out, inp, bits)
@@ -222,51 +318,71 @@ def main():
             traffic = tr["kernels"][dom]["bytes_per_launch"]
     roofline = {"kernel": dom, "bound": "mfma" if kind == "mfma" else "hbm", "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
-                "avg_us": round(avg_s * 1e6, 2), "launches_timed": dom_n, "work_per_launch": work}
+                "avg_us": round(avg_s * 1e6, 2), "launches_timed": dom_n, "work_per_launch": work,
+                "timing": "events bound to the kernel's dispatch (hipExtLaunchKernel), live in the timed region"}
 
-    # ---- the fused fp32 forward (no workspace), timed on its own as evidence
+    # ---- HBM-bound kernels with cold caches (the result) and warm (context)
+    hbm = {}
+    for label, fn in (("init_minmax", calls[0][1]), ("quant_w_hat", calls[1][1]), ("pack", calls[3][1]),
+                      ("dequant", calls[4][1])):
+        _, nbytes = work_per_launch(label, M, out, inp, bits)
+        cold = stats_ms(g.kernel_ms(label, fn, 10, True))
+        warm_us = ktab[label]["avg_us"]
+        hbm[label] = {"cold": cold, "gbs": round(nbytes / (cold["median_ms"] * 1e-3) / 1e9, 1),
+                      "frac_of_peak": round(nbytes / (cold["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "warm_us": warm_us, "gbs_warm": round(nbytes / (warm_us * 1e-6) / 1e9, 1),
+                      "bytes": nbytes}
+
+    note("cold HBM kernels done")
+    # ---- the no-workspace variants at the same workload (bit-identical outputs)
+    nows = {}
     Yf = torch.empty_like(Y)
-    for _ in range(3):
-        Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Yf, ws=None)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Yf, ws=None)
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    t_fused = e0.elapsed_time(e1) / 10
-    fused_same = bool(torch.equal(Yf, Y))
+    t = stats_ms(g.per_call(lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Yf, ws=None), 10))
+    nows["fq_fwd_fused_fp32"] = dict(t, tflops=round(2 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
+                                     bit_identical=bool(torch.equal(Yf, Y)))
+    dXf = torch.empty_like(dX)
+    t = stats_ms(g.per_call(lambda: Q.qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=dXf), 10))
+    nows["fq_dx_fused_fp32"] = dict(t, tflops=round(2 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
+                                    bit_identical=bool(torch.equal(dXf, dX)))
+    Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Y2, ws=ws)
+    t = stats_ms(g.per_call(lambda: Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Yf), 10))
+    nows["e2e_fwd_fused_packed"] = dict(t, tflops=round(2 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
+                                        bit_identical=bool(torch.equal(Yf, Y2)))
+    Q.qat_dequant_gemm_bwd_s_saved(dY, X, Wq, s, zp, ws, bits, ds2, dX=dX2)
+    t = stats_ms(g.per_call(lambda: Q.qat_dequant_gemm_bwd_s(dY, X, Wq, s, zp, bits, ds2, dX=dXf), 10))
+    nows["e2e_dx_ds_fused_packed"] = dict(t, tflops=round(4 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
+                                          bit_identical=bool(torch.equal(dXf, dX2)))
+    del Yf, dXf
 
     if args.copy_calibration:            # a plain copy of known size for the HBM counters
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         b.copy_(a)
-        torch.cuda.synchronize(dev)
-
-    breakdown = {name: {"ms": round(t, 4)} for name, t in per_call.items()}
-    breakdown["fq_fwd"]["tflops"] = round(2 * M * inp * out / (per_call["fq_fwd"] * 1e-3) / 1e12, 1)
-    breakdown["fq_bwd"]["tflops"] = round(4 * M * inp * out / (per_call["fq_bwd"] * 1e-3) / 1e12, 1)
-    breakdown["e2e_fwd"]["tflops"] = round(2 * M * inp * out / (per_call["e2e_fwd"] * 1e-3) / 1e12, 1)
-    breakdown["e2e_bwd"]["tflops"] = round(4 * M * inp * out / (per_call["e2e_bwd"] * 1e-3) / 1e12, 1)
-    breakdown["init"]["gbs"] = round(out * inp * 4.125 / (per_call["init"] * 1e-3) / 1e9, 1)
-    breakdown["pack"]["gbs"] = round(out * inp * (4.125 + bits / 8) / (per_call["pack"] * 1e-3) / 1e9, 1)
-    breakdown["fq_fwd_fused_no_ws"] = {"ms": round(t_fused, 4),
-                                       "tflops": round(2 * M * inp * out / (t_fused * 1e-3) / 1e12, 1),
-                                       "bit_identical_to_staged": fused_same}
-    fq_only = flops_fq / ((per_call["fq_fwd"] + per_call["fq_bwd"]) * 1e-3) / 1e12
+        g.sync()
+        del a, b
 
     extras = None
     if not args.no_extras:
-        extras = context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp, X, dY)
+        extras = {"measured_peaks": measured_peaks(Q, torch, dev, g)}
+        note("measured peaks done")
+        extras["q_proj_fwd_bwd_by_group"] = by_group(Q, torch, dev, g, W, X, dY, bits)
+        del W, X, dY, dW, Wq, ws, Y, Y2, dX, dX2
+        torch.cuda.empty_cache()
+        extras.update(other_workloads(Q, torch, dev, g, synth))
         extras["inference_linear_70b_block"] = deploy_measurements(Q, torch, dev, stream)
+        note("inference linear done")
         extras["block_ap_step_7b"] = block_step_measurements(Q, torch, dev, stream)
+        note("Block-AP step done")
+        extras["clocks"] = _clocks()
         roofline["frac_of_measured_peak"] = round(
             achieved / (extras["measured_peaks"]["mfma_bf16_tflops"] if kind == "mfma"
                         else extras["measured_peaks"]["hbm_read_gbs"]), 4)
+    g.release()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lin, W_np, X_np, dY_np, args.cpu_rows)
+        note("oracle on the host")
+        cpu = cpu_baseline(lin, W_np, X_np, dY_np, args.cpu_seconds)
 
     line = {
         "metric": "fake-quant linear fwd+bwd TFLOP/s (w2g64, Llama-2-7B shapes); % MFMA peak",
@@ -276,20 +392,22 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "ms_per_step_without_kernel_events": round(ms_step_clean, 4),
-        "ms_per_step_with_all_kernel_events": round(ms_step_all_events, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic (seeded; Llama-2-7B q_proj shapes, no dataset or checkpoint)",
         "config": {"workload": "llama2-7b q_proj 4096x4096, 2048 tokens, w2g64: init + fake-quant "
-                               "fwd/bwd + pack + E2E-QP fwd/bwd", "M": M, "out": out, "in": inp,
-                   "bits": bits, "group": 64},
-        "fq_fwd_bwd_tflops": round(fq_only, 2),
-        "mfma_peak_frac_fq": round(fq_only / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "fwd/bwd + pack + E2E-QP fwd/bwd per step; value over the fake-quant fwd+bwd",
+                   "M": M, "out": out, "in": inp, "bits": bits, "group": 64},
+        "value_frac_of_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "fq_fwd_bwd": dict(fq_stats, gflop=round(flops_fq / 1e9, 2),
+                           budget_ms_at_60pct=round(flops_fq / (TARGET_MFMA_FRAC * MFMA_BF16_PEAK_TFLOPS * 1e9), 4)),
+        "step_all_rows_tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
         "breakdown": breakdown,
         "kernels": ktab,
+        "hbm_kernels": hbm,
+        "no_workspace": nows,
         "wall_s": round(wall, 3),
         "roofline": roofline,
         "context": extras,
@@ -314,108 +432,104 @@ def _clocks():
         return None
 
 
-def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp, X, dY):
-    """Context beside the headline (not part of `value`):
-    - practical peaks on this GPU: a register-resident bf16 MFMA loop and a
-      read stream over 1 GiB (beyond the 256 MiB MALL);
-    - init and pack with cold caches: before each timed call a 1 GiB buffer is
-      read (not written, so no dirty lines are left to write back), which
-      evicts W from L2 and the MALL (median of 10); at the q_proj weight
-      (64 MiB) and at the Llama-2-70B gate weight (896 MiB);
-    - the q_proj fake-quant forward + backward at groups of 32, 64, 128 and
-      channel-wise (one group per row);
-    - the Llama-2-7B block of seven w3g64 linears (q, k, v, o 4096x4096; gate,
-      up 11008x4096; down 4096x11008; 2048 tokens): fake-quant forward +
-      backward of all seven, 2486.79 GFLOP counted;
-    - the clocks rocm-smi reports."""
-    from weight_quantization_aware_amd import synth
-
-    def ev_time(fn, reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize(dev)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-        return e0.elapsed_time(e1) / reps * 1e-3
-
-    # practical peaks
+def measured_peaks(Q, torch, dev, g):
+    """Practical peaks on this GPU: a register-resident bf16 MFMA loop and a
+    read stream over 1 GiB (beyond the 256 MiB MALL); medians of 5 / 10."""
     blocks = 256
     scratch = torch.empty(max(Q.lib().qat_peak_scratch_bytes(2048) // 4, 2048 * 256), device=dev)
     flops = Q.lib().qat_peak_mfma_flops(blocks, 4096)
-    t = ev_time(lambda: Q.peak_mfma(blocks, 4096, scratch), 5)
-    mfma_peak = flops / t / 1e12
-    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)          # 1 GiB
-    t = ev_time(lambda: Q.peak_read(big, 2048, scratch), 10)
-    read_peak = (1 << 30) / t / 1e9
+    t = np.median(g.per_call(lambda: Q.peak_mfma(blocks, 4096, scratch), 5)) * 1e-3
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    tr = np.median(g.per_call(lambda: Q.peak_read(big, 2048, scratch), 10)) * 1e-3
+    return {"mfma_bf16_tflops": round(flops / t / 1e12, 1), "hbm_read_gbs": round((1 << 30) / tr / 1e9, 1),
+            "what": "register-resident v_mfma_f32_16x16x32_bf16 loop, 8 waves per CU; grid-stride read of 1 GiB"}
 
-    # cold init / pack
-    def cold(fn):
-        ts = []
-        for _ in range(10):
-            Q.peak_read(big, 2048, scratch)
-            torch.cuda.synchronize(dev)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize(dev)
-            ts.append(e0.elapsed_time(e1) * 1e-3)
-        return float(np.median(ts))
-    s2, z2 = torch.empty_like(s), torch.empty_like(z)
-    Wq2, zp2 = torch.empty_like(Wq), torch.empty_like(zp)
-    t_init = cold(lambda: Q.qat_init_minmax(W, bits, s2, z2))
-    t_pack = cold(lambda: Q.qat_pack(W, s, z, bits, Wq2, zp2))
-    n = out * inp
-    init_bytes = n * 4 + 2 * out * (inp // 64) * 4
-    pack_bytes = n * (4 + bits / 8) + 3 * out * (inp // 64) * 4
-    del s2, z2, Wq2, zp2
 
-    # the same at the Llama-2-70B gate weight (28672 x 8192 fp32, 896 MiB, w2)
-    lin5 = synth.config(5, 2)[0]
-    W5 = torch.from_numpy(lin5.W()).to(dev)
-    G5 = lin5.inp // 64
-    s5 = torch.empty(lin5.out, G5, device=dev)
-    z5 = torch.empty_like(s5)
-    Wq5 = torch.empty(lin5.out, lin5.inp * 2 // 8, dtype=torch.uint8, device=dev)
-    zp5 = torch.empty_like(s5)
-    Q.qat_init_minmax(W5, 2, s5, z5)
-    t_init5 = cold(lambda: Q.qat_init_minmax(W5, 2, s5, z5))
-    t_pack5 = cold(lambda: Q.qat_pack(W5, s5, z5, 2, Wq5, zp5))
-    n5 = lin5.out * lin5.inp
-    init5_bytes = n5 * 4 + 2 * lin5.out * G5 * 4
-    pack5_bytes = n5 * (4 + 2 / 8) + 3 * lin5.out * G5 * 4
-    del W5, s5, z5, Wq5, zp5, big
-
-    # the q_proj step's fake-quant forward + backward at the other group sizes
-    groups = {}
-    M2, out2, in2 = X.shape[0], W.shape[0], W.shape[1]
-    ws2 = Q.workspace(Q.fakequant_ws_bytes(out2, in2, bits), dev)
-    Y2 = torch.empty(M2, out2, dtype=torch.bfloat16, device=dev)
-    dX2 = torch.empty(M2, in2, dtype=torch.bfloat16, device=dev)
-    dW2 = torch.empty(out2, in2, device=dev)
-    for gname, gsize in (("32", 32), ("64", 64), ("128", 128), ("row", in2)):
-        sg = torch.empty(out2, in2 // gsize, device=dev)
+def by_group(Q, torch, dev, g, W, X, dY, bits):
+    """The q_proj fake-quant forward + backward at groups of 32, 64, 128 and
+    channel-wise (one group per row)."""
+    M, out, inp = X.shape[0], W.shape[0], W.shape[1]
+    ws = Q.workspace(Q.fakequant_ws_bytes(out, inp, bits), dev)
+    Y = torch.empty(M, out, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, inp, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(out, inp, device=dev)
+    res = {}
+    for gname, gsize in (("32", 32), ("64", 64), ("128", 128), ("row", inp)):
+        sg = torch.empty(out, inp // gsize, device=dev)
         zg = torch.empty_like(sg)
         dsg, dzg = torch.empty_like(sg), torch.empty_like(sg)
         Q.qat_init_minmax(W, bits, sg, zg, group=gsize)
 
         def fq(sg=sg, zg=zg, dsg=dsg, dzg=dzg, gsize=gsize):
-            Q.qat_fakequant_linear_fwd(X, W, sg, zg, bits, Y2, ws=ws2, group=gsize)
-            Q.qat_fakequant_linear_bwd_saved(dY, X, W, sg, zg, ws2, bits, dX=dX2, dW=dW2, ds=dsg, dz=dzg,
-                                             group=gsize)
-        tg = ev_time(fq, 10)
-        groups[gname] = {"ms": round(tg * 1e3, 4), "tflops": round(6.0 * M2 * in2 * out2 / tg / 1e12, 1)}
-    del ws2, Y2, dX2, dW2
+            Q.qat_fakequant_linear_fwd(X, W, sg, zg, bits, Y, ws=ws, group=gsize)
+            Q.qat_fakequant_linear_bwd_saved(dY, X, W, sg, zg, ws, bits, dX=dX, dW=dW, ds=dsg, dz=dzg, group=gsize)
+        t = stats_ms(g.per_call(fq, 10))
+        res[gname] = dict(t, tflops=round(6.0 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1))
+    return res
 
-    # the C3 block
+
+def _rate(flops, t):
+    tf = flops / (t["median_ms"] * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "budget_ms_at_60pct": round(flops / (TARGET_MFMA_FRAC * MFMA_BF16_PEAK_TFLOPS * 1e9), 4)}
+
+
+def other_workloads(Q, torch, dev, g, synth):
+    """The other workloads, each pass between its own event pair (medians,
+    min and IQR over the passes), GEMM FLOPs counted as 6 M in out for a
+    forward + backward and 4 M in out for the E2E-QP forward + ds:
+    - C1 (256 x 256, 128 tokens, w2g64): GPU time of each call, and the host
+      time to issue one (launch latency);
+    - C3 (the seven w3g64 linears of a Llama-2-7B block, 2048 tokens):
+      fake-quant forward + backward of all seven (staged W_hat, saved for dX);
+    - C4 (E2E-QP Llama-2-7B MLP at 4096 tokens, w2g64): forward + dX + ds of
+      gate, up and down, with the W_hat workspace and without (fused packed);
+    - C5 (Llama-2-70B gate 28672x8192 and down 8192x28672, 4096 tokens) at
+      2, 3 and 4 bits: Block-AP fake-quant forward + backward of both, and the
+      E2E-QP forward + ds of their packed weights. The same seeded W, X, dY
+      serve every bit width (a bit-width sweep of one weight)."""
+    res = {}
+    # ---- C1: latency
+    lin = synth.config(1)[0]
+    M, out, inp, b = lin.m, lin.out, lin.inp, lin.bits
+    W = torch.from_numpy(lin.W()).to(dev)
+    X, dY = bf16_dev(torch, dev, lin.X()), bf16_dev(torch, dev, lin.dY())
+    s = torch.empty(out, inp // 64, device=dev)
+    z, ds, dz, zp, ds2 = (torch.empty_like(s) for _ in range(5))
+    Y, Y2 = (torch.empty(M, out, dtype=torch.bfloat16, device=dev) for _ in range(2))
+    dX, dX2 = (torch.empty(M, inp, dtype=torch.bfloat16, device=dev) for _ in range(2))
+    dW = torch.empty(out, inp, device=dev)
+    Wq = torch.empty(out, inp * b // 8, dtype=torch.uint8, device=dev)
+    ws = Q.workspace(Q.fakequant_ws_bytes(out, inp, b), dev)
+    c1 = [("init", lambda: Q.qat_init_minmax(W, b, s, z)),
+          ("fq_fwd", lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, b, Y, ws=ws)),
+          ("fq_bwd", lambda: Q.qat_fakequant_linear_bwd_saved(dY, X, W, s, z, ws, b, dX=dX, dW=dW, ds=ds, dz=dz)),
+          ("pack", lambda: Q.qat_pack(W, s, z, b, Wq, zp)),
+          ("e2e_fwd", lambda: Q.qat_dequant_gemm_fwd(X, Wq, s, zp, b, Y2, ws=ws)),
+          ("e2e_bwd", lambda: Q.qat_dequant_gemm_bwd_s_saved(dY, X, Wq, s, zp, ws, b, ds2, dX=dX2))]
+    r1 = {}
+    for name, f in c1:
+        t = stats_ms(g.per_call(f, 50))
+        g.sync()
+        h0 = time.perf_counter()
+        for _ in range(200):
+            f()
+        h1 = time.perf_counter()
+        g.sync()
+        r1[name] = {"gpu_us_median": round(t["median_ms"] * 1e3, 2), "gpu_us_min": round(t["min_ms"] * 1e3, 2),
+                    "host_us_per_call": round((h1 - h0) / 200 * 1e6, 2)}
+    step = stats_ms(g.per_call(lambda: [f() for _, f in c1], 50))
+    note("C1 latency done")
+    res["c1_latency"] = {"what": "256x256 linear, 128 tokens, w2g64; GPU time per call (event pairs) and "
+                                 "host time to issue it", "calls": r1,
+                         "step_us_median": round(step["median_ms"] * 1e3, 2)}
+    del W, X, dY, s, z, ds, dz, zp, ds2, Y, Y2, dX, dX2, dW, Wq, ws
+
+    # ---- C3: the 7B block's seven w3g64 linears
     c3 = []
     for lin in synth.config(3):
         Wc = torch.from_numpy(lin.W()).to(dev)
-        Xc = torch.from_numpy(lin.X().view(np.int16)).view(torch.bfloat16).to(dev)
-        dYc = torch.from_numpy(lin.dY().view(np.int16)).view(torch.bfloat16).to(dev)
+        Xc, dYc = bf16_dev(torch, dev, lin.X()), bf16_dev(torch, dev, lin.dY())
         sc = torch.empty(lin.out, lin.inp // 64, device=dev)
         zc = torch.empty_like(sc)
         Q.qat_init_minmax(Wc, lin.bits, sc, zc)
@@ -435,21 +549,103 @@ def context_measurements(Q, torch, dev, stream, W, s, z, Wq, zp, bits, out, inp,
             Q.qat_fakequant_linear_bwd_saved(dYc, Xc, Wc, sc, zc, ws3, lin.bits, dX=dX3[:M3 * i].view(M3, i),
                                              dW=dW3[:o * i].view(o, i), ds=ds3[:o * (i // 64)].view(o, i // 64),
                                              dz=dz3[:o * (i // 64)].view(o, i // 64))
-    t_c3 = ev_time(block, 5)
-    gflop = sum(6.0 * lin.m * lin.inp * lin.out for lin, *_ in c3) / 1e9
-    return {
-        "measured_peaks": {"mfma_bf16_tflops": round(mfma_peak, 1), "hbm_read_gbs": round(read_peak, 1),
-                           "what": "register-resident v_mfma_f32_16x16x32_bf16 loop, 8 waves per CU; "
-                                   "grid-stride read of 1 GiB"},
-        "init_cold": {"us": round(t_init * 1e6, 2), "gbs": round(init_bytes / t_init / 1e9, 1)},
-        "pack_cold": {"us": round(t_pack * 1e6, 2), "gbs": round(pack_bytes / t_pack / 1e9, 1)},
-        "init_cold_70b_gate": {"us": round(t_init5 * 1e6, 2), "gbs": round(init5_bytes / t_init5 / 1e9, 1)},
-        "pack_cold_70b_gate_w2": {"us": round(t_pack5 * 1e6, 2), "gbs": round(pack5_bytes / t_pack5 / 1e9, 1)},
-        "c3_block_w3g64": {"gflop": round(gflop, 2), "ms": round(t_c3 * 1e3, 4),
-                           "tflops": round(gflop / t_c3 / 1e3, 1)},
-        "q_proj_fwd_bwd_by_group": groups,
-        "clocks": _clocks(),
-    }
+    t = stats_ms(g.per_call(block, 10))
+    fl = sum(6.0 * lin.m * lin.inp * lin.out for lin, *_ in c3)
+    note("C3 block done")
+    res["c3_block_w3g64"] = dict(t, gflop=round(fl / 1e9, 2), **_rate(fl, t))
+    del c3, ws3, Y3, dX3, dW3, ds3, dz3
+    torch.cuda.empty_cache()
+
+    # ---- C4: E2E-QP MLP at 4096 tokens
+    c4 = []
+    for lin in synth.config(4):
+        c4.append((lin, torch.from_numpy(lin.Wq()).to(dev), torch.from_numpy(lin.s_e2e()).to(dev),
+                   torch.from_numpy(lin.z_e2e()).to(dev), bf16_dev(torch, dev, lin.X()),
+                   bf16_dev(torch, dev, lin.dY())))
+    M4 = c4[0][0].m
+    ws4 = Q.workspace(max(Q.dequant_ws_bytes(l.out, l.inp, l.bits) for l, *_ in c4), dev)
+    Y4 = torch.empty(M4 * max(l.out for l, *_ in c4), dtype=torch.bfloat16, device=dev)
+    dX4 = torch.empty(M4 * max(l.inp for l, *_ in c4), dtype=torch.bfloat16, device=dev)
+    ds4 = torch.empty(max(l.out * (l.inp // 64) for l, *_ in c4), device=dev)
+
+    def mlp(staged):
+        for lin, Wq4, s4, z4, X4, dY4 in c4:
+            o, i = lin.out, lin.inp
+            dsv = ds4[:o * (i // 64)].view(o, i // 64)
+            if staged:
+                Q.qat_dequant_gemm_fwd(X4, Wq4, s4, z4, lin.bits, Y4[:M4 * o].view(M4, o), ws=ws4)
+                Q.qat_dequant_gemm_bwd_s_saved(dY4, X4, Wq4, s4, z4, ws4, lin.bits, dsv, dX=dX4[:M4 * i].view(M4, i))
+            else:
+                Q.qat_dequant_gemm_fwd(X4, Wq4, s4, z4, lin.bits, Y4[:M4 * o].view(M4, o))
+                Q.qat_dequant_gemm_bwd_s(dY4, X4, Wq4, s4, z4, lin.bits, dsv, dX=dX4[:M4 * i].view(M4, i))
+    fl = sum(6.0 * lin.m * lin.inp * lin.out for lin, *_ in c4)
+    t = stats_ms(g.per_call(lambda: mlp(True), 10))
+    tf = stats_ms(g.per_call(lambda: mlp(False), 5))
+    note("C4 E2E-QP MLP done")
+    res["c4_e2e_mlp_w2g64"] = {"gflop": round(fl / 1e9, 2), "staged": dict(t, **_rate(fl, t)),
+                               "fused_no_workspace": dict(tf, **_rate(fl, tf))}
+    del c4, ws4, Y4, dX4, ds4
+    torch.cuda.empty_cache()
+
+    # ---- C5: the 70B gate and down at 2, 3, 4 bits
+    lins = synth.config(5, 2)
+    data = []
+    for lin in lins:
+        data.append((lin, torch.from_numpy(lin.W()).to(dev), bf16_dev(torch, dev, lin.X()),
+                     bf16_dev(torch, dev, lin.dY())))
+    M5 = lins[0].m
+    big_o = max(l.out for l in lins)
+    big_i = max(l.inp for l in lins)
+    ws5 = Q.workspace(max(Q.fakequant_ws_bytes(l.out, l.inp, 4) for l in lins), dev)
+    Y5 = torch.empty(M5 * big_o, dtype=torch.bfloat16, device=dev)
+    dX5 = torch.empty(M5 * big_i, dtype=torch.bfloat16, device=dev)
+    dW5 = torch.empty(max(l.out * l.inp for l in lins), device=dev)
+    c5 = {}
+    fl_bap = sum(6.0 * l.m * l.inp * l.out for l in lins)
+    fl_e2e = sum(4.0 * l.m * l.inp * l.out for l in lins)
+    for b in (2, 3, 4):
+        qp = []
+        for lin, W5, X5, dY5 in data:
+            o, i = lin.out, lin.inp
+            s5 = torch.empty(o, i // 64, device=dev)
+            z5, ds5, dz5, zp5 = (torch.empty_like(s5) for _ in range(4))
+            Q.qat_init_minmax(W5, b, s5, z5)
+            Wq5 = torch.empty(o, i * b // 8, dtype=torch.uint8, device=dev)
+            Q.qat_pack(W5, s5, z5, b, Wq5, zp5)
+            qp.append((lin, W5, X5, dY5, s5, z5, ds5, dz5, zp5, Wq5))
+
+        def block_ap(b=b, qp=qp):
+            for lin, W5, X5, dY5, s5, z5, ds5, dz5, zp5, Wq5 in qp:
+                o, i = lin.out, lin.inp
+                Q.qat_fakequant_linear_fwd(X5, W5, s5, z5, b, Y5[:M5 * o].view(M5, o), ws=ws5)
+                Q.qat_fakequant_linear_bwd_saved(dY5, X5, W5, s5, z5, ws5, b, dX=dX5[:M5 * i].view(M5, i),
+                                                 dW=dW5[:o * i].view(o, i), ds=ds5, dz=dz5)
+
+        def e2e(b=b, qp=qp):
+            for lin, W5, X5, dY5, s5, z5, ds5, dz5, zp5, Wq5 in qp:
+                o, i = lin.out, lin.inp
+                Q.qat_dequant_gemm_fwd(X5, Wq5, s5, zp5, b, Y5[:M5 * o].view(M5, o), ws=ws5)
+                Q.qat_dequant_gemm_bwd_s_saved(dY5, X5, Wq5, s5, zp5, ws5, b, ds5)
+        tb = stats_ms(g.per_call(block_ap, 5))
+        te = stats_ms(g.per_call(e2e, 5))
+        note(f"C5 at {b} bits done")
+        c5[f"w{b}g64"] = {"block_ap_fwd_bwd": dict(tb, **_rate(fl_bap, tb)), "e2e_fwd_ds": dict(te, **_rate(fl_e2e, te))}
+        del qp
+    # init and pack of the 896 MiB gate weight, cold
+    lin, W5 = data[0][0], data[0][1]
+    s5 = torch.empty(lin.out, lin.inp // 64, device=dev)
+    z5, zp5 = torch.empty_like(s5), torch.empty_like(s5)
+    Wq5 = torch.empty(lin.out, lin.inp * 2 // 8, dtype=torch.uint8, device=dev)
+    for label, fn in (("init_minmax", lambda: Q.qat_init_minmax(W5, 2, s5, z5)),
+                      ("pack", lambda: Q.qat_pack(W5, s5, z5, 2, Wq5, zp5))):
+        _, nbytes = work_per_launch(label, lin.m, lin.out, lin.inp, 2)
+        t = stats_ms(g.kernel_ms(label, fn, 5, True))
+        c5[f"{label}_cold_gate_w2"] = dict(t, gbs=round(nbytes / (t["median_ms"] * 1e-3) / 1e9, 1),
+                                          frac_of_peak=round(nbytes / (t["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    res["c5_70b_gate_down"] = dict(c5, gflop_block_ap=round(fl_bap / 1e9, 2), gflop_e2e_fwd_ds=round(fl_e2e / 1e9, 2))
+    del data, ws5, Y5, dX5, dW5, W5, s5, z5, zp5, Wq5
+    torch.cuda.empty_cache()
+    return res
 
 
 def deploy_measurements(Q, torch, dev, stream):
@@ -592,39 +788,40 @@ def block_step_measurements(Q, torch, dev, stream, steps=10):
             "kernel_sum_ms": round(ksum, 4), "params": nparam}
 
 
-def cpu_baseline(lin, W_np, X_np, dY_np, rows):
-    """The fp64 oracle timed on the host on a bounded sample: the same step
-    restricted to the first `rows` weight rows (all tokens, all inputs)."""
+def cpu_baseline(lin, W_np, X_np, dY_np, seconds):
+    """The fp64 oracle timed on the host on the same workload: the fake-quant
+    forward + backward of the whole q_proj linear (what `value` measures on
+    the GPU), repeated until `seconds` have passed (at least twice); the
+    median run is reported."""
     from oracle import qat_oracle as O
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    M, inp, bits = lin.m, lin.inp, lin.bits
-    W = W_np[:rows]
-    dY = dY_np[:, :rows].copy()
+    M, out, inp, bits = lin.m, lin.out, lin.inp, lin.bits
+    s, z = O.init_minmax(W_np, bits)
 
     def step():
-        s, z = O.init_minmax(W, bits)
-        O.fakequant_fwd(X_np, W, s, z, bits)
-        O.fakequant_bwd(dY, X_np, W, s, z, bits)
-        Wq, zp = O.pack(W, s, z, bits)
-        O.dequant_gemm_fwd(X_np, Wq, s, zp, inp, bits)
-        O.dequant_gemm_bwd_s(dY, X_np, Wq, s, zp, inp, bits)
+        O.fakequant_fwd(X_np, W_np, s, z, bits)
+        O.fakequant_bwd(dY_np, X_np, W_np, s, z, bits)
 
+    ts = []
     t0 = time.perf_counter()
-    step()
-    t1 = time.perf_counter()
-    reps = 1
-    while time.perf_counter() - t0 < 10.0 and reps < 5:
+    while len(ts) < 2 or (time.perf_counter() - t0 < seconds and len(ts) < 20):
+        a = time.perf_counter()
         step()
-        reps += 1
-    dt = (time.perf_counter() - t1) / max(reps - 1, 1) if reps > 1 else t1 - t0
-    flops = 12.0 * M * inp * rows
+        ts.append(time.perf_counter() - a)
+    dt = float(np.median(ts))
+    flops = 6.0 * M * inp * out
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"same step on the first {rows} of {lin.out} weight rows (all {M} tokens, all {inp} "
-                      f"inputs), {reps} runs, mean of the timed ones; fp64 numpy"}
+            "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"the fake-quant forward + backward of the whole q_proj workload ({out}x{inp}, {M} tokens, "
+                      f"w2g64), fp64 numpy oracle, {len(ts)} runs, median {dt:.2f} s"}
 
 
 if __name__ == "__main__":

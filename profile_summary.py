@@ -1,9 +1,9 @@
 """Summaries of rocprofv3 result databases for profiles/.
 
-    python -m weight_quantization_aware_amd.profile_summary stats <results.db> [--cmd "..."]
+    python profile_summary.py stats <results.db> [--cmd "..."]
         per-kernel dispatch count and mean / min / max duration (kernel trace)
 
-    python -m weight_quantization_aware_amd.profile_summary traffic <fetch.db> <write.db> \
+    python profile_summary.py traffic <fetch.db> <write.db> \
             --copy-bytes N [--cmd "..."]
         per-kernel HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE
         run, each scaled by what the same counter reads for the largest
@@ -11,7 +11,7 @@
         JSON keyed by the library's kernel labels, with the hash of the kernel
         sources it was measured on.
 
-    python -m weight_quantization_aware_amd.profile_summary pmc <results.db> [--cmd "..."]
+    python profile_summary.py pmc <results.db> [--cmd "..."]
         per-kernel means of the collected counters (summed over dimensions per
         dispatch) and, when present, MFMA utilisation =
         SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) and
@@ -19,7 +19,8 @@
         (GRBM_GUI_ACTIVE is summed over the 8 XCDs: it reads 8x the kernel's
         duration in cycles.)
 
-Reads SQLite databases written by rocprofv3 (ROCm 7); prints to stdout.
+Reads SQLite databases written by rocprofv3 (ROCm 7); prints to stdout. It
+sits beside bench.py, whose runs it summarises; the library does not use it.
 """
 from __future__ import annotations
 
@@ -31,23 +32,17 @@ import sqlite3
 import sys
 
 # rocprofv3 kernel symbol -> the label the library's own timing uses
+# k_gemm<BM, BN, BK, STAGES, WGM, WGN, GM, AMN, BMN, EP, NB>: the last four
+# template arguments name it (AMN / BMN: 0, 2 K-contiguous; 1, 3
+# MN-contiguous; EP the epilogue; NB the bit width or a tag).
+GEMM_RE = re.compile(r"k_gemm<(?:\s*\d+\s*,){7}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
+# k_gemm_fused<BM, BN, BK, STAGES, U2, BL, NB, BT, ADW>
+FUSED_RE = re.compile(r"k_gemm_fused<(?:\s*\d+\s*,){5}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
 LABELS = [
-    # k_gemm<BM, BN, BK, STAGES, AMN, BMN, EP, NB>
-    (r"k_gemm<[^>]*,\s*0,\s*\d,\s*0,\s*1>", "gemm_dx"),
-    (r"k_gemm<[^>]*,\s*1,\s*1,\s*1,\s*0>", "gemm_ste_grads"),
-    (r"k_gemm<[^>]*,\s*1,\s*1,\s*4,\s*0>", "gemm_ste_grads_adamw"),
-    (r"k_gemm<[^>]*,\s*1,\s*1,\s*2,\s*\d>", "gemm_e2e_grads"),
-    (r"k_gemm<[^>]*,\s*0,\s*0,\s*0,\s*0>", "gemm_fwd"),
-    (r"k_gemm<[^>]*,\s*0,\s*0,\s*3,\s*0>", "gemm_fwd_f32"),
-    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*5,\s*0>", "gemm_fwd_mse"),
     (r"k_attn_rowdot", "attn_rowdot"),
     (r"k_flash_fwd", "attn_fwd"),
     (r"k_flash_bwd_kv", "attn_bwd_kv"),
-    (r"k_gemm<[^>]*,\s*\d,\s*\d,\s*0,\s*5>", "attn_gemm_bf16"),
-    # k_gemm_fused<BM, BN, BK, STAGES, U2, BL, NB>
-    (r"k_gemm_fused<[^>]*,\s*1,\s*0>", "gemm_fwd_fused_fp32"),
-    (r"k_gemm_fused<[^>]*,\s*2,\s*\d>", "gemm_fwd_packed"),
-    (r"k_init_minmax", "init_minmax"),
+    (r"k_init_minmax|k_init_rows", "init_minmax"),
     (r"k_quant_codes", "quant_w_hat"),
     (r"k_w_hat_t<0,", "quant_w_hat_t"),
     (r"k_w_hat_t<1,", "dequant_t"),
@@ -57,6 +52,7 @@ LABELS = [
     (r"k_deploy_gemv_lds<2,", "deploy_gemv_w2"),
     (r"k_deploy_gemv_lds<3,", "deploy_gemv_w3"),
     (r"k_deploy_gemv_lds<4,", "deploy_gemv_w4"),
+    (r"k_deploy_gemv_xchunk<", "deploy_gemv_xchunk"),
     (r"k_deploy_gemv<2>", "deploy_gemv_xreg_w2"),
     (r"k_deploy_gemv<3>", "deploy_gemv_xreg_w3"),
     (r"k_deploy_gemv<4>", "deploy_gemv_xreg_w4"),
@@ -66,8 +62,6 @@ LABELS = [
     (r"k_rmsnorm_bwd", "rmsnorm_bwd"),
     (r"k_rope_table", "rope_table"),
     (r"k_rope\(", "rope"),
-    (r"k_softmax_fwd", "softmax_fwd"),
-    (r"k_softmax_bwd", "softmax_bwd"),
     (r"k_swiglu_fwd", "swiglu_fwd"),
     (r"k_swiglu_bwd", "swiglu_bwd"),
     (r"k_loss_final", "loss"),
@@ -77,6 +71,28 @@ LABELS = [
 
 
 def label_of(name: str):
+    m = FUSED_RE.search(name)
+    if m:
+        bl, nb, bt, _ = (int(v) for v in m.groups())
+        if bt == 1:
+            return "gemm_dx_fused_fp32" if bl == 1 else "gemm_dx_packed"
+        return "gemm_fwd_fused_fp32" if bl == 1 else "gemm_fwd_packed"
+    m = GEMM_RE.search(name)
+    if m:
+        amn, bmn, ep, nb = (int(v) for v in m.groups())
+        if ep == 1:
+            return "gemm_ste_grads"
+        if ep == 4:
+            return "gemm_ste_grads_adamw"
+        if ep == 2:
+            return "gemm_e2e_grads"
+        if ep == 5:
+            return "gemm_fwd_mse"
+        if ep == 3:
+            return "gemm_fwd_f32"
+        if nb == 5:
+            return "attn_gemm_bf16"
+        return "gemm_dx" if nb == 1 else "gemm_fwd"
     for pat, lab in LABELS:
         if re.search(pat, name):
             return lab

@@ -497,7 +497,7 @@ void launch_flash_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
   a.batches = B * a.nh;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
   LaunchTimer t("attn_fwd", st);
-  hipLaunchKernelGGL(k_flash_fwd, dim3((unsigned)((T + kBQ - 1) / kBQ), (unsigned)a.batches), dim3(256), 0, st, a);
+  QAT_LAUNCH(k_flash_fwd, dim3((unsigned)((T + kBQ - 1) / kBQ), (unsigned)a.batches), dim3(256), 0, st, a);
 }
 
 void launch_flash_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
@@ -520,7 +520,7 @@ void launch_flash_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v
   a.scale = 1.0f / sqrtf((float)kHD);
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
   LaunchTimer t("attn_bwd_kv", st);
-  hipLaunchKernelGGL(k_flash_bwd_kv, dim3((unsigned)((T + kBKV - 1) / kBKV), (unsigned)a.batches), dim3(256), 0, st,
+  QAT_LAUNCH(k_flash_bwd_kv, dim3((unsigned)((T + kBKV - 1) / kBKV), (unsigned)a.batches), dim3(256), 0, st,
                      a);
 }
 

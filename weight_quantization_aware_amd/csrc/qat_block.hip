@@ -573,7 +573,7 @@ void set_batch(GemmArgs& a, const Dims& d, View va, View vb, View vc) {
 void rope(const Dims& d, uint16_t* q, uint16_t* k, const Ws& w, float sgn, hipStream_t st) {
   LaunchTimer t("rope", st);
   const int64_t n = 2 * d.BT * (d.H / 16);
-  hipLaunchKernelGGL(k_rope, dim3((unsigned)blocks_of(n, 256)), dim3(256), 0, st, q, k, w.rope, d.BT, (int)d.T,
+  QAT_LAUNCH(k_rope, dim3((unsigned)blocks_of(n, 256)), dim3(256), 0, st, q, k, w.rope, d.BT, (int)d.T,
                      (int)d.H, sgn);
 }
 
@@ -583,12 +583,12 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
                    const uint16_t* target, float* y, float* loss, const Ws& w, hipStream_t st) {
   {
     LaunchTimer t("rope_table", st);
-    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)blocks_of(d.T * (kHeadDim / 2), 256)), dim3(256), 0, st,
+    QAT_LAUNCH(k_rope_table, dim3((unsigned)blocks_of(d.T * (kHeadDim / 2), 256)), dim3(256), 0, st,
                        w.rope, (int)d.T);
   }
   {
     LaunchTimer t("rmsnorm_fwd", st);
-    hipLaunchKernelGGL(k_rmsnorm_fwd<0>, dim3((unsigned)d.BT), dim3(256), 0, st, x, nullptr, nullptr, g1, w.h1,
+    QAT_LAUNCH(k_rmsnorm_fwd<0>, dim3((unsigned)d.BT), dim3(256), 0, st, x, nullptr, nullptr, g1, w.h1,
                        w.r1, (int)d.H);
   }
   fq_forward(d, L[QAT_BLOCK_Q], QAT_BLOCK_Q, w.h1, w.q, nullptr, w, st);
@@ -600,7 +600,7 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
   fq_forward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.attn, nullptr, w.o, w, st);
   {
     LaunchTimer t("rmsnorm_fwd", st);
-    hipLaunchKernelGGL(k_rmsnorm_fwd<1>, dim3((unsigned)d.BT), dim3(256), 0, st, x, w.o, w.x2, g2, w.h2, w.r2,
+    QAT_LAUNCH(k_rmsnorm_fwd<1>, dim3((unsigned)d.BT), dim3(256), 0, st, x, w.o, w.x2, g2, w.h2, w.r2,
                        (int)d.H);
   }
   fq_forward(d, L[QAT_BLOCK_GATE], QAT_BLOCK_GATE, w.h2, w.gate, nullptr, w, st);
@@ -608,7 +608,7 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
   {
     LaunchTimer t("swiglu_fwd", st);
     const int64_t n8 = d.BT * d.I / 8;
-    hipLaunchKernelGGL(k_swiglu_fwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.a, n8);
+    QAT_LAUNCH(k_swiglu_fwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.a, n8);
   }
   {
     // down, with y = x2 + down, dy = 2 (y - target) / n and the loss partials in its epilogue
@@ -622,7 +622,7 @@ void block_forward(const Dims& d, const qat_block_linear* L, const float* g1, co
     a.escale = (float)(2.0 / (double)n);
     const int64_t nb = launch_gemm_fwd_mse(a, st);
     LaunchTimer t("loss", st);
-    hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, st, w.partial, (int)nb, 1.0 / (double)n, loss);
+    QAT_LAUNCH(k_loss_final, dim3(1), dim3(256), 0, st, w.partial, (int)nb, 1.0 / (double)n, loss);
   }
 }
 
@@ -633,14 +633,14 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
   {
     LaunchTimer t("swiglu_bwd", st);
     const int64_t n8 = d.BT * d.I / 8;
-    hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.da, n8);
+    QAT_LAUNCH(k_swiglu_bwd, dim3((unsigned)blocks_of(n8, 256)), dim3(256), 0, st, w.gate, w.up, w.da, n8);
   }
   // gate and up now hold their output gradients
   fq_backward(d, L[QAT_BLOCK_GATE], QAT_BLOCK_GATE, w.gate, w.h2, w.dxg, w, ac, st);
   fq_backward(d, L[QAT_BLOCK_UP], QAT_BLOCK_UP, w.up, w.h2, w.dxu, w, ac, st);
   {
     LaunchTimer t("rmsnorm_bwd", st);
-    hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)d.BT), dim3(256), 0, st, w.dxg, w.dxu, w.x2, w.r2, g2, w.dy,
+    QAT_LAUNCH(k_rmsnorm_bwd, dim3((unsigned)d.BT), dim3(256), 0, st, w.dxg, w.dxu, w.x2, w.r2, g2, w.dy,
                        w.dx2, (int)d.H);
   }
   fq_backward(d, L[QAT_BLOCK_O], QAT_BLOCK_O, w.dx2, w.attn, w.dattn, w, ac, st);
@@ -648,7 +648,7 @@ void block_backward(const Dims& d, const qat_block_linear* L, const float* g2, c
     // D = rowsum(P dP) = dO . O per query
     LaunchTimer t("attn_rowdot", st);
     const int64_t n = d.BT * d.nh;
-    hipLaunchKernelGGL(k_attn_rowdot, dim3((unsigned)blocks_of(n, 256)), dim3(256), 0, st, w.dattn, w.attn, w.D,
+    QAT_LAUNCH(k_attn_rowdot, dim3((unsigned)blocks_of(n, 256)), dim3(256), 0, st, w.dattn, w.attn, w.D,
                        d.BT, (int)d.T, (int)d.H, (int)d.nh);
   }
   // dk, dv and dS^T (into the P buffer) in one pass over the causal pairs
@@ -710,7 +710,7 @@ void adamw_rest(const Dims& d, const qat_block_linear* L, const AdamConst& ac, h
   a.start[nseg] = blk;
   a.nseg = nseg;
   LaunchTimer tm("adamw", st);
-  hipLaunchKernelGGL(k_adamw, dim3((unsigned)blk), dim3(256), 0, st, a);
+  QAT_LAUNCH(k_adamw, dim3((unsigned)blk), dim3(256), 0, st, a);
 }
 
 // ---- validation ----

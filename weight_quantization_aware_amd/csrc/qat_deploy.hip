@@ -742,7 +742,7 @@ void launch_deploy_qparams(const float* s, const float* z, int64_t out, int64_t 
   const int64_t G = in / group, ldz = (G * bits + 7) / 8;
   const int64_t n = out * (G > ldz ? G : ldz);
   LaunchTimer t("deploy_qparams", st);
-  hipLaunchKernelGGL(k_deploy_qparams, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, z, out, G, bits,
+  QAT_LAUNCH(k_deploy_qparams, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, z, out, G, bits,
                      (float)((1 << bits) - 1), ldz, s16, zq);
 }
 
@@ -780,7 +780,7 @@ void launch_lds(const GemvArgs& a, int64_t nrb, int lds, hipStream_t st) {
     per_cu = 1;
   const int64_t slots = (int64_t)num_cus() * per_cu;
   const dim3 grid((unsigned)(nrb < slots ? nrb : slots));
-  hipLaunchKernelGGL((k_deploy_gemv_lds<N, RW, NB>), grid, dim3(1024), (size_t)lds, st, a);
+  QAT_LAUNCH((k_deploy_gemv_lds<N, RW, NB>), grid, dim3(1024), (size_t)lds, st, a);
 }
 
 template <int N>
@@ -791,7 +791,7 @@ void launch_xchunk(const GemvArgs& a, int64_t grid, int lds, hipStream_t st) {
                               (int)kLdsLimit);
     raised = true;
   }
-  hipLaunchKernelGGL((k_deploy_gemv_xchunk<N>), dim3((unsigned)grid), dim3(1024), (size_t)lds, st, a);
+  QAT_LAUNCH((k_deploy_gemv_xchunk<N>), dim3((unsigned)grid), dim3(1024), (size_t)lds, st, a);
 }
 
 }  // namespace
@@ -844,9 +844,9 @@ void launch_deploy_gemv(const uint16_t* X, const uint8_t* Wq, const uint16_t* s1
     return;
   }
   const dim3 grid((unsigned)((out + 15) / 16));
-  if (bits == 2) hipLaunchKernelGGL(k_deploy_gemv<2>, grid, dim3(512), 0, st, a);
-  else if (bits == 3) hipLaunchKernelGGL(k_deploy_gemv<3>, grid, dim3(512), 0, st, a);
-  else hipLaunchKernelGGL(k_deploy_gemv<4>, grid, dim3(512), 0, st, a);
+  if (bits == 2) QAT_LAUNCH(k_deploy_gemv<2>, grid, dim3(512), 0, st, a);
+  else if (bits == 3) QAT_LAUNCH(k_deploy_gemv<3>, grid, dim3(512), 0, st, a);
+  else QAT_LAUNCH(k_deploy_gemv<4>, grid, dim3(512), 0, st, a);
 }
 
 }  // namespace qat

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, int64
 void launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   const int64_t n4 = n / 4;
   LaunchTimer t("fill_zero", st);
-  hipLaunchKernelGGL(k_fill_zero, dim3(blocks_for(n4 > 0 ? n4 : 1, 256)), dim3(256), 0, st, (float4*)p, n4,
+  QAT_LAUNCH(k_fill_zero, dim3(blocks_for(n4 > 0 ? n4 : 1, 256)), dim3(256), 0, st, (float4*)p, n4,
                      p + n4 * 4, (int)(n - n4 * 4));
 }
 
@@ -273,16 +273,16 @@ void launch_init_minmax(const float* W, int64_t out, int64_t in, int group, int 
   const float K = (float)((1 << bits) - 1);
   LaunchTimer t("init_minmax", st);
   if (group == in && group != 32 && group != 64 && group != 128) {
-    hipLaunchKernelGGL(k_init_rows, dim3(blocks_for(out, 4)), dim3(256), 0, st, (const float4*)W, out, in / 4, K,
+    QAT_LAUNCH(k_init_rows, dim3(blocks_for(out, 4)), dim3(256), 0, st, (const float4*)W, out, in / 4, K,
                        s, z);
   } else if (group == 32) {
-    hipLaunchKernelGGL(k_init_minmax<32>, dim3(blocks_for(ngroups, 128)), dim3(256), 0, st, (const float4*)W,
+    QAT_LAUNCH(k_init_minmax<32>, dim3(blocks_for(ngroups, 128)), dim3(256), 0, st, (const float4*)W,
                        ngroups, K, s, z);
   } else if (group == 64) {
-    hipLaunchKernelGGL(k_init_minmax<64>, dim3(blocks_for(ngroups, 64)), dim3(256), 0, st, (const float4*)W,
+    QAT_LAUNCH(k_init_minmax<64>, dim3(blocks_for(ngroups, 64)), dim3(256), 0, st, (const float4*)W,
                        ngroups, K, s, z);
   } else {
-    hipLaunchKernelGGL(k_init_minmax<128>, dim3(blocks_for(ngroups, 32)), dim3(256), 0, st, (const float4*)W,
+    QAT_LAUNCH(k_init_minmax<128>, dim3(blocks_for(ngroups, 32)), dim3(256), 0, st, (const float4*)W,
                        ngroups, K, s, z);
   }
 }
@@ -291,7 +291,7 @@ void launch_quant_codes(const float* W, const float* s, const float* z, int64_t 
                         int bits, uint8_t* codes, uint16_t* w_hat, hipStream_t st) {
   int64_t nvec = out * in / 4;
   LaunchTimer t(codes ? "quant_codes" : "quant_w_hat", st);
-  hipLaunchKernelGGL(k_quant_codes, dim3(blocks_for(nvec, 256)), dim3(256), 0, st,
+  QAT_LAUNCH(k_quant_codes, dim3(blocks_for(nvec, 256)), dim3(256), 0, st,
                      (const float4*)W, s, z, nvec, FastDiv::make((uint32_t)group / 4), (float)((1 << bits) - 1),
                      (uint32_t*)codes, (uint2*)w_hat);
 }
@@ -304,11 +304,11 @@ void launch_pack(const float* W, const float* s, const float* z, int64_t out, in
   const FastDiv fd = FastDiv::make(cpg);
   LaunchTimer t("pack", st);
   if (bits == 2)
-    hipLaunchKernelGGL(k_pack<2>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
+    QAT_LAUNCH(k_pack<2>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
   else if (bits == 3)
-    hipLaunchKernelGGL(k_pack<3>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
+    QAT_LAUNCH(k_pack<3>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
   else
-    hipLaunchKernelGGL(k_pack<4>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
+    QAT_LAUNCH(k_pack<4>, grid, dim3(256), 0, st, (const float4*)W, s, z, nchunks, fd, cpg, Wq, zround);
 }
 
 void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t out, int64_t in, int group,
@@ -317,16 +317,16 @@ void launch_dequant(const uint8_t* Wq, const float* s, const float* z, int64_t o
   dim3 grid(blocks_for(nchunks, 256));
   const FastDiv fd = FastDiv::make((uint32_t)group / 8);
   LaunchTimer t("dequant", st);
-  if (bits == 2) hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
-  else if (bits == 3) hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
-  else hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
+  if (bits == 2) QAT_LAUNCH(k_dequant<2>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
+  else if (bits == 3) QAT_LAUNCH(k_dequant<3>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
+  else QAT_LAUNCH(k_dequant<4>, grid, dim3(256), 0, st, Wq, s, z, nchunks, fd, (uint4*)w_hat);
 }
 
 void launch_w_hat_t(const float* W, const float* s, const float* z, int64_t out, int64_t in, int group,
                     int bits, uint16_t* w_hat_t, hipStream_t st) {
   const dim3 grid((unsigned)(in / 64), (unsigned)((out + 127) / 128));
   LaunchTimer t("quant_w_hat_t", st);
-  hipLaunchKernelGGL((k_w_hat_t<0, 0>), grid, dim3(256), 0, st, W, s, z, out, in, in / group,
+  QAT_LAUNCH((k_w_hat_t<0, 0>), grid, dim3(256), 0, st, W, s, z, out, in, in / group,
                      FastDiv::make((uint32_t)group), (float)((1 << bits) - 1), w_hat_t);
 }
 
@@ -337,9 +337,9 @@ void launch_dequant_t(const uint8_t* Wq, const float* s, const float* z, int64_t
   const int64_t G = in / group;
   const FastDiv fd = FastDiv::make((uint32_t)group);
   LaunchTimer t("dequant_t", st);
-  if (bits == 2) hipLaunchKernelGGL((k_w_hat_t<1, 2>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
-  else if (bits == 3) hipLaunchKernelGGL((k_w_hat_t<1, 3>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
-  else hipLaunchKernelGGL((k_w_hat_t<1, 4>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
+  if (bits == 2) QAT_LAUNCH((k_w_hat_t<1, 2>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
+  else if (bits == 3) QAT_LAUNCH((k_w_hat_t<1, 3>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
+  else QAT_LAUNCH((k_w_hat_t<1, 4>), grid, dim3(256), 0, st, Wq, s, z, out, in, G, fd, K, w_hat_t);
 }
 
 }  // namespace qat

@@ -44,14 +44,14 @@ int batches(const GemmArgs& a) { return a.batch_h > 0 ? a.batches : 1; }
 template <int BM, int BN, int S, int WGM, int WGN, int AMN, int BMN, int EP, int NB, int GM = 0>
 void launch_bf16(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<kBf16, EP, NB>(), st);
-  hipLaunchKernelGGL((k_gemm<BM, BN, 64, S, WGM, WGN, GM, AMN, BMN, EP, NB>),
+  QAT_LAUNCH((k_gemm<BM, BN, 64, S, WGM, WGN, GM, AMN, BMN, EP, NB>),
                      dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
 template <int BM, int BN, int BK, int S, int BL, int NB, int BT = 0, int ADW = 0>
 void launch_fused(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<BL, kStoreBf16, NB, BT>(), st);
-  hipLaunchKernelGGL((k_gemm_fused<BM, BN, BK, S, 0, BL, NB, BT, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(256),
+  QAT_LAUNCH((k_gemm_fused<BM, BN, BK, S, 0, BL, NB, BT, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(256),
                      0, st, a);
 }
 

@@ -1,12 +1,16 @@
 // Internal launchers of the gfx950 kernels (not part of the C ABI).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qat {
 
-// Brackets one kernel launch with HIP events when timing is enabled
-// (qat_timing_enable); a single branch otherwise.
+// Names the kernel launched in its scope (by QAT_LAUNCH) for the library's
+// timing (qat_timing_enable): while timing is on for this label it holds two
+// HIP events that the launch binds to its own dispatch, so they time the
+// kernel from its start to its end without adding packets to the stream; a
+// single branch otherwise.
 class LaunchTimer {
  public:
   LaunchTimer(const char* label, hipStream_t st);
@@ -14,10 +18,25 @@ class LaunchTimer {
 
  private:
   const char* label_;
-  hipStream_t stream_;
   void* start_ = nullptr;
   void* stop_ = nullptr;
 };
+
+// The events of the innermost LaunchTimer of the calling thread that no launch
+// has taken yet (both null if none), for the next launch.
+void timing_events(hipEvent_t* start, hipEvent_t* stop);
+
+}  // namespace qat
+
+// hipLaunchKernelGGL's arguments; the launch carries the scope's timing events.
+#define QAT_LAUNCH(kernel, grid, block, shmem, stream, ...)                                      \
+  do {                                                                                           \
+    hipEvent_t qat_e0_ = nullptr, qat_e1_ = nullptr;                                             \
+    qat::timing_events(&qat_e0_, &qat_e1_);                                                      \
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, qat_e0_, qat_e1_, 0, __VA_ARGS__); \
+  } while (0)
+
+namespace qat {
 
 // Status of the launches a C-ABI call has just enqueued: QAT_OK, or QAT_ERR_HIP
 // with the HIP error text kept for qat_last_error (qat_api.hip).

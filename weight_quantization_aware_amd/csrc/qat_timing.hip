@@ -1,7 +1,9 @@
 // Optional per-kernel timing. While enabled, every kernel the library launches
-// (or only those with the selected label) is bracketed by a pair of HIP events
-// recorded on the launch stream; the report sums elapsed times per label. Events are created only while
-// timing is on and are kept for reuse until the process ends.
+// (or only those with the selected label) carries a pair of HIP events bound
+// to its own dispatch (hipExtLaunchKernel), which time it from its start to
+// its end without adding packets to the stream; the report sums elapsed
+// times per label. Events are created only while timing is on and are kept
+// for reuse until the process ends.
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -52,22 +54,53 @@ hipEvent_t take_event(Timing& t) {
 
 }  // namespace
 
-LaunchTimer::LaunchTimer(const char* label, hipStream_t st) : label_(label), stream_(st) {
+namespace {
+
+// The calling thread's events that the next launch binds (set by LaunchTimer).
+struct Pending {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool taken = false;
+};
+thread_local Pending g_pending;
+
+}  // namespace
+
+LaunchTimer::LaunchTimer(const char* label, hipStream_t) : label_(label) {
   Timing& t = timing();
   if (!t.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> g(t.mu);
   if (!t.only.empty() && t.only != label) return;
   start_ = take_event(t);
   stop_ = take_event(t);
-  if (start_ && stop_) hipEventRecord((hipEvent_t)start_, st);
+  if (!start_ || !stop_) {
+    if (start_) t.pool.push_back((hipEvent_t)start_);
+    if (stop_) t.pool.push_back((hipEvent_t)stop_);
+    start_ = stop_ = nullptr;
+    return;
+  }
+  g_pending = Pending{(hipEvent_t)start_, (hipEvent_t)stop_, false};
 }
 
 LaunchTimer::~LaunchTimer() {
-  if (!start_ || !stop_) return;
+  if (!start_) return;
+  const bool taken = g_pending.taken && g_pending.start == (hipEvent_t)start_;
+  g_pending = Pending{};
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  hipEventRecord((hipEvent_t)stop_, stream_);
-  t.records.push_back({label_, (hipEvent_t)start_, (hipEvent_t)stop_});
+  if (taken) {
+    t.records.push_back({label_, (hipEvent_t)start_, (hipEvent_t)stop_});
+  } else {                                          // no launch in the scope
+    t.pool.push_back((hipEvent_t)start_);
+    t.pool.push_back((hipEvent_t)stop_);
+  }
+}
+
+void timing_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (g_pending.start && !g_pending.taken) {
+    *start = g_pending.start;
+    *stop = g_pending.stop;
+    g_pending.taken = true;
+  }
 }
 
 }  // namespace qat
