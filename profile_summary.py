@@ -36,8 +36,8 @@ import sys
 # template arguments name it (AMN / BMN: 0, 2 K-contiguous; 1, 3
 # MN-contiguous; EP the epilogue; NB the bit width or a tag).
 GEMM_RE = re.compile(r"k_gemm<(?:\s*\d+\s*,){7}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
-# k_gemm_fused<BM, BN, BK, STAGES, U2, BL, NB, BT, ADW>
-FUSED_RE = re.compile(r"k_gemm_fused<(?:\s*\d+\s*,){5}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
+# k_gemm_fused<BM, BN, BL, NB, BT, ADW>
+FUSED_RE = re.compile(r"k_gemm_fused<(?:\s*\d+\s*,){2}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
 LABELS = [
     (r"k_attn_rowdot", "attn_rowdot"),
     (r"k_flash_fwd", "attn_fwd"),

@@ -7,10 +7,10 @@
 //   128x256, 3 stages   about one 128x256 tile per CU (2048-token q_proj);
 //                       8 waves
 //   128x128, 4 stages   small problems; 4 waves
-// Fused B operands (k_gemm_fused) go through an LDS ring beside the bf16
-// stages: packed codes (E2E-QP forward without workspace) with 256-row B tiles,
-// BK = 32, 4 stages; the fp32 master weight (fake-quant forward without
-// workspace) with 128-row B tiles, BK = 32, 3 stages.
+// Fused B operands (k_gemm_fused: the fp32 master weight or packed codes
+// turned into bf16 W_hat in LDS by converter waves beside the MFMA waves;
+// the forwards and the dX products without a workspace): 256x128 or 128x128
+// tiles, BK = 32, three stages.
 #include "qat_gemm_kernel.h"
 
 namespace qat {
@@ -48,11 +48,10 @@ void launch_bf16(const GemmArgs& a, hipStream_t st) {
                      dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
-template <int BM, int BN, int BK, int S, int BL, int NB, int BT = 0, int ADW = 0>
+template <int BM, int BN, int BL, int NB, int BT = 0, int ADW = 0>
 void launch_fused(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<BL, kStoreBf16, NB, BT>(), st);
-  QAT_LAUNCH((k_gemm_fused<BM, BN, BK, S, 0, BL, NB, BT, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(256),
-                     0, st, a);
+  QAT_LAUNCH((k_gemm_fused<BM, BN, BL, NB, BT, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(512), 0, st, a);
 }
 
 // Returns the number of workgroups launched.
@@ -115,31 +114,22 @@ void launch_grads(const GemmArgs& a, hipStream_t st) {
   else launch_grads_al<EP, NB, kMNContigD>(a, st);
 }
 
+// Fused B operands (k_gemm_fused, 4 MFMA + 4 converter waves, BK = 32):
+// 256 x 128 tiles where the output has at least one per CU, else 128 x 128.
 template <int BL, int NB>
 void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
-  if constexpr (BL == kPacked) {
-    if (tiles(a, 256, 256) >= 256) launch_fused<256, 256, 32, 4, BL, NB>(a, st);
-    else launch_fused<128, 256, 32, 4, BL, NB>(a, st);
-  } else {
-    if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, 32, 3, BL, NB>(a, st);
-    else launch_fused<128, 128, 32, 3, BL, NB>(a, st);
-  }
+  if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, BL, NB>(a, st);
+  else launch_fused<128, 128, BL, NB>(a, st);
 }
 
 // dX = dY W_hat with W_hat made in LDS from the weight's rows (the
-// transposed ring): fp32 master weight with 128-column B tiles; packed codes
-// with 256-column B tiles (a 32-row slab of 3-bit rows is then whole dwords).
+// transposed ring).
 // ADW: dY by 4-byte DMA with the contraction's tail masked (out not a
 // multiple of 64).
 template <int BL, int NB, int ADW>
 void launch_pick_dx_fused_a(const GemmArgs& a, hipStream_t st) {
-  if constexpr (BL == kPacked) {
-    if (tiles(a, 256, 256) >= 256) launch_fused<256, 256, 32, 4, BL, NB, 1, ADW>(a, st);
-    else launch_fused<128, 256, 32, 4, BL, NB, 1, ADW>(a, st);
-  } else {
-    if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, 32, 3, BL, NB, 1, ADW>(a, st);
-    else launch_fused<128, 128, 32, 3, BL, NB, 1, ADW>(a, st);
-  }
+  if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, BL, NB, 1, ADW>(a, st);
+  else launch_fused<128, 128, BL, NB, 1, ADW>(a, st);
 }
 
 template <int BL, int NB>

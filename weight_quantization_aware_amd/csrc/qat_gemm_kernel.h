@@ -138,11 +138,14 @@ struct DmaTileK {
   // src is [rows][ld] with K contiguous; rows >= nrows read as zero. The
   // range ends with the last row's kdim-th element, so a view into a wider
   // tensor (one head's columns) reads nothing past that tensor.
-  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int kdim_) {
+  // wave_: the wave's index among the NW loading waves (default: its index
+  // in the workgroup).
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int row0, int nrows, int kdim_,
+                                       int wave_ = -1) {
     kdim = kdim_;
     rs = buffer_rsrc(src + (int64_t)row0 * ld, ((int64_t)(nrows - 1 - row0) * ld + kdim) * 2);
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(wave_ < 0 ? (int)(threadIdx.x >> 6) : wave_);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
       const int r0 = (wave * NI + q) * RPI;
@@ -289,155 +292,181 @@ struct DmaTileOf<ROWS, BK, kMNContigD, NW> { using T = DmaTileMN<ROWS, BK, NW, 1
 // the MN-contiguous ones (read with transpose loads).
 constexpr bool k_contig(int layout) { return layout == kKContig || layout == kKContigD; }
 
-// Quantised-weight operands through an LDS ring. Per slab, the raw weight
-// bytes of ROWS rows (packed N-bit codes, BK*N/8 bytes per row; or the fp32
-// master weight, BK*4 bytes per row) and the rows' s and z reach a ring entry
-// by dword DMA, one slab ahead of the A operand. Every thread then converts
-// its share into the K-contiguous bf16 B stage two slabs ahead of the MFMAs:
+// The quantiser of the fused loaders, on its fast path: u = w * rcp with rcp
+// = v_rcp_f32(s) (within an ulp of 1/s), so u lies within 2^-22 |u| of
+// fl32(w / s); q - zr = med3(rint(u), -zr, K - zr) (exactly clamp(rint(u) +
+// zr, 0, K) - zr, small integers); W_hat = fma(q - zr, s, +0), one rounding
+// of the exact product like (q - zr) * s, with +0 where that product is a
+// zero (as the subtraction q - zr gives). Where u lies within 2^-20 |u| of a
+// half-integer (or is not finite) rint(u) may differ from the correctly
+// rounded quotient's: `tie` is set and the caller redoes the element with
+// quant_elem (the exact division), so the codes are exactly the fp32
+// quantiser's. Five VALU operations and a compare per weight.
+struct QRow {
+  float s, rcp, zr, lo, hi;
+};
+
+__device__ __forceinline__ QRow qrow(float s, float z, float K) {
+  QRow r;
+  r.s = s;
+  r.rcp = __builtin_amdgcn_rcpf(s);
+  r.zr = round_clamp_zero(z, K);
+  r.lo = -r.zr;
+  r.hi = K - r.zr;
+  return r;
+}
+
+__device__ __forceinline__ float qfast(float w, const QRow& r, bool& tie) {
+  const float u = w * r.rcp;
+  const float ru = __builtin_rintf(u);
+  const float c = __builtin_fmaf(__builtin_fabsf(u), -0x1p-20f, 0.5f);   // 0.5 - |u| 2^-20
+  tie = !(__builtin_fabsf(u - ru) < c);
+  return __builtin_fmaf(__builtin_amdgcn_fmed3f(ru, r.lo, r.hi), r.s, 0.0f);
+}
+
+// Two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, lo in bits 0-15.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  typedef float f2_ __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_ __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_{lo, hi}, b2_));
+}
+
+// A DMA instruction index of a slab loaded by 4 waves: instruction q of wave
+// cw; where the slab has fewer instructions than 4 x NI the last one repeats
+// (the same bytes to the same place), so every wave issues NI.
+template <int NTOT, int NI>
+__device__ __forceinline__ int dma_index(int cw, int q) {
+  return min(cw * NI + q, NTOT - 1);
+}
+
+// Quantised-weight operand through an LDS ring, B rows = weight rows (the
+// forward, Y = X W_hat^T), slabs of BK = 32 along `in`. A ring entry holds the
+// raw weights of ROWS rows -- the fp32 master weight, 128 bytes per row by
+// 16-byte DMA, the 16-byte piece c (4 weights) of row r at slot c ^ ((r >> 1)
+// & 3) so that the converters' reads spread over every bank; or packed N-bit
+// codes, 4 N bytes per row by dword DMA -- then the rows' s and z for the
+// slab (a 32-wide slab lies inside one group). Each of the 256 converter
+// threads turns 16 weights of one row into the K-contiguous bf16 B stage:
 //   packed (E2E-QP):  W_hat = (q - z) * s, z as stored;
-//   fp32 (Block-AP):  Eq. 1 then Eq. 2 with zr = clamp(rint(z), 0, K). u is
-//     w * fl32(1/s), within 3 ulp of fl32(w/s); where that interval could
-//     hold a half-integer the element is redone with the correctly rounded
-//     division, so the codes are exactly the fp32 quantiser's.
-// With BK = 32 a slab lies inside one quantisation group (groups of 32, 64,
-// 128 or a whole row), so one (s, z) pair per row and slab.
+//   fp32 (Block-AP):  Eq. 1 then Eq. 2 with zr = clamp(rint(z), 0, K), by
+//                     qfast (near-ties redone by quant_elem).
 template <int ROWS, int BK, int KIND, int NB>
 struct DmaRing {
   using L = LdsLayout<BK, kLdsSlots>;
-  static constexpr int DW = KIND == kPacked ? BK * NB / 32 : BK;   // weight dwords per row per slab
-  static constexpr int NI_Q = ROWS * DW / 64 / 4;                  // weight DMA instructions per wave
-  static constexpr int NI_S = 2 * ROWS / 64 / 4;                   // s and z, [2][ROWS] dwords
-  static constexpr int NI = NI_Q + NI_S;
-  static constexpr int P_BYTES = ROWS * DW * 4 + 2 * ROWS * 4;
-  static_assert(NI_Q * 256 == ROWS * DW && NI_S * 256 == 2 * ROWS, "ring tile shape");
+  static_assert(BK == 32 && ROWS == 128, "two converter threads per 32-weight row slab");
+  static constexpr int RB = KIND == kPacked ? BK * NB / 8 : BK * 4;     // ring bytes per row
+  static constexpr int W_BYTES = ROWS * RB;
+  static constexpr int P_BYTES = W_BYTES + 2 * ROWS * 4;
+  static constexpr int DMA_B = KIND == kPacked ? 256 : 1024;           // bytes per DMA instruction
+  static constexpr int NQ = W_BYTES / DMA_B, NS = 2 * ROWS / 64;       // weight / (s, z) instructions
+  static constexpr int NI_Q = (NQ + 3) / 4, NI_S = (NS + 3) / 4;
+  static constexpr int NI = NI_Q + NI_S;                               // per converter wave and slab
+  static_assert(NQ * DMA_B == W_BYTES && NS * 64 == 2 * ROWS, "ring tile shape");
   i32x4 rq, rsz[2];
-  uint32_t vq[NI_Q], vs[NI_S];
-  int wave;
+  uint32_t vq[NI_Q], dq[NI_Q], vs[NI_S], ds_[NI_S];
+  int which[NI_S];
   float K;
-  FastDiv gdiv;                                                    // k -> group index
+  FastDiv gdiv;                                                        // k -> group index
+  // cw: this converter wave's index (0..3)
   __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes, int row0, int nrows, const float* s,
-                                       const float* z, int64_t G, int group, float K_) {
+                                       const float* z, int64_t G, int group, float K_, int cw) {
     K = K_;
     gdiv = FastDiv::make((uint32_t)group);
     rq = buffer_rsrc((const uint8_t*)Wsrc + (int64_t)row0 * row_bytes, (int64_t)(nrows - row0) * row_bytes);
     rsz[0] = buffer_rsrc(s + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
     rsz[1] = buffer_rsrc(z + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
     const int lane = threadIdx.x & 63;
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int q = 0; q < NI_Q; ++q) {
-      const int idx = (wave * NI_Q + q) * 64 + lane;       // flat dword of the [ROWS][DW] slab
-      vq[q] = (uint32_t)((idx / DW) * row_bytes + (idx % DW) * 4);
+      const int idx = dma_index<NQ, NI_Q>(cw, q);
+      const int b = idx * DMA_B + lane * (DMA_B / 64);                 // ring byte of this lane
+      const int r = b / RB;
+      if constexpr (KIND == kPacked) {
+        vq[q] = (uint32_t)(r * row_bytes + b % RB);
+      } else {
+        const int chunk = ((b % RB) >> 4) ^ ((r >> 1) & 3);
+        vq[q] = (uint32_t)(r * row_bytes + chunk * 16);
+      }
+      dq[q] = (uint32_t)(idx * DMA_B);
     }
 #pragma unroll
     for (int q = 0; q < NI_S; ++q) {
-      const int idx = (wave * NI_S + q) * 64 + lane;       // flat dword of [2][ROWS]
-      vs[q] = (uint32_t)((idx % ROWS) * G * 4);
+      const int idx = dma_index<NS, NI_S>(cw, q);
+      const int f = idx * 64 + lane;                                   // dword of [2][ROWS]
+      which[q] = (idx * 64) / ROWS;                                    // 0: s, 1: z (uniform)
+      vs[q] = (uint32_t)((f % ROWS) * G * 4);
+      ds_[q] = (uint32_t)(W_BYTES + idx * 256);
     }
   }
-  // lds_p: this slab's ring entry: [ROWS][DW] weight dwords, then s[ROWS], z[ROWS].
+  // lds_p: this slab's ring entry; k0: its first weight column.
   __device__ __forceinline__ void issue(uint32_t lds_p, int k0) const {
     const uint32_t cb = KIND == kPacked ? (uint32_t)(k0 * NB / 8) : (uint32_t)(k0 * 4);
-    const uint32_t gb = gdiv.div((uint32_t)k0) * 4;               // the slab lies inside one group
+    const uint32_t gb = gdiv.div((uint32_t)k0) * 4;                    // the slab lies inside one group
 #pragma unroll
-    for (int q = 0; q < NI_Q; ++q) dma4(rq, lds_p + (uint32_t)((wave * NI_Q + q) * 256), vq[q] + cb);
+    for (int q = 0; q < NI_Q; ++q) {
+      if constexpr (KIND == kPacked) dma4(rq, lds_p + dq[q], vq[q] + cb);
+      else dma16(rq, lds_p + dq[q], vq[q] + cb);
+    }
 #pragma unroll
     for (int q = 0; q < NI_S; ++q) {
-      const int which = ((wave * NI_S + q) * 64) / ROWS;    // 0: s, 1: z (uniform per instruction)
-      i32x4 r = which ? rsz[1] : rsz[0];
+      i32x4 r = which[q] ? rsz[1] : rsz[0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_readfirstlane(r[e]);
-      dma4(r, lds_p + ROWS * DW * 4 + (uint32_t)((wave * NI_S + q) * 256), vs[q] + gb);
+      dma4(r, lds_p + ds_[q], vs[q] + gb);
     }
   }
-  // Convert one slab from the ring entry at byte p into the B stage at byte b.
-  // IL > 0: the caller's IL MFMAs of the same slab precede this in the same
-  // basic block; the conversion's VALU work is interleaved with them (all
-  // fast paths first, near-ties redone behind one branch, then the stores).
-  template <int IL = 0>
-  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b) const {
-    constexpr int PARTS = 256 / ROWS;                      // threads per row
-    constexpr int CPT = (BK / 8) / PARTS;                  // 8-element chunks per thread
-    const int row = threadIdx.x / PARTS, part = threadIdx.x % PARTS;
-    // fp32 rows are 128 bytes: odd row pairs take their two chunks in the
-    // other order, so that the 16-byte reads of 8 neighbouring lanes fall on
-    // distinct banks
-    const int cx = (KIND != kPacked && PARTS == 2 && CPT == 2) ? (row >> 1) & 1 : 0;
-    auto chunk = [&](int cc) { return (part * CPT + cc) ^ cx; };
-    const uint32_t* q = (const uint32_t*)&smem[p + row * DW * 4];
-    const float sv = *(const float*)&smem[p + ROWS * DW * 4 + row * 4];
-    const float zv = *(const float*)&smem[p + ROWS * DW * 4 + ROWS * 4 + row * 4];
-    float h[CPT][8];
-    uint32_t tie = 0;                                      // fp32: elements near a rounding tie
-    const float zr = round_clamp_zero(zv, K);
-    const float rcp = 1.0f / sv;
+  // Convert the slab in the ring entry at byte p into the B stage at byte b;
+  // tid: the converter thread (0..255): row tid / 2, weights 16 (tid % 2) ..
+  // + 15 of the slab.
+  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int tid) const {
+    const int row = tid >> 1, hf = tid & 1;
+    const float sv = *(const float*)&smem[p + W_BYTES + row * 4];
+    const float zv = *(const float*)&smem[p + W_BYTES + ROWS * 4 + row * 4];
+    float h[16];
+    if constexpr (KIND == kPacked) {
+      const uint32_t* q = (const uint32_t*)&smem[p + row * RB];
+      const int bit = hf * 16 * NB;
+      uint64_t w = q[bit >> 5];
+      if (NB != 2) w |= (uint64_t)q[(bit >> 5) + 1] << 32;
+      w >>= (bit & 31);
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-      const int c = chunk(cc);                             // chunk of this row's slab
-      if constexpr (KIND == kPacked) {
-        const int bit = c * 8 * NB;
-        uint64_t w = q[bit >> 5];
-        if (NB == 3 && (bit & 31) > 8) w |= (uint64_t)q[(bit >> 5) + 1] << 32;
-        const uint32_t word = (uint32_t)(w >> (bit & 31));
+      for (int e = 0; e < 16; ++e) h[e] = ((float)(uint32_t)((w >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv;
+    } else {
+      const QRow r = qrow(sv, zv, K);
+      const int sw = (row >> 1) & 3;
+      uint32_t tie = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) h[cc][k] = ((float)((word >> (NB * k)) & ((1u << NB) - 1)) - zv) * sv;
-      } else {
-        const uint4 w0 = *(const uint4*)&q[c * 8], w1 = *(const uint4*)&q[c * 8 + 4];
-        const uint32_t wb[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      for (int j = 0; j < 4; ++j) {
+        const float4 w4 = *(const float4*)&smem[p + row * RB + (((4 * hf + j) ^ sw) << 4)];
+        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float w = __builtin_bit_cast(float, wb[k]);
-          const float u = w * rcp;
-          const float ru = __builtin_rintf(u);
-          // distance to the nearest half-integer: 0.5 - |u - rint(u)|, exact
-          // wherever it can fall under the threshold
-          if (0.5f - fabsf(u - ru) <= fabsf(u) * 0x1p-20f + 0x1p-60f) tie |= 1u << (cc * 8 + k);
-          const float qv = fminf(fmaxf(ru + zr, 0.0f), K);
-          h[cc][k] = (qv - zr) * sv;
+        for (int e = 0; e < 4; ++e) {
+          bool t;
+          h[4 * j + e] = qfast(wv[e], r, t);
+          tie |= (uint32_t)t << (4 * j + e);
         }
       }
-    }
-    if constexpr (IL > 0) {
-      // VALU instructions placed after each MFMA: NV per converted element,
-      // spread over the IL MFMAs (NV measured best on the 2048- and 4096-token
-      // shapes; the rest of the conversion follows the last MFMA).
-      constexpr int NV = KIND == kPacked ? 2 : 6;
-      constexpr int PER = (CPT * 8 * NV + IL - 1) / IL;
+      if (tie) {                                               // near a rounding tie: exact division
 #pragma unroll
-      for (int i = 0; i < IL; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0); // then VALU
-      }
-    }
-    if constexpr (KIND != kPacked) {
-      if (tie) {                                           // near a rounding tie: exact division
+        for (int j = 0; j < 4; ++j) {
+          const float* wr = (const float*)&smem[p + row * RB + (((4 * hf + j) ^ sw) << 4)];
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
-          const uint32_t* qc = q + chunk(cc) * 8;
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (tie & (1u << (cc * 8 + k))) {
-              float wt = __builtin_bit_cast(float, qc[k]);
+          for (int e = 0; e < 4; ++e)
+            if (tie & (1u << (4 * j + e))) {
+              float wt = wr[e];
               rare_branch(wt);
-              h[cc][k] = quant_elem(wt, sv, zr, K).w_hat;
+              h[4 * j + e] = quant_elem(wt, sv, r.zr, K).w_hat;
             }
         }
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-      const int c = chunk(cc);
-      *(uint4*)&smem[b + L::off(row, c)] = make_uint4(pack_bf16x2(h[cc][0], h[cc][1]), pack_bf16x2(h[cc][2], h[cc][3]),
-                                                       pack_bf16x2(h[cc][4], h[cc][5]), pack_bf16x2(h[cc][6], h[cc][7]));
-    }
+    for (int m = 0; m < 2; ++m)
+      *(uint4*)&smem[b + L::off(row, 2 * hf + m)] =
+          make_uint4(pack2_bf16(h[8 * m], h[8 * m + 1]), pack2_bf16(h[8 * m + 2], h[8 * m + 3]),
+                     pack2_bf16(h[8 * m + 4], h[8 * m + 5]), pack2_bf16(h[8 * m + 6], h[8 * m + 7]));
   }
 };
-
-template <int BL, class Ld>
-__device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
-  if constexpr (BL == kFp32Quant) l.init(a.B, a.ldb * 4, n0, a.N, a.s, a.z, a.G, a.group, a.Kq);
-  else l.init(a.B, a.ldb, n0, a.N, a.s, a.z, a.G, a.group, a.Kq);
-}
 
 // The weight as the B operand of dX = dY W_hat (contraction over the weight's
 // rows): B[n][k] = W_hat[k][n], so a slab is BK weight rows k0 .. k0 + BK - 1
@@ -446,33 +475,35 @@ __device__ __forceinline__ void init_b(Ld& l, const GemmArgs& a, int n0) {
 // row, by dword DMA, since 3-bit rows are only 8-byte aligned), followed by
 // the (s, z) of every 32-weight slot of those rows: s[BK][SL], z[BK][SL],
 // slot t holding the group of weight n0 + 32 t (groups of 32 or more never
-// split a slot). Every thread converts its share -- fp32: 4 consecutive
-// weights of one row per step; packed: 8 -- with the quantiser of DmaRing,
-// into the bf16 B stage in the MN-contiguous layout of DmaTileMN ([BK][ROWS],
-// read back with transpose loads). Weight rows at or beyond the contraction's
-// end (kdim) read as zero and convert to exactly 0.
+// split a slot). Each converter thread turns its share -- fp32: 4 quads of
+// 4 consecutive weights; packed: 2 pieces of 8 -- with the quantiser of
+// DmaRing into the bf16 B stage in the MN-contiguous layout of DmaTileMN
+// ([BK][ROWS], read back with transpose loads). Weight rows at or beyond the
+// contraction's end (kdim) read as zero and convert to exactly 0.
 template <int ROWS, int BK, int KIND, int NB>
 struct DmaRingT {
   using LT = DmaTileMN<ROWS, BK, 4>;
+  static_assert(BK == 32, "one 32-row slab");
   static constexpr int RB = KIND == kPacked ? ROWS * NB / 8 : ROWS * 4;    // ring bytes per weight row
   static constexpr int SL = ROWS / 32;                                      // (s, z) slots per row
   static constexpr int W_BYTES = BK * RB;
   static constexpr int P_BYTES = W_BYTES + 2 * BK * SL * 4;
   static constexpr int DMA_B = KIND == kPacked ? 256 : 1024;               // bytes per DMA instruction
-  static constexpr int NI_Q = W_BYTES / DMA_B / 4;                          // weight DMAs per wave
-  static constexpr int NI_S = 2 * BK * SL / 64 / 4;                         // s and z DMAs per wave
+  static constexpr int NQ = W_BYTES / DMA_B, NS = 2 * BK * SL / 64;
+  static constexpr int NI_Q = (NQ + 3) / 4, NI_S = (NS + 3) / 4;
   static constexpr int NI = NI_Q + NI_S;
-  static_assert(NI_Q * DMA_B * 4 == W_BYTES && NI_S * 256 == 2 * BK * SL, "ring tile shape");
+  static_assert(NQ * DMA_B == W_BYTES && NS * 64 == 2 * BK * SL, "ring tile shape");
   static_assert(KIND == kPacked || RB % 16 == 0, "16-byte DMA pieces of fp32 rows");
   i32x4 rq, rsz[2];
-  uint32_t vq[NI_Q], vs[NI_S];
-  int wave, kdim;
+  uint32_t vq[NI_Q], dq[NI_Q], vs[NI_S], ds_[NI_S];
+  int which[NI_S];
+  int kdim;
   int64_t row_bytes, grow;                                                  // weight / (s, z) row strides
   float K;
   // Wsrc: the weight [kdim][ld] (fp32) or its packed rows (row_bytes each);
-  // n0: first weight column of the tile; s, z: [kdim][G].
+  // n0: first weight column of the tile; s, z: [kdim][G]; cw: converter wave.
   __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes_, int n0, int kdim_, const float* s,
-                                       const float* z, int64_t G, int group, float K_) {
+                                       const float* z, int64_t G, int group, float K_, int cw) {
     K = K_;
     kdim = kdim_;
     row_bytes = row_bytes_;
@@ -482,16 +513,20 @@ struct DmaRingT {
     rsz[0] = buffer_rsrc(s, (int64_t)kdim * G * 4);
     rsz[1] = buffer_rsrc(z, (int64_t)kdim * G * 4);
     const int lane = threadIdx.x & 63;
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int q = 0; q < NI_Q; ++q) {
-      const int b = ((wave * NI_Q + q) * 64 + lane) * (DMA_B / 64);      // byte of the [BK][RB] slab
+      const int idx = dma_index<NQ, NI_Q>(cw, q);
+      const int b = idx * DMA_B + lane * (DMA_B / 64);                 // byte of the [BK][RB] slab
       vq[q] = (uint32_t)((b / RB) * row_bytes + b % RB);
+      dq[q] = (uint32_t)(idx * DMA_B);
     }
 #pragma unroll
     for (int q = 0; q < NI_S; ++q) {
-      const int r = ((wave * NI_S + q) * 64 + lane) % (BK * SL);         // slot of [BK][SL]
+      const int idx = dma_index<NS, NI_S>(cw, q);
+      const int r = (idx * 64 + lane) % (BK * SL);                     // slot of [BK][SL]
+      which[q] = (idx * 64) / (BK * SL);                               // 0: s, 1: z (uniform)
       vs[q] = (uint32_t)((r / SL) * G * 4 + ((n0 + 32 * (r % SL)) / group) * 4);
+      ds_[q] = (uint32_t)(W_BYTES + idx * 256);
     }
   }
   // lds_p: this slab's ring entry; k0: its first weight row.
@@ -499,29 +534,27 @@ struct DmaRingT {
     const uint32_t rb = (uint32_t)(k0 * row_bytes), gb = (uint32_t)(k0 * grow);
 #pragma unroll
     for (int q = 0; q < NI_Q; ++q) {
-      const uint32_t dst = lds_p + (uint32_t)((wave * NI_Q + q) * DMA_B);
-      if constexpr (KIND == kPacked) dma4(rq, dst, vq[q] + rb);
-      else dma16(rq, dst, vq[q] + rb);
+      if constexpr (KIND == kPacked) dma4(rq, lds_p + dq[q], vq[q] + rb);
+      else dma16(rq, lds_p + dq[q], vq[q] + rb);
     }
 #pragma unroll
     for (int q = 0; q < NI_S; ++q) {
-      const int which = ((wave * NI_S + q) * 64) / (BK * SL);  // 0: s, 1: z (uniform per instruction)
-      i32x4 r = which ? rsz[1] : rsz[0];
+      i32x4 r = which[q] ? rsz[1] : rsz[0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_readfirstlane(r[e]);
-      dma4(r, lds_p + W_BYTES + (uint32_t)((wave * NI_S + q) * 256), vs[q] + gb);
+      dma4(r, lds_p + ds_[q], vs[q] + gb);
     }
   }
   // Convert the slab of weight rows k0 .. from the ring entry at byte p into
-  // the B stage at byte b.
-  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int k0) const {
+  // the B stage at byte b; tid: the converter thread (0..255).
+  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int k0, int tid) const {
     const float* sl = (const float*)&smem[p + W_BYTES];
     const float* zl = sl + BK * SL;
     if constexpr (KIND == kPacked) {
-      constexpr int CPR = ROWS / 8, CPT = BK * CPR / 256;                  // 8-weight chunks
+      constexpr int CPR = ROWS / 8, CPT = BK * CPR / 256;                  // 8-weight pieces
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int ch = threadIdx.x + 256 * i, k = ch / CPR, c = ch % CPR;
+        const int ch = tid + 256 * i, k = ch / CPR, c = ch % CPR;
         const uint32_t* q = (const uint32_t*)&smem[p + k * RB];
         const int bit = c * 8 * NB;
         uint64_t w = q[bit >> 5];
@@ -532,8 +565,8 @@ struct DmaRingT {
         float h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = live ? ((float)((word >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv : 0.0f;
-        *(uint4*)&smem[b + LT::off(k, c)] = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
-                                                        pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7]));
+        *(uint4*)&smem[b + LT::off(k, c)] = make_uint4(pack2_bf16(h[0], h[1]), pack2_bf16(h[2], h[3]),
+                                                        pack2_bf16(h[4], h[5]), pack2_bf16(h[6], h[7]));
       }
     } else {
       constexpr int QPR = ROWS / 4, QPT = BK * QPR / 256;                  // 4-weight quads
@@ -542,25 +575,21 @@ struct DmaRingT {
       uint32_t tie = 0;
 #pragma unroll
       for (int i = 0; i < QPT; ++i) {
-        const int qd = threadIdx.x + 256 * i, k = qd / QPR, qc = qd % QPR;
+        const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
         const float4 w4 = *(const float4*)&smem[p + k * RB + qc * 16];
-        const float sv = sl[k * SL + qc / 8];
-        const float zr = round_clamp_zero(zl[k * SL + qc / 8], K);
-        const float rcp = 1.0f / sv;
+        const QRow r = qrow(sl[k * SL + qc / 8], zl[k * SL + qc / 8], K);
         const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float u = wv[e] * rcp;
-          const float ru = __builtin_rintf(u);
-          if (0.5f - fabsf(u - ru) <= fabsf(u) * 0x1p-20f + 0x1p-60f) tie |= 1u << (i * 4 + e);
-          const float qv = fminf(fmaxf(ru + zr, 0.0f), K);
-          h[i][e] = (qv - zr) * sv;
+          bool t;
+          h[i][e] = qfast(wv[e], r, t);
+          tie |= (uint32_t)t << (i * 4 + e);
         }
       }
       if (tie) {                                              // near a rounding tie: exact division
 #pragma unroll
         for (int i = 0; i < QPT; ++i) {
-          const int qd = threadIdx.x + 256 * i, k = qd / QPR, qc = qd % QPR;
+          const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
           const float* wr = (const float*)&smem[p + k * RB + qc * 16];
           const float sv = sl[k * SL + qc / 8];
           const float zr = round_clamp_zero(zl[k * SL + qc / 8], K);
@@ -575,10 +604,10 @@ struct DmaRingT {
       }
 #pragma unroll
       for (int i = 0; i < QPT; ++i) {
-        const int qd = threadIdx.x + 256 * i, k = qd / QPR, qc = qd % QPR;
+        const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
         const bool live = k0 + k < kdim;
         *(uint2*)&smem[b + LT::off(k, qc >> 1) + (qc & 1) * 8] =
-            live ? make_uint2(pack_bf16x2(h[i][0], h[i][1]), pack_bf16x2(h[i][2], h[i][3])) : make_uint2(0u, 0u);
+            live ? make_uint2(pack2_bf16(h[i][0], h[i][1]), pack2_bf16(h[i][2], h[i][3])) : make_uint2(0u, 0u);
       }
     }
   }
@@ -1164,142 +1193,138 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMM with a fused B operand (packed codes or the fp32 master weight through
-// an LDS ring, see DmaRing) and a K-contiguous bf16 A; bf16 output. STAGES
-// LDS stages (>= 3). With one k-step per slab (BK = 32) U2 = 1 unrolls slabs
-// in pairs so the two fragment sets alternate; U2 = 0 copies the next slab's
-// fragments instead (fewer live registers).
-// Invariant at the top of slab kt: slabs <= kt are visible to every wave and
-// F[0] holds the first k-step's fragments of slab kt. The barrier in slab kt
-// certifies slab kt + 1, so the fragments of the next slab are read while the
-// current slab's MFMAs run, and the DMA for slab kt + STAGES - 1 goes into the
-// stage slab kt - 1 has just released. The ring runs one slab ahead of A and
-// is converted into the bf16 B stage two slabs ahead of the MFMAs.
+// GEMM with a fused B operand: W_hat is made in LDS from the fp32 master
+// weight (Eq. 1-2) or from packed codes, never stored. A is bf16 and
+// K-contiguous; bf16 output. Slabs of BK = 32.
+// The workgroup's 8 waves have two roles, one of each on every SIMD:
+// - waves 0-3 (2 x 2 over the BM x BN tile) issue only LDS fragment reads and
+//   MFMAs: the MFMAs of slab i interleaved with the reads of slab i + 1;
+// - waves 4-7 (converters) issue every DMA -- A of slab i + 3 and the raw
+//   weights (ring) of slab i + 4 -- and turn ring slab i + 2 into its bf16
+//   B stage (DmaRing / DmaRingT), VALU work that runs beside the other
+//   wave's MFMAs.
+// Both roles pass the same barriers: P0, P1, P2 in the prologue, then one
+// per slab. Three A stages, three B stages and three ring
+// entries: at iteration i the MFMA waves read slab i + 1 (A stage and B stage
+// (i + 1) % 3), the converters write B stage (i + 2) % 3 and DMA into A
+// stage i % 3 (slab i, read during iteration i - 1) and ring entry
+// (i + 1) % 3 (slab i + 1, converted during iteration i - 1); each DMA has
+// two slabs of time to land (converters wait for the previous iteration's
+// DMAs before the barrier). Slabs past the end re-load the last one (uniform
+// wait counts); nothing reads what they make.
+// BT = 0: B rows are weight rows (Y = X W_hat^T); BT = 1: B rows are weight
+// columns (dX = dY W_hat), the B stage MN-contiguous. ADW: A by 4-byte DMA
+// with the contraction's tail masked (dY rows of out % 64 != 0 elements).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int U2, int BL, int NB, int BT = 0, int ADW = 0>
-__global__ __launch_bounds__(256, 1) void k_gemm_fused(const GemmArgs a) {
+template <int BM, int BN, int BL, int NB, int BT, int ADW>
+__global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
+  constexpr int BK = 32, S = 3;
   using L = LdsLayout<BK, kLdsSlots>;
-  using LA = DmaTileK<BM, BK, kLdsSlots, 4, ADW>;         // ADW: A by 4-byte DMA, contraction tail masked
-  // BT = 0: B rows are weight rows (Y = X W_hat^T); BT = 1: B rows are weight
-  // columns (dX = dY W_hat), the stage MN-contiguous
+  using LA = DmaTileK<BM, BK, kLdsSlots, 4, ADW>;
   using LB = typename std::conditional<BT == 0, DmaRing<BN, BK, BL, NB>, DmaRingT<BN, BK, BL, NB>>::type;
   using FB = typename std::conditional<BT == 0, DmaTileK<BN, BK, kLdsSlots>, DmaTileMN<BN, BK, 4>>::type;
   static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
-  static_assert(BT == 0 || (BK == 32 && U2 == 0), "the transposed ring runs one k-step per slab");
-  static_assert(STAGES >= 3, "the shifted pipeline needs three stages");
   constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TI = WM / 16, TJ = WN / 16;
-  constexpr int KS = BK / 32;                              // k-steps per slab
-  constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int P_STAGE = LB::P_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + STAGES * P_STAGE];
-  constexpr int P0 = STAGES * STAGE;                       // byte offset of the ring
+  constexpr int TI = WM / 16, TJ = WN / 16, NM = TI * TJ, NR = TI + TJ;
+  static_assert(NR <= NM, "a slab's MFMAs cover the next slab's reads");
+  constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH, P_BYTES = LB::P_BYTES;
+  constexpr int A0 = 0, B0 = S * A_BYTES, P0 = B0 + S * B_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[P0 + S * P_BYTES];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const uint32_t lds0 = lds_addr_of(smem);
-
-  LA la;
-  LB lb;
-  la.init(a.A, a.lda, m0, a.M, a.K);
-  if constexpr (BT == 0) init_b<BL>(lb, a, n0);
-  else lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, a.Kq);
-  constexpr int NL = LA::NI + LB::NI;                     // DMA instructions per wave per slab
-
   const int nk = (a.K + BK - 1) / BK;
-  auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
-  // All DMA of one iteration: A of slab `slab`, ring weights of slab + 1.
-  auto issue = [&](int slab) {
-    const uint32_t st = lds0 + (uint32_t)((slab % STAGES) * STAGE);
-    la.issue(st, clamp_slab(slab) * BK);
-    lb.issue(lds0 + P0 + (uint32_t)(((slab + 1) % STAGES) * P_STAGE), clamp_slab(slab + 1) * BK);
-  };
-  auto b_commit = [&](int slab) {
-    if constexpr (BT == 0) lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES);
-    else lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES, slab * BK);
-  };
-  auto b_commit_il = [&](int slab) {
-    if constexpr (BT == 0)
-      lb.template commit<KS == 1 ? TI * TJ : 0>(smem, P0 + (slab % STAGES) * P_STAGE,
-                                                 (slab % STAGES) * STAGE + A_BYTES);
-    else lb.commit(smem, P0 + (slab % STAGES) * P_STAGE, (slab % STAGES) * STAGE + A_BYTES, slab * BK);
-  };
 
-  // Fragment reads index the __shared__ array directly (stage given as a byte
-  // offset) so that they stay ds_read instructions.
-  auto read_frags = [&](int st, int ks, Frags<TI, TJ>& f) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) f.a[i] = LA::frag(&smem[st], wm0 + i * 16 + (lane & 15), ks, lane);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) f.b[j] = FB::frag(&smem[st + A_BYTES], wn0 + j * 16 + (lane & 15), ks, lane);
-  };
-
-  f32x4 acc[TJ][TI];
-#pragma unroll
-  for (int j = 0; j < TJ; ++j)
-#pragma unroll
-    for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto mfmas = [&](const Frags<TI, TJ>& f) {
+  if (wave < 4) {
+    // ---- MFMA waves
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    auto read_r = [&](int slot, int r, Frags<TI, TJ>& f) {
+      const uint8_t* at = &smem[A0 + slot * A_BYTES];
+      const uint8_t* bt = &smem[B0 + slot * B_BYTES];
+      if (r < TI) f.a[r] = LA::frag(at, wm0 + r * 16 + (lane & 15), 0, lane);
+      else f.b[r - TI] = FB::frag(bt, wn0 + (r - TI) * 16 + (lane & 15), 0, lane);
+    };
+    f32x4 acc[TJ][TI];
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
-  };
-
-  // prologue: ring slabs 0, 1 converted, A slabs 0 .. STAGES-2 in flight, F[0] loaded.
-  lb.issue(lds0 + P0, 0);                     // ring slab 0; issue(sl) brings slab sl + 1
+      for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // MFMAs on `cur`, each followed by (at most) one read of slab-slot `nslot` into `nxt`
+    auto step = [&](const Frags<TI, TJ>& cur, int nslot, Frags<TI, TJ>& nxt) {
 #pragma unroll
-  for (int sl = 0; sl < STAGES - 1; ++sl) issue(sl);
-  wait_vmcnt<0>();
-  __syncthreads();                            // ring slabs 0, 1 visible
-  b_commit(0);
-  b_commit(1);
-  __syncthreads();                            // their bf16 tiles visible
-  Frags<TI, TJ> F[2];
-  read_frags(0, 0, F[0]);
-
-  // One slab: CUR holds its first k-step's fragments on entry, and the next
-  // slab's first fragments are in CUR (two k-steps) or NXT (one k-step) on exit.
-#define QAT_SLAB(KT, CUR, NXT)                                              \
-  do {                                                                      \
-    wait_vmcnt<(STAGES - 3) * NL>(); /* my DMAs for slabs <= KT+1 landed */ \
-    __syncthreads();                 /* everyone's: slab KT+1 is visible */ \
-    issue((KT) + STAGES - 1);                                               \
-    const int st_ = ((KT) % STAGES) * STAGE;                                \
-    const int nx_ = (((KT) + 1) % STAGES) * STAGE;                          \
-    if constexpr (KS == 1) {                                                \
-      read_frags(nx_, 0, NXT);                                              \
-      mfmas(CUR);                                                           \
-    } else {                                                                \
-      read_frags(st_, 1, NXT);                                              \
-      mfmas(CUR);                                                           \
-      read_frags(nx_, 0, CUR);                                              \
-      mfmas(NXT);                                                           \
-    }                                                                       \
-    b_commit_il((KT) + 2);                                                  \
-  } while (0)
-
-  for (int kt = 0; kt < nk; kt += (KS == 1 && U2) ? 2 : 1) {
-    QAT_SLAB(kt, F[0], F[1]);
-    if constexpr (KS == 1) {
-      if constexpr (U2) {
-        if (kt + 1 < nk) QAT_SLAB(kt + 1, F[1], F[0]);
-      } else {
-        F[0] = F[1];
+      for (int t = 0; t < NM; ++t) {
+        const int j = t / TI, i = t % TI;
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
+        if (t < NR) read_r(nslot, t, nxt);
+        sched_fence();
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): the next slab's reads are in
+      __syncthreads();
+    };
+    Frags<TI, TJ> F0, F1;
+    __syncthreads();                                     // P0: the converters' first DMAs landed
+    __syncthreads();                                     // P1: slabs 0 and 1 staged
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_r(0, r, F0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __syncthreads();                                     // P2: slab 0 read; its A stage may be refilled
+    int sl = 1;                                          // stage slot of the next slab
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(F0, sl, F1);
+      sl = sl == 2 ? 0 : sl + 1;
+      if (kt + 1 < nk) {
+        step(F1, sl, F0);
+        sl = sl == 2 ? 0 : sl + 1;
       }
     }
+    gemm_epilogue<kStoreBf16, NB, 0, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, nullptr);
+  } else {
+    // ---- converter waves
+    const int cw = wave - 4, tid = threadIdx.x - 256;
+    LA la;
+    LB lb;
+    la.init(a.A, a.lda, m0, a.M, a.K, cw);
+    if constexpr (BT == 0)
+      lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.N, a.s, a.z, a.G, a.group, a.Kq, cw);
+    else
+      lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, a.Kq, cw);
+    constexpr int NL = LA::NI + LB::NI;                  // DMA instructions per converter wave and slab
+    const uint32_t lds0 = lds_addr_of(smem);
+    auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
+    auto dma_a = [&](int slab) { la.issue(lds0 + A0 + (slab % S) * A_BYTES, clamp_slab(slab) * BK); };
+    auto dma_w = [&](int slab) { lb.issue(lds0 + P0 + (slab % S) * P_BYTES, clamp_slab(slab) * BK); };
+    auto convert = [&](int slab) {
+      const int p = P0 + (slab % S) * P_BYTES, b = B0 + (slab % S) * B_BYTES;
+      if constexpr (BT == 0) lb.commit(smem, p, b, tid);
+      else lb.commit(smem, p, b, slab * BK, tid);
+    };
+    dma_w(0);
+    dma_w(1);
+    dma_a(0);
+    dma_a(1);
+    dma_w(2);
+    dma_a(2);
+    wait_vmcnt<LA::NI>();                                // all but A slab 2 landed (for this wave)
+    __syncthreads();                                     // P0: everyone's ring slabs 0, 1 and A slabs 0, 1
+    convert(0);
+    convert(1);
+    __syncthreads();                                     // P1
+    dma_w(3);                                            // ring entry 0 is free again
+    __syncthreads();                                     // P2
+    int a_slab = 3, w_slab = 4;
+    for (int kt = 0; kt < nk; ++kt) {
+      dma_a(a_slab++);
+      dma_w(w_slab++);
+      convert(kt + 2);
+      wait_vmcnt<NL>();                                  // the previous iteration's DMAs landed
+      __syncthreads();
+    }
+    wait_vmcnt<0>();                                     // drain the trailing re-loads
   }
-#undef QAT_SLAB
-  wait_vmcnt<0>();                            // drain the trailing re-issued DMAs
-  __syncthreads();
-  gemm_epilogue<kStoreBf16, NB, 0, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, nullptr);
 }
 
 }  // namespace qat
