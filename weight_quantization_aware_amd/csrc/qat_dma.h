@@ -27,6 +27,24 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t lds_addr, uint32_t vof
                : "memory", "m0");
 }
 
+// The same with a wave-uniform byte offset added in the scalar offset field
+// (no per-lane add). Only for accesses whose out-of-range lanes are already
+// out of range by their per-lane offset: whether the range check counts the
+// scalar offset is not relied on.
+__device__ __forceinline__ void dma16s(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4s(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -10,7 +10,7 @@
 // Fused B operands (k_gemm_fused: the fp32 master weight or packed codes
 // turned into bf16 W_hat in LDS by converter waves beside the MFMA waves;
 // the forwards and the dX products without a workspace): 256x128 or 128x128
-// tiles, BK = 32, three stages.
+// tiles, BK = 32, as many A stages and ring entries as the LDS holds (up to six).
 #include "qat_gemm_kernel.h"
 
 namespace qat {

@@ -171,6 +171,16 @@ struct DmaTileK {
 #pragma unroll
     for (int q = 0; q < NI; ++q) issue_q(lds_tile, k0, q);
   }
+  // The same with the slab's column offset in the scalar offset field: rows
+  // at or beyond nrows are out of range by their row offset alone.
+  __device__ __forceinline__ void issue_so(uint32_t lds_tile, int k0) const {
+    const uint32_t so = (uint32_t)k0 * 2;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      if constexpr (DWD) dma4s(rs, lds_tile + lrow[q], k0 + kc[q] < kdim ? voff[q] : 0x80000000u, so);
+      else dma16s(rs, lds_tile + lrow[q], voff[q], so);
+    }
+  }
   // Per-lane byte offset of fragment 0 (tile rows r0 .. r0 + 15) for k-step ks.
   // The swizzle term (row / RPL) & (CH - 1) repeats every 16 rows (RPL * CH
   // divides 16), so fragment f of the same k-step sits f * 16 * PITCH further.
@@ -293,15 +303,21 @@ struct DmaTileOf<ROWS, BK, kMNContigD, NW> { using T = DmaTileMN<ROWS, BK, NW, 1
 constexpr bool k_contig(int layout) { return layout == kKContig || layout == kKContigD; }
 
 // The quantiser of the fused loaders, on its fast path: u = w * rcp with rcp
-// = v_rcp_f32(s) (within an ulp of 1/s), so u lies within 2^-22 |u| of
-// fl32(w / s); q - zr = med3(rint(u), -zr, K - zr) (exactly clamp(rint(u) +
-// zr, 0, K) - zr, small integers); W_hat = fma(q - zr, s, +0), one rounding
-// of the exact product like (q - zr) * s, with +0 where that product is a
-// zero (as the subtraction q - zr gives). Where u lies within 2^-20 |u| of a
-// half-integer (or is not finite) rint(u) may differ from the correctly
-// rounded quotient's: `tie` is set and the caller redoes the element with
-// quant_elem (the exact division), so the codes are exactly the fp32
-// quantiser's. Five VALU operations and a compare per weight.
+// = v_rcp_f32(s) (within an ulp of 1/s), so |u - w/s| < 2^-22.4 |w/s| and
+// |u - fl32(w/s)| < 2^-21.7 |w/s|; q - zr = med3(rint(u), -zr, K - zr)
+// (exactly clamp(rint(u) + zr, 0, K) - zr, small integers); W_hat =
+// fma(q - zr, s, +0), one rounding of the exact product like (q - zr) * s,
+// with +0 where that product is a zero (as the subtraction q - zr gives).
+// With K <= 15 and 0 <= zr <= K the code depends on rint only where |w/s| <
+// 16.5 (beyond, both neighbouring integers clamp to the same end), and there
+// u is within 2^-17.7 of fl32(w/s): rint(u) can differ from the correctly
+// rounded quotient's only if |u - rint(u)| >= 0.5 - 2^-17 (a near-tie, also
+// set for non-finite u). The caller redoes near-ties with quant_elem (the
+// exact division), so the codes are exactly the fp32 quantiser's. Six VALU
+// operations per weight; callers gather the near-tie flags as wave masks
+// (ballot, scalar ORs) and take the rare path when any lane has one.
+constexpr float kNearTie = 0.5f - 0x1p-17f;
+
 struct QRow {
   float s, rcp, zr, lo, hi;
 };
@@ -319,9 +335,14 @@ __device__ __forceinline__ QRow qrow(float s, float z, float K) {
 __device__ __forceinline__ float qfast(float w, const QRow& r, bool& tie) {
   const float u = w * r.rcp;
   const float ru = __builtin_rintf(u);
-  const float c = __builtin_fmaf(__builtin_fabsf(u), -0x1p-20f, 0.5f);   // 0.5 - |u| 2^-20
-  tie = !(__builtin_fabsf(u - ru) < c);
+  tie = !(__builtin_fabsf(u - ru) < kNearTie);
   return __builtin_fmaf(__builtin_amdgcn_fmed3f(ru, r.lo, r.hi), r.s, 0.0f);
+}
+
+// The near-tie test of qfast alone (the rare path's per-element decision).
+__device__ __forceinline__ bool qnear_tie(float w, const QRow& r) {
+  const float u = w * r.rcp;
+  return !(__builtin_fabsf(u - __builtin_rintf(u)) < kNearTie);
 }
 
 // Two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, lo in bits 0-15.
@@ -341,37 +362,49 @@ __device__ __forceinline__ int dma_index(int cw, int q) {
 
 // Quantised-weight operand through an LDS ring, B rows = weight rows (the
 // forward, Y = X W_hat^T), slabs of BK = 32 along `in`. A ring entry holds the
-// raw weights of ROWS rows -- the fp32 master weight, 128 bytes per row by
-// 16-byte DMA, the 16-byte piece c (4 weights) of row r at slot c ^ ((r >> 1)
-// & 3) so that the converters' reads spread over every bank; or packed N-bit
-// codes, 4 N bytes per row by dword DMA -- then the rows' s and z for the
-// slab (a 32-wide slab lies inside one group). Each of the 256 converter
-// threads turns 16 weights of one row into the K-contiguous bf16 B stage:
+// raw weights of ROWS rows for one slab -- the fp32 master weight, 128 bytes
+// per row by 16-byte DMA, the 16-byte piece c (4 weights) of row r at slot c
+// ^ ((r >> 1) & 3) so that the converters' reads spread over every bank; or
+// packed N-bit codes, 4 N bytes per row by dword DMA. The rows' s and z come
+// in chunks of CG = 4 consecutive groups: s[ROWS][CG] then z[ROWS][CG], 16
+// rows x 4 groups per dword DMA instruction (16 cache lines, where one
+// group's 128 values would touch 64 lines per instruction), loaded with the
+// ring DMA of the chunk's first slab into one of three chunk entries. Each of
+// the 256 converter threads turns 16 weights of one row into the
+// K-contiguous bf16 B stage:
 //   packed (E2E-QP):  W_hat = (q - z) * s, z as stored;
 //   fp32 (Block-AP):  Eq. 1 then Eq. 2 with zr = clamp(rint(z), 0, K), by
 //                     qfast (near-ties redone by quant_elem).
+// A slab lies inside one group (groups of 32, 64, 128 or a whole row).
 template <int ROWS, int BK, int KIND, int NB>
 struct DmaRing {
   using L = LdsLayout<BK, kLdsSlots>;
   static_assert(BK == 32 && ROWS == 128, "two converter threads per 32-weight row slab");
   static constexpr int RB = KIND == kPacked ? BK * NB / 8 : BK * 4;     // ring bytes per row
   static constexpr int W_BYTES = ROWS * RB;
-  static constexpr int P_BYTES = W_BYTES + 2 * ROWS * 4;
+  static constexpr int P_BYTES = W_BYTES;                              // one ring entry
+  static constexpr int CG = 4;                                         // groups per (s, z) chunk
+  static constexpr int SZ_BYTES = 2 * ROWS * CG * 4;                   // one chunk entry
+  static constexpr int SZ_ENTRIES = 3;
   static constexpr int DMA_B = KIND == kPacked ? 256 : 1024;           // bytes per DMA instruction
-  static constexpr int NQ = W_BYTES / DMA_B, NS = 2 * ROWS / 64;       // weight / (s, z) instructions
-  static constexpr int NI_Q = (NQ + 3) / 4, NI_S = (NS + 3) / 4;
-  static constexpr int NI = NI_Q + NI_S;                               // per converter wave and slab
-  static_assert(NQ * DMA_B == W_BYTES && NS * 64 == 2 * ROWS, "ring tile shape");
+  static constexpr int NQ = W_BYTES / DMA_B, NC = SZ_BYTES / 256;      // weight / chunk instructions
+  static constexpr int NI_Q = (NQ + 3) / 4, NI_C = NC / 4;
+  // per converter wave and slab, not counting the chunk DMA of a chunk's
+  // first slab (waits on this count are conservative: they also cover it)
+  static constexpr int NI = NI_Q;
+  static_assert(NQ * DMA_B == W_BYTES && NI_C * 4 == NC, "ring tile shape");
   i32x4 rq, rsz[2];
-  uint32_t vq[NI_Q], dq[NI_Q], vs[NI_S], ds_[NI_S];
-  int which[NI_S];
+  uint32_t vq[NI_Q], dq[NI_Q], vc[NI_C], dc[NI_C];
+  int which[NI_C];
+  int group;
   float K;
   FastDiv gdiv;                                                        // k -> group index
   // cw: this converter wave's index (0..3)
   __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes, int row0, int nrows, const float* s,
-                                       const float* z, int64_t G, int group, float K_, int cw) {
+                                       const float* z, int64_t G, int group_, float K_, int cw) {
     K = K_;
-    gdiv = FastDiv::make((uint32_t)group);
+    group = group_;
+    gdiv = FastDiv::make((uint32_t)group_);
     rq = buffer_rsrc((const uint8_t*)Wsrc + (int64_t)row0 * row_bytes, (int64_t)(nrows - row0) * row_bytes);
     rsz[0] = buffer_rsrc(s + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
     rsz[1] = buffer_rsrc(z + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
@@ -390,38 +423,48 @@ struct DmaRing {
       dq[q] = (uint32_t)(idx * DMA_B);
     }
 #pragma unroll
-    for (int q = 0; q < NI_S; ++q) {
-      const int idx = dma_index<NS, NI_S>(cw, q);
-      const int f = idx * 64 + lane;                                   // dword of [2][ROWS]
-      which[q] = (idx * 64) / ROWS;                                    // 0: s, 1: z (uniform)
-      vs[q] = (uint32_t)((f % ROWS) * G * 4);
-      ds_[q] = (uint32_t)(W_BYTES + idx * 256);
+    for (int q = 0; q < NI_C; ++q) {
+      const int idx = cw * NI_C + q;                                   // 0 .. NC - 1
+      const int r = (idx % (NC / 2)) * 16 + lane / CG;                 // row of the chunk
+      which[q] = idx / (NC / 2);                                       // 0: s, 1: z (uniform)
+      // groups past a row's end read the next row's (never used) or, at the
+      // last row, zeros (buffer range)
+      vc[q] = (uint32_t)((r * G + lane % CG) * 4);
+      dc[q] = (uint32_t)(idx * 256);
     }
   }
-  // lds_p: this slab's ring entry; k0: its first weight column.
-  __device__ __forceinline__ void issue(uint32_t lds_p, int k0) const {
+  // lds_p: this slab's ring entry; lds_sz: the chunk entries; k0: its first
+  // weight column. The slab that starts a chunk of CG groups also loads it.
+  __device__ __forceinline__ void issue(uint32_t lds_p, uint32_t lds_sz, int k0) const {
+    // rows at or beyond nrows are out of range by their row offset alone
     const uint32_t cb = KIND == kPacked ? (uint32_t)(k0 * NB / 8) : (uint32_t)(k0 * 4);
-    const uint32_t gb = gdiv.div((uint32_t)k0) * 4;                    // the slab lies inside one group
 #pragma unroll
     for (int q = 0; q < NI_Q; ++q) {
-      if constexpr (KIND == kPacked) dma4(rq, lds_p + dq[q], vq[q] + cb);
-      else dma16(rq, lds_p + dq[q], vq[q] + cb);
+      if constexpr (KIND == kPacked) dma4s(rq, lds_p + dq[q], vq[q], cb);
+      else dma16s(rq, lds_p + dq[q], vq[q], cb);
     }
+    const int g = (int)gdiv.div((uint32_t)k0);
+    if (g % CG == 0 && k0 == g * group) {
+      const uint32_t e = lds_sz + (uint32_t)(((g / CG) % SZ_ENTRIES) * SZ_BYTES);
 #pragma unroll
-    for (int q = 0; q < NI_S; ++q) {
-      i32x4 r = which[q] ? rsz[1] : rsz[0];
+      for (int q = 0; q < NI_C; ++q) {
+        i32x4 r = which[q] ? rsz[1] : rsz[0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_readfirstlane(r[e]);
-      dma4(r, lds_p + ds_[q], vs[q] + gb);
+        for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_readfirstlane(r[j]);
+        dma4(r, e + dc[q], vc[q] + (uint32_t)g * 4);
+      }
     }
   }
-  // Convert the slab in the ring entry at byte p into the B stage at byte b;
-  // tid: the converter thread (0..255): row tid / 2, weights 16 (tid % 2) ..
-  // + 15 of the slab.
-  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int tid) const {
+  // Convert the slab (first weight column k0) in the ring entry at byte p
+  // into the B stage at byte b, with s and z from the chunk entries at byte
+  // sz; tid: the converter thread (0..255): row tid / 2, weights 16 (tid % 2)
+  // .. + 15 of the slab.
+  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int sz, int k0, int tid) const {
     const int row = tid >> 1, hf = tid & 1;
-    const float sv = *(const float*)&smem[p + W_BYTES + row * 4];
-    const float zv = *(const float*)&smem[p + W_BYTES + ROWS * 4 + row * 4];
+    const int g = (int)gdiv.div((uint32_t)k0);
+    const int c = sz + ((g / CG) % SZ_ENTRIES) * SZ_BYTES + row * (CG * 4) + (g % CG) * 4;
+    const float sv = *(const float*)&smem[c];
+    const float zv = *(const float*)&smem[c + ROWS * CG * 4];
     float h[16];
     if constexpr (KIND == kPacked) {
       const uint32_t* q = (const uint32_t*)&smem[p + row * RB];
@@ -434,7 +477,7 @@ struct DmaRing {
     } else {
       const QRow r = qrow(sv, zv, K);
       const int sw = (row >> 1) & 3;
-      uint32_t tie = 0;
+      uint64_t tie = 0;                                        // lanes with a near-tie (wave mask)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 w4 = *(const float4*)&smem[p + row * RB + (((4 * hf + j) ^ sw) << 4)];
@@ -443,7 +486,7 @@ struct DmaRing {
         for (int e = 0; e < 4; ++e) {
           bool t;
           h[4 * j + e] = qfast(wv[e], r, t);
-          tie |= (uint32_t)t << (4 * j + e);
+          tie |= __builtin_amdgcn_ballot_w64(t);
         }
       }
       if (tie) {                                               // near a rounding tie: exact division
@@ -451,12 +494,11 @@ struct DmaRing {
         for (int j = 0; j < 4; ++j) {
           const float* wr = (const float*)&smem[p + row * RB + (((4 * hf + j) ^ sw) << 4)];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (tie & (1u << (4 * j + e))) {
-              float wt = wr[e];
-              rare_branch(wt);
-              h[4 * j + e] = quant_elem(wt, sv, r.zr, K).w_hat;
-            }
+          for (int e = 0; e < 4; ++e) {
+            float wt = wr[e];
+            rare_branch(wt);
+            if (qnear_tie(wt, r)) h[4 * j + e] = quant_elem(wt, sv, r.zr, K).w_hat;
+          }
         }
       }
     }
@@ -492,6 +534,7 @@ struct DmaRingT {
   static constexpr int NQ = W_BYTES / DMA_B, NS = 2 * BK * SL / 64;
   static constexpr int NI_Q = (NQ + 3) / 4, NI_S = (NS + 3) / 4;
   static constexpr int NI = NI_Q + NI_S;
+  static constexpr int SZ_BYTES = 0, SZ_ENTRIES = 0;                      // (s, z) travel in the ring entry
   static_assert(NQ * DMA_B == W_BYTES && NS * 64 == 2 * BK * SL, "ring tile shape");
   static_assert(KIND == kPacked || RB % 16 == 0, "16-byte DMA pieces of fp32 rows");
   i32x4 rq, rsz[2];
@@ -570,9 +613,8 @@ struct DmaRingT {
       }
     } else {
       constexpr int QPR = ROWS / 4, QPT = BK * QPR / 256;                  // 4-weight quads
-      static_assert(QPT <= 8, "tie mask bits");
-      float h[QPT][4];
-      uint32_t tie = 0;
+          float h[QPT][4];
+      uint64_t tie = 0;                                       // lanes with a near-tie (wave mask)
 #pragma unroll
       for (int i = 0; i < QPT; ++i) {
         const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
@@ -583,7 +625,7 @@ struct DmaRingT {
         for (int e = 0; e < 4; ++e) {
           bool t;
           h[i][e] = qfast(wv[e], r, t);
-          tie |= (uint32_t)t << (i * 4 + e);
+          tie |= __builtin_amdgcn_ballot_w64(t);
         }
       }
       if (tie) {                                              // near a rounding tie: exact division
@@ -591,15 +633,13 @@ struct DmaRingT {
         for (int i = 0; i < QPT; ++i) {
           const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
           const float* wr = (const float*)&smem[p + k * RB + qc * 16];
-          const float sv = sl[k * SL + qc / 8];
-          const float zr = round_clamp_zero(zl[k * SL + qc / 8], K);
+          const QRow r = qrow(sl[k * SL + qc / 8], zl[k * SL + qc / 8], K);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (tie & (1u << (i * 4 + e))) {
-              float wt = wr[e];
-              rare_branch(wt);
-              h[i][e] = quant_elem(wt, sv, zr, K).w_hat;
-            }
+          for (int e = 0; e < 4; ++e) {
+            float wt = wr[e];
+            rare_branch(wt);
+            if (qnear_tie(wt, r)) h[i][e] = quant_elem(wt, r.s, r.zr, K).w_hat;
+          }
         }
       }
 #pragma unroll
@@ -1199,37 +1239,58 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 // The workgroup's 8 waves have two roles, one of each on every SIMD:
 // - waves 0-3 (2 x 2 over the BM x BN tile) issue only LDS fragment reads and
 //   MFMAs: the MFMAs of slab i interleaved with the reads of slab i + 1;
-// - waves 4-7 (converters) issue every DMA -- A of slab i + 3 and the raw
-//   weights (ring) of slab i + 4 -- and turn ring slab i + 2 into its bf16
-//   B stage (DmaRing / DmaRingT), VALU work that runs beside the other
+// - waves 4-7 (converters) issue every DMA -- A of slab i + D and the raw
+//   weights (ring) of slab i + D + 1 -- and turn ring slab i + 2 into its
+//   bf16 B stage (DmaRing / DmaRingT), VALU work that runs beside the other
 //   wave's MFMAs.
 // Both roles pass the same barriers: P0, P1, P2 in the prologue, then one
-// per slab. Three A stages, three B stages and three ring
-// entries: at iteration i the MFMA waves read slab i + 1 (A stage and B stage
-// (i + 1) % 3), the converters write B stage (i + 2) % 3 and DMA into A
-// stage i % 3 (slab i, read during iteration i - 1) and ring entry
-// (i + 1) % 3 (slab i + 1, converted during iteration i - 1); each DMA has
-// two slabs of time to land (converters wait for the previous iteration's
-// DMAs before the barrier). Slabs past the end re-load the last one (uniform
-// wait counts); nothing reads what they make.
+// per slab. D A stages, D ring entries and three B stages: at iteration i
+// the MFMA waves read slab i + 1 (A stage (i + 1) % D, B stage (i + 1) % 3),
+// the converters write B stage (i + 2) % 3 and DMA into A stage i % D (slab
+// i, read during iteration i - 1) and ring entry (i + 1) % D (slab i + 1,
+// converted during iteration i - 1). A DMA has D - 1 iterations to land
+// (converters wait, before each barrier, for all but the last D - 2
+// iterations' DMAs): the loads' latency under load is well above one slab's
+// MFMA time, so D is as deep as the LDS allows. Slabs past the end re-load
+// the last one (uniform wait counts); nothing reads what they make.
 // BT = 0: B rows are weight rows (Y = X W_hat^T); BT = 1: B rows are weight
 // columns (dX = dY W_hat), the B stage MN-contiguous. ADW: A by 4-byte DMA
 // with the contraction's tail masked (dY rows of out % 64 != 0 elements).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BL, int NB, int BT, int ADW>
-__global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
-  constexpr int BK = 32, S = 3;
+struct FusedShape {
+  static constexpr int BK = 32;
   using L = LdsLayout<BK, kLdsSlots>;
   using LA = DmaTileK<BM, BK, kLdsSlots, 4, ADW>;
   using LB = typename std::conditional<BT == 0, DmaRing<BN, BK, BL, NB>, DmaRingT<BN, BK, BL, NB>>::type;
+  static constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH, P_BYTES = LB::P_BYTES;
+  static constexpr int NL = LA::NI + LB::NI;            // DMA instructions per converter wave and slab
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int SZ_ALL = LB::SZ_BYTES * LB::SZ_ENTRIES;           // (s, z) chunk entries
+  static constexpr int D_FIT = (LDS_MAX - 3 * B_BYTES - SZ_ALL) / (A_BYTES + P_BYTES);
+  static constexpr int D_CNT = 2 + 63 / NL;             // (D - 2) NL in-flight DMAs fit the vmcnt field
+  static constexpr int D_MIN = D_FIT < D_CNT ? D_FIT : D_CNT;
+  static constexpr int D = D_MIN < 6 ? D_MIN : 6;       // A stages = ring entries
+  static_assert(D >= 3, "three stages at least");
+  static constexpr int LDS = D * (A_BYTES + P_BYTES) + 3 * B_BYTES + SZ_ALL;
+};
+
+template <int BM, int BN, int BL, int NB, int BT, int ADW>
+__global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
+  using Sh = FusedShape<BM, BN, BL, NB, BT, ADW>;
+  constexpr int BK = Sh::BK, D = Sh::D, SB = 3;
+  using L = typename Sh::L;
+  using LA = typename Sh::LA;
+  using LB = typename Sh::LB;
   using FB = typename std::conditional<BT == 0, DmaTileK<BN, BK, kLdsSlots>, DmaTileMN<BN, BK, 4>>::type;
   static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TI = WM / 16, TJ = WN / 16, NM = TI * TJ, NR = TI + TJ;
   static_assert(NR <= NM, "a slab's MFMAs cover the next slab's reads");
-  constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH, P_BYTES = LB::P_BYTES;
-  constexpr int A0 = 0, B0 = S * A_BYTES, P0 = B0 + S * B_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[P0 + S * P_BYTES];
+  constexpr int A_BYTES = Sh::A_BYTES, B_BYTES = Sh::B_BYTES, P_BYTES = Sh::P_BYTES;
+  constexpr int A0 = 0, B0 = D * A_BYTES, P0 = B0 + SB * B_BYTES, SZ0 = P0 + D * P_BYTES;
+  static_assert(SZ0 + Sh::SZ_ALL == Sh::LDS, "LDS map");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Sh::LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1242,9 +1303,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
   if (wave < 4) {
     // ---- MFMA waves
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    auto read_r = [&](int slot, int r, Frags<TI, TJ>& f) {
-      const uint8_t* at = &smem[A0 + slot * A_BYTES];
-      const uint8_t* bt = &smem[B0 + slot * B_BYTES];
+    auto read_r = [&](int aslot, int bslot, int r, Frags<TI, TJ>& f) {
+      const uint8_t* at = &smem[A0 + aslot * A_BYTES];
+      const uint8_t* bt = &smem[B0 + bslot * B_BYTES];
       if (r < TI) f.a[r] = LA::frag(at, wm0 + r * 16 + (lane & 15), 0, lane);
       else f.b[r - TI] = FB::frag(bt, wn0 + (r - TI) * 16 + (lane & 15), 0, lane);
     };
@@ -1253,13 +1314,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // MFMAs on `cur`, each followed by (at most) one read of slab-slot `nslot` into `nxt`
-    auto step = [&](const Frags<TI, TJ>& cur, int nslot, Frags<TI, TJ>& nxt) {
+    // MFMAs on `cur`, each followed by (at most) one read of the next slab
+    // (A stage aslot, B stage bslot) into `nxt`
+    auto step = [&](const Frags<TI, TJ>& cur, int aslot, int bslot, Frags<TI, TJ>& nxt) {
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         const int j = t / TI, i = t % TI;
         acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
-        if (t < NR) read_r(nslot, t, nxt);
+        if (t < NR) read_r(aslot, bslot, t, nxt);
         sched_fence();
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): the next slab's reads are in
@@ -1269,16 +1331,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
     __syncthreads();                                     // P0: the converters' first DMAs landed
     __syncthreads();                                     // P1: slabs 0 and 1 staged
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_r(0, r, F0);
+    for (int r = 0; r < NR; ++r) read_r(0, 0, r, F0);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __syncthreads();                                     // P2: slab 0 read; its A stage may be refilled
-    int sl = 1;                                          // stage slot of the next slab
+    int sa = 1, sb = 1;                                  // A and B stage slots of the next slab
+    auto next = [&]() {
+      sa = sa == D - 1 ? 0 : sa + 1;
+      sb = sb == SB - 1 ? 0 : sb + 1;
+    };
     for (int kt = 0; kt < nk; kt += 2) {
-      step(F0, sl, F1);
-      sl = sl == 2 ? 0 : sl + 1;
+      step(F0, sa, sb, F1);
+      next();
       if (kt + 1 < nk) {
-        step(F1, sl, F0);
-        sl = sl == 2 ? 0 : sl + 1;
+        step(F1, sa, sb, F0);
+        next();
       }
     }
     gemm_epilogue<kStoreBf16, NB, 0, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, nullptr);
@@ -1292,35 +1358,53 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
       lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.N, a.s, a.z, a.G, a.group, a.Kq, cw);
     else
       lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, a.Kq, cw);
-    constexpr int NL = LA::NI + LB::NI;                  // DMA instructions per converter wave and slab
+    constexpr int NL = Sh::NL;
     const uint32_t lds0 = lds_addr_of(smem);
     auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
-    auto dma_a = [&](int slab) { la.issue(lds0 + A0 + (slab % S) * A_BYTES, clamp_slab(slab) * BK); };
-    auto dma_w = [&](int slab) { lb.issue(lds0 + P0 + (slab % S) * P_BYTES, clamp_slab(slab) * BK); };
-    auto convert = [&](int slab) {
-      const int p = P0 + (slab % S) * P_BYTES, b = B0 + (slab % S) * B_BYTES;
-      if constexpr (BT == 0) lb.commit(smem, p, b, tid);
-      else lb.commit(smem, p, b, slab * BK, tid);
+    // Stages are given as byte offsets that advance by one entry per slab
+    // (no modulo in the loop).
+    auto dma_a = [&](int slab, int aoff) { la.issue_so(lds0 + A0 + aoff, clamp_slab(slab) * BK); };
+    auto dma_w = [&](int slab, int poff) {
+      if constexpr (BT == 0) lb.issue(lds0 + P0 + poff, lds0 + SZ0, clamp_slab(slab) * BK);
+      else lb.issue(lds0 + P0 + poff, clamp_slab(slab) * BK);
     };
-    dma_w(0);
-    dma_w(1);
-    dma_a(0);
-    dma_a(1);
-    dma_w(2);
-    dma_a(2);
-    wait_vmcnt<LA::NI>();                                // all but A slab 2 landed (for this wave)
-    __syncthreads();                                     // P0: everyone's ring slabs 0, 1 and A slabs 0, 1
-    convert(0);
-    convert(1);
+    auto convert = [&](int slab, int poff, int boff) {
+      if constexpr (BT == 0) lb.commit(smem, P0 + poff, B0 + boff, SZ0, slab * BK, tid);
+      else lb.commit(smem, P0 + poff, B0 + boff, slab * BK, tid);
+    };
+    auto advance = [](int& off, int step, int end) {
+      off += step;
+      if (off == end) off = 0;
+    };
+#pragma unroll
+    for (int sl = 0; sl < D; ++sl) {
+      dma_w(sl, sl * P_BYTES);
+      dma_a(sl, sl * A_BYTES);
+    }
+    wait_vmcnt<(D - 2) * NL>();                          // slabs 0 and 1 landed (for this wave)
+    __syncthreads();                                     // P0: everyone's
+    convert(0, 0, 0);
+    convert(1, P_BYTES, B_BYTES);
     __syncthreads();                                     // P1
-    dma_w(3);                                            // ring entry 0 is free again
+    dma_w(D, 0);                                         // ring entry 0 is free again
     __syncthreads();                                     // P2
-    int a_slab = 3, w_slab = 4;
+    // Issue order: (w0, a0) .. (w_{D-1}, a_{D-1}), w_D, then per iteration i
+    // a_{i+D}, w_{i+D+1}. Iteration i needs a_{i+2} and w_{i+3} before its
+    // barrier; at most the D - 2 later iterations' DMAs (counting w_D as the
+    // tail of iteration -1) are still in flight.
+    int a_off = 0;                                       // A stage of slab i + D
+    int w_off = P_BYTES;                                 // ring entry of slab i + D + 1
+    int c_off = 2 * P_BYTES;                             // ring entry of slab i + 2
+    int b_off = 2 * B_BYTES;                             // B stage of slab i + 2
     for (int kt = 0; kt < nk; ++kt) {
-      dma_a(a_slab++);
-      dma_w(w_slab++);
-      convert(kt + 2);
-      wait_vmcnt<NL>();                                  // the previous iteration's DMAs landed
+      dma_a(kt + D, a_off);
+      dma_w(kt + D + 1, w_off);
+      convert(kt + 2, c_off, b_off);
+      advance(a_off, A_BYTES, D * A_BYTES);
+      advance(w_off, P_BYTES, D * P_BYTES);
+      advance(c_off, P_BYTES, D * P_BYTES);
+      advance(b_off, B_BYTES, SB * B_BYTES);
+      wait_vmcnt<(D - 2) * NL>();
       __syncthreads();
     }
     wait_vmcnt<0>();                                     // drain the trailing re-loads
