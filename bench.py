@@ -60,6 +60,9 @@ def parse():
                     help="after the timed region run one 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--deploy-only", action="store_true",
                     help="only the inference linear on the deployment format (Llama-2-70B block, M = 1 and 16)")
+    ap.add_argument("--deploy-gate", action="store_true",
+                    help="only the inference linear on the Llama-2-70B gate (28672 x 8192) at M = 1, w2 and w4, "
+                         "8 calls each (the shape its counters in profiles/ cover)")
     ap.add_argument("--block-only", action="store_true",
                     help="only one Block-AP step on a Llama-2-7B block (2 x 2048 tokens, w2g64)")
     ap.add_argument("--configs-only", action="store_true",
@@ -186,8 +189,16 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     g = Gpu(torch, dev, stream, Q)
+    if args.deploy_gate:
+        print(json.dumps({"inference_linear_70b_gate_m1": deploy_gate(Q, torch, dev, args.copy_calibration)}),
+              flush=True)
+        return
     if args.deploy_only:
         print(json.dumps({"inference_linear_70b_block": deploy_measurements(Q, torch, dev, stream)}), flush=True)
+        if args.copy_calibration:        # a plain copy of known size for the HBM counters
+            a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            torch.empty_like(a).copy_(a)
+            torch.cuda.synchronize(dev)
         return
     if args.block_only:
         print(json.dumps({"block_ap_step_7b": block_step_measurements(Q, torch, dev, stream)}), flush=True)
@@ -648,6 +659,38 @@ def other_workloads(Q, torch, dev, g, synth):
     return res
 
 
+def deploy_gate(Q, torch, dev, copy_calibration):
+    """The inference linear on the Llama-2-70B gate shape (28672 x 8192) at one
+    token, w2g64 and w4g64, 8 calls each (mean GPU time per call from an event
+    pair around the 8); with copy_calibration a plain 1 GiB device copy follows
+    (the reference for FETCH_SIZE)."""
+    out, inp = 28672, 8192
+    X = torch.randn(1, inp, device=dev).half()
+    Y = torch.empty(1, out, dtype=torch.float16, device=dev)
+    res = {}
+    for bits in (2, 4):
+        Wq = torch.randint(0, 256, (out, inp * bits // 8), dtype=torch.uint8, device=dev)
+        s16 = (torch.rand(out, inp // 64, device=dev) * 0.05 + 0.002).half()
+        zq = torch.randint(0, 256, (out, Q.deploy_zq_stride(inp, bits)), dtype=torch.uint8, device=dev)
+        Q.qat_deploy_gemv(X, Wq, s16, zq, bits, Y)
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(8):
+            Q.qat_deploy_gemv(X, Wq, s16, zq, bits, Y)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        us = e0.elapsed_time(e1) / 8 * 1e3
+        nbytes = Wq.numel() + s16.numel() * 2 + zq.numel() + X.numel() * 2 + Y.numel() * 2
+        res[f"w{bits}"] = {"us": round(us, 2), "tbs": round(nbytes / us / 1e6, 2)}
+        del Wq, s16, zq
+    if copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize(dev)
+    return res
+
+
 def deploy_measurements(Q, torch, dev, stream):
     """The inference linear on the deployment format (fp16 step sizes, N-bit
     zero points) for one token (M = 1) and for 16, over the seven linears of a
@@ -764,7 +807,13 @@ def block_step_measurements(Q, torch, dev, stream, steps=10):
     e1.record(stream)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
+    # one step with timing on first, so that the event pool holds every
+    # label's events before the step that is reported (an event created in
+    # the step made its first launch read ~1 ms)
     Q.timing_enable(True)
+    step()
+    torch.cuda.synchronize(dev)
+    Q.timing_enable(True)                # clears the records, keeps the events
     step()
     torch.cuda.synchronize(dev)
     rep = Q.timing_report()

@@ -101,14 +101,20 @@ def label_of(name: str):
 
 def stats(db: str, cmd: str) -> None:
     c = sqlite3.connect(db)
-    rows = c.execute("select name, count(*), avg(end-start), min(end-start), max(end-start), sum(end-start) "
-                     "from kernels group by name order by sum(end-start) desc").fetchall()
+    durs = collections.defaultdict(list)
+    for name, d in c.execute("select name, end-start from kernels"):
+        durs[name].append(d)
     print(f"# rocprofv3 kernel trace summary\n# command: {cmd}\n#")
-    print(f"{'label':22s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s}  kernel")
-    for name, n, avg, mn, mx, tot in rows:
+    print(f"{'label':22s} {'calls':>6s} {'mean_us':>9s} {'median_us':>9s} {'min_us':>9s} {'max_us':>9s} "
+          f"{'total_us':>10s}  kernel")
+    for name, ds in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        ds = sorted(ds)
+        n, tot = len(ds), sum(ds)
+        med = ds[n // 2] if n % 2 else (ds[n // 2 - 1] + ds[n // 2]) / 2
         lab = label_of(name) or "-"
         short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))[:80]
-        print(f"{lab:22s} {n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {tot / 1e3:10.1f}  {short}")
+        print(f"{lab:22s} {n:6d} {tot / n / 1e3:9.2f} {med / 1e3:9.2f} {ds[0] / 1e3:9.2f} {ds[-1] / 1e3:9.2f} "
+              f"{tot / 1e3:10.1f}  {short}")
 
 
 def _counter(db: str, counter: str):
