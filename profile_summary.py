@@ -36,8 +36,9 @@ import sys
 # template arguments name it (AMN / BMN: 0, 2 K-contiguous; 1, 3
 # MN-contiguous; EP the epilogue; NB the bit width or a tag).
 GEMM_RE = re.compile(r"k_gemm<(?:\s*\d+\s*,){7}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
-# k_gemm_fused<BM, BN, BL, NB, BT, ADW>
+# k_gemm_fused<BM, BN, BL, NB, BT, ADW> (dX), k_gemm_fused_fwd<BM, BN, BL, NB> (forward)
 FUSED_RE = re.compile(r"k_gemm_fused<(?:\s*\d+\s*,){2}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
+FUSED_FWD_RE = re.compile(r"k_gemm_fused_fwd<(?:\s*\d+\s*,){2}\s*(\d+)\s*,\s*(\d+)\s*>")
 LABELS = [
     (r"k_attn_rowdot", "attn_rowdot"),
     (r"k_flash_fwd", "attn_fwd"),
@@ -71,6 +72,9 @@ LABELS = [
 
 
 def label_of(name: str):
+    m = FUSED_FWD_RE.search(name)
+    if m:
+        return "gemm_fwd_fused_fp32" if int(m.group(1)) == 1 else "gemm_fwd_packed"
     m = FUSED_RE.search(name)
     if m:
         bl, nb, bt, _ = (int(v) for v in m.groups())

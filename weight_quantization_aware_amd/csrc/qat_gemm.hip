@@ -7,10 +7,11 @@
 //   128x256, 3 stages   about one 128x256 tile per CU (2048-token q_proj);
 //                       8 waves
 //   128x128, 4 stages   small problems; 4 waves
-// Fused B operands (k_gemm_fused: the fp32 master weight or packed codes
-// turned into bf16 W_hat in LDS by converter waves beside the MFMA waves;
-// the forwards and the dX products without a workspace): 256x128 or 128x128
-// tiles, BK = 32, as many A stages and ring entries as the LDS holds (up to six).
+// Fused B operands (the fp32 master weight or packed codes turned into bf16
+// W_hat in LDS by converter waves beside the MFMA waves; the calls without a
+// workspace): the forward in k_gemm_fused_fwd (raw weights through converter
+// registers, up to six A stages), dX in k_gemm_fused (raw weight rows through
+// an LDS ring); 256x128 or 128x128 tiles, BK = 32.
 #include "qat_gemm_kernel.h"
 
 namespace qat {
@@ -48,7 +49,7 @@ void launch_bf16(const GemmArgs& a, hipStream_t st) {
                      dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
-template <int BM, int BN, int BL, int NB, int BT = 0, int ADW = 0>
+template <int BM, int BN, int BL, int NB, int BT, int ADW>
 void launch_fused(const GemmArgs& a, hipStream_t st) {
   LaunchTimer t(gemm_label<BL, kStoreBf16, NB, BT>(), st);
   QAT_LAUNCH((k_gemm_fused<BM, BN, BL, NB, BT, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(512), 0, st, a);
@@ -114,12 +115,19 @@ void launch_grads(const GemmArgs& a, hipStream_t st) {
   else launch_grads_al<EP, NB, kMNContigD>(a, st);
 }
 
-// Fused B operands (k_gemm_fused, 4 MFMA + 4 converter waves, BK = 32):
-// 256 x 128 tiles where the output has at least one per CU, else 128 x 128.
+template <int BM, int BN, int BL, int NB>
+void launch_fused_fwd(const GemmArgs& a, hipStream_t st) {
+  LaunchTimer t(gemm_label<BL, kStoreBf16, NB, 0>(), st);
+  QAT_LAUNCH((k_gemm_fused_fwd<BM, BN, BL, NB>), dim3((unsigned)tiles(a, BM, BN)), dim3(512), 0, st, a);
+}
+
+// The forward with a fused B operand (k_gemm_fused_fwd, 4 MFMA + 4 converter
+// waves, BK = 32): 256 x 128 tiles where the output has at least one per CU,
+// else 128 x 128.
 template <int BL, int NB>
 void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, BL, NB>(a, st);
-  else launch_fused<128, 128, BL, NB>(a, st);
+  if (tiles(a, 256, 128) >= 256) launch_fused_fwd<256, 128, BL, NB>(a, st);
+  else launch_fused_fwd<128, 128, BL, NB>(a, st);
 }
 
 // dX = dY W_hat with W_hat made in LDS from the weight's rows (the

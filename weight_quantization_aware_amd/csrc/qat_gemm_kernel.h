@@ -173,13 +173,14 @@ struct DmaTileK {
   }
   // The same with the slab's column offset in the scalar offset field: rows
   // at or beyond nrows are out of range by their row offset alone.
-  __device__ __forceinline__ void issue_so(uint32_t lds_tile, int k0) const {
+  __device__ __forceinline__ void issue_so_q(uint32_t lds_tile, int k0, int q) const {
     const uint32_t so = (uint32_t)k0 * 2;
+    if constexpr (DWD) dma4s(rs, lds_tile + lrow[q], k0 + kc[q] < kdim ? voff[q] : 0x80000000u, so);
+    else dma16s(rs, lds_tile + lrow[q], voff[q], so);
+  }
+  __device__ __forceinline__ void issue_so(uint32_t lds_tile, int k0) const {
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      if constexpr (DWD) dma4s(rs, lds_tile + lrow[q], k0 + kc[q] < kdim ? voff[q] : 0x80000000u, so);
-      else dma16s(rs, lds_tile + lrow[q], voff[q], so);
-    }
+    for (int q = 0; q < NI; ++q) issue_so_q(lds_tile, k0, q);
   }
   // Per-lane byte offset of fragment 0 (tile rows r0 .. r0 + 15) for k-step ks.
   // The swizzle term (row / RPL) & (CH - 1) repeats every 16 rows (RPL * CH
@@ -360,94 +361,102 @@ __device__ __forceinline__ int dma_index(int cw, int q) {
   return min(cw * NI + q, NTOT - 1);
 }
 
-// Quantised-weight operand through an LDS ring, B rows = weight rows (the
-// forward, Y = X W_hat^T), slabs of BK = 32 along `in`. A ring entry holds the
-// raw weights of ROWS rows for one slab -- the fp32 master weight, 128 bytes
-// per row by 16-byte DMA, the 16-byte piece c (4 weights) of row r at slot c
-// ^ ((r >> 1) & 3) so that the converters' reads spread over every bank; or
-// packed N-bit codes, 4 N bytes per row by dword DMA. The rows' s and z come
-// in chunks of CG = 4 consecutive groups: s[ROWS][CG] then z[ROWS][CG], 16
-// rows x 4 groups per dword DMA instruction (16 cache lines, where one
-// group's 128 values would touch 64 lines per instruction), loaded with the
-// ring DMA of the chunk's first slab into one of three chunk entries. Each of
-// the 256 converter threads turns 16 weights of one row into the
-// K-contiguous bf16 B stage:
-//   packed (E2E-QP):  W_hat = (q - z) * s, z as stored;
-//   fp32 (Block-AP):  Eq. 1 then Eq. 2 with zr = clamp(rint(z), 0, K), by
-//                     qfast (near-ties redone by quant_elem).
-// A slab lies inside one group (groups of 32, 64, 128 or a whole row).
-template <int ROWS, int BK, int KIND, int NB>
-struct DmaRing {
-  using L = LdsLayout<BK, kLdsSlots>;
-  static_assert(BK == 32 && ROWS == 128, "two converter threads per 32-weight row slab");
-  static constexpr int RB = KIND == kPacked ? BK * NB / 8 : BK * 4;     // ring bytes per row
-  static constexpr int W_BYTES = ROWS * RB;
-  static constexpr int P_BYTES = W_BYTES;                              // one ring entry
-  static constexpr int CG = 4;                                         // groups per (s, z) chunk
-  static constexpr int SZ_BYTES = 2 * ROWS * CG * 4;                   // one chunk entry
-  static constexpr int SZ_ENTRIES = 3;
-  static constexpr int DMA_B = KIND == kPacked ? 256 : 1024;           // bytes per DMA instruction
-  static constexpr int NQ = W_BYTES / DMA_B, NC = SZ_BYTES / 256;      // weight / chunk instructions
-  static constexpr int NI_Q = (NQ + 3) / 4, NI_C = NC / 4;
-  // per converter wave and slab, not counting the chunk DMA of a chunk's
-  // first slab (waits on this count are conservative: they also cover it)
-  static constexpr int NI = NI_Q;
-  static_assert(NQ * DMA_B == W_BYTES && NI_C * 4 == NC, "ring tile shape");
-  i32x4 rq, rsz[2];
-  uint32_t vq[NI_Q], dq[NI_Q], vc[NI_C], dc[NI_C];
-  int which[NI_C];
+// The forward's weight operand without an LDS ring: each of the 256 converter
+// threads owns 16 weights of one row (row tid / 2, weights 16 (tid % 2) .. +
+// 15 of every 32-wide slab) and loads them straight into registers -- fp32:
+// four 16-byte loads; packed codes: the row's whole 4 N-byte slab (both
+// threads of a row load it, one instruction) -- several slabs ahead of their
+// conversion. The loads are the compiler's own (it waits for them before the
+// conversion reads the registers); rows at or beyond nrows read as zero
+// through the buffer range, the slab's offset rides in the scalar offset.
+template <int KIND, int NB>
+struct WSlab {
+  static constexpr int ND = KIND == kPacked ? NB : 16;  // dwords per thread and slab
+  uint32_t d[ND];
+};
+
+template <int KIND, int NB>
+struct WRowLoader {
+  static constexpr int NL = KIND == kPacked ? 1 : 4;     // load instructions per slab
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff;
+  __device__ __forceinline__ void init(const void* W, int64_t row_bytes, int row0, int nrows, int tid) {
+    int64_t n = (int64_t)(nrows - row0) * row_bytes;
+    n = n < 0 ? 0 : (n > 0x7FFFFFF0 ? 0x7FFFFFF0 : n);
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)W + (int64_t)row0 * row_bytes), (short)0,
+                                           (int)n, 0x00020000);
+    const int row = tid >> 1, hf = tid & 1;
+    voff = (uint32_t)(row * row_bytes) + (KIND == kPacked ? 0u : (uint32_t)hf * 64u);
+  }
+  __device__ __forceinline__ void load(WSlab<KIND, NB>& w, int k0) const {
+    typedef int v4i_ __attribute__((ext_vector_type(4)));
+    typedef int v3i_ __attribute__((ext_vector_type(3)));
+    typedef int v2i_ __attribute__((ext_vector_type(2)));
+    if constexpr (KIND == kPacked) {
+      const int so = k0 * NB / 8;
+      if constexpr (NB == 2) {
+        const v2i_ v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, so, 0);
+        w.d[0] = v.x, w.d[1] = v.y;
+      } else if constexpr (NB == 3) {
+        const v3i_ v = __builtin_amdgcn_raw_buffer_load_b96(rs, (int)voff, so, 0);
+        w.d[0] = v.x, w.d[1] = v.y, w.d[2] = v.z;
+      } else {
+        const v4i_ v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, so, 0);
+        w.d[0] = v.x, w.d[1] = v.y, w.d[2] = v.z, w.d[3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4i_ v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff + 16 * j, k0 * 4, 0);
+        w.d[4 * j] = v.x, w.d[4 * j + 1] = v.y, w.d[4 * j + 2] = v.z, w.d[4 * j + 3] = v.w;
+      }
+    }
+  }
+};
+
+// The rows' s and z in chunks of CG = 4 consecutive groups: s[ROWS][CG] then
+// z[ROWS][CG], 16 rows x 4 groups per dword DMA instruction (16 cache lines,
+// where one group's ROWS values would touch ROWS / 4 per instruction), into
+// one of three chunk entries, issued with the weights of the chunk's first
+// slab. A slab lies inside one group (groups of 32, 64, 128 or a whole row).
+template <int ROWS>
+struct SzChunks {
+  static constexpr int CG = 4;
+  static constexpr int SZ_BYTES = 2 * ROWS * CG * 4, ENTRIES = 3;
+  static constexpr int NC = SZ_BYTES / 256, NI = NC / 4;   // instructions per chunk, per converter wave
+  static_assert(NI * 4 == NC, "chunk shape");
+  i32x4 rsz[2];
+  uint32_t vc[NI], dc[NI];
+  int which[NI];
   int group;
   float K;
-  FastDiv gdiv;                                                        // k -> group index
-  // cw: this converter wave's index (0..3)
-  __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes, int row0, int nrows, const float* s,
-                                       const float* z, int64_t G, int group_, float K_, int cw) {
-    K = K_;
+  FastDiv gdiv;
+  __device__ __forceinline__ void init(const float* s, const float* z, int row0, int nrows, int64_t G, int group_,
+                                       float K_, int cw) {
     group = group_;
+    K = K_;
     gdiv = FastDiv::make((uint32_t)group_);
-    rq = buffer_rsrc((const uint8_t*)Wsrc + (int64_t)row0 * row_bytes, (int64_t)(nrows - row0) * row_bytes);
     rsz[0] = buffer_rsrc(s + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
     rsz[1] = buffer_rsrc(z + (int64_t)row0 * G, (int64_t)(nrows - row0) * G * 4);
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int q = 0; q < NI_Q; ++q) {
-      const int idx = dma_index<NQ, NI_Q>(cw, q);
-      const int b = idx * DMA_B + lane * (DMA_B / 64);                 // ring byte of this lane
-      const int r = b / RB;
-      if constexpr (KIND == kPacked) {
-        vq[q] = (uint32_t)(r * row_bytes + b % RB);
-      } else {
-        const int chunk = ((b % RB) >> 4) ^ ((r >> 1) & 3);
-        vq[q] = (uint32_t)(r * row_bytes + chunk * 16);
-      }
-      dq[q] = (uint32_t)(idx * DMA_B);
-    }
-#pragma unroll
-    for (int q = 0; q < NI_C; ++q) {
-      const int idx = cw * NI_C + q;                                   // 0 .. NC - 1
-      const int r = (idx % (NC / 2)) * 16 + lane / CG;                 // row of the chunk
-      which[q] = idx / (NC / 2);                                       // 0: s, 1: z (uniform)
+    for (int q = 0; q < NI; ++q) {
+      const int idx = cw * NI + q;                                       // 0 .. NC - 1
+      const int r = (idx % (NC / 2)) * 16 + lane / CG;                   // row of the chunk
+      which[q] = idx / (NC / 2);                                         // 0: s, 1: z (uniform)
       // groups past a row's end read the next row's (never used) or, at the
-      // last row, zeros (buffer range)
+      // last row, zeros (buffer range); the group offset stays per lane
       vc[q] = (uint32_t)((r * G + lane % CG) * 4);
       dc[q] = (uint32_t)(idx * 256);
     }
   }
-  // lds_p: this slab's ring entry; lds_sz: the chunk entries; k0: its first
-  // weight column. The slab that starts a chunk of CG groups also loads it.
-  __device__ __forceinline__ void issue(uint32_t lds_p, uint32_t lds_sz, int k0) const {
-    // rows at or beyond nrows are out of range by their row offset alone
-    const uint32_t cb = KIND == kPacked ? (uint32_t)(k0 * NB / 8) : (uint32_t)(k0 * 4);
-#pragma unroll
-    for (int q = 0; q < NI_Q; ++q) {
-      if constexpr (KIND == kPacked) dma4s(rq, lds_p + dq[q], vq[q], cb);
-      else dma16s(rq, lds_p + dq[q], vq[q], cb);
-    }
+  // The chunk DMA if the slab at k0 starts a chunk.
+  __device__ __forceinline__ void issue(uint32_t lds_sz, int k0) const {
     const int g = (int)gdiv.div((uint32_t)k0);
     if (g % CG == 0 && k0 == g * group) {
-      const uint32_t e = lds_sz + (uint32_t)(((g / CG) % SZ_ENTRIES) * SZ_BYTES);
+      const uint32_t e = lds_sz + (uint32_t)(((g / CG) % ENTRIES) * SZ_BYTES);
 #pragma unroll
-      for (int q = 0; q < NI_C; ++q) {
+      for (int q = 0; q < NI; ++q) {
         i32x4 r = which[q] ? rsz[1] : rsz[0];
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_readfirstlane(r[j]);
@@ -455,60 +464,68 @@ struct DmaRing {
       }
     }
   }
-  // Convert the slab (first weight column k0) in the ring entry at byte p
-  // into the B stage at byte b, with s and z from the chunk entries at byte
-  // sz; tid: the converter thread (0..255): row tid / 2, weights 16 (tid % 2)
-  // .. + 15 of the slab.
-  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int sz, int k0, int tid) const {
-    const int row = tid >> 1, hf = tid & 1;
+  // Byte offset in LDS of row's s for the slab at k0 (z sits ROWS CG 4 further).
+  __device__ __forceinline__ int at(int sz, int row, int k0) const {
     const int g = (int)gdiv.div((uint32_t)k0);
-    const int c = sz + ((g / CG) % SZ_ENTRIES) * SZ_BYTES + row * (CG * 4) + (g % CG) * 4;
-    const float sv = *(const float*)&smem[c];
-    const float zv = *(const float*)&smem[c + ROWS * CG * 4];
-    float h[16];
-    if constexpr (KIND == kPacked) {
-      const uint32_t* q = (const uint32_t*)&smem[p + row * RB];
-      const int bit = hf * 16 * NB;
-      uint64_t w = q[bit >> 5];
-      if (NB != 2) w |= (uint64_t)q[(bit >> 5) + 1] << 32;
-      w >>= (bit & 31);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) h[e] = ((float)(uint32_t)((w >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv;
-    } else {
-      const QRow r = qrow(sv, zv, K);
-      const int sw = (row >> 1) & 3;
-      uint64_t tie = 0;                                        // lanes with a near-tie (wave mask)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 w4 = *(const float4*)&smem[p + row * RB + (((4 * hf + j) ^ sw) << 4)];
-        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bool t;
-          h[4 * j + e] = qfast(wv[e], r, t);
-          tie |= __builtin_amdgcn_ballot_w64(t);
-        }
-      }
-      if (tie) {                                               // near a rounding tie: exact division
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float* wr = (const float*)&smem[p + row * RB + (((4 * hf + j) ^ sw) << 4)];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float wt = wr[e];
-            rare_branch(wt);
-            if (qnear_tie(wt, r)) h[4 * j + e] = quant_elem(wt, sv, r.zr, K).w_hat;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-      *(uint4*)&smem[b + L::off(row, 2 * hf + m)] =
-          make_uint4(pack2_bf16(h[8 * m], h[8 * m + 1]), pack2_bf16(h[8 * m + 2], h[8 * m + 3]),
-                     pack2_bf16(h[8 * m + 4], h[8 * m + 5]), pack2_bf16(h[8 * m + 6], h[8 * m + 7]));
+    return sz + ((g / CG) % ENTRIES) * SZ_BYTES + row * (CG * 4) + (g % CG) * 4;
   }
 };
+
+// One converter thread's 16 weights of the slab (registers w) into the
+// K-contiguous bf16 B stage at byte b (row tid / 2, chunks 2 (tid % 2) and
+// + 1): packed, W_hat = (q - z) s with z as stored; fp32, Eq. 1 then Eq. 2 by
+// qfast, near-ties redone by quant_elem.
+template <int KIND, int NB>
+__device__ __forceinline__ void convert_slab(const WSlab<KIND, NB>& w, float sv, float zv, float K, uint8_t* smem,
+                                             int b, int tid) {
+  using L = LdsLayout<32, kLdsSlots>;
+  const int row = tid >> 1, hf = tid & 1;
+  float h[16];
+  if constexpr (KIND == kPacked) {
+    // this thread's 16 codes start at bit 16 N hf of the row's slab; selects
+    // (not an index) pick the dwords, so the slab stays in registers
+    // (the empty asm keeps the dwords values, so that the selects are not
+    // turned back into an indexed load, which would move the slabs to LDS)
+    uint32_t d[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      d[i] = w.d[i];
+      asm volatile("" : "+v"(d[i]));
+    }
+    uint64_t x;
+    if constexpr (NB == 2) {
+      x = hf ? d[1] : d[0];
+    } else if constexpr (NB == 3) {
+      x = ((uint64_t)(hf ? d[2] : d[1]) << 32 | (hf ? d[1] : d[0])) >> (hf ? 16 : 0);
+    } else {
+      x = (uint64_t)(hf ? d[3] : d[1]) << 32 | (hf ? d[2] : d[0]);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) h[e] = ((float)(uint32_t)((x >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv;
+  } else {
+    const QRow r = qrow(sv, zv, K);
+    uint64_t tie = 0;                                          // lanes with a near-tie (wave mask)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      bool t;
+      h[e] = qfast(__builtin_bit_cast(float, w.d[e]), r, t);
+      tie |= __builtin_amdgcn_ballot_w64(t);
+    }
+    if (tie) {                                                 // near a rounding tie: exact division
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float wt = __builtin_bit_cast(float, w.d[e]);
+        rare_branch(wt);
+        if (qnear_tie(wt, r)) h[e] = quant_elem(wt, sv, r.zr, K).w_hat;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    *(uint4*)&smem[b + L::off(row, 2 * hf + m)] =
+        make_uint4(pack2_bf16(h[8 * m], h[8 * m + 1]), pack2_bf16(h[8 * m + 2], h[8 * m + 3]),
+                   pack2_bf16(h[8 * m + 4], h[8 * m + 5]), pack2_bf16(h[8 * m + 6], h[8 * m + 7]));
+}
 
 // The weight as the B operand of dX = dY W_hat (contraction over the weight's
 // rows): B[n][k] = W_hat[k][n], so a slab is BK weight rows k0 .. k0 + BK - 1
@@ -519,7 +536,7 @@ struct DmaRing {
 // slot t holding the group of weight n0 + 32 t (groups of 32 or more never
 // split a slot). Each converter thread turns its share -- fp32: 4 quads of
 // 4 consecutive weights; packed: 2 pieces of 8 -- with the quantiser of
-// DmaRing into the bf16 B stage in the MN-contiguous layout of DmaTileMN
+// the fused forward (qfast) into the bf16 B stage in the MN-contiguous layout of DmaTileMN
 // ([BK][ROWS], read back with transpose loads). Weight rows at or beyond the
 // contraction's end (kdim) read as zero and convert to exactly 0.
 template <int ROWS, int BK, int KIND, int NB>
@@ -534,7 +551,6 @@ struct DmaRingT {
   static constexpr int NQ = W_BYTES / DMA_B, NS = 2 * BK * SL / 64;
   static constexpr int NI_Q = (NQ + 3) / 4, NI_S = (NS + 3) / 4;
   static constexpr int NI = NI_Q + NI_S;
-  static constexpr int SZ_BYTES = 0, SZ_ENTRIES = 0;                      // (s, z) travel in the ring entry
   static_assert(NQ * DMA_B == W_BYTES && NS * 64 == 2 * BK * SL, "ring tile shape");
   static_assert(KIND == kPacked || RB % 16 == 0, "16-byte DMA pieces of fp32 rows");
   i32x4 rq, rsz[2];
@@ -1233,16 +1249,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMM with a fused B operand: W_hat is made in LDS from the fp32 master
-// weight (Eq. 1-2) or from packed codes, never stored. A is bf16 and
-// K-contiguous; bf16 output. Slabs of BK = 32.
+// dX = dY W_hat with a fused B operand: W_hat is made in LDS from the weight's
+// rows (fp32 master weight, Eq. 1-2, or packed codes), never stored. A (dY)
+// is bf16 and K-contiguous; bf16 output. Slabs of BK = 32.
 // The workgroup's 8 waves have two roles, one of each on every SIMD:
 // - waves 0-3 (2 x 2 over the BM x BN tile) issue only LDS fragment reads and
 //   MFMAs: the MFMAs of slab i interleaved with the reads of slab i + 1;
 // - waves 4-7 (converters) issue every DMA -- A of slab i + D and the raw
-//   weights (ring) of slab i + D + 1 -- and turn ring slab i + 2 into its
-//   bf16 B stage (DmaRing / DmaRingT), VALU work that runs beside the other
-//   wave's MFMAs.
+//   weight rows (ring, DmaRingT) of slab i + D + 1 -- and turn ring slab
+//   i + 2 into its MN-contiguous bf16 B stage, VALU work that runs beside the
+//   other wave's MFMAs.
 // Both roles pass the same barriers: P0, P1, P2 in the prologue, then one
 // per slab. D A stages, D ring entries and three B stages: at iteration i
 // the MFMA waves read slab i + 1 (A stage (i + 1) % D, B stage (i + 1) % 3),
@@ -1250,29 +1266,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 // i, read during iteration i - 1) and ring entry (i + 1) % D (slab i + 1,
 // converted during iteration i - 1). A DMA has D - 1 iterations to land
 // (converters wait, before each barrier, for all but the last D - 2
-// iterations' DMAs): the loads' latency under load is well above one slab's
-// MFMA time, so D is as deep as the LDS allows. Slabs past the end re-load
-// the last one (uniform wait counts); nothing reads what they make.
-// BT = 0: B rows are weight rows (Y = X W_hat^T); BT = 1: B rows are weight
-// columns (dX = dY W_hat), the B stage MN-contiguous. ADW: A by 4-byte DMA
-// with the contraction's tail masked (dY rows of out % 64 != 0 elements).
+// iterations' DMAs); D is as deep as the LDS allows. Slabs past the end
+// re-load the last one (uniform wait counts); nothing reads what they make.
+// BT = 1 always (B rows are weight columns); ADW: A by 4-byte DMA with the
+// contraction's tail masked (dY rows of out % 64 != 0 elements). The forward
+// has its own kernel (k_gemm_fused_fwd below).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BL, int NB, int BT, int ADW>
 struct FusedShape {
   static constexpr int BK = 32;
   using L = LdsLayout<BK, kLdsSlots>;
   using LA = DmaTileK<BM, BK, kLdsSlots, 4, ADW>;
-  using LB = typename std::conditional<BT == 0, DmaRing<BN, BK, BL, NB>, DmaRingT<BN, BK, BL, NB>>::type;
+  static_assert(BT == 1, "the dX product; the forward is k_gemm_fused_fwd");
+  using LB = DmaRingT<BN, BK, BL, NB>;
   static constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH, P_BYTES = LB::P_BYTES;
   static constexpr int NL = LA::NI + LB::NI;            // DMA instructions per converter wave and slab
   static constexpr int LDS_MAX = 160 * 1024;
-  static constexpr int SZ_ALL = LB::SZ_BYTES * LB::SZ_ENTRIES;           // (s, z) chunk entries
-  static constexpr int D_FIT = (LDS_MAX - 3 * B_BYTES - SZ_ALL) / (A_BYTES + P_BYTES);
+  static constexpr int D_FIT = (LDS_MAX - 3 * B_BYTES) / (A_BYTES + P_BYTES);
   static constexpr int D_CNT = 2 + 63 / NL;             // (D - 2) NL in-flight DMAs fit the vmcnt field
   static constexpr int D_MIN = D_FIT < D_CNT ? D_FIT : D_CNT;
   static constexpr int D = D_MIN < 6 ? D_MIN : 6;       // A stages = ring entries
   static_assert(D >= 3, "three stages at least");
-  static constexpr int LDS = D * (A_BYTES + P_BYTES) + 3 * B_BYTES + SZ_ALL;
+  static constexpr int LDS = D * (A_BYTES + P_BYTES) + 3 * B_BYTES;
 };
 
 template <int BM, int BN, int BL, int NB, int BT, int ADW>
@@ -1282,14 +1297,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
   using L = typename Sh::L;
   using LA = typename Sh::LA;
   using LB = typename Sh::LB;
-  using FB = typename std::conditional<BT == 0, DmaTileK<BN, BK, kLdsSlots>, DmaTileMN<BN, BK, 4>>::type;
+  using FB = DmaTileMN<BN, BK, 4>;
   static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TI = WM / 16, TJ = WN / 16, NM = TI * TJ, NR = TI + TJ;
   static_assert(NR <= NM, "a slab's MFMAs cover the next slab's reads");
   constexpr int A_BYTES = Sh::A_BYTES, B_BYTES = Sh::B_BYTES, P_BYTES = Sh::P_BYTES;
-  constexpr int A0 = 0, B0 = D * A_BYTES, P0 = B0 + SB * B_BYTES, SZ0 = P0 + D * P_BYTES;
-  static_assert(SZ0 + Sh::SZ_ALL == Sh::LDS, "LDS map");
+  constexpr int A0 = 0, B0 = D * A_BYTES, P0 = B0 + SB * B_BYTES;
+  static_assert(P0 + D * P_BYTES == Sh::LDS, "LDS map");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Sh::LDS];
 
   const int lane = threadIdx.x & 63;
@@ -1354,24 +1369,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
     LA la;
     LB lb;
     la.init(a.A, a.lda, m0, a.M, a.K, cw);
-    if constexpr (BT == 0)
-      lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.N, a.s, a.z, a.G, a.group, a.Kq, cw);
-    else
-      lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, a.Kq, cw);
+    lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, a.Kq, cw);
     constexpr int NL = Sh::NL;
     const uint32_t lds0 = lds_addr_of(smem);
     auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
     // Stages are given as byte offsets that advance by one entry per slab
     // (no modulo in the loop).
     auto dma_a = [&](int slab, int aoff) { la.issue_so(lds0 + A0 + aoff, clamp_slab(slab) * BK); };
-    auto dma_w = [&](int slab, int poff) {
-      if constexpr (BT == 0) lb.issue(lds0 + P0 + poff, lds0 + SZ0, clamp_slab(slab) * BK);
-      else lb.issue(lds0 + P0 + poff, clamp_slab(slab) * BK);
-    };
-    auto convert = [&](int slab, int poff, int boff) {
-      if constexpr (BT == 0) lb.commit(smem, P0 + poff, B0 + boff, SZ0, slab * BK, tid);
-      else lb.commit(smem, P0 + poff, B0 + boff, slab * BK, tid);
-    };
+    auto dma_w = [&](int slab, int poff) { lb.issue(lds0 + P0 + poff, clamp_slab(slab) * BK); };
+    auto convert = [&](int slab, int poff, int boff) { lb.commit(smem, P0 + poff, B0 + boff, slab * BK, tid); };
     auto advance = [](int& off, int step, int end) {
       off += step;
       if (off == end) off = 0;
@@ -1406,6 +1412,182 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
       advance(b_off, B_BYTES, SB * B_BYTES);
       wait_vmcnt<(D - 2) * NL>();
       __syncthreads();
+    }
+    wait_vmcnt<0>();                                     // drain the trailing re-loads
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The forward with a fused B operand (Y = X W_hat^T, no workspace): W_hat is
+// made in LDS from the fp32 master weight (Eq. 1-2) or from packed codes,
+// never stored. Slabs of BK = 32; 8 waves, one of each role per SIMD:
+// - waves 0-3 (2 x 2 over the BM x BN tile) load A themselves (D stages by
+//   DMA, slab i + D issued during slab i's MFMAs) and run the MFMAs of slab i
+//   interleaved with the fragment reads of slab i + 1;
+// - waves 4-7 (converters) keep their 16 weights of every slab in a queue of
+//   U = 4 register slabs (WRowLoader), load slab i + 2 + U while slab i + 2 is
+//   converted into B stage (i + 2) % 3, and DMA the rows' s and z in chunks
+//   of four groups (SzChunks).
+// One barrier per slab. The raw weights never pass through LDS (the LDS moves
+// A's DMA and fragment reads, the bf16 B stage and its reads only), and A has
+// up to six stages.
+// Waits: the MFMA waves allow the last D - 2 slabs' A DMAs in flight at each
+// barrier; the converters' register loads are waited for by the compiler
+// before their conversion, and at each barrier a converter allows the last
+// U slabs' loads in flight, which covers the chunk DMA issued before them.
+// Slabs past the end re-load the last one; nothing reads what they make.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BL, int NB>
+struct FusedFwdShape {
+  static constexpr int BK = 32, U = 4;
+  using L = LdsLayout<BK, kLdsSlots>;
+  using LA = DmaTileK<BM, BK, kLdsSlots, 4, 0>;
+  using SZ = SzChunks<BN>;
+  static constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH;
+  static constexpr int SZ_ALL = SZ::SZ_BYTES * SZ::ENTRIES;
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int D_FIT = (LDS_MAX - 3 * B_BYTES - SZ_ALL) / A_BYTES;
+  static constexpr int D_CNT = 2 + 63 / LA::NI;
+  static constexpr int D_MIN = D_FIT < D_CNT ? D_FIT : D_CNT;
+  static constexpr int D = D_MIN < 6 ? D_MIN : 6;
+  static_assert(D >= 3, "three A stages at least");
+  static constexpr int LDS = D * A_BYTES + 3 * B_BYTES + SZ_ALL;
+};
+
+template <int BM, int BN, int BL, int NB>
+__global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
+  using Sh = FusedFwdShape<BM, BN, BL, NB>;
+  constexpr int BK = Sh::BK, D = Sh::D, SB = 3, U = Sh::U;
+  using LA = typename Sh::LA;
+  using FB = DmaTileK<BN, BK, kLdsSlots>;
+  static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
+  static_assert(BN == 128, "two converter threads per weight row");
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TI = WM / 16, TJ = WN / 16, NM = TI * TJ, NR = TI + TJ;
+  static_assert(NR <= NM, "a slab's MFMAs cover the next slab's reads");
+  constexpr int A_BYTES = Sh::A_BYTES, B_BYTES = Sh::B_BYTES;
+  constexpr int A0 = 0, B0 = D * A_BYTES, SZ0 = B0 + SB * B_BYTES;
+  static_assert(SZ0 + Sh::SZ_ALL == Sh::LDS, "LDS map");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Sh::LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = (a.K + BK - 1) / BK;
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
+
+  if (wave < 4) {
+    // ---- MFMA waves: A by DMA, fragment reads, MFMAs
+    LA la;
+    la.init(a.A, a.lda, m0, a.M, a.K, wave);
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    auto read_r = [&](int aoff, int boff, int r, Frags<TI, TJ>& f) {
+      const uint8_t* at = &smem[A0 + aoff];
+      const uint8_t* bt = &smem[B0 + boff];
+      if (r < TI) f.a[r] = LA::frag(at, wm0 + r * 16 + (lane & 15), 0, lane);
+      else f.b[r - TI] = FB::frag(bt, wn0 + (r - TI) * 16 + (lane & 15), 0, lane);
+    };
+    f32x4 acc[TJ][TI];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int GAP = NM / LA::NI;                     // MFMAs per A DMA instruction
+    static_assert(GAP >= 1 && GAP * LA::NI <= NM, "one slab's MFMAs cover its DMA");
+    // MFMAs on `cur`, each followed by (at most) one read of the next slab
+    // (A at aoff, B at boff) into `nxt`, and A's DMA of slab dslab into the
+    // stage at doff spread over them
+    auto step = [&](const Frags<TI, TJ>& cur, int aoff, int boff, Frags<TI, TJ>& nxt, int dslab, int doff) {
+#pragma unroll
+      for (int t = 0; t < NM; ++t) {
+        const int j = t / TI, i = t % TI;
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
+        if (t < NR) read_r(aoff, boff, t, nxt);
+        if (t % GAP == GAP - 1 && t / GAP < LA::NI) la.issue_so_q(lds0 + A0 + doff, clamp_slab(dslab) * BK, t / GAP);
+        sched_fence();
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): the next slab's reads are in
+      wait_vmcnt<(D - 2) * LA::NI>();                    // A of the slab after next landed (own DMAs)
+      __syncthreads();
+    };
+#pragma unroll
+    for (int sl = 0; sl < D; ++sl) la.issue_so(lds0 + A0 + sl * A_BYTES, clamp_slab(sl) * BK);
+    wait_vmcnt<(D - 2) * LA::NI>();                      // A slabs 0 and 1 landed (own)
+    Frags<TI, TJ> F0, F1;
+    __syncthreads();                                     // P0: everyone's A 0, 1 and (s, z) chunk 0
+    __syncthreads();                                     // P1: B stages 0 and 1 converted
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_r(0, 0, r, F0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __syncthreads();                                     // P2: slab 0 read; its A stage may be refilled
+    int aoff = A_BYTES, boff = B_BYTES, doff = 0;        // slab i + 1's stages; A stage of slab i + D
+    auto next = [&]() {
+      aoff = aoff + A_BYTES == D * A_BYTES ? 0 : aoff + A_BYTES;
+      boff = boff + B_BYTES == SB * B_BYTES ? 0 : boff + B_BYTES;
+      doff = doff + A_BYTES == D * A_BYTES ? 0 : doff + A_BYTES;
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(F0, aoff, boff, F1, kt + D, doff);
+      next();
+      if (kt + 1 < nk) {
+        step(F1, aoff, boff, F0, kt + 1 + D, doff);
+        next();
+      }
+    }
+    wait_vmcnt<0>();                                     // drain the trailing re-loads
+    gemm_epilogue<kStoreBf16, NB, 0, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, nullptr);
+  } else {
+    // ---- converter waves: raw weights to registers, (s, z) chunks, B stages
+    const int cw = wave - 4, tid = threadIdx.x - 256;
+    const int row = tid >> 1;
+    WRowLoader<BL, NB> wl;
+    wl.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.N, tid);
+    typename Sh::SZ sz;
+    sz.init(a.s, a.z, n0, a.N, a.G, a.group, a.Kq, cw);
+    constexpr int NLW = WRowLoader<BL, NB>::NL;
+    const uint32_t lds_sz = lds0 + SZ0;
+    auto fetch = [&](WSlab<BL, NB>& w, int slab) {      // (s, z) chunk first, then the weights
+      const int k0 = clamp_slab(slab) * BK;
+      sz.issue(lds_sz, k0);
+      wl.load(w, k0);
+    };
+    auto convert = [&](const WSlab<BL, NB>& w, int slab, int boff) {
+      const int c = sz.at(SZ0, row, slab * BK);
+      const float sv = *(const float*)&smem[c];
+      const float zv = *(const float*)&smem[c + BN * Sh::SZ::CG * 4];
+      convert_slab<BL, NB>(w, sv, zv, sz.K, smem, B0 + boff, tid);
+    };
+    WSlab<BL, NB> R0, R1, R2, R3;                        // slab j in R[j % 4]
+    static_assert(U == 4, "four named register slabs");
+    fetch(R0, 0);
+    fetch(R1, 1);
+    fetch(R2, 2);
+    fetch(R3, 3);
+    wait_vmcnt<U * NLW>();                               // chunk 0 landed (for this wave)
+    __syncthreads();                                     // P0
+    convert(R0, 0, 0);
+    fetch(R0, U);
+    convert(R1, 1, B_BYTES);
+    fetch(R1, U + 1);
+    __syncthreads();                                     // P1
+    __syncthreads();                                     // P2
+    int boff = 2 * B_BYTES;                              // B stage of slab i + 2
+    auto iter = [&](WSlab<BL, NB>& R, int kt) {
+      convert(R, kt + 2, boff);
+      fetch(R, kt + 2 + U);
+      boff = boff + B_BYTES == SB * B_BYTES ? 0 : boff + B_BYTES;
+      wait_vmcnt<U * NLW>();                             // the chunk of slab i + 3 (issued before its weights)
+      __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 4) {
+      iter(R2, kt);
+      if (kt + 1 < nk) iter(R3, kt + 1);
+      if (kt + 2 < nk) iter(R0, kt + 2);
+      if (kt + 3 < nk) iter(R1, kt + 3);
     }
     wait_vmcnt<0>();                                     // drain the trailing re-loads
   }
