@@ -123,7 +123,9 @@ void launch_fused_fwd(const GemmArgs& a, hipStream_t st) {
 
 // The forward with a fused B operand (k_gemm_fused_fwd, 4 MFMA + 4 converter
 // waves, BK = 32): 256 x 128 tiles where the output has at least one per CU,
-// else 128 x 128.
+// else 128 x 128. (512 x 64 tiles, which halve the conversions per MFMA,
+// measured no faster for fp32 weights and 18% slower for packed codes at
+// 2048 x 4096 x 4096: the larger A tile costs more LDS traffic.)
 template <int BL, int NB>
 void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
   if (tiles(a, 256, 128) >= 256) launch_fused_fwd<256, 128, BL, NB>(a, st);

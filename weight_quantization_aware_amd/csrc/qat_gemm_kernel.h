@@ -362,22 +362,24 @@ __device__ __forceinline__ int dma_index(int cw, int q) {
 }
 
 // The forward's weight operand without an LDS ring: each of the 256 converter
-// threads owns 16 weights of one row (row tid / 2, weights 16 (tid % 2) .. +
-// 15 of every 32-wide slab) and loads them straight into registers -- fp32:
-// four 16-byte loads; packed codes: the row's whole 4 N-byte slab (both
-// threads of a row load it, one instruction) -- several slabs ahead of their
+// threads owns WPT weights of one row (a BN-row tile: TPR = 256 / BN threads
+// per row, WPT = 32 / TPR: row tid / TPR, weights WPT (tid % TPR) .. of every
+// 32-wide slab) and loads them straight into registers -- fp32: WPT / 4
+// 16-byte loads; packed codes: the row's whole 4 N-byte slab (the TPR threads
+// of a row load it, one instruction) -- several slabs ahead of their
 // conversion. The loads are the compiler's own (it waits for them before the
 // conversion reads the registers); rows at or beyond nrows read as zero
 // through the buffer range, the slab's offset rides in the scalar offset.
-template <int KIND, int NB>
+template <int KIND, int NB, int WPT>
 struct WSlab {
-  static constexpr int ND = KIND == kPacked ? NB : 16;  // dwords per thread and slab
+  static constexpr int ND = KIND == kPacked ? NB : WPT;  // dwords per thread and slab
   uint32_t d[ND];
 };
 
-template <int KIND, int NB>
+template <int KIND, int NB, int WPT>
 struct WRowLoader {
-  static constexpr int NL = KIND == kPacked ? 1 : 4;     // load instructions per slab
+  static constexpr int TPR = 32 / WPT;                    // threads per weight row
+  static constexpr int NL = KIND == kPacked ? 1 : WPT / 4; // load instructions per slab
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff;
   __device__ __forceinline__ void init(const void* W, int64_t row_bytes, int row0, int nrows, int tid) {
@@ -385,10 +387,10 @@ struct WRowLoader {
     n = n < 0 ? 0 : (n > 0x7FFFFFF0 ? 0x7FFFFFF0 : n);
     rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)W + (int64_t)row0 * row_bytes), (short)0,
                                            (int)n, 0x00020000);
-    const int row = tid >> 1, hf = tid & 1;
-    voff = (uint32_t)(row * row_bytes) + (KIND == kPacked ? 0u : (uint32_t)hf * 64u);
+    const int row = tid / TPR, q = tid % TPR;
+    voff = (uint32_t)(row * row_bytes) + (KIND == kPacked ? 0u : (uint32_t)(q * WPT * 4));
   }
-  __device__ __forceinline__ void load(WSlab<KIND, NB>& w, int k0) const {
+  __device__ __forceinline__ void load(WSlab<KIND, NB, WPT>& w, int k0) const {
     typedef int v4i_ __attribute__((ext_vector_type(4)));
     typedef int v3i_ __attribute__((ext_vector_type(3)));
     typedef int v2i_ __attribute__((ext_vector_type(2)));
@@ -406,7 +408,7 @@ struct WRowLoader {
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WPT / 4; ++j) {
         const v4i_ v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff + 16 * j, k0 * 4, 0);
         w.d[4 * j] = v.x, w.d[4 * j + 1] = v.y, w.d[4 * j + 2] = v.z, w.d[4 * j + 3] = v.w;
       }
@@ -471,49 +473,51 @@ struct SzChunks {
   }
 };
 
-// One converter thread's 16 weights of the slab (registers w) into the
-// K-contiguous bf16 B stage at byte b (row tid / 2, chunks 2 (tid % 2) and
-// + 1): packed, W_hat = (q - z) s with z as stored; fp32, Eq. 1 then Eq. 2 by
-// qfast, near-ties redone by quant_elem.
-template <int KIND, int NB>
-__device__ __forceinline__ void convert_slab(const WSlab<KIND, NB>& w, float sv, float zv, float K, uint8_t* smem,
-                                             int b, int tid) {
+// One converter thread's WPT weights of the slab (registers w) into the
+// K-contiguous bf16 B stage at byte b (row tid / TPR, 8-weight chunks
+// (WPT / 8) (tid % TPR) ..): packed, W_hat = (q - z) s with z as stored;
+// fp32, Eq. 1 then Eq. 2 by qfast, near-ties redone by quant_elem.
+template <int KIND, int NB, int WPT>
+__device__ __forceinline__ void convert_slab(const WSlab<KIND, NB, WPT>& w, float sv, float zv, float K,
+                                             uint8_t* smem, int b, int tid) {
   using L = LdsLayout<32, kLdsSlots>;
-  const int row = tid >> 1, hf = tid & 1;
-  float h[16];
+  constexpr int TPR = 32 / WPT;
+  const int row = tid / TPR, q = tid % TPR;
+  float h[WPT];
   if constexpr (KIND == kPacked) {
-    // this thread's 16 codes start at bit 16 N hf of the row's slab; selects
-    // (not an index) pick the dwords, so the slab stays in registers
-    // (the empty asm keeps the dwords values, so that the selects are not
-    // turned back into an indexed load, which would move the slabs to LDS)
+    // this thread's WPT codes start at bit WPT N q of the row's slab; selects
+    // (not an index) pick the two dwords around them, so the slab stays in
+    // registers (the empty asm keeps the dwords values, so that the selects
+    // are not turned back into an indexed load, which would move the slabs
+    // to LDS)
     uint32_t d[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       d[i] = w.d[i];
       asm volatile("" : "+v"(d[i]));
     }
-    uint64_t x;
-    if constexpr (NB == 2) {
-      x = hf ? d[1] : d[0];
-    } else if constexpr (NB == 3) {
-      x = ((uint64_t)(hf ? d[2] : d[1]) << 32 | (hf ? d[1] : d[0])) >> (hf ? 16 : 0);
-    } else {
-      x = (uint64_t)(hf ? d[3] : d[1]) << 32 | (hf ? d[2] : d[0]);
-    }
+    const int bit = q * WPT * NB, k = bit >> 5;
+    uint32_t lo = d[0], hi = NB > 1 ? d[1] : 0u;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) h[e] = ((float)(uint32_t)((x >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv;
+    for (int i = 1; i < NB; ++i) {
+      lo = k == i ? d[i] : lo;
+      hi = k + 1 == i ? d[i] : hi;
+    }
+    const uint64_t x = ((uint64_t)hi << 32 | lo) >> (bit & 31);
+#pragma unroll
+    for (int e = 0; e < WPT; ++e) h[e] = ((float)(uint32_t)((x >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv;
   } else {
     const QRow r = qrow(sv, zv, K);
     uint64_t tie = 0;                                          // lanes with a near-tie (wave mask)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < WPT; ++e) {
       bool t;
       h[e] = qfast(__builtin_bit_cast(float, w.d[e]), r, t);
       tie |= __builtin_amdgcn_ballot_w64(t);
     }
     if (tie) {                                                 // near a rounding tie: exact division
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < WPT; ++e) {
         float wt = __builtin_bit_cast(float, w.d[e]);
         rare_branch(wt);
         if (qnear_tie(wt, r)) h[e] = quant_elem(wt, sv, r.zr, K).w_hat;
@@ -521,8 +525,8 @@ __device__ __forceinline__ void convert_slab(const WSlab<KIND, NB>& w, float sv,
     }
   }
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-    *(uint4*)&smem[b + L::off(row, 2 * hf + m)] =
+  for (int m = 0; m < WPT / 8; ++m)
+    *(uint4*)&smem[b + L::off(row, (WPT / 8) * q + m)] =
         make_uint4(pack2_bf16(h[8 * m], h[8 * m + 1]), pack2_bf16(h[8 * m + 2], h[8 * m + 3]),
                    pack2_bf16(h[8 * m + 4], h[8 * m + 5]), pack2_bf16(h[8 * m + 6], h[8 * m + 7]));
 }
@@ -1421,13 +1425,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
 // The forward with a fused B operand (Y = X W_hat^T, no workspace): W_hat is
 // made in LDS from the fp32 master weight (Eq. 1-2) or from packed codes,
 // never stored. Slabs of BK = 32; 8 waves, one of each role per SIMD:
-// - waves 0-3 (2 x 2 over the BM x BN tile) load A themselves (D stages by
-//   DMA, slab i + D issued during slab i's MFMAs) and run the MFMAs of slab i
-//   interleaved with the fragment reads of slab i + 1;
-// - waves 4-7 (converters) keep their 16 weights of every slab in a queue of
-//   U = 4 register slabs (WRowLoader), load slab i + 2 + U while slab i + 2 is
-//   converted into B stage (i + 2) % 3, and DMA the rows' s and z in chunks
-//   of four groups (SzChunks).
+// - waves 0-3 (2 x 2 over a 256 x 128 or 128 x 128 tile, or 4 x 1 over a
+//   512 x 64 tile: 128 x 64 or 64 x 64 per wave) load A themselves (D stages
+//   by DMA, slab i + D issued during slab i's MFMAs) and run the MFMAs of
+//   slab i interleaved with the fragment reads of slab i + 1;
+// - waves 4-7 (converters) keep their WPT weights of every slab (16 for
+//   128-row B tiles, 8 for 64-row ones) in a queue of U = 4 register slabs
+//   (WRowLoader), load slab i + 2 + U while slab i + 2 is converted into B
+//   stage (i + 2) % 3, and DMA the rows' s and z in chunks of four groups
+//   (SzChunks). The 512 x 64 tile halves the weights converted per MFMA.
 // One barrier per slab. The raw weights never pass through LDS (the LDS moves
 // A's DMA and fragment reads, the bf16 B stage and its reads only), and A has
 // up to six stages.
@@ -1440,6 +1446,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
 template <int BM, int BN, int BL, int NB>
 struct FusedFwdShape {
   static constexpr int BK = 32, U = 4;
+  static constexpr int WGN = BN == 64 ? 1 : 2, WGM = 4 / WGN;   // MFMA-wave grid
+  static constexpr int WPT = BN * 32 / 256;             // weights per converter thread and slab
   using L = LdsLayout<BK, kLdsSlots>;
   using LA = DmaTileK<BM, BK, kLdsSlots, 4, 0>;
   using SZ = SzChunks<BN>;
@@ -1461,8 +1469,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
   using LA = typename Sh::LA;
   using FB = DmaTileK<BN, BK, kLdsSlots>;
   static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
-  static_assert(BN == 128, "two converter threads per weight row");
-  constexpr int WM = BM / 2, WN = BN / 2;
+  static_assert(BN == 128 || BN == 64, "two or four converter threads per weight row");
+  constexpr int WGN = Sh::WGN, WPT = Sh::WPT, TPR = 32 / WPT;
+  constexpr int WM = BM / Sh::WGM, WN = BN / WGN;
   constexpr int TI = WM / 16, TJ = WN / 16, NM = TI * TJ, NR = TI + TJ;
   static_assert(NR <= NM, "a slab's MFMAs cover the next slab's reads");
   constexpr int A_BYTES = Sh::A_BYTES, B_BYTES = Sh::B_BYTES;
@@ -1484,7 +1493,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
     // ---- MFMA waves: A by DMA, fragment reads, MFMAs
     LA la;
     la.init(a.A, a.lda, m0, a.M, a.K, wave);
-    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
     auto read_r = [&](int aoff, int boff, int r, Frags<TI, TJ>& f) {
       const uint8_t* at = &smem[A0 + aoff];
       const uint8_t* bt = &smem[B0 + boff];
@@ -1543,25 +1552,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
   } else {
     // ---- converter waves: raw weights to registers, (s, z) chunks, B stages
     const int cw = wave - 4, tid = threadIdx.x - 256;
-    const int row = tid >> 1;
-    WRowLoader<BL, NB> wl;
+    const int row = tid / TPR;
+    WRowLoader<BL, NB, WPT> wl;
     wl.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.N, tid);
     typename Sh::SZ sz;
     sz.init(a.s, a.z, n0, a.N, a.G, a.group, a.Kq, cw);
-    constexpr int NLW = WRowLoader<BL, NB>::NL;
+    constexpr int NLW = WRowLoader<BL, NB, WPT>::NL;
     const uint32_t lds_sz = lds0 + SZ0;
-    auto fetch = [&](WSlab<BL, NB>& w, int slab) {      // (s, z) chunk first, then the weights
+    auto fetch = [&](WSlab<BL, NB, WPT>& w, int slab) { // (s, z) chunk first, then the weights
       const int k0 = clamp_slab(slab) * BK;
       sz.issue(lds_sz, k0);
       wl.load(w, k0);
     };
-    auto convert = [&](const WSlab<BL, NB>& w, int slab, int boff) {
+    auto convert = [&](const WSlab<BL, NB, WPT>& w, int slab, int boff) {
       const int c = sz.at(SZ0, row, slab * BK);
       const float sv = *(const float*)&smem[c];
       const float zv = *(const float*)&smem[c + BN * Sh::SZ::CG * 4];
-      convert_slab<BL, NB>(w, sv, zv, sz.K, smem, B0 + boff, tid);
+      convert_slab<BL, NB, WPT>(w, sv, zv, sz.K, smem, B0 + boff, tid);
     };
-    WSlab<BL, NB> R0, R1, R2, R3;                        // slab j in R[j % 4]
+    WSlab<BL, NB, WPT> R0, R1, R2, R3;                   // slab j in R[j % 4]
     static_assert(U == 4, "four named register slabs");
     fetch(R0, 0);
     fetch(R1, 1);
@@ -1576,7 +1585,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
     __syncthreads();                                     // P1
     __syncthreads();                                     // P2
     int boff = 2 * B_BYTES;                              // B stage of slab i + 2
-    auto iter = [&](WSlab<BL, NB>& R, int kt) {
+    auto iter = [&](WSlab<BL, NB, WPT>& R, int kt) {
       convert(R, kt + 2, boff);
       fetch(R, kt + 2 + U);
       boff = boff + B_BYTES == SB * B_BYTES ? 0 : boff + B_BYTES;
