@@ -314,9 +314,11 @@ constexpr bool k_contig(int layout) { return layout == kKContig || layout == kKC
 // u is within 2^-17.7 of fl32(w/s): rint(u) can differ from the correctly
 // rounded quotient's only if |u - rint(u)| >= 0.5 - 2^-17 (a near-tie, also
 // set for non-finite u). The caller redoes near-ties with quant_elem (the
-// exact division), so the codes are exactly the fp32 quantiser's. Six VALU
-// operations per weight; callers gather the near-tie flags as wave masks
-// (ballot, scalar ORs) and take the rare path when any lane has one.
+// exact division), so the codes are exactly the fp32 quantiser's. Callers
+// keep the running maximum of |u - rint(u)| (v_maximum3, which propagates a
+// NaN, two weights per instruction) and take the rare path when any lane's
+// maximum fails the margin: five and a half VALU operations per weight and
+// one ballot per slab.
 constexpr float kNearTie = 0.5f - 0x1p-17f;
 
 struct QRow {
@@ -333,11 +335,18 @@ __device__ __forceinline__ QRow qrow(float s, float z, float K) {
   return r;
 }
 
-__device__ __forceinline__ float qfast(float w, const QRow& r, bool& tie) {
+// W_hat on the fast path; res = |u - rint(u)| (the near-tie measure).
+__device__ __forceinline__ float qfast(float w, const QRow& r, float& res) {
   const float u = w * r.rcp;
   const float ru = __builtin_rintf(u);
-  tie = !(__builtin_fabsf(u - ru) < kNearTie);
+  res = __builtin_fabsf(u - ru);
   return __builtin_fmaf(__builtin_amdgcn_fmed3f(ru, r.lo, r.hi), r.s, 0.0f);
+}
+
+// Whether any lane of the wave saw a near-tie (or a non-finite u): m is the
+// lane's running maximum of the residuals (NaN if one was NaN).
+__device__ __forceinline__ bool wave_near_tie(float m) {
+  return __builtin_amdgcn_ballot_w64(!(m < kNearTie)) != 0;
 }
 
 // The near-tie test of qfast alone (the rare path's per-element decision).
@@ -508,14 +517,13 @@ __device__ __forceinline__ void convert_slab(const WSlab<KIND, NB, WPT>& w, floa
     for (int e = 0; e < WPT; ++e) h[e] = ((float)(uint32_t)((x >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv;
   } else {
     const QRow r = qrow(sv, zv, K);
-    uint64_t tie = 0;                                          // lanes with a near-tie (wave mask)
+    float res[WPT];
 #pragma unroll
-    for (int e = 0; e < WPT; ++e) {
-      bool t;
-      h[e] = qfast(__builtin_bit_cast(float, w.d[e]), r, t);
-      tie |= __builtin_amdgcn_ballot_w64(t);
-    }
-    if (tie) {                                                 // near a rounding tie: exact division
+    for (int e = 0; e < WPT; ++e) h[e] = qfast(__builtin_bit_cast(float, w.d[e]), r, res[e]);
+    float m = res[0];                                          // the lane's largest residual
+#pragma unroll
+    for (int e = 1; e < WPT; ++e) m = __builtin_elementwise_maximum(m, res[e]);
+    if (wave_near_tie(m)) {                                    // near a rounding tie: exact division
 #pragma unroll
       for (int e = 0; e < WPT; ++e) {
         float wt = __builtin_bit_cast(float, w.d[e]);
@@ -633,8 +641,8 @@ struct DmaRingT {
       }
     } else {
       constexpr int QPR = ROWS / 4, QPT = BK * QPR / 256;                  // 4-weight quads
-          float h[QPT][4];
-      uint64_t tie = 0;                                       // lanes with a near-tie (wave mask)
+      float h[QPT][4];
+      float m = 0.0f;                                         // the lane's largest residual
 #pragma unroll
       for (int i = 0; i < QPT; ++i) {
         const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
@@ -643,12 +651,12 @@ struct DmaRingT {
         const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          bool t;
-          h[i][e] = qfast(wv[e], r, t);
-          tie |= __builtin_amdgcn_ballot_w64(t);
+          float res;
+          h[i][e] = qfast(wv[e], r, res);
+          m = __builtin_elementwise_maximum(m, res);
         }
       }
-      if (tie) {                                              // near a rounding tie: exact division
+      if (wave_near_tie(m)) {                                 // near a rounding tie: exact division
 #pragma unroll
         for (int i = 0; i < QPT; ++i) {
           const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
@@ -1440,7 +1448,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
 // Waits: the MFMA waves allow the last D - 2 slabs' A DMAs in flight at each
 // barrier; the converters' register loads are waited for by the compiler
 // before their conversion, and at each barrier a converter allows the last
-// U slabs' loads in flight, which covers the chunk DMA issued before them.
+// U - 1 slabs' loads in flight, so the chunk DMA of the slab after the next
+// one (issued before its weights) has landed when its s and z are read.
 // Slabs past the end re-load the last one; nothing reads what they make.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BL, int NB>
@@ -1564,10 +1573,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
       sz.issue(lds_sz, k0);
       wl.load(w, k0);
     };
-    auto convert = [&](const WSlab<BL, NB, WPT>& w, int slab, int boff) {
-      const int c = sz.at(SZ0, row, slab * BK);
-      const float sv = *(const float*)&smem[c];
-      const float zv = *(const float*)&smem[c + BN * Sh::SZ::CG * 4];
+    // this thread's row's s and z for a slab, read one slab before its
+    // conversion (the LDS read's latency then hides behind a conversion)
+    auto sz_read = [&](int slab, float& sv, float& zv) {
+      const int c = sz.at(SZ0, row, clamp_slab(slab) * BK);
+      sv = *(const float*)&smem[c];
+      zv = *(const float*)&smem[c + BN * Sh::SZ::CG * 4];
+    };
+    auto convert = [&](const WSlab<BL, NB, WPT>& w, float sv, float zv, int boff) {
       convert_slab<BL, NB, WPT>(w, sv, zv, sz.K, smem, B0 + boff, tid);
     };
     WSlab<BL, NB, WPT> R0, R1, R2, R3;                   // slab j in R[j % 4]
@@ -1576,27 +1589,51 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
     fetch(R1, 1);
     fetch(R2, 2);
     fetch(R3, 3);
-    wait_vmcnt<U * NLW>();                               // chunk 0 landed (for this wave)
+    wait_vmcnt<U * NLW>();                               // chunk 0 (slabs 0-3 at least) landed (for this wave)
     __syncthreads();                                     // P0
-    convert(R0, 0, 0);
+    float sv, zv, sn, zn;                                // s, z of the slab converted now, and of the next
+    sz_read(0, sv, zv);
+    sz_read(1, sn, zn);
+    convert(R0, sv, zv, 0);
     fetch(R0, U);
-    convert(R1, 1, B_BYTES);
+    sz_read(2, sv, zv);
+    convert(R1, sn, zn, B_BYTES);
     fetch(R1, U + 1);
     __syncthreads();                                     // P1
     __syncthreads();                                     // P2
     int boff = 2 * B_BYTES;                              // B stage of slab i + 2
+    // Iteration i converts slab i + 2 with the s, z read in the iteration
+    // before and reads those of slab i + 3, whose chunk landed before the
+    // last barrier: each wave issues the chunk DMA of a slab before the slab's
+    // weights, and waits at a barrier until at most the weights of the next
+    // U - 1 slabs (and chunk DMAs among them) are in flight.
     auto iter = [&](WSlab<BL, NB, WPT>& R, int kt) {
-      convert(R, kt + 2, boff);
+      sz_read(kt + 3, sn, zn);
+      convert(R, sv, zv, boff);
       fetch(R, kt + 2 + U);
+      sv = sn, zv = zn;
       boff = boff + B_BYTES == SB * B_BYTES ? 0 : boff + B_BYTES;
-      wait_vmcnt<U * NLW>();                             // the chunk of slab i + 3 (issued before its weights)
+      wait_vmcnt<(U - 1) * NLW>();
       __syncthreads();
     };
-    for (int kt = 0; kt < nk; kt += 4) {
+    // Whole groups of four slabs in a loop without guards, the rest straight
+    // after it: the compiler places the waits for the register loads, and
+    // guards inside the loop body let it branch from one slab to a later one
+    // of the same trip, after which it must assume fewer loads in flight and
+    // waits for up to three slabs' loads that the conversion does not need.
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
       iter(R2, kt);
-      if (kt + 1 < nk) iter(R3, kt + 1);
-      if (kt + 2 < nk) iter(R0, kt + 2);
-      if (kt + 3 < nk) iter(R1, kt + 3);
+      iter(R3, kt + 1);
+      iter(R0, kt + 2);
+      iter(R1, kt + 3);
+    }
+    if (kt < nk) {
+      iter(R2, kt);
+      if (kt + 1 < nk) {
+        iter(R3, kt + 1);
+        if (kt + 2 < nk) iter(R0, kt + 2);
+      }
     }
     wait_vmcnt<0>();                                     // drain the trailing re-loads
   }
