@@ -18,6 +18,17 @@ so an element's error is a few u/sqrt(3) of the row's scale (~1e-2 rms of
 the row scale measured); 2^-3 leaves room for the tails over a million
 elements while a token row or an output tile that is wrong as a whole (an
 error of the order of the row scale) falls outside it.
+dz is nonzero only in groups where the fp32 quantiser clamps a weight: at
+min-max initialisation a handful of groups at most (one of 45 M weights of the
+7B up_proj is clamped). Its zero pattern must match the oracle's exactly (both
+sides take the clamp decision in fp32). With fewer than 100 nonzero entries
+the relative Frobenius bar has nothing to average over: one entry is -s times
+one element of dY^T X, a dot product over the tokens of bf16-rounded inputs,
+whose relative error is a few u/sqrt(3) and larger where the sum cancels
+(3.2% measured for the 7B up_proj's single entry); such a dz is checked
+element by element as y - x is, |dz - dz_ref| <= 2^-3 (|dz_ref| + rms of the
+nonzero dz_ref), which a wrong sign or a dropped term (an error of the order
+of the entry) still fails.
 The optimiser itself is checked tightly on the GPU's own gradients and
 moments (fp32 rounding only): AdamW is elementwise, so its outputs must equal
 the fp64 update of those inputs to a few fp32 ulps.
@@ -160,6 +171,24 @@ def report(name, v):
     return v
 
 
+def check_grad(ctx, key, got, ref, bar):
+    """A gradient against the oracle's: relative Frobenius below bar; dz with
+    the oracle's zero pattern exactly, and element by element where it has
+    fewer than 100 nonzero entries. Returns the relative Frobenius error."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    e = rel_fro(got, ref)
+    if key == "z":
+        nz = ref != 0
+        assert np.array_equal(got != 0, nz), (ctx, key, "zero pattern")
+        if nz.sum() < 100:
+            if nz.any():
+                check_contribution(f"{ctx} dz", got[nz][None, :], ref[nz][None, :])
+            return e
+    assert e < bar, (ctx, key, e)
+    return e
+
+
 def check_contribution(name, c, c_ref, tau=2.0 ** -3):
     """|c - c_ref| <= tau (|c_ref| + rms over the row of c_ref), element by element."""
     rms = np.sqrt(np.mean(c_ref * c_ref, axis=-1, keepdims=True))
@@ -232,9 +261,8 @@ def _check_step_parity(sh, d, params, bars=None, tau=2.0 ** -3):
     for i, n in enumerate(B.LINEARS):
         bar = bars.get(n, BAR)
         for key in KEYS:
-            e = rel_fro(after[i]["d" + key], grads_ref[n][key])
+            e = check_grad(n, key, after[i]["d" + key], grads_ref[n][key], bar)
             worst = max(worst, e)
-            assert e < bar, (n, key, e)
             du, fl = check_update(after[i][key], params[n][key], p_ref[n][key], [grads_ref[n][key]], (n, key),
                                   bar)
             worst_u, worst_f = max(worst_u, du), max(worst_f, fl)
@@ -318,30 +346,55 @@ def test_block_step_without_dw_is_identical(case):
 
 
 def test_block_step_full_size_7b():
-    """Llama-2-7B block, 2 x 2048 tokens, w2g64 (the benchmark's step): the
-    forward on sampled tokens of the second sequence against the oracle; the
-    loss against the GPU's own y; the straight-through mask and the in-range
-    ds identity of every linear; AdamW on the GPU's own gradients."""
+    """Llama-2-7B block, 2 x 2048 tokens, w2g64 (the benchmark's step) against
+    the fp64 block oracle's full forward and backward (~40 s of host BLAS,
+    ~15 GB): the loss, y - x over every token (relative Frobenius and the
+    element-wise bound), every linear's dW, ds and dz and every parameter
+    update, with the small cases' bars; besides, the straight-through mask
+    and the in-range ds identity of every linear, and AdamW on the GPU's own
+    gradients."""
     H, nh, I, T, Bn = synth.BLOCK_7B
     case = (H, nh, I, T, Bn, 2, 64)
     say(f"block step full size {case}")
     sh, d, params = make(case)
+    o = B.AdamW()
     gb = GpuBlock(sh, d, params)
-    o = opt_dict(B.AdamW(), 0)
-    loss = gb.step(o)
-    y = gb.y.cpu().numpy()
+    before = [{k: params[n][k] for k in KEYS} for n in B.LINEARS[:3]]
+    loss = gb.step(opt_dict(o, 0))
+    y = gb.y.cpu().numpy().astype(np.float64)
+    after = [{k: v.cpu().numpy() for k, v in lin.items()} for lin in gb.lins]
+    del gb
+    torch.cuda.empty_cache()
+
     x64, t64 = bf(d["x"]), bf(d["target"])
-    assert abs(loss - np.mean((y - t64) ** 2)) <= 1e-5 * loss
+    g1, g2 = d["g1"].astype(np.float64), d["g2"].astype(np.float64)
+    say("  oracle forward and backward (fp64, host)")
+    c = B.block_forward(x64, params, g1, g2, sh)
+    loss_ref, dy = B.mse(c["y"], t64)
+    ref_y = c["y"]
+    grads_ref = B.block_backward(dy, c, params, g1, g2, sh)
+    del c, dy
 
-    rows = np.array([0, 1, 63, 64, 777, 1500, T - 1])
-    yr = B.block_forward_rows(x64, params, d["g1"].astype(np.float64), d["g2"].astype(np.float64), sh, 1, rows)
-    assert report("sampled y - x", rel_fro(y[T + rows] - x64[T + rows], yr - x64[T + rows])) < BAR
-    check_contribution("sampled y - x", y[T + rows] - x64[T + rows], yr - x64[T + rows])
+    assert report("loss", abs(loss - loss_ref) / loss_ref) < BAR
+    assert report("y - x", rel_fro(y - x64, ref_y - x64)) < BAR
+    check_contribution("y - x", y - x64, ref_y - x64)
+    del y, ref_y
 
+    lr_w = B.cosine_lr(o.lr_weight, 0, o.total_steps)
+    lr_q = B.cosine_lr(o.lr_quant, 0, o.total_steps)
+    worst = worst_u = worst_f = 0.0
     for i, n in enumerate(B.LINEARS):
         p = params[n]
-        dW = gb.host(i, "dW")
-        ds, dz = gb.host(i, "ds"), gb.host(i, "dz")
+        for key in KEYS:
+            g_ref = grads_ref[n][key]
+            e = check_grad(n, key, after[i]["d" + key], g_ref, BAR)
+            worst = max(worst, e)
+            lr = lr_w if key == "W" else lr_q
+            zero = np.zeros(g_ref.shape)
+            p_ref, _, _ = B.adamw_update(np.asarray(p[key], np.float64), g_ref, zero, zero, lr, 1, o)
+            du, fl = check_update(after[i][key], p[key], O.fl32(p_ref), [g_ref], (n, key))
+            worst_u, worst_f = max(worst_u, du), max(worst_f, fl)
+        dW, ds, dz = after[i]["dW"], after[i]["ds"], after[i]["dz"]
         t = O.quantize(p["W"], p["s"], p["z"], 2, 64)
         m = t["m"].astype(bool)
         assert np.all(dW[~m] == 0.0), n
@@ -353,9 +406,12 @@ def test_block_step_full_size_7b():
         scale = (np.abs(dW.astype(np.float64)) * np.abs(frac)).reshape(m.shape[0], G, 64).sum(-1)
         assert np.all(np.abs(ds - pred)[allin] <= 1e-5 * scale[allin] + 1e-30), n
         assert np.all(dz[allin] == 0.0), n
+        del t, m, frac, pred, scale
+    report("worst gradient", worst)
+    report("worst update (|g| >= 0.1 rms)", worst_u)
+    report("worst sign-flip fraction", worst_f)
     # AdamW identity on the first three linears' tensors (the others share the kernel)
     for i in range(3):
-        before = {k: params[B.LINEARS[i]][k] for k in KEYS}
-        before.update({f"{mv}_{k}": np.zeros_like(before[k]) for k in KEYS for mv in ("m", "v")})
-        after = {k: v.cpu().numpy() for k, v in gb.lins[i].items()}
-        check_adamw_identity(before, after, o, B.LINEARS[i])
+        b = dict(before[i])
+        b.update({f"{mv}_{k}": np.zeros_like(b[k]) for k in KEYS for mv in ("m", "v")})
+        check_adamw_identity(b, after[i], opt_dict(o, 0), B.LINEARS[i])
