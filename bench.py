@@ -52,7 +52,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q_proj_w2g64.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="least host time of the oracle sample")
@@ -337,7 +337,7 @@ def main():
     for label, fn in (("init_minmax", calls[0][1]), ("quant_w_hat", calls[1][1]), ("pack", calls[3][1]),
                       ("dequant", calls[4][1])):
         _, nbytes = work_per_launch(label, M, out, inp, bits)
-        cold = stats_ms(g.kernel_ms(label, fn, 10, True))
+        cold = stats_ms(g.kernel_ms(label, fn, 100, True))
         warm_us = ktab[label]["avg_us"]
         hbm[label] = {"cold": cold, "gbs": round(nbytes / (cold["median_ms"] * 1e-3) / 1e9, 1),
                       "frac_of_peak": round(nbytes / (cold["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -348,19 +348,19 @@ def main():
     # ---- the no-workspace variants at the same workload (bit-identical outputs)
     nows = {}
     Yf = torch.empty_like(Y)
-    t = stats_ms(g.per_call(lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Yf, ws=None), 10))
+    t = stats_ms(g.per_call(lambda: Q.qat_fakequant_linear_fwd(X, W, s, z, bits, Yf, ws=None), 100))
     nows["fq_fwd_fused_fp32"] = dict(t, tflops=round(2 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
                                      bit_identical=bool(torch.equal(Yf, Y)))
     dXf = torch.empty_like(dX)
-    t = stats_ms(g.per_call(lambda: Q.qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=dXf), 10))
+    t = stats_ms(g.per_call(lambda: Q.qat_fakequant_linear_bwd(dY, X, W, s, z, bits, dX=dXf), 100))
     nows["fq_dx_fused_fp32"] = dict(t, tflops=round(2 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
                                     bit_identical=bool(torch.equal(dXf, dX)))
     Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Y2, ws=ws)
-    t = stats_ms(g.per_call(lambda: Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Yf), 10))
+    t = stats_ms(g.per_call(lambda: Q.qat_dequant_gemm_fwd(X, Wq, s, zp, bits, Yf), 100))
     nows["e2e_fwd_fused_packed"] = dict(t, tflops=round(2 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
                                         bit_identical=bool(torch.equal(Yf, Y2)))
     Q.qat_dequant_gemm_bwd_s_saved(dY, X, Wq, s, zp, ws, bits, ds2, dX=dX2)
-    t = stats_ms(g.per_call(lambda: Q.qat_dequant_gemm_bwd_s(dY, X, Wq, s, zp, bits, ds2, dX=dXf), 10))
+    t = stats_ms(g.per_call(lambda: Q.qat_dequant_gemm_bwd_s(dY, X, Wq, s, zp, bits, ds2, dX=dXf), 100))
     nows["e2e_dx_ds_fused_packed"] = dict(t, tflops=round(4 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1),
                                           bit_identical=bool(torch.equal(dXf, dX2)))
     del Yf, dXf
@@ -474,7 +474,7 @@ def by_group(Q, torch, dev, g, W, X, dY, bits):
         def fq(sg=sg, zg=zg, dsg=dsg, dzg=dzg, gsize=gsize):
             Q.qat_fakequant_linear_fwd(X, W, sg, zg, bits, Y, ws=ws, group=gsize)
             Q.qat_fakequant_linear_bwd_saved(dY, X, W, sg, zg, ws, bits, dX=dX, dW=dW, ds=dsg, dz=dzg, group=gsize)
-        t = stats_ms(g.per_call(fq, 10))
+        t = stats_ms(g.per_call(fq, 100))
         res[gname] = dict(t, tflops=round(6.0 * M * inp * out / (t["median_ms"] * 1e-3) / 1e12, 1))
     return res
 
@@ -520,7 +520,7 @@ def other_workloads(Q, torch, dev, g, synth):
           ("e2e_bwd", lambda: Q.qat_dequant_gemm_bwd_s_saved(dY, X, Wq, s, zp, ws, b, ds2, dX=dX2))]
     r1 = {}
     for name, f in c1:
-        t = stats_ms(g.per_call(f, 50))
+        t = stats_ms(g.per_call(f, 100))
         g.sync()
         h0 = time.perf_counter()
         for _ in range(200):
@@ -529,7 +529,7 @@ def other_workloads(Q, torch, dev, g, synth):
         g.sync()
         r1[name] = {"gpu_us_median": round(t["median_ms"] * 1e3, 2), "gpu_us_min": round(t["min_ms"] * 1e3, 2),
                     "host_us_per_call": round((h1 - h0) / 200 * 1e6, 2)}
-    step = stats_ms(g.per_call(lambda: [f() for _, f in c1], 50))
+    step = stats_ms(g.per_call(lambda: [f() for _, f in c1], 100))
     note("C1 latency done")
     res["c1_latency"] = {"what": "256x256 linear, 128 tokens, w2g64; GPU time per call (event pairs) and "
                                  "host time to issue it", "calls": r1,
@@ -560,7 +560,7 @@ def other_workloads(Q, torch, dev, g, synth):
             Q.qat_fakequant_linear_bwd_saved(dYc, Xc, Wc, sc, zc, ws3, lin.bits, dX=dX3[:M3 * i].view(M3, i),
                                              dW=dW3[:o * i].view(o, i), ds=ds3[:o * (i // 64)].view(o, i // 64),
                                              dz=dz3[:o * (i // 64)].view(o, i // 64))
-    t = stats_ms(g.per_call(block, 10))
+    t = stats_ms(g.per_call(block, 20))
     fl = sum(6.0 * lin.m * lin.inp * lin.out for lin, *_ in c3)
     note("C3 block done")
     res["c3_block_w3g64"] = dict(t, gflop=round(fl / 1e9, 2), **_rate(fl, t))
@@ -590,8 +590,8 @@ def other_workloads(Q, torch, dev, g, synth):
                 Q.qat_dequant_gemm_fwd(X4, Wq4, s4, z4, lin.bits, Y4[:M4 * o].view(M4, o))
                 Q.qat_dequant_gemm_bwd_s(dY4, X4, Wq4, s4, z4, lin.bits, dsv, dX=dX4[:M4 * i].view(M4, i))
     fl = sum(6.0 * lin.m * lin.inp * lin.out for lin, *_ in c4)
-    t = stats_ms(g.per_call(lambda: mlp(True), 10))
-    tf = stats_ms(g.per_call(lambda: mlp(False), 5))
+    t = stats_ms(g.per_call(lambda: mlp(True), 20))
+    tf = stats_ms(g.per_call(lambda: mlp(False), 20))
     note("C4 E2E-QP MLP done")
     res["c4_e2e_mlp_w2g64"] = {"gflop": round(fl / 1e9, 2), "staged": dict(t, **_rate(fl, t)),
                                "fused_no_workspace": dict(tf, **_rate(fl, tf))}
@@ -637,8 +637,8 @@ def other_workloads(Q, torch, dev, g, synth):
                 o, i = lin.out, lin.inp
                 Q.qat_dequant_gemm_fwd(X5, Wq5, s5, zp5, b, Y5[:M5 * o].view(M5, o), ws=ws5)
                 Q.qat_dequant_gemm_bwd_s_saved(dY5, X5, Wq5, s5, zp5, ws5, b, ds5)
-        tb = stats_ms(g.per_call(block_ap, 5))
-        te = stats_ms(g.per_call(e2e, 5))
+        tb = stats_ms(g.per_call(block_ap, 20))
+        te = stats_ms(g.per_call(e2e, 20))
         note(f"C5 at {b} bits done")
         c5[f"w{b}g64"] = {"block_ap_fwd_bwd": dict(tb, **_rate(fl_bap, tb)), "e2e_fwd_ds": dict(te, **_rate(fl_e2e, te))}
         del qp
@@ -650,7 +650,7 @@ def other_workloads(Q, torch, dev, g, synth):
     for label, fn in (("init_minmax", lambda: Q.qat_init_minmax(W5, 2, s5, z5)),
                       ("pack", lambda: Q.qat_pack(W5, s5, z5, 2, Wq5, zp5))):
         _, nbytes = work_per_launch(label, lin.m, lin.out, lin.inp, 2)
-        t = stats_ms(g.kernel_ms(label, fn, 5, True))
+        t = stats_ms(g.kernel_ms(label, fn, 20, True))
         c5[f"{label}_cold_gate_w2"] = dict(t, gbs=round(nbytes / (t["median_ms"] * 1e-3) / 1e9, 1),
                                           frac_of_peak=round(nbytes / (t["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
     res["c5_70b_gate_down"] = dict(c5, gflop_block_ap=round(fl_bap / 1e9, 2), gflop_e2e_fwd_ds=round(fl_e2e / 1e9, 2))
