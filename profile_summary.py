@@ -36,8 +36,9 @@ import sys
 # template arguments name it (AMN / BMN: 0, 2 K-contiguous; 1, 3
 # MN-contiguous; EP the epilogue; NB the bit width or a tag).
 GEMM_RE = re.compile(r"k_gemm<(?:\s*\d+\s*,){7}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
-# k_gemm_fused<BM, BN, BL, NB, BT, ADW> (dX), k_gemm_fused_fwd<BM, BN, BL, NB> (forward)
-FUSED_RE = re.compile(r"k_gemm_fused<(?:\s*\d+\s*,){2}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
+# k_gemm_fused_dx<BM, BN, BL, NB, ADW> (dX), k_gemm_fused_fwd<BM, BN, BL, NB> (forward); BL 1: fp32
+# master weight, 2: packed codes
+FUSED_DX_RE = re.compile(r"k_gemm_fused_dx<(?:\s*\d+\s*,){2}\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*>")
 FUSED_FWD_RE = re.compile(r"k_gemm_fused_fwd<(?:\s*\d+\s*,){2}\s*(\d+)\s*,\s*(\d+)\s*>")
 LABELS = [
     (r"k_attn_rowdot", "attn_rowdot"),
@@ -75,12 +76,9 @@ def label_of(name: str):
     m = FUSED_FWD_RE.search(name)
     if m:
         return "gemm_fwd_fused_fp32" if int(m.group(1)) == 1 else "gemm_fwd_packed"
-    m = FUSED_RE.search(name)
+    m = FUSED_DX_RE.search(name)
     if m:
-        bl, nb, bt, _ = (int(v) for v in m.groups())
-        if bt == 1:
-            return "gemm_dx_fused_fp32" if bl == 1 else "gemm_dx_packed"
-        return "gemm_fwd_fused_fp32" if bl == 1 else "gemm_fwd_packed"
+        return "gemm_dx_fused_fp32" if int(m.group(1)) == 1 else "gemm_dx_packed"
     m = GEMM_RE.search(name)
     if m:
         amn, bmn, ep, nb = (int(v) for v in m.groups())

@@ -9,9 +9,9 @@
 //   128x128, 4 stages   small problems; 4 waves
 // Fused B operands (the fp32 master weight or packed codes turned into bf16
 // W_hat in LDS by converter waves beside the MFMA waves; the calls without a
-// workspace): the forward in k_gemm_fused_fwd (raw weights through converter
-// registers, up to six A stages), dX in k_gemm_fused (raw weight rows through
-// an LDS ring); 256x128 or 128x128 tiles, BK = 32.
+// workspace): the forward in k_gemm_fused_fwd and dX in k_gemm_fused_dx (raw
+// weights through converter registers, the activations' DMA on the MFMA
+// waves); 256x128 or 128x128 tiles, BK = 32.
 #include "qat_gemm_kernel.h"
 
 namespace qat {
@@ -49,10 +49,10 @@ void launch_bf16(const GemmArgs& a, hipStream_t st) {
                      dim3((unsigned)tiles(a, BM, BN), (unsigned)batches(a)), dim3(64 * WGM * WGN), 0, st, a);
 }
 
-template <int BM, int BN, int BL, int NB, int BT, int ADW>
-void launch_fused(const GemmArgs& a, hipStream_t st) {
-  LaunchTimer t(gemm_label<BL, kStoreBf16, NB, BT>(), st);
-  QAT_LAUNCH((k_gemm_fused<BM, BN, BL, NB, BT, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(512), 0, st, a);
+template <int BM, int BN, int BL, int NB, int ADW>
+void launch_fused_dx(const GemmArgs& a, hipStream_t st) {
+  LaunchTimer t(gemm_label<BL, kStoreBf16, NB, 1>(), st);
+  QAT_LAUNCH((k_gemm_fused_dx<BM, BN, BL, NB, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(512), 0, st, a);
 }
 
 // Returns the number of workgroups launched.
@@ -132,14 +132,14 @@ void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
   else launch_fused_fwd<128, 128, BL, NB>(a, st);
 }
 
-// dX = dY W_hat with W_hat made in LDS from the weight's rows (the
-// transposed ring).
+// dX = dY W_hat with W_hat^T made in LDS from the weight's rows
+// (k_gemm_fused_dx).
 // ADW: dY by 4-byte DMA with the contraction's tail masked (out not a
 // multiple of 64).
 template <int BL, int NB, int ADW>
 void launch_pick_dx_fused_a(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 128) >= 256) launch_fused<256, 128, BL, NB, 1, ADW>(a, st);
-  else launch_fused<128, 128, BL, NB, 1, ADW>(a, st);
+  if (tiles(a, 256, 128) >= 256) launch_fused_dx<256, 128, BL, NB, ADW>(a, st);
+  else launch_fused_dx<128, 128, BL, NB, ADW>(a, st);
 }
 
 template <int BL, int NB>

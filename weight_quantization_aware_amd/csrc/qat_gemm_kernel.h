@@ -539,147 +539,118 @@ __device__ __forceinline__ void convert_slab(const WSlab<KIND, NB, WPT>& w, floa
                    pack2_bf16(h[8 * m + 4], h[8 * m + 5]), pack2_bf16(h[8 * m + 6], h[8 * m + 7]));
 }
 
-// The weight as the B operand of dX = dY W_hat (contraction over the weight's
-// rows): B[n][k] = W_hat[k][n], so a slab is BK weight rows k0 .. k0 + BK - 1
-// of ROWS consecutive weights n0 .. n0 + ROWS - 1 each (fp32 master weight,
-// 4 ROWS bytes per row, by 16-byte DMA; or packed codes, ROWS N / 8 bytes per
-// row, by dword DMA, since 3-bit rows are only 8-byte aligned), followed by
-// the (s, z) of every 32-weight slot of those rows: s[BK][SL], z[BK][SL],
-// slot t holding the group of weight n0 + 32 t (groups of 32 or more never
-// split a slot). Each converter thread turns its share -- fp32: 4 quads of
-// 4 consecutive weights; packed: 2 pieces of 8 -- with the quantiser of
-// the fused forward (qfast) into the bf16 B stage in the MN-contiguous layout of DmaTileMN
-// ([BK][ROWS], read back with transpose loads). Weight rows at or beyond the
-// contraction's end (kdim) read as zero and convert to exactly 0.
-template <int ROWS, int BK, int KIND, int NB>
-struct DmaRingT {
-  using LT = DmaTileMN<ROWS, BK, 4>;
-  static_assert(BK == 32, "one 32-row slab");
-  static constexpr int RB = KIND == kPacked ? ROWS * NB / 8 : ROWS * 4;    // ring bytes per weight row
-  static constexpr int SL = ROWS / 32;                                      // (s, z) slots per row
-  static constexpr int W_BYTES = BK * RB;
-  static constexpr int P_BYTES = W_BYTES + 2 * BK * SL * 4;
-  static constexpr int DMA_B = KIND == kPacked ? 256 : 1024;               // bytes per DMA instruction
-  static constexpr int NQ = W_BYTES / DMA_B, NS = 2 * BK * SL / 64;
-  static constexpr int NI_Q = (NQ + 3) / 4, NI_S = (NS + 3) / 4;
-  static constexpr int NI = NI_Q + NI_S;
-  static_assert(NQ * DMA_B == W_BYTES && NS * 64 == 2 * BK * SL, "ring tile shape");
-  static_assert(KIND == kPacked || RB % 16 == 0, "16-byte DMA pieces of fp32 rows");
-  i32x4 rq, rsz[2];
-  uint32_t vq[NI_Q], dq[NI_Q], vs[NI_S], ds_[NI_S];
-  int which[NI_S];
-  int kdim;
-  int64_t row_bytes, grow;                                                  // weight / (s, z) row strides
-  float K;
-  // Wsrc: the weight [kdim][ld] (fp32) or its packed rows (row_bytes each);
-  // n0: first weight column of the tile; s, z: [kdim][G]; cw: converter wave.
-  __device__ __forceinline__ void init(const void* Wsrc, int64_t row_bytes_, int n0, int kdim_, const float* s,
-                                       const float* z, int64_t G, int group, float K_, int cw) {
-    K = K_;
-    kdim = kdim_;
-    row_bytes = row_bytes_;
-    grow = G * 4;
+// The weight as the B operand of dX = dY W_hat without an LDS ring: B[n][k] =
+// W_hat[k][n], so a slab is BK = 32 weight rows k0 .. k0 + 31 (the
+// contraction) by ROWS = 128 weight columns n0 .. (dX's columns). Converter
+// thread tid (0..255) owns row k0 + tid / 8 and its 16 columns n0 + 16
+// (tid % 8) .., loaded straight into registers -- fp32: four 16-byte loads;
+// packed codes: the 2 N bytes that hold them (one or two dwords) -- with the
+// row's s and z of their group (a group of 32 or more columns holds all 16).
+// Every offset, the slab's row included, is in the per-lane offset, so rows
+// at or beyond kdim are out of the buffer's range and read as zero; the
+// conversion zeroes them. Columns at or beyond the weight's width only feed
+// dX columns that are never stored.
+template <int KIND, int NB>
+struct WColSlab {
+  static constexpr int ND = KIND == kPacked ? (NB == 2 ? 1 : 2) : 16;
+  uint32_t d[ND];
+  float s, z;
+};
+
+template <int KIND, int NB>
+struct WColLoader {
+  static constexpr int NL = (KIND == kPacked ? 1 : 4) + 2;  // load instructions per slab
+  __amdgpu_buffer_rsrc_t rw, rs, rz;
+  uint32_t vw, vsz;
+  uint32_t wrow, grow;                                     // bytes per weight row, per (s, z) row
+  int sh;                                                  // 3-bit codes: bit of the first code in d
+  __device__ __forceinline__ void init(const void* W, int64_t row_bytes, int n0, int kdim, const float* s,
+                                       const float* z, int64_t G, int group, int tid) {
+    const int r = tid / 8, c16 = tid % 8;
+    wrow = (uint32_t)row_bytes;
+    grow = (uint32_t)(G * 4);
     const int64_t cb = KIND == kPacked ? (int64_t)n0 * NB / 8 : (int64_t)n0 * 4;
-    rq = buffer_rsrc((const uint8_t*)Wsrc + cb, (int64_t)kdim * row_bytes - cb);
-    rsz[0] = buffer_rsrc(s, (int64_t)kdim * G * 4);
-    rsz[1] = buffer_rsrc(z, (int64_t)kdim * G * 4);
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int q = 0; q < NI_Q; ++q) {
-      const int idx = dma_index<NQ, NI_Q>(cw, q);
-      const int b = idx * DMA_B + lane * (DMA_B / 64);                 // byte of the [BK][RB] slab
-      vq[q] = (uint32_t)((b / RB) * row_bytes + b % RB);
-      dq[q] = (uint32_t)(idx * DMA_B);
-    }
-#pragma unroll
-    for (int q = 0; q < NI_S; ++q) {
-      const int idx = dma_index<NS, NI_S>(cw, q);
-      const int r = (idx * 64 + lane) % (BK * SL);                     // slot of [BK][SL]
-      which[q] = (idx * 64) / (BK * SL);                               // 0: s, 1: z (uniform)
-      vs[q] = (uint32_t)((r / SL) * G * 4 + ((n0 + 32 * (r % SL)) / group) * 4);
-      ds_[q] = (uint32_t)(W_BYTES + idx * 256);
-    }
-  }
-  // lds_p: this slab's ring entry; k0: its first weight row.
-  __device__ __forceinline__ void issue(uint32_t lds_p, int k0) const {
-    const uint32_t rb = (uint32_t)(k0 * row_bytes), gb = (uint32_t)(k0 * grow);
-#pragma unroll
-    for (int q = 0; q < NI_Q; ++q) {
-      if constexpr (KIND == kPacked) dma4(rq, lds_p + dq[q], vq[q] + rb);
-      else dma16(rq, lds_p + dq[q], vq[q] + rb);
-    }
-#pragma unroll
-    for (int q = 0; q < NI_S; ++q) {
-      i32x4 r = which[q] ? rsz[1] : rsz[0];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_readfirstlane(r[e]);
-      dma4(r, lds_p + ds_[q], vs[q] + gb);
-    }
-  }
-  // Convert the slab of weight rows k0 .. from the ring entry at byte p into
-  // the B stage at byte b; tid: the converter thread (0..255).
-  __device__ __forceinline__ void commit(uint8_t* smem, int p, int b, int k0, int tid) const {
-    const float* sl = (const float*)&smem[p + W_BYTES];
-    const float* zl = sl + BK * SL;
+    int64_t n = (int64_t)kdim * row_bytes - cb;
+    n = n < 0 ? 0 : (n > 0x7FFFFFF0 ? 0x7FFFFFF0 : n);
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)W + cb), (short)0, (int)n, 0x00020000);
+    int64_t ns = (int64_t)kdim * G * 4;
+    ns = ns > 0x7FFFFFF0 ? 0x7FFFFFF0 : ns;
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)s, (short)0, (int)ns, 0x00020000);
+    rz = __builtin_amdgcn_make_buffer_rsrc((void*)z, (short)0, (int)ns, 0x00020000);
     if constexpr (KIND == kPacked) {
-      constexpr int CPR = ROWS / 8, CPT = BK * CPR / 256;                  // 8-weight pieces
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int ch = tid + 256 * i, k = ch / CPR, c = ch % CPR;
-        const uint32_t* q = (const uint32_t*)&smem[p + k * RB];
-        const int bit = c * 8 * NB;
-        uint64_t w = q[bit >> 5];
-        if (NB == 3 && (bit & 31) > 8) w |= (uint64_t)q[(bit >> 5) + 1] << 32;
-        const uint32_t word = (uint32_t)(w >> (bit & 31));
-        const float sv = sl[k * SL + c / 4], zv = zl[k * SL + c / 4];
-        const bool live = k0 + k < kdim;
-        float h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = live ? ((float)((word >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv : 0.0f;
-        *(uint4*)&smem[b + LT::off(k, c)] = make_uint4(pack2_bf16(h[0], h[1]), pack2_bf16(h[2], h[3]),
-                                                        pack2_bf16(h[4], h[5]), pack2_bf16(h[6], h[7]));
+      const int bit = c16 * 16 * NB;
+      vw = (uint32_t)(r * row_bytes + (bit >> 5) * 4);
+      sh = bit & 31;
+    } else {
+      vw = (uint32_t)(r * row_bytes + c16 * 64);
+      sh = 0;
+    }
+    vsz = (uint32_t)(r * G * 4 + (int64_t)((n0 + 16 * c16) / group) * 4);
+  }
+  __device__ __forceinline__ void load(WColSlab<KIND, NB>& w, int k0) const {
+    typedef int v4i_ __attribute__((ext_vector_type(4)));
+    typedef int v2i_ __attribute__((ext_vector_type(2)));
+    const uint32_t ow = vw + (uint32_t)k0 * wrow;
+    if constexpr (KIND == kPacked) {
+      if constexpr (NB == 2) {
+        w.d[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)ow, 0, 0);
+      } else {
+        const v2i_ v = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)ow, 0, 0);
+        w.d[0] = v.x, w.d[1] = v.y;
       }
     } else {
-      constexpr int QPR = ROWS / 4, QPT = BK * QPR / 256;                  // 4-weight quads
-      float h[QPT][4];
-      float m = 0.0f;                                         // the lane's largest residual
 #pragma unroll
-      for (int i = 0; i < QPT; ++i) {
-        const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
-        const float4 w4 = *(const float4*)&smem[p + k * RB + qc * 16];
-        const QRow r = qrow(sl[k * SL + qc / 8], zl[k * SL + qc / 8], K);
-        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float res;
-          h[i][e] = qfast(wv[e], r, res);
-          m = __builtin_elementwise_maximum(m, res);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const v4i_ v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ow + 16 * j), 0, 0);
+        w.d[4 * j] = v.x, w.d[4 * j + 1] = v.y, w.d[4 * j + 2] = v.z, w.d[4 * j + 3] = v.w;
       }
-      if (wave_near_tie(m)) {                                 // near a rounding tie: exact division
+    }
+    const uint32_t os = vsz + (uint32_t)k0 * grow;
+    w.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)os, 0, 0));
+    w.z = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, (int)os, 0, 0));
+  }
+};
+
+// One converter thread's 16 weights of a slab row as bf16 W_hat (pk, two
+// 16-byte pieces of 8 columns): packed, W_hat = (q - z) s with z as stored;
+// fp32, Eq. 1 then Eq. 2 by qfast, near-ties redone by quant_elem; zero for a
+// row at or beyond the contraction's end (live false).
+template <int KIND, int NB>
+__device__ __forceinline__ void convert_cols(const WColSlab<KIND, NB>& w, float K, bool live, int sh,
+                                             uint4 (&pk)[2]) {
+  float h[16];
+  if constexpr (KIND == kPacked) {
+    uint64_t x;
+    if constexpr (NB == 2) x = w.d[0];
+    else if constexpr (NB == 3) x = ((uint64_t)w.d[1] << 32 | w.d[0]) >> sh;
+    else x = (uint64_t)w.d[1] << 32 | w.d[0];
 #pragma unroll
-        for (int i = 0; i < QPT; ++i) {
-          const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
-          const float* wr = (const float*)&smem[p + k * RB + qc * 16];
-          const QRow r = qrow(sl[k * SL + qc / 8], zl[k * SL + qc / 8], K);
+    for (int e = 0; e < 16; ++e) h[e] = ((float)(uint32_t)((x >> (NB * e)) & ((1u << NB) - 1)) - w.z) * w.s;
+  } else {
+    const QRow r = qrow(w.s, w.z, K);
+    float res[16];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float wt = wr[e];
-            rare_branch(wt);
-            if (qnear_tie(wt, r)) h[i][e] = quant_elem(wt, r.s, r.zr, K).w_hat;
-          }
-        }
-      }
+    for (int e = 0; e < 16; ++e) h[e] = qfast(__builtin_bit_cast(float, w.d[e]), r, res[e]);
+    float m = res[0];                                          // the lane's largest residual
 #pragma unroll
-      for (int i = 0; i < QPT; ++i) {
-        const int qd = tid + 256 * i, k = qd / QPR, qc = qd % QPR;
-        const bool live = k0 + k < kdim;
-        *(uint2*)&smem[b + LT::off(k, qc >> 1) + (qc & 1) * 8] =
-            live ? make_uint2(pack2_bf16(h[i][0], h[i][1]), pack2_bf16(h[i][2], h[i][3])) : make_uint2(0u, 0u);
+    for (int e = 1; e < 16; ++e) m = __builtin_elementwise_maximum(m, res[e]);
+    if (wave_near_tie(m)) {                                    // near a rounding tie: exact division
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float wt = __builtin_bit_cast(float, w.d[e]);
+        rare_branch(wt);
+        if (qnear_tie(wt, r)) h[e] = quant_elem(wt, w.s, r.zr, K).w_hat;
       }
     }
   }
-};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) h[e] = live ? h[e] : 0.0f;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    pk[m] = make_uint4(pack2_bf16(h[8 * m], h[8 * m + 1]), pack2_bf16(h[8 * m + 2], h[8 * m + 3]),
+                       pack2_bf16(h[8 * m + 4], h[8 * m + 5]), pack2_bf16(h[8 * m + 6], h[8 * m + 7]));
+}
+
 
 // Four consecutive codes c0..c0+3 (c0 % 4 == 0) of a packed row.
 template <int NB>
@@ -1261,175 +1232,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(const GemmArgs a0) {
 }
 
 // ---------------------------------------------------------------------------
-// dX = dY W_hat with a fused B operand: W_hat is made in LDS from the weight's
-// rows (fp32 master weight, Eq. 1-2, or packed codes), never stored. A (dY)
-// is bf16 and K-contiguous; bf16 output. Slabs of BK = 32.
-// The workgroup's 8 waves have two roles, one of each on every SIMD:
-// - waves 0-3 (2 x 2 over the BM x BN tile) issue only LDS fragment reads and
-//   MFMAs: the MFMAs of slab i interleaved with the reads of slab i + 1;
-// - waves 4-7 (converters) issue every DMA -- A of slab i + D and the raw
-//   weight rows (ring, DmaRingT) of slab i + D + 1 -- and turn ring slab
-//   i + 2 into its MN-contiguous bf16 B stage, VALU work that runs beside the
-//   other wave's MFMAs.
-// Both roles pass the same barriers: P0, P1, P2 in the prologue, then one
-// per slab. D A stages, D ring entries and three B stages: at iteration i
-// the MFMA waves read slab i + 1 (A stage (i + 1) % D, B stage (i + 1) % 3),
-// the converters write B stage (i + 2) % 3 and DMA into A stage i % D (slab
-// i, read during iteration i - 1) and ring entry (i + 1) % D (slab i + 1,
-// converted during iteration i - 1). A DMA has D - 1 iterations to land
-// (converters wait, before each barrier, for all but the last D - 2
-// iterations' DMAs); D is as deep as the LDS allows. Slabs past the end
-// re-load the last one (uniform wait counts); nothing reads what they make.
-// BT = 1 always (B rows are weight columns); ADW: A by 4-byte DMA with the
-// contraction's tail masked (dY rows of out % 64 != 0 elements). The forward
-// has its own kernel (k_gemm_fused_fwd below).
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int BL, int NB, int BT, int ADW>
-struct FusedShape {
-  static constexpr int BK = 32;
-  using L = LdsLayout<BK, kLdsSlots>;
-  using LA = DmaTileK<BM, BK, kLdsSlots, 4, ADW>;
-  static_assert(BT == 1, "the dX product; the forward is k_gemm_fused_fwd");
-  using LB = DmaRingT<BN, BK, BL, NB>;
-  static constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BN * L::PITCH, P_BYTES = LB::P_BYTES;
-  static constexpr int NL = LA::NI + LB::NI;            // DMA instructions per converter wave and slab
-  static constexpr int LDS_MAX = 160 * 1024;
-  static constexpr int D_FIT = (LDS_MAX - 3 * B_BYTES) / (A_BYTES + P_BYTES);
-  static constexpr int D_CNT = 2 + 63 / NL;             // (D - 2) NL in-flight DMAs fit the vmcnt field
-  static constexpr int D_MIN = D_FIT < D_CNT ? D_FIT : D_CNT;
-  static constexpr int D = D_MIN < 6 ? D_MIN : 6;       // A stages = ring entries
-  static_assert(D >= 3, "three stages at least");
-  static constexpr int LDS = D * (A_BYTES + P_BYTES) + 3 * B_BYTES;
-};
-
-template <int BM, int BN, int BL, int NB, int BT, int ADW>
-__global__ __launch_bounds__(512, 1) void k_gemm_fused(const GemmArgs a) {
-  using Sh = FusedShape<BM, BN, BL, NB, BT, ADW>;
-  constexpr int BK = Sh::BK, D = Sh::D, SB = 3;
-  using L = typename Sh::L;
-  using LA = typename Sh::LA;
-  using LB = typename Sh::LB;
-  using FB = DmaTileMN<BN, BK, 4>;
-  static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TI = WM / 16, TJ = WN / 16, NM = TI * TJ, NR = TI + TJ;
-  static_assert(NR <= NM, "a slab's MFMAs cover the next slab's reads");
-  constexpr int A_BYTES = Sh::A_BYTES, B_BYTES = Sh::B_BYTES, P_BYTES = Sh::P_BYTES;
-  constexpr int A0 = 0, B0 = D * A_BYTES, P0 = B0 + SB * B_BYTES;
-  static_assert(P0 + D * P_BYTES == Sh::LDS, "LDS map");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Sh::LDS];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = (a.K + BK - 1) / BK;
-
-  if (wave < 4) {
-    // ---- MFMA waves
-    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    auto read_r = [&](int aslot, int bslot, int r, Frags<TI, TJ>& f) {
-      const uint8_t* at = &smem[A0 + aslot * A_BYTES];
-      const uint8_t* bt = &smem[B0 + bslot * B_BYTES];
-      if (r < TI) f.a[r] = LA::frag(at, wm0 + r * 16 + (lane & 15), 0, lane);
-      else f.b[r - TI] = FB::frag(bt, wn0 + (r - TI) * 16 + (lane & 15), 0, lane);
-    };
-    f32x4 acc[TJ][TI];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // MFMAs on `cur`, each followed by (at most) one read of the next slab
-    // (A stage aslot, B stage bslot) into `nxt`
-    auto step = [&](const Frags<TI, TJ>& cur, int aslot, int bslot, Frags<TI, TJ>& nxt) {
-#pragma unroll
-      for (int t = 0; t < NM; ++t) {
-        const int j = t / TI, i = t % TI;
-        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
-        if (t < NR) read_r(aslot, bslot, t, nxt);
-        sched_fence();
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): the next slab's reads are in
-      __syncthreads();
-    };
-    Frags<TI, TJ> F0, F1;
-    __syncthreads();                                     // P0: the converters' first DMAs landed
-    __syncthreads();                                     // P1: slabs 0 and 1 staged
-#pragma unroll
-    for (int r = 0; r < NR; ++r) read_r(0, 0, r, F0);
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __syncthreads();                                     // P2: slab 0 read; its A stage may be refilled
-    int sa = 1, sb = 1;                                  // A and B stage slots of the next slab
-    auto next = [&]() {
-      sa = sa == D - 1 ? 0 : sa + 1;
-      sb = sb == SB - 1 ? 0 : sb + 1;
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(F0, sa, sb, F1);
-      next();
-      if (kt + 1 < nk) {
-        step(F1, sa, sb, F0);
-        next();
-      }
-    }
-    gemm_epilogue<kStoreBf16, NB, 0, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, nullptr);
-  } else {
-    // ---- converter waves
-    const int cw = wave - 4, tid = threadIdx.x - 256;
-    LA la;
-    LB lb;
-    la.init(a.A, a.lda, m0, a.M, a.K, cw);
-    lb.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, a.Kq, cw);
-    constexpr int NL = Sh::NL;
-    const uint32_t lds0 = lds_addr_of(smem);
-    auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
-    // Stages are given as byte offsets that advance by one entry per slab
-    // (no modulo in the loop).
-    auto dma_a = [&](int slab, int aoff) { la.issue_so(lds0 + A0 + aoff, clamp_slab(slab) * BK); };
-    auto dma_w = [&](int slab, int poff) { lb.issue(lds0 + P0 + poff, clamp_slab(slab) * BK); };
-    auto convert = [&](int slab, int poff, int boff) { lb.commit(smem, P0 + poff, B0 + boff, slab * BK, tid); };
-    auto advance = [](int& off, int step, int end) {
-      off += step;
-      if (off == end) off = 0;
-    };
-#pragma unroll
-    for (int sl = 0; sl < D; ++sl) {
-      dma_w(sl, sl * P_BYTES);
-      dma_a(sl, sl * A_BYTES);
-    }
-    wait_vmcnt<(D - 2) * NL>();                          // slabs 0 and 1 landed (for this wave)
-    __syncthreads();                                     // P0: everyone's
-    convert(0, 0, 0);
-    convert(1, P_BYTES, B_BYTES);
-    __syncthreads();                                     // P1
-    dma_w(D, 0);                                         // ring entry 0 is free again
-    __syncthreads();                                     // P2
-    // Issue order: (w0, a0) .. (w_{D-1}, a_{D-1}), w_D, then per iteration i
-    // a_{i+D}, w_{i+D+1}. Iteration i needs a_{i+2} and w_{i+3} before its
-    // barrier; at most the D - 2 later iterations' DMAs (counting w_D as the
-    // tail of iteration -1) are still in flight.
-    int a_off = 0;                                       // A stage of slab i + D
-    int w_off = P_BYTES;                                 // ring entry of slab i + D + 1
-    int c_off = 2 * P_BYTES;                             // ring entry of slab i + 2
-    int b_off = 2 * B_BYTES;                             // B stage of slab i + 2
-    for (int kt = 0; kt < nk; ++kt) {
-      dma_a(kt + D, a_off);
-      dma_w(kt + D + 1, w_off);
-      convert(kt + 2, c_off, b_off);
-      advance(a_off, A_BYTES, D * A_BYTES);
-      advance(w_off, P_BYTES, D * P_BYTES);
-      advance(c_off, P_BYTES, D * P_BYTES);
-      advance(b_off, B_BYTES, SB * B_BYTES);
-      wait_vmcnt<(D - 2) * NL>();
-      __syncthreads();
-    }
-    wait_vmcnt<0>();                                     // drain the trailing re-loads
-  }
-}
-
-// ---------------------------------------------------------------------------
 // The forward with a fused B operand (Y = X W_hat^T, no workspace): W_hat is
 // made in LDS from the fp32 master weight (Eq. 1-2) or from packed codes,
 // never stored. Slabs of BK = 32; 8 waves, one of each role per SIMD:
@@ -1621,6 +1423,183 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fused_fwd(const GemmArgs a) {
     // guards inside the loop body let it branch from one slab to a later one
     // of the same trip, after which it must assume fewer loads in flight and
     // waits for up to three slabs' loads that the conversion does not need.
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
+      iter(R2, kt);
+      iter(R3, kt + 1);
+      iter(R0, kt + 2);
+      iter(R1, kt + 3);
+    }
+    if (kt < nk) {
+      iter(R2, kt);
+      if (kt + 1 < nk) {
+        iter(R3, kt + 1);
+        if (kt + 2 < nk) iter(R0, kt + 2);
+      }
+    }
+    wait_vmcnt<0>();                                     // drain the trailing re-loads
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dX = dY W_hat with a fused B operand (no workspace): W_hat^T made in LDS from
+// the fp32 master weight (Eq. 1-2) or from packed codes, never stored. The
+// same two roles as the forward: waves 0-3 load dY themselves (D stages by
+// DMA, 4-byte DMA with the contraction's tail masked when ADW) and run the
+// MFMAs of slab i with the transpose reads of slab i + 1; waves 4-7 keep their
+// 16 weights of every slab (and the row's s, z) in a queue of U = 4 register
+// slabs (WColLoader), load slab i + 2 + U while slab i + 2 is converted into
+// the MN-contiguous B stage (i + 2) % 3. One barrier per slab; the
+// converters' loads land in their own registers, so their barrier waits for
+// nothing but their B-stage writes.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BL, int NB, int ADW>
+struct FusedDxShape {
+  static constexpr int BK = 32, U = 4, SB = 3;
+  using L = LdsLayout<BK, kLdsSlots>;
+  using LA = DmaTileK<BM, BK, kLdsSlots, 4, ADW>;
+  using LT = DmaTileMN<BN, BK, 4>;
+  static constexpr int A_BYTES = BM * L::PITCH, B_BYTES = BK * LT::PITCH;
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int D_FIT = (LDS_MAX - SB * B_BYTES) / A_BYTES;
+  static constexpr int D_CNT = 2 + 63 / LA::NI;
+  static constexpr int D_MIN = D_FIT < D_CNT ? D_FIT : D_CNT;
+  static constexpr int D = D_MIN < 6 ? D_MIN : 6;
+  static_assert(D >= 3, "three A stages at least");
+  static constexpr int LDS = D * A_BYTES + SB * B_BYTES;
+};
+
+template <int BM, int BN, int BL, int NB, int ADW>
+__global__ __launch_bounds__(512, 1) void k_gemm_fused_dx(const GemmArgs a) {
+  using Sh = FusedDxShape<BM, BN, BL, NB, ADW>;
+  constexpr int BK = Sh::BK, D = Sh::D, SB = Sh::SB, U = Sh::U;
+  using LA = typename Sh::LA;
+  using LT = typename Sh::LT;
+  static_assert(BL == kFp32Quant || BL == kPacked, "fused B operands only");
+  static_assert(BN == 128, "eight converter threads per weight row, 16 columns each");
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TI = WM / 16, TJ = WN / 16, NM = TI * TJ, NR = TI + TJ;
+  static_assert(NR <= NM, "a slab's MFMAs cover the next slab's reads");
+  constexpr int A_BYTES = Sh::A_BYTES, B_BYTES = Sh::B_BYTES;
+  constexpr int A0 = 0, B0 = D * A_BYTES;
+  static_assert(B0 + SB * B_BYTES == Sh::LDS, "LDS map");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Sh::LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = (a.K + BK - 1) / BK;
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto clamp_slab = [&](int slab) { return slab < nk ? slab : nk - 1; };
+
+  if (wave < 4) {
+    // ---- MFMA waves: dY by DMA, fragment reads (B by transpose reads), MFMAs
+    LA la;
+    la.init(a.A, a.lda, m0, a.M, a.K, wave);
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    auto read_r = [&](int aoff, int boff, int r, Frags<TI, TJ>& f) {
+      const uint8_t* at = &smem[A0 + aoff];
+      const uint8_t* bt = &smem[B0 + boff];
+      if (r < TI) f.a[r] = LA::frag(at, wm0 + r * 16 + (lane & 15), 0, lane);
+      else f.b[r - TI] = LT::frag(bt, wn0 + (r - TI) * 16 + (lane & 15), 0, lane);
+    };
+    f32x4 acc[TJ][TI];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int i = 0; i < TI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int GAP = NM / LA::NI > 0 ? NM / LA::NI : 1;   // MFMAs per dY DMA instruction
+    constexpr int DPM = (LA::NI + NM - 1) / NM;            // DMA instructions per MFMA
+    static_assert(DPM * NM >= LA::NI, "one slab's MFMAs cover its DMA");
+    auto step = [&](const Frags<TI, TJ>& cur, int aoff, int boff, Frags<TI, TJ>& nxt, int dslab, int doff) {
+#pragma unroll
+      for (int t = 0; t < NM; ++t) {
+        const int j = t / TI, i = t % TI;
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
+        if (t < NR) read_r(aoff, boff, t, nxt);
+#pragma unroll
+        for (int u = 0; u < DPM; ++u) {
+          const int q = DPM > 1 ? t * DPM + u : t / GAP;
+          if ((DPM > 1 || t % GAP == GAP - 1) && q < LA::NI)
+            la.issue_so_q(lds0 + A0 + doff, clamp_slab(dslab) * BK, q);
+        }
+        sched_fence();
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): the next slab's reads are in
+      wait_vmcnt<(D - 2) * LA::NI>();                    // dY of the slab after next landed (own DMAs)
+      __syncthreads();
+    };
+#pragma unroll
+    for (int sl = 0; sl < D; ++sl) la.issue_so(lds0 + A0 + sl * A_BYTES, clamp_slab(sl) * BK);
+    wait_vmcnt<(D - 2) * LA::NI>();                      // dY slabs 0 and 1 landed (own)
+    Frags<TI, TJ> F0, F1;
+    __syncthreads();                                     // P0: everyone's dY 0 and 1
+    __syncthreads();                                     // P1: B stages 0 and 1 converted
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_r(0, 0, r, F0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __syncthreads();                                     // P2: slab 0 read; its dY stage may be refilled
+    int aoff = A_BYTES, boff = B_BYTES, doff = 0;        // slab i + 1's stages; dY stage of slab i + D
+    auto next = [&]() {
+      aoff = aoff + A_BYTES == D * A_BYTES ? 0 : aoff + A_BYTES;
+      boff = boff + B_BYTES == SB * B_BYTES ? 0 : boff + B_BYTES;
+      doff = doff + A_BYTES == D * A_BYTES ? 0 : doff + A_BYTES;
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(F0, aoff, boff, F1, kt + D, doff);
+      next();
+      if (kt + 1 < nk) {
+        step(F1, aoff, boff, F0, kt + 1 + D, doff);
+        next();
+      }
+    }
+    wait_vmcnt<0>();                                     // drain the trailing re-loads
+    gemm_epilogue<kStoreBf16, NB, 0, BM, BN, TI, TJ, WN>(a, acc, m0, n0, wm0, wn0, lane, nullptr);
+  } else {
+    // ---- converter waves: weight rows to registers, B stages (W_hat^T)
+    const int tid = threadIdx.x - 256;
+    const int row = tid / 8, c16 = tid % 8;
+    WColLoader<BL, NB> wl;
+    wl.init(a.B, BL == kFp32Quant ? a.ldb * 4 : a.ldb, n0, a.K, a.s, a.z, a.G, a.group, tid);
+    uint4 pk[2];
+    auto fetch = [&](WColSlab<BL, NB>& w, int slab) { wl.load(w, clamp_slab(slab) * BK); };
+    auto convert = [&](const WColSlab<BL, NB>& w, int slab, int boff) {
+      convert_cols<BL, NB>(w, a.Kq, slab * BK + row < a.K, wl.sh, pk);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) *(uint4*)&smem[B0 + boff + LT::off(row, 2 * c16 + m)] = pk[m];
+    };
+    WColSlab<BL, NB> R0, R1, R2, R3;                     // slab j in R[j % 4]
+    static_assert(U == 4, "four named register slabs");
+    fetch(R0, 0);
+    fetch(R1, 1);
+    fetch(R2, 2);
+    fetch(R3, 3);
+    __syncthreads();                                     // P0
+    convert(R0, 0, 0);
+    fetch(R0, U);
+    convert(R1, 1, B_BYTES);
+    fetch(R1, U + 1);
+    __syncthreads();                                     // P1
+    __syncthreads();                                     // P2
+    int boff = 2 * B_BYTES;                              // B stage of slab i + 2
+    // The scheduling fence keeps each conversion after the barrier before
+    // it: the conversions are register work, and the compiler otherwise
+    // hoists a whole trip's of them to its start, where they wait for every
+    // weight load in flight.
+    auto iter = [&](WColSlab<BL, NB>& R, int kt) {
+      sched_fence();
+      convert(R, kt + 2, boff);
+      fetch(R, kt + 2 + U);
+      boff = boff + B_BYTES == SB * B_BYTES ? 0 : boff + B_BYTES;
+      __syncthreads();
+    };
+    // Whole groups of four slabs in a loop without guards, the rest straight
+    // after it: with guards inside the loop body the compiler may branch from
+    // one slab to a later one of the same trip and then waits for register
+    // loads the conversion does not need.
     int kt = 0;
     for (; kt + 4 <= nk; kt += 4) {
       iter(R2, kt);
