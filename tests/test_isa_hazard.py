@@ -7,7 +7,8 @@ see the MFMA's write-back latency. The kernel waits it out itself (three
 transformation that copies or reads accumulators in between (e.g. a peeled
 loop iteration whose accumulators live in other AGPRs) gives wrong results
 without any fault, so every instantiation is checked: after each MFMA, no
-v_accvgpr_read / v_accvgpr_mov may come before the drain.
+v_accvgpr_read / v_accvgpr_mov of its result registers may come before the
+drain.
 """
 import os
 import re
@@ -37,22 +38,42 @@ def _device_asm(src: str) -> str:
     return open(out).read()
 
 
+def _agprs(op: str):
+    """The AGPR numbers an operand names (a5, a[4:7])."""
+    m = re.fullmatch(r"a(\d+)", op) or re.fullmatch(r"a\[(\d+):(\d+)\]", op)
+    if not m:
+        return set()
+    lo = int(m.group(1))
+    hi = int(m.group(2)) if m.lastindex == 2 else lo
+    return set(range(lo, hi + 1))
+
+
 def accumulator_hazards(asm: str):
-    """{kernel: count} of accumulator reads or moves between an MFMA and the drain."""
+    """{kernel: count} of reads or moves of an MFMA's result AGPRs between the MFMA and the drain.
+
+    The kernel text is walked in order; the result registers of every MFMA
+    since the last drain (three `s_nop 15`) are pending, and a v_accvgpr_read
+    or v_accvgpr_mov whose source is pending counts. (Moves of other AGPRs,
+    e.g. zeros copied into accumulators before their first MFMA, do not.)
+    """
     found = {}
     for m in re.finditer(r"^(_Z[^:\s]+):", asm, re.M):
         name = m.group(1)
         end = asm.index(".Lfunc_end", m.end())
-        pending, nops, cnt = False, 0, 0
+        pending, nops, cnt = set(), 0, 0
         for line in asm[m.end():end].split("\n"):
-            t = line.strip()
+            t = line.split(";")[0].strip()
+            ops = [o.strip() for o in t.split(None, 1)[1].split(",")] if " " in t else []
             if t.startswith("v_mfma"):
-                pending, nops = True, 0
+                pending |= _agprs(ops[0])
+                nops = 0
             elif pending and t.startswith("s_nop 15"):
                 nops += 1
-                pending = nops < 3
+                if nops == 3:
+                    pending, nops = set(), 0
             elif pending and (t.startswith("v_accvgpr_read") or t.startswith("v_accvgpr_mov")):
-                cnt += 1
+                if _agprs(ops[1]) & pending:
+                    cnt += 1
         if cnt:
             found[name] = cnt
     return found
@@ -74,8 +95,14 @@ _Zok:
 \ts_nop 15
 \tv_accvgpr_read_b32 v8, a0
 .Lfunc_end1:
+_Zzero:
+\tv_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]
+\tv_accvgpr_mov_b32 a5, a24
+\tv_accvgpr_read_b32 v9, a2 ; the MFMA's result
+\ts_nop 15
+.Lfunc_end2:
 """
-    assert accumulator_hazards(asm) == {"_Zk": 1}
+    assert accumulator_hazards(asm) == {"_Zk": 1, "_Zzero": 1}
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")

@@ -133,6 +133,48 @@ def perturb_qparams(seed: int, s: np.ndarray, z: np.ndarray, bits: int, frac: fl
     return s2, z2
 
 
+@dataclasses.dataclass
+class ExactSum:
+    """Inputs on which every GEMM of the path sums exactly in fp32 (see exact_sum_inputs)."""
+    X: np.ndarray        # bf16 bits [m, in], integer values in [-amp, amp]
+    dY: np.ndarray       # bf16 bits [m, out], integer values in [-amp, amp]
+    W: np.ndarray        # fp32 [out, in] = s * t, t ~ U(-(K + 2), K + 2) per element
+    s: np.ndarray        # fp32 [out, G], powers of two 2^-5, 2^-6 or 2^-7
+    z: np.ndarray        # fp32 [out, G], an integer in [0, K] plus U(-0.4, 0.4)
+    zp: np.ndarray       # fp32 [out, G], integers in [0, K] (a frozen zero point)
+    Wq: np.ndarray       # uint8 [out, in*bits/8], uniform random packed bytes
+
+
+def exact_sum_inputs(seed: int, m: int, out: int, inp: int, bits: int, amp: int = 2,
+                     group: int = GROUP) -> ExactSum:
+    """Seeded inputs whose GEMMs are exact in fp32 in any summation order.
+
+    Activations and output gradients are small integers, step sizes are powers
+    of two 2^-e (e in 5..7) and the zero points used are integers, so any
+    dequantised weight (q - z) s is an integer times 2^-e and every product of
+    an activation and a weight is a multiple of 2^-7. While the sum of the
+    magnitudes of one output's products stays below 2^17 (amp * K * 2^-5 per
+    product, at most 2^-2 * K_dim * amp * K), every partial sum is a multiple
+    of 2^-7 below 2^24 * 2^-7 and hence exact in fp32, whatever the order of
+    the additions. The same holds for dY^T X (integers below 2^24). W = s * t
+    is exact in fp32 (a power-of-two scaling), so W / s = t exactly.
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    k = (1 << bits) - 1
+    G = inp // group
+    X = g.integers(-amp, amp + 1, size=(m, inp)).astype(np.float32)
+    dY = g.integers(-amp, amp + 1, size=(m, out)).astype(np.float32)
+    s = np.ldexp(np.float32(1.0), -g.integers(5, 8, size=(out, G))).astype(np.float32)
+    zi = g.integers(0, k + 1, size=(out, G))
+    z = (zi + g.uniform(-0.4, 0.4, size=(out, G))).astype(np.float32)
+    zp = g.integers(0, k + 1, size=(out, G)).astype(np.float32)
+    t = g.uniform(-(k + 2), k + 2, size=(out, inp)).astype(np.float32)
+    W = (np.repeat(s, group, axis=1) * t).astype(np.float32)
+    assert (inp * bits) % 8 == 0
+    Wq = g.integers(0, 256, size=(out, inp * bits // 8), dtype=np.uint8)
+    return ExactSum(to_bf16_bits(X), to_bf16_bits(dY), W, s, z, zp, Wq)
+
+
 # --------------------------------------------------------------------------
 # The five workloads
 # --------------------------------------------------------------------------
