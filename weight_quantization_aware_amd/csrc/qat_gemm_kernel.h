@@ -362,6 +362,37 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_{lo, hi}, b2_));
 }
 
+// bf16 W_hat = bf16(fl32((q - z) s)) of 2-bit codes by table: the group's
+// four values are made once per call, with the per-element arithmetic, and
+// v_perm_b32 (byte k of {S0, S1} is byte k of S1 for k < 4, of S0 - 4 for
+// k >= 4) picks each pair's two bf16 from them. lo holds the low bytes of the
+// four values, hi their high bytes; for codes (a, b) (4 bits t = a + 4 b) the
+// selector bytes are (a, 4 + a, b, 4 + b): t times 1 + 2^8 + 2^14 + 2^22 puts
+// copies of t at bits 0, 8, 14 and 22 (disjoint, no carries), the mask keeps
+// a at bits 0-1 and 8-9 and b at bits 16-17 and 24-25. Four VALU operations
+// per pair instead of an extraction, a conversion, a subtraction and a
+// multiplication per code. x: codes LSB-first from bit 0; dword m of o is
+// codes 2m, 2m + 1 (the first in the low half); dead (live false) gives +0.
+template <int NP>
+__device__ __forceinline__ void lut2_pairs(uint32_t x, float sv, float zv, bool live, uint32_t (&o)[NP]) {
+  const uint32_t p01 = pack2_bf16((0.f - zv) * sv, (1.f - zv) * sv);
+  const uint32_t p23 = pack2_bf16((2.f - zv) * sv, (3.f - zv) * sv);
+  const uint32_t lo = live ? __builtin_amdgcn_perm(p23, p01, 0x06040200u) : 0u;
+  const uint32_t hi = live ? __builtin_amdgcn_perm(p23, p01, 0x07050301u) : 0u;
+  // the mask in an SGPR and the high-half bits in a VGPR (opaque to the
+  // compiler, so that the two fold into one v_and_or_b32, whose VOP3 form
+  // takes no literals)
+  uint32_t kmask, kor;
+  asm("s_mov_b32 %0, 0x03030303" : "=s"(kmask));
+  asm("v_mov_b32 %0, 0x04000400" : "=v"(kor));
+#pragma unroll
+  for (int m = 0; m < NP; ++m) {
+    const uint32_t t = (x >> (4 * m)) & 15u;
+    const uint32_t sel = ((t * 0x00404101u) & kmask) | kor;
+    o[m] = __builtin_amdgcn_perm(hi, lo, sel);
+  }
+}
+
 // A DMA instruction index of a slab loaded by 4 waves: instruction q of wave
 // cw; where the slab has fewer instructions than 4 x NI the last one repeats
 // (the same bytes to the same place), so every wave issues NI.
@@ -513,6 +544,15 @@ __device__ __forceinline__ void convert_slab(const WSlab<KIND, NB, WPT>& w, floa
       hi = k + 1 == i ? d[i] : hi;
     }
     const uint64_t x = ((uint64_t)hi << 32 | lo) >> (bit & 31);
+    if constexpr (NB == 2) {
+      uint32_t o[WPT / 2];
+      lut2_pairs<WPT / 2>((uint32_t)x, sv, zv, true, o);
+#pragma unroll
+      for (int m = 0; m < WPT / 8; ++m)
+        *(uint4*)&smem[b + L::off(row, (WPT / 8) * q + m)] = make_uint4(o[4 * m], o[4 * m + 1], o[4 * m + 2],
+                                                                        o[4 * m + 3]);
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < WPT; ++e) h[e] = ((float)(uint32_t)((x >> (NB * e)) & ((1u << NB) - 1)) - zv) * sv;
   } else {
@@ -619,6 +659,13 @@ template <int KIND, int NB>
 __device__ __forceinline__ void convert_cols(const WColSlab<KIND, NB>& w, float K, bool live, int sh,
                                              uint4 (&pk)[2]) {
   float h[16];
+  if constexpr (KIND == kPacked && NB == 2) {
+    uint32_t o[8];
+    lut2_pairs<8>(w.d[0], w.s, w.z, live, o);
+    pk[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    pk[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    return;
+  }
   if constexpr (KIND == kPacked) {
     uint64_t x;
     if constexpr (NB == 2) x = w.d[0];
