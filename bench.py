@@ -388,6 +388,14 @@ def main():
         roofline["frac_of_measured_peak"] = round(
             achieved / (extras["measured_peaks"]["mfma_bf16_tflops"] if kind == "mfma"
                         else extras["measured_peaks"]["hbm_read_gbs"]), 4)
+        # each HBM-bound kernel against the time its reads and writes take at
+        # the measured stream rates (reads at the read peak, writes at the write peak)
+        pk = extras["measured_peaks"]
+        for label, row in hbm.items():
+            rd, wr = rw_bytes(label, out, inp, bits)
+            t_floor = rd / (pk["hbm_read_gbs"] * 1e9) + wr / (pk["hbm_write_gbs"] * 1e9)
+            row["frac_of_measured_rw"] = round(t_floor / (row["cold"]["median_ms"] * 1e-3), 4)
+            row["frac_of_measured_rw_warm"] = round(t_floor / (row["warm_us"] * 1e-6), 4)
     g.release()
 
     cpu = None
@@ -444,16 +452,36 @@ def _clocks():
 
 
 def measured_peaks(Q, torch, dev, g):
-    """Practical peaks on this GPU: a register-resident bf16 MFMA loop and a
-    read stream over 1 GiB (beyond the 256 MiB MALL); medians of 5 / 10."""
+    """Practical peaks on this GPU: a register-resident bf16 MFMA loop, and a
+    read stream and a write stream over 1 GiB (beyond the 256 MiB MALL);
+    medians of 5 / 10 / 10."""
     blocks = 256
     scratch = torch.empty(max(Q.lib().qat_peak_scratch_bytes(2048) // 4, 2048 * 256), device=dev)
     flops = Q.lib().qat_peak_mfma_flops(blocks, 4096)
     t = np.median(g.per_call(lambda: Q.peak_mfma(blocks, 4096, scratch), 5)) * 1e-3
     big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     tr = np.median(g.per_call(lambda: Q.peak_read(big, 2048, scratch), 10)) * 1e-3
+    tw = np.median(g.per_call(lambda: Q.peak_write(big, 2048), 10)) * 1e-3
     return {"mfma_bf16_tflops": round(flops / t / 1e12, 1), "hbm_read_gbs": round((1 << 30) / tr / 1e9, 1),
-            "what": "register-resident v_mfma_f32_16x16x32_bf16 loop, 8 waves per CU; grid-stride read of 1 GiB"}
+            "hbm_write_gbs": round((1 << 30) / tw / 1e9, 1),
+            "what": "register-resident v_mfma_f32_16x16x32_bf16 loop, 8 waves per CU; grid-stride read and "
+                    "grid-stride write of 1 GiB"}
+
+
+def rw_bytes(label, out, inp, bits):
+    """(read, written) bytes of one launch of an HBM-bound kernel; they add up
+    to work_per_launch's bytes."""
+    G = inp // 64
+    n = out * inp
+    if label == "init_minmax":
+        return n * 4, 2 * out * G * 4
+    if label in ("quant_w_hat", "quant_w_hat_t"):
+        return n * 4 + 2 * out * G * 4, n * 2
+    if label == "pack":
+        return n * 4 + 2 * out * G * 4, n * bits / 8 + out * G * 4
+    if label in ("dequant", "dequant_t"):
+        return n * bits / 8 + 2 * out * G * 4, n * 2
+    raise KeyError(label)
 
 
 def by_group(Q, torch, dev, g, W, X, dY, bits):

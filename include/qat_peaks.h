@@ -31,6 +31,14 @@ int32_t qat_peak_mfma(int32_t blocks, int32_t iters, float* scratch, hipStream_t
  */
 int32_t qat_peak_read(const void* buf, size_t bytes, int32_t blocks, float* scratch, hipStream_t stream);
 
+/*
+ * A grid-stride store over the first bytes / 16 * 16 bytes of buf (16-byte
+ * aligned, device; its contents are overwritten) by `blocks` 256-thread
+ * workgroups. Time it with events over a buffer larger than the 256 MiB MALL
+ * for the HBM write ceiling.
+ */
+int32_t qat_peak_write(void* buf, size_t bytes, int32_t blocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

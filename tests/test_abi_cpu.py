@@ -160,6 +160,9 @@ def test_peak_probe_host_validation():
     assert L.qat_peak_mfma(0, 10, FAKE, None) == 1
     assert L.qat_peak_read(None, 1 << 20, 16, FAKE, None) == 1
     assert L.qat_peak_read(FAKE + 4, 1 << 20, 16, FAKE, None) == 1
+    assert L.qat_peak_write(None, 1 << 20, 16, None) == 1
+    assert L.qat_peak_write(FAKE + 4, 1 << 20, 16, None) == 1
+    assert L.qat_peak_write(FAKE, 8, 16, None) == 1
 
 
 def test_deploy_validation():

@@ -51,6 +51,7 @@ _SIGS = {
     "qat_peak_scratch_bytes": [_c_i32],
     "qat_peak_mfma": [_c_i32, _c_i32, _c_vp, _c_vp],
     "qat_peak_read": [_c_vp, _c_sz, _c_i32, _c_vp, _c_vp],
+    "qat_peak_write": [_c_vp, _c_sz, _c_i32, _c_vp],
     "qat_fakequant_linear_fwd_noalloc": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
                                          _c_vp, _c_vp],
     "qat_noalloc_max_weights": [],
@@ -457,6 +458,13 @@ def peak_read(buf: torch.Tensor, blocks: int, scratch: torch.Tensor) -> int:
     """Launch the read-stream kernel over buf on the current stream; returns bytes read."""
     nbytes = buf.numel() * buf.element_size()
     _call("qat_peak_read", _p(buf), nbytes, blocks, _p(scratch), _stream())
+    return nbytes - nbytes % 16
+
+
+def peak_write(buf: torch.Tensor, blocks: int) -> int:
+    """Launch the write-stream kernel over buf (overwritten) on the current stream; returns bytes written."""
+    nbytes = buf.numel() * buf.element_size()
+    _call("qat_peak_write", _p(buf), nbytes, blocks, _stream())
     return nbytes - nbytes % 16
 
 

@@ -1,7 +1,8 @@
 // Practical-peak probes for the roofline: a register-resident MFMA loop (the
-// bf16 matrix-core ceiling at the running clock) and a read-stream kernel (the
-// HBM read ceiling for a buffer larger than the 256 MiB MALL). Measurement
-// utilities beside the method's calls; they compute nothing of the method.
+// bf16 matrix-core ceiling at the running clock) and read- and write-stream
+// kernels (the HBM read and write ceilings for buffers larger than the
+// 256 MiB MALL). Measurement utilities beside the method's calls; they
+// compute nothing of the method.
 #include <hip/hip_runtime.h>
 
 #include "../../include/qat_peaks.h"
@@ -45,6 +46,15 @@ __global__ __launch_bounds__(256) void k_read_stream(const float4* __restrict__ 
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Grid-stride store of n float4 (each the index as a float, so every store
+// writes data the kernel computed).
+__global__ __launch_bounds__(256) void k_write_stream(float4* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float f = (float)i;
+    p[i] = make_float4(f, f, f, f);
+  }
+}
+
 }  // namespace
 
 extern "C" __attribute__((visibility("default"))) int64_t qat_peak_mfma_flops(int32_t blocks, int32_t iters) {
@@ -68,5 +78,13 @@ extern "C" __attribute__((visibility("default"))) int32_t qat_peak_read(const vo
   if (!buf || !scratch || blocks <= 0 || bytes < 16 || ((uintptr_t)buf & 15)) return 1;
   hipLaunchKernelGGL(k_read_stream, dim3((unsigned)blocks), dim3(256), 0, stream, (const float4*)buf,
                      (int64_t)(bytes / 16), scratch);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+extern "C" __attribute__((visibility("default"))) int32_t qat_peak_write(void* buf, size_t bytes, int32_t blocks,
+                                                                         hipStream_t stream) {
+  if (!buf || blocks <= 0 || bytes < 16 || ((uintptr_t)buf & 15)) return 1;
+  hipLaunchKernelGGL(k_write_stream, dim3((unsigned)blocks), dim3(256), 0, stream, (float4*)buf,
+                     (int64_t)(bytes / 16));
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
