@@ -135,10 +135,13 @@ void launch_pick_fused(const GemmArgs& a, hipStream_t st) {
 // dX = dY W_hat with W_hat^T made in LDS from the weight's rows
 // (k_gemm_fused_dx).
 // ADW: dY by 4-byte DMA with the contraction's tail masked (out not a
-// multiple of 64).
+// multiple of 64). Its 256x128 instance needs more than the 256 VGPRs of two
+// waves per SIMD (328 bytes of scratch per lane, spills inside the main
+// loop): 2.5-5x slower than 128x128 tiles at out = 4100 and 11000, so ragged
+// contractions always take 128x128.
 template <int BL, int NB, int ADW>
 void launch_pick_dx_fused_a(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 128) >= 256) launch_fused_dx<256, 128, BL, NB, ADW>(a, st);
+  if (ADW == 0 && tiles(a, 256, 128) >= 256) launch_fused_dx<256, 128, BL, NB, ADW>(a, st);
   else launch_fused_dx<128, 128, BL, NB, ADW>(a, st);
 }
 
@@ -184,7 +187,10 @@ void launch_gemm_dx(const GemmArgs& a, hipStream_t st) {
 // K = 11008).
 template <int AL>
 void launch_gemm_dx_mn_al(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
+  // with dY by 4-byte DMA (kKContigD) the 256x256 eight-wave instance spills
+  // inside its main loop; 128x256 tiles measured 1.3-1.6x faster there
+  // (M = 4096, out = 4100 and 11000)
+  if (AL == kKContig && tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
   else if (tiles(a, 128, 256) >= 192) launch_bf16<128, 256, 3, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
   else launch_bf16<128, 128, 4, 2, 2, AL, kMNContig, kStoreBf16, 1>(a, st);
 }
