@@ -69,10 +69,12 @@ def _premise(a: np.ndarray, w: np.ndarray) -> None:
 
 
 # (M, out, in, bits): several tiles with ragged edges in M, out and in; a
-# short contraction; a long one that is not a multiple of 64 in out; and the
-# Llama-2-7B q_proj workload at full size.
+# short contraction; a long one that is not a multiple of 64 in out; the
+# Llama-2-7B q_proj workload at full size; and q_proj-sized products with
+# out = 4100 at 4096 tokens, whose dX contractions end mid-slab on the tile
+# shapes that large ragged products take (128x128 fused, 128x256 staged).
 CASES = [(300, 320, 512, 3), (2085, 4096, 256, 2), (100, 4160, 4160, 3), (257, 4100, 192, 4),
-         (2048, 4096, 4096, 2)]
+         (2048, 4096, 4096, 2), (4096, 4100, 4096, 2)]
 
 
 @pytest.mark.parametrize("M,out,inp,bits", CASES)
