@@ -55,10 +55,22 @@ void launch_fused_dx(const GemmArgs& a, hipStream_t st) {
   QAT_LAUNCH((k_gemm_fused_dx<BM, BN, BL, NB, ADW>), dim3((unsigned)tiles(a, BM, BN)), dim3(512), 0, st, a);
 }
 
+// 256x256 tiles (8 waves) or 128x256 (8 waves) for a product with at least
+// one round of 256x256 tiles on the 256 CUs: whichever needs less time,
+// counting whole rounds of tiles. A 256x256 tile takes ~1.7x as long as a
+// 128x256 one (measured at K = 4096), so the bigger tiles lose where their
+// last round is mostly empty: 2048 x 11008 has 344 tiles of 256x256 (two
+// rounds, the second 34% full) but 688 of 128x256 (three rounds), and ran
+// 168-183 us on 256x256 tiles against 147-170 us on 128x256.
+bool prefer_256x256(const GemmArgs& a) {
+  const int64_t t256 = tiles(a, 256, 256), t128 = tiles(a, 128, 256);
+  return t256 >= 256 && ((t256 + 255) / 256) * 17 <= ((t128 + 255) / 256) * 10;
+}
+
 // Returns the number of workgroups launched.
 template <int AMN, int BMN, int EP, int NB>
 int64_t launch_pick(const GemmArgs& a, hipStream_t st) {
-  if (tiles(a, 256, 256) >= 256) {
+  if (prefer_256x256(a)) {
     if (a.K <= 4096) launch_bf16<256, 256, 2, 2, 4, AMN, BMN, EP, NB>(a, st);
     else launch_bf16<256, 256, 2, 2, 2, AMN, BMN, EP, NB>(a, st);
     return tiles(a, 256, 256);
@@ -190,7 +202,7 @@ void launch_gemm_dx_mn_al(const GemmArgs& a, hipStream_t st) {
   // with dY by 4-byte DMA (kKContigD) the 256x256 eight-wave instance spills
   // inside its main loop; 128x256 tiles measured 1.3-1.6x faster there
   // (M = 4096, out = 4100 and 11000)
-  if (AL == kKContig && tiles(a, 256, 256) >= 256) launch_bf16<256, 256, 2, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
+  if (AL == kKContig && prefer_256x256(a)) launch_bf16<256, 256, 2, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
   else if (tiles(a, 128, 256) >= 192) launch_bf16<128, 256, 3, 2, 4, AL, kMNContig, kStoreBf16, 1>(a, st);
   else launch_bf16<128, 128, 4, 2, 2, AL, kMNContig, kStoreBf16, 1>(a, st);
 }
