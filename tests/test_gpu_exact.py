@@ -72,9 +72,12 @@ def _premise(a: np.ndarray, w: np.ndarray) -> None:
 # short contraction; a long one that is not a multiple of 64 in out; the
 # Llama-2-7B q_proj workload at full size; and q_proj-sized products with
 # out = 4100 at 4096 tokens, whose dX contractions end mid-slab on the tile
-# shapes that large ragged products take (128x128 fused, 128x256 staged).
+# shapes that large ragged products take (128x128 fused, 128x256 staged);
+# and a Llama-2-7B down projection at 2048 tokens, whose 2048 x 11008 dX
+# takes 128x256 tiles because 256x256 ones would leave their second round
+# mostly empty.
 CASES = [(300, 320, 512, 3), (2085, 4096, 256, 2), (100, 4160, 4160, 3), (257, 4100, 192, 4),
-         (2048, 4096, 4096, 2), (4096, 4100, 4096, 2)]
+         (2048, 4096, 4096, 2), (4096, 4100, 4096, 2), (2048, 4096, 11008, 3)]
 
 
 @pytest.mark.parametrize("M,out,inp,bits", CASES)
@@ -116,7 +119,9 @@ def test_fakequant_exact(M, out, inp, bits):
         assert rel_fro(gs.cpu().numpy(), r["ds"]) < TOL_F32, name
 
 
-E2E_CASES = CASES + [(4096, 11008, 4096, 2)]      # + the E2E-QP MLP's gate/up shape
+# + the E2E-QP MLP's gate/up shape, and the same at 2048 tokens (a 2048 x
+# 11008 forward on 128x256 tiles)
+E2E_CASES = CASES + [(4096, 11008, 4096, 2), (2048, 11008, 4096, 2)]
 
 
 @pytest.mark.parametrize("M,out,inp,bits", E2E_CASES)
